@@ -1,0 +1,248 @@
+"""CPU oracle for the BinaryAttention forward pass (numpy, float64).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
+links this module: only the test suite, the smoke check and the benchmark's
+CPU-baseline leg do.  It shares no code, table or helper with the HIP library.
+
+Sources (the two gist.science summaries of "BinaryAttention: One-Bit
+QK-Attention for Vision and Diffusion Transformers"):
+
+* es page, technical summary, section 2 "Metodologia", item "Representaciones
+  Binarias Escaladas": queries and keys become s_i = mu_q * sign(q_i) and
+  t_j = mu_k * sign(k_j), and their similarity is taken with XNOR + popcount.
+* es page, section 2, item "Mejora mediante Sesgo": a learnable bias b_ij is
+  added to the scores; one of its forms is position-sensitive.
+* es page, section 2, item "Implementacion en Hardware" and ko page, section
+  2 (c) "hardware-aware implementation": the kernel follows FlashAttention2,
+  i.e. it computes exactly softmax(S) V; tiling changes the order, not the
+  result.
+* ko page, section 2 (b).1: the scale is a mean taken over the token's
+  channels.
+
+Readings where the pages are silent (each one is listed with its reason in
+the design notes that accompany the repository):
+
+* the per-token scale is alpha = mean over the d channels of |x|;
+* sign(x) = -1 if x < 0 else +1, so +0.0 and -0.0 both give +1 (bit 0);
+* packed bits: channel c goes to word c // 32, bit c % 32 (LSB first);
+  bit = 1 means negative; bits for channels >= d are 0;
+* <sign q, sign k> = d - 2 * popcount(qbits XOR kbits) (XOR with zero pad
+  bits, equal to the XNOR-popcount form over the d real channels);
+* S_ij = scale * alpha_q,i * alpha_k,j * D_ij + T[h, yi - yj + gh - 1,
+  xi - xj + gw - 1] with tokens in row-major (y, x) order on a gh x gw grid,
+  the table shared over the batch, and scale = 1/sqrt(d) by default;
+* no masking: vision/diffusion attention is bidirectional.
+
+Every value is computed in float64 from the exact widening of the bf16
+inputs; integer quantities (bits, D) are returned as integers.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "sign_pm1",
+    "token_scale",
+    "pack_words",
+    "pack_sign_bits",
+    "unpack_sign_bits",
+    "sign_dots",
+    "sign_dots_from_bits",
+    "rel_pos_bias",
+    "binary_scores",
+    "softmax_rows",
+    "binary_attention",
+    "binary_attention_rows",
+]
+
+
+def _f64(x) -> np.ndarray:
+    """Widen an array-like (float32 holding bf16 values, or float64) to float64."""
+    a = np.asarray(x)
+    if a.dtype.kind != "f":
+        raise TypeError(f"expected a floating-point array, got {a.dtype}")
+    return a.astype(np.float64, copy=False)
+
+
+def pack_words(d: int) -> int:
+    """Number of 32-bit sign words per token: ceil(d / 32)."""
+    if d < 1:
+        raise ValueError("d must be >= 1")
+    return (d + 31) // 32
+
+
+def sign_pm1(x) -> np.ndarray:
+    """sign() of the scaled binary representation (es page, section 2,
+    "Representaciones Binarias Escaladas"), with sign(0) = +1.
+
+    Uses an IEEE compare, so -0.0 < 0 is False and -0.0 maps to +1.
+    """
+    a = _f64(x)
+    return np.where(a < 0.0, -1.0, 1.0)
+
+
+def token_scale(x) -> np.ndarray:
+    """Per-token scale mu (alpha): the mean of |x| over the last axis (the d
+    channels of one token).  es page section 2 "Representaciones Binarias
+    Escaladas" (mu is a mean of the queries/keys); ko page section 2 (b).1
+    (mean over the channel axis)."""
+    a = _f64(x)
+    return np.abs(a).sum(axis=-1) / a.shape[-1]
+
+
+def pack_sign_bits(x) -> np.ndarray:
+    """Pack the signs of x[..., d] into uint32 words [..., ceil(d/32)].
+
+    Channel c -> word c // 32, bit c % 32; bit = 1 iff x_c < 0; pad bits 0.
+    The packing is what lets the similarity be taken with XOR/XNOR and
+    popcount (es page, section 2, "Representaciones Binarias Escaladas").
+    """
+    a = _f64(x)
+    d = a.shape[-1]
+    w = pack_words(d)
+    neg = a < 0.0
+    pad = np.zeros(a.shape[:-1] + (32 * w - d,), dtype=bool)
+    neg = np.concatenate([neg, pad], axis=-1).reshape(a.shape[:-1] + (w, 32))
+    weights = np.left_shift(np.uint64(1), np.arange(32, dtype=np.uint64))
+    words = (neg.astype(np.uint64) * weights).sum(axis=-1)
+    return words.astype(np.uint32)
+
+
+def unpack_sign_bits(bits, d: int) -> np.ndarray:
+    """Inverse of pack_sign_bits: +/-1 float64 array [..., d]."""
+    b = np.asarray(bits, dtype=np.uint32)
+    w = b.shape[-1]
+    if w != pack_words(d):
+        raise ValueError("word count does not match d")
+    shifts = np.arange(32, dtype=np.uint32)
+    flags = (b[..., :, None] >> shifts) & np.uint32(1)
+    flags = flags.reshape(b.shape[:-1] + (32 * w,))[..., :d]
+    return np.where(flags == 1, -1.0, 1.0)
+
+
+def sign_dots(q, k) -> np.ndarray:
+    """D = sign(Q) sign(K)^T per leading index, as int64.
+
+    A float64 matmul of +/-1 entries is exact (|D| <= d << 2**53)."""
+    sq = sign_pm1(q)
+    sk = sign_pm1(k)
+    dots = np.matmul(sq, np.swapaxes(sk, -1, -2))
+    return np.rint(dots).astype(np.int64)
+
+
+def sign_dots_from_bits(qbits, kbits, d: int) -> np.ndarray:
+    """D = d - 2 * popcount(qbits XOR kbits), the XNOR/popcount similarity
+    of the es page (section 2, "Representaciones Binarias Escaladas")
+    written with XOR over zero-padded words.
+
+    qbits [..., Nq, W], kbits [..., Nk, W] -> int64 [..., Nq, Nk]."""
+    qb = np.asarray(qbits, dtype=np.uint32)
+    kb = np.asarray(kbits, dtype=np.uint32)
+    x = np.bitwise_xor(qb[..., :, None, :], kb[..., None, :, :])
+    ham = np.bitwise_count(x).astype(np.int64).sum(axis=-1)
+    return d - 2 * ham
+
+
+def rel_pos_bias(table, gh: int, gw: int) -> np.ndarray:
+    """Dense position-sensitive bias b_ij (es page, section 2, "Mejora
+    mediante Sesgo") from a per-head 2-D relative-position table.
+
+    table: [H, 2*gh-1, 2*gw-1]; tokens are row-major on a gh x gw grid,
+    token i at (yi, xi) = (i // gw, i % gw).
+    Returns [H, N, N] with B[h, i, j] = table[h, yi-yj+gh-1, xi-xj+gw-1].
+    """
+    t = _f64(table)
+    if t.ndim != 3 or t.shape[1] != 2 * gh - 1 or t.shape[2] != 2 * gw - 1:
+        raise ValueError("table must be [H, 2*gh-1, 2*gw-1]")
+    n = gh * gw
+    idx = np.arange(n)
+    y, x = idx // gw, idx % gw
+    dy = y[:, None] - y[None, :] + gh - 1
+    dx = x[:, None] - x[None, :] + gw - 1
+    return t[:, dy, dx]
+
+
+def binary_scores(q, k, table=None, gh: int = 0, gw: int = 0, scale=None,
+                  rows=None) -> dict:
+    """Scores S = scale * alpha_q alpha_k^T * D + b for q, k [B, H, N, d].
+
+    rows: optional 1-D array of query indices; then only those rows of S
+    are formed (keys are always all N).  Returns the intermediates.
+    """
+    qf = _f64(q)
+    kf = _f64(k)
+    if qf.shape != kf.shape or qf.ndim != 4:
+        raise ValueError("q and k must both be [B, H, N, d]")
+    n, d = qf.shape[2], qf.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    r = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    aq = token_scale(qf)
+    ak = token_scale(kf)
+    dots = sign_dots(qf[:, :, r, :], kf)
+    s = float(scale) * aq[:, :, r, None] * ak[:, :, None, :] * dots
+    if table is not None:
+        if gh * gw != n:
+            raise ValueError("N must equal gh * gw when a bias table is given")
+        t = _f64(table)
+        idx = np.arange(n)
+        y, x = idx // gw, idx % gw
+        dy = y[r][:, None] - y[None, :] + gh - 1
+        dx = x[r][:, None] - x[None, :] + gw - 1
+        s = s + t[:, dy, dx][None, :, :, :]
+    return {"alpha_q": aq, "alpha_k": ak, "D": dots, "S": s, "rows": r}
+
+
+def softmax_rows(s) -> np.ndarray:
+    """Row softmax over the last axis, in float64 (max-shifted for range)."""
+    a = _f64(s)
+    m = a.max(axis=-1, keepdims=True)
+    e = np.exp(a - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def binary_attention_rows(q, k, v, table=None, gh: int = 0, gw: int = 0,
+                          scale=None, rows=None, keep=False) -> dict:
+    """O = softmax(S) V for a subset of query rows (all rows if rows=None).
+
+    Rows of attention are independent, so a subset of rows is computed
+    exactly as in the full problem.  keep=True also returns S and P.
+    """
+    vf = _f64(v)
+    sc = binary_scores(q, k, table, gh, gw, scale, rows)
+    p = softmax_rows(sc["S"])
+    o = np.matmul(p, vf)
+    out = {"O": o, "alpha_q": sc["alpha_q"], "alpha_k": sc["alpha_k"],
+           "rows": sc["rows"]}
+    if keep:
+        out.update(S=sc["S"], P=p, D=sc["D"])
+    return out
+
+
+def binary_attention(q, k, v, table=None, gh: int = 0, gw: int = 0,
+                     scale=None, block_rows: int = 1024) -> dict:
+    """Full BinaryAttention forward in float64.
+
+    q, k, v: [B, H, N, d] float arrays holding the (bf16) inputs.
+    table:   [H, 2*gh-1, 2*gw-1] or None (no bias).
+    Returns bits (uint32 [B,H,N,W]) for q and k, alpha (float64 [B,H,N]) for
+    q and k, and O (float64 [B,H,N,d]).  Rows are processed in blocks only to
+    bound memory; the result does not depend on block_rows.
+    """
+    qf, kf, vf = _f64(q), _f64(k), _f64(v)
+    b, h, n, d = qf.shape
+    o = np.empty((b, h, n, d), dtype=np.float64)
+    for r0 in range(0, n, block_rows):
+        rows = np.arange(r0, min(n, r0 + block_rows))
+        o[:, :, rows, :] = binary_attention_rows(
+            qf, kf, vf, table, gh, gw, scale, rows)["O"]
+    return {
+        "q_bits": pack_sign_bits(qf),
+        "k_bits": pack_sign_bits(kf),
+        "alpha_q": token_scale(qf),
+        "alpha_k": token_scale(kf),
+        "O": o,
+    }

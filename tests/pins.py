@@ -1,0 +1,346 @@
+"""Pins that tie the CPU oracle to what the BinaryAttention pages and plain
+mathematics fix, without trusting the oracle itself.
+
+Each pin takes the oracle module (``oracle.dense_fp64``) as ``ob`` and
+raises AssertionError on a mismatch.  The same pins run against deliberately
+broken copies of the oracle in test_oracle_mutations.py, where at least one
+of them must fail for every planted mistake.
+
+What each pin compares against:
+* golden_hand_example: a worked example derived by hand (tests/golden/);
+* bits_*: the per-element definition of the sign bit, popcounts, +/-0;
+* alpha_*: closed forms (x = a * (+/-1 pattern) gives mu = |a|);
+* dots_*: the +/-1 dot product against d - 2*Hamming, parity and extremes;
+* textbook_reduction: when every Q/K token has entries of one magnitude,
+  BinaryAttention is exactly softmax(scale Q K^T + B) V, which torch's
+  scaled_dot_product_attention computes (an independent library routine);
+* bias_*: which key a single large table entry points at, on a non-square
+  grid, and the closed form O = mean(V) when Q = 0 without bias;
+* brute_force_tiny: a triple loop in Python ints and math.fsum;
+* sheppard: E[sign(q) sign(k)] = (2/pi) asin(rho) for correlated normals.
+"""
+
+from __future__ import annotations
+
+import math
+import pathlib
+
+import numpy as np
+import torch
+
+GOLDEN = pathlib.Path(__file__).parent / "golden"
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _bf16_values(rng, shape, scale=1.0):
+    """Random float64 values that are exactly representable in bf16."""
+    x = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+# --------------------------------------------------------------------------
+# golden
+# --------------------------------------------------------------------------
+
+def load_hand_example():
+    rec: dict = {}
+    for line in (GOLDEN / "hand_example_d4.txt").read_text().splitlines():
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, *vals = line.split()
+        rec.setdefault(key, []).append(vals)
+    grid = tuple(int(x) for x in rec["grid"][0])
+    d = int(rec["d"][0][0])
+
+    def arr(key, dtype=float):
+        return np.array([[dtype(x) for x in row] for row in rec[key]])
+
+    return {
+        "gh": grid[0], "gw": grid[1], "d": d,
+        "q": arr("q")[None, None], "k": arr("k")[None, None],
+        "v": arr("v")[None, None], "table": arr("table")[None],
+        "qbits": arr("qbits", int)[:, 0], "kbits": arr("kbits", int)[:, 0],
+        "alpha_q": arr("alpha_q")[0], "alpha_k": arr("alpha_k")[0],
+        "D": arr("D", int), "S": arr("S"),
+    }
+
+
+def golden_hand_example(ob):
+    g = load_hand_example()
+    assert np.array_equal(ob.pack_sign_bits(g["q"])[0, 0, :, 0], g["qbits"])
+    assert np.array_equal(ob.pack_sign_bits(g["k"])[0, 0, :, 0], g["kbits"])
+    assert np.array_equal(ob.token_scale(g["q"])[0, 0], g["alpha_q"])
+    assert np.array_equal(ob.token_scale(g["k"])[0, 0], g["alpha_k"])
+    assert np.array_equal(ob.sign_dots(g["q"], g["k"])[0, 0], g["D"])
+    res = ob.binary_attention_rows(g["q"], g["k"], g["v"], g["table"],
+                                   g["gh"], g["gw"], keep=True)
+    assert np.allclose(res["S"][0, 0], g["S"], rtol=0, atol=1e-15)
+    v = g["v"][0, 0]
+    for i in range(2):
+        w = [math.exp(s) for s in g["S"][i]]
+        tot = math.fsum(w)
+        expect = [math.fsum(w[j] * v[j, c] for j in range(2)) / tot
+                  for c in range(g["d"])]
+        assert np.allclose(res["O"][0, 0, i], expect, rtol=0, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# bits
+# --------------------------------------------------------------------------
+
+def bits_definition(ob):
+    rng = _rng(11)
+    for d in (1, 7, 31, 32, 33, 64, 72, 96, 128, 200):
+        x = _bf16_values(rng, (3, d))
+        x[0, : d // 3] = 0.0
+        x[1, : d // 3] = -0.0
+        bits = ob.pack_sign_bits(x)
+        w = (d + 31) // 32
+        assert bits.shape == (3, w) and bits.dtype == np.uint32
+        for t in range(3):
+            for c in range(32 * w):
+                got = (int(bits[t, c // 32]) >> (c % 32)) & 1
+                want = int(c < d and x[t, c] < 0)
+                assert got == want, (d, t, c)
+            assert sum(bin(int(b)).count("1") for b in bits[t]) == \
+                int(np.sum(x[t] < 0))
+        assert np.array_equal(ob.unpack_sign_bits(bits, d),
+                              np.where(x < 0, -1.0, 1.0))
+
+
+def bits_special_values(ob):
+    for d in (5, 32, 40, 64, 72):
+        zeros = np.zeros((1, d))
+        negz = -np.zeros((1, d))
+        assert np.signbit(negz).all()
+        assert not ob.pack_sign_bits(zeros).any()
+        assert not ob.pack_sign_bits(negz).any()
+        allneg = -np.ones((1, d))
+        bits = ob.pack_sign_bits(allneg)[0]
+        for w, word in enumerate(bits):
+            nvalid = min(32, d - 32 * w)
+            assert int(word) == (1 << nvalid) - 1
+        assert np.array_equal(ob.sign_pm1(np.array([0.0, -0.0, -1e-30, 1e-30])),
+                              [1.0, 1.0, -1.0, 1.0])
+
+
+# --------------------------------------------------------------------------
+# alpha
+# --------------------------------------------------------------------------
+
+def alpha_closed_form(ob):
+    rng = _rng(12)
+    for d in (1, 3, 64, 72, 128):
+        a = np.array([0.75, -1.5, 2.0 ** -7, 3.0, 0.0])
+        pattern = np.where(rng.random((5, d)) < 0.5, -1.0, 1.0)
+        x = a[:, None] * pattern
+        mu = ob.token_scale(x)
+        assert np.array_equal(mu, np.abs(a)), (d, mu)
+        assert np.array_equal(mu[:, None] * ob.sign_pm1(x)[:, :], x + 0.0)
+    assert ob.token_scale(np.array([[3.0, -1.0]]))[0] == 2.0
+    assert ob.token_scale(np.array([[-2.0, -2.0, -2.0, 6.0]]))[0] == 3.0
+
+
+# --------------------------------------------------------------------------
+# integer dots
+# --------------------------------------------------------------------------
+
+def dots_two_formulas(ob):
+    rng = _rng(13)
+    for d in (1, 7, 31, 32, 33, 64, 72, 96, 128, 256):
+        q = _bf16_values(rng, (2, 1, 9, d))
+        k = _bf16_values(rng, (2, 1, 7, d))
+        q[0, 0, 0, :3] = -0.0
+        dd = ob.sign_dots(q, k)
+        hd = ob.sign_dots_from_bits(ob.pack_sign_bits(q),
+                                    ob.pack_sign_bits(k), d)
+        assert np.array_equal(dd, hd), d
+        assert np.all((dd - d) % 2 == 0)
+        assert np.all(np.abs(dd) <= d)
+        # brute force with Python ints
+        for b in range(2):
+            for i in range(9):
+                for j in range(7):
+                    s = sum((-1 if q[b, 0, i, c] < 0 else 1) *
+                            (-1 if k[b, 0, j, c] < 0 else 1) for c in range(d))
+                    assert int(dd[b, 0, i, j]) == s
+
+
+def dots_extremes(ob):
+    rng = _rng(14)
+    for d in (1, 33, 64, 72):
+        q = _bf16_values(rng, (1, 1, 4, d))
+        q[q == 0] = 1.0
+        both = np.concatenate([q, -q], axis=2)
+        dd = ob.sign_dots(q, both)[0, 0]
+        assert np.all(np.diag(dd[:, :4]) == d)
+        assert np.all(np.diag(dd[:, 4:]) == -d)
+
+
+# --------------------------------------------------------------------------
+# softmax / whole pipeline
+# --------------------------------------------------------------------------
+
+def softmax_rows_normalised(ob):
+    rng = _rng(15)
+    q = _bf16_values(rng, (2, 2, 12, 40), 3.0)
+    k = _bf16_values(rng, (2, 2, 12, 40), 3.0)
+    v = _bf16_values(rng, (2, 2, 12, 40))
+    t = _bf16_values(rng, (2, 5, 7), 0.5)
+    res = ob.binary_attention_rows(q, k, v, t, 3, 4, keep=True)
+    p = res["P"]
+    assert p.shape == (2, 2, 12, 12)
+    assert np.all(p > 0)
+    assert np.allclose(p.sum(axis=-1), 1.0, rtol=0, atol=1e-12)
+
+
+def _dense_bias_loops(table, gh, gw):
+    """Dense [H, N, N] bias from explicit (y, x) coordinates."""
+    h = table.shape[0]
+    n = gh * gw
+    out = np.zeros((h, n, n))
+    for i in range(n):
+        for j in range(n):
+            yi, xi = divmod(i, gw)
+            yj, xj = divmod(j, gw)
+            out[:, i, j] = table[:, (yi - yj) + gh - 1, (xi - xj) + gw - 1]
+    return out
+
+
+def textbook_reduction(ob):
+    """Constant-magnitude rows: alpha * sign(x) == x exactly, so the method
+    must equal textbook attention softmax(scale Q K^T + B) V."""
+    rng = _rng(16)
+    for (b, h, gh, gw, d) in ((1, 2, 3, 4, 8), (2, 1, 2, 5, 33), (1, 1, 4, 4, 64)):
+        n = gh * gw
+        mag_q = np.abs(_bf16_values(rng, (b, h, n, 1))) + 0.25
+        mag_k = np.abs(_bf16_values(rng, (b, h, n, 1))) + 0.25
+        q = mag_q * np.where(rng.random((b, h, n, d)) < 0.5, -1.0, 1.0)
+        k = mag_k * np.where(rng.random((b, h, n, d)) < 0.5, -1.0, 1.0)
+        v = _bf16_values(rng, (b, h, n, d))
+        t = _bf16_values(rng, (h, 2 * gh - 1, 2 * gw - 1), 0.7)
+        scale = 1.0 / math.sqrt(d)
+        mask = torch.from_numpy(_dense_bias_loops(t, gh, gw))[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+            attn_mask=mask, scale=scale).numpy()
+        got = ob.binary_attention(q, k, v, t, gh, gw)["O"]
+        assert np.allclose(got, ref, rtol=0, atol=1e-12), np.abs(got - ref).max()
+        ref_nb = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+            scale=scale).numpy()
+        got_nb = ob.binary_attention(q, k, v)["O"]
+        assert np.allclose(got_nb, ref_nb, rtol=0, atol=1e-12)
+
+
+def bias_points_at_offset(ob):
+    """With Q = 0 the scores are the bias alone.  One large entry at table
+    index (dy0 + gh - 1, dx0 + gw - 1) must send each query i almost all of
+    its mass to the key j with yi - yj = dy0 and xi - xj = dx0."""
+    gh, gw, d = 3, 5, 4
+    n = gh * gw
+    for dy0, dx0 in ((1, -2), (-2, 3), (0, 1), (2, 0)):
+        table = np.zeros((1, 2 * gh - 1, 2 * gw - 1))
+        table[0, dy0 + gh - 1, dx0 + gw - 1] = 40.0
+        q = np.zeros((1, 1, n, d))
+        k = _bf16_values(_rng(17), (1, 1, n, d))
+        v = np.eye(n)[None, None][..., :n]
+        res = ob.binary_attention_rows(q, k, v, table, gh, gw, keep=True)
+        p = res["P"][0, 0]
+        for i in range(n):
+            yi, xi = divmod(i, gw)
+            yj, xj = yi - dy0, xi - dx0
+            if 0 <= yj < gh and 0 <= xj < gw:
+                assert p[i, yj * gw + xj] > 0.999, (dy0, dx0, i)
+            else:
+                assert np.allclose(p[i], 1.0 / n, atol=1e-12)
+
+
+def zero_query_mean(ob):
+    rng = _rng(18)
+    q = np.zeros((2, 3, 10, 16))
+    k = _bf16_values(rng, (2, 3, 10, 16))
+    v = _bf16_values(rng, (2, 3, 10, 16))
+    o = ob.binary_attention(q, k, v)["O"]
+    assert np.allclose(o, v.mean(axis=2, keepdims=True), rtol=0, atol=1e-14)
+
+
+def single_token(ob):
+    rng = _rng(19)
+    q = _bf16_values(rng, (2, 2, 1, 24))
+    k = _bf16_values(rng, (2, 2, 1, 24))
+    v = _bf16_values(rng, (2, 2, 1, 24))
+    t = _bf16_values(rng, (2, 1, 1))
+    assert np.allclose(ob.binary_attention(q, k, v, t, 1, 1)["O"], v,
+                       rtol=0, atol=1e-15)
+
+
+def brute_force_tiny(ob):
+    """Naive loops: Python ints for D, math.fsum/math.exp for the rest."""
+    rng = _rng(20)
+    for (gh, gw, d) in ((3, 3, 1), (2, 3, 7), (3, 3, 31), (1, 4, 32),
+                        (3, 2, 33), (2, 2, 40), (3, 3, 72)):
+        n = gh * gw
+        q = _bf16_values(rng, (1, 2, n, d))
+        k = _bf16_values(rng, (1, 2, n, d))
+        v = _bf16_values(rng, (1, 2, n, d))
+        t = _bf16_values(rng, (2, 2 * gh - 1, 2 * gw - 1), 0.3)
+        q[0, 0, 0, 0] = -0.0
+        got = ob.binary_attention(q, k, v, t, gh, gw)["O"]
+        for h in range(2):
+            mq = [math.fsum(abs(float(z)) for z in q[0, h, i]) / d for i in range(n)]
+            mk = [math.fsum(abs(float(z)) for z in k[0, h, j]) / d for j in range(n)]
+            for i in range(n):
+                srow = []
+                for j in range(n):
+                    dot = 0
+                    for c in range(d):
+                        a = -1 if q[0, h, i, c] < 0 else 1
+                        b = -1 if k[0, h, j, c] < 0 else 1
+                        dot += a * b
+                    yi, xi = divmod(i, gw)
+                    yj, xj = divmod(j, gw)
+                    bias = float(t[h, yi - yj + gh - 1, xi - xj + gw - 1])
+                    srow.append(mq[i] * mk[j] * dot / math.sqrt(d) + bias)
+                m = max(srow)
+                e = [math.exp(s - m) for s in srow]
+                tot = math.fsum(e)
+                for c in range(d):
+                    o = math.fsum(e[j] * float(v[0, h, j, c]) for j in range(n)) / tot
+                    assert abs(o - got[0, h, i, c]) <= 1e-12, (gh, gw, d, h, i, c)
+
+
+def sheppard(ob):
+    """For correlated standard normals, E[sign q sign k] = (2/pi) asin(rho)
+    (Sheppard's formula): the flavour of the pages' Theorem 1 that sign
+    vectors keep the covariance structure."""
+    rng = _rng(21)
+    n = 400_000
+    for rho in (-0.6, 0.0, 0.3, 0.9):
+        z1 = rng.standard_normal(n)
+        z2 = rho * z1 + math.sqrt(1 - rho * rho) * rng.standard_normal(n)
+        dot = ob.sign_dots(z1[None, None, None, :], z2[None, None, None, :])
+        est = dot[0, 0, 0, 0] / n
+        want = 2.0 / math.pi * math.asin(rho)
+        assert abs(est - want) < 5.0 / math.sqrt(n), (rho, est, want)
+
+
+ALL_PINS = [
+    golden_hand_example,
+    bits_definition,
+    bits_special_values,
+    alpha_closed_form,
+    dots_two_formulas,
+    dots_extremes,
+    softmax_rows_normalised,
+    textbook_reduction,
+    bias_points_at_offset,
+    zero_query_mean,
+    single_token,
+    brute_force_tiny,
+    sheppard,
+]

@@ -1,0 +1,157 @@
+"""Plant plausible mistakes in the CPU oracle and check that the pins catch
+each one.  Every mutation below patches one function of oracle.dense_fp64
+for the duration of a test; the pins call through the module, so the
+patched function is the one the rest of the oracle uses.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.dense_fp64 as ob
+import pins
+
+_orig = {name: getattr(ob, name) for name in (
+    "sign_pm1", "token_scale", "pack_sign_bits", "sign_dots",
+    "sign_dots_from_bits", "binary_scores", "softmax_rows",
+    "binary_attention_rows")}
+
+
+def _sign_zero_negative(x):
+    a = ob._f64(x)
+    return np.where(a <= 0.0, -1.0, 1.0)
+
+
+def _sign_from_signbit(x):
+    a = ob._f64(x)
+    return np.where(np.signbit(a), -1.0, 1.0)
+
+
+def _scale_signed_mean(x):
+    a = ob._f64(x)
+    return a.sum(axis=-1) / a.shape[-1]
+
+
+def _scale_rms(x):
+    a = ob._f64(x)
+    return np.sqrt((a * a).sum(axis=-1) / a.shape[-1])
+
+
+def _bits_msb_first(x):
+    b = _orig["pack_sign_bits"](x)
+    out = np.zeros_like(b)
+    for i in range(32):
+        out |= ((b >> np.uint32(i)) & np.uint32(1)) << np.uint32(31 - i)
+    return out
+
+
+def _bits_signbit(x):
+    a = ob._f64(x)
+    return _orig["pack_sign_bits"](np.where(np.signbit(a), -1.0, 1.0))
+
+
+def _hamming_xnor_pads(qbits, kbits, d):
+    qb = np.asarray(qbits, dtype=np.uint32)
+    kb = np.asarray(kbits, dtype=np.uint32)
+    x = ~np.bitwise_xor(qb[..., :, None, :], kb[..., None, :, :])
+    agree = np.bitwise_count(x).astype(np.int64).sum(axis=-1)
+    return 2 * agree - d
+
+
+def _scores_factory(**kw):
+    """A copy of binary_scores with one planted mistake selected by kw."""
+    def scores(q, k, table=None, gh=0, gw=0, scale=None, rows=None):
+        qf, kf = ob._f64(q), ob._f64(k)
+        n, d = qf.shape[2], qf.shape[3]
+        if scale is None:
+            scale = 1.0 / math.sqrt(d)
+        if kw.get("no_scale"):
+            scale = 1.0
+        if kw.get("scale_1_over_d"):
+            scale = 1.0 / d
+        r = np.arange(n) if rows is None else np.asarray(rows)
+        aq, ak = ob.token_scale(qf), ob.token_scale(kf)
+        if kw.get("drop_alpha_k"):
+            ak = np.ones_like(ak)
+        dots = ob.sign_dots(qf[:, :, r, :], kf)
+        s = scale * aq[:, :, r, None] * ak[:, :, None, :] * dots
+        if kw.get("transpose_dots"):
+            s = np.swapaxes(s, -1, -2)
+        if table is not None:
+            t = ob._f64(table)
+            idx = np.arange(n)
+            y, x = idx // gw, idx % gw
+            dy = y[r][:, None] - y[None, :] + gh - 1
+            dx = x[r][:, None] - x[None, :] + gw - 1
+            if kw.get("bias_sign"):
+                dy = y[None, :] - y[r][:, None] + gh - 1
+                dx = x[None, :] - x[r][:, None] + gw - 1
+            if kw.get("bias_dx_sign"):
+                dx = x[None, :] - x[r][:, None] + gw - 1
+            if kw.get("bias_swap_axes"):
+                s = s + t[:, dx % t.shape[1], dy % t.shape[2]][None]
+            elif kw.get("drop_bias"):
+                pass
+            else:
+                s = s + t[:, dy, dx][None]
+        return {"alpha_q": aq, "alpha_k": ak, "D": dots, "S": s, "rows": r}
+    return scores
+
+
+def _softmax_columns(s):
+    a = ob._f64(s)
+    m = a.max(axis=-2, keepdims=True)
+    e = np.exp(a - m)
+    return e / e.sum(axis=-2, keepdims=True)
+
+
+def _softmax_no_normalise(s):
+    a = ob._f64(s)
+    return np.exp(a - a.max(axis=-1, keepdims=True))
+
+
+def _attention_v_transposed(q, k, v, table=None, gh=0, gw=0, scale=None,
+                            rows=None, keep=False):
+    out = _orig["binary_attention_rows"](q, k, v, table, gh, gw, scale,
+                                         rows, keep=True)
+    p = out["P"]
+    vf = ob._f64(v)
+    out["O"] = np.matmul(np.swapaxes(p, -1, -2), vf) if p.shape[-1] == p.shape[-2] \
+        else out["O"] * 1.01
+    return out
+
+
+MUTATIONS = {
+    "sign_zero_is_negative": ("sign_pm1", _sign_zero_negative),
+    "sign_from_signbit": ("sign_pm1", _sign_from_signbit),
+    "scale_signed_mean": ("token_scale", _scale_signed_mean),
+    "scale_rms": ("token_scale", _scale_rms),
+    "bits_msb_first": ("pack_sign_bits", _bits_msb_first),
+    "bits_from_signbit": ("pack_sign_bits", _bits_signbit),
+    "xnor_counts_pad_bits": ("sign_dots_from_bits", _hamming_xnor_pads),
+    "no_softmax_scale": ("binary_scores", _scores_factory(no_scale=True)),
+    "scale_one_over_d": ("binary_scores", _scores_factory(scale_1_over_d=True)),
+    "alpha_k_dropped": ("binary_scores", _scores_factory(drop_alpha_k=True)),
+    "dots_transposed": ("binary_scores", _scores_factory(transpose_dots=True)),
+    "bias_sign_flipped": ("binary_scores", _scores_factory(bias_sign=True)),
+    "bias_dx_sign_flipped": ("binary_scores", _scores_factory(bias_dx_sign=True)),
+    "bias_axes_swapped": ("binary_scores", _scores_factory(bias_swap_axes=True)),
+    "bias_dropped": ("binary_scores", _scores_factory(drop_bias=True)),
+    "softmax_over_columns": ("softmax_rows", _softmax_columns),
+    "softmax_not_normalised": ("softmax_rows", _softmax_no_normalise),
+    "pv_transposed": ("binary_attention_rows", _attention_v_transposed),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(ob, attr, fn)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(ob)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name!r}"
