@@ -1,0 +1,139 @@
+"""BinaryAttention forward on MI355X (gfx950): Python binding.
+
+The binding only marshals arguments: torch supplies device memory and the
+current HIP stream, and every step of the computation runs in the HIP
+kernels of libbinattn.so (built by ``python -m bit_qk_quantisation_amd.build``).
+If the library is missing the calls raise; there is no CPU fallback.
+
+    pack_signs(x)                          -> (bits uint32-as-int32, alpha f32)
+    attention_fwd(q, k, v, table, gh, gw)  -> O (bf16)
+    qk_int_dot(qbits, kbits, d, route)     -> D (int32)
+    workspace_bytes(B, H, N, d, gh, gw)    -> int
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from ._lib import (BinAttnError, EXPORTS, ROUTE_MFMA_FP4,  # noqa: F401
+                   ROUTE_VALU_POPCOUNT, check, load)
+
+__all__ = ["pack_signs", "attention_fwd", "qk_int_dot", "workspace_bytes",
+           "pack_words", "BinAttnError", "ROUTE_MFMA_FP4", "ROUTE_VALU_POPCOUNT",
+           "Workspace"]
+
+
+def _stream(device: torch.device):
+    return ctypes_ptr(torch.cuda.current_stream(device).cuda_stream)
+
+
+def ctypes_ptr(x):
+    return None if x in (None, 0) else int(x)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def pack_words(d: int) -> int:
+    return load().ba_pack_words(int(d))
+
+
+def workspace_bytes(B, H, N, d, gh=0, gw=0) -> int:
+    return int(load().ba_workspace_bytes(int(B), int(H), int(N), int(d), int(gh), int(gw)))
+
+
+def pack_signs(x: torch.Tensor):
+    """Packed signs and per-token scale of a bf16 [B,H,N,d] tensor.
+
+    Returns (bits int32 [B,H,N,W] holding the uint32 words, alpha f32 [B,H,N])."""
+    lib = load()
+    _need(x, "x", torch.bfloat16, 4)
+    B, H, N, d = x.shape
+    W = lib.ba_pack_words(d)
+    bits = torch.empty((B, H, N, max(W, 1)), dtype=torch.int32, device=x.device)
+    alpha = torch.empty((B, H, N), dtype=torch.float32, device=x.device)
+    check(lib, lib.ba_pack_signs(x.data_ptr(), B, H, N, d, bits.data_ptr(),
+                                 alpha.data_ptr(), _stream(x.device)))
+    return bits, alpha
+
+
+class Workspace:
+    """A reusable device workspace, grown on demand (one per device)."""
+
+    def __init__(self):
+        self._buf = {}
+
+    def get(self, device: torch.device, nbytes: int) -> torch.Tensor:
+        buf = self._buf.get(device)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(max(nbytes, 256) + 256, dtype=torch.uint8, device=device)
+            self._buf[device] = buf
+        return buf
+
+
+_default_ws = Workspace()
+
+
+def attention_fwd(q, k, v, table=None, gh: int = 0, gw: int = 0, scale=None,
+                  out=None, workspace: Workspace | None = None):
+    """BinaryAttention forward: bf16 q, k, v [B,H,N,d] (+ bf16 table
+    [H, 2gh-1, 2gw-1]) -> bf16 O [B,H,N,d]."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    if q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k and v must have the same shape")
+    B, H, N, d = q.shape
+    if table is not None:
+        _need(table, "table", torch.bfloat16, 3)
+        if tuple(table.shape) != (H, 2 * gh - 1, 2 * gw - 1):
+            raise ValueError(f"table must be [H, 2gh-1, 2gw-1] = {(H, 2*gh-1, 2*gw-1)}")
+    else:
+        gh = gw = 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 4)
+    nbytes = lib.ba_workspace_bytes(B, H, N, d, gh, gw)
+    if nbytes == 0:
+        raise BinAttnError(2, f"unsupported problem B={B} H={H} N={N} d={d} grid={gh}x{gw}")
+    ws = (workspace or _default_ws).get(q.device, nbytes)
+    base = ws.data_ptr()
+    aligned = (base + 255) // 256 * 256
+    check(lib, lib.ba_attention_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(),
+        None if table is None else table.data_ptr(), int(gh), int(gw),
+        B, H, N, d, float(scale), out.data_ptr(), aligned,
+        ws.numel() - (aligned - base), _stream(q.device)))
+    return out
+
+
+def qk_int_dot(qbits, kbits, d: int, route: int = ROUTE_MFMA_FP4):
+    """All-pairs integer dots <sign q_i, sign k_j> from packed bits."""
+    lib = load()
+    _need(qbits, "qbits", torch.int32, 4)
+    _need(kbits, "kbits", torch.int32, 4)
+    if qbits.shape != kbits.shape:
+        raise ValueError("qbits and kbits must have the same shape")
+    B, H, N, W = qbits.shape
+    if W != lib.ba_pack_words(d):
+        raise ValueError("word count does not match d")
+    dots = torch.empty((B, H, N, N), dtype=torch.int32, device=qbits.device)
+    check(lib, lib.ba_qk_int_dot(qbits.data_ptr(), kbits.data_ptr(), B, H, N, int(d),
+                                 int(route), dots.data_ptr(), _stream(qbits.device)))
+    return dots

@@ -1,0 +1,67 @@
+"""ctypes view of libbinattn.so: declarations only, no compute."""
+
+from __future__ import annotations
+
+import ctypes
+import pathlib
+
+LIB_PATH = pathlib.Path(__file__).resolve().parent / "libbinattn.so"
+
+# Every symbol that include/binattn.h declares.
+EXPORTS = (
+    "ba_version", "ba_status_string", "ba_last_error", "ba_pack_words",
+    "ba_pack_signs", "ba_workspace_bytes", "ba_attention_fwd", "ba_qk_int_dot",
+)
+
+STATUS = {0: "BA_OK", 1: "BA_ERR_NULL", 2: "BA_ERR_SHAPE", 3: "BA_ERR_UNSUPPORTED",
+          4: "BA_ERR_ALIGN", 5: "BA_ERR_WORKSPACE", 6: "BA_ERR_HIP"}
+
+ROUTE_MFMA_FP4 = 0
+ROUTE_VALU_POPCOUNT = 1
+
+_lib = None
+
+
+class BinAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def load(path=None) -> ctypes.CDLL:
+    """Load (once) and declare the C ABI.  Raises if the library is missing:
+    there is no fallback path."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = pathlib.Path(path) if path else LIB_PATH
+    if not p.exists():
+        raise ImportError(
+            f"{p} is missing: build it with `python -m bit_qk_quantisation_amd.build`")
+    lib = ctypes.CDLL(str(p))
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    lib.ba_version.restype = i32
+    lib.ba_version.argtypes = []
+    lib.ba_status_string.restype = ctypes.c_char_p
+    lib.ba_status_string.argtypes = [i32]
+    lib.ba_last_error.restype = ctypes.c_char_p
+    lib.ba_last_error.argtypes = []
+    lib.ba_pack_words.restype = i32
+    lib.ba_pack_words.argtypes = [i32]
+    lib.ba_pack_signs.restype = i32
+    lib.ba_pack_signs.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp]
+    lib.ba_workspace_bytes.restype = sz
+    lib.ba_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.ba_attention_fwd.restype = i32
+    lib.ba_attention_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32,
+                                     ctypes.c_float, vp, vp, sz, vp]
+    lib.ba_qk_int_dot.restype = i32
+    lib.ba_qk_int_dot.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp, vp]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def check(lib: ctypes.CDLL, status: int) -> None:
+    if status != 0:
+        raise BinAttnError(status, lib.ba_last_error().decode(errors="replace"))

@@ -1,0 +1,60 @@
+"""Build libbinattn.so (the HIP kernels and the C ABI) for gfx950, in tree.
+
+    python -m bit_qk_quantisation_amd.build
+
+hipcc compiles every csrc/*.hip file into one shared library next to this
+file.  Packed fp32 VALU forms are disabled for all device code.
+"""
+
+from __future__ import annotations
+
+import os
+import pathlib
+import shutil
+import subprocess
+import sys
+
+PKG = pathlib.Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+INCLUDE = ROOT / "include"
+LIB = PKG / "libbinattn.so"
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libbinattn.so)")
+
+
+def sources():
+    return sorted(str(p) for p in CSRC.glob("*.hip"))
+
+
+def build(verbose: bool = False, extra=()) -> pathlib.Path:
+    """Compile every kernel and the host layer into LIB; returns its path."""
+    tmp = LIB.with_name(LIB.name + f".tmp{os.getpid()}")
+    cmd = [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-unused-command-line-argument",
+        f"-I{INCLUDE}", f"-I{CSRC}",
+        *extra, *sources(), "-o", str(tmp),
+    ]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

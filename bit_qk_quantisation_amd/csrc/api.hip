@@ -1,0 +1,262 @@
+// Host side of libbinattn.so: argument validation, workspace layout, kernel
+// selection and launches.  See include/binattn.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "ba_internal.h"
+#include "binattn.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ba_status fail(ba_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+constexpr int64_t kMaxTokens = (int64_t{1} << 31) - 1;
+
+ba_status check_dims(int64_t B, int64_t H, int64_t N, int d) {
+  if (B < 1 || H < 1 || N < 1) return fail(BA_ERR_SHAPE, "B, H and N must be >= 1 (got %lld, %lld, %lld)",
+                                           (long long)B, (long long)H, (long long)N);
+  if (d < 8 || d > 256 || d % 8 != 0)
+    return fail(BA_ERR_UNSUPPORTED, "head dim d=%d unsupported (need 8 <= d <= 256, d %% 8 == 0)", d);
+  if (B > kMaxTokens / H || B * H > kMaxTokens / round_up(N, ba::kNAlign))
+    return fail(BA_ERR_SHAPE, "B*H*N too large (must stay below 2^31 tokens)");
+  return BA_OK;
+}
+
+// Byte offsets of the workspace sections of ba_attention_fwd.
+struct Layout {
+  int64_t Npad, W, dpad, Lpad;
+  int64_t qbits, kbits, alpha_q, alpha_k, vt, bias4, total;
+  int mode;
+};
+
+int bias_mode(const void* bias, int gw) {
+  if (bias == nullptr) return ba::kBiasNone;
+  return (gw % 32 == 0) ? ba::kBiasRows : ba::kBiasTable;
+}
+
+Layout layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int gw) {
+  Layout L{};
+  L.Npad = round_up(N, ba::kNAlign);
+  L.W = (d + 31) / 32;
+  L.dpad = 32 * ((d + 31) / 32);
+  L.mode = has_bias ? ((gw % 32 == 0) ? ba::kBiasRows : ba::kBiasTable) : ba::kBiasNone;
+  L.Lpad = (L.mode == ba::kBiasRows) ? round_up(2 * gw - 1 + 3, 4) : 0;
+  const int64_t BH = B * H;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  L.qbits = take(BH * L.Npad * L.W * 4);
+  L.kbits = take(BH * L.Npad * L.W * 4);
+  L.alpha_q = take(BH * L.Npad * 4);
+  L.alpha_k = take(BH * L.Npad * 4);
+  L.vt = take(BH * L.dpad * L.Npad * 2);
+  L.bias4 = take(L.mode == ba::kBiasRows ? H * (2 * gh - 1) * 4 * L.Lpad * 4 : 0);
+  L.total = off;
+  return L;
+}
+
+// Largest number of bias-table rows one (query tile, key tile) pair needs.
+int window_rows(int64_t N, int gw) {
+  int best = 1;
+  const int64_t nqt = round_up(N, ba::kNAlign) / ba::kBM;
+  const int64_t nkt = (N + ba::kBN - 1) / ba::kBN;
+  int qspan = 0, kspan = 0;
+  for (int64_t t = 0; t < nqt; ++t) {
+    const int64_t q0 = t * ba::kBM;
+    const int s = static_cast<int>((q0 + ba::kBM - 1) / gw - q0 / gw);
+    if (s > qspan) qspan = s;
+  }
+  for (int64_t t = 0; t < nkt; ++t) {
+    const int64_t k0 = t * ba::kBN;
+    const int s = static_cast<int>((k0 + ba::kBN - 1) / gw - k0 / gw);
+    if (s > kspan) kspan = s;
+  }
+  best = qspan + kspan + 1;
+  return best;
+}
+
+ba_status hip_fail(int err, const char* what) {
+  return fail(BA_ERR_HIP, "%s: %s", what, hipGetErrorString(static_cast<hipError_t>(err)));
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Max LDS bytes a workgroup may use on gfx950.
+constexpr int kMaxLds = 160 * 1024;
+
+}  // namespace
+
+extern "C" {
+
+int ba_version(void) { return BA_VERSION; }
+
+const char* ba_status_string(ba_status s) {
+  switch (s) {
+    case BA_OK: return "BA_OK";
+    case BA_ERR_NULL: return "BA_ERR_NULL";
+    case BA_ERR_SHAPE: return "BA_ERR_SHAPE";
+    case BA_ERR_UNSUPPORTED: return "BA_ERR_UNSUPPORTED";
+    case BA_ERR_ALIGN: return "BA_ERR_ALIGN";
+    case BA_ERR_WORKSPACE: return "BA_ERR_WORKSPACE";
+    case BA_ERR_HIP: return "BA_ERR_HIP";
+  }
+  return "BA_ERR_UNKNOWN";
+}
+
+const char* ba_last_error(void) { return g_err; }
+
+int ba_pack_words(int d) { return d < 1 ? 0 : (d + 31) / 32; }
+
+ba_status ba_pack_signs(const void* x, int64_t B, int64_t H, int64_t N, int d,
+                        uint32_t* bits, float* alpha, void* stream) {
+  if (!x || !bits || !alpha) return fail(BA_ERR_NULL, "x, bits and alpha must be non-NULL");
+  ba_status st = check_dims(B, H, N, d);
+  if (st != BA_OK) return st;
+  if (!aligned16(x) || !aligned16(bits) || !aligned16(alpha))
+    return fail(BA_ERR_ALIGN, "x, bits and alpha must be 16-byte aligned");
+  ba::PrologueArgs p{};
+  p.pack[0] = ba::PackJob{static_cast<const uint16_t*>(x), bits, alpha, B * H,
+                          static_cast<int>(N), static_cast<int>(N), d, (d + 31) / 32};
+  p.npack = 1;
+  p.pack_blocks = (B * H * N + 63) / 64;
+  if (p.pack_blocks > 0x7fffffff) return fail(BA_ERR_SHAPE, "problem too large");
+  const int err = ba::launch_prologue(p, stream);
+  if (err != 0) return hip_fail(err, "pack launch");
+  return BA_OK;
+}
+
+size_t ba_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int gh, int gw) {
+  if (check_dims(B, H, N, d) != BA_OK) return 0;
+  const bool has_bias = gh > 0 || gw > 0;
+  if (has_bias && (gh < 1 || gw < 1 || static_cast<int64_t>(gh) * gw != N)) return 0;
+  return static_cast<size_t>(layout(B, H, N, d, has_bias, gh, gw).total);
+}
+
+ba_status ba_attention_fwd(const void* q, const void* k, const void* v,
+                           const void* bias, int gh, int gw,
+                           int64_t B, int64_t H, int64_t N, int d, float scale,
+                           void* o, void* workspace, size_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !o) return fail(BA_ERR_NULL, "q, k, v and o must be non-NULL");
+  ba_status st = check_dims(B, H, N, d);
+  if (st != BA_OK) return st;
+  if (!std::isfinite(scale) || scale < 0.0f) return fail(BA_ERR_SHAPE, "scale must be finite and >= 0");
+  if (bias) {
+    if (gh < 1 || gw < 1 || static_cast<int64_t>(gh) * gw != N)
+      return fail(BA_ERR_SHAPE, "with a bias table gh*gw must equal N (gh=%d gw=%d N=%lld)", gh, gw,
+                  (long long)N);
+  }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (bias && !aligned16(bias)))
+    return fail(BA_ERR_ALIGN, "q, k, v, o and bias must be 16-byte aligned");
+  const size_t tensor_bytes = static_cast<size_t>(B * H * N * d) * 2;
+  if (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(o, tensor_bytes, k, tensor_bytes) ||
+      overlaps(o, tensor_bytes, v, tensor_bytes))
+    return fail(BA_ERR_SHAPE, "o must not overlap q, k or v");
+  const int mode = bias_mode(bias, gw);
+  if (mode == ba::kBiasTable && static_cast<int64_t>(2 * gh - 1) * (2 * gw - 1) * 4 > 48 * 1024)
+    return fail(BA_ERR_UNSUPPORTED,
+                "bias grid %dx%d: gw not a multiple of 32 and the table exceeds 48 KiB of LDS", gh, gw);
+  const Layout L = layout(B, H, N, d, bias != nullptr, gh, gw);
+  if (!workspace) return fail(BA_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(BA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (ws_bytes < static_cast<size_t>(L.total))
+    return fail(BA_ERR_WORKSPACE, "workspace too small: %zu < %lld bytes", ws_bytes, (long long)L.total);
+  if (overlaps(workspace, L.total, o, tensor_bytes))
+    return fail(BA_ERR_WORKSPACE, "workspace must not overlap o");
+
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  const int64_t BH = B * H;
+  ba::FwdArgs f{};
+  f.qbits = reinterpret_cast<const uint32_t*>(ws + L.qbits);
+  f.kbits = reinterpret_cast<const uint32_t*>(ws + L.kbits);
+  f.alpha_q = reinterpret_cast<const float*>(ws + L.alpha_q);
+  f.alpha_k = reinterpret_cast<const float*>(ws + L.alpha_k);
+  f.vt = reinterpret_cast<const uint16_t*>(ws + L.vt);
+  f.bias4 = reinterpret_cast<const float*>(ws + L.bias4);
+  f.table = static_cast<const uint16_t*>(bias);
+  f.o = static_cast<uint16_t*>(o);
+  f.H = static_cast<int>(H);
+  f.N = static_cast<int>(N);
+  f.Npad = static_cast<int>(L.Npad);
+  f.d = d;
+  f.W = static_cast<int>(L.W);
+  f.dpad = static_cast<int>(L.dpad);
+  f.gh = gh;
+  f.gw = gw;
+  f.Lpad = static_cast<int>(L.Lpad);
+  f.win_rows = (mode == ba::kBiasRows) ? window_rows(N, gw) : 0;
+  f.qscale = scale * ba::kLog2e;
+  f.nqt = static_cast<int>(L.Npad / ba::kBM);
+  const int64_t nwg = BH * f.nqt;
+  if (nwg > 0x7fffffff) return fail(BA_ERR_SHAPE, "too many workgroups");
+  f.nwg = static_cast<int>(nwg);
+  f.xcd_remap = (f.nwg % 8 == 0) ? 1 : 0;
+  // static LDS of the fused kernel: fp4 key operands, key scales and grid
+  // offsets, and the V^T tile.
+  const int nch = (d + 63) / 64;
+  const int static_lds = nch * ba::kBN * 2 * 16 + 2 * ba::kBN * 4 + f.dpad * ba::kVtStride * 2;
+  if (static_lds + ba::fwd_dynamic_lds(f, mode) > kMaxLds)
+    return fail(BA_ERR_UNSUPPORTED, "bias window does not fit in LDS");
+
+  ba::PrologueArgs p{};
+  p.pack[0] = ba::PackJob{static_cast<const uint16_t*>(q), const_cast<uint32_t*>(f.qbits),
+                          const_cast<float*>(f.alpha_q), BH, f.N, f.Npad, d, f.W};
+  p.pack[1] = ba::PackJob{static_cast<const uint16_t*>(k), const_cast<uint32_t*>(f.kbits),
+                          const_cast<float*>(f.alpha_k), BH, f.N, f.Npad, d, f.W};
+  p.npack = 2;
+  p.pack_blocks = (BH * L.Npad + 63) / 64;
+  p.vt = ba::VtJob{static_cast<const uint16_t*>(v), const_cast<uint16_t*>(f.vt), BH, f.N, f.Npad, d, f.dpad};
+  p.vt_blocks = BH * (L.Npad / 64);
+  if (mode == ba::kBiasRows) {
+    p.bias = ba::BiasJob{static_cast<const uint16_t*>(bias), const_cast<float*>(f.bias4), gh, gw, f.Lpad};
+    p.bias_blocks = H * (2 * gh - 1);
+  }
+  const int64_t pblocks = 2 * p.pack_blocks + p.vt_blocks + p.bias_blocks;
+  if (pblocks > 0x7fffffff) return fail(BA_ERR_SHAPE, "problem too large");
+  int err = ba::launch_prologue(p, stream);
+  if (err != 0) return hip_fail(err, "prologue launch");
+  err = ba::launch_attention(f, mode, stream);
+  if (err != 0) return hip_fail(err, "attention launch");
+  return BA_OK;
+}
+
+ba_status ba_qk_int_dot(const uint32_t* qbits, const uint32_t* kbits, int64_t B, int64_t H, int64_t N,
+                        int d, int route, int32_t* dots, void* stream) {
+  if (!qbits || !kbits || !dots) return fail(BA_ERR_NULL, "qbits, kbits and dots must be non-NULL");
+  ba_status st = check_dims(B, H, N, d);
+  if (st != BA_OK) return st;
+  if (route != BA_ROUTE_MFMA_FP4 && route != BA_ROUTE_VALU_POPCOUNT)
+    return fail(BA_ERR_UNSUPPORTED, "unknown route %d", route);
+  if (N > 65535 || B * H > 65535) return fail(BA_ERR_SHAPE, "qk_int_dot needs N <= 65535 and B*H <= 65535");
+  if (B * H * N > (int64_t{1} << 40) / N) return fail(BA_ERR_SHAPE, "B*H*N*N exceeds 2^40");
+  if (!aligned16(qbits) || !aligned16(kbits) || !aligned16(dots))
+    return fail(BA_ERR_ALIGN, "qbits, kbits and dots must be 16-byte aligned");
+  ba::DotArgs a{qbits, kbits, dots, B * H, static_cast<int>(N), d, (d + 31) / 32};
+  const int err = ba::launch_qk_dot(a, route, stream);
+  if (err != 0) return hip_fail(err, "qk_int_dot launch");
+  return BA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// Device-side building blocks for the gfx950 BinaryAttention kernels.
+//
+// Everything here is shared by the fused forward kernel and the QK
+// integer-dot kernel, so the "integer dots" that the checker sees are
+// computed by the very code the fused kernel runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ba {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Sign bit of the scaled binary representation: 1 iff x < 0 (an IEEE
+// compare, so +0.0 and -0.0 both give 0, i.e. sign +1).  The sign function
+// of s_i = mu_q sign(q_i) ("Representaciones Binarias Escaladas").
+__device__ __forceinline__ uint32_t neg_bit(float x) { return x < 0.0f ? 1u : 0u; }
+
+// --------------------------------------------------------------------------
+// +/-1 operands in fp4 (e2m1) for the scaled f8f6f4 MFMA.
+//
+// In e2m1, +1.0 = 0b0010, -1.0 = 0b1010 and 0 = 0b0000.  A product of two
+// +/-1 values is exact and the MFMA accumulates in fp32, so the result is the
+// exact integer <sign q, sign k> = d - 2 popcount(q XOR k) (|D| <= 256).
+//
+// One 32-bit sign word (32 channels) fills the four operand dwords of one
+// MFMA lane: dword k, nibble n holds the channel of bit 4n+k.  Every operand
+// (query and key side alike) uses this same channel-to-slot map, and the
+// contraction runs over all slots, so the slot order cancels out.  Channels
+// past d carry sign bit 0 and get magnitude 0, so they contribute nothing.
+// --------------------------------------------------------------------------
+
+// Magnitude nibbles (0x2) for the valid channels of a word with `nvalid`
+// channels (0, 8, 16, 24 or 32: d is a multiple of 8).  Bit 4n+k is valid iff
+// 4n+k < nvalid, i.e. n < nvalid/4 for every k.
+__device__ __forceinline__ uint32_t fp4_magnitude(int nvalid) {
+  if (nvalid >= 32) return 0x22222222u;
+  if (nvalid <= 0) return 0u;
+  return 0x22222222u & ((1u << nvalid) - 1u);
+}
+
+// Valid channels of word `w` for head dim d.
+__device__ __forceinline__ int word_valid(int d, int w) {
+  int v = d - 32 * w;
+  return v < 0 ? 0 : (v > 32 ? 32 : v);
+}
+
+__device__ __forceinline__ v4i expand_signs_fp4(uint32_t w, uint32_t mag) {
+  v4i r;
+  r[0] = static_cast<int>(((w << 3) & 0x88888888u) | mag);
+  r[1] = static_cast<int>(((w << 2) & 0x88888888u) | mag);
+  r[2] = static_cast<int>(((w << 1) & 0x88888888u) | mag);
+  r[3] = static_cast<int>((w & 0x88888888u) | mag);
+  return r;
+}
+
+// 32x32 block of sign dots over 64 channels: rows from `a` (lane = row % 32,
+// channel group = lane / 32), columns from `b` (same map), accumulated into
+// acc.  Output layout (CDNA 32x32 accumulator): lane l holds column l % 32
+// and, in register r, row 8*(r/4) + 4*(l/32) + r%4.  The E8M0 scales are
+// 127, i.e. 1.0.
+__device__ __forceinline__ v16f mfma_signs_32x32x64(v4i a, v4i b, v16f acc) {
+  v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc, 4, 4, 0, 127, 0, 127);
+}
+
+// bf16 32x32x16: lane l supplies row (A) / column (B) l % 32 and the eight
+// k-slots 8*(l/32) .. 8*(l/32)+7.
+__device__ __forceinline__ v16f mfma_bf16_32x32x16(v8bf a, v8bf b, v16f acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+
+// Cross-half reductions for the 32x32 layout: lanes l and l^32 hold the two
+// halves of one query's keys.  v_permlane32_swap of x with itself leaves
+// (lower, lower) in r[0] and (upper, upper) in r[1], so r[0] op r[1] is the
+// same value in both lanes of the pair.
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  v2f f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2bf));
+}
+
+// acc + lo + hi of a packed bf16 pair (v_dot2 with (1, 1)).
+__device__ __forceinline__ float add_bf16x2(uint32_t pair, float acc) {
+  const v2bf one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, pair), one, acc, false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// MFMA results must be formed while every lane of the wave is active: a
+// matrix instruction mixes data across lanes, and one issued under a partial
+// EXEC mask drops the inactive lanes' rows.  LLVM treats the MFMA intrinsics
+// as speculatable, so it may sink one below a divergent branch when its
+// result is only used inside that branch.  Passing the result through an
+// empty volatile asm in uniform control flow pins the MFMA above it.
+__device__ __forceinline__ void pin_uniform(v16f& x) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float e = x[i];
+    asm volatile("" : "+v"(e));
+    x[i] = e;
+  }
+}
+
+}  // namespace ba

@@ -1,0 +1,92 @@
+// Internal declarations shared by the host layer and the kernels.
+#pragma once
+
+#include <stdint.h>
+
+#include "ba_device.h"
+
+namespace ba {
+
+// Tile sizes of the fused kernel: 4 waves x 32 queries, 64 keys per step.
+constexpr int kBM = 128;
+constexpr int kBN = 64;
+constexpr int kThreads = 256;
+// N is padded per head to a multiple of this in every workspace array.
+constexpr int kNAlign = 128;
+// V^T rows in LDS: 64 keys + 8 bf16 of padding (144 bytes, 16-byte aligned,
+// spreads rows over the LDS banks).
+constexpr int kVtStride = 72;
+
+// Largest LDS footprint of a prologue block (vt tile at d = 256).
+constexpr int kPrologueSmem = 64 * (256 + 8) * 2;
+
+struct PackJob {
+  const uint16_t* x;  // bf16 [BH][N][d]
+  uint32_t* bits;     // [BH][Npad][W]
+  float* alpha;       // [BH][Npad]
+  int64_t BH;
+  int N, Npad, d, W;
+};
+
+struct VtJob {
+  const uint16_t* v;  // bf16 [BH][N][d]
+  uint16_t* vt;       // bf16 [BH][dpad][Npad], keys in P.V slot order
+  int64_t BH;
+  int N, Npad, d, dpad;
+};
+
+struct BiasJob {
+  const uint16_t* table;  // bf16 [H][2gh-1][2gw-1]
+  float* bias4;           // [H][2gh-1][4][Lpad]
+  int gh, gw, Lpad;
+};
+
+struct PrologueArgs {
+  PackJob pack[2];
+  int npack;
+  int64_t pack_blocks;  // per pack job
+  VtJob vt;
+  int64_t vt_blocks;
+  BiasJob bias;
+  int64_t bias_blocks;
+};
+
+int launch_prologue(const PrologueArgs& a, void* stream);
+
+enum BiasMode { kBiasNone = 0, kBiasRows = 1, kBiasTable = 2 };
+
+struct FwdArgs {
+  const uint32_t* qbits;   // [BH][Npad][W]
+  const uint32_t* kbits;   // [BH][Npad][W]
+  const float* alpha_q;    // [BH][Npad]
+  const float* alpha_k;    // [BH][Npad]
+  const uint16_t* vt;      // [BH][dpad][Npad]
+  const float* bias4;      // kBiasRows: [H][2gh-1][4][Lpad]
+  const uint16_t* table;   // kBiasTable: bf16 [H][2gh-1][2gw-1]
+  uint16_t* o;             // bf16 [BH][N][d]
+  int H, N, Npad, d, W, dpad;
+  int gh, gw, Lpad;
+  int win_rows;            // kBiasRows: rows of the per-tile bias window
+  float qscale;            // softmax scale * log2(e)
+  int nqt;                 // query tiles per head
+  int nwg;                 // workgroups
+  int xcd_remap;           // 1: spread consecutive heads over the 8 XCDs
+};
+
+// Dynamic LDS bytes of the fused kernel for these arguments.
+int fwd_dynamic_lds(const FwdArgs& a, int mode);
+
+// Launch the fused kernel (template selected from d and the bias mode).
+int launch_attention(const FwdArgs& a, int mode, void* stream);
+
+struct DotArgs {
+  const uint32_t* qbits;  // [BH][N][W]
+  const uint32_t* kbits;  // [BH][N][W]
+  int32_t* dots;          // [BH][N][N]
+  int64_t BH;
+  int N, d, W;
+};
+
+int launch_qk_dot(const DotArgs& a, int route, void* stream);
+
+}  // namespace ba

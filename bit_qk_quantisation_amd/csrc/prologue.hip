@@ -1,0 +1,177 @@
+// Prologue kernel of the BinaryAttention forward, plus the standalone sign
+// pack.
+//
+// One launch does three independent jobs, split by block index:
+//   * pack: per token, the scale alpha = mean |x| over d and the packed sign
+//     words (s_i = mu sign(q_i), "Representaciones Binarias Escaladas" of
+//     the BinaryAttention summary).  It covers Q and K, or a single tensor
+//     for ba_pack_signs.
+//   * vt: a key-major copy of V (V^T, bf16 [BH][dpad][Npad]) whose keys are
+//     permuted inside each group of 16 to match the P.V operand order of the
+//     fused kernel.
+//   * bias rows: the relative-position table ("Mejora mediante Sesgo") as
+//     float32 * log2(e), with the dx axis reversed, in four copies shifted
+//     by 0..3 entries, so that any 4 consecutive entries can be read with
+//     one aligned 16-byte LDS load.
+// All three are bound by HBM traffic.  Loads are 16-byte and coalesced.
+#include "ba_internal.h"
+
+namespace ba {
+
+// ---------------------------------------------------------------- pack ----
+// One block = 64 tokens.  Each thread takes 8-channel chunks (16 bytes), so
+// consecutive threads read consecutive 16-byte pieces of the rows.  Sign
+// bytes and partial |x| sums meet in LDS, then words and scales are written.
+constexpr int kPackTok = 64;
+
+__device__ void pack_block(const PackJob& job, int64_t blk, unsigned char* smem) {
+  const int d = job.d, W = job.W, C = d / 8;
+  const int64_t T = job.BH * static_cast<int64_t>(job.Npad);
+  const int64_t t0 = blk * kPackTok;
+  uint32_t* sw = reinterpret_cast<uint32_t*>(smem);            // [64][W] words
+  float* sp = reinterpret_cast<float*>(smem + kPackTok * 8 * 4);  // [64][33]
+
+  for (int e = threadIdx.x; e < kPackTok * W; e += blockDim.x) sw[e] = 0u;
+  __syncthreads();
+
+  unsigned char* sb = reinterpret_cast<unsigned char*>(sw);
+  for (int g = threadIdx.x; g < kPackTok * C; g += blockDim.x) {
+    const int tok = g / C, ch = g - tok * C;
+    const int64_t t = t0 + tok;
+    uint32_t byte = 0;
+    float part = 0.0f;
+    if (t < T) {
+      const int64_t bh = t / job.Npad;
+      const int n = static_cast<int>(t - bh * job.Npad);
+      if (n < job.N) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(
+            job.x + ((bh * job.N + n) * d + ch * 8));
+        const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+        float a[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float lo = bf16_to_f32(static_cast<uint16_t>(wv[k] & 0xffffu));
+          const float hi = bf16_to_f32(static_cast<uint16_t>(wv[k] >> 16));
+          byte |= neg_bit(lo) << (2 * k);
+          byte |= neg_bit(hi) << (2 * k + 1);
+          a[2 * k] = fabsf(lo);
+          a[2 * k + 1] = fabsf(hi);
+        }
+        part = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+      }
+    }
+    // channel 8*ch + b -> word ch/4, bit 8*(ch%4) + b: byte ch of the
+    // token's little-endian word array.
+    sb[tok * 4 * W + ch] = static_cast<unsigned char>(byte);
+    sp[tok * 33 + ch] = part;
+  }
+  __syncthreads();
+
+  for (int e = threadIdx.x; e < kPackTok * W; e += blockDim.x) {
+    const int tok = e / W;
+    const int64_t t = t0 + tok;
+    if (t < T) job.bits[t * W + (e - tok * W)] = sw[e];
+  }
+  if (threadIdx.x < kPackTok) {
+    const int tok = threadIdx.x;
+    const int64_t t = t0 + tok;
+    if (t < T) {
+      float* v = sp + tok * 33;
+      // pairwise sum in a fixed order: error <= ceil(log2 d) ulps-ish
+      for (int s = 1; s < C; s *= 2)
+        for (int i = 0; i + s < C; i += 2 * s) v[i] += v[i + s];
+      const int64_t bh = t / job.Npad;
+      const int n = static_cast<int>(t - bh * job.Npad);
+      job.alpha[t] = (n < job.N) ? v[0] / static_cast<float>(d) : 0.0f;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ vt ----
+// One block = one (b,h) and 64 keys.  Loads the 64 x d tile row-major into
+// LDS, then writes dpad rows of 64 keys in P.V slot order (zeros past N and
+// past d).
+__device__ __forceinline__ int vt_slot_key(int slot) {
+  // slot (0..63) -> key offset in the 64-key tile.  Within a 16-group, slots
+  // 8h..8h+3 are keys 4h..4h+3 and slots 8h+4..8h+7 are keys 8+4h..8+4h+3.
+  const int g = slot >> 4, s16 = slot & 15, hh = s16 >> 3, s = s16 & 7;
+  return g * 16 + (s < 4 ? 4 * hh + s : 8 + 4 * hh + (s - 4));
+}
+
+__device__ void vt_block(const VtJob& job, int64_t blk, unsigned char* smem) {
+  const int d = job.d, C = d / 8, stride = d + 8;  // bf16 units
+  const int tiles = job.Npad / 64;
+  const int64_t bh = blk / tiles;
+  const int n0 = static_cast<int>(blk - bh * tiles) * 64;
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);  // [64][d+8]
+
+  for (int g = threadIdx.x; g < 64 * C; g += blockDim.x) {
+    const int key = g / C, ch = g - key * C;
+    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+    if (n0 + key < job.N)
+      raw = *reinterpret_cast<const uint4*>(job.v + ((bh * job.N + n0 + key) * d + ch * 8));
+    *reinterpret_cast<uint4*>(tile + key * stride + ch * 8) = raw;
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < job.dpad * 8; g += blockDim.x) {
+    const int c = g >> 3, q = g & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t lo = 0, hi = 0;
+      if (c < d) {
+        lo = tile[vt_slot_key(8 * q + 2 * k) * stride + c];
+        hi = tile[vt_slot_key(8 * q + 2 * k + 1) * stride + c];
+      }
+      w[k] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint4*>(job.vt + ((bh * job.dpad + c) * static_cast<int64_t>(job.Npad) + n0 + 8 * q)) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// ---------------------------------------------------------------- bias ----
+// One block = one (h, dy) table row -> 4 shifted copies of Lpad floats.
+// R[u] = log2e * T[h, dy, 2gw-2-u] for 0 <= u <= 2gw-2 (else 0), and copy s
+// holds C_s[v] = R[v+s].
+__device__ void bias_block(const BiasJob& job, int64_t blk) {
+  const int rows = 2 * job.gh - 1, cols = 2 * job.gw - 1;
+  const int64_t h = blk / rows;
+  const int dy = static_cast<int>(blk - h * rows);
+  const uint16_t* trow = job.table + (h * rows + dy) * cols;
+  float* out = job.bias4 + (h * rows + dy) * 4 * static_cast<int64_t>(job.Lpad);
+  for (int e = threadIdx.x; e < 4 * job.Lpad; e += blockDim.x) {
+    const int s = e / job.Lpad, v = e - s * job.Lpad;
+    const int u = v + s;
+    float val = 0.0f;
+    if (u <= cols - 1) val = kLog2e * bf16_to_f32(trow[cols - 1 - u]);
+    out[e] = val;
+  }
+}
+
+__global__ void __launch_bounds__(256) prologue_kernel(PrologueArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kPrologueSmem];
+  int64_t blk = blockIdx.x;
+  for (int t = 0; t < a.npack; ++t) {
+    if (blk < a.pack_blocks) {
+      pack_block(a.pack[t], blk, smem);
+      return;
+    }
+    blk -= a.pack_blocks;
+  }
+  if (blk < a.vt_blocks) {
+    vt_block(a.vt, blk, smem);
+    return;
+  }
+  blk -= a.vt_blocks;
+  if (blk < a.bias_blocks) bias_block(a.bias, blk);
+}
+
+int launch_prologue(const PrologueArgs& a, void* stream) {
+  const int64_t blocks = a.npack * a.pack_blocks + a.vt_blocks + a.bias_blocks;
+  hipLaunchKernelGGL(prologue_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace ba

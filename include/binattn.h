@@ -1,0 +1,152 @@
+/*
+ * binattn.h -- C ABI of the MI355X (gfx950) BinaryAttention forward library
+ * (libbinattn.so).
+ *
+ * The method is the one described by the gist.science summaries of
+ * "BinaryAttention: One-Bit QK-Attention for Vision and Diffusion
+ * Transformers".  Queries and keys are reduced to a per-token scale times a
+ * sign ("Representaciones Binarias Escaladas", technical summary section 2):
+ * s_i = mu_q sign(q_i), t_j = mu_k sign(k_j).  Their similarity is an
+ * XNOR/popcount count of sign agreements.  A learnable position-sensitive bias
+ * b_ij is added ("Mejora mediante Sesgo").  Softmax and the product with V
+ * follow inside one tiled kernel in the FlashAttention2 manner
+ * ("Implementacion en Hardware").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are dense, row-major, with no strides:
+ *   Q, K, V and O are bf16 [B, H, N, d].  The bias table is bf16
+ *   [H, 2*gh-1, 2*gw-1].  Packed sign words are uint32 [B, H, N, W] with
+ *   W = ceil(d/32).  Scales are float32 [B, H, N].
+ * - All pointers are device pointers (hipMalloc'ed or equivalent) aligned to
+ *   16 bytes.  The caller owns every buffer.  The library never allocates,
+ *   frees or synchronises.
+ * - stream is a hipStream_t passed as void*; NULL means the default stream.
+ *   All work is enqueued on it, and the call returns before it completes.
+ *   Buffers must stay valid until the stream has passed the work.
+ * - Arguments are validated before anything is enqueued.  On a validation
+ *   error nothing is launched and outputs are untouched.  Launch errors are
+ *   reported as BA_ERR_HIP.  Faults inside kernels surface at the caller's
+ *   next synchronisation, as for any HIP work.
+ * - ba_last_error() returns a thread-local message for the last failing call
+ *   on the calling thread.
+ * - Supported head dims: 8 <= d <= 256 with d % 8 == 0.  Any other d gives
+ *   BA_ERR_UNSUPPORTED.  N >= 1, B >= 1, H >= 1, and B*H*N must stay below
+ *   2^31 tokens.
+ *
+ * Packed-sign layout (fixed; ba_pack_signs writes it and the fused kernel
+ * reads it): channel c goes to word c/32, bit c%32, least significant bit
+ * first.  A bit is 1 iff the channel value compares < 0, so +0.0 and -0.0
+ * both give 0 (sign +1).  Bits for channels >= d are 0.
+ */
+#ifndef BINATTN_H
+#define BINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BA_VERSION 1
+
+typedef enum ba_status {
+  BA_OK = 0,
+  BA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  BA_ERR_SHAPE = 2,       /* inconsistent or non-positive sizes             */
+  BA_ERR_UNSUPPORTED = 3, /* valid request outside what the library handles */
+  BA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned               */
+  BA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required     */
+  BA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed     */
+} ba_status;
+
+/* Library version (BA_VERSION of the build). */
+int ba_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char* ba_status_string(ba_status s);
+
+/* Thread-local message describing the last failing call on this thread
+ * (empty string if none).  Valid until the next failing call on the thread. */
+const char* ba_last_error(void);
+
+/* Number of 32-bit sign words per token, W = ceil(d/32); 0 if d < 1. */
+int ba_pack_words(int d);
+
+/* ba_pack_signs -- scaled 1-bit representation of one tensor.
+ * Reduces each token x[b,h,n,:] to its scale and its signs: the scale is
+ * alpha = mean over the d channels of |x| (the mu of s_i = mu sign(q_i) in
+ * "Representaciones Binarias Escaladas") and the signs go into the packed
+ * layout above.
+ *   x      bf16  [B,H,N,d]   input (read only)
+ *   bits   uint32 [B,H,N,W]  output, every word written
+ *   alpha  float [B,H,N]     output; the fp32 sum over d is taken in a fixed
+ *                            order, so results are deterministic (within
+ *                            1e-6 relative of the exact mean for d <= 256)
+ * Errors: BA_ERR_NULL, BA_ERR_SHAPE, BA_ERR_UNSUPPORTED, BA_ERR_ALIGN,
+ *         BA_ERR_HIP. */
+ba_status ba_pack_signs(const void* x, int64_t B, int64_t H, int64_t N, int d,
+                        uint32_t* bits, float* alpha, void* stream);
+
+/* Workspace bytes that ba_attention_fwd needs for this problem: packed Q and
+ * K signs and scales, a key-major V^T copy (per head, N padded to a multiple
+ * of 128) and, for a bias grid with gw % 32 == 0, the table rows in float32.
+ * Pass gh = gw = 0 for a call without bias table.  Returns 0 for sizes the
+ * library rejects (including gh*gw != N when a grid is given). */
+size_t ba_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int gh, int gw);
+
+/* ba_attention_fwd -- BinaryAttention forward.
+ *   O[b,h,i,:] = sum_j P_ij V[b,h,j,:],  P = row softmax of
+ *   S_ij = scale * alpha_q,i * alpha_k,j * D_ij + bias(h,i,j),
+ *   D_ij = <sign q_i, sign k_j> = d - 2 popcount(qbits_i XOR kbits_j)
+ * (XNOR/popcount similarity, "Representaciones Binarias Escaladas"; added
+ * bias, "Mejora mediante Sesgo").  There is no masking (bidirectional
+ * attention).
+ *   q, k, v    bf16 [B,H,N,d]
+ *   bias       bf16 [H, 2*gh-1, 2*gw-1] or NULL.  Tokens lie row-major on a
+ *              gh x gw grid (token i at (i/gw, i%gw)), and
+ *              bias(h,i,j) = bias[h, yi-yj+gh-1, xi-xj+gw-1], shared over b.
+ *              With a table, gh*gw must equal N; without one, gh and gw are
+ *              ignored.
+ *   scale      softmax scale; pass 1/sqrt(d) for the standard scaling.  It
+ *              must be finite and >= 0.
+ *   o          bf16 [B,H,N,d] output (must not alias the inputs)
+ *   workspace  device buffer of at least ba_workspace_bytes(B,H,N,d,gh,gw)
+ *              bytes (gh = gw = 0 there when bias is NULL),
+ *              256-byte aligned.  Its contents on entry do not matter, and it
+ *              must not be shared by calls that may overlap on the GPU.
+ * Two kernels are enqueued: the sign/scale pack of Q and K (with the V^T
+ * copy), then the fused attention kernel.
+ * Errors: BA_ERR_NULL, BA_ERR_SHAPE, BA_ERR_UNSUPPORTED, BA_ERR_ALIGN,
+ *         BA_ERR_WORKSPACE, BA_ERR_HIP. */
+ba_status ba_attention_fwd(const void* q, const void* k, const void* v,
+                           const void* bias, int gh, int gw,
+                           int64_t B, int64_t H, int64_t N, int d, float scale,
+                           void* o, void* workspace, size_t ws_bytes,
+                           void* stream);
+
+/* QK integer-dot routes for ba_qk_int_dot. */
+#define BA_ROUTE_MFMA_FP4 0 /* +/-1 in fp4 (e2m1) on the scaled f8f6f4 MFMA;
+                               the route the fused kernel uses */
+#define BA_ROUTE_VALU_POPCOUNT 1 /* v_xor + v_bcnt on the packed words */
+
+/* ba_qk_int_dot -- the integer similarities D_ij = <sign q_i, sign k_j> for
+ * all pairs, from packed signs ("XNOR y popcount", "Representaciones
+ * Binarias Escaladas").  It exists to check the fused kernel's QK step bit
+ * for bit: route BA_ROUTE_MFMA_FP4 runs the same device code the fused kernel
+ * uses.
+ *   qbits, kbits  uint32 [B,H,N,W] in the packed layout
+ *   dots          int32 [B,H,N,N] output, dots[b,h,i,j] = D_ij
+ * Errors: BA_ERR_NULL, BA_ERR_SHAPE (also if B*H*N*N overflows int64 or
+ *         exceeds 2^40 elements), BA_ERR_UNSUPPORTED (unknown route or d),
+ *         BA_ERR_ALIGN, BA_ERR_HIP. */
+ba_status ba_qk_int_dot(const uint32_t* qbits, const uint32_t* kbits,
+                        int64_t B, int64_t H, int64_t N, int d, int route,
+                        int32_t* dots, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BINATTN_H */

@@ -1,0 +1,161 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/binattn.h declares, and rejects bad arguments synchronously, before
+any HIP call (no compute happens in these tests)."""
+
+import ctypes
+import pathlib
+import re
+
+import pytest
+
+from bit_qk_quantisation_amd import _lib
+
+HEADER = pathlib.Path(__file__).resolve().parents[1] / "include" / "binattn.h"
+
+pytestmark = pytest.mark.skipif(not _lib.LIB_PATH.exists(),
+                                reason="libbinattn.so not built")
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ba_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_matches_binding_list():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strings(lib):
+    assert lib.ba_version() == 1
+    for code, name in _lib.STATUS.items():
+        assert lib.ba_status_string(code).decode() == name
+    assert lib.ba_status_string(99).decode() == "BA_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("d,w", [(0, 0), (1, 1), (8, 1), (32, 1), (33, 2), (64, 2),
+                                 (72, 3), (128, 4), (256, 8)])
+def test_pack_words(lib, d, w):
+    assert lib.ba_pack_words(d) == w
+
+
+def _round(x, m):
+    return (x + m - 1) // m * m
+
+
+def expected_workspace(B, H, N, d, gh=0, gw=0):
+    """Workspace sections as the header describes them: two sign arrays, two
+    scale arrays and V^T, per head padded to a multiple of 128 tokens, each
+    section 256-byte aligned, plus the float32 bias rows when gw % 32 == 0."""
+    npad = _round(N, 128)
+    W = (d + 31) // 32
+    dpad = 32 * W
+    secs = [B * H * npad * W * 4] * 2 + [B * H * npad * 4] * 2 + [B * H * dpad * npad * 2]
+    if gh and gw % 32 == 0:
+        lpad = _round(2 * gw - 1 + 3, 4)
+        secs.append(H * (2 * gh - 1) * 4 * lpad * 4)
+    return sum(_round(s, 256) for s in secs)
+
+
+@pytest.mark.parametrize("shape", [(1, 3, 196, 64, 14, 14), (32, 12, 196, 64, 14, 14),
+                                   (8, 16, 1024, 72, 32, 32), (2, 12, 4096, 64, 64, 64),
+                                   (1, 16, 16384, 128, 128, 128), (2, 2, 100, 40, 0, 0)])
+def test_workspace_bytes(lib, shape):
+    B, H, N, d, gh, gw = shape
+    assert lib.ba_workspace_bytes(B, H, N, d, gh, gw) == expected_workspace(*shape)
+
+
+@pytest.mark.parametrize("args", [(1, 1, 10, 7, 0, 0), (1, 1, 10, 264, 0, 0), (0, 1, 10, 64, 0, 0),
+                                  (1, 1, 0, 64, 0, 0), (1, 1, 12, 64, 3, 5), (1, 1, 12, 64, 0, 12)])
+def test_workspace_bytes_rejects(lib, args):
+    assert lib.ba_workspace_bytes(*args) == 0
+
+
+# Fake, never-dereferenced device addresses: validation must fail before use.
+A = 0x100000
+GB = 1 << 30
+
+
+def fwd(lib, q=A, k=A + GB, v=A + 2 * GB, bias=None, gh=0, gw=0, B=1, H=2, N=64, d=64,
+        scale=0.125, o=A + 3 * GB, ws=A + 4 * GB, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    return lib.ba_attention_fwd(q, k, v, bias, gh, gw, B, H, N, d, scale, o, ws, ws_bytes, None)
+
+
+def test_fwd_null_pointers(lib):
+    assert fwd(lib, q=None) == 1
+    assert fwd(lib, v=None) == 1
+    assert fwd(lib, o=None) == 1
+    assert b"non-NULL" in lib.ba_last_error()
+
+
+def test_fwd_shapes(lib):
+    assert fwd(lib, N=0) == 2
+    assert fwd(lib, B=-1) == 2
+    assert fwd(lib, bias=A + 5 * GB, gh=4, gw=15, N=64) == 2      # gh*gw != N
+    assert fwd(lib, scale=float("nan")) == 2
+    assert fwd(lib, scale=-1.0) == 2
+    assert fwd(lib, o=A + 16) == 2                                 # o overlaps q
+    assert fwd(lib, B=1 << 20, H=1 << 10, N=1 << 12) == 2           # > 2^31 tokens
+
+
+@pytest.mark.parametrize("d", [0, 4, 12, 100, 264, 512])
+def test_fwd_unsupported_d(lib, d):
+    assert fwd(lib, d=d) == 3
+
+
+def test_fwd_unsupported_bias_table(lib):
+    # gw not a multiple of 32 and a table bigger than 48 KiB of float32
+    assert fwd(lib, bias=A + 5 * GB, gh=100, gw=70, N=7000) == 3
+
+
+def test_fwd_alignment(lib):
+    assert fwd(lib, q=A + 8) == 4
+    assert fwd(lib, bias=A + 5 * GB + 2, gh=8, gw=8) == 4
+    assert fwd(lib, ws=A + 4 * GB + 16) == 4                       # needs 256
+
+
+def test_fwd_workspace(lib):
+    assert fwd(lib, ws=None) == 5
+    need = lib.ba_workspace_bytes(1, 2, 64, 64, 0, 0)
+    assert fwd(lib, ws_bytes=need - 1) == 5
+    assert b"too small" in lib.ba_last_error()
+
+
+def test_pack_validation(lib):
+    assert lib.ba_pack_signs(None, 1, 1, 8, 64, A, A + GB, None) == 1
+    assert lib.ba_pack_signs(A, 1, 1, 8, 63, A + GB, A + 2 * GB, None) == 3
+    assert lib.ba_pack_signs(A, 1, 1, 0, 64, A + GB, A + 2 * GB, None) == 2
+    assert lib.ba_pack_signs(A + 4, 1, 1, 8, 64, A + GB, A + 2 * GB, None) == 4
+
+
+def test_qk_dot_validation(lib):
+    assert lib.ba_qk_int_dot(None, A, 1, 1, 8, 64, 0, A + GB, None) == 1
+    assert lib.ba_qk_int_dot(A, A + GB, 1, 1, 8, 64, 7, A + 2 * GB, None) == 3
+    assert lib.ba_qk_int_dot(A, A + GB, 1, 1, 70000, 64, 0, A + 2 * GB, None) == 2
+    assert lib.ba_qk_int_dot(A, A + GB, 1, 1, 8, 64, 0, A + 2 * GB + 4, None) == 4
+
+
+def test_last_error_is_thread_local(lib):
+    import threading
+    assert fwd(lib, d=12) == 3
+    seen = []
+
+    def other():
+        seen.append(lib.ba_last_error())
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen == [b""]
+    assert b"d=12" in lib.ba_last_error()

@@ -1,0 +1,115 @@
+"""GPU parity of the fused BinaryAttention forward (ba_attention_fwd) with
+the float64 oracle.
+
+Bar: max |O_gpu - O_oracle| <= 1e-2 * max |V| (bf16 P.V).  The derivation:
+rounding P to bf16 and O to bf16 each cost <= 2^-8 max|V|, and the fp32
+scores, exp2 and alpha contribute ~1e-6, so the bound is ~0.008 max|V|.
+
+Small problems are checked on every row.  The workload shapes are run at
+full size in the launch configuration the benchmark times, and checked on a
+seeded sample of rows (rows are independent, so a row of the full problem is
+exactly what the oracle computes for that row)."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_cases import announce, o_error, oracle_rows, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+bq = pytest.importorskip("bit_qk_quantisation_amd")
+
+TOL = 1e-2
+
+
+def run(inp):
+    dev = to_dev(inp)
+    o = bq.attention_fwd(dev["q"], dev["k"], dev["v"], dev["table"], inp["gh"], inp["gw"])
+    torch.cuda.synchronize()
+    return o
+
+
+@pytest.mark.parametrize("B,H,gh,gw,d", [
+    (1, 2, 1, 1, 64),      # N = 1: O = V
+    (1, 1, 1, 2, 32),      # N = 2
+    (1, 2, 7, 9, 64),      # N = 63, generic table path
+    (2, 1, 8, 8, 64),      # N = 64
+    (1, 2, 5, 13, 64),     # N = 65
+    (1, 3, 14, 14, 64),    # the tiny ViT grid
+    (1, 2, 4, 32, 64),     # gw % 32 == 0: table-row path, N = 128
+    (1, 1, 3, 32, 72),     # d = 72 (bits padded to 96), N = 96: ragged tile
+    (1, 2, 6, 32, 96),
+    (1, 1, 5, 64, 128),    # N = 320
+    (1, 1, 2, 96, 40),     # gw = 96, d = 40
+    (1, 1, 3, 32, 200),
+    (1, 1, 2, 64, 256),
+    (1, 1, 2, 128, 8),
+])
+def test_fwd_small_with_bias(B, H, gh, gw, d):
+    announce("fwd bias", B, H, gh, gw, d)
+    inp = workloads.make_inputs(B, H, gh * gw, d, seed=300 + gh * gw + d, grid=(gh, gw))
+    o = run(inp)
+    err = o_error(o, oracle_rows(inp), inp["v"])
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 1, 1, 64), (1, 2, 2, 64), (2, 1, 63, 32), (1, 1, 64, 64),
+                                     (1, 2, 65, 72), (1, 1, 129, 128), (1, 1, 300, 16)])
+def test_fwd_small_no_bias(B, H, N, d):
+    announce("fwd nobias", B, H, N, d)
+    inp = workloads.make_inputs(B, H, N, d, seed=400 + N + d, bias=False)
+    o = run(inp)
+    err = o_error(o, oracle_rows(inp), inp["v"])
+    assert err <= TOL, err
+
+
+def test_fwd_single_token_is_v():
+    announce("fwd N=1")
+    inp = workloads.make_inputs(2, 3, 1, 64, seed=5, grid=(1, 1))
+    o = run(inp)
+    assert torch.equal(o.cpu(), inp["v"])
+
+
+@pytest.mark.parametrize("scale", [4.0, 16.0])
+def test_fwd_large_logits(scale):
+    """Large |S| (Q and K scaled up): the running max moves by more than the
+    lazy-rescale threshold, so the rescale branch runs."""
+    announce("fwd large logits", scale)
+    inp = workloads.make_inputs(1, 2, 256, 64, seed=9, grid=(8, 32), q_scale=scale, k_scale=scale)
+    o = run(inp)
+    err = o_error(o, oracle_rows(inp), inp["v"])
+    assert err <= TOL, err
+
+
+def test_fwd_zero_queries_give_bias_softmax():
+    """Q = 0: alpha_q = 0, so S is the bias alone."""
+    announce("fwd zero q")
+    inp = workloads.make_inputs(1, 2, 128, 64, seed=10, grid=(4, 32))
+    inp["q"] = torch.zeros_like(inp["q"])
+    o = run(inp)
+    err = o_error(o, oracle_rows(inp), inp["v"])
+    assert err <= TOL, err
+
+
+def test_fwd_deterministic():
+    announce("fwd determinism")
+    inp = workloads.make_inputs(2, 3, 1024, 64, seed=11, grid=(32, 32))
+    dev = to_dev(inp)
+    o1 = bq.attention_fwd(dev["q"], dev["k"], dev["v"], dev["table"], 32, 32)
+    o2 = bq.attention_fwd(dev["q"], dev["k"], dev["v"], dev["table"], 32, 32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_fwd_workloads(name):
+    w = workloads.WORKLOADS[name]
+    announce("fwd workload", name)
+    inp = workloads.workload_inputs(w)
+    o = run(inp)
+    assert torch.isfinite(o.float()).all()
+    rows = None if w.N * w.B * w.H <= 600 else sample_rows(w.N, 48, w.seed)
+    err = o_error(o, oracle_rows(inp, rows), inp["v"], rows)
+    assert err <= TOL, (name, err)
