@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the BinaryAttention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one full forward (ba_attention_prepare + ba_attention_fwd_prepared,
+i.e. exactly ba_attention_fwd) over the resident bf16 inputs of the chosen
+workload (default: the 64x64-grid detection backbone, B=2 H=12 N=4096 d=64).
+W untimed steps run first, then exactly K steps are timed between two
+device synchronisations.  HIP events on the launch stream also bracket each
+kernel, which gives the average duration of the fused kernel and of the
+prologue.
+
+Printed: one JSON line on stdout with the throughput in TFLOP-eq/s
+(4*B*H*N^2*d per step, the FLOPs of dense QK^T and P.V), the fused kernel's
+roofline position and the CPU oracle's own throughput on a bounded sample of
+the same workload (the oracle runs on the host cores; it is a baseline, not
+the target).  Diagnostics go to stderr.
+
+Only one GPU is used: --gpus above 1 exits with a message.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import pathlib
+import sys
+import time
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = ("binary-QK attention fwd TFLOP-eq/s (4·B·H·N²·d) "
+          "+ % roofline, N=4096 d=64")
+
+# MI355X dense peaks (published): fp4 MFMA 10.1 PFLOP/s, bf16 MFMA 2.5
+# PFLOP/s, int8 MFMA 5.0 POP/s; HBM3E 8 TB/s.
+PEAK_FP4 = 10100.0
+PEAK_BF16 = 2500.0
+PEAK_INT8 = 5000.0
+PEAK_HBM_GBS = 8000.0
+# The fused kernel runs QK (2d flops-eq per score) on the fp4 unit and P.V
+# (2d flops per score) on the bf16 unit; with both at their peaks, one after
+# the other, the matrix-core bound of 4d flops-eq per score is:
+PEAK_MFMA_COMPOSITE = 4.0 / (2.0 / PEAK_FP4 + 2.0 / PEAK_BF16)
+PEAK_MFMA_INT8_BF16 = 4.0 / (2.0 / PEAK_INT8 + 2.0 / PEAK_BF16)
+
+PROFILES = ROOT / "profiles"
+FUSED_SOURCES = ("bit_qk_quantisation_amd/csrc/attention.hip",
+                 "bit_qk_quantisation_amd/csrc/ba_device.h",
+                 "bit_qk_quantisation_amd/csrc/ba_internal.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update((ROOT / p).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per fused-kernel launch from the committed rocprofv3 counter
+    summary, or None when there is none or the kernel source changed since."""
+    f = PROFILES / f"fused_attention_{workload}_traffic.json"
+    if not f.exists():
+        return None
+    rec = json.loads(f.read_text())
+    if rec.get("source_hash") != source_hash(FUSED_SOURCES):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def algorithmic_bytes(w, npad):
+    """Compulsory HBM bytes of the two kernels of one step."""
+    W = (w.d + 31) // 32
+    dpad = 32 * W
+    bh = w.B * w.H
+    tok = bh * w.N
+    packed = 2 * bh * npad * (4 * W + 4)            # Q and K signs + scales
+    vt = bh * dpad * npad * 2
+    rows = 0
+    if w.gw % 32 == 0:
+        lpad = (2 * w.gw - 1 + 3 + 3) // 4 * 4
+        rows = w.H * (2 * w.gh - 1) * 4 * lpad * 4
+    table = w.H * (2 * w.gh - 1) * (2 * w.gw - 1) * 2
+    prologue = 3 * tok * w.d * 2 + packed + vt + table + rows
+    fused = packed + vt + tok * w.d * 2 + (rows if rows else table)
+    return prologue, fused
+
+
+def cpu_baseline(w, inp, o_gpu, seconds: float):
+    """The float64 oracle on whole (b, h) heads of the same inputs, for about
+    `seconds` of host time; also returns the parity of those rows."""
+    import numpy as np
+
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 1 for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover - informational only
+        threads = os.cpu_count() or 1
+    q = workloads.as_f32(inp["q"])
+    k = workloads.as_f32(inp["k"])
+    v = workloads.as_f32(inp["v"])
+    t = workloads.as_f32(inp["table"])
+    og = o_gpu.float().cpu().numpy()
+    vmax = float(np.abs(v).max())
+    heads, worst = 0, 0.0
+    rows_per = min(w.N, 1024)
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            for r0 in range(0, w.N, rows_per):
+                rows = np.arange(r0, min(w.N, r0 + rows_per))
+                res = oracle.binary_attention_rows(
+                    q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                    None if t is None else t[h:h + 1], inp["gh"], inp["gw"], rows=rows)
+                err = float(np.abs(res["O"][0, 0] - og[b, h, rows]).max()) / vmax
+                worst = max(worst, err)
+            heads += 1
+            elapsed = time.perf_counter() - t0
+            if elapsed >= seconds:
+                break
+        if elapsed >= seconds:
+            break
+    flop = 4.0 * heads * w.N * w.N * w.d
+    return {
+        "value": flop / elapsed / 1e12,
+        "unit": "TFLOP-eq/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{heads} of {w.B * w.H} (b,h) heads, all {w.N} query rows each, "
+                  f"float64 numpy on the host ({elapsed:.1f} s)",
+        "parity_max_err_over_max_v": worst,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="host time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="also run one plain device copy of this many MiB "
+                         "(reference kernel for HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the BinaryAttention forward here is "
+              "a single-GPU kernel; run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import bit_qk_quantisation_amd as bq
+    import workloads
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    name = args.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[name]
+    lib = bq._lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    inp = workloads.workload_inputs(w)
+    q = inp["q"].to(dev)
+    k = inp["k"].to(dev)
+    v = inp["v"].to(dev)
+    table = inp["table"].to(dev) if inp["table"] is not None else None
+    gh, gw = inp["gh"], inp["gw"]
+    B, H, N, d = w.B, w.H, w.N, w.d
+    scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q)
+    nbytes = lib.ba_workspace_bytes(B, H, N, d, gh, gw)
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    wsp = (ws.data_ptr() + 255) // 256 * 256
+    tp = None if table is None else table.data_ptr()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def prepare():
+        bq.check(lib, lib.ba_attention_prepare(q.data_ptr(), k.data_ptr(), v.data_ptr(), tp, gh, gw,
+                                               B, H, N, d, wsp, nbytes, sp))
+
+    def fused():
+        bq.check(lib, lib.ba_attention_fwd_prepared(tp, gh, gw, B, H, N, d, scale, out.data_ptr(),
+                                                    wsp, nbytes, sp))
+
+    for _ in range(args.warmup):
+        prepare()
+        fused()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        prepare()
+        ev[i][1].record(stream)
+        fused()
+        ev[i][2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / K
+    pro_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    fus_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+
+    if args.copy_mb:
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    flop = w.flop_eq
+    value = flop / (ms_step * 1e-3) / 1e12
+    fused_tf = flop / (fus_ms * 1e-3) / 1e12
+    npad = (N + 127) // 128 * 128
+    pro_bytes, fus_bytes = algorithmic_bytes(w, npad)
+    traffic = measured_traffic(name)
+
+    baseline = None
+    if args.cpu_seconds > 0:
+        baseline = cpu_baseline(w, inp, out, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP-eq/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {**w.describe(), "qk": "1-bit signs as +/-1 fp4 on MFMA (exact integer dots)",
+                   "pv": "bf16 MFMA, fp32 accumulate", "softmax": "fp32, base 2",
+                   "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_kernel (fused)",
+            "achieved": round(fused_tf, 1),
+            "peak": round(PEAK_MFMA_COMPOSITE, 1),
+            "unit": "TFLOP/s",
+            "frac": round(fused_tf / PEAK_MFMA_COMPOSITE, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": baseline,
+        "detail": {
+            "fused_us": round(fus_ms * 1e3, 2),
+            "prologue_us": round(pro_ms * 1e3, 2),
+            "step_us": round(ms_step * 1e3, 2),
+            "frac_of_int8_bf16_mfma_roofline": round(fused_tf / PEAK_MFMA_INT8_BF16, 4),
+            "step_frac_of_composite_mfma_roofline": round(value / PEAK_MFMA_COMPOSITE, 4),
+            "prologue_algorithmic_GBps": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
+            "prologue_frac_of_hbm": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "fused_algorithmic_bytes": fus_bytes,
+            "device": torch.cuda.get_device_name(dev),
+        },
+    }
+    log(f"[bench] {name}: step {ms_step * 1e3:.1f} us (prologue {pro_ms * 1e3:.1f} us, "
+        f"fused {fus_ms * 1e3:.1f} us) -> {value:.1f} TFLOP-eq/s")
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -10,7 +10,8 @@ LIB_PATH = pathlib.Path(__file__).resolve().parent / "libbinattn.so"
 # Every symbol that include/binattn.h declares.
 EXPORTS = (
     "ba_version", "ba_status_string", "ba_last_error", "ba_pack_words",
-    "ba_pack_signs", "ba_workspace_bytes", "ba_attention_fwd", "ba_qk_int_dot",
+    "ba_pack_signs", "ba_workspace_bytes", "ba_attention_fwd", "ba_attention_prepare",
+    "ba_attention_fwd_prepared", "ba_qk_int_dot",
 )
 
 STATUS = {0: "BA_OK", 1: "BA_ERR_NULL", 2: "BA_ERR_SHAPE", 3: "BA_ERR_UNSUPPORTED",
@@ -55,6 +56,11 @@ def load(path=None) -> ctypes.CDLL:
     lib.ba_attention_fwd.restype = i32
     lib.ba_attention_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32,
                                      ctypes.c_float, vp, vp, sz, vp]
+    lib.ba_attention_prepare.restype = i32
+    lib.ba_attention_prepare.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp, sz, vp]
+    lib.ba_attention_fwd_prepared.restype = i32
+    lib.ba_attention_fwd_prepared.argtypes = [vp, i32, i32, i64, i64, i64, i32, ctypes.c_float,
+                                              vp, vp, sz, vp]
     lib.ba_qk_int_dot.restype = i32
     lib.ba_qk_int_dot.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp, vp]
     if path is None:

@@ -38,45 +38,8 @@ ba_status check_dims(int64_t B, int64_t H, int64_t N, int d) {
   return BA_OK;
 }
 
-// Byte offsets of the workspace sections of ba_attention_fwd.
-struct Layout {
-  int64_t Npad, W, dpad, Lpad;
-  int64_t qbits, kbits, alpha_q, alpha_k, vt, bias4, total;
-  int mode;
-};
-
-int bias_mode(const void* bias, int gw) {
-  if (bias == nullptr) return ba::kBiasNone;
-  return (gw % 32 == 0) ? ba::kBiasRows : ba::kBiasTable;
-}
-
-Layout layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int gw) {
-  Layout L{};
-  L.Npad = round_up(N, ba::kNAlign);
-  L.W = (d + 31) / 32;
-  L.dpad = 32 * ((d + 31) / 32);
-  L.mode = has_bias ? ((gw % 32 == 0) ? ba::kBiasRows : ba::kBiasTable) : ba::kBiasNone;
-  L.Lpad = (L.mode == ba::kBiasRows) ? round_up(2 * gw - 1 + 3, 4) : 0;
-  const int64_t BH = B * H;
-  int64_t off = 0;
-  auto take = [&](int64_t bytes) {
-    const int64_t at = off;
-    off = round_up(off + bytes, 256);
-    return at;
-  };
-  L.qbits = take(BH * L.Npad * L.W * 4);
-  L.kbits = take(BH * L.Npad * L.W * 4);
-  L.alpha_q = take(BH * L.Npad * 4);
-  L.alpha_k = take(BH * L.Npad * 4);
-  L.vt = take(BH * L.dpad * L.Npad * 2);
-  L.bias4 = take(L.mode == ba::kBiasRows ? H * (2 * gh - 1) * 4 * L.Lpad * 4 : 0);
-  L.total = off;
-  return L;
-}
-
 // Largest number of bias-table rows one (query tile, key tile) pair needs.
 int window_rows(int64_t N, int gw) {
-  int best = 1;
   const int64_t nqt = round_up(N, ba::kNAlign) / ba::kBM;
   const int64_t nkt = (N + ba::kBN - 1) / ba::kBN;
   int qspan = 0, kspan = 0;
@@ -90,8 +53,56 @@ int window_rows(int64_t N, int gw) {
     const int s = static_cast<int>((k0 + ba::kBN - 1) / gw - k0 / gw);
     if (s > kspan) kspan = s;
   }
-  best = qspan + kspan + 1;
-  return best;
+  return qspan + kspan + 1;
+}
+
+int64_t row_pad(int gw) { return round_up(2 * static_cast<int64_t>(gw) - 1 + 3, 4); }
+
+// How the fused kernel reads the bias: table rows staged per key tile (grid
+// width a multiple of 32, window small enough for the tile prefetch), the
+// whole table in LDS (small tables), or no bias.  -1: unsupported.
+int choose_mode(bool has_bias, int gh, int gw, int64_t N) {
+  if (!has_bias) return ba::kBiasNone;
+  if (gw % 32 == 0 && window_rows(N, gw) > 0 && window_rows(N, gw) <= ba::kBiasPadRows &&
+      window_rows(N, gw) * 4 * row_pad(gw) <= ba::kMaxWindowFloats)
+    return ba::kBiasRows;
+  if (static_cast<int64_t>(2 * gh - 1) * (2 * gw - 1) * 4 <= 48 * 1024) return ba::kBiasTable;
+  return -1;
+}
+
+// Byte offsets of the workspace sections of ba_attention_fwd.
+struct Layout {
+  int64_t Npad, W, dpad, Lpad;
+  int64_t qbits, kbits, alpha_q, alpha_k, qmax, kmax, vt, bias4, rowmax, total;
+  int mode;
+};
+
+Layout layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int gw) {
+  Layout L{};
+  L.Npad = round_up(N, ba::kNAlign);
+  L.W = (d + 31) / 32;
+  L.dpad = 32 * ((d + 31) / 32);
+  L.mode = choose_mode(has_bias, gh, gw, N);
+  L.Lpad = (L.mode == ba::kBiasRows) ? row_pad(gw) : 0;
+  const int64_t BH = B * H;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  L.qbits = take(BH * L.Npad * L.W * 4);
+  L.kbits = take(BH * L.Npad * L.W * 4);
+  L.alpha_q = take(BH * L.Npad * 4);
+  L.alpha_k = take(BH * L.Npad * 4);
+  L.qmax = take(BH * (L.Npad / 64) * 4);
+  L.kmax = take(BH * (L.Npad / 64) * 4);
+  L.vt = take(BH * L.dpad * L.Npad * 2);
+  const bool rows = L.mode == ba::kBiasRows;
+  L.bias4 = take(rows ? H * (2 * gh - 1 + 2 * ba::kBiasPadRows) * 4 * L.Lpad * 4 : 0);
+  L.rowmax = take(rows ? H * (2 * gh - 1) * 4 : 0);
+  L.total = off;
+  return L;
 }
 
 ba_status hip_fail(int err, const char* what) {
@@ -137,7 +148,7 @@ ba_status ba_pack_signs(const void* x, int64_t B, int64_t H, int64_t N, int d,
   if (!aligned16(x) || !aligned16(bits) || !aligned16(alpha))
     return fail(BA_ERR_ALIGN, "x, bits and alpha must be 16-byte aligned");
   ba::PrologueArgs p{};
-  p.pack[0] = ba::PackJob{static_cast<const uint16_t*>(x), bits, alpha, B * H,
+  p.pack[0] = ba::PackJob{static_cast<const uint16_t*>(x), bits, alpha, nullptr, B * H,
                           static_cast<int>(N), static_cast<int>(N), d, (d + 31) / 32};
   p.npack = 1;
   p.pack_blocks = (B * H * N + 63) / 64;
@@ -151,50 +162,77 @@ size_t ba_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int gh, int gw
   if (check_dims(B, H, N, d) != BA_OK) return 0;
   const bool has_bias = gh > 0 || gw > 0;
   if (has_bias && (gh < 1 || gw < 1 || static_cast<int64_t>(gh) * gw != N)) return 0;
-  return static_cast<size_t>(layout(B, H, N, d, has_bias, gh, gw).total);
+  const Layout L = layout(B, H, N, d, has_bias, gh, gw);
+  if (L.mode < 0) return 0;
+  return static_cast<size_t>(L.total);
 }
 
-ba_status ba_attention_fwd(const void* q, const void* k, const void* v,
-                           const void* bias, int gh, int gw,
-                           int64_t B, int64_t H, int64_t N, int d, float scale,
-                           void* o, void* workspace, size_t ws_bytes, void* stream) {
-  if (!q || !k || !v || !o) return fail(BA_ERR_NULL, "q, k, v and o must be non-NULL");
+}  // extern "C"
+
+namespace {
+
+// Everything one forward needs: validated sizes, workspace sections and the
+// arguments of both kernels.
+struct Plan {
+  ba::FwdArgs f;
+  ba::PrologueArgs p;
+  int mode;
+};
+
+// Validates a forward request.  `inputs` selects the checks of q, k, v (the
+// prologue's inputs) and `output` those of o (the fused kernel's output).
+ba_status make_plan(const void* q, const void* k, const void* v, bool inputs, const void* bias,
+                    int gh, int gw, int64_t B, int64_t H, int64_t N, int d, float scale, void* o,
+                    bool output, void* workspace, size_t ws_bytes, Plan* plan) {
+  if (inputs && (!q || !k || !v)) return fail(BA_ERR_NULL, "q, k and v must be non-NULL");
+  if (output && !o) return fail(BA_ERR_NULL, "o must be non-NULL");
   ba_status st = check_dims(B, H, N, d);
   if (st != BA_OK) return st;
-  if (!std::isfinite(scale) || scale < 0.0f) return fail(BA_ERR_SHAPE, "scale must be finite and >= 0");
+  if (output && (!std::isfinite(scale) || scale < 0.0f))
+    return fail(BA_ERR_SHAPE, "scale must be finite and >= 0");
   if (bias) {
     if (gh < 1 || gw < 1 || static_cast<int64_t>(gh) * gw != N)
       return fail(BA_ERR_SHAPE, "with a bias table gh*gw must equal N (gh=%d gw=%d N=%lld)", gh, gw,
                   (long long)N);
   }
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (bias && !aligned16(bias)))
+  if ((inputs && (!aligned16(q) || !aligned16(k) || !aligned16(v))) || (output && !aligned16(o)) ||
+      (bias && !aligned16(bias)))
     return fail(BA_ERR_ALIGN, "q, k, v, o and bias must be 16-byte aligned");
   const size_t tensor_bytes = static_cast<size_t>(B * H * N * d) * 2;
-  if (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(o, tensor_bytes, k, tensor_bytes) ||
-      overlaps(o, tensor_bytes, v, tensor_bytes))
+  if (inputs && output &&
+      (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(o, tensor_bytes, k, tensor_bytes) ||
+       overlaps(o, tensor_bytes, v, tensor_bytes)))
     return fail(BA_ERR_SHAPE, "o must not overlap q, k or v");
-  const int mode = bias_mode(bias, gw);
-  if (mode == ba::kBiasTable && static_cast<int64_t>(2 * gh - 1) * (2 * gw - 1) * 4 > 48 * 1024)
+  const int mode = choose_mode(bias != nullptr, gh, gw, N);
+  if (mode < 0)
     return fail(BA_ERR_UNSUPPORTED,
-                "bias grid %dx%d: gw not a multiple of 32 and the table exceeds 48 KiB of LDS", gh, gw);
+                "bias grid %dx%d: the table rows do not fit the tile window and the table exceeds 48 KiB",
+                gh, gw);
   const Layout L = layout(B, H, N, d, bias != nullptr, gh, gw);
   if (!workspace) return fail(BA_ERR_WORKSPACE, "workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(BA_ERR_ALIGN, "workspace must be 256-byte aligned");
   if (ws_bytes < static_cast<size_t>(L.total))
     return fail(BA_ERR_WORKSPACE, "workspace too small: %zu < %lld bytes", ws_bytes, (long long)L.total);
-  if (overlaps(workspace, L.total, o, tensor_bytes))
+  if (output && overlaps(workspace, L.total, o, tensor_bytes))
     return fail(BA_ERR_WORKSPACE, "workspace must not overlap o");
+  if (inputs && (overlaps(workspace, L.total, q, tensor_bytes) || overlaps(workspace, L.total, k, tensor_bytes) ||
+                 overlaps(workspace, L.total, v, tensor_bytes)))
+    return fail(BA_ERR_WORKSPACE, "workspace must not overlap q, k or v");
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   const int64_t BH = B * H;
-  ba::FwdArgs f{};
+  ba::FwdArgs& f = plan->f;
+  f = ba::FwdArgs{};
   f.qbits = reinterpret_cast<const uint32_t*>(ws + L.qbits);
   f.kbits = reinterpret_cast<const uint32_t*>(ws + L.kbits);
   f.alpha_q = reinterpret_cast<const float*>(ws + L.alpha_q);
   f.alpha_k = reinterpret_cast<const float*>(ws + L.alpha_k);
   f.vt = reinterpret_cast<const uint16_t*>(ws + L.vt);
   f.bias4 = reinterpret_cast<const float*>(ws + L.bias4);
+  f.bias_row_max = reinterpret_cast<const float*>(ws + L.rowmax);
+  f.qmax_blk = reinterpret_cast<const float*>(ws + L.qmax);
+  f.kmax_blk = reinterpret_cast<const float*>(ws + L.kmax);
   f.table = static_cast<const uint16_t*>(bias);
   f.o = static_cast<uint16_t*>(o);
   f.H = static_cast<int>(H);
@@ -213,31 +251,71 @@ ba_status ba_attention_fwd(const void* q, const void* k, const void* v,
   if (nwg > 0x7fffffff) return fail(BA_ERR_SHAPE, "too many workgroups");
   f.nwg = static_cast<int>(nwg);
   f.xcd_remap = (f.nwg % 8 == 0) ? 1 : 0;
-  // static LDS of the fused kernel: fp4 key operands, key scales and grid
-  // offsets, and the V^T tile.
-  const int nch = (d + 63) / 64;
-  const int static_lds = nch * ba::kBN * 2 * 16 + 2 * ba::kBN * 4 + f.dpad * ba::kVtStride * 2;
-  if (static_lds + ba::fwd_dynamic_lds(f, mode) > kMaxLds)
+  if (ba::fwd_static_lds(f.dpad) + ba::fwd_dynamic_lds(f, mode) > kMaxLds)
     return fail(BA_ERR_UNSUPPORTED, "bias window does not fit in LDS");
 
-  ba::PrologueArgs p{};
+  ba::PrologueArgs& p = plan->p;
+  p = ba::PrologueArgs{};
   p.pack[0] = ba::PackJob{static_cast<const uint16_t*>(q), const_cast<uint32_t*>(f.qbits),
-                          const_cast<float*>(f.alpha_q), BH, f.N, f.Npad, d, f.W};
+                          const_cast<float*>(f.alpha_q), const_cast<float*>(f.qmax_blk), BH,
+                          f.N, f.Npad, d, f.W};
   p.pack[1] = ba::PackJob{static_cast<const uint16_t*>(k), const_cast<uint32_t*>(f.kbits),
-                          const_cast<float*>(f.alpha_k), BH, f.N, f.Npad, d, f.W};
+                          const_cast<float*>(f.alpha_k), const_cast<float*>(f.kmax_blk), BH,
+                          f.N, f.Npad, d, f.W};
   p.npack = 2;
   p.pack_blocks = (BH * L.Npad + 63) / 64;
   p.vt = ba::VtJob{static_cast<const uint16_t*>(v), const_cast<uint16_t*>(f.vt), BH, f.N, f.Npad, d, f.dpad};
   p.vt_blocks = BH * (L.Npad / 64);
   if (mode == ba::kBiasRows) {
-    p.bias = ba::BiasJob{static_cast<const uint16_t*>(bias), const_cast<float*>(f.bias4), gh, gw, f.Lpad};
-    p.bias_blocks = H * (2 * gh - 1);
+    p.bias = ba::BiasJob{static_cast<const uint16_t*>(bias), const_cast<float*>(f.bias4),
+                         const_cast<float*>(f.bias_row_max), gh, gw, f.Lpad};
+    p.bias_blocks = H * (2 * gh - 1 + 2 * ba::kBiasPadRows);
   }
   const int64_t pblocks = 2 * p.pack_blocks + p.vt_blocks + p.bias_blocks;
   if (pblocks > 0x7fffffff) return fail(BA_ERR_SHAPE, "problem too large");
-  int err = ba::launch_prologue(p, stream);
+  plan->mode = mode;
+  return BA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ba_status ba_attention_prepare(const void* q, const void* k, const void* v, const void* bias, int gh,
+                               int gw, int64_t B, int64_t H, int64_t N, int d, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  Plan plan;
+  ba_status st = make_plan(q, k, v, true, bias, gh, gw, B, H, N, d, 0.0f, nullptr, false, workspace,
+                           ws_bytes, &plan);
+  if (st != BA_OK) return st;
+  const int err = ba::launch_prologue(plan.p, stream);
   if (err != 0) return hip_fail(err, "prologue launch");
-  err = ba::launch_attention(f, mode, stream);
+  return BA_OK;
+}
+
+ba_status ba_attention_fwd_prepared(const void* bias, int gh, int gw, int64_t B, int64_t H, int64_t N,
+                                    int d, float scale, void* o, const void* workspace,
+                                    size_t ws_bytes, void* stream) {
+  Plan plan;
+  ba_status st = make_plan(nullptr, nullptr, nullptr, false, bias, gh, gw, B, H, N, d, scale, o, true,
+                           const_cast<void*>(workspace), ws_bytes, &plan);
+  if (st != BA_OK) return st;
+  const int err = ba::launch_attention(plan.f, plan.mode, stream);
+  if (err != 0) return hip_fail(err, "attention launch");
+  return BA_OK;
+}
+
+ba_status ba_attention_fwd(const void* q, const void* k, const void* v,
+                           const void* bias, int gh, int gw,
+                           int64_t B, int64_t H, int64_t N, int d, float scale,
+                           void* o, void* workspace, size_t ws_bytes, void* stream) {
+  Plan plan;
+  ba_status st = make_plan(q, k, v, true, bias, gh, gw, B, H, N, d, scale, o, true, workspace,
+                           ws_bytes, &plan);
+  if (st != BA_OK) return st;
+  int err = ba::launch_prologue(plan.p, stream);
+  if (err != 0) return hip_fail(err, "prologue launch");
+  err = ba::launch_attention(plan.f, plan.mode, stream);
   if (err != 0) return hip_fail(err, "attention launch");
   return BA_OK;
 }

@@ -16,212 +16,387 @@
 //   P.V : O^T += V^T P^T on v_mfma_f32_32x32x16_bf16.  The 32x32 QK result
 //         already holds, per lane, one query and 8 keys of each 16-key step,
 //         which is the B-operand layout, so P never leaves registers.  The
-//         O^T accumulator keeps one query per lane, so the softmax
-//         rescale and the final 1/l are per-lane scalars.
+//         O^T accumulator keeps one query per lane, so the softmax scalars
+//         (offset, 1/l) are per lane.
 //
-// Workgroup: 4 waves x 32 queries = 128 queries of one (b, h).  Each 64-key
-// step stages the fp4 key operands (expanded once from the packed bits), the
-// key scales, the V^T tile and a window of the bias table in LDS.  Softmax is
-// the exact online form in base 2: running row max m, l and O rescaled by
-// 2^(m_old - m_new), with the rescale skipped while the max grows by at most
-// 8 (P values stay <= 2^8, so nothing overflows).
+// Workgroup: 4 waves x 32 queries = 128 queries of one (b, h).  Key tiles of
+// 64 are staged in LDS (fp4 key operands expanded once from the packed
+// bits, key scales, the V^T tile and a window of the bias table), double
+// buffered: the global loads of tile t+1 are in flight while tile t is
+// computed, and one barrier per tile separates the two buffers.
+//
+// Softmax, in base 2.  Every logit of a workgroup obeys |s| <= M with
+//   M = scale log2e max_i alpha_q,i max_j alpha_k,j d + log2e max|b|
+// (|D| <= d).  When M <= kFastMaxLogit, exp2(s) lies in [2^-M, 2^M] and
+// softmax is taken without any offset (it does not depend on one): one
+// multiply, one FMA and one exp2 per score, no running maximum.  Otherwise
+// the exact online softmax runs (running row max, rescale skipped while the
+// max grows by <= 8, so P <= 2^8).
 #include "ba_internal.h"
 
 namespace ba {
 
-template <int NCH, int CB, int BIAS>
-__global__ void __launch_bounds__(kThreads) attn_fwd_kernel(FwdArgs a) {
-  constexpr int DPAD = 32 * CB;
-  __shared__ __attribute__((aligned(16))) v4i s_k[NCH * kBN * 2];
-  __shared__ __attribute__((aligned(16))) float s_ak[kBN];
-  __shared__ __attribute__((aligned(16))) int s_gk[kBN];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[DPAD * kVtStride];
-  extern __shared__ __attribute__((aligned(16))) float s_bias[];
+// Largest logit bound (log2 units) for the offset-free path: exp2 stays in
+// [2^-32, 2^32], row sums below 2^48, so nothing under- or overflows for
+// |V| < 2^80.
+constexpr float kFastMaxLogit = 32.0f;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int li = lane & 31, lh = lane >> 5;
+// One LDS tile buffer.  The kernel declares two of them as separate LDS
+// objects, so the compiler can tell the asynchronous copies into one buffer
+// from the reads of the other and need not wait for the copies early.
+template <int NCH, int CB>
+struct TileBuf {
+  v4i k[NCH * kBN * 2];          // fp4 key operands [c][key][h]
+  float ak[kBN];                  // key scales
+  int gk[kBN];                    // grid offsets (table mode)
+  uint16_t vt[32 * CB * kBN];     // V^T tile: rows of 64 keys, swizzled
+  float win[kMaxWindowFloats];    // bias window (table-row mode)
+};
+
+// Per-thread registers holding the next tile's packed key bits (expanded
+// into LDS after the current tile) and grid offsets.
+template <int NCH>
+struct Prefetch {
+  static constexpr int kKWords = (NCH * kBN * 2 + kThreads - 1) / kThreads;
+  uint32_t kw[kKWords];
+  int gk;
+};
+
+template <int NCH>
+struct Ctx {
+  const FwdArgs* a;
+  float* table;        // dynamic LDS: the whole bias table (table mode)
+  int win_floats;      // floats in the bias window (table-row mode)
+  int tid, lane, wave, li, lh;
+  int bh, head, q0, qi;
+  int64_t tokbase;
+  int yq, xq, bsel, yq_lo, fidx;
+  float aq;            // alpha_q * scale * log2e
+  v4i qop[NCH];        // this lane's query operand (fp4 +/-1)
+};
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+
+// Byte offset of the 16-byte V^T chunk (slots 8q..8q+7) of row r in a tile.
+__device__ __forceinline__ int vt_chunk(int r, int q) { return r * 128 + ((q ^ ((r >> 1) & 7)) << 4); }
+
+// ---------------------------------------------------------------- staging --
+// Copies that go straight from global memory into LDS buffer `nb`
+// (global_load_lds: lane l of a wave fills bytes [16l, 16l+16) of a 1 KiB
+// block, or [4l, 4l+4) of a 256-byte block).
+template <int NCH, int CB, int BIAS>
+__device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb, int k0) {
+  const FwdArgs& a = *c.a;
+  constexpr int kVtChunks = 32 * CB * kBN * 2 / 1024;  // 1 KiB pieces of a V^T tile
+  const char* vsrc = reinterpret_cast<const char*>(
+      a.vt + (static_cast<int64_t>(c.bh) * (a.Npad / kBN) + k0 / kBN) * (32 * CB * kBN));
+  char* vdst = reinterpret_cast<char*>(&tb.vt[0]);
+#pragma unroll
+  for (int j = 0; j < kVtChunks / 4; ++j) {
+    const int chunk = c.wave + 4 * j;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(vsrc + chunk * 1024 + c.lane * 16),
+                                     static_cast<void*>(vdst + chunk * 1024), 16, 0, 0);
+  }
+  if (c.wave == 0)
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(a.alpha_k + c.tokbase + k0 + c.lane),
+                                     static_cast<void*>(&tb.ak[0]), 4, 0, 0);
+  if (BIAS == kBiasRows) {
+    const int rows_p = 2 * a.gh - 1 + 2 * kBiasPadRows;
+    const int dy0 = c.yq_lo - (k0 + kBN - 1) / a.gw + a.gh - 1 + kBiasPadRows;
+    const char* bsrc = reinterpret_cast<const char*>(
+        a.bias4 + (static_cast<int64_t>(c.head) * rows_p + dy0) * 4 * a.Lpad);
+    char* bdst = reinterpret_cast<char*>(&tb.win[0]);
+    const int bytes = c.win_floats * 4;
+    for (int chunk = c.wave; chunk * 1024 < bytes; chunk += 4) {
+      if (chunk * 1024 + c.lane * 16 < bytes)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(bsrc + chunk * 1024 + c.lane * 16),
+                                         static_cast<void*>(bdst + chunk * 1024), 16, 0, 0);
+    }
+  }
+}
+
+template <int NCH, int BIAS>
+__device__ __forceinline__ void load_keys(const Ctx<NCH>& c, int k0, Prefetch<NCH>& pf) {
+  const FwdArgs& a = *c.a;
+#pragma unroll
+  for (int j = 0; j < Prefetch<NCH>::kKWords; ++j) {
+    const int e = c.tid + j * kThreads;
+    uint32_t w = 0u;
+    if (e < NCH * kBN * 2) {
+      const int word = 2 * (e / (kBN * 2)) + (e & 1), key = (e >> 1) & (kBN - 1);
+      if (word < a.W) w = a.kbits[(c.tokbase + k0 + key) * a.W + word];
+    }
+    pf.kw[j] = w;
+  }
+  if (BIAS == kBiasTable && c.tid < kBN) {
+    const int j = (k0 + c.tid < a.N) ? k0 + c.tid : a.N - 1;
+    const int yj = j / a.gw;
+    pf.gk = yj * (2 * a.gw - 1) + (j - yj * a.gw);
+  }
+}
+
+template <int NCH, int CB, int BIAS>
+__device__ __forceinline__ void store_keys(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb, const Prefetch<NCH>& pf) {
+  const FwdArgs& a = *c.a;
+#pragma unroll
+  for (int j = 0; j < Prefetch<NCH>::kKWords; ++j) {
+    const int e = c.tid + j * kThreads;
+    if (e < NCH * kBN * 2) {
+      const int word = 2 * (e / (kBN * 2)) + (e & 1);
+      tb.k[e] = expand_signs_fp4(pf.kw[j], fp4_magnitude(word_valid(a.d, word)));
+    }
+  }
+  if (BIAS == kBiasTable && c.tid < kBN) tb.gk[c.tid] = pf.gk;
+}
+
+// ---------------------------------------------------------------- compute --
+// One 64-key tile for this wave's 32 queries, one 32-key block at a time.
+// FAST: offset-free exp2, no row max.  MASK: keys >= N get probability 0
+// (last tile only).
+template <bool FAST, bool MASK, int NCH, int CB, int BIAS>
+__device__ __forceinline__ void compute_tile(const Ctx<NCH>& c, const TileBuf<NCH, CB>& tb, int k0,
+                                             v16f (&oacc)[CB], float& lsum, float& mrow) {
+  const FwdArgs& a = *c.a;
+  const int li = c.li, lh = c.lh;
+  const float* win = &tb.win[0];
+  const char* vt = reinterpret_cast<const char*>(&tb.vt[0]);
+
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    // ---- QK: D for 32 keys x 32 queries ------------------------------------
+    v16f s = v16f{};
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+      s = mfma_signs_32x32x64(tb.k[(ch * kBN + blk * 32 + li) * 2 + lh], c.qop[ch], s);
+
+    // ---- logits in base 2: D * alpha_k * (alpha_q scale log2e) + log2e b ----
+    int brow = 0, bu0 = 0;
+    if (BIAS == kBiasRows) {
+      const int kb0 = k0 + blk * 32;
+      const int yk = kb0 / a.gw, xk0 = kb0 - yk * a.gw;
+      const int dy_min = c.yq_lo - (k0 + kBN - 1) / a.gw;
+      brow = c.yq - yk - dy_min;
+      bu0 = a.gw - 1 - c.xq + xk0 + 4 * lh - c.bsel;
+    }
+    float sc[16];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float4 ak = *reinterpret_cast<const float4*>(&tb.ak[blk * 32 + 8 * b + 4 * lh]);
+      float4 u = make_float4(s[4 * b] * ak.x, s[4 * b + 1] * ak.y, s[4 * b + 2] * ak.z, s[4 * b + 3] * ak.w);
+      if (BIAS == kBiasRows) {
+        const float4 bias = *reinterpret_cast<const float4*>(win + (brow * 4 + c.bsel) * a.Lpad + bu0 + 8 * b);
+        sc[4 * b + 0] = fmaf(u.x, c.aq, bias.x);
+        sc[4 * b + 1] = fmaf(u.y, c.aq, bias.y);
+        sc[4 * b + 2] = fmaf(u.z, c.aq, bias.z);
+        sc[4 * b + 3] = fmaf(u.w, c.aq, bias.w);
+      } else if (BIAS == kBiasTable) {
+        const int4 g = *reinterpret_cast<const int4*>(&tb.gk[blk * 32 + 8 * b + 4 * lh]);
+        sc[4 * b + 0] = fmaf(u.x, c.aq, c.table[c.fidx - g.x]);
+        sc[4 * b + 1] = fmaf(u.y, c.aq, c.table[c.fidx - g.y]);
+        sc[4 * b + 2] = fmaf(u.z, c.aq, c.table[c.fidx - g.z]);
+        sc[4 * b + 3] = fmaf(u.w, c.aq, c.table[c.fidx - g.w]);
+      } else {
+        sc[4 * b + 0] = u.x * c.aq;
+        sc[4 * b + 1] = u.y * c.aq;
+        sc[4 * b + 2] = u.z * c.aq;
+        sc[4 * b + 3] = u.w * c.aq;
+      }
+    }
+    if (MASK) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + blk * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (key >= a.N) sc[r] = -INFINITY;
+      }
+    }
+    if (!FAST) {
+      float mt = sc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+      mt = max_halves(mt);
+      const float mnew = fmaxf(mrow, mt);
+      if (__any(mnew > mrow + 8.0f)) {
+        const float f = fast_exp2(mrow - mnew);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) oacc[cb] *= f;
+        lsum *= f;
+        mrow = mnew;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] -= mrow;
+    }
+    // ---- P = exp2(logit) as bf16 pairs, row sum of the rounded values ------
+    uint32_t pk[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pk[j] = pack_bf16x2(fast_exp2(sc[2 * j]), fast_exp2(sc[2 * j + 1]));
+      lsum = add_bf16x2(pk[j], lsum);
+    }
+    // ---- P.V: two 16-key steps ----------------------------------------------
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int p = 2 * blk + half;
+      const v4u pw = {pk[4 * half], pk[4 * half + 1], pk[4 * half + 2], pk[4 * half + 3]};
+      const v8bf pop = __builtin_bit_cast(v8bf, pw);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const v8bf vop = *reinterpret_cast<const v8bf*>(vt + vt_chunk(cb * 32 + li, 2 * p + lh));
+        oacc[cb] = mfma_bf16_32x32x16(vop, pop, oacc[cb]);
+      }
+    }
+  }
+}
+
+// One key tile: start the copies of the next tile into `nxt`, compute the
+// current one from `cur`, expand the next keys into `nxt`, wait, barrier.
+template <bool FAST, int NCH, int CB, int BIAS>
+__device__ __forceinline__ void pass_step(const Ctx<NCH>& c, const TileBuf<NCH, CB>& cur, TileBuf<NCH, CB>& nxt,
+                                          int kt, int nkt, Prefetch<NCH>& pf, v16f (&oacc)[CB], float& lsum,
+                                          float& mrow) {
+  const FwdArgs& a = *c.a;
+  const int k0 = kt * kBN;
+  const bool more = kt + 1 < nkt;
+  if (more) {
+    copy_tile_async<NCH, CB, BIAS>(c, nxt, k0 + kBN);
+    load_keys<NCH, BIAS>(c, k0 + kBN, pf);
+  }
+  if (k0 + kBN <= a.N)
+    compute_tile<FAST, false, NCH, CB, BIAS>(c, cur, k0, oacc, lsum, mrow);
+  else
+    compute_tile<FAST, true, NCH, CB, BIAS>(c, cur, k0, oacc, lsum, mrow);
+  if (more) store_keys<NCH, CB, BIAS>(c, nxt, pf);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// One pass over all keys.  Returns the lane's partial row sum; O^T in oacc.
+template <bool FAST, int NCH, int CB, int BIAS>
+__device__ __forceinline__ float run_pass(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb0, TileBuf<NCH, CB>& tb1,
+                                          v16f (&oacc)[CB]) {
+  const FwdArgs& a = *c.a;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) oacc[cb] = v16f{};
+  float lsum = 0.0f, mrow = -INFINITY;
+  Prefetch<NCH> pf;
+  copy_tile_async<NCH, CB, BIAS>(c, tb0, 0);
+  load_keys<NCH, BIAS>(c, 0, pf);
+  store_keys<NCH, CB, BIAS>(c, tb0, pf);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int nkt = (a.N + kBN - 1) / kBN;
+  for (int kt = 0; kt < nkt; kt += 2) {
+    pass_step<FAST, NCH, CB, BIAS>(c, tb0, tb1, kt, nkt, pf, oacc, lsum, mrow);
+    if (kt + 1 < nkt) pass_step<FAST, NCH, CB, BIAS>(c, tb1, tb0, kt + 1, nkt, pf, oacc, lsum, mrow);
+  }
+  return lsum;
+}
+
+// Waves per SIMD the register budget is sized for.
+template <int CB>
+struct Occupancy {
+  static constexpr int kWaves = CB <= 2 ? 3 : (CB <= 4 ? 2 : 1);
+};
+
+template <int NCH, int CB, int BIAS>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<CB>::kWaves)))
+attn_fwd_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB> tb0;
+  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB> tb1;
+  __shared__ float red[kThreads / 64];
+  extern __shared__ __attribute__((aligned(16))) float s_table[];
+
+  Ctx<NCH> c;
+  c.a = &a;
+  c.table = s_table;
+  c.win_floats = (BIAS == kBiasRows) ? a.win_rows * 4 * a.Lpad : 0;
+  c.tid = threadIdx.x;
+  c.lane = c.tid & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+  c.li = c.lane & 31;
+  c.lh = c.lane >> 5;
 
   int wg = blockIdx.x;
   if (a.xcd_remap) {
     const int per = a.nwg >> 3;
     wg = (wg & 7) * per + (wg >> 3);
   }
-  const int bh = wg / a.nqt, qt = wg - bh * a.nqt;
-  const int head = bh % a.H;
-  const int q0 = qt * kBM;
-  const int qi = q0 + wave * 32 + li;
-  const int64_t tokbase = static_cast<int64_t>(bh) * a.Npad;
+  c.bh = wg / a.nqt;
+  const int qt = wg - c.bh * a.nqt;
+  c.head = c.bh % a.H;
+  c.q0 = qt * kBM;
+  c.qi = c.q0 + c.wave * 32 + c.li;
+  c.tokbase = static_cast<int64_t>(c.bh) * a.Npad;
 
-  // Query operands: word 2c + lh of this lane's query, as fp4 +/-1.
-  v4i qop[NCH];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int word = 2 * c + lh;
-    const uint32_t w = word < a.W ? a.qbits[(tokbase + qi) * a.W + word] : 0u;
-    qop[c] = expand_signs_fp4(w, fp4_magnitude(word_valid(a.d, word)));
+  for (int ch = 0; ch < NCH; ++ch) {
+    const int word = 2 * ch + c.lh;
+    const uint32_t w = word < a.W ? a.qbits[(c.tokbase + c.qi) * a.W + word] : 0u;
+    c.qop[ch] = expand_signs_fp4(w, fp4_magnitude(word_valid(a.d, word)));
   }
-  const float aq = a.alpha_q[tokbase + qi] * a.qscale;
-
-  int yq = 0, xq = 0, fidx = 0, bsel = 0, yq_lo = 0;
+  c.aq = a.alpha_q[c.tokbase + c.qi] * a.qscale;
+  c.yq = c.xq = c.bsel = c.yq_lo = c.fidx = 0;
   if (BIAS != kBiasNone) {
-    yq = qi / a.gw;
-    xq = qi - yq * a.gw;
+    c.yq = c.qi / a.gw;
+    c.xq = c.qi - c.yq * a.gw;
   }
   if (BIAS == kBiasRows) {
-    bsel = (a.gw - 1 - xq) & 3;
-    yq_lo = q0 / a.gw;
+    c.bsel = (a.gw - 1 - c.xq) & 3;
+    c.yq_lo = c.q0 / a.gw;
   }
-  if (BIAS == kBiasTable) {
-    const int yc = yq < a.gh ? yq : a.gh - 1;
-    fidx = (yc + a.gh - 1) * (2 * a.gw - 1) + xq + a.gw - 1;
+
+  // ---- logit bound M (log2 units) ------------------------------------------
+  const int nblk = a.Npad / 64;
+  float km = 0.0f, bm = 0.0f;
+  for (int e = c.tid; e < nblk; e += kThreads) km = fmaxf(km, a.kmax_blk[static_cast<int64_t>(c.bh) * nblk + e]);
+  if (BIAS == kBiasRows) {
+    const int rows = 2 * a.gh - 1;
+    for (int e = c.tid; e < rows; e += kThreads) bm = fmaxf(bm, a.bias_row_max[c.head * rows + e]);
+  } else if (BIAS == kBiasTable) {
+    // the whole table goes to LDS once, as float32 * log2e
     const int n = (2 * a.gh - 1) * (2 * a.gw - 1);
-    const uint16_t* t = a.table + static_cast<int64_t>(head) * n;
-    for (int e = tid; e < n; e += kThreads) s_bias[e] = kLog2e * bf16_to_f32(t[e]);
+    const uint16_t* t = a.table + static_cast<int64_t>(c.head) * n;
+    for (int e = c.tid; e < n; e += kThreads) {
+      const float v = kLog2e * bf16_to_f32(t[e]);
+      c.table[e] = v;
+      bm = fmaxf(bm, fabsf(v));
+    }
+    const int yc = c.yq < a.gh ? c.yq : a.gh - 1;
+    c.fidx = (yc + a.gh - 1) * (2 * a.gw - 1) + c.xq + a.gw - 1;
   }
+  km = block_max(km, red);
+  bm = block_max(bm, red);
+  const int qb = c.bh * nblk + c.q0 / 64;
+  const float qm = fmaxf(a.qmax_blk[qb], a.qmax_blk[qb + 1]);
+  const float M = a.qscale * qm * km * static_cast<float>(a.d) + bm;
 
   v16f oacc[CB];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) oacc[cb] = v16f{};
-  float lsum = 0.0f;
-  float mrow = -INFINITY;
-
-  const int nkt = (a.N + kBN - 1) / kBN;
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * kBN;
-    __syncthreads();
-    // ---- stage the key tile -------------------------------------------
-    for (int e = tid; e < NCH * kBN * 2; e += kThreads) {
-      const int c = e / (kBN * 2), key = (e >> 1) & (kBN - 1), word = 2 * c + (e & 1);
-      const uint32_t w = word < a.W ? a.kbits[(tokbase + k0 + key) * a.W + word] : 0u;
-      s_k[e] = expand_signs_fp4(w, fp4_magnitude(word_valid(a.d, word)));
-    }
-    if (tid < kBN) {
-      s_ak[tid] = a.alpha_k[tokbase + k0 + tid];
-      if (BIAS == kBiasTable) {
-        const int j = (k0 + tid < a.N) ? k0 + tid : a.N - 1;
-        const int yj = j / a.gw;
-        s_gk[tid] = yj * (2 * a.gw - 1) + (j - yj * a.gw);
-      }
-    }
-    for (int e = tid; e < DPAD * 8; e += kThreads) {
-      const int c = e >> 3, q = e & 7;
-      *reinterpret_cast<uint4*>(s_vt + c * kVtStride + 8 * q) = *reinterpret_cast<const uint4*>(
-          a.vt + (static_cast<int64_t>(bh) * DPAD + c) * a.Npad + k0 + 8 * q);
-    }
-    int dy_min = 0;
-    if (BIAS == kBiasRows) {
-      dy_min = yq_lo - (k0 + kBN - 1) / a.gw;
-      const int per = 4 * a.Lpad;
-      const int nvec = a.win_rows * a.Lpad;  // float4 count
-      const int rows_tab = 2 * a.gh - 1;
-      for (int e = tid; e < nvec; e += kThreads) {
-        const int r = (4 * e) / per;
-        const int dyidx = dy_min + r + a.gh - 1;
-        float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (dyidx >= 0 && dyidx < rows_tab)
-          val = *reinterpret_cast<const float4*>(
-              a.bias4 + (static_cast<int64_t>(head) * rows_tab + dyidx) * per + (4 * e - r * per));
-        *reinterpret_cast<float4*>(s_bias + 4 * e) = val;
-      }
-    }
-    __syncthreads();
-
-    // ---- QK: D for 64 keys x 32 queries (two 32x32 blocks) -------------
-    v16f sblk[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      sblk[blk] = v16f{};
-#pragma unroll
-      for (int c = 0; c < NCH; ++c)
-        sblk[blk] = mfma_signs_32x32x64(s_k[(c * kBN + blk * 32 + li) * 2 + lh], qop[c], sblk[blk]);
-    }
-
-    // ---- scores in base 2: D * alpha_k * (alpha_q scale log2e) + log2e b --
-    float sc[2][16];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      int brow = 0, bu0 = 0;
-      if (BIAS == kBiasRows) {
-        const int kb0 = k0 + blk * 32;
-        const int yk = kb0 / a.gw, xk0 = kb0 - yk * a.gw;
-        brow = yq - yk - dy_min;
-        bu0 = a.gw - 1 - xq + xk0 + 4 * lh - bsel;
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float4 ak = *reinterpret_cast<const float4*>(s_ak + blk * 32 + 8 * b + 4 * lh);
-        float4 bias = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (BIAS == kBiasRows) {
-          bias = *reinterpret_cast<const float4*>(s_bias + (brow * 4 + bsel) * a.Lpad + bu0 + 8 * b);
-        } else if (BIAS == kBiasTable) {
-          const int4 g = *reinterpret_cast<const int4*>(s_gk + blk * 32 + 8 * b + 4 * lh);
-          bias = make_float4(s_bias[fidx - g.x], s_bias[fidx - g.y], s_bias[fidx - g.z], s_bias[fidx - g.w]);
-        }
-        sc[blk][4 * b + 0] = fmaf(sblk[blk][4 * b + 0] * ak.x, aq, bias.x);
-        sc[blk][4 * b + 1] = fmaf(sblk[blk][4 * b + 1] * ak.y, aq, bias.y);
-        sc[blk][4 * b + 2] = fmaf(sblk[blk][4 * b + 2] * ak.z, aq, bias.z);
-        sc[blk][4 * b + 3] = fmaf(sblk[blk][4 * b + 3] * ak.w, aq, bias.w);
-      }
-    }
-    if (k0 + kBN > a.N) {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + blk * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          if (key >= a.N) sc[blk][r] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax (exact, base 2, lazy rescale) -------------------
-    float mt = sc[0][0];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[blk][r]);
-    mt = max_halves(mt);
-    const float mnew = fmaxf(mrow, mt);
-    if (__any(mnew > mrow + 8.0f)) {
-      const float f = fast_exp2(mrow - mnew);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) oacc[cb] *= f;
-      lsum *= f;
-      mrow = mnew;
-    }
-    uint32_t pk[2][8];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pk[blk][j] = pack_bf16x2(fast_exp2(sc[blk][2 * j] - mrow), fast_exp2(sc[blk][2 * j + 1] - mrow));
-        lsum = add_bf16x2(pk[blk][j], lsum);
-      }
-
-    // ---- P.V: O^T[c][i] += sum_k V^T[c][k] P^T[k][i] -------------------
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int blk = p >> 1, off = (p & 1) * 4;
-      const v4u pw = {pk[blk][off], pk[blk][off + 1], pk[blk][off + 2], pk[blk][off + 3]};
-      const v8bf pop = __builtin_bit_cast(v8bf, pw);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const v8bf vop = *reinterpret_cast<const v8bf*>(s_vt + (cb * 32 + li) * kVtStride + 16 * p + 8 * lh);
-        oacc[cb] = mfma_bf16_32x32x16(vop, pop, oacc[cb]);
-      }
-    }
-  }
+  float lsum;
+  if (M <= kFastMaxLogit)  // false for NaN as well
+    lsum = sum_halves(run_pass<true, NCH, CB, BIAS>(c, tb0, tb1, oacc));
+  else
+    lsum = sum_halves(run_pass<false, NCH, CB, BIAS>(c, tb0, tb1, oacc));
 
   // ---- epilogue: O = O^T / l, bf16, one query per lane --------------------
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) pin_uniform(oacc[cb]);
-  const float inv = 1.0f / sum_halves(lsum);
-  if (qi < a.N) {
-    uint16_t* orow = a.o + (static_cast<int64_t>(bh) * a.N + qi) * a.d;
+  const float inv = 1.0f / lsum;
+  if (c.qi < a.N) {
+    uint16_t* orow = a.o + (static_cast<int64_t>(c.bh) * a.N + c.qi) * a.d;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int c0 = cb * 32 + 8 * b + 4 * lh;
+        const int c0 = cb * 32 + 8 * b + 4 * c.lh;
         if (c0 < a.d) {
           uint2 w;
           w.x = pack_bf16x2(oacc[cb][4 * b + 0] * inv, oacc[cb][4 * b + 1] * inv);
@@ -233,9 +408,23 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(FwdArgs a) {
 }
 
 int fwd_dynamic_lds(const FwdArgs& a, int mode) {
-  if (mode == kBiasRows) return a.win_rows * 4 * a.Lpad * 4;
   if (mode == kBiasTable) return (2 * a.gh - 1) * (2 * a.gw - 1) * 4;
   return 0;
+}
+
+int fwd_static_lds(int dpad) {
+  const int cb = dpad / 32;
+  constexpr int kRed = kThreads / 64 * 4;
+  switch (cb) {
+    case 1: return 2 * sizeof(TileBuf<1, 1>) + kRed;
+    case 2: return 2 * sizeof(TileBuf<1, 2>) + kRed;
+    case 3: return 2 * sizeof(TileBuf<2, 3>) + kRed;
+    case 4: return 2 * sizeof(TileBuf<2, 4>) + kRed;
+    case 5: return 2 * sizeof(TileBuf<3, 5>) + kRed;
+    case 6: return 2 * sizeof(TileBuf<3, 6>) + kRed;
+    case 7: return 2 * sizeof(TileBuf<4, 7>) + kRed;
+    default: return 2 * sizeof(TileBuf<4, 8>) + kRed;
+  }
 }
 
 template <int NCH, int CB>

@@ -17,6 +17,12 @@ constexpr int kNAlign = 128;
 // spreads rows over the LDS banks).
 constexpr int kVtStride = 72;
 
+// Zero rows on each side of the float32 bias rows in the workspace.
+constexpr int kBiasPadRows = 8;
+// Largest bias window (floats) the table-row path stages per key tile: two
+// table rows of a 128-wide grid, or one of a 256-wide grid.
+constexpr int kMaxWindowFloats = 2304;
+
 // Largest LDS footprint of a prologue block (vt tile at d = 256).
 constexpr int kPrologueSmem = 64 * (256 + 8) * 2;
 
@@ -24,20 +30,22 @@ struct PackJob {
   const uint16_t* x;  // bf16 [BH][N][d]
   uint32_t* bits;     // [BH][Npad][W]
   float* alpha;       // [BH][Npad]
+  float* alpha_max;   // [BH*Npad/64]: max alpha of each 64-token block, or null
   int64_t BH;
   int N, Npad, d, W;
 };
 
 struct VtJob {
   const uint16_t* v;  // bf16 [BH][N][d]
-  uint16_t* vt;       // bf16 [BH][dpad][Npad], keys in P.V slot order
+  uint16_t* vt;       // bf16 [BH][Npad/64][dpad][64], see vt_block
   int64_t BH;
   int N, Npad, d, dpad;
 };
 
 struct BiasJob {
   const uint16_t* table;  // bf16 [H][2gh-1][2gw-1]
-  float* bias4;           // [H][2gh-1][4][Lpad]
+  float* bias4;           // [H][2gh-1+2*kBiasPadRows][4][Lpad]
+  float* row_max;         // [H][2gh-1]: max |entry| * log2(e) of each row
   int gh, gw, Lpad;
 };
 
@@ -60,8 +68,11 @@ struct FwdArgs {
   const uint32_t* kbits;   // [BH][Npad][W]
   const float* alpha_q;    // [BH][Npad]
   const float* alpha_k;    // [BH][Npad]
-  const uint16_t* vt;      // [BH][dpad][Npad]
-  const float* bias4;      // kBiasRows: [H][2gh-1][4][Lpad]
+  const uint16_t* vt;      // [BH][Npad/64][dpad][64] (slot order, swizzled)
+  const float* bias4;      // kBiasRows: [H][2gh-1+2*kBiasPadRows][4][Lpad]
+  const float* bias_row_max;  // kBiasRows: [H][2gh-1], max |b| log2e per row
+  const float* qmax_blk;   // [BH][Npad/64] max alpha_q per 64-token block
+  const float* kmax_blk;   // [BH][Npad/64] max alpha_k per 64-token block
   const uint16_t* table;   // kBiasTable: bf16 [H][2gh-1][2gw-1]
   uint16_t* o;             // bf16 [BH][N][d]
   int H, N, Npad, d, W, dpad;
@@ -73,8 +84,9 @@ struct FwdArgs {
   int xcd_remap;           // 1: spread consecutive heads over the 8 XCDs
 };
 
-// Dynamic LDS bytes of the fused kernel for these arguments.
+// Dynamic / static LDS bytes of the fused kernel.
 int fwd_dynamic_lds(const FwdArgs& a, int mode);
+int fwd_static_lds(int dpad);
 
 // Launch the fused kernel (template selected from d and the bias mode).
 int launch_attention(const FwdArgs& a, int mode, void* stream);

@@ -85,15 +85,34 @@ __device__ void pack_block(const PackJob& job, int64_t blk, unsigned char* smem)
       job.alpha[t] = (n < job.N) ? v[0] / static_cast<float>(d) : 0.0f;
     }
   }
+  if (job.alpha_max != nullptr && threadIdx.x < 64) {
+    // Block maximum of alpha (64 tokens, never straddling heads since Npad is
+    // a multiple of 64).  alpha >= 0, so the lane fold starts from 0.
+    const int tok = threadIdx.x;
+    const int64_t t = t0 + tok;
+    float m = 0.0f;
+    if (t < T) {
+      const int64_t bh = t / job.Npad;
+      const int n = static_cast<int>(t - bh * job.Npad);
+      if (n < job.N) m = sp[tok * 33] / static_cast<float>(d);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (tok == 0) job.alpha_max[blk] = m;
+  }
 }
 
 // ------------------------------------------------------------------ vt ----
 // One block = one (b,h) and 64 keys.  Loads the 64 x d tile row-major into
-// LDS, then writes dpad rows of 64 keys in P.V slot order (zeros past N and
-// past d).
+// LDS, then writes the tile's dpad rows of 64 keys (zeros past N and past d)
+// as one contiguous dpad x 128-byte block, in the order the fused kernel
+// copies straight into LDS:
+//   * keys are permuted inside each group of 16 into the P.V slot order
+//     (slots 8h..8h+3 = keys 4h..4h+3, slots 8h+4..8h+7 = keys 8+4h..8+4h+3);
+//   * the eight 16-byte chunks of row c are stored at chunk position
+//     q ^ ((c >> 1) & 7), so that 16 lanes reading one chunk from 16
+//     consecutive rows touch 16 different 4-bank groups.
 __device__ __forceinline__ int vt_slot_key(int slot) {
-  // slot (0..63) -> key offset in the 64-key tile.  Within a 16-group, slots
-  // 8h..8h+3 are keys 4h..4h+3 and slots 8h+4..8h+7 are keys 8+4h..8+4h+3.
   const int g = slot >> 4, s16 = slot & 15, hh = s16 >> 3, s = s16 & 7;
   return g * 16 + (s < 4 ? 4 * hh + s : 8 + 4 * hh + (s - 4));
 }
@@ -102,17 +121,18 @@ __device__ void vt_block(const VtJob& job, int64_t blk, unsigned char* smem) {
   const int d = job.d, C = d / 8, stride = d + 8;  // bf16 units
   const int tiles = job.Npad / 64;
   const int64_t bh = blk / tiles;
-  const int n0 = static_cast<int>(blk - bh * tiles) * 64;
-  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);  // [64][d+8]
+  const int tile = static_cast<int>(blk - bh * tiles), n0 = tile * 64;
+  uint16_t* t = reinterpret_cast<uint16_t*>(smem);  // [64][d+8]
 
   for (int g = threadIdx.x; g < 64 * C; g += blockDim.x) {
     const int key = g / C, ch = g - key * C;
     uint4 raw = make_uint4(0u, 0u, 0u, 0u);
     if (n0 + key < job.N)
       raw = *reinterpret_cast<const uint4*>(job.v + ((bh * job.N + n0 + key) * d + ch * 8));
-    *reinterpret_cast<uint4*>(tile + key * stride + ch * 8) = raw;
+    *reinterpret_cast<uint4*>(t + key * stride + ch * 8) = raw;
   }
   __syncthreads();
+  uint16_t* out = job.vt + (bh * tiles + tile) * static_cast<int64_t>(job.dpad) * 64;
   for (int g = threadIdx.x; g < job.dpad * 8; g += blockDim.x) {
     const int c = g >> 3, q = g & 7;
     uint32_t w[4];
@@ -120,32 +140,50 @@ __device__ void vt_block(const VtJob& job, int64_t blk, unsigned char* smem) {
     for (int k = 0; k < 4; ++k) {
       uint32_t lo = 0, hi = 0;
       if (c < d) {
-        lo = tile[vt_slot_key(8 * q + 2 * k) * stride + c];
-        hi = tile[vt_slot_key(8 * q + 2 * k + 1) * stride + c];
+        lo = t[vt_slot_key(8 * q + 2 * k) * stride + c];
+        hi = t[vt_slot_key(8 * q + 2 * k + 1) * stride + c];
       }
       w[k] = lo | (hi << 16);
     }
-    *reinterpret_cast<uint4*>(job.vt + ((bh * job.dpad + c) * static_cast<int64_t>(job.Npad) + n0 + 8 * q)) =
-        make_uint4(w[0], w[1], w[2], w[3]);
+    const int pos = q ^ ((c >> 1) & 7);
+    *reinterpret_cast<uint4*>(out + c * 64 + pos * 8) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
 // ---------------------------------------------------------------- bias ----
-// One block = one (h, dy) table row -> 4 shifted copies of Lpad floats.
+// One block = one row of the padded table: rows kBiasPadRows..kBiasPadRows +
+// 2gh-2 hold the table rows dy = 0..2gh-2, the kBiasPadRows rows on each side
+// are zero (the fused kernel's windows may reach past the grid for padded
+// tokens).  Each row is 4 shifted copies of Lpad floats:
 // R[u] = log2e * T[h, dy, 2gw-2-u] for 0 <= u <= 2gw-2 (else 0), and copy s
 // holds C_s[v] = R[v+s].
 __device__ void bias_block(const BiasJob& job, int64_t blk) {
   const int rows = 2 * job.gh - 1, cols = 2 * job.gw - 1;
-  const int64_t h = blk / rows;
-  const int dy = static_cast<int>(blk - h * rows);
-  const uint16_t* trow = job.table + (h * rows + dy) * cols;
-  float* out = job.bias4 + (h * rows + dy) * 4 * static_cast<int64_t>(job.Lpad);
+  const int prow = rows + 2 * kBiasPadRows;
+  const int64_t h = blk / prow;
+  const int dyp = static_cast<int>(blk - h * prow), dy = dyp - kBiasPadRows;
+  const bool inside = dy >= 0 && dy < rows;
+  const uint16_t* trow = job.table + (h * rows + (inside ? dy : 0)) * cols;
+  float* out = job.bias4 + (h * prow + dyp) * 4 * static_cast<int64_t>(job.Lpad);
+  float m = 0.0f;
   for (int e = threadIdx.x; e < 4 * job.Lpad; e += blockDim.x) {
     const int s = e / job.Lpad, v = e - s * job.Lpad;
     const int u = v + s;
     float val = 0.0f;
-    if (u <= cols - 1) val = kLog2e * bf16_to_f32(trow[cols - 1 - u]);
+    if (inside && u <= cols - 1) val = kLog2e * bf16_to_f32(trow[cols - 1 - u]);
     out[e] = val;
+    m = fmaxf(m, fabsf(val));
+  }
+  // row maximum of |entry| * log2e, for the logit bound
+  __shared__ float wmax[kThreads / 64];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0 && inside) {
+    float r = wmax[0];
+    for (int i = 1; i < static_cast<int>(blockDim.x >> 6); ++i) r = fmaxf(r, wmax[i]);
+    job.row_max[h * rows + dy] = r;
   }
 }
 

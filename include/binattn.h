@@ -126,6 +126,33 @@ ba_status ba_attention_fwd(const void* q, const void* k, const void* v,
                            void* o, void* workspace, size_t ws_bytes,
                            void* stream);
 
+/* The two halves of ba_attention_fwd, for callers that time or schedule the
+ * two kernels separately.
+ *
+ * ba_attention_prepare -- enqueues the prologue kernel: packed signs and
+ * scales of Q and K ("Representaciones Binarias Escaladas"), the key-major
+ * V^T copy and, for gw % 32 == 0, the float32 bias rows, all written into
+ * `workspace`.  Same arguments and errors as ba_attention_fwd, without scale
+ * and o.
+ *
+ * ba_attention_fwd_prepared -- enqueues only the fused kernel, reading a
+ * workspace that ba_attention_prepare filled with the same bias, gh, gw, B,
+ * H, N and d (stream order must put the prepare first).  The bias table is
+ * read again here when gw % 32 != 0.  Same errors as ba_attention_fwd.
+ *
+ * ba_attention_fwd(...) is ba_attention_prepare(...) followed by
+ * ba_attention_fwd_prepared(...) on the same stream. */
+ba_status ba_attention_prepare(const void* q, const void* k, const void* v,
+                               const void* bias, int gh, int gw,
+                               int64_t B, int64_t H, int64_t N, int d,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+ba_status ba_attention_fwd_prepared(const void* bias, int gh, int gw,
+                                    int64_t B, int64_t H, int64_t N, int d,
+                                    float scale, void* o,
+                                    const void* workspace, size_t ws_bytes,
+                                    void* stream);
+
 /* QK integer-dot routes for ba_qk_int_dot. */
 #define BA_ROUTE_MFMA_FP4 0 /* +/-1 in fp4 (e2m1) on the scaled f8f6f4 MFMA;
                                the route the fused kernel uses */

@@ -55,15 +55,19 @@ def _round(x, m):
 
 def expected_workspace(B, H, N, d, gh=0, gw=0):
     """Workspace sections as the header describes them: two sign arrays, two
-    scale arrays and V^T, per head padded to a multiple of 128 tokens, each
-    section 256-byte aligned, plus the float32 bias rows when gw % 32 == 0."""
+    scale arrays, two arrays of per-64-token scale maxima and V^T, per head
+    padded to a multiple of 128 tokens, each section 256-byte aligned; plus,
+    for a grid width that is a multiple of 32, the float32 bias rows (4
+    shifted copies per row, 8 zero rows on each side) and their maxima."""
     npad = _round(N, 128)
     W = (d + 31) // 32
     dpad = 32 * W
-    secs = [B * H * npad * W * 4] * 2 + [B * H * npad * 4] * 2 + [B * H * dpad * npad * 2]
+    secs = [B * H * npad * W * 4] * 2 + [B * H * npad * 4] * 2 + [B * H * (npad // 64) * 4] * 2
+    secs.append(B * H * dpad * npad * 2)
     if gh and gw % 32 == 0:
         lpad = _round(2 * gw - 1 + 3, 4)
-        secs.append(H * (2 * gh - 1) * 4 * lpad * 4)
+        secs.append(H * (2 * gh - 1 + 16) * 4 * lpad * 4)
+        secs.append(H * (2 * gh - 1) * 4)
     return sum(_round(s, 256) for s in secs)
 
 
