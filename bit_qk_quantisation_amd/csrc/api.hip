@@ -56,7 +56,14 @@ int window_rows(int64_t N, int gw) {
   return qspan + kspan + 1;
 }
 
-int64_t row_pad(int gw) { return round_up(2 * static_cast<int64_t>(gw) - 1 + 3, 4); }
+// Floats per copy of a bias row: 2gw-1 entries + 3 of shift slack, rounded
+// up to 16 (mod 64), so that the four shifted copies start 16 banks apart and
+// 16 lanes reading 4 consecutive entries each never share a bank.
+int64_t row_pad(int gw) {
+  int64_t l = round_up(2 * static_cast<int64_t>(gw) - 1 + 3, 4);
+  while (l % 64 != 16) l += 4;
+  return l;
+}
 
 // How the fused kernel reads the bias: table rows staged per key tile (grid
 // width a multiple of 32, window small enough for the tile prefetch), the

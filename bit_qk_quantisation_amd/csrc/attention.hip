@@ -17,13 +17,16 @@
 //         already holds, per lane, one query and 8 keys of each 16-key step,
 //         which is the B-operand layout, so P never leaves registers.  The
 //         O^T accumulator keeps one query per lane, so the softmax scalars
-//         (offset, 1/l) are per lane.
+//         are per lane.  V^T carries rows of ones (or an extra constant
+//         operand block), so the same product also yields the row sums l.
 //
 // Workgroup: 4 waves x 32 queries = 128 queries of one (b, h).  Key tiles of
-// 64 are staged in LDS (fp4 key operands expanded once from the packed
-// bits, key scales, the V^T tile and a window of the bias table), double
-// buffered: the global loads of tile t+1 are in flight while tile t is
-// computed, and one barrier per tile separates the two buffers.
+// 64 live in two LDS buffers: while tile t is computed from one, the next
+// tile's V^T, key scales and bias window stream into the other with
+// global_load_lds, and its packed key bits are loaded into registers, then
+// expanded to fp4 operands after the compute.  One barrier per tile.  Every
+// LDS address is a per-lane base fixed at kernel start plus a constant or a
+// wave-uniform offset; no division runs inside the key loop.
 //
 // Softmax, in base 2.  Every logit of a workgroup obeys |s| <= M with
 //   M = scale log2e max_i alpha_q,i max_j alpha_k,j d + log2e max|b|
@@ -53,27 +56,57 @@ struct TileBuf {
   float win[kMaxWindowFloats];    // bias window (table-row mode)
 };
 
-// Per-thread registers holding the next tile's packed key bits (expanded
-// into LDS after the current tile) and grid offsets.
-template <int NCH>
-struct Prefetch {
-  static constexpr int kKWords = (NCH * kBN * 2 + kThreads - 1) / kThreads;
-  uint32_t kw[kKWords];
-  int gk;
+// The row sums l of P come out of the P.V product: V^T carries rows of ones
+// (rows d and d+4 when d % 32 != 0; otherwise an extra 32-row block whose A
+// operand is a constant register), so accumulator row d (or row 0 of the
+// extra block) holds sum_j P_ij.
+template <int CB, bool XONES>
+struct Acc {
+  v16f o[CB];
+  v16f ones[1];  // used when XONES
 };
 
+// Per-lane and per-workgroup constants.
 template <int NCH>
 struct Ctx {
   const FwdArgs* a;
   float* table;        // dynamic LDS: the whole bias table (table mode)
-  int win_floats;      // floats in the bias window (table-row mode)
   int tid, lane, wave, li, lh;
   int bh, head, q0, qi;
   int64_t tokbase;
-  int yq, xq, bsel, yq_lo, fidx;
   float aq;            // alpha_q * scale * log2e
   v4i qop[NCH];        // this lane's query operand (fp4 +/-1)
+  // LDS byte offsets inside a TileBuf, per lane
+  int off_k, off_ak, off_v[4], off_win;
+  int yq, xq, yq_lo, fidx;
+  // Asynchronous tile copies: wave-uniform bases (scalar registers) plus
+  // per-lane 32-bit byte offsets.
+  const char* vbase;   // V^T tiles of this (b, h)
+  int voff;            // this lane's byte in a V^T tile (first 1 KiB piece)
+  const char* kbase;   // packed key words of this (b, h)
+  int koff[2];         // this thread's key words (bytes, tile 0)
+  int kword[2];        // their word index (-1: no entry for the thread)
+  const char* bbase;   // bias rows of this head (table-row mode)
+  int boff[2];         // this lane's byte in its 1 KiB window pieces
+  bool bvalid[2];      // whether that byte lies inside the window
 };
+
+// Uniform per-tile position of the keys on the grid (table-row mode).
+struct KeyPos {
+  int k0;
+  int ky[2], kx[2];  // row and column of the first key of each 32-key block
+};
+
+__device__ __forceinline__ KeyPos next_keys(const KeyPos& p, int gw) {
+  KeyPos n;
+  n.k0 = p.k0 + kBN;
+  // blocks are 32-aligned and gw % 32 == 0: a block never straddles rows
+  n.ky[0] = p.ky[1] + (p.kx[1] + 32 == gw ? 1 : 0);
+  n.kx[0] = p.kx[1] + 32 == gw ? 0 : p.kx[1] + 32;
+  n.ky[1] = n.ky[0] + (n.kx[0] + 32 == gw ? 1 : 0);
+  n.kx[1] = n.kx[0] + 32 == gw ? 0 : n.kx[0] + 32;
+  return n;
+}
 
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
@@ -87,228 +120,370 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return r;
 }
 
-// Byte offset of the 16-byte V^T chunk (slots 8q..8q+7) of row r in a tile.
-__device__ __forceinline__ int vt_chunk(int r, int q) { return r * 128 + ((q ^ ((r >> 1) & 7)) << 4); }
+template <typename T>
+__device__ __forceinline__ T lds_load(const void* base, int byte_off) {
+  return *reinterpret_cast<const T*>(__builtin_assume_aligned(static_cast<const char*>(base) + byte_off, 16));
+}
 
 // ---------------------------------------------------------------- staging --
-// Copies that go straight from global memory into LDS buffer `nb`
+// Starts the copies of key tile `t` (first key kp.k0) into `tb`: V^T, key
+// scales and (table-row mode) the bias window go straight to LDS
 // (global_load_lds: lane l of a wave fills bytes [16l, 16l+16) of a 1 KiB
-// block, or [4l, 4l+4) of a 256-byte block).
+// block, or [4l, 4l+4) of a 256-byte block); the packed key words go to
+// registers.
 template <int NCH, int CB, int BIAS>
-__device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb, int k0) {
+__device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb, int t, const KeyPos& kp,
+                                                uint32_t (&kw)[2], int& gk) {
   const FwdArgs& a = *c.a;
-  constexpr int kVtChunks = 32 * CB * kBN * 2 / 1024;  // 1 KiB pieces of a V^T tile
-  const char* vsrc = reinterpret_cast<const char*>(
-      a.vt + (static_cast<int64_t>(c.bh) * (a.Npad / kBN) + k0 / kBN) * (32 * CB * kBN));
+  // The key words first: vmcnt counts in issue order, so waiting for them
+  // later leaves the LDS copies below in flight.
+  const char* ksrc = c.kbase + static_cast<int64_t>(kp.k0) * a.W * 4;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    kw[j] = 0u;
+    if (j * kThreads < NCH * kBN * 2 && c.kword[j] >= 0 && c.kword[j] < a.W)
+      kw[j] = *reinterpret_cast<const uint32_t*>(ksrc + static_cast<uint32_t>(c.koff[j]));
+  }
+  constexpr int kVtBytes = 32 * CB * kBN * 2;
+  const char* vsrc = c.vbase + static_cast<int64_t>(t) * kVtBytes;
   char* vdst = reinterpret_cast<char*>(&tb.vt[0]);
 #pragma unroll
-  for (int j = 0; j < kVtChunks / 4; ++j) {
-    const int chunk = c.wave + 4 * j;
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(vsrc + chunk * 1024 + c.lane * 16),
-                                     static_cast<void*>(vdst + chunk * 1024), 16, 0, 0);
-  }
-  if (c.wave == 0)
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(a.alpha_k + c.tokbase + k0 + c.lane),
+  for (int j = 0; j < kVtBytes / 4096; ++j)
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(vsrc + static_cast<uint32_t>(c.voff + j * 4096)),
+                                     static_cast<void*>(vdst + (c.wave + 4 * j) * 1024), 16, 0, 0);
+  if (c.wave == 0) {
+    const char* asrc = reinterpret_cast<const char*>(a.alpha_k + c.tokbase + kp.k0);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(asrc + static_cast<uint32_t>(c.lane * 4)),
                                      static_cast<void*>(&tb.ak[0]), 4, 0, 0);
-  if (BIAS == kBiasRows) {
-    const int rows_p = 2 * a.gh - 1 + 2 * kBiasPadRows;
-    const int dy0 = c.yq_lo - (k0 + kBN - 1) / a.gw + a.gh - 1 + kBiasPadRows;
-    const char* bsrc = reinterpret_cast<const char*>(
-        a.bias4 + (static_cast<int64_t>(c.head) * rows_p + dy0) * 4 * a.Lpad);
-    char* bdst = reinterpret_cast<char*>(&tb.win[0]);
-    const int bytes = c.win_floats * 4;
-    for (int chunk = c.wave; chunk * 1024 < bytes; chunk += 4) {
-      if (chunk * 1024 + c.lane * 16 < bytes)
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(bsrc + chunk * 1024 + c.lane * 16),
-                                         static_cast<void*>(bdst + chunk * 1024), 16, 0, 0);
-    }
   }
-}
-
-template <int NCH, int BIAS>
-__device__ __forceinline__ void load_keys(const Ctx<NCH>& c, int k0, Prefetch<NCH>& pf) {
-  const FwdArgs& a = *c.a;
+  if (BIAS == kBiasRows) {
+    // window rows start at dy = yq_lo - yk_hi; yk_hi is the row of block 1
+    const int dy0 = c.yq_lo - kp.ky[1] + a.gh - 1 + kBiasPadRows;
+    const char* bsrc = c.bbase + static_cast<int64_t>(dy0) * 16 * a.Lpad;
+    char* bdst = reinterpret_cast<char*>(&tb.win[0]);
 #pragma unroll
-  for (int j = 0; j < Prefetch<NCH>::kKWords; ++j) {
-    const int e = c.tid + j * kThreads;
-    uint32_t w = 0u;
-    if (e < NCH * kBN * 2) {
-      const int word = 2 * (e / (kBN * 2)) + (e & 1), key = (e >> 1) & (kBN - 1);
-      if (word < a.W) w = a.kbits[(c.tokbase + k0 + key) * a.W + word];
-    }
-    pf.kw[j] = w;
+    for (int j = 0; j < 2; ++j)
+      if (c.bvalid[j])
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(bsrc + static_cast<uint32_t>(c.boff[j])),
+                                         static_cast<void*>(bdst + (c.wave + 4 * j) * 1024), 16, 0, 0);
   }
   if (BIAS == kBiasTable && c.tid < kBN) {
-    const int j = (k0 + c.tid < a.N) ? k0 + c.tid : a.N - 1;
+    const int j = (kp.k0 + c.tid < a.N) ? kp.k0 + c.tid : a.N - 1;
     const int yj = j / a.gw;
-    pf.gk = yj * (2 * a.gw - 1) + (j - yj * a.gw);
+    gk = yj * (2 * a.gw - 1) + (j - yj * a.gw);
   }
 }
 
+// Expands the key words loaded by copy_tile_async into fp4 operands in LDS.
 template <int NCH, int CB, int BIAS>
-__device__ __forceinline__ void store_keys(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb, const Prefetch<NCH>& pf) {
+__device__ __forceinline__ void store_keys(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb, const uint32_t (&kw)[2], int gk) {
   const FwdArgs& a = *c.a;
 #pragma unroll
-  for (int j = 0; j < Prefetch<NCH>::kKWords; ++j) {
-    const int e = c.tid + j * kThreads;
-    if (e < NCH * kBN * 2) {
-      const int word = 2 * (e / (kBN * 2)) + (e & 1);
-      tb.k[e] = expand_signs_fp4(pf.kw[j], fp4_magnitude(word_valid(a.d, word)));
-    }
+  for (int j = 0; j < 2; ++j) {
+    if (j * kThreads < NCH * kBN * 2 && c.kword[j] >= 0)
+      tb.k[c.tid + j * kThreads] = expand_signs_fp4(kw[j], fp4_magnitude(word_valid(a.d, c.kword[j])));
   }
-  if (BIAS == kBiasTable && c.tid < kBN) tb.gk[c.tid] = pf.gk;
+  if (BIAS == kBiasTable && c.tid < kBN) tb.gk[c.tid] = gk;
 }
 
 // ---------------------------------------------------------------- compute --
-// One 64-key tile for this wave's 32 queries, one 32-key block at a time.
-// FAST: offset-free exp2, no row max.  MASK: keys >= N get probability 0
-// (last tile only).
-template <bool FAST, bool MASK, int NCH, int CB, int BIAS>
-__device__ __forceinline__ void compute_tile(const Ctx<NCH>& c, const TileBuf<NCH, CB>& tb, int k0,
-                                             v16f (&oacc)[CB], float& lsum, float& mrow) {
+// Logits of one 32-key block in base 2:
+//   D * alpha_k * (alpha_q scale log2e) + log2e b
+template <bool MASK, int NCH, int CB, int BIAS>
+__device__ __forceinline__ void block_logits(const Ctx<NCH>& c, const TileBuf<NCH, CB>& tb, const KeyPos& kp,
+                                             int blk, const v16f& s, float (&sc)[16]) {
   const FwdArgs& a = *c.a;
-  const int li = c.li, lh = c.lh;
-  const float* win = &tb.win[0];
-  const char* vt = reinterpret_cast<const char*>(&tb.vt[0]);
+  int woff = 0;
+  if (BIAS == kBiasRows) woff = c.off_win + (kp.ky[1] - kp.ky[blk]) * 16 * a.Lpad + kp.kx[blk] * 4;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const float4 ak = lds_load<float4>(tb.ak, c.off_ak + (blk * 32 + 8 * b) * 4);
+    const float u0 = s[4 * b] * ak.x, u1 = s[4 * b + 1] * ak.y, u2 = s[4 * b + 2] * ak.z, u3 = s[4 * b + 3] * ak.w;
+    if (BIAS == kBiasRows) {
+      const float4 bias = lds_load<float4>(tb.win, woff + 32 * b);
+      sc[4 * b + 0] = fmaf(u0, c.aq, bias.x);
+      sc[4 * b + 1] = fmaf(u1, c.aq, bias.y);
+      sc[4 * b + 2] = fmaf(u2, c.aq, bias.z);
+      sc[4 * b + 3] = fmaf(u3, c.aq, bias.w);
+    } else if (BIAS == kBiasTable) {
+      const int4 g = lds_load<int4>(tb.gk, c.off_ak + (blk * 32 + 8 * b) * 4);
+      sc[4 * b + 0] = fmaf(u0, c.aq, c.table[c.fidx - g.x]);
+      sc[4 * b + 1] = fmaf(u1, c.aq, c.table[c.fidx - g.y]);
+      sc[4 * b + 2] = fmaf(u2, c.aq, c.table[c.fidx - g.z]);
+      sc[4 * b + 3] = fmaf(u3, c.aq, c.table[c.fidx - g.w]);
+    } else {
+      sc[4 * b + 0] = u0 * c.aq;
+      sc[4 * b + 1] = u1 * c.aq;
+      sc[4 * b + 2] = u2 * c.aq;
+      sc[4 * b + 3] = u3 * c.aq;
+    }
+  }
+  if (MASK) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kp.k0 + blk * 32 + 8 * (r >> 2) + 4 * c.lh + (r & 3);
+      if (key >= a.N) sc[r] = -INFINITY;
+    }
+  }
+}
 
+// Exact path only: running row max over this block; rescales the
+// accumulators when it grows by more than 8, and shifts the logits by it.
+template <int CB, bool XONES>
+__device__ __forceinline__ void block_rescale(float (&sc)[16], Acc<CB, XONES>& acc, float& mrow) {
+  float mt = sc[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+  mt = max_halves(mt);
+  const float mnew = fmaxf(mrow, mt);
+  if (__any(mnew > mrow + 8.0f)) {
+    const float f = fast_exp2(mrow - mnew);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc.o[cb] *= f;
+    if (XONES) acc.ones[0] *= f;
+    mrow = mnew;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sc[r] -= mrow;
+}
+
+// One 64-key tile for this wave's 32 queries, one 32-key block at a time:
+// QK, logits, exp2 and bf16 packing, then P.V (and the row sums).
+// FAST: offset-free exp2, no row max.  MASK: keys >= N get probability 0.
+template <bool FAST, bool MASK, int NCH, int CB, bool XONES, int BIAS>
+__device__ __forceinline__ void compute_tile(const Ctx<NCH>& c, const TileBuf<NCH, CB>& tb, const KeyPos& kp,
+                                             Acc<CB, XONES>& acc, float& mrow, const v8bf& ones_op) {
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    // ---- QK: D for 32 keys x 32 queries ------------------------------------
     v16f s = v16f{};
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch)
-      s = mfma_signs_32x32x64(tb.k[(ch * kBN + blk * 32 + li) * 2 + lh], c.qop[ch], s);
-
-    // ---- logits in base 2: D * alpha_k * (alpha_q scale log2e) + log2e b ----
-    int brow = 0, bu0 = 0;
-    if (BIAS == kBiasRows) {
-      const int kb0 = k0 + blk * 32;
-      const int yk = kb0 / a.gw, xk0 = kb0 - yk * a.gw;
-      const int dy_min = c.yq_lo - (k0 + kBN - 1) / a.gw;
-      brow = c.yq - yk - dy_min;
-      bu0 = a.gw - 1 - c.xq + xk0 + 4 * lh - c.bsel;
-    }
+      s = mfma_signs_32x32x64(lds_load<v4i>(tb.k, c.off_k + ch * 2048 + blk * 1024), c.qop[ch], s);
     float sc[16];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const float4 ak = *reinterpret_cast<const float4*>(&tb.ak[blk * 32 + 8 * b + 4 * lh]);
-      float4 u = make_float4(s[4 * b] * ak.x, s[4 * b + 1] * ak.y, s[4 * b + 2] * ak.z, s[4 * b + 3] * ak.w);
-      if (BIAS == kBiasRows) {
-        const float4 bias = *reinterpret_cast<const float4*>(win + (brow * 4 + c.bsel) * a.Lpad + bu0 + 8 * b);
-        sc[4 * b + 0] = fmaf(u.x, c.aq, bias.x);
-        sc[4 * b + 1] = fmaf(u.y, c.aq, bias.y);
-        sc[4 * b + 2] = fmaf(u.z, c.aq, bias.z);
-        sc[4 * b + 3] = fmaf(u.w, c.aq, bias.w);
-      } else if (BIAS == kBiasTable) {
-        const int4 g = *reinterpret_cast<const int4*>(&tb.gk[blk * 32 + 8 * b + 4 * lh]);
-        sc[4 * b + 0] = fmaf(u.x, c.aq, c.table[c.fidx - g.x]);
-        sc[4 * b + 1] = fmaf(u.y, c.aq, c.table[c.fidx - g.y]);
-        sc[4 * b + 2] = fmaf(u.z, c.aq, c.table[c.fidx - g.z]);
-        sc[4 * b + 3] = fmaf(u.w, c.aq, c.table[c.fidx - g.w]);
-      } else {
-        sc[4 * b + 0] = u.x * c.aq;
-        sc[4 * b + 1] = u.y * c.aq;
-        sc[4 * b + 2] = u.z * c.aq;
-        sc[4 * b + 3] = u.w * c.aq;
-      }
-    }
-    if (MASK) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + blk * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (key >= a.N) sc[r] = -INFINITY;
-      }
-    }
-    if (!FAST) {
-      float mt = sc[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
-      mt = max_halves(mt);
-      const float mnew = fmaxf(mrow, mt);
-      if (__any(mnew > mrow + 8.0f)) {
-        const float f = fast_exp2(mrow - mnew);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) oacc[cb] *= f;
-        lsum *= f;
-        mrow = mnew;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] -= mrow;
-    }
-    // ---- P = exp2(logit) as bf16 pairs, row sum of the rounded values ------
+    block_logits<MASK, NCH, CB, BIAS>(c, tb, kp, blk, s, sc);
+    if (!FAST) block_rescale(sc, acc, mrow);
     uint32_t pk[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pk[j] = pack_bf16x2(fast_exp2(sc[2 * j]), fast_exp2(sc[2 * j + 1]));
-      lsum = add_bf16x2(pk[j], lsum);
-    }
-    // ---- P.V: two 16-key steps ----------------------------------------------
+    for (int j = 0; j < 8; ++j) pk[j] = pack_bf16x2(fast_exp2(sc[2 * j]), fast_exp2(sc[2 * j + 1]));
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int p = 2 * blk + half;
       const v4u pw = {pk[4 * half], pk[4 * half + 1], pk[4 * half + 2], pk[4 * half + 3]};
       const v8bf pop = __builtin_bit_cast(v8bf, pw);
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const v8bf vop = *reinterpret_cast<const v8bf*>(vt + vt_chunk(cb * 32 + li, 2 * p + lh));
-        oacc[cb] = mfma_bf16_32x32x16(vop, pop, oacc[cb]);
-      }
+      for (int cb = 0; cb < CB; ++cb)
+        acc.o[cb] = mfma_bf16_32x32x16(lds_load<v8bf>(tb.vt, c.off_v[p] + cb * 4096), pop, acc.o[cb]);
+      if (XONES) acc.ones[0] = mfma_bf16_32x32x16(ones_op, pop, acc.ones[0]);
     }
   }
 }
 
-// One key tile: start the copies of the next tile into `nxt`, compute the
-// current one from `cur`, expand the next keys into `nxt`, wait, barrier.
-template <bool FAST, int NCH, int CB, int BIAS>
-__device__ __forceinline__ void pass_step(const Ctx<NCH>& c, const TileBuf<NCH, CB>& cur, TileBuf<NCH, CB>& nxt,
-                                          int kt, int nkt, Prefetch<NCH>& pf, v16f (&oacc)[CB], float& lsum,
-                                          float& mrow) {
-  const FwdArgs& a = *c.a;
-  const int k0 = kt * kBN;
-  const bool more = kt + 1 < nkt;
-  if (more) {
-    copy_tile_async<NCH, CB, BIAS>(c, nxt, k0 + kBN);
-    load_keys<NCH, BIAS>(c, k0 + kBN, pf);
-  }
-  if (k0 + kBN <= a.N)
-    compute_tile<FAST, false, NCH, CB, BIAS>(c, cur, k0, oacc, lsum, mrow);
+// ------------------------------------------------- pipelined fast path ----
+// P.V of a finished 32-key block waits in registers (bf16 P and its V^T
+// operands) and runs while the next block's logits are formed: each of its
+// 2 (CB + XONES) matrix instructions is followed by a quarter of the next
+// block's vector work, so the matrix cores and the vector ALUs of a SIMD
+// overlap even within one wave, and the V^T operands no longer tie the
+// block to its LDS buffer (the pipeline runs across tile barriers).
+template <int CB>
+struct PendingPV {
+  uint32_t pk[8];     // bf16 P, 16 keys x 2 steps
+  v8bf vop[2][CB];    // V^T operands of the two 16-key steps
+};
+
+template <int CB, bool XONES>
+__device__ __forceinline__ void pv_mfma(int i, const PendingPV<CB>& pp, Acc<CB, XONES>& acc, const v8bf& ones_op) {
+  constexpr int per = CB + (XONES ? 1 : 0);
+  const int half = i / per, cb = i % per;
+  const v4u pw = {pp.pk[4 * half], pp.pk[4 * half + 1], pp.pk[4 * half + 2], pp.pk[4 * half + 3]};
+  const v8bf pop = __builtin_bit_cast(v8bf, pw);
+  if (cb < CB)
+    acc.o[cb] = mfma_bf16_32x32x16(pp.vop[half][cb], pop, acc.o[cb]);
   else
-    compute_tile<FAST, true, NCH, CB, BIAS>(c, cur, k0, oacc, lsum, mrow);
-  if (more) store_keys<NCH, CB, BIAS>(c, nxt, pf);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+    acc.ones[0] = mfma_bf16_32x32x16(ones_op, pop, acc.ones[0]);
 }
 
-// One pass over all keys.  Returns the lane's partial row sum; O^T in oacc.
-template <bool FAST, int NCH, int CB, int BIAS>
-__device__ __forceinline__ float run_pass(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb0, TileBuf<NCH, CB>& tb1,
-                                          v16f (&oacc)[CB]) {
+// Block `blk` of tile `tb`: its QK, then the pending block's P.V interleaved
+// with this block's logits / exp2 / bf16 packing; this block becomes pending.
+template <bool MASK, bool HAVE_PENDING, int NCH, int CB, bool XONES, int BIAS>
+__device__ __forceinline__ void pipelined_block(const Ctx<NCH>& c, const TileBuf<NCH, CB>& tb, const KeyPos& kp,
+                                                int blk, PendingPV<CB>& pp, Acc<CB, XONES>& acc,
+                                                const v8bf& ones_op) {
+  const FwdArgs& a = *c.a;
+  constexpr int kMf = 2 * (CB + (XONES ? 1 : 0));
+  v16f s = v16f{};
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+    s = mfma_signs_32x32x64(lds_load<v4i>(tb.k, c.off_k + ch * 2048 + blk * 1024), c.qop[ch], s);
+  int woff = 0;
+  if (BIAS == kBiasRows) woff = c.off_win + (kp.ky[1] - kp.ky[blk]) * 16 * a.Lpad + kp.kx[blk] * 4;
+  uint32_t pk[8];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (HAVE_PENDING) {
+      // this group's share of the pending block's matrix instructions
+#pragma unroll
+      for (int i = b * kMf / 4; i < (b + 1) * kMf / 4; ++i) pv_mfma<CB, XONES>(i, pp, acc, ones_op);
+    }
+    const float4 ak = lds_load<float4>(tb.ak, c.off_ak + (blk * 32 + 8 * b) * 4);
+    float x0 = s[4 * b] * ak.x, x1 = s[4 * b + 1] * ak.y, x2 = s[4 * b + 2] * ak.z, x3 = s[4 * b + 3] * ak.w;
+    if (BIAS == kBiasRows) {
+      const float4 bias = lds_load<float4>(tb.win, woff + 32 * b);
+      x0 = fmaf(x0, c.aq, bias.x);
+      x1 = fmaf(x1, c.aq, bias.y);
+      x2 = fmaf(x2, c.aq, bias.z);
+      x3 = fmaf(x3, c.aq, bias.w);
+    } else if (BIAS == kBiasTable) {
+      const int4 g = lds_load<int4>(tb.gk, c.off_ak + (blk * 32 + 8 * b) * 4);
+      x0 = fmaf(x0, c.aq, c.table[c.fidx - g.x]);
+      x1 = fmaf(x1, c.aq, c.table[c.fidx - g.y]);
+      x2 = fmaf(x2, c.aq, c.table[c.fidx - g.z]);
+      x3 = fmaf(x3, c.aq, c.table[c.fidx - g.w]);
+    } else {
+      x0 *= c.aq;
+      x1 *= c.aq;
+      x2 *= c.aq;
+      x3 *= c.aq;
+    }
+    if (MASK) {
+      const int key = kp.k0 + blk * 32 + 8 * b + 4 * c.lh;
+      if (key + 0 >= a.N) x0 = -INFINITY;
+      if (key + 1 >= a.N) x1 = -INFINITY;
+      if (key + 2 >= a.N) x2 = -INFINITY;
+      if (key + 3 >= a.N) x3 = -INFINITY;
+    }
+    pk[2 * b] = pack_bf16x2(fast_exp2(x0), fast_exp2(x1));
+    pk[2 * b + 1] = pack_bf16x2(fast_exp2(x2), fast_exp2(x3));
+  }
+  // this block becomes pending: P and its V^T operands
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pp.pk[j] = pk[j];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      pp.vop[half][cb] = lds_load<v8bf>(tb.vt, c.off_v[2 * blk + half] + cb * 4096);
+}
+
+// Pipelined (offset-free) version of pass_step: tile t's two blocks each
+// overlap the previous block's P.V.
+template <bool FIRST, int NCH, int CB, bool XONES, int BIAS>
+__device__ __forceinline__ void fast_step(const Ctx<NCH>& c, const TileBuf<NCH, CB>& cur, TileBuf<NCH, CB>& nxt,
+                                          int t, int nkt, KeyPos& kp, Acc<CB, XONES>& acc, PendingPV<CB>& pp,
+                                          const v8bf& ones_op) {
+  const FwdArgs& a = *c.a;
+  const bool more = t + 1 < nkt;
+  const KeyPos kn = next_keys(kp, a.gw);
+  uint32_t kw[2] = {0u, 0u};
+  int gk = 0;
+  if (more) copy_tile_async<NCH, CB, BIAS>(c, nxt, t + 1, kn, kw, gk);
+  if (BIAS == kBiasRows || kp.k0 + kBN <= a.N) {
+    pipelined_block<false, !FIRST, NCH, CB, XONES, BIAS>(c, cur, kp, 0, pp, acc, ones_op);
+    pipelined_block<false, true, NCH, CB, XONES, BIAS>(c, cur, kp, 1, pp, acc, ones_op);
+  } else {
+    pipelined_block<true, !FIRST, NCH, CB, XONES, BIAS>(c, cur, kp, 0, pp, acc, ones_op);
+    pipelined_block<true, true, NCH, CB, XONES, BIAS>(c, cur, kp, 1, pp, acc, ones_op);
+  }
+  if (more) store_keys<NCH, CB, BIAS>(c, nxt, kw, gk);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  kp = kn;
+}
+
+template <int NCH, int CB, bool XONES, int BIAS>
+__device__ __forceinline__ void run_fast_pass(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb0, TileBuf<NCH, CB>& tb1,
+                                              Acc<CB, XONES>& acc, const v8bf& ones_op) {
   const FwdArgs& a = *c.a;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) oacc[cb] = v16f{};
-  float lsum = 0.0f, mrow = -INFINITY;
-  Prefetch<NCH> pf;
-  copy_tile_async<NCH, CB, BIAS>(c, tb0, 0);
-  load_keys<NCH, BIAS>(c, 0, pf);
-  store_keys<NCH, CB, BIAS>(c, tb0, pf);
+  for (int cb = 0; cb < CB; ++cb) acc.o[cb] = v16f{};
+  acc.ones[0] = v16f{};
+  KeyPos kp;
+  kp.k0 = 0;
+  kp.ky[0] = 0;
+  kp.kx[0] = 0;
+  kp.ky[1] = (BIAS == kBiasRows && a.gw == 32) ? 1 : 0;
+  kp.kx[1] = (BIAS == kBiasRows && a.gw == 32) ? 0 : 32;
+  {
+    uint32_t kw[2] = {0u, 0u};
+    int gk = 0;
+    copy_tile_async<NCH, CB, BIAS>(c, tb0, 0, kp, kw, gk);
+    store_keys<NCH, CB, BIAS>(c, tb0, kw, gk);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int nkt = (a.N + kBN - 1) / kBN;
-  for (int kt = 0; kt < nkt; kt += 2) {
-    pass_step<FAST, NCH, CB, BIAS>(c, tb0, tb1, kt, nkt, pf, oacc, lsum, mrow);
-    if (kt + 1 < nkt) pass_step<FAST, NCH, CB, BIAS>(c, tb1, tb0, kt + 1, nkt, pf, oacc, lsum, mrow);
+  PendingPV<CB> pp;
+  fast_step<true, NCH, CB, XONES, BIAS>(c, tb0, tb1, 0, nkt, kp, acc, pp, ones_op);
+  for (int t = 1; t < nkt; t += 2) {
+    fast_step<false, NCH, CB, XONES, BIAS>(c, tb1, tb0, t, nkt, kp, acc, pp, ones_op);
+    if (t + 1 < nkt) fast_step<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, t + 1, nkt, kp, acc, pp, ones_op);
   }
-  return lsum;
+  // drain: the last block's P.V
+#pragma unroll
+  for (int i = 0; i < 2 * (CB + (XONES ? 1 : 0)); ++i) pv_mfma<CB, XONES>(i, pp, acc, ones_op);
 }
 
-// Waves per SIMD the register budget is sized for.
-template <int CB>
+// One key tile: start the copies of tile t+1 into `nxt`, compute tile t from
+// `cur`, expand the next keys into `nxt`, wait, barrier.
+template <bool FAST, int NCH, int CB, bool XONES, int BIAS>
+__device__ __forceinline__ void pass_step(const Ctx<NCH>& c, const TileBuf<NCH, CB>& cur, TileBuf<NCH, CB>& nxt,
+                                          int t, int nkt, KeyPos& kp, Acc<CB, XONES>& acc, float& mrow,
+                                          const v8bf& ones_op) {
+  const FwdArgs& a = *c.a;
+  const bool more = t + 1 < nkt;
+  const KeyPos kn = next_keys(kp, a.gw);
+  uint32_t kw[2] = {0u, 0u};
+  int gk = 0;
+  if (more) copy_tile_async<NCH, CB, BIAS>(c, nxt, t + 1, kn, kw, gk);
+  // With table rows, keys past N meet -inf padding rows: no mask needed.
+  if (BIAS == kBiasRows || kp.k0 + kBN <= a.N)
+    compute_tile<FAST, false, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow, ones_op);
+  else
+    compute_tile<FAST, true, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow, ones_op);
+  if (more) store_keys<NCH, CB, BIAS>(c, nxt, kw, gk);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  kp = kn;
+}
+
+// One pass over all keys; O^T (and the row sums) accumulate in acc.
+template <bool FAST, int NCH, int CB, bool XONES, int BIAS>
+__device__ __forceinline__ void run_pass(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb0, TileBuf<NCH, CB>& tb1,
+                                         Acc<CB, XONES>& acc, const v8bf& ones_op) {
+  const FwdArgs& a = *c.a;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) acc.o[cb] = v16f{};
+  acc.ones[0] = v16f{};
+  float mrow = -INFINITY;
+  KeyPos kp;
+  kp.k0 = 0;
+  kp.ky[0] = 0;
+  kp.kx[0] = 0;
+  kp.ky[1] = (BIAS == kBiasRows && a.gw == 32) ? 1 : 0;
+  kp.kx[1] = (BIAS == kBiasRows && a.gw == 32) ? 0 : 32;
+  {
+    uint32_t kw[2] = {0u, 0u};
+    int gk = 0;
+    copy_tile_async<NCH, CB, BIAS>(c, tb0, 0, kp, kw, gk);
+    store_keys<NCH, CB, BIAS>(c, tb0, kw, gk);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int nkt = (a.N + kBN - 1) / kBN;
+  for (int t = 0; t < nkt; t += 2) {
+    pass_step<FAST, NCH, CB, XONES, BIAS>(c, tb0, tb1, t, nkt, kp, acc, mrow, ones_op);
+    if (t + 1 < nkt) pass_step<FAST, NCH, CB, XONES, BIAS>(c, tb1, tb0, t + 1, nkt, kp, acc, mrow, ones_op);
+  }
+}
+
+// Waves per SIMD the register budget is sized for (accumulator blocks).
+template <int NB>
 struct Occupancy {
-  static constexpr int kWaves = CB <= 2 ? 3 : (CB <= 4 ? 2 : 1);
+  static constexpr int kWaves = NB <= 3 ? 3 : (NB <= 5 ? 2 : 1);
 };
 
-template <int NCH, int CB, int BIAS>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<CB>::kWaves)))
+template <int NCH, int CB, bool XONES, int BIAS>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<CB + XONES>::kWaves)))
 attn_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB> tb0;
   __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB> tb1;
@@ -318,7 +493,6 @@ attn_fwd_kernel(FwdArgs a) {
   Ctx<NCH> c;
   c.a = &a;
   c.table = s_table;
-  c.win_floats = (BIAS == kBiasRows) ? a.win_rows * 4 * a.Lpad : 0;
   c.tid = threadIdx.x;
   c.lane = c.tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
@@ -344,14 +518,56 @@ attn_fwd_kernel(FwdArgs a) {
     c.qop[ch] = expand_signs_fp4(w, fp4_magnitude(word_valid(a.d, word)));
   }
   c.aq = a.alpha_q[c.tokbase + c.qi] * a.qscale;
-  c.yq = c.xq = c.bsel = c.yq_lo = c.fidx = 0;
+
+  // ---- per-lane LDS offsets ------------------------------------------------
+  c.off_k = (c.li * 2 + c.lh) * 16;
+  c.off_ak = c.lh * 16;
+  {
+    const int sw = (c.li >> 1) & 7;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) c.off_v[p] = c.li * 128 + (((2 * p + c.lh) ^ sw) << 4);
+  }
+  c.yq = c.xq = c.yq_lo = c.fidx = c.off_win = 0;
   if (BIAS != kBiasNone) {
     c.yq = c.qi / a.gw;
     c.xq = c.qi - c.yq * a.gw;
   }
   if (BIAS == kBiasRows) {
-    c.bsel = (a.gw - 1 - c.xq) & 3;
+    // bias(i, j) = R[dy][gw-1-xi+xj], read from copy s = (gw-1-xi) & 3 at an
+    // aligned float offset, in window row (yq - yq_lo) + (yk_hi - yk).
     c.yq_lo = c.q0 / a.gw;
+    const int bsel = (a.gw - 1 - c.xq) & 3;
+    c.off_win = (((c.yq - c.yq_lo) * 4 + bsel) * a.Lpad + (a.gw - 1 - c.xq + 4 * c.lh - bsel)) * 4;
+  }
+
+  // ---- global sources of the tile copies -----------------------------------
+  constexpr int kVtBytes = 32 * CB * kBN * 2;
+  c.vbase = reinterpret_cast<const char*>(a.vt) + static_cast<int64_t>(c.bh) * (a.Npad / kBN) * kVtBytes;
+  c.voff = c.wave * 1024 + c.lane * 16;
+  c.kbase = reinterpret_cast<const char*>(a.kbits + c.tokbase * a.W);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = c.tid + j * kThreads;
+    c.kword[j] = -1;
+    c.koff[j] = 0;
+    if (e < NCH * kBN * 2) {
+      const int word = 2 * (e / (kBN * 2)) + (e & 1), key = (e >> 1) & (kBN - 1);
+      c.kword[j] = word;
+      c.koff[j] = (key * a.W + (word < a.W ? word : 0)) * 4;
+    }
+  }
+  c.bbase = nullptr;
+  c.bvalid[0] = c.bvalid[1] = false;
+  c.boff[0] = c.boff[1] = 0;
+  if (BIAS == kBiasRows) {
+    const int rows_p = 2 * a.gh - 1 + 2 * kBiasPadRows;
+    c.bbase = reinterpret_cast<const char*>(a.bias4 + static_cast<int64_t>(c.head) * rows_p * 4 * a.Lpad);
+    const int bytes = a.win_rows * 16 * a.Lpad;  // <= 8 KiB: two pieces per wave
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      c.boff[j] = (c.wave + 4 * j) * 1024 + c.lane * 16;
+      c.bvalid[j] = c.boff[j] < bytes;
+    }
   }
 
   // ---- logit bound M (log2 units) ------------------------------------------
@@ -379,16 +595,30 @@ attn_fwd_kernel(FwdArgs a) {
   const float qm = fmaxf(a.qmax_blk[qb], a.qmax_blk[qb + 1]);
   const float M = a.qscale * qm * km * static_cast<float>(a.d) + bm;
 
-  v16f oacc[CB];
-  float lsum;
+  // A operand of the extra row-sum block: rows 0 and 4 are ones.
+  const uint32_t one2 = (c.li == 0 || c.li == 4) ? 0x3F803F80u : 0u;
+  const v4u ones4 = {one2, one2, one2, one2};
+  const v8bf ones_op = __builtin_bit_cast(v8bf, ones4);
+
+  Acc<CB, XONES> acc;
   if (M <= kFastMaxLogit)  // false for NaN as well
-    lsum = sum_halves(run_pass<true, NCH, CB, BIAS>(c, tb0, tb1, oacc));
+    run_fast_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc, ones_op);
   else
-    lsum = sum_halves(run_pass<false, NCH, CB, BIAS>(c, tb0, tb1, oacc));
+    run_pass<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, acc, ones_op);
 
   // ---- epilogue: O = O^T / l, bf16, one query per lane --------------------
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) pin_uniform(oacc[cb]);
+  for (int cb = 0; cb < CB; ++cb) pin_uniform(acc.o[cb]);
+  float lsum;
+  if (XONES) {
+    pin_uniform(acc.ones[0]);
+    lsum = acc.ones[0][0];
+  } else {
+    // rows d and d+4 of the last block: register 4 * ((d % 32) / 8)
+    const int b1 = (a.d & 31) >> 3;
+    const v16f& last = acc.o[CB - 1];
+    lsum = b1 == 1 ? last[4] : (b1 == 2 ? last[8] : last[12]);
+  }
   const float inv = 1.0f / lsum;
   if (c.qi < a.N) {
     uint16_t* orow = a.o + (static_cast<int64_t>(c.bh) * a.N + c.qi) * a.d;
@@ -399,8 +629,8 @@ attn_fwd_kernel(FwdArgs a) {
         const int c0 = cb * 32 + 8 * b + 4 * c.lh;
         if (c0 < a.d) {
           uint2 w;
-          w.x = pack_bf16x2(oacc[cb][4 * b + 0] * inv, oacc[cb][4 * b + 1] * inv);
-          w.y = pack_bf16x2(oacc[cb][4 * b + 2] * inv, oacc[cb][4 * b + 3] * inv);
+          w.x = pack_bf16x2(acc.o[cb][4 * b + 0] * inv, acc.o[cb][4 * b + 1] * inv);
+          w.y = pack_bf16x2(acc.o[cb][4 * b + 2] * inv, acc.o[cb][4 * b + 3] * inv);
           *reinterpret_cast<uint2*>(orow + c0) = w;
         }
       }
@@ -427,20 +657,20 @@ int fwd_static_lds(int dpad) {
   }
 }
 
-template <int NCH, int CB>
+template <int NCH, int CB, bool XONES>
 static int launch_nc(const FwdArgs& a, int mode, void* stream) {
   const int lds = fwd_dynamic_lds(a, mode);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(a.nwg), block(kThreads);
   switch (mode) {
     case kBiasNone:
-      hipLaunchKernelGGL((attn_fwd_kernel<NCH, CB, kBiasNone>), grid, block, lds, s, a);
+      hipLaunchKernelGGL((attn_fwd_kernel<NCH, CB, XONES, kBiasNone>), grid, block, lds, s, a);
       break;
     case kBiasRows:
-      hipLaunchKernelGGL((attn_fwd_kernel<NCH, CB, kBiasRows>), grid, block, lds, s, a);
+      hipLaunchKernelGGL((attn_fwd_kernel<NCH, CB, XONES, kBiasRows>), grid, block, lds, s, a);
       break;
     default:
-      hipLaunchKernelGGL((attn_fwd_kernel<NCH, CB, kBiasTable>), grid, block, lds, s, a);
+      hipLaunchKernelGGL((attn_fwd_kernel<NCH, CB, XONES, kBiasTable>), grid, block, lds, s, a);
       break;
   }
   return static_cast<int>(hipGetLastError());
@@ -448,15 +678,24 @@ static int launch_nc(const FwdArgs& a, int mode, void* stream) {
 
 int launch_attention(const FwdArgs& a, int mode, void* stream) {
   const int cb = a.dpad / 32;
-  switch (cb) {
-    case 1: return launch_nc<1, 1>(a, mode, stream);
-    case 2: return launch_nc<1, 2>(a, mode, stream);
-    case 3: return launch_nc<2, 3>(a, mode, stream);
-    case 4: return launch_nc<2, 4>(a, mode, stream);
-    case 5: return launch_nc<3, 5>(a, mode, stream);
-    case 6: return launch_nc<3, 6>(a, mode, stream);
-    case 7: return launch_nc<4, 7>(a, mode, stream);
-    case 8: return launch_nc<4, 8>(a, mode, stream);
+  const bool xones = (a.d % 32) == 0;
+  switch (cb * 2 + (xones ? 1 : 0)) {
+    case 2: return launch_nc<1, 1, false>(a, mode, stream);
+    case 3: return launch_nc<1, 1, true>(a, mode, stream);
+    case 4: return launch_nc<1, 2, false>(a, mode, stream);
+    case 5: return launch_nc<1, 2, true>(a, mode, stream);
+    case 6: return launch_nc<2, 3, false>(a, mode, stream);
+    case 7: return launch_nc<2, 3, true>(a, mode, stream);
+    case 8: return launch_nc<2, 4, false>(a, mode, stream);
+    case 9: return launch_nc<2, 4, true>(a, mode, stream);
+    case 10: return launch_nc<3, 5, false>(a, mode, stream);
+    case 11: return launch_nc<3, 5, true>(a, mode, stream);
+    case 12: return launch_nc<3, 6, false>(a, mode, stream);
+    case 13: return launch_nc<3, 6, true>(a, mode, stream);
+    case 14: return launch_nc<4, 7, false>(a, mode, stream);
+    case 15: return launch_nc<4, 7, true>(a, mode, stream);
+    case 16: return launch_nc<4, 8, false>(a, mode, stream);
+    case 17: return launch_nc<4, 8, true>(a, mode, stream);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
 }

@@ -19,9 +19,9 @@ constexpr int kVtStride = 72;
 
 // Zero rows on each side of the float32 bias rows in the workspace.
 constexpr int kBiasPadRows = 8;
-// Largest bias window (floats) the table-row path stages per key tile: two
-// table rows of a 128-wide grid, or one of a 256-wide grid.
-constexpr int kMaxWindowFloats = 2304;
+// Largest bias window (floats) the table-row path stages per key tile
+// (8 KiB: two 1 KiB copy pieces per wave); covers grids up to 128 wide.
+constexpr int kMaxWindowFloats = 2048;
 
 // Largest LDS footprint of a prologue block (vt tile at d = 256).
 constexpr int kPrologueSmem = 64 * (256 + 8) * 2;

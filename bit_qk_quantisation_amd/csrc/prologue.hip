@@ -104,8 +104,9 @@ __device__ void pack_block(const PackJob& job, int64_t blk, unsigned char* smem)
 
 // ------------------------------------------------------------------ vt ----
 // One block = one (b,h) and 64 keys.  Loads the 64 x d tile row-major into
-// LDS, then writes the tile's dpad rows of 64 keys (zeros past N and past d)
-// as one contiguous dpad x 128-byte block, in the order the fused kernel
+// LDS, then writes the tile's dpad rows of 64 keys (zeros past N and past d,
+// except rows d and d+4 when d is not a multiple of 32: those hold 1.0 for
+// every key < N) as one contiguous dpad x 128-byte block, in the order the fused kernel
 // copies straight into LDS:
 //   * keys are permuted inside each group of 16 into the P.V slot order
 //     (slots 8h..8h+3 = keys 4h..4h+3, slots 8h+4..8h+7 = keys 8+4h..8+4h+3);
@@ -142,6 +143,10 @@ __device__ void vt_block(const VtJob& job, int64_t blk, unsigned char* smem) {
       if (c < d) {
         lo = t[vt_slot_key(8 * q + 2 * k) * stride + c];
         hi = t[vt_slot_key(8 * q + 2 * k + 1) * stride + c];
+      } else if (c == d || c == d + 4) {
+        // rows of ones: the P.V product then also yields the row sums of P
+        lo = (n0 + vt_slot_key(8 * q + 2 * k) < job.N) ? 0x3F80u : 0u;
+        hi = (n0 + vt_slot_key(8 * q + 2 * k + 1) < job.N) ? 0x3F80u : 0u;
       }
       w[k] = lo | (hi << 16);
     }
@@ -152,9 +157,8 @@ __device__ void vt_block(const VtJob& job, int64_t blk, unsigned char* smem) {
 
 // ---------------------------------------------------------------- bias ----
 // One block = one row of the padded table: rows kBiasPadRows..kBiasPadRows +
-// 2gh-2 hold the table rows dy = 0..2gh-2, the kBiasPadRows rows on each side
-// are zero (the fused kernel's windows may reach past the grid for padded
-// tokens).  Each row is 4 shifted copies of Lpad floats:
+// 2gh-2 hold the table rows dy = 0..2gh-2; the kBiasPadRows rows on each side
+// are -inf (the fused kernel's windows reach them only for padded tokens).  Each row is 4 shifted copies of Lpad floats:
 // R[u] = log2e * T[h, dy, 2gw-2-u] for 0 <= u <= 2gw-2 (else 0), and copy s
 // holds C_s[v] = R[v+s].
 __device__ void bias_block(const BiasJob& job, int64_t blk) {
@@ -169,10 +173,12 @@ __device__ void bias_block(const BiasJob& job, int64_t blk) {
   for (int e = threadIdx.x; e < 4 * job.Lpad; e += blockDim.x) {
     const int s = e / job.Lpad, v = e - s * job.Lpad;
     const int u = v + s;
-    float val = 0.0f;
+    // Padding rows are -inf: the only (query, key) pairs that reach them
+    // involve a padded token, and a padded key must get probability 0.
+    float val = inside ? 0.0f : -INFINITY;
     if (inside && u <= cols - 1) val = kLog2e * bf16_to_f32(trow[cols - 1 - u]);
     out[e] = val;
-    m = fmaxf(m, fabsf(val));
+    if (inside) m = fmaxf(m, fabsf(val));
   }
   // row maximum of |entry| * log2e, for the logit bound
   __shared__ float wmax[kThreads / 64];

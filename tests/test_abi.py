@@ -58,7 +58,8 @@ def expected_workspace(B, H, N, d, gh=0, gw=0):
     scale arrays, two arrays of per-64-token scale maxima and V^T, per head
     padded to a multiple of 128 tokens, each section 256-byte aligned; plus,
     for a grid width that is a multiple of 32, the float32 bias rows (4
-    shifted copies per row, 8 zero rows on each side) and their maxima."""
+    shifted copies per row, each padded to 16 mod 64 floats, 8 padding rows
+    on each side) and their maxima."""
     npad = _round(N, 128)
     W = (d + 31) // 32
     dpad = 32 * W
@@ -66,6 +67,8 @@ def expected_workspace(B, H, N, d, gh=0, gw=0):
     secs.append(B * H * dpad * npad * 2)
     if gh and gw % 32 == 0:
         lpad = _round(2 * gw - 1 + 3, 4)
+        while lpad % 64 != 16:
+            lpad += 4
         secs.append(H * (2 * gh - 1 + 16) * 4 * lpad * 4)
         secs.append(H * (2 * gh - 1) * 4)
     return sum(_round(s, 256) for s in secs)
