@@ -81,13 +81,14 @@ struct Ctx {
   int yq, xq, yq_lo, fidx;
   // Asynchronous tile copies: wave-uniform bases (scalar registers) plus
   // per-lane 32-bit byte offsets.
-  const char* vbase;   // V^T tiles of this (b, h)
-  int voff;            // this lane's byte in a V^T tile (first 1 KiB piece)
-  const char* kbase;   // packed key words of this (b, h)
-  int koff[2];         // this thread's key words (bytes, tile 0)
+  rsrc_t vrs;          // V^T tiles of this (b, h)
+  uint32_t voff;       // this lane's byte in a V^T tile (first 1 KiB piece)
+  rsrc_t krs;          // packed key words of this (b, h)
+  uint32_t koff[2];    // this thread's key words (bytes, tile 0; out of range: none)
   int kword[2];        // their word index (-1: no entry for the thread)
-  const char* bbase;   // bias rows of this head (table-row mode)
-  int boff[2];         // this lane's byte in its 1 KiB window pieces
+  rsrc_t ars;          // key scales of this (b, h)
+  rsrc_t brs;          // bias rows of this head (table-row mode)
+  uint32_t boff[2];    // this lane's byte in its 1 KiB window pieces
   bool bvalid[2];      // whether that byte lies inside the window
 };
 
@@ -100,11 +101,15 @@ struct KeyPos {
 __device__ __forceinline__ KeyPos next_keys(const KeyPos& p, int gw) {
   KeyPos n;
   n.k0 = p.k0 + kBN;
-  // blocks are 32-aligned and gw % 32 == 0: a block never straddles rows
-  n.ky[0] = p.ky[1] + (p.kx[1] + 32 == gw ? 1 : 0);
-  n.kx[0] = p.kx[1] + 32 == gw ? 0 : p.kx[1] + 32;
-  n.ky[1] = n.ky[0] + (n.kx[0] + 32 == gw ? 1 : 0);
-  n.kx[1] = n.kx[0] + 32 == gw ? 0 : n.kx[0] + 32;
+  // Blocks are 32-aligned and gw % 32 == 0: a block never straddles rows.
+  // The wrap flag is formed with a shift, which keeps it in scalar registers.
+  int x = p.kx[1] + 32, w = static_cast<int>(static_cast<uint32_t>(gw - 1 - x) >> 31);
+  n.ky[0] = p.ky[1] + w;
+  n.kx[0] = x - w * gw;
+  x = n.kx[0] + 32;
+  w = static_cast<int>(static_cast<uint32_t>(gw - 1 - x) >> 31);
+  n.ky[1] = n.ky[0] + w;
+  n.kx[1] = x - w * gw;
   return n;
 }
 
@@ -136,36 +141,25 @@ __device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TileBuf<NCH, 
                                                 uint32_t (&kw)[2], int& gk) {
   const FwdArgs& a = *c.a;
   // The key words first: vmcnt counts in issue order, so waiting for them
-  // later leaves the LDS copies below in flight.
-  const char* ksrc = c.kbase + static_cast<int64_t>(kp.k0) * a.W * 4;
+  // later leaves the LDS copies below in flight.  Threads without a word
+  // carry an out-of-range offset and read 0.
+  const uint32_t ks = static_cast<uint32_t>(kp.k0 * a.W * 4);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    kw[j] = 0u;
-    if (j * kThreads < NCH * kBN * 2 && c.kword[j] >= 0 && c.kword[j] < a.W)
-      kw[j] = *reinterpret_cast<const uint32_t*>(ksrc + static_cast<uint32_t>(c.koff[j]));
-  }
+  for (int j = 0; j < 2; ++j) kw[j] = (j * kThreads < NCH * kBN * 2) ? buffer_u32(c.krs, c.koff[j], ks) : 0u;
   constexpr int kVtBytes = 32 * CB * kBN * 2;
-  const char* vsrc = c.vbase + static_cast<int64_t>(t) * kVtBytes;
   char* vdst = reinterpret_cast<char*>(&tb.vt[0]);
 #pragma unroll
   for (int j = 0; j < kVtBytes / 4096; ++j)
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(vsrc + static_cast<uint32_t>(c.voff + j * 4096)),
-                                     static_cast<void*>(vdst + (c.wave + 4 * j) * 1024), 16, 0, 0);
-  if (c.wave == 0) {
-    const char* asrc = reinterpret_cast<const char*>(a.alpha_k + c.tokbase + kp.k0);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(asrc + static_cast<uint32_t>(c.lane * 4)),
-                                     static_cast<void*>(&tb.ak[0]), 4, 0, 0);
-  }
+    dma16(c.vrs, vdst + (c.wave + 4 * j) * 1024, c.voff, static_cast<uint32_t>(t * kVtBytes + j * 4096));
+  if (c.wave == 0) dma4(c.ars, &tb.ak[0], static_cast<uint32_t>(c.lane * 4), static_cast<uint32_t>(kp.k0 * 4));
   if (BIAS == kBiasRows) {
     // window rows start at dy = yq_lo - yk_hi; yk_hi is the row of block 1
     const int dy0 = c.yq_lo - kp.ky[1] + a.gh - 1 + kBiasPadRows;
-    const char* bsrc = c.bbase + static_cast<int64_t>(dy0) * 16 * a.Lpad;
+    const uint32_t bs = static_cast<uint32_t>(dy0 * 16 * a.Lpad);
     char* bdst = reinterpret_cast<char*>(&tb.win[0]);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      if (c.bvalid[j])
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(bsrc + static_cast<uint32_t>(c.boff[j])),
-                                         static_cast<void*>(bdst + (c.wave + 4 * j) * 1024), 16, 0, 0);
+      if (c.bvalid[j]) dma16(c.brs, bdst + (c.wave + 4 * j) * 1024, c.boff[j], bs);
   }
   if (BIAS == kBiasTable && c.tid < kBN) {
     const int j = (kp.k0 + c.tid < a.N) ? kp.k0 + c.tid : a.N - 1;
@@ -542,31 +536,37 @@ attn_fwd_kernel(FwdArgs a) {
 
   // ---- global sources of the tile copies -----------------------------------
   constexpr int kVtBytes = 32 * CB * kBN * 2;
-  c.vbase = reinterpret_cast<const char*>(a.vt) + static_cast<int64_t>(c.bh) * (a.Npad / kBN) * kVtBytes;
-  c.voff = c.wave * 1024 + c.lane * 16;
-  c.kbase = reinterpret_cast<const char*>(a.kbits + c.tokbase * a.W);
+  // Per-head ranges: every byte of a range lies inside the workspace section
+  // it names, and each range is far below 2^31 bytes.
+  c.vrs = make_rsrc(reinterpret_cast<const char*>(a.vt) + static_cast<int64_t>(c.bh) * (a.Npad / kBN) * kVtBytes,
+                    static_cast<uint32_t>((a.Npad / kBN) * kVtBytes));
+  c.voff = static_cast<uint32_t>(c.wave * 1024 + c.lane * 16);
+  c.krs = make_rsrc(a.kbits + c.tokbase * a.W, static_cast<uint32_t>(a.Npad * a.W * 4));
+  c.ars = make_rsrc(a.alpha_k + c.tokbase, static_cast<uint32_t>(a.Npad * 4));
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int e = c.tid + j * kThreads;
     c.kword[j] = -1;
-    c.koff[j] = 0;
+    c.koff[j] = kOutOfRange;
     if (e < NCH * kBN * 2) {
       const int word = 2 * (e / (kBN * 2)) + (e & 1), key = (e >> 1) & (kBN - 1);
       c.kword[j] = word;
-      c.koff[j] = (key * a.W + (word < a.W ? word : 0)) * 4;
+      if (word < a.W) c.koff[j] = static_cast<uint32_t>((key * a.W + word) * 4);
     }
   }
-  c.bbase = nullptr;
+  c.brs = c.ars;
   c.bvalid[0] = c.bvalid[1] = false;
   c.boff[0] = c.boff[1] = 0;
   if (BIAS == kBiasRows) {
     const int rows_p = 2 * a.gh - 1 + 2 * kBiasPadRows;
-    c.bbase = reinterpret_cast<const char*>(a.bias4 + static_cast<int64_t>(c.head) * rows_p * 4 * a.Lpad);
+    c.brs = make_rsrc(a.bias4 + static_cast<int64_t>(c.head) * rows_p * 4 * a.Lpad,
+                      static_cast<uint32_t>(rows_p * 16 * a.Lpad));
     const int bytes = a.win_rows * 16 * a.Lpad;  // <= 8 KiB: two pieces per wave
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      c.boff[j] = (c.wave + 4 * j) * 1024 + c.lane * 16;
-      c.bvalid[j] = c.boff[j] < bytes;
+      const int off = (c.wave + 4 * j) * 1024 + c.lane * 16;
+      c.boff[j] = static_cast<uint32_t>(off);
+      c.bvalid[j] = off < bytes;
     }
   }
 

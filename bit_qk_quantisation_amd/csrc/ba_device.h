@@ -111,6 +111,44 @@ __device__ __forceinline__ float add_bf16x2(uint32_t pair, float acc) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- raw buffer access -------------------------------------------------------
+// A buffer resource holds a uniform base address and a byte range; loads then
+// take a per-lane 32-bit offset and a uniform (scalar) offset, so no per-lane
+// 64-bit address arithmetic is needed.  A load whose offset falls outside the
+// range returns 0.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw (untyped) buffer, 32-bit elements
+constexpr uint32_t kOutOfRange = 0x80000000u; // an offset past every range used here
+
+// `base` and `bytes` must be the same in every lane of the wave; they are
+// moved to scalar registers here, so the compiler never has to assume
+// otherwise (a resource it takes for per-lane would cost a loop per load).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+  void* u = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, 0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
+                                           kRsrcWord3);
+}
+
+// 16 bytes per lane from the buffer straight into LDS: lane l writes
+// lds[16 l, 16 l + 16).  `lds` must be wave-uniform.
+__device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds), 16,
+                                           voff, soff, 0, 0);
+}
+
+// 4 bytes per lane into LDS: lane l writes lds[4 l, 4 l + 4).
+__device__ __forceinline__ void dma4(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds), 4,
+                                           voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t buffer_u32(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 // MFMA results must be formed while every lane of the wave is active: a
 // matrix instruction mixes data across lanes, and one issued under a partial
 // EXEC mask drops the inactive lanes' rows.  LLVM treats the MFMA intrinsics
