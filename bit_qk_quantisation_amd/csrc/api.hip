@@ -80,7 +80,7 @@ int choose_mode(bool has_bias, int gh, int gw, int64_t N) {
 // Byte offsets of the workspace sections of ba_attention_fwd.
 struct Layout {
   int64_t Npad, W, dpad, Lpad;
-  int64_t qbits, kbits, alpha_q, alpha_k, qmax, kmax, vt, bias4, rowmax, total;
+  int64_t qbits, kop, alpha_q, alpha_k, qmax, kmax, vt, bias4, rowmax, total;
   int mode;
 };
 
@@ -99,7 +99,7 @@ Layout layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int
     return at;
   };
   L.qbits = take(BH * L.Npad * L.W * 4);
-  L.kbits = take(BH * L.Npad * L.W * 4);
+  L.kop = take(BH * L.Npad * ((L.W + 1) / 2) * 32);  // fp4 key operands: 32 B per 64 channels
   L.alpha_q = take(BH * L.Npad * 4);
   L.alpha_k = take(BH * L.Npad * 4);
   L.qmax = take(BH * (L.Npad / 64) * 4);
@@ -155,8 +155,8 @@ ba_status ba_pack_signs(const void* x, int64_t B, int64_t H, int64_t N, int d,
   if (!aligned16(x) || !aligned16(bits) || !aligned16(alpha))
     return fail(BA_ERR_ALIGN, "x, bits and alpha must be 16-byte aligned");
   ba::PrologueArgs p{};
-  p.pack[0] = ba::PackJob{static_cast<const uint16_t*>(x), bits, alpha, nullptr, B * H,
-                          static_cast<int>(N), static_cast<int>(N), d, (d + 31) / 32};
+  p.pack[0] = ba::PackJob{static_cast<const uint16_t*>(x), bits, nullptr, alpha, nullptr, B * H,
+                          static_cast<int>(N), static_cast<int>(N), d, (d + 31) / 32, 0};
   p.npack = 1;
   p.pack_blocks = (B * H * N + 63) / 64;
   if (p.pack_blocks > 0x7fffffff) return fail(BA_ERR_SHAPE, "problem too large");
@@ -232,7 +232,7 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool inputs, co
   ba::FwdArgs& f = plan->f;
   f = ba::FwdArgs{};
   f.qbits = reinterpret_cast<const uint32_t*>(ws + L.qbits);
-  f.kbits = reinterpret_cast<const uint32_t*>(ws + L.kbits);
+  f.kop = reinterpret_cast<const uint32_t*>(ws + L.kop);
   f.alpha_q = reinterpret_cast<const float*>(ws + L.alpha_q);
   f.alpha_k = reinterpret_cast<const float*>(ws + L.alpha_k);
   f.vt = reinterpret_cast<const uint16_t*>(ws + L.vt);
@@ -263,12 +263,12 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool inputs, co
 
   ba::PrologueArgs& p = plan->p;
   p = ba::PrologueArgs{};
-  p.pack[0] = ba::PackJob{static_cast<const uint16_t*>(q), const_cast<uint32_t*>(f.qbits),
+  p.pack[0] = ba::PackJob{static_cast<const uint16_t*>(q), const_cast<uint32_t*>(f.qbits), nullptr,
                           const_cast<float*>(f.alpha_q), const_cast<float*>(f.qmax_blk), BH,
-                          f.N, f.Npad, d, f.W};
-  p.pack[1] = ba::PackJob{static_cast<const uint16_t*>(k), const_cast<uint32_t*>(f.kbits),
+                          f.N, f.Npad, d, f.W, 0};
+  p.pack[1] = ba::PackJob{static_cast<const uint16_t*>(k), nullptr, const_cast<uint32_t*>(f.kop),
                           const_cast<float*>(f.alpha_k), const_cast<float*>(f.kmax_blk), BH,
-                          f.N, f.Npad, d, f.W};
+                          f.N, f.Npad, d, f.W, (f.W + 1) / 2};
   p.npack = 2;
   p.pack_blocks = (BH * L.Npad + 63) / 64;
   p.vt = ba::VtJob{static_cast<const uint16_t*>(v), const_cast<uint16_t*>(f.vt), BH, f.N, f.Npad, d, f.dpad};

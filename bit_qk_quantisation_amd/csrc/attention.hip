@@ -77,15 +77,15 @@ struct Ctx {
   float aq;            // alpha_q * scale * log2e
   v4i qop[NCH];        // this lane's query operand (fp4 +/-1)
   // LDS byte offsets inside a TileBuf, per lane
-  int off_k, off_ak, off_v[4], off_win;
+  // off_akb: the key scale this lane holds for the row broadcasts;
+  // off_gk: this lane's first grid offset (table mode)
+  int off_k, off_akb, off_gk, off_v[4], off_win;
   int yq, xq, yq_lo, fidx;
   // Asynchronous tile copies: wave-uniform bases (scalar registers) plus
   // per-lane 32-bit byte offsets.
   rsrc_t vrs;          // V^T tiles of this (b, h)
   uint32_t voff;       // this lane's byte in a V^T tile (first 1 KiB piece)
-  rsrc_t krs;          // packed key words of this (b, h)
-  uint32_t koff[2];    // this thread's key words (bytes, tile 0; out of range: none)
-  int kword[2];        // their word index (-1: no entry for the thread)
+  rsrc_t krs;          // fp4 key operand tiles of this (b, h)
   rsrc_t ars;          // key scales of this (b, h)
   rsrc_t brs;          // bias rows of this head (table-row mode)
   uint32_t boff[2];    // this lane's byte in its 1 KiB window pieces
@@ -125,27 +125,33 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return r;
 }
 
+// LDS loads use whole vector types (ext_vector_type), never the HIP float4 /
+// int4 structs: a struct load is split into scalar loads, which the backend
+// re-merges without the alias scope that tells the compiler the load cannot
+// touch the other tile buffer, and it then waits for every copy in flight
+// before the load.
 template <typename T>
 __device__ __forceinline__ T lds_load(const void* base, int byte_off) {
   return *reinterpret_cast<const T*>(__builtin_assume_aligned(static_cast<const char*>(base) + byte_off, 16));
 }
 
 // ---------------------------------------------------------------- staging --
-// Starts the copies of key tile `t` (first key kp.k0) into `tb`: V^T, key
-// scales and (table-row mode) the bias window go straight to LDS
-// (global_load_lds: lane l of a wave fills bytes [16l, 16l+16) of a 1 KiB
-// block, or [4l, 4l+4) of a 256-byte block); the packed key words go to
-// registers.
+// Starts the copies of key tile `t` (first key kp.k0) into `tb`: the fp4 key
+// operands, V^T, key scales and (table-row mode) the bias window go straight
+// to LDS (buffer_load ... lds: lane l of a wave fills bytes [16l, 16l+16) of
+// a 1 KiB block, or [4l, 4l+4) of a 256-byte block).  In table mode the
+// grid offsets of the tile's keys are computed and stored directly: `tb` was
+// last read before the previous barrier.
 template <int NCH, int CB, int BIAS>
-__device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb, int t, const KeyPos& kp,
-                                                uint32_t (&kw)[2], int& gk) {
+__device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb, int t, const KeyPos& kp) {
   const FwdArgs& a = *c.a;
-  // The key words first: vmcnt counts in issue order, so waiting for them
-  // later leaves the LDS copies below in flight.  Threads without a word
-  // carry an out-of-range offset and read 0.
-  const uint32_t ks = static_cast<uint32_t>(kp.k0 * a.W * 4);
+  constexpr int kKBytes = NCH * kBN * 2 * 16;
+  char* kdst = reinterpret_cast<char*>(&tb.k[0]);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) kw[j] = (j * kThreads < NCH * kBN * 2) ? buffer_u32(c.krs, c.koff[j], ks) : 0u;
+  for (int j = 0; j < 2; ++j)
+    if (c.wave + 4 * j < kKBytes / 1024)
+      dma16(c.krs, kdst + (c.wave + 4 * j) * 1024, static_cast<uint32_t>(c.lane * 16),
+            static_cast<uint32_t>(t * kKBytes + (c.wave + 4 * j) * 1024));
   constexpr int kVtBytes = 32 * CB * kBN * 2;
   char* vdst = reinterpret_cast<char*>(&tb.vt[0]);
 #pragma unroll
@@ -164,23 +170,23 @@ __device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TileBuf<NCH, 
   if (BIAS == kBiasTable && c.tid < kBN) {
     const int j = (kp.k0 + c.tid < a.N) ? kp.k0 + c.tid : a.N - 1;
     const int yj = j / a.gw;
-    gk = yj * (2 * a.gw - 1) + (j - yj * a.gw);
+    tb.gk[c.tid] = yj * (2 * a.gw - 1) + (j - yj * a.gw);
   }
-}
-
-// Expands the key words loaded by copy_tile_async into fp4 operands in LDS.
-template <int NCH, int CB, int BIAS>
-__device__ __forceinline__ void store_keys(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb, const uint32_t (&kw)[2], int gk) {
-  const FwdArgs& a = *c.a;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (j * kThreads < NCH * kBN * 2 && c.kword[j] >= 0)
-      tb.k[c.tid + j * kThreads] = expand_signs_fp4(kw[j], fp4_magnitude(word_valid(a.d, c.kword[j])));
-  }
-  if (BIAS == kBiasTable && c.tid < kBN) tb.gk[c.tid] = gk;
 }
 
 // ---------------------------------------------------------------- compute --
+// Byte offset of this lane's bias entries for block `blk` inside the tile's
+// window.  The empty asm makes it one opaque value, so every window read is a
+// single constant offset from it; a longer chain of address arithmetic hides
+// from the compiler which LDS buffer the read touches, and it then waits for
+// the copies into the other buffer before the read.
+template <int NCH>
+__device__ __forceinline__ int window_offset(const Ctx<NCH>& c, const KeyPos& kp, int blk) {
+  int off = c.off_win + (kp.ky[1] - kp.ky[blk]) * 16 * c.a->Lpad + kp.kx[blk] * 4;
+  asm("" : "+v"(off));
+  return off;
+}
+
 // Logits of one 32-key block in base 2:
 //   D * alpha_k * (alpha_q scale log2e) + log2e b
 template <bool MASK, int NCH, int CB, int BIAS>
@@ -188,19 +194,20 @@ __device__ __forceinline__ void block_logits(const Ctx<NCH>& c, const TileBuf<NC
                                              int blk, const v16f& s, float (&sc)[16]) {
   const FwdArgs& a = *c.a;
   int woff = 0;
-  if (BIAS == kBiasRows) woff = c.off_win + (kp.ky[1] - kp.ky[blk]) * 16 * a.Lpad + kp.kx[blk] * 4;
+  if (BIAS == kBiasRows) woff = window_offset(c, kp, blk);
+  const float akv = lds_load<float>(tb.ak, c.off_akb + blk * 128);
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const float4 ak = lds_load<float4>(tb.ak, c.off_ak + (blk * 32 + 8 * b) * 4);
-    const float u0 = s[4 * b] * ak.x, u1 = s[4 * b + 1] * ak.y, u2 = s[4 * b + 2] * ak.z, u3 = s[4 * b + 3] * ak.w;
+    const float u0 = s[4 * b] * row_bcast(akv, 4 * b), u1 = s[4 * b + 1] * row_bcast(akv, 4 * b + 1);
+    const float u2 = s[4 * b + 2] * row_bcast(akv, 4 * b + 2), u3 = s[4 * b + 3] * row_bcast(akv, 4 * b + 3);
     if (BIAS == kBiasRows) {
-      const float4 bias = lds_load<float4>(tb.win, woff + 32 * b);
+      const v4f bias = lds_load<v4f>(tb.win, woff + 32 * b);
       sc[4 * b + 0] = fmaf(u0, c.aq, bias.x);
       sc[4 * b + 1] = fmaf(u1, c.aq, bias.y);
       sc[4 * b + 2] = fmaf(u2, c.aq, bias.z);
       sc[4 * b + 3] = fmaf(u3, c.aq, bias.w);
     } else if (BIAS == kBiasTable) {
-      const int4 g = lds_load<int4>(tb.gk, c.off_ak + (blk * 32 + 8 * b) * 4);
+      const v4i g = lds_load<v4i>(tb.gk, c.off_gk + (blk * 32 + 8 * b) * 4);
       sc[4 * b + 0] = fmaf(u0, c.aq, c.table[c.fidx - g.x]);
       sc[4 * b + 1] = fmaf(u1, c.aq, c.table[c.fidx - g.y]);
       sc[4 * b + 2] = fmaf(u2, c.aq, c.table[c.fidx - g.z]);
@@ -310,7 +317,8 @@ __device__ __forceinline__ void pipelined_block(const Ctx<NCH>& c, const TileBuf
   for (int ch = 0; ch < NCH; ++ch)
     s = mfma_signs_32x32x64(lds_load<v4i>(tb.k, c.off_k + ch * 2048 + blk * 1024), c.qop[ch], s);
   int woff = 0;
-  if (BIAS == kBiasRows) woff = c.off_win + (kp.ky[1] - kp.ky[blk]) * 16 * a.Lpad + kp.kx[blk] * 4;
+  if (BIAS == kBiasRows) woff = window_offset(c, kp, blk);
+  const float akv = lds_load<float>(tb.ak, c.off_akb + blk * 128);
   uint32_t pk[8];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -319,16 +327,16 @@ __device__ __forceinline__ void pipelined_block(const Ctx<NCH>& c, const TileBuf
 #pragma unroll
       for (int i = b * kMf / 4; i < (b + 1) * kMf / 4; ++i) pv_mfma<CB, XONES>(i, pp, acc, ones_op);
     }
-    const float4 ak = lds_load<float4>(tb.ak, c.off_ak + (blk * 32 + 8 * b) * 4);
-    float x0 = s[4 * b] * ak.x, x1 = s[4 * b + 1] * ak.y, x2 = s[4 * b + 2] * ak.z, x3 = s[4 * b + 3] * ak.w;
+    float x0 = s[4 * b] * row_bcast(akv, 4 * b), x1 = s[4 * b + 1] * row_bcast(akv, 4 * b + 1);
+    float x2 = s[4 * b + 2] * row_bcast(akv, 4 * b + 2), x3 = s[4 * b + 3] * row_bcast(akv, 4 * b + 3);
     if (BIAS == kBiasRows) {
-      const float4 bias = lds_load<float4>(tb.win, woff + 32 * b);
+      const v4f bias = lds_load<v4f>(tb.win, woff + 32 * b);
       x0 = fmaf(x0, c.aq, bias.x);
       x1 = fmaf(x1, c.aq, bias.y);
       x2 = fmaf(x2, c.aq, bias.z);
       x3 = fmaf(x3, c.aq, bias.w);
     } else if (BIAS == kBiasTable) {
-      const int4 g = lds_load<int4>(tb.gk, c.off_ak + (blk * 32 + 8 * b) * 4);
+      const v4i g = lds_load<v4i>(tb.gk, c.off_gk + (blk * 32 + 8 * b) * 4);
       x0 = fmaf(x0, c.aq, c.table[c.fidx - g.x]);
       x1 = fmaf(x1, c.aq, c.table[c.fidx - g.y]);
       x2 = fmaf(x2, c.aq, c.table[c.fidx - g.z]);
@@ -368,9 +376,7 @@ __device__ __forceinline__ void fast_step(const Ctx<NCH>& c, const TileBuf<NCH, 
   const FwdArgs& a = *c.a;
   const bool more = t + 1 < nkt;
   const KeyPos kn = next_keys(kp, a.gw);
-  uint32_t kw[2] = {0u, 0u};
-  int gk = 0;
-  if (more) copy_tile_async<NCH, CB, BIAS>(c, nxt, t + 1, kn, kw, gk);
+  if (more) copy_tile_async<NCH, CB, BIAS>(c, nxt, t + 1, kn);
   if (BIAS == kBiasRows || kp.k0 + kBN <= a.N) {
     pipelined_block<false, !FIRST, NCH, CB, XONES, BIAS>(c, cur, kp, 0, pp, acc, ones_op);
     pipelined_block<false, true, NCH, CB, XONES, BIAS>(c, cur, kp, 1, pp, acc, ones_op);
@@ -378,7 +384,6 @@ __device__ __forceinline__ void fast_step(const Ctx<NCH>& c, const TileBuf<NCH, 
     pipelined_block<true, !FIRST, NCH, CB, XONES, BIAS>(c, cur, kp, 0, pp, acc, ones_op);
     pipelined_block<true, true, NCH, CB, XONES, BIAS>(c, cur, kp, 1, pp, acc, ones_op);
   }
-  if (more) store_keys<NCH, CB, BIAS>(c, nxt, kw, gk);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   kp = kn;
@@ -397,12 +402,7 @@ __device__ __forceinline__ void run_fast_pass(const Ctx<NCH>& c, TileBuf<NCH, CB
   kp.kx[0] = 0;
   kp.ky[1] = (BIAS == kBiasRows && a.gw == 32) ? 1 : 0;
   kp.kx[1] = (BIAS == kBiasRows && a.gw == 32) ? 0 : 32;
-  {
-    uint32_t kw[2] = {0u, 0u};
-    int gk = 0;
-    copy_tile_async<NCH, CB, BIAS>(c, tb0, 0, kp, kw, gk);
-    store_keys<NCH, CB, BIAS>(c, tb0, kw, gk);
-  }
+  copy_tile_async<NCH, CB, BIAS>(c, tb0, 0, kp);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int nkt = (a.N + kBN - 1) / kBN;
@@ -426,15 +426,12 @@ __device__ __forceinline__ void pass_step(const Ctx<NCH>& c, const TileBuf<NCH, 
   const FwdArgs& a = *c.a;
   const bool more = t + 1 < nkt;
   const KeyPos kn = next_keys(kp, a.gw);
-  uint32_t kw[2] = {0u, 0u};
-  int gk = 0;
-  if (more) copy_tile_async<NCH, CB, BIAS>(c, nxt, t + 1, kn, kw, gk);
+  if (more) copy_tile_async<NCH, CB, BIAS>(c, nxt, t + 1, kn);
   // With table rows, keys past N meet -inf padding rows: no mask needed.
   if (BIAS == kBiasRows || kp.k0 + kBN <= a.N)
     compute_tile<FAST, false, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow, ones_op);
   else
     compute_tile<FAST, true, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow, ones_op);
-  if (more) store_keys<NCH, CB, BIAS>(c, nxt, kw, gk);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   kp = kn;
@@ -455,12 +452,7 @@ __device__ __forceinline__ void run_pass(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb
   kp.kx[0] = 0;
   kp.ky[1] = (BIAS == kBiasRows && a.gw == 32) ? 1 : 0;
   kp.kx[1] = (BIAS == kBiasRows && a.gw == 32) ? 0 : 32;
-  {
-    uint32_t kw[2] = {0u, 0u};
-    int gk = 0;
-    copy_tile_async<NCH, CB, BIAS>(c, tb0, 0, kp, kw, gk);
-    store_keys<NCH, CB, BIAS>(c, tb0, kw, gk);
-  }
+  copy_tile_async<NCH, CB, BIAS>(c, tb0, 0, kp);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int nkt = (a.N + kBN - 1) / kBN;
@@ -515,7 +507,12 @@ attn_fwd_kernel(FwdArgs a) {
 
   // ---- per-lane LDS offsets ------------------------------------------------
   c.off_k = (c.li * 2 + c.lh) * 16;
-  c.off_ak = c.lh * 16;
+  // Key scales reach the logits by row broadcast: accumulator register r of
+  // every lane in a 16-lane row holds key 8(r/4) + 4(lane/32) + r%4 of the
+  // block, so lane 16 row + r keeps that key's scale and register r reads it
+  // with row_newbcast:r, folded into the multiply.
+  c.off_akb = 4 * (8 * ((c.lane & 15) >> 2) + 4 * c.lh + (c.lane & 3));
+  c.off_gk = c.lh * 16;
   {
     const int sw = (c.li >> 1) & 7;
 #pragma unroll
@@ -541,19 +538,10 @@ attn_fwd_kernel(FwdArgs a) {
   c.vrs = make_rsrc(reinterpret_cast<const char*>(a.vt) + static_cast<int64_t>(c.bh) * (a.Npad / kBN) * kVtBytes,
                     static_cast<uint32_t>((a.Npad / kBN) * kVtBytes));
   c.voff = static_cast<uint32_t>(c.wave * 1024 + c.lane * 16);
-  c.krs = make_rsrc(a.kbits + c.tokbase * a.W, static_cast<uint32_t>(a.Npad * a.W * 4));
+  constexpr int kKBytes = NCH * kBN * 2 * 16;
+  c.krs = make_rsrc(reinterpret_cast<const char*>(a.kop) + static_cast<int64_t>(c.bh) * (a.Npad / kBN) * kKBytes,
+                    static_cast<uint32_t>((a.Npad / kBN) * kKBytes));
   c.ars = make_rsrc(a.alpha_k + c.tokbase, static_cast<uint32_t>(a.Npad * 4));
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int e = c.tid + j * kThreads;
-    c.kword[j] = -1;
-    c.koff[j] = kOutOfRange;
-    if (e < NCH * kBN * 2) {
-      const int word = 2 * (e / (kBN * 2)) + (e & 1), key = (e >> 1) & (kBN - 1);
-      c.kword[j] = word;
-      if (word < a.W) c.koff[j] = static_cast<uint32_t>((key * a.W + word) * 4);
-    }
-  }
   c.brs = c.ars;
   c.bvalid[0] = c.bvalid[1] = false;
   c.boff[0] = c.boff[1] = 0;

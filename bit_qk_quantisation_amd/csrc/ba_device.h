@@ -1,8 +1,8 @@
 // Device-side building blocks for the gfx950 BinaryAttention kernels.
 //
-// Everything here is shared by the fused forward kernel and the QK
-// integer-dot kernel, so the "integer dots" that the checker sees are
-// computed by the very code the fused kernel runs.
+// Everything here is shared by the prologue (which expands the key signs),
+// the fused forward kernel and the QK integer-dot kernel, so the integer dots
+// that ba_qk_int_dot returns come from the very code the fused kernel runs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -83,6 +83,34 @@ __device__ __forceinline__ v16f mfma_signs_32x32x64(v4i a, v4i b, v16f acc) {
 // k-slots 8*(l/32) .. 8*(l/32)+7.
 __device__ __forceinline__ v16f mfma_bf16_32x32x16(v8bf a, v8bf b, v16f acc) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+
+// Value of x in lane n of this lane's row of 16 lanes (DPP row_newbcast:n).
+// n must be a constant once loops are unrolled; the broadcast then folds
+// into the instruction that uses it as a DPP source operand.
+template <int N>
+__device__ __forceinline__ float row_bcast_c(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + N, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_bcast(float x, int n) {
+  switch (n) {
+    case 0: return row_bcast_c<0>(x);
+    case 1: return row_bcast_c<1>(x);
+    case 2: return row_bcast_c<2>(x);
+    case 3: return row_bcast_c<3>(x);
+    case 4: return row_bcast_c<4>(x);
+    case 5: return row_bcast_c<5>(x);
+    case 6: return row_bcast_c<6>(x);
+    case 7: return row_bcast_c<7>(x);
+    case 8: return row_bcast_c<8>(x);
+    case 9: return row_bcast_c<9>(x);
+    case 10: return row_bcast_c<10>(x);
+    case 11: return row_bcast_c<11>(x);
+    case 12: return row_bcast_c<12>(x);
+    case 13: return row_bcast_c<13>(x);
+    case 14: return row_bcast_c<14>(x);
+    default: return row_bcast_c<15>(x);
+  }
 }
 
 // Cross-half reductions for the 32x32 layout: lanes l and l^32 hold the two

@@ -28,11 +28,12 @@ constexpr int kPrologueSmem = 64 * (256 + 8) * 2;
 
 struct PackJob {
   const uint16_t* x;  // bf16 [BH][N][d]
-  uint32_t* bits;     // [BH][Npad][W]
+  uint32_t* bits;     // [BH][Npad][W], or null
+  uint32_t* kop;      // fp4 key operands [BH][Npad/64][NCH][64][2][4], or null
   float* alpha;       // [BH][Npad]
   float* alpha_max;   // [BH*Npad/64]: max alpha of each 64-token block, or null
   int64_t BH;
-  int N, Npad, d, W;
+  int N, Npad, d, W, nch;
 };
 
 struct VtJob {
@@ -65,7 +66,8 @@ enum BiasMode { kBiasNone = 0, kBiasRows = 1, kBiasTable = 2 };
 
 struct FwdArgs {
   const uint32_t* qbits;   // [BH][Npad][W]
-  const uint32_t* kbits;   // [BH][Npad][W]
+  const uint32_t* kop;     // [BH][Npad/64][NCH][64 keys][2][4]: the fp4 +/-1
+                           // operand dwords of each key, in LDS tile order
   const float* alpha_q;    // [BH][Npad]
   const float* alpha_k;    // [BH][Npad]
   const uint16_t* vt;      // [BH][Npad/64][dpad][64] (slot order, swizzled)

@@ -5,7 +5,8 @@
 //   * pack: per token, the scale alpha = mean |x| over d and the packed sign
 //     words (s_i = mu sign(q_i), "Representaciones Binarias Escaladas" of
 //     the BinaryAttention summary).  It covers Q and K, or a single tensor
-//     for ba_pack_signs.
+//     for ba_pack_signs.  For K the signs are written as the fp4 +/-1 MFMA
+//     operand tiles the fused kernel copies straight into LDS.
 //   * vt: a key-major copy of V (V^T, bf16 [BH][dpad][Npad]) whose keys are
 //     permuted inside each group of 16 to match the P.V operand order of the
 //     fused kernel.
@@ -67,10 +68,27 @@ __device__ void pack_block(const PackJob& job, int64_t blk, unsigned char* smem)
   }
   __syncthreads();
 
-  for (int e = threadIdx.x; e < kPackTok * W; e += blockDim.x) {
-    const int tok = e / W;
-    const int64_t t = t0 + tok;
-    if (t < T) job.bits[t * W + (e - tok * W)] = sw[e];
+  if (job.bits != nullptr) {
+    for (int e = threadIdx.x; e < kPackTok * W; e += blockDim.x) {
+      const int tok = e / W;
+      const int64_t t = t0 + tok;
+      if (t < T) job.bits[t * W + (e - tok * W)] = sw[e];
+    }
+  }
+  if (job.kop != nullptr) {
+    // fp4 +/-1 operands of the 64 keys (one key tile: blocks never straddle
+    // tiles, Npad % 64 == 0), in the fused kernel's LDS order
+    // [chunk][key][half][4 dwords]: word 2*chunk + half of the key, expanded
+    // exactly as the fused kernel expands its query words.  Consecutive
+    // threads write consecutive 16-byte pieces.
+    uint4* dst = reinterpret_cast<uint4*>(job.kop) + blk * (kPackTok * 2 * job.nch);
+    for (int e = threadIdx.x; e < kPackTok * 2 * job.nch; e += blockDim.x) {
+      const int ch = e >> 7, key = (e >> 1) & (kPackTok - 1), w = 2 * ch + (e & 1);
+      const uint32_t word = w < W ? sw[key * W + w] : 0u;
+      const v4i op = expand_signs_fp4(word, fp4_magnitude(word_valid(d, w)));
+      dst[e] = make_uint4(static_cast<uint32_t>(op[0]), static_cast<uint32_t>(op[1]),
+                          static_cast<uint32_t>(op[2]), static_cast<uint32_t>(op[3]));
+    }
   }
   if (threadIdx.x < kPackTok) {
     const int tok = threadIdx.x;

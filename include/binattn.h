@@ -89,9 +89,11 @@ int ba_pack_words(int d);
 ba_status ba_pack_signs(const void* x, int64_t B, int64_t H, int64_t N, int d,
                         uint32_t* bits, float* alpha, void* stream);
 
-/* Workspace bytes that ba_attention_fwd needs for this problem: packed Q and
- * K signs and scales, a key-major V^T copy (per head, N padded to a multiple
- * of 128) and, for a bias grid with gw % 32 == 0, the table rows in float32.
+/* Workspace bytes that ba_attention_fwd needs for this problem: the packed Q
+ * signs, the K signs as fp4 +/-1 matrix operands (32 bytes per token and 64
+ * channels), the Q and K scales, a key-major V^T copy (per head, N padded to
+ * a multiple of 128) and, for a bias grid with gw % 32 == 0, the table rows
+ * in float32.
  * Pass gh = gw = 0 for a call without bias table.  Returns 0 for sizes the
  * library rejects (including gh*gw != N when a grid is given). */
 size_t ba_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int gh, int gw);

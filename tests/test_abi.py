@@ -54,8 +54,9 @@ def _round(x, m):
 
 
 def expected_workspace(B, H, N, d, gh=0, gw=0):
-    """Workspace sections as the header describes them: two sign arrays, two
-    scale arrays, two arrays of per-64-token scale maxima and V^T, per head
+    """Workspace sections as the header describes them: the Q sign words, the
+    K signs as fp4 MFMA operands (32 bytes per 64 channels), two scale arrays,
+    two arrays of per-64-token scale maxima and V^T, per head
     padded to a multiple of 128 tokens, each section 256-byte aligned; plus,
     for a grid width that is a multiple of 32, the float32 bias rows (4
     shifted copies per row, each padded to 16 mod 64 floats, 8 padding rows
@@ -63,7 +64,7 @@ def expected_workspace(B, H, N, d, gh=0, gw=0):
     npad = _round(N, 128)
     W = (d + 31) // 32
     dpad = 32 * W
-    secs = [B * H * npad * W * 4] * 2 + [B * H * npad * 4] * 2 + [B * H * (npad // 64) * 4] * 2
+    secs = [B * H * npad * W * 4, B * H * npad * ((W + 1) // 2) * 32] + [B * H * npad * 4] * 2 + [B * H * (npad // 64) * 4] * 2
     secs.append(B * H * dpad * npad * 2)
     if gh and gw % 32 == 0:
         lpad = _round(2 * gw - 1 + 3, 4)
