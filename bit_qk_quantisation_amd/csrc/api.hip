@@ -2,6 +2,7 @@
 // selection and launches.  See include/binattn.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -121,8 +122,41 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-// Max LDS bytes a workgroup may use on gfx950.
+// LDS bytes per compute unit on gfx950 (also the most one workgroup may use),
+// and the allocation granule.
 constexpr int kMaxLds = 160 * 1024;
+constexpr int kLdsGranule = 512;
+
+// Compute units of the current device, read once per device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Dynamic LDS of the fused kernel: the bias table (table mode), raised when
+// needed so that at most ceil(nwg / CUs) workgroups fit on one compute unit.
+// With about k workgroups per unit in the grid, letting a unit take k+1 of
+// them leaves others with k-1, and the busiest units set the time.
+int fused_dynamic_lds(int static_lds, int table_lds, int64_t nwg) {
+  int dyn = table_lds;
+  const int cus = device_cus();
+  if (cus > 0) {
+    const int64_t k = (nwg + cus - 1) / cus;
+    if (k >= 1 && k <= 4) {
+      // more than kMaxLds / (k + 1) bytes each keeps the (k+1)-th out
+      const int need = (kMaxLds / static_cast<int>(k + 1) / kLdsGranule + 1) * kLdsGranule;
+      if (static_lds + dyn < need && need * k <= kMaxLds) dyn = need - static_lds;
+    }
+  }
+  return dyn;
+}
 
 }  // namespace
 
@@ -258,8 +292,9 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool inputs, co
   if (nwg > 0x7fffffff) return fail(BA_ERR_SHAPE, "too many workgroups");
   f.nwg = static_cast<int>(nwg);
   f.xcd_remap = (f.nwg % 8 == 0) ? 1 : 0;
-  if (ba::fwd_static_lds(f.dpad) + ba::fwd_dynamic_lds(f, mode) > kMaxLds)
-    return fail(BA_ERR_UNSUPPORTED, "bias window does not fit in LDS");
+  const int static_lds = ba::fwd_static_lds(f.dpad), table_lds = ba::fwd_table_lds(f, mode);
+  if (static_lds + table_lds > kMaxLds) return fail(BA_ERR_UNSUPPORTED, "bias window does not fit in LDS");
+  f.dyn_lds = fused_dynamic_lds(static_lds, table_lds, nwg);
 
   ba::PrologueArgs& p = plan->p;
   p = ba::PrologueArgs{};

@@ -56,10 +56,12 @@ struct TileBuf {
   float win[kMaxWindowFloats];    // bias window (table-row mode)
 };
 
-// The row sums l of P come out of the P.V product: V^T carries rows of ones
-// (rows d and d+4 when d % 32 != 0; otherwise an extra 32-row block whose A
-// operand is a constant register), so accumulator row d (or row 0 of the
-// extra block) holds sum_j P_ij.
+// The row sums l of P: when d % 32 != 0, V^T carries rows of ones (rows d
+// and d+4), so accumulator row d of the P.V product holds sum_j P_ij.  When
+// d % 32 == 0 (XONES), the offset-free pass sums P on the vector ALU into
+// ones[0][0..1], and the exact pass runs an extra 32-row block whose A
+// operand is a constant register with ones in rows 0 and 4; either way
+// ones[0][0] holds sum_j P_ij at the end.
 template <int CB, bool XONES>
 struct Acc {
   v16f o[CB];
@@ -282,7 +284,7 @@ __device__ __forceinline__ void compute_tile(const Ctx<NCH>& c, const TileBuf<NC
 // ------------------------------------------------- pipelined fast path ----
 // P.V of a finished 32-key block waits in registers (bf16 P and its V^T
 // operands) and runs while the next block's logits are formed: each of its
-// 2 (CB + XONES) matrix instructions is followed by a quarter of the next
+// 2 CB matrix instructions is followed by a quarter of the next
 // block's vector work, so the matrix cores and the vector ALUs of a SIMD
 // overlap even within one wave, and the V^T operands no longer tie the
 // block to its LDS buffer (the pipeline runs across tile barriers).
@@ -293,25 +295,19 @@ struct PendingPV {
 };
 
 template <int CB, bool XONES>
-__device__ __forceinline__ void pv_mfma(int i, const PendingPV<CB>& pp, Acc<CB, XONES>& acc, const v8bf& ones_op) {
-  constexpr int per = CB + (XONES ? 1 : 0);
-  const int half = i / per, cb = i % per;
+__device__ __forceinline__ void pv_mfma(int i, const PendingPV<CB>& pp, Acc<CB, XONES>& acc) {
+  const int half = i / CB, cb = i % CB;
   const v4u pw = {pp.pk[4 * half], pp.pk[4 * half + 1], pp.pk[4 * half + 2], pp.pk[4 * half + 3]};
-  const v8bf pop = __builtin_bit_cast(v8bf, pw);
-  if (cb < CB)
-    acc.o[cb] = mfma_bf16_32x32x16(pp.vop[half][cb], pop, acc.o[cb]);
-  else
-    acc.ones[0] = mfma_bf16_32x32x16(ones_op, pop, acc.ones[0]);
+  acc.o[cb] = mfma_bf16_32x32x16(pp.vop[half][cb], __builtin_bit_cast(v8bf, pw), acc.o[cb]);
 }
 
 // Block `blk` of tile `tb`: its QK, then the pending block's P.V interleaved
 // with this block's logits / exp2 / bf16 packing; this block becomes pending.
 template <bool MASK, bool HAVE_PENDING, int NCH, int CB, bool XONES, int BIAS>
 __device__ __forceinline__ void pipelined_block(const Ctx<NCH>& c, const TileBuf<NCH, CB>& tb, const KeyPos& kp,
-                                                int blk, PendingPV<CB>& pp, Acc<CB, XONES>& acc,
-                                                const v8bf& ones_op) {
+                                                int blk, PendingPV<CB>& pp, Acc<CB, XONES>& acc) {
   const FwdArgs& a = *c.a;
-  constexpr int kMf = 2 * (CB + (XONES ? 1 : 0));
+  constexpr int kMf = 2 * CB;
   v16f s = v16f{};
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch)
@@ -325,7 +321,7 @@ __device__ __forceinline__ void pipelined_block(const Ctx<NCH>& c, const TileBuf
     if (HAVE_PENDING) {
       // this group's share of the pending block's matrix instructions
 #pragma unroll
-      for (int i = b * kMf / 4; i < (b + 1) * kMf / 4; ++i) pv_mfma<CB, XONES>(i, pp, acc, ones_op);
+      for (int i = b * kMf / 4; i < (b + 1) * kMf / 4; ++i) pv_mfma<CB, XONES>(i, pp, acc);
     }
     float x0 = s[4 * b] * row_bcast(akv, 4 * b), x1 = s[4 * b + 1] * row_bcast(akv, 4 * b + 1);
     float x2 = s[4 * b + 2] * row_bcast(akv, 4 * b + 2), x3 = s[4 * b + 3] * row_bcast(akv, 4 * b + 3);
@@ -356,6 +352,10 @@ __device__ __forceinline__ void pipelined_block(const Ctx<NCH>& c, const TileBuf
     }
     pk[2 * b] = pack_bf16x2(fast_exp2(x0), fast_exp2(x1));
     pk[2 * b + 1] = pack_bf16x2(fast_exp2(x2), fast_exp2(x3));
+    // Row sums on the vector ALU (two partial sums per lane), cheaper here
+    // than the extra matrix instructions of a ones block; they add the same
+    // bf16 P that multiplies V.
+    if (XONES) acc.ones[0][b & 1] = add_bf16x2(pk[2 * b], add_bf16x2(pk[2 * b + 1], acc.ones[0][b & 1]));
   }
   // this block becomes pending: P and its V^T operands
 #pragma unroll
@@ -371,18 +371,17 @@ __device__ __forceinline__ void pipelined_block(const Ctx<NCH>& c, const TileBuf
 // overlap the previous block's P.V.
 template <bool FIRST, int NCH, int CB, bool XONES, int BIAS>
 __device__ __forceinline__ void fast_step(const Ctx<NCH>& c, const TileBuf<NCH, CB>& cur, TileBuf<NCH, CB>& nxt,
-                                          int t, int nkt, KeyPos& kp, Acc<CB, XONES>& acc, PendingPV<CB>& pp,
-                                          const v8bf& ones_op) {
+                                          int t, int nkt, KeyPos& kp, Acc<CB, XONES>& acc, PendingPV<CB>& pp) {
   const FwdArgs& a = *c.a;
   const bool more = t + 1 < nkt;
   const KeyPos kn = next_keys(kp, a.gw);
   if (more) copy_tile_async<NCH, CB, BIAS>(c, nxt, t + 1, kn);
   if (BIAS == kBiasRows || kp.k0 + kBN <= a.N) {
-    pipelined_block<false, !FIRST, NCH, CB, XONES, BIAS>(c, cur, kp, 0, pp, acc, ones_op);
-    pipelined_block<false, true, NCH, CB, XONES, BIAS>(c, cur, kp, 1, pp, acc, ones_op);
+    pipelined_block<false, !FIRST, NCH, CB, XONES, BIAS>(c, cur, kp, 0, pp, acc);
+    pipelined_block<false, true, NCH, CB, XONES, BIAS>(c, cur, kp, 1, pp, acc);
   } else {
-    pipelined_block<true, !FIRST, NCH, CB, XONES, BIAS>(c, cur, kp, 0, pp, acc, ones_op);
-    pipelined_block<true, true, NCH, CB, XONES, BIAS>(c, cur, kp, 1, pp, acc, ones_op);
+    pipelined_block<true, !FIRST, NCH, CB, XONES, BIAS>(c, cur, kp, 0, pp, acc);
+    pipelined_block<true, true, NCH, CB, XONES, BIAS>(c, cur, kp, 1, pp, acc);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -391,7 +390,7 @@ __device__ __forceinline__ void fast_step(const Ctx<NCH>& c, const TileBuf<NCH, 
 
 template <int NCH, int CB, bool XONES, int BIAS>
 __device__ __forceinline__ void run_fast_pass(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb0, TileBuf<NCH, CB>& tb1,
-                                              Acc<CB, XONES>& acc, const v8bf& ones_op) {
+                                              Acc<CB, XONES>& acc) {
   const FwdArgs& a = *c.a;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc.o[cb] = v16f{};
@@ -407,14 +406,17 @@ __device__ __forceinline__ void run_fast_pass(const Ctx<NCH>& c, TileBuf<NCH, CB
   __syncthreads();
   const int nkt = (a.N + kBN - 1) / kBN;
   PendingPV<CB> pp;
-  fast_step<true, NCH, CB, XONES, BIAS>(c, tb0, tb1, 0, nkt, kp, acc, pp, ones_op);
+  fast_step<true, NCH, CB, XONES, BIAS>(c, tb0, tb1, 0, nkt, kp, acc, pp);
   for (int t = 1; t < nkt; t += 2) {
-    fast_step<false, NCH, CB, XONES, BIAS>(c, tb1, tb0, t, nkt, kp, acc, pp, ones_op);
-    if (t + 1 < nkt) fast_step<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, t + 1, nkt, kp, acc, pp, ones_op);
+    fast_step<false, NCH, CB, XONES, BIAS>(c, tb1, tb0, t, nkt, kp, acc, pp);
+    if (t + 1 < nkt) fast_step<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, t + 1, nkt, kp, acc, pp);
   }
   // drain: the last block's P.V
 #pragma unroll
-  for (int i = 0; i < 2 * (CB + (XONES ? 1 : 0)); ++i) pv_mfma<CB, XONES>(i, pp, acc, ones_op);
+  for (int i = 0; i < 2 * CB; ++i) pv_mfma<CB, XONES>(i, pp, acc);
+  // the row sums, in the register the epilogue reads: both halves of each
+  // query's keys (lanes l and l^32)
+  if (XONES) acc.ones[0][0] = sum_halves(acc.ones[0][0] + acc.ones[0][1]);
 }
 
 // One key tile: start the copies of tile t+1 into `nxt`, compute tile t from
@@ -590,7 +592,7 @@ attn_fwd_kernel(FwdArgs a) {
 
   Acc<CB, XONES> acc;
   if (M <= kFastMaxLogit)  // false for NaN as well
-    run_fast_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc, ones_op);
+    run_fast_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
   else
     run_pass<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, acc, ones_op);
 
@@ -625,7 +627,7 @@ attn_fwd_kernel(FwdArgs a) {
   }
 }
 
-int fwd_dynamic_lds(const FwdArgs& a, int mode) {
+int fwd_table_lds(const FwdArgs& a, int mode) {
   if (mode == kBiasTable) return (2 * a.gh - 1) * (2 * a.gw - 1) * 4;
   return 0;
 }
@@ -647,7 +649,7 @@ int fwd_static_lds(int dpad) {
 
 template <int NCH, int CB, bool XONES>
 static int launch_nc(const FwdArgs& a, int mode, void* stream) {
-  const int lds = fwd_dynamic_lds(a, mode);
+  const int lds = a.dyn_lds;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(a.nwg), block(kThreads);
   switch (mode) {

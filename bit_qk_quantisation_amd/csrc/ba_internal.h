@@ -84,10 +84,12 @@ struct FwdArgs {
   int nqt;                 // query tiles per head
   int nwg;                 // workgroups
   int xcd_remap;           // 1: spread consecutive heads over the 8 XCDs
+  int dyn_lds;             // dynamic LDS bytes per workgroup (table and/or padding)
 };
 
-// Dynamic / static LDS bytes of the fused kernel.
-int fwd_dynamic_lds(const FwdArgs& a, int mode);
+// LDS bytes of the fused kernel: the bias table (table mode, dynamic) and
+// the static tile buffers.
+int fwd_table_lds(const FwdArgs& a, int mode);
 int fwd_static_lds(int dpad);
 
 // Launch the fused kernel (template selected from d and the bias mode).
