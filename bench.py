@@ -79,20 +79,26 @@ def measured_traffic(workload: str):
 
 
 def algorithmic_bytes(w, npad):
-    """Compulsory HBM bytes of the two kernels of one step."""
+    """Compulsory HBM bytes of the two kernels of one step: the prologue reads
+    K and V and writes the fp4 key operands, the key scales (and their maxima
+    per 64 tokens), V^T and the bias rows; the fused kernel reads Q and all of
+    those and writes O."""
     W = (w.d + 31) // 32
+    nch = (W + 1) // 2
     dpad = 32 * W
     bh = w.B * w.H
     tok = bh * w.N
-    packed = 2 * bh * npad * (4 * W + 4)            # Q and K signs + scales
+    keys = bh * npad * (32 * nch + 4) + bh * (npad // 64) * 4
     vt = bh * dpad * npad * 2
     rows = 0
     if w.gw % 32 == 0:
         lpad = (2 * w.gw - 1 + 3 + 3) // 4 * 4
-        rows = w.H * (2 * w.gh - 1) * 4 * lpad * 4
+        while lpad % 64 != 16:
+            lpad += 4
+        rows = w.H * (2 * w.gh - 1 + 16) * 4 * lpad * 4
     table = w.H * (2 * w.gh - 1) * (2 * w.gw - 1) * 2
-    prologue = 3 * tok * w.d * 2 + packed + vt + table + rows
-    fused = packed + vt + tok * w.d * 2 + (rows if rows else table)
+    prologue = 2 * tok * w.d * 2 + keys + vt + ((table + rows) if rows else 0)
+    fused = tok * w.d * 2 + keys + vt + (rows if rows else table) + tok * w.d * 2
     return prologue, fused
 
 
@@ -195,11 +201,11 @@ def main() -> int:
     sp = stream.cuda_stream
 
     def prepare():
-        bq.check(lib, lib.ba_attention_prepare(q.data_ptr(), k.data_ptr(), v.data_ptr(), tp, gh, gw,
+        bq.check(lib, lib.ba_attention_prepare(k.data_ptr(), v.data_ptr(), tp, gh, gw,
                                                B, H, N, d, wsp, nbytes, sp))
 
     def fused():
-        bq.check(lib, lib.ba_attention_fwd_prepared(tp, gh, gw, B, H, N, d, scale, out.data_ptr(),
+        bq.check(lib, lib.ba_attention_fwd_prepared(q.data_ptr(), tp, gh, gw, B, H, N, d, scale, out.data_ptr(),
                                                     wsp, nbytes, sp))
 
     for _ in range(args.warmup):

@@ -57,9 +57,9 @@ def load(path=None) -> ctypes.CDLL:
     lib.ba_attention_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32,
                                      ctypes.c_float, vp, vp, sz, vp]
     lib.ba_attention_prepare.restype = i32
-    lib.ba_attention_prepare.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp, sz, vp]
+    lib.ba_attention_prepare.argtypes = [vp, vp, vp, i32, i32, i64, i64, i64, i32, vp, sz, vp]
     lib.ba_attention_fwd_prepared.restype = i32
-    lib.ba_attention_fwd_prepared.argtypes = [vp, i32, i32, i64, i64, i64, i32, ctypes.c_float,
+    lib.ba_attention_fwd_prepared.argtypes = [vp, vp, i32, i32, i64, i64, i64, i32, ctypes.c_float,
                                               vp, vp, sz, vp]
     lib.ba_qk_int_dot.restype = i32
     lib.ba_qk_int_dot.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp, vp]

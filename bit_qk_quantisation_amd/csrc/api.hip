@@ -81,7 +81,7 @@ int choose_mode(bool has_bias, int gh, int gw, int64_t N) {
 // Byte offsets of the workspace sections of ba_attention_fwd.
 struct Layout {
   int64_t Npad, W, dpad, Lpad;
-  int64_t qbits, kop, alpha_q, alpha_k, qmax, kmax, vt, bias4, rowmax, total;
+  int64_t kop, alpha_k, kmax, vt, bias4, rowmax, total;
   int mode;
 };
 
@@ -99,11 +99,8 @@ Layout layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int
     off = round_up(off + bytes, 256);
     return at;
   };
-  L.qbits = take(BH * L.Npad * L.W * 4);
   L.kop = take(BH * L.Npad * ((L.W + 1) / 2) * 32);  // fp4 key operands: 32 B per 64 channels
-  L.alpha_q = take(BH * L.Npad * 4);
   L.alpha_k = take(BH * L.Npad * 4);
-  L.qmax = take(BH * (L.Npad / 64) * 4);
   L.kmax = take(BH * (L.Npad / 64) * 4);
   L.vt = take(BH * L.dpad * L.Npad * 2);
   const bool rows = L.mode == ba::kBiasRows;
@@ -152,7 +149,7 @@ int fused_dynamic_lds(int static_lds, int table_lds, int64_t nwg) {
     if (k >= 1 && k <= 4) {
       // more than kMaxLds / (k + 1) bytes each keeps the (k+1)-th out
       const int need = (kMaxLds / static_cast<int>(k + 1) / kLdsGranule + 1) * kLdsGranule;
-      if (static_lds + dyn < need && need * k <= kMaxLds) dyn = need - static_lds;
+      if (static_lds + dyn < need && need * k <= kMaxLds && need <= 64 * 1024) dyn = need - static_lds;
     }
   }
   return dyn;
@@ -189,10 +186,9 @@ ba_status ba_pack_signs(const void* x, int64_t B, int64_t H, int64_t N, int d,
   if (!aligned16(x) || !aligned16(bits) || !aligned16(alpha))
     return fail(BA_ERR_ALIGN, "x, bits and alpha must be 16-byte aligned");
   ba::PrologueArgs p{};
-  p.pack[0] = ba::PackJob{static_cast<const uint16_t*>(x), bits, nullptr, alpha, nullptr, B * H,
-                          static_cast<int>(N), static_cast<int>(N), d, (d + 31) / 32, 0};
-  p.npack = 1;
-  p.pack_blocks = (B * H * N + 63) / 64;
+  p.pack = ba::PackJob{static_cast<const uint16_t*>(x), bits, alpha, B * H, static_cast<int>(N), d, (d + 31) / 32};
+  p.pack_blocks = (B * H * N + ba::kPackTok - 1) / ba::kPackTok;
+  p.lds = ba::prologue_lds(d, false);
   if (p.pack_blocks > 0x7fffffff) return fail(BA_ERR_SHAPE, "problem too large");
   const int err = ba::launch_prologue(p, stream);
   if (err != 0) return hip_fail(err, "pack launch");
@@ -220,29 +216,29 @@ struct Plan {
   int mode;
 };
 
-// Validates a forward request.  `inputs` selects the checks of q, k, v (the
-// prologue's inputs) and `output` those of o (the fused kernel's output).
-ba_status make_plan(const void* q, const void* k, const void* v, bool inputs, const void* bias,
-                    int gh, int gw, int64_t B, int64_t H, int64_t N, int d, float scale, void* o,
-                    bool output, void* workspace, size_t ws_bytes, Plan* plan) {
-  if (inputs && (!q || !k || !v)) return fail(BA_ERR_NULL, "q, k and v must be non-NULL");
-  if (output && !o) return fail(BA_ERR_NULL, "o must be non-NULL");
+// Validates a forward request.  `kv` selects the checks of k and v (the
+// prologue's inputs), `qo` those of q and o (the fused kernel's input and
+// output).
+ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const void* bias, int gh, int gw,
+                    int64_t B, int64_t H, int64_t N, int d, float scale, void* o, bool qo, void* workspace,
+                    size_t ws_bytes, Plan* plan) {
+  if (kv && (!k || !v)) return fail(BA_ERR_NULL, "k and v must be non-NULL");
+  if (qo && (!q || !o)) return fail(BA_ERR_NULL, "q and o must be non-NULL");
   ba_status st = check_dims(B, H, N, d);
   if (st != BA_OK) return st;
-  if (output && (!std::isfinite(scale) || scale < 0.0f))
+  if (qo && (!std::isfinite(scale) || scale < 0.0f))
     return fail(BA_ERR_SHAPE, "scale must be finite and >= 0");
   if (bias) {
     if (gh < 1 || gw < 1 || static_cast<int64_t>(gh) * gw != N)
       return fail(BA_ERR_SHAPE, "with a bias table gh*gw must equal N (gh=%d gw=%d N=%lld)", gh, gw,
                   (long long)N);
   }
-  if ((inputs && (!aligned16(q) || !aligned16(k) || !aligned16(v))) || (output && !aligned16(o)) ||
+  if ((kv && (!aligned16(k) || !aligned16(v))) || (qo && (!aligned16(q) || !aligned16(o))) ||
       (bias && !aligned16(bias)))
     return fail(BA_ERR_ALIGN, "q, k, v, o and bias must be 16-byte aligned");
   const size_t tensor_bytes = static_cast<size_t>(B * H * N * d) * 2;
-  if (inputs && output &&
-      (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(o, tensor_bytes, k, tensor_bytes) ||
-       overlaps(o, tensor_bytes, v, tensor_bytes)))
+  if (qo && (overlaps(o, tensor_bytes, q, tensor_bytes) ||
+             (kv && (overlaps(o, tensor_bytes, k, tensor_bytes) || overlaps(o, tensor_bytes, v, tensor_bytes)))))
     return fail(BA_ERR_SHAPE, "o must not overlap q, k or v");
   const int mode = choose_mode(bias != nullptr, gh, gw, N);
   if (mode < 0)
@@ -255,24 +251,21 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool inputs, co
     return fail(BA_ERR_ALIGN, "workspace must be 256-byte aligned");
   if (ws_bytes < static_cast<size_t>(L.total))
     return fail(BA_ERR_WORKSPACE, "workspace too small: %zu < %lld bytes", ws_bytes, (long long)L.total);
-  if (output && overlaps(workspace, L.total, o, tensor_bytes))
-    return fail(BA_ERR_WORKSPACE, "workspace must not overlap o");
-  if (inputs && (overlaps(workspace, L.total, q, tensor_bytes) || overlaps(workspace, L.total, k, tensor_bytes) ||
-                 overlaps(workspace, L.total, v, tensor_bytes)))
-    return fail(BA_ERR_WORKSPACE, "workspace must not overlap q, k or v");
+  if (qo && (overlaps(workspace, L.total, o, tensor_bytes) || overlaps(workspace, L.total, q, tensor_bytes)))
+    return fail(BA_ERR_WORKSPACE, "workspace must not overlap q or o");
+  if (kv && (overlaps(workspace, L.total, k, tensor_bytes) || overlaps(workspace, L.total, v, tensor_bytes)))
+    return fail(BA_ERR_WORKSPACE, "workspace must not overlap k or v");
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   const int64_t BH = B * H;
   ba::FwdArgs& f = plan->f;
   f = ba::FwdArgs{};
-  f.qbits = reinterpret_cast<const uint32_t*>(ws + L.qbits);
+  f.q = static_cast<const uint16_t*>(q);
   f.kop = reinterpret_cast<const uint32_t*>(ws + L.kop);
-  f.alpha_q = reinterpret_cast<const float*>(ws + L.alpha_q);
   f.alpha_k = reinterpret_cast<const float*>(ws + L.alpha_k);
   f.vt = reinterpret_cast<const uint16_t*>(ws + L.vt);
   f.bias4 = reinterpret_cast<const float*>(ws + L.bias4);
   f.bias_row_max = reinterpret_cast<const float*>(ws + L.rowmax);
-  f.qmax_blk = reinterpret_cast<const float*>(ws + L.qmax);
   f.kmax_blk = reinterpret_cast<const float*>(ws + L.kmax);
   f.table = static_cast<const uint16_t*>(bias);
   f.o = static_cast<uint16_t*>(o);
@@ -298,22 +291,17 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool inputs, co
 
   ba::PrologueArgs& p = plan->p;
   p = ba::PrologueArgs{};
-  p.pack[0] = ba::PackJob{static_cast<const uint16_t*>(q), const_cast<uint32_t*>(f.qbits), nullptr,
-                          const_cast<float*>(f.alpha_q), const_cast<float*>(f.qmax_blk), BH,
-                          f.N, f.Npad, d, f.W, 0};
-  p.pack[1] = ba::PackJob{static_cast<const uint16_t*>(k), nullptr, const_cast<uint32_t*>(f.kop),
-                          const_cast<float*>(f.alpha_k), const_cast<float*>(f.kmax_blk), BH,
-                          f.N, f.Npad, d, f.W, (f.W + 1) / 2};
-  p.npack = 2;
-  p.pack_blocks = (BH * L.Npad + 63) / 64;
-  p.vt = ba::VtJob{static_cast<const uint16_t*>(v), const_cast<uint16_t*>(f.vt), BH, f.N, f.Npad, d, f.dpad};
-  p.vt_blocks = BH * (L.Npad / 64);
+  p.kv = ba::KvJob{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), const_cast<uint32_t*>(f.kop),
+                   const_cast<float*>(f.alpha_k), const_cast<float*>(f.kmax_blk), const_cast<uint16_t*>(f.vt),
+                   BH, f.N, f.Npad, d, f.W, (f.W + 1) / 2, f.dpad};
+  p.kv_blocks = BH * (L.Npad / ba::kPackTok);
+  p.lds = ba::prologue_lds(d, true);
   if (mode == ba::kBiasRows) {
     p.bias = ba::BiasJob{static_cast<const uint16_t*>(bias), const_cast<float*>(f.bias4),
                          const_cast<float*>(f.bias_row_max), gh, gw, f.Lpad};
     p.bias_blocks = H * (2 * gh - 1 + 2 * ba::kBiasPadRows);
   }
-  const int64_t pblocks = 2 * p.pack_blocks + p.vt_blocks + p.bias_blocks;
+  const int64_t pblocks = p.kv_blocks + p.bias_blocks;
   if (pblocks > 0x7fffffff) return fail(BA_ERR_SHAPE, "problem too large");
   plan->mode = mode;
   return BA_OK;
@@ -323,11 +311,10 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool inputs, co
 
 extern "C" {
 
-ba_status ba_attention_prepare(const void* q, const void* k, const void* v, const void* bias, int gh,
-                               int gw, int64_t B, int64_t H, int64_t N, int d, void* workspace,
-                               size_t ws_bytes, void* stream) {
+ba_status ba_attention_prepare(const void* k, const void* v, const void* bias, int gh, int gw, int64_t B,
+                               int64_t H, int64_t N, int d, void* workspace, size_t ws_bytes, void* stream) {
   Plan plan;
-  ba_status st = make_plan(q, k, v, true, bias, gh, gw, B, H, N, d, 0.0f, nullptr, false, workspace,
+  ba_status st = make_plan(nullptr, k, v, true, bias, gh, gw, B, H, N, d, 0.0f, nullptr, false, workspace,
                            ws_bytes, &plan);
   if (st != BA_OK) return st;
   const int err = ba::launch_prologue(plan.p, stream);
@@ -335,11 +322,11 @@ ba_status ba_attention_prepare(const void* q, const void* k, const void* v, cons
   return BA_OK;
 }
 
-ba_status ba_attention_fwd_prepared(const void* bias, int gh, int gw, int64_t B, int64_t H, int64_t N,
-                                    int d, float scale, void* o, const void* workspace,
+ba_status ba_attention_fwd_prepared(const void* q, const void* bias, int gh, int gw, int64_t B, int64_t H,
+                                    int64_t N, int d, float scale, void* o, const void* workspace,
                                     size_t ws_bytes, void* stream) {
   Plan plan;
-  ba_status st = make_plan(nullptr, nullptr, nullptr, false, bias, gh, gw, B, H, N, d, scale, o, true,
+  ba_status st = make_plan(q, nullptr, nullptr, false, bias, gh, gw, B, H, N, d, scale, o, true,
                            const_cast<void*>(workspace), ws_bytes, &plan);
   if (st != BA_OK) return st;
   const int err = ba::launch_attention(plan.f, plan.mode, stream);

@@ -499,13 +499,33 @@ attn_fwd_kernel(FwdArgs a) {
   c.qi = c.q0 + c.wave * 32 + c.li;
   c.tokbase = static_cast<int64_t>(c.bh) * a.Npad;
 
+  // ---- this lane's query, packed straight from Q ---------------------------
+  // Lane (li, lh) forms the sign words 2 ch + lh of query qi (channels
+  // 32 word .. 32 word + 31) and sums |q| over them; the partner lane l ^ 32
+  // holds the other words, so the two partial sums make the scale
+  // alpha_q = mean |q| ("Representaciones Binarias Escaladas").  Queries past
+  // N are all zero: scale 0.
+  float qpart = 0.0f;
+  {
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(c.bh) * a.N + (c.qi < a.N ? c.qi : 0)) * a.d;
 #pragma unroll
-  for (int ch = 0; ch < NCH; ++ch) {
-    const int word = 2 * ch + c.lh;
-    const uint32_t w = word < a.W ? a.qbits[(c.tokbase + c.qi) * a.W + word] : 0u;
-    c.qop[ch] = expand_signs_fp4(w, fp4_magnitude(word_valid(a.d, word)));
+    for (int ch = 0; ch < NCH; ++ch) {
+      const int word = 2 * ch + c.lh;
+      uint32_t w = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c0 = 32 * word + 8 * k;
+        if (c.qi < a.N && c0 < a.d) {
+          float part;
+          w |= chunk_signs(*reinterpret_cast<const uint4*>(qrow + c0), part) << (8 * k);
+          qpart += part;
+        }
+      }
+      c.qop[ch] = expand_signs_fp4(w, fp4_magnitude(word_valid(a.d, word)));
+    }
   }
-  c.aq = a.alpha_q[c.tokbase + c.qi] * a.qscale;
+  const float alpha_q = sum_halves(qpart) / static_cast<float>(a.d);
+  c.aq = alpha_q * a.qscale;
 
   // ---- per-lane LDS offsets ------------------------------------------------
   c.off_k = (c.li * 2 + c.lh) * 16;
@@ -581,8 +601,7 @@ attn_fwd_kernel(FwdArgs a) {
   }
   km = block_max(km, red);
   bm = block_max(bm, red);
-  const int qb = c.bh * nblk + c.q0 / 64;
-  const float qm = fmaxf(a.qmax_blk[qb], a.qmax_blk[qb + 1]);
+  const float qm = block_max(alpha_q, red);
   const float M = a.qscale * qm * km * static_cast<float>(a.d) + bm;
 
   // A operand of the extra row-sum block: rows 0 and 4 are ones.

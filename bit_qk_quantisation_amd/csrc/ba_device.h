@@ -30,6 +30,25 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 // of s_i = mu_q sign(q_i) ("Representaciones Binarias Escaladas").
 __device__ __forceinline__ uint32_t neg_bit(float x) { return x < 0.0f ? 1u : 0u; }
 
+// Sign byte (bit b set iff channel b of the 8-channel chunk is negative) and
+// the sum of |x| over the chunk, in a fixed order.
+__device__ __forceinline__ uint32_t chunk_signs(const uint4& raw, float& part) {
+  const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t byte = 0;
+  float a[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float lo = bf16_to_f32(static_cast<uint16_t>(wv[k] & 0xffffu));
+    const float hi = bf16_to_f32(static_cast<uint16_t>(wv[k] >> 16));
+    byte |= neg_bit(lo) << (2 * k);
+    byte |= neg_bit(hi) << (2 * k + 1);
+    a[2 * k] = fabsf(lo);
+    a[2 * k + 1] = fabsf(hi);
+  }
+  part = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+  return byte;
+}
+
 // --------------------------------------------------------------------------
 // +/-1 operands in fp4 (e2m1) for the scaled f8f6f4 MFMA.
 //

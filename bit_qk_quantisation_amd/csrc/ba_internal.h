@@ -23,24 +23,28 @@ constexpr int kBiasPadRows = 8;
 // (8 KiB: two 1 KiB copy pieces per wave); covers grids up to 128 wide.
 constexpr int kMaxWindowFloats = 2048;
 
-// Largest LDS footprint of a prologue block (vt tile at d = 256).
-constexpr int kPrologueSmem = 64 * (256 + 8) * 2;
+// Tokens per prologue block (one key tile).
+constexpr int kPackTok = 64;
 
+// Standalone sign pack of one tensor (ba_pack_signs).
 struct PackJob {
   const uint16_t* x;  // bf16 [BH][N][d]
-  uint32_t* bits;     // [BH][Npad][W], or null
-  uint32_t* kop;      // fp4 key operands [BH][Npad/64][NCH][64][2][4], or null
-  float* alpha;       // [BH][Npad]
-  float* alpha_max;   // [BH*Npad/64]: max alpha of each 64-token block, or null
+  uint32_t* bits;     // [BH][N][W]
+  float* alpha;       // [BH][N]
   int64_t BH;
-  int N, Npad, d, W, nch;
+  int N, d, W;
 };
 
-struct VtJob {
+// Keys and values of one forward, one 64-token tile of one (b, h) per block.
+struct KvJob {
+  const uint16_t* k;  // bf16 [BH][N][d]
   const uint16_t* v;  // bf16 [BH][N][d]
-  uint16_t* vt;       // bf16 [BH][Npad/64][dpad][64], see vt_block
+  uint32_t* kop;      // fp4 key operands [BH][Npad/64][NCH][64][2][4]
+  float* alpha;       // key scales [BH][Npad]
+  float* alpha_max;   // largest key scale of each tile [BH][Npad/64]
+  uint16_t* vt;       // bf16 [BH][Npad/64][dpad][64], see the prologue
   int64_t BH;
-  int N, Npad, d, dpad;
+  int N, Npad, d, W, nch, dpad;
 };
 
 struct BiasJob {
@@ -50,30 +54,33 @@ struct BiasJob {
   int gh, gw, Lpad;
 };
 
+// One launch runs the blocks of every job present (a job with 0 blocks is
+// absent): the pack blocks first, then the key/value tiles, then the bias rows.
 struct PrologueArgs {
-  PackJob pack[2];
-  int npack;
-  int64_t pack_blocks;  // per pack job
-  VtJob vt;
-  int64_t vt_blocks;
+  PackJob pack;
+  int64_t pack_blocks;
+  KvJob kv;
+  int64_t kv_blocks;
   BiasJob bias;
   int64_t bias_blocks;
+  int lds;  // dynamic LDS bytes per block
 };
+
+// Dynamic LDS the prologue needs for head dim d.
+int prologue_lds(int d, bool kv);
 
 int launch_prologue(const PrologueArgs& a, void* stream);
 
 enum BiasMode { kBiasNone = 0, kBiasRows = 1, kBiasTable = 2 };
 
 struct FwdArgs {
-  const uint32_t* qbits;   // [BH][Npad][W]
+  const uint16_t* q;       // bf16 [BH][N][d]: queries, packed in the kernel
   const uint32_t* kop;     // [BH][Npad/64][NCH][64 keys][2][4]: the fp4 +/-1
                            // operand dwords of each key, in LDS tile order
-  const float* alpha_q;    // [BH][Npad]
   const float* alpha_k;    // [BH][Npad]
   const uint16_t* vt;      // [BH][Npad/64][dpad][64] (slot order, swizzled)
   const float* bias4;      // kBiasRows: [H][2gh-1+2*kBiasPadRows][4][Lpad]
   const float* bias_row_max;  // kBiasRows: [H][2gh-1], max |b| log2e per row
-  const float* qmax_blk;   // [BH][Npad/64] max alpha_q per 64-token block
   const float* kmax_blk;   // [BH][Npad/64] max alpha_k per 64-token block
   const uint16_t* table;   // kBiasTable: bf16 [H][2gh-1][2gw-1]
   uint16_t* o;             // bf16 [BH][N][d]

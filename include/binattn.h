@@ -89,11 +89,11 @@ int ba_pack_words(int d);
 ba_status ba_pack_signs(const void* x, int64_t B, int64_t H, int64_t N, int d,
                         uint32_t* bits, float* alpha, void* stream);
 
-/* Workspace bytes that ba_attention_fwd needs for this problem: the packed Q
- * signs, the K signs as fp4 +/-1 matrix operands (32 bytes per token and 64
- * channels), the Q and K scales, a key-major V^T copy (per head, N padded to
- * a multiple of 128) and, for a bias grid with gw % 32 == 0, the table rows
- * in float32.
+/* Workspace bytes that ba_attention_fwd needs for this problem: the K signs
+ * as fp4 +/-1 matrix operands (32 bytes per token and 64 channels), the K
+ * scales and their maximum per 64 tokens, a key-major V^T copy (per head, N
+ * padded to a multiple of 128) and, for a bias grid with gw % 32 == 0, the
+ * table rows in float32.  The queries are packed inside the fused kernel.
  * Pass gh = gw = 0 for a call without bias table.  Returns 0 for sizes the
  * library rejects (including gh*gw != N when a grid is given). */
 size_t ba_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int gh, int gw);
@@ -118,8 +118,8 @@ size_t ba_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int gh, int gw
  *              bytes (gh = gw = 0 there when bias is NULL),
  *              256-byte aligned.  Its contents on entry do not matter, and it
  *              must not be shared by calls that may overlap on the GPU.
- * Two kernels are enqueued: the sign/scale pack of Q and K (with the V^T
- * copy), then the fused attention kernel.
+ * Two kernels are enqueued: the sign/scale pack of K with the V^T copy,
+ * then the fused attention kernel (which packs Q).
  * Errors: BA_ERR_NULL, BA_ERR_SHAPE, BA_ERR_UNSUPPORTED, BA_ERR_ALIGN,
  *         BA_ERR_WORKSPACE, BA_ERR_HIP. */
 ba_status ba_attention_fwd(const void* q, const void* k, const void* v,
@@ -131,25 +131,25 @@ ba_status ba_attention_fwd(const void* q, const void* k, const void* v,
 /* The two halves of ba_attention_fwd, for callers that time or schedule the
  * two kernels separately.
  *
- * ba_attention_prepare -- enqueues the prologue kernel: packed signs and
- * scales of Q and K ("Representaciones Binarias Escaladas"), the key-major
- * V^T copy and, for gw % 32 == 0, the float32 bias rows, all written into
- * `workspace`.  Same arguments and errors as ba_attention_fwd, without scale
- * and o.
+ * ba_attention_prepare -- enqueues the prologue kernel: the signs and scales
+ * of K ("Representaciones Binarias Escaladas"), the key-major V^T copy and,
+ * for gw % 32 == 0, the float32 bias rows, all written into `workspace`.
+ * Same arguments and errors as ba_attention_fwd, without q, scale and o.
  *
- * ba_attention_fwd_prepared -- enqueues only the fused kernel, reading a
- * workspace that ba_attention_prepare filled with the same bias, gh, gw, B,
- * H, N and d (stream order must put the prepare first).  The bias table is
- * read again here when gw % 32 != 0.  Same errors as ba_attention_fwd.
+ * ba_attention_fwd_prepared -- enqueues only the fused kernel, which packs
+ * the queries itself and reads a workspace that ba_attention_prepare filled
+ * with the same bias, gh, gw, B, H, N and d (stream order must put the
+ * prepare first).  The bias table is read again here when gw % 32 != 0.
+ * Same arguments and errors as ba_attention_fwd, without k and v.
  *
  * ba_attention_fwd(...) is ba_attention_prepare(...) followed by
  * ba_attention_fwd_prepared(...) on the same stream. */
-ba_status ba_attention_prepare(const void* q, const void* k, const void* v,
+ba_status ba_attention_prepare(const void* k, const void* v,
                                const void* bias, int gh, int gw,
                                int64_t B, int64_t H, int64_t N, int d,
                                void* workspace, size_t ws_bytes, void* stream);
 
-ba_status ba_attention_fwd_prepared(const void* bias, int gh, int gw,
+ba_status ba_attention_fwd_prepared(const void* q, const void* bias, int gh, int gw,
                                     int64_t B, int64_t H, int64_t N, int d,
                                     float scale, void* o,
                                     const void* workspace, size_t ws_bytes,

@@ -54,9 +54,9 @@ def _round(x, m):
 
 
 def expected_workspace(B, H, N, d, gh=0, gw=0):
-    """Workspace sections as the header describes them: the Q sign words, the
-    K signs as fp4 MFMA operands (32 bytes per 64 channels), two scale arrays,
-    two arrays of per-64-token scale maxima and V^T, per head
+    """Workspace sections as the header describes them: the K signs as fp4
+    MFMA operands (32 bytes per 64 channels), the K scales, their maxima per
+    64 tokens and V^T, per head
     padded to a multiple of 128 tokens, each section 256-byte aligned; plus,
     for a grid width that is a multiple of 32, the float32 bias rows (4
     shifted copies per row, each padded to 16 mod 64 floats, 8 padding rows
@@ -64,7 +64,7 @@ def expected_workspace(B, H, N, d, gh=0, gw=0):
     npad = _round(N, 128)
     W = (d + 31) // 32
     dpad = 32 * W
-    secs = [B * H * npad * W * 4, B * H * npad * ((W + 1) // 2) * 32] + [B * H * npad * 4] * 2 + [B * H * (npad // 64) * 4] * 2
+    secs = [B * H * npad * ((W + 1) // 2) * 32, B * H * npad * 4, B * H * (npad // 64) * 4]
     secs.append(B * H * dpad * npad * 2)
     if gh and gw % 32 == 0:
         lpad = _round(2 * gw - 1 + 3, 4)
@@ -167,3 +167,17 @@ def test_last_error_is_thread_local(lib):
     t.join()
     assert seen == [b""]
     assert b"d=12" in lib.ba_last_error()
+
+
+def test_split_entry_validation(lib):
+    """ba_attention_prepare takes k and v, ba_attention_fwd_prepared takes q
+    and o; each validates only what it reads or writes."""
+    ws = A + 4 * GB
+    assert lib.ba_attention_prepare(None, A + 2 * GB, None, 0, 0, 1, 2, 64, 64, ws, 1 << 40, None) == 1
+    assert lib.ba_attention_prepare(A + GB + 8, A + 2 * GB, None, 0, 0, 1, 2, 64, 64, ws, 1 << 40, None) == 4
+    assert lib.ba_attention_prepare(A + GB, A + 2 * GB, None, 0, 0, 1, 2, 64, 64, ws, 16, None) == 5
+    assert lib.ba_attention_fwd_prepared(None, None, 0, 0, 1, 2, 64, 64, 0.125, A + 3 * GB, ws, 1 << 40, None) == 1
+    assert lib.ba_attention_fwd_prepared(A, None, 0, 0, 1, 2, 64, 64, 0.125, None, ws, 1 << 40, None) == 1
+    assert lib.ba_attention_fwd_prepared(A, None, 0, 0, 1, 2, 64, 64, float("inf"), A + 3 * GB, ws, 1 << 40,
+                                         None) == 2
+    assert lib.ba_attention_fwd_prepared(A, None, 0, 0, 1, 2, 64, 64, 0.125, A + 16, ws, 1 << 40, None) == 2
