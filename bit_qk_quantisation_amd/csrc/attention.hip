@@ -86,12 +86,10 @@ struct Ctx {
   // Asynchronous tile copies: wave-uniform bases (scalar registers) plus
   // per-lane 32-bit byte offsets.
   rsrc_t vrs;          // V^T tiles of this (b, h)
-  uint32_t voff;       // this lane's byte in a V^T tile (first 1 KiB piece)
   rsrc_t krs;          // fp4 key operand tiles of this (b, h)
   rsrc_t ars;          // key scales of this (b, h)
   rsrc_t brs;          // bias rows of this head (table-row mode)
-  uint32_t boff[2];    // this lane's byte in its 1 KiB window pieces
-  bool bvalid[2];      // whether that byte lies inside the window
+  int win_bytes;       // bytes of the per-tile bias window (table-row mode)
 };
 
 // Uniform per-tile position of the keys on the grid (table-row mode).
@@ -156,9 +154,12 @@ __device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TileBuf<NCH, 
             static_cast<uint32_t>(t * kKBytes + (c.wave + 4 * j) * 1024));
   constexpr int kVtBytes = 32 * CB * kBN * 2;
   char* vdst = reinterpret_cast<char*>(&tb.vt[0]);
+  // this lane's byte in its 1 KiB pieces, recomputed here rather than kept
+  // in a register through the key loop
+  const uint32_t loff = static_cast<uint32_t>(c.wave * 1024 + c.lane * 16);
 #pragma unroll
   for (int j = 0; j < kVtBytes / 4096; ++j)
-    dma16(c.vrs, vdst + (c.wave + 4 * j) * 1024, c.voff, static_cast<uint32_t>(t * kVtBytes + j * 4096));
+    dma16(c.vrs, vdst + (c.wave + 4 * j) * 1024, loff, static_cast<uint32_t>(t * kVtBytes + j * 4096));
   if (c.wave == 0) dma4(c.ars, &tb.ak[0], static_cast<uint32_t>(c.lane * 4), static_cast<uint32_t>(kp.k0 * 4));
   if (BIAS == kBiasRows) {
     // window rows start at dy = yq_lo - yk_hi; yk_hi is the row of block 1
@@ -167,7 +168,8 @@ __device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TileBuf<NCH, 
     char* bdst = reinterpret_cast<char*>(&tb.win[0]);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      if (c.bvalid[j]) dma16(c.brs, bdst + (c.wave + 4 * j) * 1024, c.boff[j], bs);
+      if (static_cast<int>(loff) + 4096 * j < c.win_bytes)
+        dma16(c.brs, bdst + (c.wave + 4 * j) * 1024, loff + 4096 * j, bs);
   }
   if (BIAS == kBiasTable && c.tid < kBN) {
     const int j = (kp.k0 + c.tid < a.N) ? kp.k0 + c.tid : a.N - 1;
@@ -559,25 +561,17 @@ attn_fwd_kernel(FwdArgs a) {
   // it names, and each range is far below 2^31 bytes.
   c.vrs = make_rsrc(reinterpret_cast<const char*>(a.vt) + static_cast<int64_t>(c.bh) * (a.Npad / kBN) * kVtBytes,
                     static_cast<uint32_t>((a.Npad / kBN) * kVtBytes));
-  c.voff = static_cast<uint32_t>(c.wave * 1024 + c.lane * 16);
   constexpr int kKBytes = NCH * kBN * 2 * 16;
   c.krs = make_rsrc(reinterpret_cast<const char*>(a.kop) + static_cast<int64_t>(c.bh) * (a.Npad / kBN) * kKBytes,
                     static_cast<uint32_t>((a.Npad / kBN) * kKBytes));
   c.ars = make_rsrc(a.alpha_k + c.tokbase, static_cast<uint32_t>(a.Npad * 4));
   c.brs = c.ars;
-  c.bvalid[0] = c.bvalid[1] = false;
-  c.boff[0] = c.boff[1] = 0;
+  c.win_bytes = 0;
   if (BIAS == kBiasRows) {
     const int rows_p = 2 * a.gh - 1 + 2 * kBiasPadRows;
     c.brs = make_rsrc(a.bias4 + static_cast<int64_t>(c.head) * rows_p * 4 * a.Lpad,
                       static_cast<uint32_t>(rows_p * 16 * a.Lpad));
-    const int bytes = a.win_rows * 16 * a.Lpad;  // <= 8 KiB: two pieces per wave
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int off = (c.wave + 4 * j) * 1024 + c.lane * 16;
-      c.boff[j] = static_cast<uint32_t>(off);
-      c.bvalid[j] = off < bytes;
-    }
+    c.win_bytes = a.win_rows * 16 * a.Lpad;  // <= 8 KiB: two pieces per wave
   }
 
   // ---- logit bound M (log2 units) ------------------------------------------
