@@ -20,13 +20,13 @@
 //         are per lane.  V^T carries rows of ones (or an extra constant
 //         operand block), so the same product also yields the row sums l.
 //
-// Workgroup: 4 waves x 32 queries = 128 queries of one (b, h).  Key tiles of
-// 64 live in two LDS buffers: while tile t is computed from one, the next
-// tile's V^T, key scales and bias window stream into the other with
-// global_load_lds, and its packed key bits are loaded into registers, then
-// expanded to fp4 operands after the compute.  One barrier per tile.  Every
-// LDS address is a per-lane base fixed at kernel start plus a constant or a
-// wave-uniform offset; no division runs inside the key loop.
+// Workgroup: 4 waves x 32 queries = 128 queries of one (b, h).  Each wave
+// packs its own 32 queries (signs and alpha_q) from bf16 at the start.  Key
+// tiles of 64 live in two LDS buffers: while tile t is computed from one, the
+// next tile's fp4 key operands (written by the prologue), key scales, V^T and
+// bias window stream into the other with buffer-to-LDS copies.  One barrier
+// per tile.  Every LDS address is a per-lane base fixed at kernel start plus
+// a constant or a wave-uniform offset; no division runs inside the key loop.
 //
 // Softmax, in base 2.  Every logit of a workgroup obeys |s| <= M with
 //   M = scale log2e max_i alpha_q,i max_j alpha_k,j d + log2e max|b|
