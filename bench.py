@@ -2,6 +2,7 @@
 """Benchmark of the BinaryAttention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--layout bhnd|bnhd|qkv]
 
 One step is one full forward (ba_attention_prepare + ba_attention_fwd_prepared,
 i.e. exactly ba_attention_fwd) over the resident bf16 inputs of the chosen
@@ -10,6 +11,11 @@ W untimed steps run first, then exactly K steps are timed between two
 device synchronisations.  HIP events on the launch stream also bracket each
 kernel, which gives the average duration of the fused kernel and of the
 prologue.
+
+--layout bnhd stores q, k, v and o as [B,N,H,d]; --layout qkv takes q, k and
+v as the slices of one [B,N,3,H,d] tensor and writes a [B,N,H,d] o.  Both go
+through ba_attention_fwd_strided, one call per step, so only the whole step
+is timed and the roofline figure is taken over the step.
 
 Printed: one JSON line on stdout with the throughput in TFLOP-eq/s
 (4*B*H*N^2*d per step, the FLOPs of dense QK^T and P.V), the fused kernel's
@@ -159,6 +165,8 @@ def main() -> int:
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="host time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--layout", choices=("bhnd", "bnhd", "qkv"), default="bhnd",
+                    help="memory layout of q, k, v and o (see above)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB "
                          "(reference kernel for HBM counter calibration)")
@@ -208,6 +216,30 @@ def main() -> int:
         bq.check(lib, lib.ba_attention_fwd_prepared(q.data_ptr(), tp, gh, gw, B, H, N, d, scale, out.data_ptr(),
                                                     wsp, nbytes, sp))
 
+    split = args.layout == "bhnd"
+    if not split:
+        import ctypes
+        if args.layout == "bnhd":
+            views = [x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v)]
+        else:
+            qkv = torch.stack([q, k, v], dim=1).permute(0, 3, 1, 2, 4).contiguous()  # [B,N,3,H,d]
+            views = [qkv[:, :, i].transpose(1, 2) for i in range(3)]
+        sq, sk, sv = views
+        so = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=dev).transpose(1, 2)
+        strides = (ctypes.c_int64 * 12)(*[t.stride(i) for t in (sq, sk, sv, so) for i in range(3)])
+        del q, k, v
+        out = so
+
+        def whole():
+            bq.check(lib, lib.ba_attention_fwd_strided(sq.data_ptr(), sk.data_ptr(), sv.data_ptr(), tp, gh, gw,
+                                                       B, H, N, d, scale, so.data_ptr(), strides, wsp, nbytes, sp))
+
+        def prepare():  # noqa: F811 -- one call runs both kernels
+            whole()
+
+        def fused():  # noqa: F811
+            pass
+
     for _ in range(args.warmup):
         prepare()
         fused()
@@ -241,6 +273,8 @@ def main() -> int:
     torch.cuda.synchronize()
     pro_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
     fus_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    if not split:  # the "prologue" interval held the whole step
+        fus_ms = pro_ms
 
     if args.copy_mb:
         src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
@@ -253,7 +287,7 @@ def main() -> int:
     fused_tf = flop / (fus_ms * 1e-3) / 1e12
     npad = (N + 127) // 128 * 128
     pro_bytes, fus_bytes = algorithmic_bytes(w, npad)
-    traffic = measured_traffic(name)
+    traffic = measured_traffic(name) if split else None
 
     baseline = None
     if args.cpu_seconds > 0:
@@ -274,10 +308,10 @@ def main() -> int:
         "data": "synthetic",
         "config": {**w.describe(), "qk": "1-bit signs as +/-1 fp4 on MFMA (exact integer dots)",
                    "pv": "bf16 MFMA, fp32 accumulate", "softmax": "fp32, base 2",
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "layout": args.layout},
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_kernel (fused)",
+            "kernel": "attn_fwd_kernel (fused)" if split else "whole step (prologue + fused, one strided call)",
             "achieved": round(fused_tf, 1),
             "peak": round(PEAK_MFMA_COMPOSITE, 1),
             "unit": "TFLOP/s",
@@ -286,19 +320,22 @@ def main() -> int:
         },
         "cpu_baseline": baseline,
         "detail": {
-            "fused_us": round(fus_ms * 1e3, 2),
-            "prologue_us": round(pro_ms * 1e3, 2),
+            "fused_us": round(fus_ms * 1e3, 2) if split else None,
+            "prologue_us": round(pro_ms * 1e3, 2) if split else None,
             "step_us": round(ms_step * 1e3, 2),
             "frac_of_int8_bf16_mfma_roofline": round(fused_tf / PEAK_MFMA_INT8_BF16, 4),
             "step_frac_of_composite_mfma_roofline": round(value / PEAK_MFMA_COMPOSITE, 4),
-            "prologue_algorithmic_GBps": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
-            "prologue_frac_of_hbm": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "prologue_algorithmic_GBps": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1) if split else None,
+            "prologue_frac_of_hbm": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if split else None,
             "fused_algorithmic_bytes": fus_bytes,
             "device": torch.cuda.get_device_name(dev),
         },
     }
-    log(f"[bench] {name}: step {ms_step * 1e3:.1f} us (prologue {pro_ms * 1e3:.1f} us, "
-        f"fused {fus_ms * 1e3:.1f} us) -> {value:.1f} TFLOP-eq/s")
+    if split:
+        log(f"[bench] {name}: step {ms_step * 1e3:.1f} us (prologue {pro_ms * 1e3:.1f} us, "
+            f"fused {fus_ms * 1e3:.1f} us) -> {value:.1f} TFLOP-eq/s")
+    else:
+        log(f"[bench] {name} ({args.layout}): step {ms_step * 1e3:.1f} us -> {value:.1f} TFLOP-eq/s")
     print(json.dumps(rec), flush=True)
     return 0
 

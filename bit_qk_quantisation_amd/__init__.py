@@ -6,13 +6,16 @@ kernels of libbinattn.so (built by ``python -m bit_qk_quantisation_amd.build``).
 If the library is missing the calls raise; there is no CPU fallback.
 
     pack_signs(x)                          -> (bits uint32-as-int32, alpha f32)
-    attention_fwd(q, k, v, table, gh, gw)  -> O (bf16)
+    attention_fwd(q, k, v, table, gh, gw)  -> O (bf16); q, k, v and out may be
+                                              strided [B,H,N,d] views (e.g.
+                                              a [B,N,H,d] tensor transposed)
     qk_int_dot(qbits, kbits, d, route)     -> D (int32)
     workspace_bytes(B, H, N, d, gh, gw)    -> int
 """
 
 from __future__ import annotations
 
+import ctypes
 import math
 
 import torch
@@ -44,6 +47,20 @@ def _need(t: torch.Tensor, name: str, dtype, ndim=None):
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _need_view(t: torch.Tensor, name: str):
+    """A bf16 [B,H,N,d] view on a HIP device whose channels are contiguous."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be torch.bfloat16, got {t.dtype}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must have 4 dims, got {tuple(t.shape)}")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError(f"{name} must have contiguous channels (stride 1 in the last dim)")
 
 
 def pack_words(d: int) -> int:
@@ -91,9 +108,9 @@ def attention_fwd(q, k, v, table=None, gh: int = 0, gw: int = 0, scale=None,
     """BinaryAttention forward: bf16 q, k, v [B,H,N,d] (+ bf16 table
     [H, 2gh-1, 2gw-1]) -> bf16 O [B,H,N,d]."""
     lib = load()
-    _need(q, "q", torch.bfloat16, 4)
-    _need(k, "k", torch.bfloat16, 4)
-    _need(v, "v", torch.bfloat16, 4)
+    _need_view(q, "q")
+    _need_view(k, "k")
+    _need_view(v, "v")
     if q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k and v must have the same shape")
     B, H, N, d = q.shape
@@ -108,18 +125,28 @@ def attention_fwd(q, k, v, table=None, gh: int = 0, gw: int = 0, scale=None,
     if out is None:
         out = torch.empty_like(q)
     else:
-        _need(out, "out", torch.bfloat16, 4)
+        _need_view(out, "out")
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
     nbytes = lib.ba_workspace_bytes(B, H, N, d, gh, gw)
     if nbytes == 0:
         raise BinAttnError(2, f"unsupported problem B={B} H={H} N={N} d={d} grid={gh}x{gw}")
     ws = (workspace or _default_ws).get(q.device, nbytes)
     base = ws.data_ptr()
     aligned = (base + 255) // 256 * 256
-    check(lib, lib.ba_attention_fwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(),
-        None if table is None else table.data_ptr(), int(gh), int(gw),
-        B, H, N, d, float(scale), out.data_ptr(), aligned,
-        ws.numel() - (aligned - base), _stream(q.device)))
+    tp = None if table is None else table.data_ptr()
+    ws_len = ws.numel() - (aligned - base)
+    views = (q, k, v, out)
+    if all(t.is_contiguous() for t in views):
+        check(lib, lib.ba_attention_fwd(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), tp, int(gh), int(gw),
+            B, H, N, d, float(scale), out.data_ptr(), aligned, ws_len, _stream(q.device)))
+    else:
+        strides = (ctypes.c_int64 * 12)(*[t.stride(i) for t in views for i in range(3)])
+        check(lib, lib.ba_attention_fwd_strided(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), tp, int(gh), int(gw),
+            B, H, N, d, float(scale), out.data_ptr(), strides, aligned, ws_len,
+            _stream(q.device)))
     return out
 
 

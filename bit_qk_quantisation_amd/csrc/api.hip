@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <utility>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -119,6 +120,47 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// ---- strided [B,H,N,d] views -------------------------------------------------
+
+ba::Strides contiguous_strides(int64_t H, int64_t N, int d) { return ba::Strides{H * N * d, N * d, d}; }
+
+constexpr int64_t kMaxStride = int64_t{1} << 40;  // elements
+constexpr int64_t kMaxSpan = int64_t{1} << 50;
+
+// Checks one view's strides (non-negative, at most 2^40, multiples of 8 so
+// that every row stays 16-byte aligned) and returns the number of bytes from
+// its first to one past its last element, or -1.
+int64_t view_span_bytes(const ba::Strides& s, int64_t B, int64_t H, int64_t N, int d) {
+  const int64_t st[3] = {s.sb, s.sh, s.sn}, ext[3] = {B, H, N};
+  int64_t span = d;
+  for (int i = 0; i < 3; ++i) {
+    if (st[i] < 0 || st[i] > kMaxStride || st[i] % 8 != 0) return -1;
+    if (ext[i] > 1 && st[i] > (kMaxSpan - span) / (ext[i] - 1)) return -1;
+    span += st[i] * (ext[i] - 1);
+  }
+  return span * 2;
+}
+
+// True when no element of the view belongs to two (b, h, n) rows: taken in
+// order of increasing stride, each dimension's stride must step past
+// everything the smaller ones reach.  Sufficient, not necessary; output views
+// must pass it so that no two rows are written to the same place.
+bool rows_disjoint(const ba::Strides& s, int64_t B, int64_t H, int64_t N, int d) {
+  int64_t st[3] = {s.sb, s.sh, s.sn}, ext[3] = {B, H, N};
+  for (int i = 1; i < 3; ++i)  // insertion sort by stride
+    for (int j = i; j > 0 && st[j] < st[j - 1]; --j) {
+      std::swap(st[j], st[j - 1]);
+      std::swap(ext[j], ext[j - 1]);
+    }
+  int64_t reach = d;
+  for (int i = 0; i < 3; ++i) {
+    if (ext[i] <= 1) continue;
+    if (st[i] < reach) return false;
+    reach += st[i] * (ext[i] - 1);
+  }
+  return true;
+}
+
 // LDS bytes per compute unit on gfx950 (also the most one workgroup may use),
 // and the allocation granule.
 constexpr int kMaxLds = 160 * 1024;
@@ -219,9 +261,11 @@ struct Plan {
 // Validates a forward request.  `kv` selects the checks of k and v (the
 // prologue's inputs), `qo` those of q and o (the fused kernel's input and
 // output).
+// `strides` holds the (batch, head, token) element strides of q, k, v and o,
+// in that order (12 values), or is NULL for contiguous [B,H,N,d] tensors.
 ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const void* bias, int gh, int gw,
-                    int64_t B, int64_t H, int64_t N, int d, float scale, void* o, bool qo, void* workspace,
-                    size_t ws_bytes, Plan* plan) {
+                    int64_t B, int64_t H, int64_t N, int d, float scale, void* o, bool qo,
+                    const int64_t* strides, void* workspace, size_t ws_bytes, Plan* plan) {
   if (kv && (!k || !v)) return fail(BA_ERR_NULL, "k and v must be non-NULL");
   if (qo && (!q || !o)) return fail(BA_ERR_NULL, "q and o must be non-NULL");
   ba_status st = check_dims(B, H, N, d);
@@ -236,9 +280,23 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   if ((kv && (!aligned16(k) || !aligned16(v))) || (qo && (!aligned16(q) || !aligned16(o))) ||
       (bias && !aligned16(bias)))
     return fail(BA_ERR_ALIGN, "q, k, v, o and bias must be 16-byte aligned");
-  const size_t tensor_bytes = static_cast<size_t>(B * H * N * d) * 2;
-  if (qo && (overlaps(o, tensor_bytes, q, tensor_bytes) ||
-             (kv && (overlaps(o, tensor_bytes, k, tensor_bytes) || overlaps(o, tensor_bytes, v, tensor_bytes)))))
+  ba::Strides vs[4];  // q, k, v, o
+  for (int t = 0; t < 4; ++t)
+    vs[t] = strides ? ba::Strides{strides[3 * t], strides[3 * t + 1], strides[3 * t + 2]}
+                    : contiguous_strides(H, N, d);
+  int64_t span[4];
+  static const char* const names[4] = {"q", "k", "v", "o"};
+  for (int t = 0; t < 4; ++t) {
+    span[t] = view_span_bytes(vs[t], B, H, N, d);
+    if (span[t] < 0)
+      return fail(BA_ERR_SHAPE, "%s strides (%lld, %lld, %lld) must be multiples of 8 in [0, 2^40] and span "
+                  "at most 2^50 elements", names[t], (long long)vs[t].sb, (long long)vs[t].sh, (long long)vs[t].sn);
+  }
+  if (qo && !rows_disjoint(vs[3], B, H, N, d))
+    return fail(BA_ERR_SHAPE, "o strides (%lld, %lld, %lld) let two output rows overlap", (long long)vs[3].sb,
+                (long long)vs[3].sh, (long long)vs[3].sn);
+  const size_t qb = span[0], kb = span[1], vb = span[2], ob = span[3];
+  if (qo && (overlaps(o, ob, q, qb) || (kv && (overlaps(o, ob, k, kb) || overlaps(o, ob, v, vb)))))
     return fail(BA_ERR_SHAPE, "o must not overlap q, k or v");
   const int mode = choose_mode(bias != nullptr, gh, gw, N);
   if (mode < 0)
@@ -251,9 +309,9 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
     return fail(BA_ERR_ALIGN, "workspace must be 256-byte aligned");
   if (ws_bytes < static_cast<size_t>(L.total))
     return fail(BA_ERR_WORKSPACE, "workspace too small: %zu < %lld bytes", ws_bytes, (long long)L.total);
-  if (qo && (overlaps(workspace, L.total, o, tensor_bytes) || overlaps(workspace, L.total, q, tensor_bytes)))
+  if (qo && (overlaps(workspace, L.total, o, ob) || overlaps(workspace, L.total, q, qb)))
     return fail(BA_ERR_WORKSPACE, "workspace must not overlap q or o");
-  if (kv && (overlaps(workspace, L.total, k, tensor_bytes) || overlaps(workspace, L.total, v, tensor_bytes)))
+  if (kv && (overlaps(workspace, L.total, k, kb) || overlaps(workspace, L.total, v, vb)))
     return fail(BA_ERR_WORKSPACE, "workspace must not overlap k or v");
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -269,6 +327,8 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   f.kmax_blk = reinterpret_cast<const float*>(ws + L.kmax);
   f.table = static_cast<const uint16_t*>(bias);
   f.o = static_cast<uint16_t*>(o);
+  f.qs = vs[0];
+  f.os = vs[3];
   f.H = static_cast<int>(H);
   f.N = static_cast<int>(N);
   f.Npad = static_cast<int>(L.Npad);
@@ -293,7 +353,7 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   p = ba::PrologueArgs{};
   p.kv = ba::KvJob{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), const_cast<uint32_t*>(f.kop),
                    const_cast<float*>(f.alpha_k), const_cast<float*>(f.kmax_blk), const_cast<uint16_t*>(f.vt),
-                   BH, f.N, f.Npad, d, f.W, (f.W + 1) / 2, f.dpad};
+                   vs[1], vs[2], BH, static_cast<int>(H), f.N, f.Npad, d, f.W, (f.W + 1) / 2, f.dpad};
   p.kv_blocks = BH * (L.Npad / ba::kPackTok);
   p.lds = ba::prologue_lds(d, true);
   if (mode == ba::kBiasRows) {
@@ -307,6 +367,20 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   return BA_OK;
 }
 
+ba_status run_forward(const void* q, const void* k, const void* v, const void* bias, int gh, int gw, int64_t B,
+                      int64_t H, int64_t N, int d, float scale, void* o, const int64_t* strides, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  Plan plan;
+  ba_status st = make_plan(q, k, v, true, bias, gh, gw, B, H, N, d, scale, o, true, strides, workspace,
+                           ws_bytes, &plan);
+  if (st != BA_OK) return st;
+  int err = ba::launch_prologue(plan.p, stream);
+  if (err != 0) return hip_fail(err, "prologue launch");
+  err = ba::launch_attention(plan.f, plan.mode, stream);
+  if (err != 0) return hip_fail(err, "attention launch");
+  return BA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -314,8 +388,8 @@ extern "C" {
 ba_status ba_attention_prepare(const void* k, const void* v, const void* bias, int gh, int gw, int64_t B,
                                int64_t H, int64_t N, int d, void* workspace, size_t ws_bytes, void* stream) {
   Plan plan;
-  ba_status st = make_plan(nullptr, k, v, true, bias, gh, gw, B, H, N, d, 0.0f, nullptr, false, workspace,
-                           ws_bytes, &plan);
+  ba_status st = make_plan(nullptr, k, v, true, bias, gh, gw, B, H, N, d, 0.0f, nullptr, false, nullptr,
+                           workspace, ws_bytes, &plan);
   if (st != BA_OK) return st;
   const int err = ba::launch_prologue(plan.p, stream);
   if (err != 0) return hip_fail(err, "prologue launch");
@@ -326,7 +400,7 @@ ba_status ba_attention_fwd_prepared(const void* q, const void* bias, int gh, int
                                     int64_t N, int d, float scale, void* o, const void* workspace,
                                     size_t ws_bytes, void* stream) {
   Plan plan;
-  ba_status st = make_plan(q, nullptr, nullptr, false, bias, gh, gw, B, H, N, d, scale, o, true,
+  ba_status st = make_plan(q, nullptr, nullptr, false, bias, gh, gw, B, H, N, d, scale, o, true, nullptr,
                            const_cast<void*>(workspace), ws_bytes, &plan);
   if (st != BA_OK) return st;
   const int err = ba::launch_attention(plan.f, plan.mode, stream);
@@ -338,15 +412,16 @@ ba_status ba_attention_fwd(const void* q, const void* k, const void* v,
                            const void* bias, int gh, int gw,
                            int64_t B, int64_t H, int64_t N, int d, float scale,
                            void* o, void* workspace, size_t ws_bytes, void* stream) {
-  Plan plan;
-  ba_status st = make_plan(q, k, v, true, bias, gh, gw, B, H, N, d, scale, o, true, workspace,
-                           ws_bytes, &plan);
-  if (st != BA_OK) return st;
-  int err = ba::launch_prologue(plan.p, stream);
-  if (err != 0) return hip_fail(err, "prologue launch");
-  err = ba::launch_attention(plan.f, plan.mode, stream);
-  if (err != 0) return hip_fail(err, "attention launch");
-  return BA_OK;
+  return run_forward(q, k, v, bias, gh, gw, B, H, N, d, scale, o, nullptr, workspace, ws_bytes, stream);
+}
+
+ba_status ba_attention_fwd_strided(const void* q, const void* k, const void* v,
+                                   const void* bias, int gh, int gw,
+                                   int64_t B, int64_t H, int64_t N, int d, float scale,
+                                   void* o, const int64_t* strides,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+  if (!strides) return fail(BA_ERR_NULL, "strides must be non-NULL");
+  return run_forward(q, k, v, bias, gh, gw, B, H, N, d, scale, o, strides, workspace, ws_bytes, stream);
 }
 
 ba_status ba_qk_int_dot(const uint32_t* qbits, const uint32_t* kbits, int64_t B, int64_t H, int64_t N,

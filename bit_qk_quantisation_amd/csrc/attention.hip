@@ -509,7 +509,7 @@ attn_fwd_kernel(FwdArgs a) {
   // N are all zero: scale 0.
   float qpart = 0.0f;
   {
-    const uint16_t* qrow = a.q + (static_cast<int64_t>(c.bh) * a.N + (c.qi < a.N ? c.qi : 0)) * a.d;
+    const uint16_t* qrow = a.q + token_offset(a.qs, c.bh / a.H, c.head, c.qi < a.N ? c.qi : 0);
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       const int word = 2 * ch + c.lh;
@@ -624,7 +624,7 @@ attn_fwd_kernel(FwdArgs a) {
   }
   const float inv = 1.0f / lsum;
   if (c.qi < a.N) {
-    uint16_t* orow = a.o + (static_cast<int64_t>(c.bh) * a.N + c.qi) * a.d;
+    uint16_t* orow = a.o + token_offset(a.os, c.bh / a.H, c.head, c.qi);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll

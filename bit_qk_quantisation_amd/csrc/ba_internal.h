@@ -36,15 +36,26 @@ struct PackJob {
 };
 
 // Keys and values of one forward, one 64-token tile of one (b, h) per block.
+// Where token n of head (b, h) of a bf16 [B,H,N,d]-shaped view starts, in
+// elements: b * sb + h * sh + n * sn (channels are contiguous).
+struct Strides {
+  int64_t sb, sh, sn;
+};
+
+__host__ __device__ inline int64_t token_offset(const Strides& s, int64_t b, int64_t h, int64_t n) {
+  return b * s.sb + h * s.sh + n * s.sn;
+}
+
 struct KvJob {
-  const uint16_t* k;  // bf16 [BH][N][d]
-  const uint16_t* v;  // bf16 [BH][N][d]
+  const uint16_t* k;  // bf16, strides ks
+  const uint16_t* v;  // bf16, strides vs
   uint32_t* kop;      // fp4 key operands [BH][Npad/64][NCH][64][2][4]
   float* alpha;       // key scales [BH][Npad]
   float* alpha_max;   // largest key scale of each tile [BH][Npad/64]
   uint16_t* vt;       // bf16 [BH][Npad/64][dpad][64], see the prologue
+  Strides ks, vs;
   int64_t BH;
-  int N, Npad, d, W, nch, dpad;
+  int H, N, Npad, d, W, nch, dpad;
 };
 
 struct BiasJob {
@@ -74,7 +85,7 @@ int launch_prologue(const PrologueArgs& a, void* stream);
 enum BiasMode { kBiasNone = 0, kBiasRows = 1, kBiasTable = 2 };
 
 struct FwdArgs {
-  const uint16_t* q;       // bf16 [BH][N][d]: queries, packed in the kernel
+  const uint16_t* q;       // bf16 queries (strides qs), packed in the kernel
   const uint32_t* kop;     // [BH][Npad/64][NCH][64 keys][2][4]: the fp4 +/-1
                            // operand dwords of each key, in LDS tile order
   const float* alpha_k;    // [BH][Npad]
@@ -83,7 +94,8 @@ struct FwdArgs {
   const float* bias_row_max;  // kBiasRows: [H][2gh-1], max |b| log2e per row
   const float* kmax_blk;   // [BH][Npad/64] max alpha_k per 64-token block
   const uint16_t* table;   // kBiasTable: bf16 [H][2gh-1][2gw-1]
-  uint16_t* o;             // bf16 [BH][N][d]
+  uint16_t* o;             // bf16 output (strides os)
+  Strides qs, os;
   int H, N, Npad, d, W, dpad;
   int gh, gw, Lpad;
   int win_rows;            // kBiasRows: rows of the per-tile bias window

@@ -123,19 +123,23 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
   unsigned char* sb = smem + kPackTok * 33 * 4;                             // [64][4W]
   uint16_t* vs = reinterpret_cast<uint16_t*>(sb + kPackTok * 4 * W);       // [64][d+8]
 
-  // The tile's rows are contiguous in K and V: chunk g is token g / C,
-  // channels 8 (g % C) .. + 7.  Tokens past N read as 0.
+  // Chunk g of the tile is token n0 + g / C, channels 8 (g % C) .. + 7; a
+  // token's channels are contiguous, tokens are ks.sn / vs.sn apart.  Tokens
+  // past N read as 0.
   const int rows = job.N - n0 < kPackTok ? job.N - n0 : kPackTok;
   const int total = rows * C;
-  const int64_t off = (bh * job.N + n0) * static_cast<int64_t>(d);
+  const int64_t b = bh / job.H, h = bh - b * job.H;
+  const uint16_t* kbase = job.k + token_offset(job.ks, b, h, n0);
+  const uint16_t* vbase = job.v + token_offset(job.vs, b, h, n0);
   uint4 kr[kMaxChunks], vr[kMaxChunks];
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
     const int g = threadIdx.x + i * kThreads;
     kr[i] = vr[i] = make_uint4(0u, 0u, 0u, 0u);
     if (g < total) {
-      kr[i] = *reinterpret_cast<const uint4*>(job.k + off + static_cast<int64_t>(g) * 8);
-      vr[i] = *reinterpret_cast<const uint4*>(job.v + off + static_cast<int64_t>(g) * 8);
+      const int tok = g / C, ch = g - tok * C;
+      kr[i] = *reinterpret_cast<const uint4*>(kbase + tok * job.ks.sn + ch * 8);
+      vr[i] = *reinterpret_cast<const uint4*>(vbase + tok * job.vs.sn + ch * 8);
     }
   }
 #pragma unroll

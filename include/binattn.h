@@ -128,6 +128,29 @@ ba_status ba_attention_fwd(const void* q, const void* k, const void* v,
                            void* o, void* workspace, size_t ws_bytes,
                            void* stream);
 
+/* ba_attention_fwd_strided -- ba_attention_fwd on strided views, e.g. the
+ * [B,N,H,d] tensors a QKV projection writes, or q, k and v as three slices
+ * of one [B,N,3,H,d] tensor, without a transpose first.
+ *   strides    host array of 12 int64 element strides: the (batch, head,
+ *              token) strides of q, then k, then v, then o.  Row (b,h,n) of
+ *              a view starts at ptr + b*sb + h*sh + n*sn elements and holds
+ *              d contiguous bf16 channels.  ba_attention_fwd is this call
+ *              with (H*N*d, N*d, d) for all four.
+ * Every stride must be a multiple of 8 (rows stay 16-byte aligned) in
+ * [0, 2^40]; a view may span at most 2^50 elements.  Input views may repeat
+ * rows (stride 0 broadcasts); o's strides must keep its rows apart (taken
+ * in order of increasing stride, each stride at least the extent the
+ * smaller ones reach), and o's span must not overlap the spans of q, k, v or
+ * the workspace.  The strides are read before the call returns.  Other
+ * arguments, the workspace size and the errors are those of
+ * ba_attention_fwd (BA_ERR_NULL also for strides == NULL, BA_ERR_SHAPE for
+ * strides that break the rules above). */
+ba_status ba_attention_fwd_strided(const void* q, const void* k, const void* v,
+                                   const void* bias, int gh, int gw,
+                                   int64_t B, int64_t H, int64_t N, int d, float scale,
+                                   void* o, const int64_t* strides,
+                                   void* workspace, size_t ws_bytes, void* stream);
+
 /* The two halves of ba_attention_fwd, for callers that time or schedule the
  * two kernels separately.
  *

@@ -181,3 +181,63 @@ def test_split_entry_validation(lib):
     assert lib.ba_attention_fwd_prepared(A, None, 0, 0, 1, 2, 64, 64, float("inf"), A + 3 * GB, ws, 1 << 40,
                                          None) == 2
     assert lib.ba_attention_fwd_prepared(A, None, 0, 0, 1, 2, 64, 64, 0.125, A + 16, ws, 1 << 40, None) == 2
+
+
+def fwd_strided(lib, strides, q=A, k=A + GB, v=A + 2 * GB, o=A + 3 * GB, B=1, H=2, N=64, d=64,
+                ws_bytes=1 << 40):
+    arr = None if strides is None else (ctypes.c_int64 * 12)(*strides)
+    return lib.ba_attention_fwd_strided(q, k, v, None, 0, 0, B, H, N, d, 0.125, o, arr,
+                                        A + 4 * GB, ws_bytes, None)
+
+
+# Stride checks come before the workspace size check, so a call with valid
+# strides and a 16-byte workspace stops with BA_ERR_WORKSPACE: nothing is
+# launched on the fake addresses these tests use.
+WS_TOO_SMALL = 5
+
+
+def bnhd(B, H, N, d):
+    """(batch, head, token) strides of a [B,N,H,d] tensor viewed as [B,H,N,d]."""
+    return (N * H * d, d, H * d)
+
+
+def test_strided_validation(lib):
+    """Checks the strided entry makes before it launches anything."""
+    s = bnhd(1, 2, 64, 64) * 4
+    assert fwd_strided(lib, None) == 1
+    assert b"strides" in lib.ba_last_error()
+    bad = list(s)
+    bad[2] = 68                                    # q token stride not a multiple of 8
+    assert fwd_strided(lib, bad) == 2
+    bad = list(s)
+    bad[4] = -8                                    # negative k head stride
+    assert fwd_strided(lib, bad) == 2
+    bad = list(s)
+    bad[9:12] = [0, 64, 64]                        # o: heads 0 and 1 share rows 1.. of head 0
+    assert fwd_strided(lib, bad) == 2
+    assert b"overlap" in lib.ba_last_error()
+    bad = list(s)
+    bad[9:12] = [8192, 64, 32]                     # o rows 32 channels apart, d = 64
+    assert fwd_strided(lib, bad) == 2
+    # q, k and v as slices of one [B,N,3,H,d] tensor; o written over it
+    qkv = (64 * 3 * 2 * 64, 64, 3 * 2 * 64)
+    assert fwd_strided(lib, list(qkv) * 3 + list(bnhd(1, 2, 64, 64)),
+                       q=A, k=A + 256, v=A + 512, o=A + 1024) == 2
+    assert b"o must not overlap" in lib.ba_last_error()
+    # broadcast inputs (stride 0) are fine for reads
+    assert fwd_strided(lib, [0, 0, 64] * 3 + [2 * 64 * 64, 64 * 64, 64], o=A + 8 * GB,
+                       ws_bytes=16) == WS_TOO_SMALL
+
+
+def test_rows_disjoint_rule(lib):
+    """The output-layout rule on a few permutations: every dense layout of
+    [B,H,N,d] passes, a padded one passes, and a folded one fails."""
+    B, H, N, d = 2, 3, 16, 64
+    ok = [(H * N * d, N * d, d), bnhd(B, H, N, d), (d, B * N * d, B * d),
+          (H * N * (d + 64), N * (d + 64), d + 64)]
+    for o in ok:
+        st = fwd_strided(lib, list(bnhd(B, H, N, d)) * 3 + list(o), o=A + 8 * GB, B=B, H=H, N=N,
+                         ws_bytes=16)
+        assert st == WS_TOO_SMALL, (o, lib.ba_last_error())
+    assert fwd_strided(lib, list(bnhd(B, H, N, d)) * 3 + [N * d, N * d, d], o=A + 8 * GB,
+                       B=B, H=H, N=N) == 2
