@@ -7,6 +7,7 @@ nothing from it.
 
 from .dense_fp64 import (  # noqa: F401
     binary_attention,
+    binary_attention_dense_bias_rows,
     binary_attention_rows,
     binary_scores,
     pack_sign_bits,

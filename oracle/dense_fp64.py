@@ -246,3 +246,31 @@ def binary_attention(q, k, v, table=None, gh: int = 0, gw: int = 0,
         "alpha_k": token_scale(kf),
         "O": o,
     }
+
+
+def binary_attention_dense_bias_rows(q, k, v, bias, scale=None, rows=None,
+                                     keep=False) -> dict:
+    """O = softmax(S) V with a dense bias, for a subset of query rows.
+
+    The bias term b_ij of es page, section 2, item "Mejora mediante Sesgo"
+    (ko page, section 2 (b).2) may be dense: one learnable value per query,
+    key and head.  Here it is given in full:
+
+    bias: [Bb, H, N, N] with Bb = 1 (one bias for the whole batch) or Bb = B;
+    S[b, h, i, j] = scale * alpha_q,i * alpha_k,j * D_ij + bias[b', h, i, j]
+    with b' = b when Bb = B and b' = 0 when Bb = 1.
+    """
+    vf = _f64(v)
+    sc = binary_scores(q, k, None, 0, 0, scale, rows)
+    bf = _f64(bias)
+    bq, hq, n = vf.shape[0], vf.shape[1], vf.shape[2]
+    if bf.ndim != 4 or bf.shape[1:] != (hq, n, n) or bf.shape[0] not in (1, bq):
+        raise ValueError("bias must be [1 or B, H, N, N]")
+    s = sc["S"] + bf[:, :, sc["rows"], :]
+    p = softmax_rows(s)
+    o = np.matmul(p, vf)
+    out = {"O": o, "alpha_q": sc["alpha_q"], "alpha_k": sc["alpha_k"],
+           "rows": sc["rows"]}
+    if keep:
+        out.update(S=s, P=p, D=sc["D"])
+    return out

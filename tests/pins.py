@@ -329,6 +329,69 @@ def sheppard(ob):
         assert abs(est - want) < 5.0 / math.sqrt(n), (rho, est, want)
 
 
+def dense_bias_matches_table(ob):
+    """A dense bias written out from a relative-position table gives the
+    table path's O (the table path is pinned on its own above); the table's
+    bias is not symmetric in (i, j), so this also fixes which index is the
+    query."""
+    rng = _rng(22)
+    for (b, h, gh, gw, d) in ((2, 2, 3, 4, 16), (1, 3, 2, 5, 40)):
+        n = gh * gw
+        q = _bf16_values(rng, (b, h, n, d))
+        k = _bf16_values(rng, (b, h, n, d))
+        v = _bf16_values(rng, (b, h, n, d))
+        t = _bf16_values(rng, (h, 2 * gh - 1, 2 * gw - 1), 0.8)
+        dense = _dense_bias_loops(t, gh, gw)[None]
+        got = ob.binary_attention_dense_bias_rows(q, k, v, dense)["O"]
+        ref = ob.binary_attention(q, k, v, t, gh, gw)["O"]
+        assert np.allclose(got, ref, rtol=0, atol=1e-13), np.abs(got - ref).max()
+
+
+def dense_bias_one_hot(ob):
+    """With Q = 0 the scores are the bias alone.  A bias of 40 at (i, pi(i))
+    for a per-batch permutation pi sends query i almost all of its mass to
+    key pi(i): O_i = V_pi(i) up to e^-40."""
+    rng = _rng(23)
+    b, h, n, d = 2, 2, 7, 5
+    q = np.zeros((b, h, n, d))
+    k = _bf16_values(rng, (b, h, n, d))
+    v = _bf16_values(rng, (b, h, n, d))
+    bias = np.zeros((b, h, n, n))
+    perm = [[rng.permutation(n) for _ in range(h)] for _ in range(b)]
+    for bi in range(b):
+        for hi in range(h):
+            bias[bi, hi, np.arange(n), perm[bi][hi]] = 40.0
+    o = ob.binary_attention_dense_bias_rows(q, k, v, bias)["O"]
+    for bi in range(b):
+        for hi in range(h):
+            want = v[bi, hi, perm[bi][hi]]
+            assert np.allclose(o[bi, hi], want, rtol=0, atol=1e-14), (bi, hi)
+
+
+def dense_bias_row_shift_and_broadcast(ob):
+    """Adding c_i to a whole bias row changes nothing (softmax ignores a
+    per-row shift), a zero bias is no bias, and a [1, H, N, N] bias acts
+    like the same bias repeated for every batch entry."""
+    rng = _rng(24)
+    b, h, n, d = 3, 2, 6, 24
+    q = _bf16_values(rng, (b, h, n, d))
+    k = _bf16_values(rng, (b, h, n, d))
+    v = _bf16_values(rng, (b, h, n, d))
+    base = ob.binary_attention(q, k, v)["O"]
+    zero = ob.binary_attention_dense_bias_rows(q, k, v, np.zeros((1, h, n, n)))["O"]
+    assert np.allclose(zero, base, rtol=0, atol=1e-15)
+    shift = np.broadcast_to(rng.normal(size=(b, h, n, 1)) * 5.0, (b, h, n, n))
+    got = ob.binary_attention_dense_bias_rows(q, k, v, shift)["O"]
+    assert np.allclose(got, base, rtol=0, atol=1e-13)
+    one = rng.normal(size=(1, h, n, n))
+    a1 = ob.binary_attention_dense_bias_rows(q, k, v, one)["O"]
+    a2 = ob.binary_attention_dense_bias_rows(q, k, v, np.repeat(one, b, axis=0))["O"]
+    assert np.array_equal(a1, a2)
+    rows = np.array([5, 0, 3])
+    part = ob.binary_attention_dense_bias_rows(q, k, v, one, rows=rows)["O"]
+    assert np.allclose(part, a1[:, :, rows, :], rtol=0, atol=1e-15)
+
+
 ALL_PINS = [
     golden_hand_example,
     bits_definition,
@@ -343,4 +406,7 @@ ALL_PINS = [
     single_token,
     brute_force_tiny,
     sheppard,
+    dense_bias_matches_table,
+    dense_bias_one_hot,
+    dense_bias_row_shift_and_broadcast,
 ]

@@ -122,6 +122,24 @@ def _attention_v_transposed(q, k, v, table=None, gh=0, gw=0, scale=None,
     return out
 
 
+
+def _dense_factory(**kw):
+    """A copy of binary_attention_dense_bias_rows with one planted mistake."""
+    def dense(q, k, v, bias, scale=None, rows=None, keep=False):
+        vf = ob._f64(v)
+        sc = ob.binary_scores(q, k, None, 0, 0, scale, rows)
+        bf = ob._f64(bias)
+        if kw.get("transposed"):
+            bf = np.swapaxes(bf, -1, -2)
+        if kw.get("first_batch_only"):
+            bf = bf[:1]
+        s = sc["S"] if kw.get("dropped") else sc["S"] + bf[:, :, sc["rows"], :]
+        p = ob.softmax_rows(s)
+        return {"O": np.matmul(p, vf), "alpha_q": sc["alpha_q"], "alpha_k": sc["alpha_k"],
+                "rows": sc["rows"]}
+    return dense
+
+
 MUTATIONS = {
     "sign_zero_is_negative": ("sign_pm1", _sign_zero_negative),
     "sign_from_signbit": ("sign_pm1", _sign_from_signbit),
@@ -141,6 +159,10 @@ MUTATIONS = {
     "softmax_over_columns": ("softmax_rows", _softmax_columns),
     "softmax_not_normalised": ("softmax_rows", _softmax_no_normalise),
     "pv_transposed": ("binary_attention_rows", _attention_v_transposed),
+    "dense_bias_transposed": ("binary_attention_dense_bias_rows", _dense_factory(transposed=True)),
+    "dense_bias_dropped": ("binary_attention_dense_bias_rows", _dense_factory(dropped=True)),
+    "dense_bias_first_batch_only": ("binary_attention_dense_bias_rows",
+                                    _dense_factory(first_batch_only=True)),
 }
 
 
