@@ -2,7 +2,7 @@
 """Benchmark of the BinaryAttention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--layout bhnd|bnhd|qkv]
+                    [--layout bhnd|bnhd|qkv] [--bias table|dense|dense-batch]
 
 One step is one full forward (ba_attention_prepare + ba_attention_fwd_prepared,
 i.e. exactly ba_attention_fwd) over the resident bf16 inputs of the chosen
@@ -16,6 +16,12 @@ prologue.
 v as the slices of one [B,N,3,H,d] tensor and writes a [B,N,H,d] o.  Both go
 through ba_attention_fwd_strided, one call per step, so only the whole step
 is timed and the roofline figure is taken over the step.
+
+--bias dense replaces the workload's relative-position table by a dense bf16
+bias [H,N,N] shared by the batch (dense-batch: [B,H,N,N]), drawn N(0, 0.02);
+the step is then ba_attention_prepare + ba_attention_fwd_dense_bias_prepared,
+and the roofline object names whichever bound (matrix cores or HBM) the fused
+kernel is closer to.
 
 Printed: one JSON line on stdout with the throughput in TFLOP-eq/s
 (4*B*H*N^2*d per step, the FLOPs of dense QK^T and P.V), the fused kernel's
@@ -84,7 +90,7 @@ def measured_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def algorithmic_bytes(w, npad):
+def algorithmic_bytes(w, npad, dense_bytes=None):
     """Compulsory HBM bytes of the two kernels of one step: the prologue reads
     K and V and writes the fp4 key operands, the key scales (and their maxima
     per 64 tokens), V^T and the bias rows; the fused kernel reads Q and all of
@@ -103,6 +109,8 @@ def algorithmic_bytes(w, npad):
             lpad += 4
         rows = w.H * (2 * w.gh - 1 + 16) * 4 * lpad * 4
     table = w.H * (2 * w.gh - 1) * (2 * w.gw - 1) * 2
+    if dense_bytes is not None:  # no table: the fused kernel reads the dense bias once
+        return 2 * tok * w.d * 2 + keys + vt, tok * w.d * 2 + keys + vt + dense_bytes + tok * w.d * 2
     prologue = 2 * tok * w.d * 2 + keys + vt + ((table + rows) if rows else 0)
     fused = tok * w.d * 2 + keys + vt + (rows if rows else table) + tok * w.d * 2
     return prologue, fused
@@ -167,6 +175,8 @@ def main() -> int:
                     help="host time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--layout", choices=("bhnd", "bnhd", "qkv"), default="bhnd",
                     help="memory layout of q, k, v and o (see above)")
+    ap.add_argument("--bias", choices=("table", "dense", "dense-batch"), default="table",
+                    help="bias form (see above)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB "
                          "(reference kernel for HBM counter calibration)")
@@ -198,6 +208,15 @@ def main() -> int:
     v = inp["v"].to(dev)
     table = inp["table"].to(dev) if inp["table"] is not None else None
     gh, gw = inp["gh"], inp["gw"]
+    dense = None
+    if args.bias != "table":
+        if args.layout != "bhnd":
+            log("--bias dense runs with the contiguous layout only")
+            return 2
+        table, gh, gw = None, 0, 0
+        Bb = w.B if args.bias == "dense-batch" else 1
+        dense = workloads.make_dense_bias(Bb, w.H, w.N, seed=w.seed + 100).to(dev)
+        dsb = 0 if Bb == 1 else dense.stride(0)
     B, H, N, d = w.B, w.H, w.N, w.d
     scale = 1.0 / math.sqrt(d)
     out = torch.empty_like(q)
@@ -215,6 +234,12 @@ def main() -> int:
     def fused():
         bq.check(lib, lib.ba_attention_fwd_prepared(q.data_ptr(), tp, gh, gw, B, H, N, d, scale, out.data_ptr(),
                                                     wsp, nbytes, sp))
+
+    if dense is not None:
+        def fused():  # noqa: F811
+            bq.check(lib, lib.ba_attention_fwd_dense_bias_prepared(
+                q.data_ptr(), dense.data_ptr(), dsb, dense.stride(1), dense.stride(2), B, H, N, d, scale,
+                out.data_ptr(), wsp, nbytes, sp))
 
     split = args.layout == "bhnd"
     if not split:
@@ -286,11 +311,16 @@ def main() -> int:
     value = flop / (ms_step * 1e-3) / 1e12
     fused_tf = flop / (fus_ms * 1e-3) / 1e12
     npad = (N + 127) // 128 * 128
-    pro_bytes, fus_bytes = algorithmic_bytes(w, npad)
-    traffic = measured_traffic(name) if split else None
+    dense_bytes = None if dense is None else dense.numel() * 2
+    pro_bytes, fus_bytes = algorithmic_bytes(w, npad, dense_bytes)
+    traffic = measured_traffic(name) if split and dense is None else None
+    fused_gbs = fus_bytes / (fus_ms * 1e-3) / 1e9
+    hbm_bound = dense is not None and fused_gbs / PEAK_HBM_GBS > fused_tf / PEAK_MFMA_COMPOSITE
 
     baseline = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and dense is not None:
+        log("[bench] no CPU baseline with --bias dense")
+    elif args.cpu_seconds > 0:
         baseline = cpu_baseline(w, inp, out, args.cpu_seconds)
 
     rec = {
@@ -308,7 +338,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {**w.describe(), "qk": "1-bit signs as +/-1 fp4 on MFMA (exact integer dots)",
                    "pv": "bf16 MFMA, fp32 accumulate", "softmax": "fp32, base 2",
-                   "parallelism": "single GPU", "layout": args.layout},
+                   "parallelism": "single GPU", "layout": args.layout, "bias": args.bias},
         "roofline": {
             "bound": "mfma",
             "kernel": "attn_fwd_kernel (fused)" if split else "whole step (prologue + fused, one strided call)",
@@ -316,6 +346,14 @@ def main() -> int:
             "peak": round(PEAK_MFMA_COMPOSITE, 1),
             "unit": "TFLOP/s",
             "frac": round(fused_tf / PEAK_MFMA_COMPOSITE, 4),
+            "traffic": traffic,
+        } if not hbm_bound else {
+            "bound": "hbm",
+            "kernel": "attn_fwd_kernel (fused, dense bias)",
+            "achieved": round(fused_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(fused_gbs / PEAK_HBM_GBS, 4),
             "traffic": traffic,
         },
         "cpu_baseline": baseline,
@@ -328,6 +366,8 @@ def main() -> int:
             "prologue_algorithmic_GBps": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1) if split else None,
             "prologue_frac_of_hbm": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if split else None,
             "fused_algorithmic_bytes": fus_bytes,
+            "fused_algorithmic_GBps": round(fused_gbs, 1),
+            "fused_frac_of_composite_mfma_roofline": round(fused_tf / PEAK_MFMA_COMPOSITE, 4),
             "device": torch.cuda.get_device_name(dev),
         },
     }

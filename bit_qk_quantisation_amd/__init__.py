@@ -9,6 +9,7 @@ If the library is missing the calls raise; there is no CPU fallback.
     attention_fwd(q, k, v, table, gh, gw)  -> O (bf16); q, k, v and out may be
                                               strided [B,H,N,d] views (e.g.
                                               a [B,N,H,d] tensor transposed)
+    attention_fwd_dense_bias(q, k, v, bias) -> O (bf16); bias [1 or B, H, N, N]
     qk_int_dot(qbits, kbits, d, route)     -> D (int32)
     workspace_bytes(B, H, N, d, gh, gw)    -> int
 """
@@ -23,7 +24,7 @@ import torch
 from ._lib import (BinAttnError, EXPORTS, ROUTE_MFMA_FP4,  # noqa: F401
                    ROUTE_VALU_POPCOUNT, check, load)
 
-__all__ = ["pack_signs", "attention_fwd", "qk_int_dot", "workspace_bytes",
+__all__ = ["pack_signs", "attention_fwd", "attention_fwd_dense_bias", "qk_int_dot", "workspace_bytes",
            "pack_words", "BinAttnError", "ROUTE_MFMA_FP4", "ROUTE_VALU_POPCOUNT",
            "Workspace"]
 
@@ -147,6 +148,45 @@ def attention_fwd(q, k, v, table=None, gh: int = 0, gw: int = 0, scale=None,
             q.data_ptr(), k.data_ptr(), v.data_ptr(), tp, int(gh), int(gw),
             B, H, N, d, float(scale), out.data_ptr(), strides, aligned, ws_len,
             _stream(q.device)))
+    return out
+
+
+def attention_fwd_dense_bias(q, k, v, bias, scale=None, out=None,
+                             workspace: Workspace | None = None):
+    """BinaryAttention forward with a dense bias: bf16 q, k, v [B,H,N,d]
+    views (channels contiguous) and a bf16 bias [1 or B, H, N, N] whose rows
+    are contiguous and whose strides are multiples of 8 elements (size-1
+    batch: shared by the whole batch) -> bf16 O [B,H,N,d]."""
+    lib = load()
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need_view(t, name)
+    if q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k and v must have the same shape")
+    B, H, N, d = q.shape
+    _need_view(bias, "bias")
+    if bias.shape[1:] != (H, N, N) or bias.shape[0] not in (1, B):
+        raise ValueError(f"bias must be [1 or {B}, {H}, {N}, {N}], got {tuple(bias.shape)}")
+    sb = 0 if bias.shape[0] == 1 else bias.stride(0)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_view(out, "out")
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    nbytes = lib.ba_workspace_bytes(B, H, N, d, 0, 0)
+    if nbytes == 0:
+        raise BinAttnError(2, f"unsupported problem B={B} H={H} N={N} d={d}")
+    ws = (workspace or _default_ws).get(q.device, nbytes)
+    base = ws.data_ptr()
+    aligned = (base + 255) // 256 * 256
+    views = (q, k, v, out)
+    strides = (ctypes.c_int64 * 12)(*[t.stride(i) for t in views for i in range(3)])
+    check(lib, lib.ba_attention_fwd_dense_bias(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), bias.data_ptr(), sb, bias.stride(1),
+        bias.stride(2), B, H, N, d, float(scale), out.data_ptr(), strides, aligned,
+        ws.numel() - (aligned - base), _stream(q.device)))
     return out
 
 

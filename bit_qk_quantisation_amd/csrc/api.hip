@@ -250,6 +250,12 @@ size_t ba_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int gh, int gw
 
 namespace {
 
+// A dense bias: bias(b, h, i, j) at ptr + b*sb + h*sh + i*ld + j elements.
+struct DenseBias {
+  const void* ptr;
+  int64_t sb, sh, ld;
+};
+
 // Everything one forward needs: validated sizes, workspace sections and the
 // arguments of both kernels.
 struct Plan {
@@ -263,9 +269,11 @@ struct Plan {
 // output).
 // `strides` holds the (batch, head, token) element strides of q, k, v and o,
 // in that order (12 values), or is NULL for contiguous [B,H,N,d] tensors.
+// `dense` (or NULL) is a dense bias; it excludes a bias table.
 ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const void* bias, int gh, int gw,
                     int64_t B, int64_t H, int64_t N, int d, float scale, void* o, bool qo,
-                    const int64_t* strides, void* workspace, size_t ws_bytes, Plan* plan) {
+                    const int64_t* strides, const DenseBias* dense, void* workspace, size_t ws_bytes,
+                    Plan* plan) {
   if (kv && (!k || !v)) return fail(BA_ERR_NULL, "k and v must be non-NULL");
   if (qo && (!q || !o)) return fail(BA_ERR_NULL, "q and o must be non-NULL");
   ba_status st = check_dims(B, H, N, d);
@@ -298,12 +306,33 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   const size_t qb = span[0], kb = span[1], vb = span[2], ob = span[3];
   if (qo && (overlaps(o, ob, q, qb) || (kv && (overlaps(o, ob, k, kb) || overlaps(o, ob, v, vb)))))
     return fail(BA_ERR_SHAPE, "o must not overlap q, k or v");
-  const int mode = choose_mode(bias != nullptr, gh, gw, N);
+  if (dense && qo) {
+    if (bias) return fail(BA_ERR_SHAPE, "a dense bias and a bias table cannot be combined");
+    if (!dense->ptr) return fail(BA_ERR_NULL, "bias must be non-NULL");
+    if (!aligned16(dense->ptr)) return fail(BA_ERR_ALIGN, "bias must be 16-byte aligned");
+    const int64_t st[3] = {dense->sb, dense->sh, dense->ld}, ext[3] = {B, H, N};
+    int64_t bspan = N;  // elements from the first to one past the last
+    for (int i = 0; i < 3; ++i) {
+      if (st[i] < 0 || st[i] > kMaxStride || st[i] % 8 != 0)
+        return fail(BA_ERR_SHAPE, "dense bias strides (%lld, %lld, %lld) must be multiples of 8 in [0, 2^40]",
+                    (long long)dense->sb, (long long)dense->sh, (long long)dense->ld);
+      if (ext[i] > 1 && st[i] > (kMaxSpan - bspan) / (ext[i] - 1))
+        return fail(BA_ERR_SHAPE, "dense bias spans more than 2^50 elements");
+      bspan += st[i] * (ext[i] - 1);
+    }
+    const int64_t npad = round_up(N, ba::kNAlign);
+    if ((npad * dense->ld + npad) * 2 >= (int64_t{1} << 32))
+      return fail(BA_ERR_UNSUPPORTED, "dense bias of one head must span less than 4 GiB ((N rounded up to 128) "
+                  "* (ld + 1) * 2 bytes)");
+    if (overlaps(o, ob, dense->ptr, static_cast<size_t>(bspan) * 2))
+      return fail(BA_ERR_SHAPE, "o must not overlap the bias");
+  }
+  const int mode = dense ? static_cast<int>(ba::kBiasDense) : choose_mode(bias != nullptr, gh, gw, N);
   if (mode < 0)
     return fail(BA_ERR_UNSUPPORTED,
                 "bias grid %dx%d: the table rows do not fit the tile window and the table exceeds 48 KiB",
                 gh, gw);
-  const Layout L = layout(B, H, N, d, bias != nullptr, gh, gw);
+  const Layout L = layout(B, H, N, d, bias != nullptr, dense ? 0 : gh, dense ? 0 : gw);
   if (!workspace) return fail(BA_ERR_WORKSPACE, "workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(BA_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -326,9 +355,17 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   f.bias_row_max = reinterpret_cast<const float*>(ws + L.rowmax);
   f.kmax_blk = reinterpret_cast<const float*>(ws + L.kmax);
   f.table = static_cast<const uint16_t*>(bias);
+  if (dense) {
+    f.dense = static_cast<const uint16_t*>(dense->ptr);
+    f.dsb = dense->sb;
+    f.dsh = dense->sh;
+    f.dld = dense->ld;
+    f.dense_shared = (dense->sb == 0 && B > 1) ? 1 : 0;
+  }
   f.o = static_cast<uint16_t*>(o);
   f.qs = vs[0];
   f.os = vs[3];
+  f.B = static_cast<int>(B);
   f.H = static_cast<int>(H);
   f.N = static_cast<int>(N);
   f.Npad = static_cast<int>(L.Npad);
@@ -339,13 +376,13 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   f.gw = gw;
   f.Lpad = static_cast<int>(L.Lpad);
   f.win_rows = (mode == ba::kBiasRows) ? window_rows(N, gw) : 0;
-  f.qscale = scale * ba::kLog2e;
+  f.qscale = dense ? scale : scale * ba::kLog2e;  // dense logits stay in natural units
   f.nqt = static_cast<int>(L.Npad / ba::kBM);
   const int64_t nwg = BH * f.nqt;
   if (nwg > 0x7fffffff) return fail(BA_ERR_SHAPE, "too many workgroups");
   f.nwg = static_cast<int>(nwg);
   f.xcd_remap = (f.nwg % 8 == 0) ? 1 : 0;
-  const int static_lds = ba::fwd_static_lds(f.dpad), table_lds = ba::fwd_table_lds(f, mode);
+  const int static_lds = ba::fwd_static_lds(f.dpad, mode), table_lds = ba::fwd_table_lds(f, mode);
   if (static_lds + table_lds > kMaxLds) return fail(BA_ERR_UNSUPPORTED, "bias window does not fit in LDS");
   f.dyn_lds = fused_dynamic_lds(static_lds, table_lds, nwg);
 
@@ -368,10 +405,10 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
 }
 
 ba_status run_forward(const void* q, const void* k, const void* v, const void* bias, int gh, int gw, int64_t B,
-                      int64_t H, int64_t N, int d, float scale, void* o, const int64_t* strides, void* workspace,
-                      size_t ws_bytes, void* stream) {
+                      int64_t H, int64_t N, int d, float scale, void* o, const int64_t* strides,
+                      const DenseBias* dense, void* workspace, size_t ws_bytes, void* stream) {
   Plan plan;
-  ba_status st = make_plan(q, k, v, true, bias, gh, gw, B, H, N, d, scale, o, true, strides, workspace,
+  ba_status st = make_plan(q, k, v, true, bias, gh, gw, B, H, N, d, scale, o, true, strides, dense, workspace,
                            ws_bytes, &plan);
   if (st != BA_OK) return st;
   int err = ba::launch_prologue(plan.p, stream);
@@ -388,7 +425,7 @@ extern "C" {
 ba_status ba_attention_prepare(const void* k, const void* v, const void* bias, int gh, int gw, int64_t B,
                                int64_t H, int64_t N, int d, void* workspace, size_t ws_bytes, void* stream) {
   Plan plan;
-  ba_status st = make_plan(nullptr, k, v, true, bias, gh, gw, B, H, N, d, 0.0f, nullptr, false, nullptr,
+  ba_status st = make_plan(nullptr, k, v, true, bias, gh, gw, B, H, N, d, 0.0f, nullptr, false, nullptr, nullptr,
                            workspace, ws_bytes, &plan);
   if (st != BA_OK) return st;
   const int err = ba::launch_prologue(plan.p, stream);
@@ -400,7 +437,21 @@ ba_status ba_attention_fwd_prepared(const void* q, const void* bias, int gh, int
                                     int64_t N, int d, float scale, void* o, const void* workspace,
                                     size_t ws_bytes, void* stream) {
   Plan plan;
-  ba_status st = make_plan(q, nullptr, nullptr, false, bias, gh, gw, B, H, N, d, scale, o, true, nullptr,
+  ba_status st = make_plan(q, nullptr, nullptr, false, bias, gh, gw, B, H, N, d, scale, o, true, nullptr, nullptr,
+                           const_cast<void*>(workspace), ws_bytes, &plan);
+  if (st != BA_OK) return st;
+  const int err = ba::launch_attention(plan.f, plan.mode, stream);
+  if (err != 0) return hip_fail(err, "attention launch");
+  return BA_OK;
+}
+
+ba_status ba_attention_fwd_dense_bias_prepared(const void* q, const void* bias, int64_t bias_sb, int64_t bias_sh,
+                                               int64_t bias_ld, int64_t B, int64_t H, int64_t N, int d,
+                                               float scale, void* o, const void* workspace, size_t ws_bytes,
+                                               void* stream) {
+  Plan plan;
+  const DenseBias dense{bias, bias_sb, bias_sh, bias_ld};
+  ba_status st = make_plan(q, nullptr, nullptr, false, nullptr, 0, 0, B, H, N, d, scale, o, true, nullptr, &dense,
                            const_cast<void*>(workspace), ws_bytes, &plan);
   if (st != BA_OK) return st;
   const int err = ba::launch_attention(plan.f, plan.mode, stream);
@@ -412,7 +463,7 @@ ba_status ba_attention_fwd(const void* q, const void* k, const void* v,
                            const void* bias, int gh, int gw,
                            int64_t B, int64_t H, int64_t N, int d, float scale,
                            void* o, void* workspace, size_t ws_bytes, void* stream) {
-  return run_forward(q, k, v, bias, gh, gw, B, H, N, d, scale, o, nullptr, workspace, ws_bytes, stream);
+  return run_forward(q, k, v, bias, gh, gw, B, H, N, d, scale, o, nullptr, nullptr, workspace, ws_bytes, stream);
 }
 
 ba_status ba_attention_fwd_strided(const void* q, const void* k, const void* v,
@@ -421,7 +472,16 @@ ba_status ba_attention_fwd_strided(const void* q, const void* k, const void* v,
                                    void* o, const int64_t* strides,
                                    void* workspace, size_t ws_bytes, void* stream) {
   if (!strides) return fail(BA_ERR_NULL, "strides must be non-NULL");
-  return run_forward(q, k, v, bias, gh, gw, B, H, N, d, scale, o, strides, workspace, ws_bytes, stream);
+  return run_forward(q, k, v, bias, gh, gw, B, H, N, d, scale, o, strides, nullptr, workspace, ws_bytes, stream);
+}
+
+ba_status ba_attention_fwd_dense_bias(const void* q, const void* k, const void* v,
+                                      const void* bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_ld,
+                                      int64_t B, int64_t H, int64_t N, int d, float scale,
+                                      void* o, const int64_t* strides,
+                                      void* workspace, size_t ws_bytes, void* stream) {
+  const DenseBias dense{bias, bias_sb, bias_sh, bias_ld};
+  return run_forward(q, k, v, nullptr, 0, 0, B, H, N, d, scale, o, strides, &dense, workspace, ws_bytes, stream);
 }
 
 ba_status ba_qk_int_dot(const uint32_t* qbits, const uint32_t* kbits, int64_t B, int64_t H, int64_t N,

@@ -17,8 +17,9 @@
 //         already holds, per lane, one query and 8 keys of each 16-key step,
 //         which is the B-operand layout, so P never leaves registers.  The
 //         O^T accumulator keeps one query per lane, so the softmax scalars
-//         are per lane.  V^T carries rows of ones (or an extra constant
-//         operand block), so the same product also yields the row sums l.
+//         are per lane.  V^T carries rows of ones, so the same product
+//         also yields the row sums l (when d % 32 == 0 they are added on the
+//         vector ALU instead).
 //
 // Workgroup: 4 waves x 32 queries = 128 queries of one (b, h).  Each wave
 // packs its own 32 queries (signs and alpha_q) from bf16 at the start.  Key
@@ -44,28 +45,37 @@ namespace ba {
 // |V| < 2^80.
 constexpr float kFastMaxLogit = 32.0f;
 
+// Bias storage per tile buffer, by bias mode (modes that do not use an
+// array keep a token 16 bytes of it).
+template <int BIAS>
+struct BiasSizes {
+  static constexpr int kWin =
+      BIAS == kBiasRows ? kMaxWindowFloats : (BIAS == kBiasDense ? kDenseTileFloats : 4);
+  static constexpr int kGk = BIAS == kBiasTable ? kBN : 4;
+};
+
 // One LDS tile buffer.  The kernel declares two of them as separate LDS
 // objects, so the compiler can tell the asynchronous copies into one buffer
 // from the reads of the other and need not wait for the copies early.
-template <int NCH, int CB>
+template <int NCH, int CB, int BIAS>
 struct TileBuf {
-  v4i k[NCH * kBN * 2];          // fp4 key operands [c][key][h]
-  float ak[kBN];                  // key scales
-  int gk[kBN];                    // grid offsets (table mode)
-  uint16_t vt[32 * CB * kBN];     // V^T tile: rows of 64 keys, swizzled
-  float win[kMaxWindowFloats];    // bias window (table-row mode)
+  v4i k[NCH * kBN * 2];                // fp4 key operands [c][key][h]
+  float ak[kBN];                        // key scales
+  int gk[BiasSizes<BIAS>::kGk];         // grid offsets (table mode)
+  uint16_t vt[32 * CB * kBN];           // V^T tile: rows of 64 keys, swizzled
+  float win[BiasSizes<BIAS>::kWin];     // bias window (table-row mode) or
+                                        // dense bias tile (dense mode)
 };
 
 // The row sums l of P: when d % 32 != 0, V^T carries rows of ones (rows d
 // and d+4), so accumulator row d of the P.V product holds sum_j P_ij.  When
-// d % 32 == 0 (XONES), the offset-free pass sums P on the vector ALU into
-// ones[0][0..1], and the exact pass runs an extra 32-row block whose A
-// operand is a constant register with ones in rows 0 and 4; either way
-// ones[0][0] holds sum_j P_ij at the end.
+// d % 32 == 0 (XONES), both passes add the bf16 P pairs on the vector ALU
+// into two partial sums per lane, rs[0..1]; at the end of the pass rs[0]
+// holds sum_j P_ij in both lanes of the query.
 template <int CB, bool XONES>
 struct Acc {
   v16f o[CB];
-  v16f ones[1];  // used when XONES
+  float rs[2];  // used when XONES
 };
 
 // Per-lane and per-workgroup constants.
@@ -90,6 +100,10 @@ struct Ctx {
   rsrc_t ars;          // key scales of this (b, h)
   rsrc_t brs;          // bias rows of this head (table-row mode)
   int win_bytes;       // bytes of the per-tile bias window (table-row mode)
+  rsrc_t drs;          // dense bias of this (b, h) (dense mode)
+  uint32_t dvoff;      // this lane's byte offset in its dense-tile copies
+  uint32_t dld2;       // dense bias row stride in bytes
+  int off_dn[4];       // this lane's dense-tile LDS bytes, group b of block 0
 };
 
 // Uniform per-tile position of the keys on the grid (table-row mode).
@@ -143,7 +157,7 @@ __device__ __forceinline__ T lds_load(const void* base, int byte_off) {
 // grid offsets of the tile's keys are computed and stored directly: `tb` was
 // last read before the previous barrier.
 template <int NCH, int CB, int BIAS>
-__device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb, int t, const KeyPos& kp) {
+__device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TileBuf<NCH, CB, BIAS>& tb, int t, const KeyPos& kp) {
   const FwdArgs& a = *c.a;
   constexpr int kKBytes = NCH * kBN * 2 * 16;
   char* kdst = reinterpret_cast<char*>(&tb.k[0]);
@@ -171,6 +185,19 @@ __device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TileBuf<NCH, 
       if (static_cast<int>(loff) + 4096 * j < c.win_bytes)
         dma16(c.brs, bdst + (c.wave + 4 * j) * 1024, loff + 4096 * j, bs);
   }
+  if (BIAS == kBiasDense) {
+    // 128 query rows x 64 keys of bf16 = 16 pieces of 1 KiB, 4 per wave.
+    // Piece m holds rows 8m .. 8m+7; lane l fills slot 64m + l, i.e. row
+    // 8m + l/8 and 16-byte chunk (l%8) ^ ((l/16) & 3) of that row (the XOR
+    // spreads the rows a wave reads over the LDS banks).
+    char* ddst = reinterpret_cast<char*>(&tb.win[0]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = c.wave + 4 * j;
+      dma16(c.drs, ddst + m * 1024, c.dvoff + static_cast<uint32_t>(m * 8) * c.dld2 + static_cast<uint32_t>(kp.k0 * 2),
+            0u);
+    }
+  }
   if (BIAS == kBiasTable && c.tid < kBN) {
     const int j = (kp.k0 + c.tid < a.N) ? kp.k0 + c.tid : a.N - 1;
     const int yj = j / a.gw;
@@ -194,7 +221,7 @@ __device__ __forceinline__ int window_offset(const Ctx<NCH>& c, const KeyPos& kp
 // Logits of one 32-key block in base 2:
 //   D * alpha_k * (alpha_q scale log2e) + log2e b
 template <bool MASK, int NCH, int CB, int BIAS>
-__device__ __forceinline__ void block_logits(const Ctx<NCH>& c, const TileBuf<NCH, CB>& tb, const KeyPos& kp,
+__device__ __forceinline__ void block_logits(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& tb, const KeyPos& kp,
                                              int blk, const v16f& s, float (&sc)[16]) {
   const FwdArgs& a = *c.a;
   int woff = 0;
@@ -216,6 +243,14 @@ __device__ __forceinline__ void block_logits(const Ctx<NCH>& c, const TileBuf<NC
       sc[4 * b + 1] = fmaf(u1, c.aq, c.table[c.fidx - g.y]);
       sc[4 * b + 2] = fmaf(u2, c.aq, c.table[c.fidx - g.z]);
       sc[4 * b + 3] = fmaf(u3, c.aq, c.table[c.fidx - g.w]);
+    } else if (BIAS == kBiasDense) {
+      // keys 4 lh .. 4 lh + 3 of group b: four bf16 in two dwords; natural
+      // units (c.aq holds alpha_q * scale), log2e comes with the row shift
+      const v2u w = lds_load<v2u>(tb.win, c.off_dn[b] + 64 * blk);
+      sc[4 * b + 0] = fmaf(u0, c.aq, __uint_as_float(w.x << 16));
+      sc[4 * b + 1] = fmaf(u1, c.aq, __uint_as_float(w.x & 0xffff0000u));
+      sc[4 * b + 2] = fmaf(u2, c.aq, __uint_as_float(w.y << 16));
+      sc[4 * b + 3] = fmaf(u3, c.aq, __uint_as_float(w.y & 0xffff0000u));
     } else {
       sc[4 * b + 0] = u0 * c.aq;
       sc[4 * b + 1] = u1 * c.aq;
@@ -232,32 +267,46 @@ __device__ __forceinline__ void block_logits(const Ctx<NCH>& c, const TileBuf<NC
   }
 }
 
-// Exact path only: running row max over this block; rescales the
-// accumulators when it grows by more than 8, and shifts the logits by it.
-template <int CB, bool XONES>
+// Exact path only: running row max over this block (mrow, in log2 units);
+// rescales the accumulators when it grows by more than 8, and shifts the
+// logits by it.  NATURAL: the logits come in natural-log units and are
+// turned into log2 units by the shift itself (one FMA per logit).  A row
+// whose keys so far all have logit -inf (a dense bias may mask keys) keeps
+// mrow = -inf and is shifted by 0, so its probabilities stay 0, not NaN.
+template <bool NATURAL, int CB, bool XONES>
 __device__ __forceinline__ void block_rescale(float (&sc)[16], Acc<CB, XONES>& acc, float& mrow) {
   float mt = sc[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
   mt = max_halves(mt);
+  if (NATURAL) mt *= kLog2e;
   const float mnew = fmaxf(mrow, mt);
   if (__any(mnew > mrow + 8.0f)) {
     const float f = fast_exp2(mrow - mnew);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc.o[cb] *= f;
-    if (XONES) acc.ones[0] *= f;
+    if (XONES) {
+      acc.rs[0] *= f;
+      acc.rs[1] *= f;
+    }
     mrow = mnew;
   }
+  if (NATURAL) {
+    const float shift = mrow == -INFINITY ? 0.0f : mrow;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sc[r] -= mrow;
+    for (int r = 0; r < 16; ++r) sc[r] = fmaf(sc[r], kLog2e, -shift);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] -= mrow;
+  }
 }
 
 // One 64-key tile for this wave's 32 queries, one 32-key block at a time:
 // QK, logits, exp2 and bf16 packing, then P.V (and the row sums).
 // FAST: offset-free exp2, no row max.  MASK: keys >= N get probability 0.
 template <bool FAST, bool MASK, int NCH, int CB, bool XONES, int BIAS>
-__device__ __forceinline__ void compute_tile(const Ctx<NCH>& c, const TileBuf<NCH, CB>& tb, const KeyPos& kp,
-                                             Acc<CB, XONES>& acc, float& mrow, const v8bf& ones_op) {
+__device__ __forceinline__ void compute_tile(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& tb, const KeyPos& kp,
+                                             Acc<CB, XONES>& acc, float& mrow) {
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     v16f s = v16f{};
@@ -266,10 +315,14 @@ __device__ __forceinline__ void compute_tile(const Ctx<NCH>& c, const TileBuf<NC
       s = mfma_signs_32x32x64(lds_load<v4i>(tb.k, c.off_k + ch * 2048 + blk * 1024), c.qop[ch], s);
     float sc[16];
     block_logits<MASK, NCH, CB, BIAS>(c, tb, kp, blk, s, sc);
-    if (!FAST) block_rescale(sc, acc, mrow);
+    if (!FAST) block_rescale<BIAS == kBiasDense>(sc, acc, mrow);
     uint32_t pk[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) pk[j] = pack_bf16x2(fast_exp2(sc[2 * j]), fast_exp2(sc[2 * j + 1]));
+    if (XONES) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc.rs[b & 1] = add_bf16x2(pk[2 * b], add_bf16x2(pk[2 * b + 1], acc.rs[b & 1]));
+    }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int p = 2 * blk + half;
@@ -278,7 +331,6 @@ __device__ __forceinline__ void compute_tile(const Ctx<NCH>& c, const TileBuf<NC
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
         acc.o[cb] = mfma_bf16_32x32x16(lds_load<v8bf>(tb.vt, c.off_v[p] + cb * 4096), pop, acc.o[cb]);
-      if (XONES) acc.ones[0] = mfma_bf16_32x32x16(ones_op, pop, acc.ones[0]);
     }
   }
 }
@@ -306,7 +358,7 @@ __device__ __forceinline__ void pv_mfma(int i, const PendingPV<CB>& pp, Acc<CB, 
 // Block `blk` of tile `tb`: its QK, then the pending block's P.V interleaved
 // with this block's logits / exp2 / bf16 packing; this block becomes pending.
 template <bool MASK, bool HAVE_PENDING, int NCH, int CB, bool XONES, int BIAS>
-__device__ __forceinline__ void pipelined_block(const Ctx<NCH>& c, const TileBuf<NCH, CB>& tb, const KeyPos& kp,
+__device__ __forceinline__ void pipelined_block(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& tb, const KeyPos& kp,
                                                 int blk, PendingPV<CB>& pp, Acc<CB, XONES>& acc) {
   const FwdArgs& a = *c.a;
   constexpr int kMf = 2 * CB;
@@ -357,7 +409,7 @@ __device__ __forceinline__ void pipelined_block(const Ctx<NCH>& c, const TileBuf
     // Row sums on the vector ALU (two partial sums per lane), cheaper here
     // than the extra matrix instructions of a ones block; they add the same
     // bf16 P that multiplies V.
-    if (XONES) acc.ones[0][b & 1] = add_bf16x2(pk[2 * b], add_bf16x2(pk[2 * b + 1], acc.ones[0][b & 1]));
+    if (XONES) acc.rs[b & 1] = add_bf16x2(pk[2 * b], add_bf16x2(pk[2 * b + 1], acc.rs[b & 1]));
   }
   // this block becomes pending: P and its V^T operands
 #pragma unroll
@@ -372,7 +424,7 @@ __device__ __forceinline__ void pipelined_block(const Ctx<NCH>& c, const TileBuf
 // Pipelined (offset-free) version of pass_step: tile t's two blocks each
 // overlap the previous block's P.V.
 template <bool FIRST, int NCH, int CB, bool XONES, int BIAS>
-__device__ __forceinline__ void fast_step(const Ctx<NCH>& c, const TileBuf<NCH, CB>& cur, TileBuf<NCH, CB>& nxt,
+__device__ __forceinline__ void fast_step(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& cur, TileBuf<NCH, CB, BIAS>& nxt,
                                           int t, int nkt, KeyPos& kp, Acc<CB, XONES>& acc, PendingPV<CB>& pp) {
   const FwdArgs& a = *c.a;
   const bool more = t + 1 < nkt;
@@ -391,12 +443,12 @@ __device__ __forceinline__ void fast_step(const Ctx<NCH>& c, const TileBuf<NCH, 
 }
 
 template <int NCH, int CB, bool XONES, int BIAS>
-__device__ __forceinline__ void run_fast_pass(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb0, TileBuf<NCH, CB>& tb1,
+__device__ __forceinline__ void run_fast_pass(const Ctx<NCH>& c, TileBuf<NCH, CB, BIAS>& tb0, TileBuf<NCH, CB, BIAS>& tb1,
                                               Acc<CB, XONES>& acc) {
   const FwdArgs& a = *c.a;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc.o[cb] = v16f{};
-  acc.ones[0] = v16f{};
+  acc.rs[0] = acc.rs[1] = 0.0f;
   KeyPos kp;
   kp.k0 = 0;
   kp.ky[0] = 0;
@@ -418,24 +470,23 @@ __device__ __forceinline__ void run_fast_pass(const Ctx<NCH>& c, TileBuf<NCH, CB
   for (int i = 0; i < 2 * CB; ++i) pv_mfma<CB, XONES>(i, pp, acc);
   // the row sums, in the register the epilogue reads: both halves of each
   // query's keys (lanes l and l^32)
-  if (XONES) acc.ones[0][0] = sum_halves(acc.ones[0][0] + acc.ones[0][1]);
+  if (XONES) acc.rs[0] = sum_halves(acc.rs[0] + acc.rs[1]);
 }
 
 // One key tile: start the copies of tile t+1 into `nxt`, compute tile t from
 // `cur`, expand the next keys into `nxt`, wait, barrier.
 template <bool FAST, int NCH, int CB, bool XONES, int BIAS>
-__device__ __forceinline__ void pass_step(const Ctx<NCH>& c, const TileBuf<NCH, CB>& cur, TileBuf<NCH, CB>& nxt,
-                                          int t, int nkt, KeyPos& kp, Acc<CB, XONES>& acc, float& mrow,
-                                          const v8bf& ones_op) {
+__device__ __forceinline__ void pass_step(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& cur, TileBuf<NCH, CB, BIAS>& nxt,
+                                          int t, int nkt, KeyPos& kp, Acc<CB, XONES>& acc, float& mrow) {
   const FwdArgs& a = *c.a;
   const bool more = t + 1 < nkt;
   const KeyPos kn = next_keys(kp, a.gw);
   if (more) copy_tile_async<NCH, CB, BIAS>(c, nxt, t + 1, kn);
   // With table rows, keys past N meet -inf padding rows: no mask needed.
   if (BIAS == kBiasRows || kp.k0 + kBN <= a.N)
-    compute_tile<FAST, false, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow, ones_op);
+    compute_tile<FAST, false, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow);
   else
-    compute_tile<FAST, true, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow, ones_op);
+    compute_tile<FAST, true, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   kp = kn;
@@ -443,12 +494,12 @@ __device__ __forceinline__ void pass_step(const Ctx<NCH>& c, const TileBuf<NCH, 
 
 // One pass over all keys; O^T (and the row sums) accumulate in acc.
 template <bool FAST, int NCH, int CB, bool XONES, int BIAS>
-__device__ __forceinline__ void run_pass(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb0, TileBuf<NCH, CB>& tb1,
-                                         Acc<CB, XONES>& acc, const v8bf& ones_op) {
+__device__ __forceinline__ void run_pass(const Ctx<NCH>& c, TileBuf<NCH, CB, BIAS>& tb0, TileBuf<NCH, CB, BIAS>& tb1,
+                                         Acc<CB, XONES>& acc) {
   const FwdArgs& a = *c.a;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc.o[cb] = v16f{};
-  acc.ones[0] = v16f{};
+  acc.rs[0] = acc.rs[1] = 0.0f;
   float mrow = -INFINITY;
   KeyPos kp;
   kp.k0 = 0;
@@ -461,9 +512,10 @@ __device__ __forceinline__ void run_pass(const Ctx<NCH>& c, TileBuf<NCH, CB>& tb
   __syncthreads();
   const int nkt = (a.N + kBN - 1) / kBN;
   for (int t = 0; t < nkt; t += 2) {
-    pass_step<FAST, NCH, CB, XONES, BIAS>(c, tb0, tb1, t, nkt, kp, acc, mrow, ones_op);
-    if (t + 1 < nkt) pass_step<FAST, NCH, CB, XONES, BIAS>(c, tb1, tb0, t + 1, nkt, kp, acc, mrow, ones_op);
+    pass_step<FAST, NCH, CB, XONES, BIAS>(c, tb0, tb1, t, nkt, kp, acc, mrow);
+    if (t + 1 < nkt) pass_step<FAST, NCH, CB, XONES, BIAS>(c, tb1, tb0, t + 1, nkt, kp, acc, mrow);
   }
+  if (XONES) acc.rs[0] = sum_halves(acc.rs[0] + acc.rs[1]);
 }
 
 // Waves per SIMD the register budget is sized for (accumulator blocks).
@@ -475,8 +527,8 @@ struct Occupancy {
 template <int NCH, int CB, bool XONES, int BIAS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<CB + XONES>::kWaves)))
 attn_fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB> tb0;
-  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB> tb1;
+  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb0;
+  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb1;
   __shared__ float red[kThreads / 64];
   extern __shared__ __attribute__((aligned(16))) float s_table[];
 
@@ -494,8 +546,19 @@ attn_fwd_kernel(FwdArgs a) {
     const int per = a.nwg >> 3;
     wg = (wg & 7) * per + (wg >> 3);
   }
-  c.bh = wg / a.nqt;
-  const int qt = wg - c.bh * a.nqt;
+  int qt;
+  if (BIAS == kBiasDense && a.dense_shared) {
+    // One bias for the whole batch: the B workgroups that read the same
+    // bias tiles get consecutive indices (batch fastest), so they run side
+    // by side on one XCD and the second reads of a tile hit its L2.
+    const int b = wg % a.B, t = wg / a.B;
+    const int h = t / a.nqt;
+    qt = t - h * a.nqt;
+    c.bh = b * a.H + h;
+  } else {
+    c.bh = wg / a.nqt;
+    qt = wg - c.bh * a.nqt;
+  }
   c.head = c.bh % a.H;
   c.q0 = qt * kBM;
   c.qi = c.q0 + c.wave * 32 + c.li;
@@ -543,7 +606,7 @@ attn_fwd_kernel(FwdArgs a) {
     for (int p = 0; p < 4; ++p) c.off_v[p] = c.li * 128 + (((2 * p + c.lh) ^ sw) << 4);
   }
   c.yq = c.xq = c.yq_lo = c.fidx = c.off_win = 0;
-  if (BIAS != kBiasNone) {
+  if (BIAS == kBiasRows || BIAS == kBiasTable) {
     c.yq = c.qi / a.gw;
     c.xq = c.qi - c.yq * a.gw;
   }
@@ -573,6 +636,23 @@ attn_fwd_kernel(FwdArgs a) {
                       static_cast<uint32_t>(rows_p * 16 * a.Lpad));
     c.win_bytes = a.win_rows * 16 * a.Lpad;  // <= 8 KiB: two pieces per wave
   }
+  c.drs = c.ars;
+  c.dvoff = c.dld2 = 0;
+  if (BIAS == kBiasDense) {
+    // The range ends at the last real entry of this (b, h), so rows and
+    // keys past N read 0 (rows past N are never stored, keys past N are
+    // masked); every offset the copies form stays below 2^32.
+    const int64_t b = c.bh / a.H;
+    c.drs = make_rsrc(a.dense + b * a.dsb + static_cast<int64_t>(c.head) * a.dsh,
+                      static_cast<uint32_t>(((a.N - 1) * a.dld + a.N) * 2));
+    c.dld2 = static_cast<uint32_t>(a.dld * 2);
+    const int l = c.lane;
+    c.dvoff = static_cast<uint32_t>(c.q0 + (l >> 3)) * c.dld2 + static_cast<uint32_t>(((l & 7) ^ ((l >> 4) & 3)) * 16);
+    // row r = 32 wave + li, group b of block 0 sits in chunk b ^ ((r/2) & 3)
+    const int r = c.wave * 32 + c.li, x = (c.li >> 1) & 3;
+#pragma unroll
+    for (int b2 = 0; b2 < 4; ++b2) c.off_dn[b2] = r * 128 + ((b2 ^ x) << 4) + 8 * c.lh;
+  }
 
   // ---- logit bound M (log2 units) ------------------------------------------
   const int nblk = a.Npad / 64;
@@ -598,24 +678,24 @@ attn_fwd_kernel(FwdArgs a) {
   const float qm = block_max(alpha_q, red);
   const float M = a.qscale * qm * km * static_cast<float>(a.d) + bm;
 
-  // A operand of the extra row-sum block: rows 0 and 4 are ones.
-  const uint32_t one2 = (c.li == 0 || c.li == 4) ? 0x3F803F80u : 0u;
-  const v4u ones4 = {one2, one2, one2, one2};
-  const v8bf ones_op = __builtin_bit_cast(v8bf, ones4);
-
   Acc<CB, XONES> acc;
-  if (M <= kFastMaxLogit)  // false for NaN as well
-    run_fast_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
-  else
-    run_pass<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, acc, ones_op);
+  if constexpr (BIAS == kBiasDense) {
+    // no bound on a dense bias short of reading all of it: exact softmax
+    (void)M;
+    run_pass<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
+  } else {
+    if (M <= kFastMaxLogit)  // false for NaN as well
+      run_fast_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
+    else
+      run_pass<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
+  }
 
   // ---- epilogue: O = O^T / l, bf16, one query per lane --------------------
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) pin_uniform(acc.o[cb]);
   float lsum;
   if (XONES) {
-    pin_uniform(acc.ones[0]);
-    lsum = acc.ones[0][0];
+    lsum = acc.rs[0];
   } else {
     // rows d and d+4 of the last block: register 4 * ((d % 32) / 8)
     const int b1 = (a.d & 31) >> 3;
@@ -645,18 +725,28 @@ int fwd_table_lds(const FwdArgs& a, int mode) {
   return 0;
 }
 
-int fwd_static_lds(int dpad) {
-  const int cb = dpad / 32;
+template <int BIAS>
+static int static_lds_for(int cb) {
   constexpr int kRed = kThreads / 64 * 4;
   switch (cb) {
-    case 1: return 2 * sizeof(TileBuf<1, 1>) + kRed;
-    case 2: return 2 * sizeof(TileBuf<1, 2>) + kRed;
-    case 3: return 2 * sizeof(TileBuf<2, 3>) + kRed;
-    case 4: return 2 * sizeof(TileBuf<2, 4>) + kRed;
-    case 5: return 2 * sizeof(TileBuf<3, 5>) + kRed;
-    case 6: return 2 * sizeof(TileBuf<3, 6>) + kRed;
-    case 7: return 2 * sizeof(TileBuf<4, 7>) + kRed;
-    default: return 2 * sizeof(TileBuf<4, 8>) + kRed;
+    case 1: return 2 * sizeof(TileBuf<1, 1, BIAS>) + kRed;
+    case 2: return 2 * sizeof(TileBuf<1, 2, BIAS>) + kRed;
+    case 3: return 2 * sizeof(TileBuf<2, 3, BIAS>) + kRed;
+    case 4: return 2 * sizeof(TileBuf<2, 4, BIAS>) + kRed;
+    case 5: return 2 * sizeof(TileBuf<3, 5, BIAS>) + kRed;
+    case 6: return 2 * sizeof(TileBuf<3, 6, BIAS>) + kRed;
+    case 7: return 2 * sizeof(TileBuf<4, 7, BIAS>) + kRed;
+    default: return 2 * sizeof(TileBuf<4, 8, BIAS>) + kRed;
+  }
+}
+
+int fwd_static_lds(int dpad, int mode) {
+  const int cb = dpad / 32;
+  switch (mode) {
+    case kBiasNone: return static_lds_for<kBiasNone>(cb);
+    case kBiasRows: return static_lds_for<kBiasRows>(cb);
+    case kBiasTable: return static_lds_for<kBiasTable>(cb);
+    default: return static_lds_for<kBiasDense>(cb);
   }
 }
 
@@ -671,6 +761,9 @@ static int launch_nc(const FwdArgs& a, int mode, void* stream) {
       break;
     case kBiasRows:
       hipLaunchKernelGGL((attn_fwd_kernel<NCH, CB, XONES, kBiasRows>), grid, block, lds, s, a);
+      break;
+    case kBiasDense:
+      hipLaunchKernelGGL((attn_fwd_kernel<NCH, CB, XONES, kBiasDense>), grid, block, lds, s, a);
       break;
     default:
       hipLaunchKernelGGL((attn_fwd_kernel<NCH, CB, XONES, kBiasTable>), grid, block, lds, s, a);

@@ -22,6 +22,9 @@ constexpr int kBiasPadRows = 8;
 // Largest bias window (floats) the table-row path stages per key tile
 // (8 KiB: two 1 KiB copy pieces per wave); covers grids up to 128 wide.
 constexpr int kMaxWindowFloats = 2048;
+// Dense-bias tile the fused kernel stages per key tile: 128 queries x 64 keys
+// of bf16 (16 KiB, as floats).
+constexpr int kDenseTileFloats = kBM * kBN / 2;
 
 // Tokens per prologue block (one key tile).
 constexpr int kPackTok = 64;
@@ -82,7 +85,9 @@ int prologue_lds(int d, bool kv);
 
 int launch_prologue(const PrologueArgs& a, void* stream);
 
-enum BiasMode { kBiasNone = 0, kBiasRows = 1, kBiasTable = 2 };
+// kBiasRows / kBiasTable: a relative-position table; kBiasDense: one bf16
+// value per (query, key) of each head (and batch entry).
+enum BiasMode { kBiasNone = 0, kBiasRows = 1, kBiasTable = 2, kBiasDense = 3 };
 
 struct FwdArgs {
   const uint16_t* q;       // bf16 queries (strides qs), packed in the kernel
@@ -94,12 +99,15 @@ struct FwdArgs {
   const float* bias_row_max;  // kBiasRows: [H][2gh-1], max |b| log2e per row
   const float* kmax_blk;   // [BH][Npad/64] max alpha_k per 64-token block
   const uint16_t* table;   // kBiasTable: bf16 [H][2gh-1][2gw-1]
+  const uint16_t* dense;   // kBiasDense: bias(b, h, i, j) at b*dsb + h*dsh + i*dld + j
+  int64_t dsb, dsh, dld;
+  int dense_shared;        // kBiasDense: 1 when dsb == 0 and B > 1
   uint16_t* o;             // bf16 output (strides os)
   Strides qs, os;
-  int H, N, Npad, d, W, dpad;
+  int B, H, N, Npad, d, W, dpad;
   int gh, gw, Lpad;
   int win_rows;            // kBiasRows: rows of the per-tile bias window
-  float qscale;            // softmax scale * log2(e)
+  float qscale;            // softmax scale * log2(e) (kBiasDense: softmax scale)
   int nqt;                 // query tiles per head
   int nwg;                 // workgroups
   int xcd_remap;           // 1: spread consecutive heads over the 8 XCDs
@@ -109,7 +117,7 @@ struct FwdArgs {
 // LDS bytes of the fused kernel: the bias table (table mode, dynamic) and
 // the static tile buffers.
 int fwd_table_lds(const FwdArgs& a, int mode);
-int fwd_static_lds(int dpad);
+int fwd_static_lds(int dpad, int mode);
 
 // Launch the fused kernel (template selected from d and the bias mode).
 int launch_attention(const FwdArgs& a, int mode, void* stream);

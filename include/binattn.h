@@ -151,6 +151,35 @@ ba_status ba_attention_fwd_strided(const void* q, const void* k, const void* v,
                                    void* o, const int64_t* strides,
                                    void* workspace, size_t ws_bytes, void* stream);
 
+/* ba_attention_fwd_dense_bias -- the forward with a dense bias: one learnable
+ * value per query, key and head ("Mejora mediante Sesgo": besides the
+ * position-sensitive form, the bias may be dense), in place of the
+ * relative-position table:
+ *   S_ij = scale * alpha_q,i * alpha_k,j * D_ij + bias(b,h,i,j)
+ *   bias       bf16, bias(b,h,i,j) at bias + b*bias_sb + h*bias_sh +
+ *              i*bias_ld + j elements.  bias_sb = 0 shares one [H,N,N] bias
+ *              over the batch; a contiguous [B,H,N,N] tensor has
+ *              (H*N*N, N*N, N).  All three strides must be multiples of 8 in
+ *              [0, 2^40] (rows 16-byte aligned: pad the rows when N % 8 != 0),
+ *              and (N rounded up to 128) * (bias_ld + 1) * 2 must stay below
+ *              2^32 bytes.  Entries must be finite or -inf (-inf masks the
+ *              key; a row whose entries are all -inf gives NaN, as softmax
+ *              does).
+ *   strides    as for ba_attention_fwd_strided, or NULL for contiguous
+ *              [B,H,N,d] q, k, v and o.
+ *   workspace  ba_workspace_bytes(B,H,N,d,0,0) bytes (no table section).
+ * A dense bias has no cheap bound on its values, so the fused kernel always
+ * runs the exact online softmax (running row maximum).  Two kernels are
+ * enqueued, as for ba_attention_fwd.  o must not overlap the bias.
+ * Errors: as ba_attention_fwd; BA_ERR_UNSUPPORTED when the bias of one head
+ * spans 4 GiB or more. */
+ba_status ba_attention_fwd_dense_bias(const void* q, const void* k, const void* v,
+                                      const void* bias, int64_t bias_sb, int64_t bias_sh,
+                                      int64_t bias_ld,
+                                      int64_t B, int64_t H, int64_t N, int d, float scale,
+                                      void* o, const int64_t* strides,
+                                      void* workspace, size_t ws_bytes, void* stream);
+
 /* The two halves of ba_attention_fwd, for callers that time or schedule the
  * two kernels separately.
  *
@@ -177,6 +206,21 @@ ba_status ba_attention_fwd_prepared(const void* q, const void* bias, int gh, int
                                     float scale, void* o,
                                     const void* workspace, size_t ws_bytes,
                                     void* stream);
+
+/* ba_attention_fwd_dense_bias_prepared -- the fused kernel of
+ * ba_attention_fwd_dense_bias alone, on a workspace that
+ * ba_attention_prepare(k, v, NULL, 0, 0, B, H, N, d, ...) filled (stream
+ * order must put the prepare first): a prepared K/V can serve several
+ * queries or biases.  q and o are contiguous [B,H,N,d]; the bias arguments,
+ * the rules on them and the errors are those of ba_attention_fwd_dense_bias.
+ * ba_attention_prepare followed by this call on one stream gives the same O
+ * as ba_attention_fwd_dense_bias, bit for bit. */
+ba_status ba_attention_fwd_dense_bias_prepared(const void* q, const void* bias,
+                                               int64_t bias_sb, int64_t bias_sh, int64_t bias_ld,
+                                               int64_t B, int64_t H, int64_t N, int d,
+                                               float scale, void* o,
+                                               const void* workspace, size_t ws_bytes,
+                                               void* stream);
 
 /* QK integer-dot routes for ba_qk_int_dot. */
 #define BA_ROUTE_MFMA_FP4 0 /* +/-1 in fp4 (e2m1) on the scaled f8f6f4 MFMA;

@@ -241,3 +241,29 @@ def test_rows_disjoint_rule(lib):
         assert st == WS_TOO_SMALL, (o, lib.ba_last_error())
     assert fwd_strided(lib, list(bnhd(B, H, N, d)) * 3 + [N * d, N * d, d], o=A + 8 * GB,
                        B=B, H=H, N=N) == 2
+
+
+def fwd_dense(lib, bias=A + 5 * GB, sb=0, sh=64 * 64, ld=64, B=1, H=2, N=64, d=64, o=A + 3 * GB,
+              strides=None, ws_bytes=1 << 40):
+    arr = None if strides is None else (ctypes.c_int64 * 12)(*strides)
+    return lib.ba_attention_fwd_dense_bias(A, A + GB, A + 2 * GB, bias, sb, sh, ld, B, H, N, d, 0.125, o,
+                                           arr, A + 4 * GB, ws_bytes, None)
+
+
+def test_dense_bias_validation(lib):
+    """Checks of the dense-bias entry, all before any launch (the valid
+    cases stop at the 16-byte workspace)."""
+    assert fwd_dense(lib, bias=None) == 1
+    assert fwd_dense(lib, bias=A + 5 * GB + 8) == 4
+    assert fwd_dense(lib, ld=60) == 2                       # row stride not a multiple of 8
+    assert fwd_dense(lib, sh=-8) == 2
+    assert fwd_dense(lib, o=A + 5 * GB + 64) == 2           # o overlaps the bias
+    assert b"bias" in lib.ba_last_error()
+    # one head's bias must stay below 4 GiB of offsets
+    assert fwd_dense(lib, N=40000, ld=60000, sh=0, ws_bytes=16) == 3
+    assert fwd_dense(lib, ws_bytes=16) == WS_TOO_SMALL
+    assert fwd_dense(lib, sb=2 * 64 * 64, B=2, ws_bytes=16) == WS_TOO_SMALL
+    assert fwd_dense(lib, strides=list(bnhd(1, 2, 64, 64)) * 4, ws_bytes=16) == WS_TOO_SMALL
+    # the workspace is the one without a table
+    need = lib.ba_workspace_bytes(1, 2, 64, 64, 0, 0)
+    assert fwd_dense(lib, ws_bytes=need - 1) == 5

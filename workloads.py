@@ -11,7 +11,9 @@ Recipe, per workload:
 * for the outlier workload, the first round(frac * d) channels of that
   permutation are multiplied by 8 in Q, K and V (all heads, all tokens);
 * one conversion to bf16 (torch CPU, round-to-nearest-even) produces the only
-  copy of the inputs.
+  copy of the inputs;
+* a dense bias [1 or B, H, N, N] (make_dense_bias) comes from its own
+  default_rng(seed): float32 normals times sigma, then one bf16 rounding.
 
 The five named workloads stand in for the token counts of the vision and
 diffusion experiments the BinaryAttention pages report.  Those are ViT at
@@ -114,6 +116,25 @@ def make_inputs(B: int, H: int, N: int, d: int, seed: int, *,
 def workload_inputs(w: Workload) -> dict:
     return make_inputs(w.B, w.H, w.N, w.d, w.seed, grid=(w.gh, w.gw),
                        outlier_frac=w.outlier_frac)
+
+
+def make_dense_bias(Bb: int, H: int, N: int, seed: int, sigma: float = 0.02,
+                    ld: int | None = None) -> torch.Tensor:
+    """Seeded dense bias [Bb, H, N, N] in bf16: numpy default_rng(seed) draws
+    float32 standard normals, times sigma, rounded once to bf16.  With ld > N
+    the rows are stored ld apart (zero padding past N) and a [Bb, H, N, N]
+    view of that storage is returned, so that every row starts 16-byte
+    aligned when N % 8 != 0."""
+    rng = np.random.default_rng(seed)
+    b = np.float32(sigma) * rng.standard_normal((Bb, H, N, N), dtype=np.float32)
+    t = _to_bf16(b)
+    if ld is None or ld == N:
+        return t
+    if ld < N:
+        raise ValueError("ld must be >= N")
+    wide = torch.zeros((Bb, H, N, ld), dtype=torch.bfloat16)
+    wide[..., :N] = t
+    return wide[..., :N]
 
 
 def as_f32(t):
