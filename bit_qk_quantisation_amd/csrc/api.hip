@@ -2,6 +2,7 @@
 // selection and launches.  See include/binattn.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <utility>
 #include <cmath>
@@ -385,6 +386,12 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   const int static_lds = ba::fwd_static_lds(f.dpad, mode), table_lds = ba::fwd_table_lds(f, mode);
   if (static_lds + table_lds > kMaxLds) return fail(BA_ERR_UNSUPPORTED, "bias window does not fit in LDS");
   f.dyn_lds = fused_dynamic_lds(static_lds, table_lds, nwg);
+  {
+    const int cus = device_cus();
+    const int per_wg = static_cast<int>(round_up(static_lds + f.dyn_lds, kLdsGranule));
+    const int resident = std::min(ba::fwd_waves_per_simd(f.dpad, d), kMaxLds / per_wg);
+    f.prio_balance = (cus > 0 && nwg <= static_cast<int64_t>(cus) * resident) ? 1 : 0;
+  }
 
   ba::PrologueArgs& p = plan->p;
   p = ba::PrologueArgs{};

@@ -421,6 +421,29 @@ __device__ __forceinline__ void pipelined_block(const Ctx<NCH>& c, const TileBuf
       pp.vop[half][cb] = lds_load<v8bf>(tb.vt, c.off_v[2 * blk + half] + cb * 4096);
 }
 
+// Wave priority for key tile t of nkt: 3 (the highest) through the first
+// five eighths of the keys, then 2, 1 and 0 for the last three.  The waves of
+// a SIMD come from several workgroups, and when they are equal the hardware
+// favours the oldest, so the first workgroup of a CU would finish long before
+// the last, which then runs alone with one wave per SIMD and no second wave to
+// overlap its matrix and vector work with.  Lowering a wave's priority as it
+// nears the end lets the later workgroups catch up.  Only for grids whose
+// workgroups are all resident at once (the host sets prio_balance): with
+// more workgroups than slots, holding back the ones about to finish delays
+// the slots the rest are waiting for.
+__device__ __forceinline__ void tile_priority(const FwdArgs& a, int t, int nkt) {
+  if (!a.prio_balance) return;
+  const int e = (8 * t) / nkt;
+  if (e <= 4)
+    __builtin_amdgcn_s_setprio(3);
+  else if (e == 5)
+    __builtin_amdgcn_s_setprio(2);
+  else if (e == 6)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // Pipelined (offset-free) version of pass_step: tile t's two blocks each
 // overlap the previous block's P.V.
 template <bool FIRST, int NCH, int CB, bool XONES, int BIAS>
@@ -462,6 +485,7 @@ __device__ __forceinline__ void run_fast_pass(const Ctx<NCH>& c, TileBuf<NCH, CB
   PendingPV<CB> pp;
   fast_step<true, NCH, CB, XONES, BIAS>(c, tb0, tb1, 0, nkt, kp, acc, pp);
   for (int t = 1; t < nkt; t += 2) {
+    tile_priority(a, t, nkt);
     fast_step<false, NCH, CB, XONES, BIAS>(c, tb1, tb0, t, nkt, kp, acc, pp);
     if (t + 1 < nkt) fast_step<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, t + 1, nkt, kp, acc, pp);
   }
@@ -479,6 +503,7 @@ template <bool FAST, int NCH, int CB, bool XONES, int BIAS>
 __device__ __forceinline__ void pass_step(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& cur, TileBuf<NCH, CB, BIAS>& nxt,
                                           int t, int nkt, KeyPos& kp, Acc<CB, XONES>& acc, float& mrow) {
   const FwdArgs& a = *c.a;
+  tile_priority(a, t, nkt);
   const bool more = t + 1 < nkt;
   const KeyPos kn = next_keys(kp, a.gw);
   if (more) copy_tile_async<NCH, CB, BIAS>(c, nxt, t + 1, kn);
@@ -521,7 +546,7 @@ __device__ __forceinline__ void run_pass(const Ctx<NCH>& c, TileBuf<NCH, CB, BIA
 // Waves per SIMD the register budget is sized for (accumulator blocks).
 template <int NB>
 struct Occupancy {
-  static constexpr int kWaves = NB <= 3 ? 3 : (NB <= 5 ? 2 : 1);
+  static constexpr int kWaves = fwd_waves_for_blocks(NB);
 };
 
 template <int NCH, int CB, bool XONES, int BIAS>
@@ -739,6 +764,8 @@ static int static_lds_for(int cb) {
     default: return 2 * sizeof(TileBuf<4, 8, BIAS>) + kRed;
   }
 }
+
+int fwd_waves_per_simd(int dpad, int d) { return fwd_waves_for_blocks(dpad / 32 + (d % 32 == 0 ? 1 : 0)); }
 
 int fwd_static_lds(int dpad, int mode) {
   const int cb = dpad / 32;

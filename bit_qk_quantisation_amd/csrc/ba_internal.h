@@ -112,12 +112,20 @@ struct FwdArgs {
   int nwg;                 // workgroups
   int xcd_remap;           // 1: spread consecutive heads over the 8 XCDs
   int dyn_lds;             // dynamic LDS bytes per workgroup (table and/or padding)
+  int prio_balance;        // 1: lower the wave priority over the last keys
+                           // (every workgroup of the grid is resident at once)
 };
 
 // LDS bytes of the fused kernel: the bias table (table mode, dynamic) and
 // the static tile buffers.
 int fwd_table_lds(const FwdArgs& a, int mode);
 int fwd_static_lds(int dpad, int mode);
+
+// Waves per SIMD the fused kernel's register budget allows: 3 for up to 3
+// accumulator blocks (32 output channels each, plus one when d % 32 == 0),
+// 2 for up to 5, else 1.
+constexpr int fwd_waves_for_blocks(int nb) { return nb <= 3 ? 3 : (nb <= 5 ? 2 : 1); }
+int fwd_waves_per_simd(int dpad, int d);
 
 // Launch the fused kernel (template selected from d and the bias mode).
 int launch_attention(const FwdArgs& a, int mode, void* stream);
