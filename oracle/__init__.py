@@ -8,10 +8,13 @@ nothing from it.
 from .dense_fp64 import (  # noqa: F401
     binary_attention,
     binary_attention_dense_bias_rows,
+    binary_attention_int8_pv_rows,
     binary_attention_rows,
     binary_scores,
     pack_sign_bits,
     pack_words,
+    quantize_probs_u8,
+    quantize_values_int8,
     rel_pos_bias,
     sign_dots,
     sign_dots_from_bits,

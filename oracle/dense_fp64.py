@@ -274,3 +274,60 @@ def binary_attention_dense_bias_rows(q, k, v, bias, scale=None, rows=None,
     if keep:
         out.update(S=s, P=p, D=sc["D"])
     return out
+
+
+def quantize_values_int8(v) -> dict:
+    """Per-channel signed 8-bit values (es page, section 2, item
+    "Cuantizacion Hibrida": the values are quantized to 8 bits per channel;
+    ko page, section 2 (b).3).
+
+    For each leading index and channel c: amax_c = max_j |v_jc|, the scale
+    s_c = amax_c / 127 and the code vq_jc = round-half-even(v_jc * (127 /
+    amax_c)) in [-127, 127]; a channel that is all zero gets scale 0 and
+    codes 0.  The codes are decided in float32 (127 / amax_c correctly
+    rounded, then the product, then the rounding), the precision a kernel
+    decides them in.  Returns float64 scale [..., d] and int64 codes
+    [..., N, d]."""
+    vf = np.asarray(_f64(v), dtype=np.float32)
+    amax = np.abs(vf).max(axis=-2)
+    safe = np.where(amax > 0, amax, np.float32(1.0))
+    inv = np.where(amax > 0, np.float32(127.0) / safe, np.float32(0.0)).astype(np.float32)
+    codes = np.rint(vf * inv[..., None, :]).astype(np.int64)
+    return {"scale": amax.astype(np.float64) / 127.0, "codes": codes}
+
+
+def quantize_probs_u8(s) -> np.ndarray:
+    """Static unsigned 8-bit attention coefficients (es page, section 2,
+    item "Cuantizacion Hibrida": coefficients in [0, 1] take a static
+    unsigned 8-bit quantization).
+
+    Over the last axis, p = exp(s - max s) lies in [0, 1] (1 at the row
+    maximum), and the code is round-half-even(255 p) in [0, 255], decided in
+    float32.  Returns int64 codes."""
+    a = _f64(s)
+    m = a.max(axis=-1, keepdims=True)
+    p = np.exp(a - m).astype(np.float32)
+    return np.rint(np.float32(255.0) * p).astype(np.int64)
+
+
+def binary_attention_int8_pv_rows(q, k, v, table=None, gh: int = 0, gw: int = 0,
+                                  scale=None, rows=None, keep=False) -> dict:
+    """BinaryAttention with the pages' hybrid 8-bit P.V (es page, section 2,
+    item "Cuantizacion Hibrida"; ko page, section 2 (b).3: 1-bit Q/K, 8-bit
+    attention coefficients and values), for a subset of query rows.
+
+    S as in binary_scores; Pq = quantize_probs_u8(S) (row maximum -> 255);
+    (s_c, Vq) = quantize_values_int8(V) over all N keys of each (b, h);
+    O_ic = s_c * sum_j Pq_ij Vq_jc / sum_j Pq_ij.
+    The row sum is taken over the same codes that multiply V, so the 1/255
+    of the static scale cancels."""
+    sc = binary_scores(q, k, table, gh, gw, scale, rows)
+    pq = quantize_probs_u8(sc["S"])
+    vq = quantize_values_int8(v)
+    num = np.matmul(pq, vq["codes"]).astype(np.float64)
+    den = pq.sum(axis=-1, keepdims=True).astype(np.float64)
+    o = vq["scale"][..., None, :] * num / den
+    out = {"O": o, "alpha_q": sc["alpha_q"], "alpha_k": sc["alpha_k"], "rows": sc["rows"]}
+    if keep:
+        out.update(S=sc["S"], Pq=pq, Vq=vq["codes"], v_scale=vq["scale"])
+    return out

@@ -392,6 +392,91 @@ def dense_bias_row_shift_and_broadcast(ob):
     assert np.allclose(part, a1[:, :, rows, :], rtol=0, atol=1e-15)
 
 
+def _grid_values(rng, shape, step):
+    """Values step * n with integer n in [-127, 127] and |n| = 127 reached in
+    every channel of every (b, h): exactly what per-channel 8-bit codes with
+    scale `step` represent."""
+    n = rng.integers(-127, 128, size=shape)
+    n[..., 0, :] = np.where(rng.random(shape[:-2] + (shape[-1],)) < 0.5, -127, 127)
+    return step * n.astype(np.float64), n
+
+
+def int8_quantizers(ob):
+    """Per-channel value codes: v = s*n + e with |e| < s/2 must give code n
+    (round to nearest) and scale s when |n| reaches 127; an all-zero channel
+    gives scale 0 and codes 0.  Coefficient codes: every row's maximum maps
+    to 255, all codes lie in [0, 255], and a score ln(2)·k below the
+    maximum gives round(255 / 2^k)."""
+    rng = _rng(25)
+    step = 2.0 ** -5
+    v, n = _grid_values(rng, (2, 3, 40, 16), step)
+    e = rng.uniform(-0.45, 0.45, size=v.shape) * step
+    e[np.abs(n) == 127] = 0.0   # keep max |v| of each channel at exactly 127 steps
+    v = v + e
+    v[..., 7] = 0.0
+    n[..., 7] = 0
+    res = ob.quantize_values_int8(v)
+    assert np.array_equal(res["codes"], n)
+    want = np.full((2, 3, 16), step)
+    want[..., 7] = 0.0
+    assert np.allclose(res["scale"], want, rtol=0, atol=1e-15)
+    s = rng.normal(size=(3, 5, 30)) * 4.0
+    pq = ob.quantize_probs_u8(s)
+    assert pq.min() >= 0 and pq.max() <= 255
+    assert np.array_equal(pq.max(axis=-1), np.full((3, 5), 255))
+    assert np.array_equal(np.argmax(s, axis=-1), np.argmax(pq, axis=-1))
+    ladder = -math.log(2.0) * np.arange(9.0)
+    assert np.array_equal(ob.quantize_probs_u8(ladder[None]),
+                          np.array([[255, 128, 64, 32, 16, 8, 4, 2, 1]]))
+
+
+def int8_closed_forms(ob):
+    """Hybrid 8-bit attention on values that lie on their code grid: with
+    Q = 0 and no bias every coefficient code is 255 and O is the exact column
+    mean of V; with a one-hot table entry of 20 (other codes round to 0) each
+    query gets exactly the value row of the key at that grid offset."""
+    rng = _rng(26)
+    step = 2.0 ** -4
+    b, h, gh, gw, d = 2, 2, 3, 4, 8
+    n = gh * gw
+    v, _ = _grid_values(rng, (b, h, n, d), step)
+    k = _bf16_values(rng, (b, h, n, d))
+    q = np.zeros((b, h, n, d))
+    o = ob.binary_attention_int8_pv_rows(q, k, v)["O"]
+    assert np.allclose(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape), rtol=0, atol=1e-15)
+    dy0, dx0 = 1, -2
+    table = np.zeros((h, 2 * gh - 1, 2 * gw - 1))
+    table[:, dy0 + gh - 1, dx0 + gw - 1] = 20.0
+    o = ob.binary_attention_int8_pv_rows(q, k, v, table, gh, gw)["O"]
+    for i in range(n):
+        yi, xi = divmod(i, gw)
+        yj, xj = yi - dy0, xi - dx0
+        if 0 <= yj < gh and 0 <= xj < gw:
+            assert np.allclose(o[:, :, i], v[:, :, yj * gw + xj], rtol=0, atol=1e-15), i
+        else:
+            assert np.allclose(o[:, :, i], v.mean(axis=2), rtol=0, atol=1e-15), i
+
+
+def int8_error_bound(ob):
+    """Against the exact attention (itself pinned above): rounding V costs at
+    most s_c / 2, and rounding each coefficient by at most 1/2 of a code
+    moves the normalised weights by at most N / sum_j Pq_ij in total, so
+    |O8 - O| <= s_c / 2 + max_j |v_jc| * N / sum_j Pq_ij, element by element."""
+    rng = _rng(27)
+    for (b, h, gh, gw, d, spread) in ((1, 2, 4, 4, 16, 1.0), (2, 1, 3, 7, 33, 3.0), (1, 1, 8, 8, 64, 0.3)):
+        n = gh * gw
+        q = _bf16_values(rng, (b, h, n, d), spread)
+        k = _bf16_values(rng, (b, h, n, d), spread)
+        v = _bf16_values(rng, (b, h, n, d))
+        t = _bf16_values(rng, (h, 2 * gh - 1, 2 * gw - 1), 0.5)
+        r8 = ob.binary_attention_int8_pv_rows(q, k, v, t, gh, gw, keep=True)
+        ref = ob.binary_attention(q, k, v, t, gh, gw)["O"]
+        den = r8["Pq"].sum(axis=-1, keepdims=True)
+        vmax = np.abs(v).max(axis=2, keepdims=True)
+        bound = r8["v_scale"][:, :, None, :] / 2 + vmax * n / den + 1e-12
+        assert (np.abs(r8["O"] - ref) <= bound).all(), float((np.abs(r8["O"] - ref) - bound).max())
+
+
 ALL_PINS = [
     golden_hand_example,
     bits_definition,
@@ -409,4 +494,7 @@ ALL_PINS = [
     dense_bias_matches_table,
     dense_bias_one_hot,
     dense_bias_row_shift_and_broadcast,
+    int8_quantizers,
+    int8_closed_forms,
+    int8_error_bound,
 ]

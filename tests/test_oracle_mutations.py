@@ -140,6 +140,52 @@ def _dense_factory(**kw):
     return dense
 
 
+
+def _qv_per_token(v):
+    vf = np.asarray(ob._f64(v), dtype=np.float32)
+    amax = np.abs(vf).max(axis=-1, keepdims=True)
+    inv = (np.float32(127.0) / np.where(amax > 0, amax, np.float32(1.0))).astype(np.float32)
+    return {"scale": np.broadcast_to(amax.max(axis=-2), vf.shape[:-2] + vf.shape[-1:]).astype(np.float64) / 127.0,
+            "codes": np.rint(vf * inv).astype(np.int64)}
+
+
+def _qv_floor(v):
+    vf = np.asarray(ob._f64(v), dtype=np.float32)
+    amax = np.abs(vf).max(axis=-2)
+    inv = np.where(amax > 0, np.float32(127.0) / np.where(amax > 0, amax, 1), 0).astype(np.float32)
+    return {"scale": amax.astype(np.float64) / 127.0, "codes": np.floor(vf * inv[..., None, :]).astype(np.int64)}
+
+
+def _qp_not_shifted(s):
+    a = ob._f64(s)
+    return np.rint(np.float32(255.0) * np.minimum(np.exp(a), 1.0).astype(np.float32)).astype(np.int64)
+
+
+def _qp_127(s):
+    a = ob._f64(s)
+    p = np.exp(a - a.max(axis=-1, keepdims=True)).astype(np.float32)
+    return np.rint(np.float32(127.0) * p).astype(np.int64)
+
+
+def _int8_factory(**kw):
+    def f(q, k, v, table=None, gh=0, gw=0, scale=None, rows=None, keep=False):
+        sc = ob.binary_scores(q, k, table, gh, gw, scale, rows)
+        pq = ob.quantize_probs_u8(sc["S"])
+        vq = ob.quantize_values_int8(v)
+        num = np.matmul(pq, vq["codes"]).astype(np.float64)
+        if kw.get("den_float"):
+            a = sc["S"]
+            den = 255.0 * np.exp(a - a.max(axis=-1, keepdims=True)).sum(axis=-1, keepdims=True)
+        else:
+            den = pq.sum(axis=-1, keepdims=True).astype(np.float64)
+        sv = 1.0 if kw.get("no_scale") else vq["scale"][..., None, :]
+        out = {"O": sv * num / den, "alpha_q": sc["alpha_q"], "alpha_k": sc["alpha_k"], "rows": sc["rows"]}
+        if keep:
+            out.update(S=sc["S"], Pq=pq, Vq=vq["codes"], v_scale=vq["scale"])
+        return out
+    return f
+
+
 MUTATIONS = {
     "sign_zero_is_negative": ("sign_pm1", _sign_zero_negative),
     "sign_from_signbit": ("sign_pm1", _sign_from_signbit),
@@ -163,6 +209,12 @@ MUTATIONS = {
     "dense_bias_dropped": ("binary_attention_dense_bias_rows", _dense_factory(dropped=True)),
     "dense_bias_first_batch_only": ("binary_attention_dense_bias_rows",
                                     _dense_factory(first_batch_only=True)),
+    "int8_v_scale_per_token": ("quantize_values_int8", _qv_per_token),
+    "int8_v_codes_floor": ("quantize_values_int8", _qv_floor),
+    "int8_p_not_shifted_by_row_max": ("quantize_probs_u8", _qp_not_shifted),
+    "int8_p_scale_127": ("quantize_probs_u8", _qp_127),
+    "int8_row_sum_unquantized": ("binary_attention_int8_pv_rows", _int8_factory(den_float=True)),
+    "int8_value_scale_dropped": ("binary_attention_int8_pv_rows", _int8_factory(no_scale=True)),
 }
 
 
