@@ -2,7 +2,7 @@
 """Benchmark of the BinaryAttention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--layout bhnd|bnhd|qkv] [--bias table|dense|dense-batch]
+                    [--layout bhnd|bnhd|qkv] [--bias table|dense|dense-batch] [--pv bf16|int8]
 
 One step is one full forward (ba_attention_prepare + ba_attention_fwd_prepared,
 i.e. exactly ba_attention_fwd) over the resident bf16 inputs of the chosen
@@ -22,6 +22,10 @@ bias [H,N,N] shared by the batch (dense-batch: [B,H,N,N]), drawn N(0, 0.02);
 the step is then ba_attention_prepare + ba_attention_fwd_dense_bias_prepared,
 and the roofline object names whichever bound (matrix cores or HBM) the fused
 kernel is closer to.
+
+--pv int8 runs the pages' hybrid 8-bit P.V (ba_attention_fwd_int8pv: three
+kernels in one call), so only the whole step is timed; its roofline takes the
+fp4 QK + int8 P.V matrix-core bound.
 
 Printed: one JSON line on stdout with the throughput in TFLOP-eq/s
 (4*B*H*N^2*d per step, the FLOPs of dense QK^T and P.V), the fused kernel's
@@ -60,6 +64,8 @@ PEAK_HBM_GBS = 8000.0
 # the other, the matrix-core bound of 4d flops-eq per score is:
 PEAK_MFMA_COMPOSITE = 4.0 / (2.0 / PEAK_FP4 + 2.0 / PEAK_BF16)
 PEAK_MFMA_INT8_BF16 = 4.0 / (2.0 / PEAK_INT8 + 2.0 / PEAK_BF16)
+# 8-bit P.V: QK on the fp4 unit, P.V on the int8 unit.
+PEAK_MFMA_FP4_INT8 = 4.0 / (2.0 / PEAK_FP4 + 2.0 / PEAK_INT8)
 
 PROFILES = ROOT / "profiles"
 FUSED_SOURCES = ("bit_qk_quantisation_amd/csrc/attention.hip",
@@ -175,6 +181,8 @@ def main() -> int:
                     help="host time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--layout", choices=("bhnd", "bnhd", "qkv"), default="bhnd",
                     help="memory layout of q, k, v and o (see above)")
+    ap.add_argument("--pv", choices=("bf16", "int8"), default="bf16",
+                    help="P.V precision (see above)")
     ap.add_argument("--bias", choices=("table", "dense", "dense-batch"), default="table",
                     help="bias form (see above)")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -241,8 +249,22 @@ def main() -> int:
                 q.data_ptr(), dense.data_ptr(), dsb, dense.stride(1), dense.stride(2), B, H, N, d, scale,
                 out.data_ptr(), wsp, nbytes, sp))
 
-    split = args.layout == "bhnd"
-    if not split:
+    split = args.layout == "bhnd" and args.pv == "bf16"
+    if args.pv == "int8":
+        if args.layout != "bhnd" or dense is not None:
+            log("--pv int8 runs with the contiguous layout and the table bias only")
+            return 2
+        nb8 = lib.ba_workspace_bytes_int8pv(B, H, N, d, gh, gw)
+        ws8 = torch.empty(nb8 + 256, dtype=torch.uint8, device=dev)
+        wsp8 = (ws8.data_ptr() + 255) // 256 * 256
+
+        def prepare():  # noqa: F811 -- one call runs all three kernels
+            bq.check(lib, lib.ba_attention_fwd_int8pv(q.data_ptr(), k.data_ptr(), v.data_ptr(), tp, gh, gw,
+                                                      B, H, N, d, scale, out.data_ptr(), wsp8, nb8, sp))
+
+        def fused():  # noqa: F811
+            pass
+    elif not split:
         import ctypes
         if args.layout == "bnhd":
             views = [x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v)]
@@ -300,6 +322,7 @@ def main() -> int:
     fus_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
     if not split:  # the "prologue" interval held the whole step
         fus_ms = pro_ms
+    peak = PEAK_MFMA_FP4_INT8 if args.pv == "int8" else PEAK_MFMA_COMPOSITE
 
     if args.copy_mb:
         src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
@@ -315,11 +338,11 @@ def main() -> int:
     pro_bytes, fus_bytes = algorithmic_bytes(w, npad, dense_bytes)
     traffic = measured_traffic(name) if split and dense is None else None
     fused_gbs = fus_bytes / (fus_ms * 1e-3) / 1e9
-    hbm_bound = dense is not None and fused_gbs / PEAK_HBM_GBS > fused_tf / PEAK_MFMA_COMPOSITE
+    hbm_bound = dense is not None and fused_gbs / PEAK_HBM_GBS > fused_tf / peak
 
     baseline = None
-    if args.cpu_seconds > 0 and dense is not None:
-        log("[bench] no CPU baseline with --bias dense")
+    if args.cpu_seconds > 0 and (dense is not None or args.pv != "bf16"):
+        log("[bench] no CPU baseline with --bias dense or --pv int8")
     elif args.cpu_seconds > 0:
         baseline = cpu_baseline(w, inp, out, args.cpu_seconds)
 
@@ -334,18 +357,22 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if args.pv == "bf16" else "int8",
         "data": "synthetic",
         "config": {**w.describe(), "qk": "1-bit signs as +/-1 fp4 on MFMA (exact integer dots)",
-                   "pv": "bf16 MFMA, fp32 accumulate", "softmax": "fp32, base 2",
+                   "pv": ("bf16 MFMA, fp32 accumulate" if args.pv == "bf16" else
+                          "u8 coefficients x per-channel s8 values on int8 MFMA, int32 accumulate"),
+                   "softmax": "fp32, base 2",
                    "parallelism": "single GPU", "layout": args.layout, "bias": args.bias},
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_kernel (fused)" if split else "whole step (prologue + fused, one strided call)",
+            "kernel": ("attn_fwd_kernel (fused)" if split else
+                       "whole step (3 kernels, one call; fp4 QK + int8 P.V bound)" if args.pv == "int8" else
+                       "whole step (prologue + fused, one strided call)"),
             "achieved": round(fused_tf, 1),
-            "peak": round(PEAK_MFMA_COMPOSITE, 1),
+            "peak": round(peak, 1),
             "unit": "TFLOP/s",
-            "frac": round(fused_tf / PEAK_MFMA_COMPOSITE, 4),
+            "frac": round(fused_tf / peak, 4),
             "traffic": traffic,
         } if not hbm_bound else {
             "bound": "hbm",
@@ -375,7 +402,7 @@ def main() -> int:
         log(f"[bench] {name}: step {ms_step * 1e3:.1f} us (prologue {pro_ms * 1e3:.1f} us, "
             f"fused {fus_ms * 1e3:.1f} us) -> {value:.1f} TFLOP-eq/s")
     else:
-        log(f"[bench] {name} ({args.layout}): step {ms_step * 1e3:.1f} us -> {value:.1f} TFLOP-eq/s")
+        log(f"[bench] {name} ({args.layout}, pv {args.pv}): step {ms_step * 1e3:.1f} us -> {value:.1f} TFLOP-eq/s")
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -10,6 +10,7 @@ If the library is missing the calls raise; there is no CPU fallback.
                                               strided [B,H,N,d] views (e.g.
                                               a [B,N,H,d] tensor transposed)
     attention_fwd_dense_bias(q, k, v, bias) -> O (bf16); bias [1 or B, H, N, N]
+    attention_fwd_int8pv(q, k, v, table, gh, gw) -> O (bf16), 8-bit P.V
     qk_int_dot(qbits, kbits, d, route)     -> D (int32)
     workspace_bytes(B, H, N, d, gh, gw)    -> int
 """
@@ -24,7 +25,7 @@ import torch
 from ._lib import (BinAttnError, EXPORTS, ROUTE_MFMA_FP4,  # noqa: F401
                    ROUTE_VALU_POPCOUNT, check, load)
 
-__all__ = ["pack_signs", "attention_fwd", "attention_fwd_dense_bias", "qk_int_dot", "workspace_bytes",
+__all__ = ["pack_signs", "attention_fwd", "attention_fwd_dense_bias", "attention_fwd_int8pv", "qk_int_dot", "workspace_bytes",
            "pack_words", "BinAttnError", "ROUTE_MFMA_FP4", "ROUTE_VALU_POPCOUNT",
            "Workspace"]
 
@@ -186,6 +187,42 @@ def attention_fwd_dense_bias(q, k, v, bias, scale=None, out=None,
     check(lib, lib.ba_attention_fwd_dense_bias(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), bias.data_ptr(), sb, bias.stride(1),
         bias.stride(2), B, H, N, d, float(scale), out.data_ptr(), strides, aligned,
+        ws.numel() - (aligned - base), _stream(q.device)))
+    return out
+
+
+def attention_fwd_int8pv(q, k, v, table=None, gh: int = 0, gw: int = 0, scale=None,
+                         out=None, workspace: Workspace | None = None):
+    """BinaryAttention forward with the 8-bit P.V (8-bit attention
+    coefficients and per-channel 8-bit values): contiguous bf16 q, k, v
+    [B,H,N,d] (+ bf16 table [H, 2gh-1, 2gw-1]) -> bf16 O [B,H,N,d]."""
+    lib = load()
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, torch.bfloat16, 4)
+    if q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k and v must have the same shape")
+    B, H, N, d = q.shape
+    if table is not None:
+        _need(table, "table", torch.bfloat16, 3)
+        if tuple(table.shape) != (H, 2 * gh - 1, 2 * gw - 1):
+            raise ValueError(f"table must be [H, 2gh-1, 2gw-1] = {(H, 2*gh-1, 2*gw-1)}")
+    else:
+        gh = gw = 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 4)
+    nbytes = lib.ba_workspace_bytes_int8pv(B, H, N, d, gh, gw)
+    if nbytes == 0:
+        raise BinAttnError(3, f"unsupported problem B={B} H={H} N={N} d={d} grid={gh}x{gw}")
+    ws = (workspace or _default_ws).get(q.device, nbytes)
+    base = ws.data_ptr()
+    aligned = (base + 255) // 256 * 256
+    check(lib, lib.ba_attention_fwd_int8pv(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), None if table is None else table.data_ptr(),
+        int(gh), int(gw), B, H, N, d, float(scale), out.data_ptr(), aligned,
         ws.numel() - (aligned - base), _stream(q.device)))
     return out
 

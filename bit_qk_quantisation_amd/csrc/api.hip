@@ -83,11 +83,13 @@ int choose_mode(bool has_bias, int gh, int gw, int64_t N) {
 // Byte offsets of the workspace sections of ba_attention_fwd.
 struct Layout {
   int64_t Npad, W, dpad, Lpad;
-  int64_t kop, alpha_k, kmax, vt, bias4, rowmax, total;
+  int64_t kop, alpha_k, kmax, vt, vq, vpart, vscale, vcsum, bias4, rowmax, total;
   int mode;
 };
 
-Layout layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int gw) {
+// int8pv: the 8-bit P.V forward, whose values are int8 code tiles with
+// per-channel scales instead of the bf16 V^T copy.
+Layout layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int gw, bool int8pv = false) {
   Layout L{};
   L.Npad = round_up(N, ba::kNAlign);
   L.W = (d + 31) / 32;
@@ -104,7 +106,11 @@ Layout layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int
   L.kop = take(BH * L.Npad * ((L.W + 1) / 2) * 32);  // fp4 key operands: 32 B per 64 channels
   L.alpha_k = take(BH * L.Npad * 4);
   L.kmax = take(BH * (L.Npad / 64) * 4);
-  L.vt = take(BH * L.dpad * L.Npad * 2);
+  L.vt = take(int8pv ? 0 : BH * L.dpad * L.Npad * 2);
+  L.vq = take(int8pv ? BH * L.dpad * L.Npad : 0);
+  L.vpart = take(int8pv ? BH * (L.Npad / ba::kPackTok) * L.dpad * 4 : 0);
+  L.vscale = take(int8pv ? BH * L.dpad * 4 : 0);
+  L.vcsum = take(int8pv ? BH * L.dpad * 4 : 0);
   const bool rows = L.mode == ba::kBiasRows;
   L.bias4 = take(rows ? H * (2 * gh - 1 + 2 * ba::kBiasPadRows) * 4 * L.Lpad * 4 : 0);
   L.rowmax = take(rows ? H * (2 * gh - 1) * 4 : 0);
@@ -238,6 +244,15 @@ ba_status ba_pack_signs(const void* x, int64_t B, int64_t H, int64_t N, int d,
   return BA_OK;
 }
 
+size_t ba_workspace_bytes_int8pv(int64_t B, int64_t H, int64_t N, int d, int gh, int gw) {
+  if (check_dims(B, H, N, d) != BA_OK || d > 128 || N > 65536) return 0;
+  const bool has_bias = gh > 0 || gw > 0;
+  if (has_bias && (gh < 1 || gw < 1 || static_cast<int64_t>(gh) * gw != N)) return 0;
+  const Layout L = layout(B, H, N, d, has_bias, gh, gw, true);
+  if (L.mode < 0) return 0;
+  return static_cast<size_t>(L.total);
+}
+
 size_t ba_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int gh, int gw) {
   if (check_dims(B, H, N, d) != BA_OK) return 0;
   const bool has_bias = gh > 0 || gw > 0;
@@ -261,8 +276,10 @@ struct DenseBias {
 // arguments of both kernels.
 struct Plan {
   ba::FwdArgs f;
+  ba::PrologueArgs p0;  // 8-bit P.V only: value statistics and bias rows, before p
   ba::PrologueArgs p;
   int mode;
+  bool int8pv;
 };
 
 // Validates a forward request.  `kv` selects the checks of k and v (the
@@ -274,7 +291,7 @@ struct Plan {
 ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const void* bias, int gh, int gw,
                     int64_t B, int64_t H, int64_t N, int d, float scale, void* o, bool qo,
                     const int64_t* strides, const DenseBias* dense, void* workspace, size_t ws_bytes,
-                    Plan* plan) {
+                    Plan* plan, bool int8pv = false) {
   if (kv && (!k || !v)) return fail(BA_ERR_NULL, "k and v must be non-NULL");
   if (qo && (!q || !o)) return fail(BA_ERR_NULL, "q and o must be non-NULL");
   ba_status st = check_dims(B, H, N, d);
@@ -328,12 +345,18 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
     if (overlaps(o, ob, dense->ptr, static_cast<size_t>(bspan) * 2))
       return fail(BA_ERR_SHAPE, "o must not overlap the bias");
   }
+  if (int8pv) {
+    if (d > 128) return fail(BA_ERR_UNSUPPORTED, "the 8-bit P.V forward supports d <= 128 (d = %d)", d);
+    if (N > 65536)
+      return fail(BA_ERR_UNSUPPORTED, "the 8-bit P.V forward supports N <= 65536 (exact int32 sums), N = %lld",
+                  (long long)N);
+  }
   const int mode = dense ? static_cast<int>(ba::kBiasDense) : choose_mode(bias != nullptr, gh, gw, N);
   if (mode < 0)
     return fail(BA_ERR_UNSUPPORTED,
                 "bias grid %dx%d: the table rows do not fit the tile window and the table exceeds 48 KiB",
                 gh, gw);
-  const Layout L = layout(B, H, N, d, bias != nullptr, dense ? 0 : gh, dense ? 0 : gw);
+  const Layout L = layout(B, H, N, d, bias != nullptr, dense ? 0 : gh, dense ? 0 : gw, int8pv);
   if (!workspace) return fail(BA_ERR_WORKSPACE, "workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(BA_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -352,6 +375,11 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   f.kop = reinterpret_cast<const uint32_t*>(ws + L.kop);
   f.alpha_k = reinterpret_cast<const float*>(ws + L.alpha_k);
   f.vt = reinterpret_cast<const uint16_t*>(ws + L.vt);
+  if (int8pv) {
+    f.vq = reinterpret_cast<const int8_t*>(ws + L.vq);
+    f.vscale = reinterpret_cast<const float*>(ws + L.vscale);
+    f.vcsum = reinterpret_cast<const int*>(ws + L.vcsum);
+  }
   f.bias4 = reinterpret_cast<const float*>(ws + L.bias4);
   f.bias_row_max = reinterpret_cast<const float*>(ws + L.rowmax);
   f.kmax_blk = reinterpret_cast<const float*>(ws + L.kmax);
@@ -397,17 +425,35 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   p = ba::PrologueArgs{};
   p.kv = ba::KvJob{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), const_cast<uint32_t*>(f.kop),
                    const_cast<float*>(f.alpha_k), const_cast<float*>(f.kmax_blk), const_cast<uint16_t*>(f.vt),
+                   nullptr, nullptr, nullptr, nullptr,
                    vs[1], vs[2], BH, static_cast<int>(H), f.N, f.Npad, d, f.W, (f.W + 1) / 2, f.dpad};
   p.kv_blocks = BH * (L.Npad / ba::kPackTok);
   p.lds = ba::prologue_lds(d, true);
+  // the 8-bit forward builds the bias rows in its first launch, beside the
+  // value statistics the second launch needs
+  plan->p0 = ba::PrologueArgs{};
+  ba::PrologueArgs& pb = int8pv ? plan->p0 : p;
   if (mode == ba::kBiasRows) {
-    p.bias = ba::BiasJob{static_cast<const uint16_t*>(bias), const_cast<float*>(f.bias4),
-                         const_cast<float*>(f.bias_row_max), gh, gw, f.Lpad};
-    p.bias_blocks = H * (2 * gh - 1 + 2 * ba::kBiasPadRows);
+    pb.bias = ba::BiasJob{static_cast<const uint16_t*>(bias), const_cast<float*>(f.bias4),
+                          const_cast<float*>(f.bias_row_max), gh, gw, f.Lpad};
+    pb.bias_blocks = H * (2 * gh - 1 + 2 * ba::kBiasPadRows);
   }
-  const int64_t pblocks = p.kv_blocks + p.bias_blocks;
+  if (int8pv) {
+    float* vpart = reinterpret_cast<float*>(ws + L.vpart);
+    int* vcsum = reinterpret_cast<int*>(ws + L.vcsum);
+    pb.vstat = ba::VstatJob{static_cast<const uint16_t*>(v), vpart, vcsum, vs[2], BH, static_cast<int>(H),
+                            f.N, f.Npad, d, f.dpad};
+    pb.vstat_blocks = kv ? BH * (L.Npad / ba::kPackTok) : 0;
+    pb.lds = f.dpad * 4;
+    p.kv.vq = reinterpret_cast<int8_t*>(ws + L.vq);
+    p.kv.vpart = vpart;
+    p.kv.vscale = reinterpret_cast<float*>(ws + L.vscale);
+    p.kv.vcsum = vcsum;
+  }
+  const int64_t pblocks = p.kv_blocks + pb.bias_blocks + pb.vstat_blocks;
   if (pblocks > 0x7fffffff) return fail(BA_ERR_SHAPE, "problem too large");
   plan->mode = mode;
+  plan->int8pv = int8pv;
   return BA_OK;
 }
 
@@ -448,6 +494,22 @@ ba_status ba_attention_fwd_prepared(const void* q, const void* bias, int gh, int
                            const_cast<void*>(workspace), ws_bytes, &plan);
   if (st != BA_OK) return st;
   const int err = ba::launch_attention(plan.f, plan.mode, stream);
+  if (err != 0) return hip_fail(err, "attention launch");
+  return BA_OK;
+}
+
+ba_status ba_attention_fwd_int8pv(const void* q, const void* k, const void* v, const void* bias, int gh, int gw,
+                                  int64_t B, int64_t H, int64_t N, int d, float scale, void* o, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  Plan plan;
+  ba_status st = make_plan(q, k, v, true, bias, gh, gw, B, H, N, d, scale, o, true, nullptr, nullptr, workspace,
+                           ws_bytes, &plan, true);
+  if (st != BA_OK) return st;
+  int err = ba::launch_prologue(plan.p0, stream);
+  if (err != 0) return hip_fail(err, "value statistics launch");
+  err = ba::launch_prologue(plan.p, stream);
+  if (err != 0) return hip_fail(err, "prologue launch");
+  err = ba::launch_attention_int8(plan.f, plan.mode, stream);
   if (err != 0) return hip_fail(err, "attention launch");
   return BA_OK;
 }

@@ -104,6 +104,7 @@ struct Ctx {
   uint32_t dvoff;      // this lane's byte offset in its dense-tile copies
   uint32_t dld2;       // dense bias row stride in bytes
   int off_dn[4];       // this lane's dense-tile LDS bytes, group b of block 0
+  int off8[2];         // this lane's int8 value-operand LDS bytes, per block (8-bit P.V)
 };
 
 // Uniform per-tile position of the keys on the grid (table-row mode).
@@ -156,7 +157,11 @@ __device__ __forceinline__ T lds_load(const void* base, int byte_off) {
 // a 1 KiB block, or [4l, 4l+4) of a 256-byte block).  In table mode the
 // grid offsets of the tile's keys are computed and stored directly: `tb` was
 // last read before the previous barrier.
-template <int NCH, int CB, int BIAS>
+// What a tile copy brings of the values: nothing (the 8-bit path's row
+// maximum pass), the bf16 V^T tile, or the int8 value-code tile.
+enum VCopy { kVNone = 0, kVBf16 = 1, kVInt8 = 2 };
+
+template <int NCH, int CB, int BIAS, int VM = kVBf16>
 __device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TileBuf<NCH, CB, BIAS>& tb, int t, const KeyPos& kp) {
   const FwdArgs& a = *c.a;
   constexpr int kKBytes = NCH * kBN * 2 * 16;
@@ -171,9 +176,19 @@ __device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TileBuf<NCH, 
   // this lane's byte in its 1 KiB pieces, recomputed here rather than kept
   // in a register through the key loop
   const uint32_t loff = static_cast<uint32_t>(c.wave * 1024 + c.lane * 16);
+  if (VM == kVBf16) {
 #pragma unroll
-  for (int j = 0; j < kVtBytes / 4096; ++j)
-    dma16(c.vrs, vdst + (c.wave + 4 * j) * 1024, loff, static_cast<uint32_t>(t * kVtBytes + j * 4096));
+    for (int j = 0; j < kVtBytes / 4096; ++j)
+      dma16(c.vrs, vdst + (c.wave + 4 * j) * 1024, loff, static_cast<uint32_t>(t * kVtBytes + j * 4096));
+  } else if (VM == kVInt8) {
+    // 2 CB pieces of 1 KiB (dpad rows of 64 bytes), piece = wave + 4 j
+    constexpr int kV8Bytes = 32 * CB * kBN;
+#pragma unroll
+    for (int j = 0; j < (2 * CB + 3) / 4; ++j)
+      if (c.wave + 4 * j < 2 * CB)
+        dma16(c.vrs, vdst + (c.wave + 4 * j) * 1024, static_cast<uint32_t>(c.lane * 16),
+              static_cast<uint32_t>(t * kV8Bytes + (c.wave + 4 * j) * 1024));
+  }
   if (c.wave == 0) dma4(c.ars, &tb.ak[0], static_cast<uint32_t>(c.lane * 4), static_cast<uint32_t>(kp.k0 * 4));
   if (BIAS == kBiasRows) {
     // window rows start at dy = yq_lo - yk_hi; yk_hi is the row of block 1
@@ -453,7 +468,7 @@ __device__ __forceinline__ void fast_step(const Ctx<NCH>& c, const TileBuf<NCH, 
   const bool more = t + 1 < nkt;
   const KeyPos kn = next_keys(kp, a.gw);
   if (more) copy_tile_async<NCH, CB, BIAS>(c, nxt, t + 1, kn);
-  if (BIAS == kBiasRows || kp.k0 + kBN <= a.N) {
+  if (kp.k0 + kBN <= a.N) {  // a full tile; the ragged last one is masked
     pipelined_block<false, !FIRST, NCH, CB, XONES, BIAS>(c, cur, kp, 0, pp, acc);
     pipelined_block<false, true, NCH, CB, XONES, BIAS>(c, cur, kp, 1, pp, acc);
   } else {
@@ -507,8 +522,11 @@ __device__ __forceinline__ void pass_step(const Ctx<NCH>& c, const TileBuf<NCH, 
   const bool more = t + 1 < nkt;
   const KeyPos kn = next_keys(kp, a.gw);
   if (more) copy_tile_async<NCH, CB, BIAS>(c, nxt, t + 1, kn);
-  // With table rows, keys past N meet -inf padding rows: no mask needed.
-  if (BIAS == kBiasRows || kp.k0 + kBN <= a.N)
+  // Keys past N are masked on the ragged last tile, in every bias mode: the
+  // padding rows of the table-row bias keep the window reads inside the
+  // rows, but a padded key (grid row >= gh) seen from a query on grid row
+  // >= 1 falls on a real table row.
+  if (kp.k0 + kBN <= a.N)
     compute_tile<FAST, false, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow);
   else
     compute_tile<FAST, true, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow);
@@ -543,21 +561,12 @@ __device__ __forceinline__ void run_pass(const Ctx<NCH>& c, TileBuf<NCH, CB, BIA
   if (XONES) acc.rs[0] = sum_halves(acc.rs[0] + acc.rs[1]);
 }
 
-// Waves per SIMD the register budget is sized for (accumulator blocks).
-template <int NB>
-struct Occupancy {
-  static constexpr int kWaves = fwd_waves_for_blocks(NB);
-};
-
-template <int NCH, int CB, bool XONES, int BIAS>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<CB + XONES>::kWaves)))
-attn_fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb0;
-  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb1;
-  __shared__ float red[kThreads / 64];
-  extern __shared__ __attribute__((aligned(16))) float s_table[];
-
-  Ctx<NCH> c;
+// Everything a workgroup sets up before its key loop: its (b, h) and
+// query tile, this lane's packed query, the per-lane LDS offsets, the
+// buffer resources of the tile copies, the bias table in LDS (table mode).
+// Returns the logit bound M (log2 units) of the workgroup.
+template <int NCH, int CB, int BIAS>
+__device__ __forceinline__ float workgroup_setup(Ctx<NCH>& c, const FwdArgs& a, float* red, float* s_table) {
   c.a = &a;
   c.table = s_table;
   c.tid = threadIdx.x;
@@ -701,7 +710,25 @@ attn_fwd_kernel(FwdArgs a) {
   km = block_max(km, red);
   bm = block_max(bm, red);
   const float qm = block_max(alpha_q, red);
-  const float M = a.qscale * qm * km * static_cast<float>(a.d) + bm;
+  return a.qscale * qm * km * static_cast<float>(a.d) + bm;
+}
+
+// Waves per SIMD the register budget is sized for (accumulator blocks).
+template <int NB>
+struct Occupancy {
+  static constexpr int kWaves = fwd_waves_for_blocks(NB);
+};
+
+template <int NCH, int CB, bool XONES, int BIAS>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<CB + XONES>::kWaves)))
+attn_fwd_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb0;
+  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb1;
+  __shared__ float red[kThreads / 64];
+  extern __shared__ __attribute__((aligned(16))) float s_table[];
+
+  Ctx<NCH> c;
+  const float M = workgroup_setup<NCH, CB, BIAS>(c, a, red, s_table);
 
   Acc<CB, XONES> acc;
   if constexpr (BIAS == kBiasDense) {
@@ -739,6 +766,169 @@ attn_fwd_kernel(FwdArgs a) {
           uint2 w;
           w.x = pack_bf16x2(acc.o[cb][4 * b + 0] * inv, acc.o[cb][4 * b + 1] * inv);
           w.y = pack_bf16x2(acc.o[cb][4 * b + 2] * inv, acc.o[cb][4 * b + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + c0) = w;
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------ 8-bit P.V path ---
+// The pages' hybrid quantization ("Cuantizacion Hibrida"): 1-bit Q and K,
+// 8-bit attention coefficients and values.  Coefficients in [0, 1] take a
+// static unsigned 8-bit code, values a per-channel signed 8-bit code:
+//   code_ij = round-half-even(255 * 2^(s_ij - m_i)),  m_i = max_j s_ij,
+//   O_ic    = s_c * sum_j code_ij vq_jc / sum_j code_ij.
+// The codes are taken against the true row maximum, so a first pass over
+// the keys finds m_i (QK and logits only), and the second forms the codes
+// and runs P.V on v_mfma_i32_32x32x32_i8.  That instruction multiplies
+// signed bytes, so the coefficient codes enter as code - 128 (the sign bit
+// flipped) and the epilogue adds back 128 * sum_j vq_jc, a column sum of
+// the value codes the prologue wrote: the integer product is exact.
+constexpr float kLog2_255 = 7.994353436858858f;
+
+template <int CB>
+struct Acc8 {
+  v16i o[CB];
+};
+
+__device__ __forceinline__ void pin_uniform_i(v16i& x) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    int e = x[i];
+    asm volatile("" : "+v"(e));
+    x[i] = e;
+  }
+}
+
+// One 64-key tile of the 8-bit path.  MAIN = false: running maximum of the
+// logits only.  MAIN: the lane's 16 codes of each 32-key block, 4 per dword
+// in the order the lane holds the keys (slot 16 lh + 4 g + i = key
+// 8 g + 4 lh + i, the order of the value-code tile), the row sum of the
+// codes, and the product with the value codes.
+template <bool MAIN, bool MASK, int NCH, int CB, int BIAS>
+__device__ __forceinline__ void int8_tile(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& tb, const KeyPos& kp,
+                                          float& mrow, float off, Acc8<CB>& acc, uint32_t& rsum) {
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    v16f s = v16f{};
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+      s = mfma_signs_32x32x64(lds_load<v4i>(tb.k, c.off_k + ch * 2048 + blk * 1024), c.qop[ch], s);
+    float sc[16];
+    block_logits<MASK, NCH, CB, BIAS>(c, tb, kp, blk, s, sc);
+    if (!MAIN) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mrow = fmaxf(mrow, sc[r]);
+      continue;
+    }
+    v4i pb;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t w = 0u;
+      w = __builtin_amdgcn_cvt_pk_u8_f32(fast_exp2(sc[4 * g + 0] + off), 0, w);
+      w = __builtin_amdgcn_cvt_pk_u8_f32(fast_exp2(sc[4 * g + 1] + off), 1, w);
+      w = __builtin_amdgcn_cvt_pk_u8_f32(fast_exp2(sc[4 * g + 2] + off), 2, w);
+      w = __builtin_amdgcn_cvt_pk_u8_f32(fast_exp2(sc[4 * g + 3] + off), 3, w);
+      rsum = __builtin_amdgcn_udot4(w, 0x01010101u, rsum, false);
+      pb[g] = static_cast<int>(w ^ 0x80808080u);
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      acc.o[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(lds_load<v4i>(tb.vt, c.off8[blk] + cb * 2048), pb, acc.o[cb],
+                                                         0, 0, 0);
+  }
+}
+
+template <bool MAIN, int NCH, int CB, int BIAS>
+__device__ __forceinline__ void int8_step(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& cur,
+                                          TileBuf<NCH, CB, BIAS>& nxt, int t, int nkt, KeyPos& kp, float& mrow,
+                                          float off, Acc8<CB>& acc, uint32_t& rsum) {
+  const FwdArgs& a = *c.a;
+  const KeyPos kn = next_keys(kp, a.gw);
+  if (t + 1 < nkt) copy_tile_async<NCH, CB, BIAS, MAIN ? kVInt8 : kVNone>(c, nxt, t + 1, kn);
+  if (kp.k0 + kBN <= a.N)
+    int8_tile<MAIN, false, NCH, CB, BIAS>(c, cur, kp, mrow, off, acc, rsum);
+  else
+    int8_tile<MAIN, true, NCH, CB, BIAS>(c, cur, kp, mrow, off, acc, rsum);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  kp = kn;
+}
+
+template <bool MAIN, int NCH, int CB, int BIAS>
+__device__ __forceinline__ void int8_pass(const Ctx<NCH>& c, TileBuf<NCH, CB, BIAS>& tb0, TileBuf<NCH, CB, BIAS>& tb1,
+                                          float& mrow, float off, Acc8<CB>& acc, uint32_t& rsum) {
+  const FwdArgs& a = *c.a;
+  KeyPos kp;
+  kp.k0 = 0;
+  kp.ky[0] = 0;
+  kp.kx[0] = 0;
+  kp.ky[1] = (BIAS == kBiasRows && a.gw == 32) ? 1 : 0;
+  kp.kx[1] = (BIAS == kBiasRows && a.gw == 32) ? 0 : 32;
+  copy_tile_async<NCH, CB, BIAS, MAIN ? kVInt8 : kVNone>(c, tb0, 0, kp);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int nkt = (a.N + kBN - 1) / kBN;
+  for (int t = 0; t < nkt; t += 2) {
+    int8_step<MAIN, NCH, CB, BIAS>(c, tb0, tb1, t, nkt, kp, mrow, off, acc, rsum);
+    if (t + 1 < nkt) int8_step<MAIN, NCH, CB, BIAS>(c, tb1, tb0, t + 1, nkt, kp, mrow, off, acc, rsum);
+  }
+}
+
+template <int NCH, int CB, int BIAS>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<CB>::kWaves)))
+attn_fwd_int8_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb0;
+  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb1;
+  __shared__ float red[kThreads / 64];
+  extern __shared__ __attribute__((aligned(16))) float s_table[];
+
+  Ctx<NCH> c;
+  (void)workgroup_setup<NCH, CB, BIAS>(c, a, red, s_table);
+  // the value-code tiles of this (b, h): dpad rows of 64 bytes per tile
+  constexpr int kV8Bytes = 32 * CB * kBN;
+  c.vrs = make_rsrc(reinterpret_cast<const char*>(a.vq) + static_cast<int64_t>(c.bh) * (a.Npad / kBN) * kV8Bytes,
+                    static_cast<uint32_t>((a.Npad / kBN) * kV8Bytes));
+  {
+    // operand of block b: row li (+ 32 cb), chunk (2 b + lh) ^ ((li / 4) & 3)
+    const int x = (c.li >> 2) & 3;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) c.off8[b] = c.li * 64 + (((2 * b + c.lh) ^ x) << 4);
+  }
+
+  Acc8<CB> acc;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) acc.o[cb] = v16i{};
+  uint32_t rsum = 0u;
+  float mrow = -INFINITY;
+  int8_pass<false, NCH, CB, BIAS>(c, tb0, tb1, mrow, 0.0f, acc, rsum);
+  mrow = max_halves(mrow);
+  // exp2(s + off) = 255 * 2^(s - m): the row maximum gets code 255
+  int8_pass<true, NCH, CB, BIAS>(c, tb0, tb1, mrow, kLog2_255 - mrow, acc, rsum);
+
+  // ---- epilogue: O = s_c (acc + 128 colsum_c) / sum of codes, bf16 --------
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) pin_uniform_i(acc.o[cb]);
+  const auto pr = __builtin_amdgcn_permlane32_swap(rsum, rsum, false, false);
+  const float inv = 1.0f / static_cast<float>(pr[0] + pr[1]);
+  if (c.qi < a.N) {
+    uint16_t* orow = a.o + token_offset(a.os, c.bh / a.H, c.head, c.qi);
+    const float* vsc = a.vscale + static_cast<int64_t>(c.bh) * a.dpad;
+    const int* vcs = a.vcsum + static_cast<int64_t>(c.bh) * a.dpad;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int c0 = cb * 32 + 8 * b + 4 * c.lh;
+        if (c0 < a.d) {
+          const v4f sv = *reinterpret_cast<const v4f*>(vsc + c0);
+          const v4i cs = *reinterpret_cast<const v4i*>(vcs + c0);
+          float o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = static_cast<float>(acc.o[cb][4 * b + i] + 128 * cs[i]) * sv[i] * inv;
+          uint2 w;
+          w.x = pack_bf16x2(o[0], o[1]);
+          w.y = pack_bf16x2(o[2], o[3]);
           *reinterpret_cast<uint2*>(orow + c0) = w;
         }
       }
@@ -797,6 +987,37 @@ static int launch_nc(const FwdArgs& a, int mode, void* stream) {
       break;
   }
   return static_cast<int>(hipGetLastError());
+}
+
+template <int NCH, int CB>
+static int launch_int8_nc(const FwdArgs& a, int mode, void* stream) {
+  const int lds = a.dyn_lds;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(a.nwg), block(kThreads);
+  switch (mode) {
+    case kBiasNone:
+      hipLaunchKernelGGL((attn_fwd_int8_kernel<NCH, CB, kBiasNone>), grid, block, lds, s, a);
+      break;
+    case kBiasRows:
+      hipLaunchKernelGGL((attn_fwd_int8_kernel<NCH, CB, kBiasRows>), grid, block, lds, s, a);
+      break;
+    case kBiasTable:
+      hipLaunchKernelGGL((attn_fwd_int8_kernel<NCH, CB, kBiasTable>), grid, block, lds, s, a);
+      break;
+    default:
+      return static_cast<int>(hipErrorInvalidValue);
+  }
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_attention_int8(const FwdArgs& a, int mode, void* stream) {
+  switch (a.dpad / 32) {
+    case 1: return launch_int8_nc<1, 1>(a, mode, stream);
+    case 2: return launch_int8_nc<1, 2>(a, mode, stream);
+    case 3: return launch_int8_nc<2, 3>(a, mode, stream);
+    case 4: return launch_int8_nc<2, 4>(a, mode, stream);
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
 }
 
 int launch_attention(const FwdArgs& a, int mode, void* stream) {

@@ -56,9 +56,28 @@ struct KvJob {
   float* alpha;       // key scales [BH][Npad]
   float* alpha_max;   // largest key scale of each tile [BH][Npad/64]
   uint16_t* vt;       // bf16 [BH][Npad/64][dpad][64], see the prologue
+  // 8-bit P.V (vq != nullptr, then vt is unused): value codes, written as
+  // the fused kernel's int8 operand tiles, from the per-tile channel maxima
+  // of a previous launch; the scales and the column sums of the codes.
+  int8_t* vq;         // [BH][Npad/64][dpad][64], see the prologue
+  const float* vpart; // [BH][Npad/64][dpad] max |v| of each tile and channel
+  float* vscale;      // [BH][dpad] max |v| / 127 (written by tile 0)
+  int* vcsum;         // [BH][dpad] sum of the codes over the keys (atomic adds)
   Strides ks, vs;
   int64_t BH;
   int H, N, Npad, d, W, nch, dpad;
+};
+
+// Per-tile channel maxima of |V| for the 8-bit value codes, one 64-token
+// tile of one (b, h) per block; tile 0 of each head also clears the head's
+// column sums for the next launch.
+struct VstatJob {
+  const uint16_t* v;  // bf16, strides vs
+  float* vpart;       // [BH][Npad/64][dpad]
+  int* vcsum;         // [BH][dpad]
+  Strides vs;
+  int64_t BH;
+  int H, N, Npad, d, dpad;
 };
 
 struct BiasJob {
@@ -77,6 +96,8 @@ struct PrologueArgs {
   int64_t kv_blocks;
   BiasJob bias;
   int64_t bias_blocks;
+  VstatJob vstat;
+  int64_t vstat_blocks;
   int lds;  // dynamic LDS bytes per block
 };
 
@@ -102,6 +123,9 @@ struct FwdArgs {
   const uint16_t* dense;   // kBiasDense: bias(b, h, i, j) at b*dsb + h*dsh + i*dld + j
   int64_t dsb, dsh, dld;
   int dense_shared;        // kBiasDense: 1 when dsb == 0 and B > 1
+  const int8_t* vq;        // 8-bit P.V: value code tiles [BH][Npad/64][dpad][64]
+  const float* vscale;     // 8-bit P.V: [BH][dpad] value scales
+  const int* vcsum;        // 8-bit P.V: [BH][dpad] column sums of the codes
   uint16_t* o;             // bf16 output (strides os)
   Strides qs, os;
   int B, H, N, Npad, d, W, dpad;
@@ -129,6 +153,8 @@ int fwd_waves_per_simd(int dpad, int d);
 
 // Launch the fused kernel (template selected from d and the bias mode).
 int launch_attention(const FwdArgs& a, int mode, void* stream);
+// The fused kernel of the 8-bit P.V forward (d <= 128; no dense bias).
+int launch_attention_int8(const FwdArgs& a, int mode, void* stream);
 
 struct DotArgs {
   const uint32_t* qbits;  // [BH][N][W]

@@ -53,7 +53,8 @@ __device__ __forceinline__ void zero_pad_bytes(unsigned char* sb, int C, int W) 
 int prologue_lds(int d, bool kv) {
   const int W = (d + 31) / 32;
   const int common = kPackTok * 33 * 4 + kPackTok * W * 4;  // partial sums, sign words
-  return kv ? common + kPackTok * (d + 8) * 2 : common;      // + the value tile
+  // + the value tile and, for the 8-bit value codes, 1/scale per channel
+  return kv ? common + kPackTok * (d + 8) * 2 + 32 * W * 4 : common;
 }
 
 // ---------------------------------------------------------------- pack ----
@@ -113,6 +114,9 @@ __device__ __forceinline__ int vt_slot_key(int slot) {
   return g * 16 + (s < 4 ? 4 * hh + s : 8 + 4 * hh + (s - 4));
 }
 
+
+__device__ void kv_codes(const KvJob& job, int64_t blk, int64_t bh, int tile, const uint16_t* vs, int stride,
+                         float* sinv);
 
 __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
   const int d = job.d, W = job.W, C = d / 8, stride = d + 8;  // bf16 units
@@ -180,6 +184,11 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
                          static_cast<uint32_t>(op[2]), static_cast<uint32_t>(op[3]));
   }
 
+  if (job.vq) {
+    kv_codes(job, blk, bh, tile, vs, stride, reinterpret_cast<float*>(vs + kPackTok * stride));
+    return;
+  }
+
   // V^T
   uint16_t* out = job.vt + blk * static_cast<int64_t>(job.dpad) * kPackTok;
   for (int g = threadIdx.x; g < job.dpad * 8; g += kThreads) {
@@ -203,6 +212,97 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
   }
 }
 
+// 8-bit value codes of one tile ("Cuantizacion Hibrida": the values take a
+// per-channel 8-bit quantization).  Channel c of head (b, h) has scale
+// s_c = max_j |v_jc| / 127 over all N keys, the maximum of the tile maxima
+// the previous launch wrote; the code of v is round-half-even(v * (127 /
+// max)), the division correctly rounded.  The tile is written as dpad rows
+// of 64 bytes in the order of the fused kernel's int8 operands: within each
+// 32-key block, slot 16h + 4g + i holds key 8g + 4h + i (the order in which
+// a lane of the QK result holds its keys), and the four 16-byte chunks
+// q = 2 block + h of row c sit at chunk position q ^ ((c >> 2) & 3), so that
+// the 16 rows one quarter-wave reads hit 16 different bank groups.  The
+// codes of each channel are summed over the tile's keys into vcsum.
+__device__ void kv_codes(const KvJob& job, int64_t blk, int64_t bh, int tile, const uint16_t* vs, int stride,
+                         float* sinv) {
+  const int tiles = job.Npad / kPackTok, n0 = tile * kPackTok;
+  for (int c = threadIdx.x; c < job.dpad; c += kThreads) {
+    float m = 0.0f;
+    for (int t = 0; t < tiles; ++t) m = fmaxf(m, job.vpart[(bh * tiles + t) * job.dpad + c]);
+    sinv[c] = m > 0.0f ? __fdiv_rn(127.0f, m) : 0.0f;
+    if (tile == 0) job.vscale[bh * job.dpad + c] = __fdiv_rn(m, 127.0f);
+  }
+  __syncthreads();
+  int8_t* out = job.vq + blk * static_cast<int64_t>(job.dpad) * kPackTok;
+  // (channel, chunk) pairs; the four chunks of a channel are in 4
+  // consecutive lanes, and every wave that enters an iteration is full
+  // (dpad * 4 is a multiple of 128)
+  for (int e = threadIdx.x; e < job.dpad * 4; e += kThreads) {
+    const int c = e >> 2, q = e & 3, b = q >> 1, h = q & 1;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    int sum = 0;
+    if (c < job.d) {
+      const float inv = sinv[c];
+#pragma unroll
+      for (int sl = 0; sl < 16; ++sl) {
+        const int key = 32 * b + 8 * (sl >> 2) + 4 * h + (sl & 3);
+        int code = 0;
+        if (n0 + key < job.N) code = static_cast<int>(rintf(bf16_to_f32(vs[key * stride + c]) * inv));
+        sum += code;
+        w[sl >> 2] |= (static_cast<uint32_t>(code) & 0xffu) << (8 * (sl & 3));
+      }
+    }
+    const int pos = q ^ ((c >> 2) & 3);
+    *reinterpret_cast<uint4*>(out + c * kPackTok + pos * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    if (q == 0 && sum != 0) atomicAdd(job.vcsum + bh * job.dpad + c, sum);
+  }
+}
+
+// ---------------------------------------------------------------- vstat ---
+// Channel maxima of |v| over one 64-token tile (tokens past N count as 0).
+__device__ void vstat_block(const VstatJob& job, int64_t blk, unsigned char* smem) {
+  const int d = job.d, C = d / 8;
+  const int tiles = job.Npad / kPackTok;
+  const int64_t bh = blk / tiles;
+  const int tile = static_cast<int>(blk - bh * tiles), n0 = tile * kPackTok;
+  unsigned* smax = reinterpret_cast<unsigned*>(smem);  // float bits; |v| >= 0 orders like the bits
+  for (int c = threadIdx.x; c < job.dpad; c += kThreads) smax[c] = 0u;
+  __syncthreads();
+  const int rows = job.N - n0 < kPackTok ? job.N - n0 : kPackTok;
+  const int64_t b = bh / job.H, hh = bh - b * job.H;
+  const uint16_t* vbase = job.v + token_offset(job.vs, b, hh, n0);
+  uint4 vr[kMaxChunks];
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int g = threadIdx.x + i * kThreads;
+    vr[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (g < rows * C) {
+      const int tok = g / C, ch = g - tok * C;
+      vr[i] = *reinterpret_cast<const uint4*>(vbase + tok * job.vs.sn + ch * 8);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int g = threadIdx.x + i * kThreads;
+    if (g < rows * C) {
+      const int ch = g % C;
+      const uint32_t wv[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        atomicMax(smax + 8 * ch + 2 * k, __float_as_uint(fabsf(bf16_to_f32(static_cast<uint16_t>(wv[k] & 0xffffu)))));
+        atomicMax(smax + 8 * ch + 2 * k + 1, __float_as_uint(fabsf(bf16_to_f32(static_cast<uint16_t>(wv[k] >> 16)))));
+      }
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < job.dpad; c += kThreads) {
+    job.vpart[blk * job.dpad + c] = __uint_as_float(smax[c]);
+    if (tile == 0) job.vcsum[bh * job.dpad + c] = 0;
+  }
+}
+
 // ---------------------------------------------------------------- bias ----
 // One block = one row of the padded table: rows kBiasPadRows..kBiasPadRows +
 // 2gh-2 hold the table rows dy = 0..2gh-2; the kBiasPadRows rows on each side
@@ -222,7 +322,9 @@ __device__ void bias_block(const BiasJob& job, int64_t blk) {
     const int s = e / job.Lpad, v = e - s * job.Lpad;
     const int u = v + s;
     // Padding rows are -inf: the only (query, key) pairs that reach them
-    // involve a padded token, and a padded key must get probability 0.
+    // involve a padded token.  They keep the fused kernel's window reads
+    // inside the rows; that kernel masks padded keys itself, since a padded
+    // key seen from a query on grid row >= 1 falls on a real row.
     float val = inside ? 0.0f : -INFINITY;
     if (inside && u <= cols - 1) val = kLog2e * bf16_to_f32(trow[cols - 1 - u]);
     out[e] = val;
@@ -254,11 +356,16 @@ __global__ void __launch_bounds__(kThreads) prologue_kernel(PrologueArgs a) {
     return;
   }
   blk -= a.kv_blocks;
-  if (blk < a.bias_blocks) bias_block(a.bias, blk);
+  if (blk < a.bias_blocks) {
+    bias_block(a.bias, blk);
+    return;
+  }
+  blk -= a.bias_blocks;
+  if (blk < a.vstat_blocks) vstat_block(a.vstat, blk, smem);
 }
 
 int launch_prologue(const PrologueArgs& a, void* stream) {
-  const int64_t blocks = a.pack_blocks + a.kv_blocks + a.bias_blocks;
+  const int64_t blocks = a.pack_blocks + a.kv_blocks + a.bias_blocks + a.vstat_blocks;
   hipLaunchKernelGGL(prologue_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), a.lds,
                      static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());

@@ -180,6 +180,36 @@ ba_status ba_attention_fwd_dense_bias(const void* q, const void* k, const void* 
                                       void* o, const int64_t* strides,
                                       void* workspace, size_t ws_bytes, void* stream);
 
+/* Workspace bytes of ba_attention_fwd_int8pv: as ba_workspace_bytes, with
+ * int8 value-code tiles, per-tile channel maxima, channel scales and code
+ * column sums in place of the bf16 V^T copy.  0 for sizes that entry point
+ * rejects (also d > 128 or N > 65536). */
+size_t ba_workspace_bytes_int8pv(int64_t B, int64_t H, int64_t N, int d, int gh, int gw);
+
+/* ba_attention_fwd_int8pv -- the forward with the pages' hybrid 8-bit P.V
+ * ("Cuantizacion Hibrida": the attention coefficients, in [0, 1], take a
+ * static unsigned 8-bit quantization and the values a per-channel 8-bit
+ * one, with Q and K in 1 bit as in ba_attention_fwd):
+ *   code_ij = round-half-even(255 exp(S_ij - max_j S_ij))   in [0, 255]
+ *   s_c     = max_j |V_jc| / 127 per (b, h, channel c)
+ *   vq_jc   = round-half-even(V_jc * (127 / max_j |V_jc|))  in [-127, 127]
+ *   O_ic    = s_c * sum_j code_ij vq_jc / sum_j code_ij
+ * S as in ba_attention_fwd.  The products and sums of codes are exact
+ * (int32 on the int8 matrix cores); the coefficient codes come from a
+ * float32 exp2, so one may differ by one from a float64 evaluation where
+ * 255 exp(.) lies within rounding of a half-integer.
+ * Arguments, layouts and errors are those of ba_attention_fwd, with
+ * workspace >= ba_workspace_bytes_int8pv(B,H,N,d,gh,gw) bytes, and
+ * BA_ERR_UNSUPPORTED for d > 128 or N > 65536.  Three kernels are enqueued:
+ * per-tile channel maxima of |V| (with the bias rows), the K signs/scales
+ * with the value codes, then the fused kernel (a pass for the row maxima,
+ * then the 8-bit pass). */
+ba_status ba_attention_fwd_int8pv(const void* q, const void* k, const void* v,
+                                  const void* bias, int gh, int gw,
+                                  int64_t B, int64_t H, int64_t N, int d, float scale,
+                                  void* o, void* workspace, size_t ws_bytes,
+                                  void* stream);
+
 /* The two halves of ba_attention_fwd, for callers that time or schedule the
  * two kernels separately.
  *

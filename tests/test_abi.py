@@ -53,7 +53,7 @@ def _round(x, m):
     return (x + m - 1) // m * m
 
 
-def expected_workspace(B, H, N, d, gh=0, gw=0):
+def expected_workspace(B, H, N, d, gh=0, gw=0, int8pv=False):
     """Workspace sections as the header describes them: the K signs as fp4
     MFMA operands (32 bytes per 64 channels), the K scales, their maxima per
     64 tokens and V^T, per head
@@ -65,7 +65,11 @@ def expected_workspace(B, H, N, d, gh=0, gw=0):
     W = (d + 31) // 32
     dpad = 32 * W
     secs = [B * H * npad * ((W + 1) // 2) * 32, B * H * npad * 4, B * H * (npad // 64) * 4]
-    secs.append(B * H * dpad * npad * 2)
+    if int8pv:
+        # int8 value codes, per-tile channel maxima, channel scales, code column sums
+        secs += [B * H * dpad * npad, B * H * (npad // 64) * dpad * 4, B * H * dpad * 4, B * H * dpad * 4]
+    else:
+        secs.append(B * H * dpad * npad * 2)
     if gh and gw % 32 == 0:
         lpad = _round(2 * gw - 1 + 3, 4)
         while lpad % 64 != 16:
@@ -267,3 +271,30 @@ def test_dense_bias_validation(lib):
     # the workspace is the one without a table
     need = lib.ba_workspace_bytes(1, 2, 64, 64, 0, 0)
     assert fwd_dense(lib, ws_bytes=need - 1) == 5
+
+
+@pytest.mark.parametrize("shape", [(1, 3, 196, 64, 14, 14), (8, 16, 1024, 72, 32, 32), (2, 12, 4096, 64, 64, 64),
+                                   (1, 16, 16384, 128, 128, 128), (2, 2, 100, 40, 0, 0)])
+def test_workspace_bytes_int8pv(lib, shape):
+    assert lib.ba_workspace_bytes_int8pv(*shape) == expected_workspace(*shape, int8pv=True)
+
+
+def test_int8pv_validation(lib):
+    """The 8-bit P.V entry: d <= 128 and N <= 65536 (exact int32 sums),
+    otherwise the checks of ba_attention_fwd; nothing is launched."""
+    assert lib.ba_workspace_bytes_int8pv(1, 1, 64, 136, 0, 0) == 0
+    assert lib.ba_workspace_bytes_int8pv(1, 1, 65537, 64, 0, 0) == 0
+
+    def call(**kw):
+        a = dict(q=A, k=A + GB, v=A + 2 * GB, bias=None, gh=0, gw=0, B=1, H=2, N=64, d=64, scale=0.125,
+                 o=A + 3 * GB, ws=A + 4 * GB, ws_bytes=1 << 40)
+        a.update(kw)
+        return lib.ba_attention_fwd_int8pv(a["q"], a["k"], a["v"], a["bias"], a["gh"], a["gw"], a["B"], a["H"],
+                                           a["N"], a["d"], a["scale"], a["o"], a["ws"], a["ws_bytes"], None)
+    assert call(d=136) == 3
+    assert call(N=65537) == 3
+    assert call(q=None) == 1
+    assert call(o=A + 16) == 2
+    need = lib.ba_workspace_bytes_int8pv(1, 2, 64, 64, 0, 0)
+    assert need > lib.ba_workspace_bytes(1, 2, 64, 64, 0, 0) - 2 * 64 * 128 * 2
+    assert call(ws_bytes=need - 1) == 5

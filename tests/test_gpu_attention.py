@@ -46,6 +46,11 @@ def run(inp):
     (1, 1, 3, 32, 200),
     (1, 1, 2, 64, 256),
     (1, 1, 2, 128, 8),
+    # table rows with a ragged last tile (N % 64 == 32) and d % 32 == 0, where
+    # the row sums come from the vector ALU and padded keys must be masked
+    (1, 1, 3, 32, 64),
+    (1, 2, 3, 32, 128),
+    (2, 1, 5, 96, 32),
 ])
 def test_fwd_small_with_bias(B, H, gh, gw, d):
     announce("fwd bias", B, H, gh, gw, d)
@@ -78,6 +83,15 @@ def test_fwd_large_logits(scale):
     lazy-rescale threshold, so the rescale branch runs."""
     announce("fwd large logits", scale)
     inp = workloads.make_inputs(1, 2, 256, 64, seed=9, grid=(8, 32), q_scale=scale, k_scale=scale)
+    o = run(inp)
+    err = o_error(o, oracle_rows(inp), inp["v"])
+    assert err <= TOL, err
+
+
+def test_fwd_large_logits_ragged_rows():
+    """The exact path on table rows with a ragged last tile (N = 96)."""
+    announce("fwd large logits ragged rows")
+    inp = workloads.make_inputs(1, 2, 96, 64, seed=19, grid=(3, 32), q_scale=8.0, k_scale=8.0)
     o = run(inp)
     err = o_error(o, oracle_rows(inp), inp["v"])
     assert err <= TOL, err

@@ -1,0 +1,106 @@
+"""GPU parity of ba_attention_fwd_int8pv (the pages' hybrid 8-bit P.V) with
+the oracle's binary_attention_int8_pv_rows.
+
+Bar: max |O_gpu - O_oracle| <= 1e-2 * max |V|.  Derivation: the value codes
+are decided the same way on both sides (float32, one correctly rounded
+division, one product, one rounding) and every product and sum of codes is
+exact (int32); a coefficient code can differ by one where 255 * 2^(s - m)
+lies within float32 rounding of a half-integer, which moves O_i by at most
+2 max|V| / sum_j code_ij <= 2 max|V| / 255 (the row maximum is code 255);
+the bf16 output adds 2^-9 |O|.  In practice far fewer codes flip, and the
+measured error is printed with each case."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_cases import announce, np32, o_error, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+bq = pytest.importorskip("bit_qk_quantisation_amd")
+
+TOL = 1e-2
+
+
+def oracle_int8(inp, rows=None):
+    table = inp.get("table")
+    return oracle.binary_attention_int8_pv_rows(
+        np32(inp["q"]), np32(inp["k"]), np32(inp["v"]), None if table is None else np32(table),
+        inp["gh"], inp["gw"], rows=rows)["O"]
+
+
+def run(inp):
+    dev = to_dev(inp)
+    o = bq.attention_fwd_int8pv(dev["q"], dev["k"], dev["v"], dev["table"], inp["gh"], inp["gw"])
+    torch.cuda.synchronize()
+    return o
+
+
+@pytest.mark.parametrize("B,H,gh,gw,d", [
+    (1, 2, 1, 1, 64),      # N = 1
+    (1, 1, 1, 2, 32),
+    (1, 2, 7, 9, 64),      # table mode, N = 63 (ragged tile)
+    (2, 1, 8, 8, 64),
+    (1, 3, 14, 14, 64),    # the tiny ViT grid
+    (1, 2, 4, 32, 64),     # table rows (gw % 32 == 0)
+    (1, 1, 3, 32, 72),     # d = 72: value codes padded to 96 channels
+    (1, 2, 6, 32, 96),
+    (1, 1, 5, 64, 128),
+    (1, 1, 2, 96, 40),
+])
+def test_int8_small_with_bias(B, H, gh, gw, d):
+    announce("int8 bias", B, H, gh, gw, d)
+    inp = workloads.make_inputs(B, H, gh * gw, d, seed=3000 + gh * gw + d, grid=(gh, gw))
+    o = run(inp)
+    err = o_error(o, oracle_int8(inp), inp["v"])
+    print("max err / max|V| =", err)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 1, 64, 64), (2, 1, 63, 32), (1, 2, 300, 16), (1, 1, 129, 128)])
+def test_int8_small_no_bias(B, H, N, d):
+    announce("int8 no bias", B, H, N, d)
+    inp = workloads.make_inputs(B, H, N, d, seed=3100 + N + d, bias=False)
+    o = run(inp)
+    err = o_error(o, oracle_int8(inp), inp["v"])
+    print("max err / max|V| =", err)
+    assert err <= TOL, err
+
+
+def test_int8_grid_values_and_zero_channel():
+    """Q = 0 and no bias: every code is 255, so O is the exact column mean of
+    the values' codes times their scales; values on their code grid make that
+    the column mean of V, up to the bf16 output.  An all-zero channel has
+    scale 0 and gives exactly 0."""
+    announce("int8 grid values")
+    B, H, N, d = 2, 2, 200, 64
+    rng = np.random.default_rng(3201)
+    n = rng.integers(-127, 128, size=(B, H, N, d))
+    n[:, :, 0, :] = 127
+    v = torch.from_numpy((n * 2.0 ** -6).astype(np.float32)).to(torch.bfloat16)
+    v[..., 5] = 0.0
+    inp = workloads.make_inputs(B, H, N, d, seed=3202, bias=False)
+    inp["q"] = torch.zeros_like(inp["q"])
+    inp["v"] = v
+    o = run(inp).float().cpu().numpy()
+    want = np32(v).astype(np.float64).mean(axis=2, keepdims=True)
+    assert np.allclose(o, np.broadcast_to(want, o.shape), rtol=2 ** -8, atol=1e-6)
+    assert (o[..., 5] == 0).all()
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_int8_workloads(name):
+    """The workload shapes at full size, sampled rows against the oracle (the
+    value codes use all N keys of each head, as in the full problem)."""
+    w = workloads.WORKLOADS[name]
+    announce("int8 workload", name)
+    inp = workloads.workload_inputs(w)
+    o = run(inp)
+    assert torch.isfinite(o.float()).all()
+    rows = None if w.N * w.B * w.H <= 600 else sample_rows(w.N, 32, w.seed + 50)
+    err = o_error(o, oracle_int8(inp, rows), inp["v"], rows)
+    print(name, "max err / max|V| =", err)
+    assert err <= TOL, (name, err)
