@@ -6,7 +6,9 @@ nothing from it.
 """
 
 from .dense_fp64 import (  # noqa: F401
+    binarize_backward,
     binary_attention,
+    binary_attention_backward,
     binary_attention_dense_bias_rows,
     binary_attention_int8_pv_rows,
     binary_attention_rows,

@@ -331,3 +331,68 @@ def binary_attention_int8_pv_rows(q, k, v, table=None, gh: int = 0, gw: int = 0,
     if keep:
         out.update(S=sc["S"], Pq=pq, Vq=vq["codes"], v_scale=vq["scale"])
     return out
+
+
+def binarize_backward(x, g) -> np.ndarray:
+    """Gradient through the scaled binary representation x~ = alpha(x) sign(x)
+    of es page, section 2, item "Representaciones Binarias Escaladas".
+
+    The pages train with quantization-aware training and self-distillation
+    (es section 2, item "Entrenamiento y Optimizacion"; ko section 2 (c))
+    but give no gradient for sign.  Reading: alpha = mean |x| takes its exact
+    derivative sign(x_c) / d, and sign takes the clipped straight-through
+    estimator, derivative 1 where |x| <= 1 and 0 elsewhere.  So for the
+    gradient g of x~ (one token, last axis = channels):
+        dx = sign(x) * <sign(x), g> / d + alpha * 1{|x| <= 1} * g."""
+    xf = _f64(x)
+    gf = _f64(g)
+    d = xf.shape[-1]
+    s = sign_pm1(xf)
+    a = token_scale(xf)[..., None]
+    return s * (s * gf).sum(axis=-1, keepdims=True) / d + a * (np.abs(xf) <= 1.0) * gf
+
+
+def binary_attention_backward(q, k, v, do, table=None, gh: int = 0, gw: int = 0,
+                              scale=None) -> dict:
+    """Gradients of the BinaryAttention forward for the output gradient dO
+    (the loss L with dL/dO = dO), in float64.
+
+    With q~ = alpha_q sign(q), k~ = alpha_k sign(k) and
+    S = scale q~ k~^T + b, P = softmax_rows(S), O = P V:
+        dV = P^T dO
+        dS = P * (dO V^T - rowsum(dO * O))
+        dq~ = scale dS k~,   dk~ = scale dS^T q~
+        dq, dk = binarize_backward(q, dq~), binarize_backward(k, dk~)
+        dtable[h, dy, dx] = sum over b and all (i, j) at grid offset
+                            (yi - yj, xi - xj) = (dy - gh + 1, dx - gw + 1) of dS_ij
+    (the table is shared over the batch).  Returns dq, dk, dv [B,H,N,d],
+    dtable [H, 2gh-1, 2gw-1] (or None), and O."""
+    qf, kf, vf, gf = _f64(q), _f64(k), _f64(v), _f64(do)
+    b, h, n, d = qf.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    qt = token_scale(qf)[..., None] * sign_pm1(qf)
+    kt = token_scale(kf)[..., None] * sign_pm1(kf)
+    s = float(scale) * np.matmul(qt, np.swapaxes(kt, -1, -2))
+    if table is not None:
+        s = s + rel_pos_bias(table, gh, gw)[None]
+    p = softmax_rows(s)
+    o = np.matmul(p, vf)
+    dv = np.matmul(np.swapaxes(p, -1, -2), gf)
+    delta = (gf * o).sum(axis=-1, keepdims=True)
+    ds = p * (np.matmul(gf, np.swapaxes(vf, -1, -2)) - delta)
+    dqt = float(scale) * np.matmul(ds, kt)
+    dkt = float(scale) * np.matmul(np.swapaxes(ds, -1, -2), qt)
+    dtable = None
+    if table is not None:
+        t = _f64(table)
+        dtable = np.zeros_like(t)
+        idx = np.arange(n)
+        y, x = idx // gw, idx % gw
+        dy = (y[:, None] - y[None, :] + gh - 1).ravel()
+        dx = (x[:, None] - x[None, :] + gw - 1).ravel()
+        dsum = ds.sum(axis=0)  # over the batch
+        for hh in range(h):
+            np.add.at(dtable[hh], (dy, dx), dsum[hh].ravel())
+    return {"dq": binarize_backward(qf, dqt), "dk": binarize_backward(kf, dkt), "dv": dv,
+            "dtable": dtable, "O": o}

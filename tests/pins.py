@@ -477,6 +477,92 @@ def int8_error_bound(ob):
         assert (np.abs(r8["O"] - ref) <= bound).all(), float((np.abs(r8["O"] - ref) - bound).max())
 
 
+def _loss_fd(fn, x, dof, eps=1e-6):
+    """Central differences of L = sum(dO * O(x)) for every entry of x."""
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        old = x[i]
+        x[i] = old + eps
+        lp = float((dof * fn(x)).sum())
+        x[i] = old - eps
+        lm = float((dof * fn(x)).sum())
+        x[i] = old
+        g[i] = (lp - lm) / (2 * eps)
+    return g
+
+
+def backward_values_and_table(ob):
+    """dV and the table gradient are exact derivatives (the forward is smooth
+    in V and in the table): central differences of L = sum(dO * O) agree,
+    and the invariants sum_j dV_j = sum_i dO_i and sum(dtable) = 0 (each
+    row of dS sums to 0) hold."""
+    rng = _rng(28)
+    b, h, gh, gw, d = 2, 2, 2, 3, 5
+    n = gh * gw
+    q = _bf16_values(rng, (b, h, n, d))
+    k = _bf16_values(rng, (b, h, n, d))
+    v = _bf16_values(rng, (b, h, n, d))
+    t = _bf16_values(rng, (h, 2 * gh - 1, 2 * gw - 1), 0.7)
+    do = rng.normal(size=(b, h, n, d))
+    g = ob.binary_attention_backward(q, k, v, do, t, gh, gw)
+    fd_v = _loss_fd(lambda x: ob.binary_attention(q, k, x, t, gh, gw)["O"], v.copy(), do)
+    assert np.allclose(g["dv"], fd_v, rtol=0, atol=1e-7), np.abs(g["dv"] - fd_v).max()
+    fd_t = _loss_fd(lambda x: ob.binary_attention(q, k, v, x, gh, gw)["O"], t.copy(), do)
+    assert np.allclose(g["dtable"], fd_t, rtol=0, atol=1e-7), np.abs(g["dtable"] - fd_t).max()
+    assert np.allclose(g["dv"].sum(axis=2), do.sum(axis=2), rtol=0, atol=1e-12)
+    assert abs(g["dtable"].sum()) < 1e-12
+
+
+def backward_queries_keys_alpha_path(ob):
+    """With every |x| > 1 the straight-through term vanishes and sign is
+    constant near x, so dq and dk are the exact derivatives (through alpha
+    = mean |x| only): central differences of L agree."""
+    rng = _rng(29)
+    b, h, gh, gw, d = 1, 2, 2, 3, 6
+    n = gh * gw
+
+    def far(shape):
+        return np.where(rng.random(shape) < 0.5, -1.0, 1.0) * (1.25 + np.abs(rng.normal(size=shape)))
+    q, k = far((b, h, n, d)), far((b, h, n, d))
+    v = _bf16_values(rng, (b, h, n, d))
+    t = _bf16_values(rng, (h, 2 * gh - 1, 2 * gw - 1), 0.7)
+    do = rng.normal(size=(b, h, n, d))
+    g = ob.binary_attention_backward(q, k, v, do, t, gh, gw)
+    fd_q = _loss_fd(lambda x: ob.binary_attention(x, k, v, t, gh, gw)["O"], q.copy(), do)
+    fd_k = _loss_fd(lambda x: ob.binary_attention(q, x, v, t, gh, gw)["O"], k.copy(), do)
+    assert np.allclose(g["dq"], fd_q, rtol=0, atol=1e-7), np.abs(g["dq"] - fd_q).max()
+    assert np.allclose(g["dk"], fd_k, rtol=0, atol=1e-7), np.abs(g["dk"] - fd_k).max()
+
+
+def binarize_backward_surrogate(ob):
+    """The reading of the sign gradient, checked on its own: at x0 the
+    gradient equals the transposed Jacobian of the surrogate
+    F(x) = alpha(x) sign(x0) + alpha(x0) (clip(x, -1, 1) - clip(x0, -1, 1)),
+    which has the same value as alpha(x) sign(x) at x0 and the clipped
+    straight-through derivative; the Jacobian comes from central
+    differences."""
+    rng = _rng(30)
+    d = 9
+    for _ in range(4):
+        x0 = rng.normal(size=d) * 1.2
+        x0[np.abs(np.abs(x0) - 1.0) < 1e-3] += 0.01  # stay off the clip corners
+        g = rng.normal(size=d)
+        s0 = np.where(x0 < 0, -1.0, 1.0)
+        a0 = np.abs(x0).mean()
+
+        def f(x):
+            return np.abs(x).mean() * s0 + a0 * (np.clip(x, -1, 1) - np.clip(x0, -1, 1))
+        jac = np.zeros((d, d))
+        for c in range(d):
+            e = np.zeros(d)
+            e[c] = 1e-6
+            jac[:, c] = (f(x0 + e) - f(x0 - e)) / 2e-6
+        got = ob.binarize_backward(x0[None], g[None])[0]
+        assert np.allclose(got, jac.T @ g, rtol=0, atol=1e-8), np.abs(got - jac.T @ g).max()
+
+
 ALL_PINS = [
     golden_hand_example,
     bits_definition,
@@ -497,4 +583,7 @@ ALL_PINS = [
     int8_quantizers,
     int8_closed_forms,
     int8_error_bound,
+    backward_values_and_table,
+    backward_queries_keys_alpha_path,
+    binarize_backward_surrogate,
 ]

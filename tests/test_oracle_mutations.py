@@ -186,6 +186,54 @@ def _int8_factory(**kw):
     return f
 
 
+
+def _bwd_factory(**kw):
+    """A copy of binary_attention_backward with one planted mistake."""
+    def bwd(q, k, v, do, table=None, gh=0, gw=0, scale=None):
+        qf, kf, vf, gf = ob._f64(q), ob._f64(k), ob._f64(v), ob._f64(do)
+        b, h, n, d = qf.shape
+        sc = 1.0 / math.sqrt(d) if scale is None else scale
+        qt = ob.token_scale(qf)[..., None] * ob.sign_pm1(qf)
+        kt = ob.token_scale(kf)[..., None] * ob.sign_pm1(kf)
+        s = sc * np.matmul(qt, np.swapaxes(kt, -1, -2))
+        if table is not None:
+            s = s + ob.rel_pos_bias(table, gh, gw)[None]
+        p = ob.softmax_rows(s)
+        o = np.matmul(p, vf)
+        dv = np.matmul(p if kw.get("dv_untransposed") else np.swapaxes(p, -1, -2), gf)
+        delta = 0.0 if kw.get("no_delta") else (gf * o).sum(axis=-1, keepdims=True)
+        ds = p * (np.matmul(gf, np.swapaxes(vf, -1, -2)) - delta)
+        dqt = sc * np.matmul(ds, kt)
+        dkt = sc * np.matmul(ds if kw.get("dk_untransposed") else np.swapaxes(ds, -1, -2), qt)
+        dtable = None
+        if table is not None:
+            t = ob._f64(table)
+            dtable = np.zeros_like(t)
+            idx = np.arange(n)
+            y, x = idx // gw, idx % gw
+            sgn = -1 if kw.get("dtable_mirrored") else 1
+            dy = (sgn * (y[:, None] - y[None, :]) + gh - 1).ravel()
+            dx = (sgn * (x[:, None] - x[None, :]) + gw - 1).ravel()
+            dsum = ds.sum(axis=0)
+            for hh in range(h):
+                np.add.at(dtable[hh], (dy, dx), dsum[hh].ravel())
+        return {"dq": ob.binarize_backward(qf, dqt), "dk": ob.binarize_backward(kf, dkt), "dv": dv,
+                "dtable": dtable, "O": o}
+    return bwd
+
+
+def _binb_unclipped(x, g):
+    xf, gf = ob._f64(x), ob._f64(g)
+    d = xf.shape[-1]
+    s = ob.sign_pm1(xf)
+    return s * (s * gf).sum(axis=-1, keepdims=True) / d + ob.token_scale(xf)[..., None] * gf
+
+
+def _binb_no_alpha_path(x, g):
+    xf, gf = ob._f64(x), ob._f64(g)
+    return ob.token_scale(xf)[..., None] * (np.abs(xf) <= 1.0) * gf
+
+
 MUTATIONS = {
     "sign_zero_is_negative": ("sign_pm1", _sign_zero_negative),
     "sign_from_signbit": ("sign_pm1", _sign_from_signbit),
@@ -215,6 +263,12 @@ MUTATIONS = {
     "int8_p_scale_127": ("quantize_probs_u8", _qp_127),
     "int8_row_sum_unquantized": ("binary_attention_int8_pv_rows", _int8_factory(den_float=True)),
     "int8_value_scale_dropped": ("binary_attention_int8_pv_rows", _int8_factory(no_scale=True)),
+    "bwd_dv_untransposed": ("binary_attention_backward", _bwd_factory(dv_untransposed=True)),
+    "bwd_no_delta": ("binary_attention_backward", _bwd_factory(no_delta=True)),
+    "bwd_dk_untransposed": ("binary_attention_backward", _bwd_factory(dk_untransposed=True)),
+    "bwd_dtable_mirrored": ("binary_attention_backward", _bwd_factory(dtable_mirrored=True)),
+    "bwd_ste_unclipped": ("binarize_backward", _binb_unclipped),
+    "bwd_alpha_path_dropped": ("binarize_backward", _binb_no_alpha_path),
 }
 
 
