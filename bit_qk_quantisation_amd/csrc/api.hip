@@ -425,7 +425,7 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   p = ba::PrologueArgs{};
   p.kv = ba::KvJob{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), const_cast<uint32_t*>(f.kop),
                    const_cast<float*>(f.alpha_k), const_cast<float*>(f.kmax_blk), const_cast<uint16_t*>(f.vt),
-                   nullptr, nullptr, nullptr, nullptr,
+                   nullptr, nullptr, nullptr, nullptr, nullptr,
                    vs[1], vs[2], BH, static_cast<int>(H), f.N, f.Npad, d, f.W, (f.W + 1) / 2, f.dpad};
   p.kv_blocks = BH * (L.Npad / ba::kPackTok);
   p.lds = ba::prologue_lds(d, true);

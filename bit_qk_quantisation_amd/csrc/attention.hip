@@ -87,6 +87,7 @@ struct Ctx {
   int bh, head, q0, qi;
   int64_t tokbase;
   float aq;            // alpha_q * scale * log2e
+  float alpha;         // alpha_q itself (the backward's row tokens)
   v4i qop[NCH];        // this lane's query operand (fp4 +/-1)
   // LDS byte offsets inside a TileBuf, per lane
   // off_akb: the key scale this lane holds for the row broadcasts;
@@ -161,8 +162,9 @@ __device__ __forceinline__ T lds_load(const void* base, int byte_off) {
 // maximum pass), the bf16 V^T tile, or the int8 value-code tile.
 enum VCopy { kVNone = 0, kVBf16 = 1, kVInt8 = 2 };
 
-template <int NCH, int CB, int BIAS, int VM = kVBf16>
-__device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TileBuf<NCH, CB, BIAS>& tb, int t, const KeyPos& kp) {
+// TB is TileBuf<NCH, CB, BIAS> or the backward's tile buffer (same members).
+template <int NCH, int CB, int BIAS, int VM = kVBf16, class TB = TileBuf<NCH, CB, BIAS>>
+__device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TB& tb, int t, const KeyPos& kp) {
   const FwdArgs& a = *c.a;
   constexpr int kKBytes = NCH * kBN * 2 * 16;
   char* kdst = reinterpret_cast<char*>(&tb.k[0]);
@@ -235,8 +237,8 @@ __device__ __forceinline__ int window_offset(const Ctx<NCH>& c, const KeyPos& kp
 
 // Logits of one 32-key block in base 2:
 //   D * alpha_k * (alpha_q scale log2e) + log2e b
-template <bool MASK, int NCH, int CB, int BIAS>
-__device__ __forceinline__ void block_logits(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& tb, const KeyPos& kp,
+template <bool MASK, int NCH, int CB, int BIAS, class TB = TileBuf<NCH, CB, BIAS>>
+__device__ __forceinline__ void block_logits(const Ctx<NCH>& c, const TB& tb, const KeyPos& kp,
                                              int blk, const v16f& s, float (&sc)[16]) {
   const FwdArgs& a = *c.a;
   int woff = 0;
@@ -321,9 +323,10 @@ __device__ __forceinline__ void block_rescale(float (&sc)[16], Acc<CB, XONES>& a
 // FAST: offset-free exp2, no row max.  MASK: keys >= N get probability 0.
 template <bool FAST, bool MASK, int NCH, int CB, bool XONES, int BIAS>
 __device__ __forceinline__ void compute_tile(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& tb, const KeyPos& kp,
-                                             Acc<CB, XONES>& acc, float& mrow) {
+                                             Acc<CB, XONES>& acc, float& mrow, int nblk) {
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
+    if (blk >= nblk) break;  // uniform: the padded block of a ragged table-row tile
     v16f s = v16f{};
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch)
@@ -468,7 +471,12 @@ __device__ __forceinline__ void fast_step(const Ctx<NCH>& c, const TileBuf<NCH, 
   const bool more = t + 1 < nkt;
   const KeyPos kn = next_keys(kp, a.gw);
   if (more) copy_tile_async<NCH, CB, BIAS>(c, nxt, t + 1, kn);
-  if (kp.k0 + kBN <= a.N) {  // a full tile; the ragged last one is masked
+  if (BIAS == kBiasRows) {
+    // N % 32 == 0 here: a ragged last tile is one real block and one block
+    // of padded keys, which is skipped (see pass_step)
+    pipelined_block<false, !FIRST, NCH, CB, XONES, BIAS>(c, cur, kp, 0, pp, acc);
+    if (kp.k0 + 32 < a.N) pipelined_block<false, true, NCH, CB, XONES, BIAS>(c, cur, kp, 1, pp, acc);
+  } else if (kp.k0 + kBN <= a.N) {  // a full tile; the ragged last one is masked
     pipelined_block<false, !FIRST, NCH, CB, XONES, BIAS>(c, cur, kp, 0, pp, acc);
     pipelined_block<false, true, NCH, CB, XONES, BIAS>(c, cur, kp, 1, pp, acc);
   } else {
@@ -522,23 +530,28 @@ __device__ __forceinline__ void pass_step(const Ctx<NCH>& c, const TileBuf<NCH, 
   const bool more = t + 1 < nkt;
   const KeyPos kn = next_keys(kp, a.gw);
   if (more) copy_tile_async<NCH, CB, BIAS>(c, nxt, t + 1, kn);
-  // Keys past N are masked on the ragged last tile, in every bias mode: the
+  // Keys past N must get probability 0 on the ragged last tile.  The
   // padding rows of the table-row bias keep the window reads inside the
-  // rows, but a padded key (grid row >= gh) seen from a query on grid row
-  // >= 1 falls on a real table row.
-  if (kp.k0 + kBN <= a.N)
-    compute_tile<FAST, false, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow);
+  // rows but do not cover every padded key (one on grid row >= gh, seen from
+  // a query on grid row >= 1, falls on a real table row).  Table rows have
+  // N % 32 == 0, so there the ragged tile is a real block and a block of
+  // padded keys, which is skipped; the other modes mask key by key.
+  if (BIAS == kBiasRows)
+    compute_tile<FAST, false, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow, kp.k0 + 32 < a.N ? 2 : 1);
+  else if (kp.k0 + kBN <= a.N)
+    compute_tile<FAST, false, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow, 2);
   else
-    compute_tile<FAST, true, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow);
+    compute_tile<FAST, true, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow, 2);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   kp = kn;
 }
 
 // One pass over all keys; O^T (and the row sums) accumulate in acc.
+// Returns the row maximum (log2 units) the sums are taken against.
 template <bool FAST, int NCH, int CB, bool XONES, int BIAS>
-__device__ __forceinline__ void run_pass(const Ctx<NCH>& c, TileBuf<NCH, CB, BIAS>& tb0, TileBuf<NCH, CB, BIAS>& tb1,
-                                         Acc<CB, XONES>& acc) {
+__device__ __forceinline__ float run_pass(const Ctx<NCH>& c, TileBuf<NCH, CB, BIAS>& tb0, TileBuf<NCH, CB, BIAS>& tb1,
+                                          Acc<CB, XONES>& acc) {
   const FwdArgs& a = *c.a;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc.o[cb] = v16f{};
@@ -559,6 +572,7 @@ __device__ __forceinline__ void run_pass(const Ctx<NCH>& c, TileBuf<NCH, CB, BIA
     if (t + 1 < nkt) pass_step<FAST, NCH, CB, XONES, BIAS>(c, tb1, tb0, t + 1, nkt, kp, acc, mrow);
   }
   if (XONES) acc.rs[0] = sum_halves(acc.rs[0] + acc.rs[1]);
+  return mrow;
 }
 
 // Everything a workgroup sets up before its key loop: its (b, h) and
@@ -625,6 +639,7 @@ __device__ __forceinline__ float workgroup_setup(Ctx<NCH>& c, const FwdArgs& a, 
   }
   const float alpha_q = sum_halves(qpart) / static_cast<float>(a.d);
   c.aq = alpha_q * a.qscale;
+  c.alpha = alpha_q;
 
   // ---- per-lane LDS offsets ------------------------------------------------
   c.off_k = (c.li * 2 + c.lh) * 16;
@@ -700,7 +715,7 @@ __device__ __forceinline__ float workgroup_setup(Ctx<NCH>& c, const FwdArgs& a, 
     const int n = (2 * a.gh - 1) * (2 * a.gw - 1);
     const uint16_t* t = a.table + static_cast<int64_t>(c.head) * n;
     for (int e = c.tid; e < n; e += kThreads) {
-      const float v = kLog2e * bf16_to_f32(t[e]);
+      const float v = kLog2e * bf16_to_f32(t[a.table_flip ? n - 1 - e : e]);  // flip: both axes
       c.table[e] = v;
       bm = fmaxf(bm, fabsf(v));
     }
@@ -731,15 +746,16 @@ attn_fwd_kernel(FwdArgs a) {
   const float M = workgroup_setup<NCH, CB, BIAS>(c, a, red, s_table);
 
   Acc<CB, XONES> acc;
+  float mrow = 0.0f;  // the offset the row sums are taken against (log2 units)
   if constexpr (BIAS == kBiasDense) {
     // no bound on a dense bias short of reading all of it: exact softmax
     (void)M;
-    run_pass<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
+    mrow = run_pass<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
   } else {
     if (M <= kFastMaxLogit)  // false for NaN as well
       run_fast_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
     else
-      run_pass<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
+      mrow = run_pass<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
   }
 
   // ---- epilogue: O = O^T / l, bf16, one query per lane --------------------
@@ -755,6 +771,9 @@ attn_fwd_kernel(FwdArgs a) {
     lsum = b1 == 1 ? last[4] : (b1 == 2 ? last[8] : last[12]);
   }
   const float inv = 1.0f / lsum;
+  // log2 of the softmax denominator, kept for the backward pass (0 for the
+  // padding rows, which the backward reads as masked columns)
+  if (a.lse && c.lh == 0) a.lse[c.tokbase + c.qi] = c.qi < a.N ? mrow + log2f(lsum) : 0.0f;
   if (c.qi < a.N) {
     uint16_t* orow = a.o + token_offset(a.os, c.bh / a.H, c.head, c.qi);
 #pragma unroll
@@ -807,9 +826,10 @@ __device__ __forceinline__ void pin_uniform_i(v16i& x) {
 // codes, and the product with the value codes.
 template <bool MAIN, bool MASK, int NCH, int CB, int BIAS>
 __device__ __forceinline__ void int8_tile(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& tb, const KeyPos& kp,
-                                          float& mrow, float off, Acc8<CB>& acc, uint32_t& rsum) {
+                                          float& mrow, float off, Acc8<CB>& acc, uint32_t& rsum, int nblk) {
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
+    if (blk >= nblk) break;  // uniform: the padded block of a ragged table-row tile
     v16f s = v16f{};
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch)
@@ -846,10 +866,12 @@ __device__ __forceinline__ void int8_step(const Ctx<NCH>& c, const TileBuf<NCH, 
   const FwdArgs& a = *c.a;
   const KeyPos kn = next_keys(kp, a.gw);
   if (t + 1 < nkt) copy_tile_async<NCH, CB, BIAS, MAIN ? kVInt8 : kVNone>(c, nxt, t + 1, kn);
-  if (kp.k0 + kBN <= a.N)
-    int8_tile<MAIN, false, NCH, CB, BIAS>(c, cur, kp, mrow, off, acc, rsum);
+  if (BIAS == kBiasRows)  // as in pass_step
+    int8_tile<MAIN, false, NCH, CB, BIAS>(c, cur, kp, mrow, off, acc, rsum, kp.k0 + 32 < a.N ? 2 : 1);
+  else if (kp.k0 + kBN <= a.N)
+    int8_tile<MAIN, false, NCH, CB, BIAS>(c, cur, kp, mrow, off, acc, rsum, 2);
   else
-    int8_tile<MAIN, true, NCH, CB, BIAS>(c, cur, kp, mrow, off, acc, rsum);
+    int8_tile<MAIN, true, NCH, CB, BIAS>(c, cur, kp, mrow, off, acc, rsum, 2);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   kp = kn;
@@ -932,6 +954,377 @@ attn_fwd_int8_kernel(FwdArgs a) {
           *reinterpret_cast<uint2*>(orow + c0) = w;
         }
       }
+  }
+}
+
+// ================================================================ backward ==
+// Gradients of the forward for an output gradient dO, with the reading of
+// the sign gradient (alpha = mean |x| differentiated exactly, sign through
+// the clipped straight-through estimator).  With P = softmax(S), rebuilt
+// from the forward's log2-sum-exp2, and delta_i = <dO_i, O_i>:
+//   dP_ij = <dO_i, V_j>,   dS_ij = P_ij (dP_ij - delta_i),
+//   dq~_i = scale sum_j dS_ij alpha_k,j sign(k_j),
+//   dk~_j = scale sum_i dS_ij alpha_q,i sign(q_i),   dV_j = sum_i P_ij dO_i,
+//   dx = sign(x) <sign(x), dx~> / d + alpha_x 1{|x| <= 1} dx~  (x = q, k).
+// One kernel, two roles.  kRoleQ: a lane holds a query, the columns are the
+// keys (the forward's layout).  kRoleKV: a lane holds a key, the columns are
+// the queries; with queries and keys exchanged the bias is the same
+// relative-position form with the table flipped in both axes, so the
+// forward's setup, tile copies and logits serve both.  Per 32-column block:
+// S on the fp4 unit as in the forward; dP (rows = columns, one row token
+// per lane, like S) on bf16 MFMA from a natural [64][d] tile of V or dO and
+// the lane's own dO or V row; then the products that sum over the columns,
+// on bf16 MFMA with the column tiles transposed as the forward's V^T: the
+// +/-1 signs of K (kRoleQ), dO^T and the +/-1 signs of Q (kRoleKV).
+template <int ROLE, int NCH, int CB, int BIAS>
+struct BwdTileBuf {
+  v4i k[NCH * kBN * 2];                         // column fp4 operands
+  float ak[kBN];                                 // column scales
+  int gk[BiasSizes<BIAS>::kGk];                  // grid offsets (table mode)
+  float cl[kBN];                                 // kRoleKV: columns' log2-sum-exp2
+  float cd[kBN];                                 // kRoleKV: columns' delta
+  uint16_t y[kBN * 32 * CB];                     // natural tile [64][dpad]
+  uint16_t vt[32 * CB * kBN];                    // K signs (kRoleQ) / dO^T (kRoleKV)
+  uint16_t vt2[ROLE == kRoleKV ? 32 * CB * kBN : 8];  // Q signs (kRoleKV)
+  float win[BiasSizes<BIAS>::kWin];              // bias window (table-row mode)
+};
+
+// Buffer resources of the backward's own column copies.
+struct BwdCtx {
+  rsrc_t zrs, z2rs, yrs, lrs, drs;
+};
+
+// 16-byte chunk position of chunk `ch` of row `row` in the natural tile
+// (C = 4 CB chunks per row): the XOR spreads the 16 rows that one
+// quarter-wave reads over 16 different bank groups.
+template <int CB>
+__device__ __forceinline__ int ychunk(int row, int ch) {
+  constexpr int C = 4 * CB;
+  constexpr int sh = CB == 1 ? 2 : (CB == 2 ? 1 : 0);
+  return ch ^ ((row >> sh) & (C - 1));
+}
+
+template <int ROLE, int NCH, int CB, int BIAS>
+__device__ __forceinline__ void bwd_copy(const Ctx<NCH>& c, const BwdCtx& bc, BwdTileBuf<ROLE, NCH, CB, BIAS>& tb,
+                                         int t, const KeyPos& kp) {
+  copy_tile_async<NCH, CB, BIAS, kVNone>(c, tb, t, kp);
+  constexpr int kTBytes = 32 * CB * kBN * 2;
+  const uint32_t loff = static_cast<uint32_t>(c.wave * 1024 + c.lane * 16);
+#pragma unroll
+  for (int j = 0; j < kTBytes / 4096; ++j) {
+    dma16(bc.zrs, reinterpret_cast<char*>(&tb.vt[0]) + (c.wave + 4 * j) * 1024, loff,
+          static_cast<uint32_t>(t * kTBytes + j * 4096));
+    if (ROLE == kRoleKV)
+      dma16(bc.z2rs, reinterpret_cast<char*>(&tb.vt2[0]) + (c.wave + 4 * j) * 1024, loff,
+            static_cast<uint32_t>(t * kTBytes + j * 4096));
+  }
+  if (ROLE == kRoleKV) {
+    if (c.wave == 1) dma4(bc.lrs, &tb.cl[0], static_cast<uint32_t>(c.lane * 4), static_cast<uint32_t>(kp.k0 * 4));
+    if (c.wave == 2) dma4(bc.drs, &tb.cd[0], static_cast<uint32_t>(c.lane * 4), static_cast<uint32_t>(kp.k0 * 4));
+  }
+  // natural tile: rows k0 .. k0 + 63 of [N][d], 4 CB pieces of 1 KiB; every
+  // offset is in the per-lane part, so rows past N fall outside the range
+  // and read 0
+  constexpr int C = 4 * CB, lgC = CB == 1 ? 2 : (CB == 2 ? 3 : 4);
+  const int d = c.a->d;
+#pragma unroll
+  for (int j = 0; j < CB; ++j) {
+    const int m = c.wave + 4 * j;
+    const int row = (64 * m + c.lane) >> lgC, pos = c.lane & (C - 1);
+    const int ch = ychunk<CB>(row, pos);  // the XOR is its own inverse
+    const uint32_t voff = static_cast<uint32_t>(((kp.k0 + row) * d + ch * 8) * 2);
+    dma16(bc.yrs, reinterpret_cast<char*>(&tb.y[0]) + m * 1024, voff, 0u);
+  }
+}
+
+template <int ROLE, int CB>
+struct BwdAcc {
+  v16f a1[CB];                         // dq~ (kRoleQ) or dk~ (kRoleKV), O^T-like layout
+  v16f a2[ROLE == kRoleKV ? CB : 1];   // dv (kRoleKV)
+};
+
+template <int ROLE, bool MASK, int NCH, int CB, int BIAS>
+__device__ __forceinline__ void bwd_tile(const Ctx<NCH>& c, const BwdTileBuf<ROLE, NCH, CB, BIAS>& tb,
+                                         const KeyPos& kp, const v8bf (&xop)[2 * CB], float lrow, float drow,
+                                         BwdAcc<ROLE, CB>& acc, int nblk) {
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    if (blk >= nblk) break;  // uniform: the padded block of a ragged table-row tile
+    v16f s = v16f{};
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+      s = mfma_signs_32x32x64(lds_load<v4i>(tb.k, c.off_k + ch * 2048 + blk * 1024), c.qop[ch], s);
+    float sc[16];
+    block_logits<MASK, NCH, CB, BIAS>(c, tb, kp, blk, s, sc);
+    // dP: rows = the block's columns, one row token per lane
+    v16f dp = v16f{};
+    const int yrow = blk * 32 + c.li;
+#pragma unroll
+    for (int t = 0; t < 2 * CB; ++t)
+      dp = mfma_bf16_32x32x16(lds_load<v8bf>(tb.y, (yrow * 4 * CB + ychunk<CB>(yrow, 2 * t + c.lh)) * 16), xop[t], dp);
+    const float akv = lds_load<float>(tb.ak, c.off_akb + blk * 128);
+    float clv = 0.0f, cdv = 0.0f;
+    if (ROLE == kRoleKV) {
+      clv = lds_load<float>(tb.cl, c.off_akb + blk * 128);
+      cdv = lds_load<float>(tb.cd, c.off_akb + blk * 128);
+    }
+    uint32_t pw[8], ww[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float p0, p1, d0, d1;
+      if (ROLE == kRoleQ) {
+        p0 = fast_exp2(sc[r] - lrow);
+        p1 = fast_exp2(sc[r + 1] - lrow);
+        d0 = p0 * (dp[r] - drow);
+        d1 = p1 * (dp[r + 1] - drow);
+      } else {
+        p0 = fast_exp2(sc[r] - row_bcast(clv, r));
+        p1 = fast_exp2(sc[r + 1] - row_bcast(clv, r + 1));
+        d0 = p0 * (dp[r] - row_bcast(cdv, r));
+        d1 = p1 * (dp[r + 1] - row_bcast(cdv, r + 1));
+      }
+      ww[r / 2] = pack_bf16x2(d0 * row_bcast(akv, r), d1 * row_bcast(akv, r + 1));
+      pw[r / 2] = pack_bf16x2(p0, p1);
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int pidx = 2 * blk + half;
+      const v4u wv = {ww[4 * half], ww[4 * half + 1], ww[4 * half + 2], ww[4 * half + 3]};
+      const v8bf wop = __builtin_bit_cast(v8bf, wv);
+      if (ROLE == kRoleQ) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          acc.a1[cb] = mfma_bf16_32x32x16(lds_load<v8bf>(tb.vt, c.off_v[pidx] + cb * 4096), wop, acc.a1[cb]);
+      } else {
+        const v4u pv = {pw[4 * half], pw[4 * half + 1], pw[4 * half + 2], pw[4 * half + 3]};
+        const v8bf pop = __builtin_bit_cast(v8bf, pv);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          acc.a2[cb] = mfma_bf16_32x32x16(lds_load<v8bf>(tb.vt, c.off_v[pidx] + cb * 4096), pop, acc.a2[cb]);
+          acc.a1[cb] = mfma_bf16_32x32x16(lds_load<v8bf>(tb.vt2, c.off_v[pidx] + cb * 4096), wop, acc.a1[cb]);
+        }
+      }
+    }
+  }
+}
+
+template <int ROLE, int NCH, int CB, int BIAS>
+__device__ __forceinline__ void bwd_step(const Ctx<NCH>& c, const BwdCtx& bc,
+                                         const BwdTileBuf<ROLE, NCH, CB, BIAS>& cur,
+                                         BwdTileBuf<ROLE, NCH, CB, BIAS>& nxt, int t, int nkt, KeyPos& kp,
+                                         const v8bf (&xop)[2 * CB], float lrow, float drow, BwdAcc<ROLE, CB>& acc) {
+  const FwdArgs& a = *c.a;
+  const KeyPos kn = next_keys(kp, a.gw);
+  if (t + 1 < nkt) bwd_copy<ROLE, NCH, CB, BIAS>(c, bc, nxt, t + 1, kn);
+  if (BIAS == kBiasRows)  // as in pass_step
+    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, kp.k0 + 32 < a.N ? 2 : 1);
+  else if (kp.k0 + kBN <= a.N)
+    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2);
+  else
+    bwd_tile<ROLE, true, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  kp = kn;
+}
+
+// dx = sign(x) <sign(x), dx~> / d + alpha 1{|x| <= 1} dx~ for the lane's row
+// token x, whose dx~ / scale sits in acc, stored as float32.
+template <int CB>
+__device__ __forceinline__ void binarize_back_store(bool valid, const uint16_t* xr, float alpha, int d, int lh,
+                                                    float scale, const v16f (&acc)[CB], float* out) {
+  float dot = 0.0f;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int c0 = cb * 32 + 8 * b + 4 * lh;
+      const uint2 raw = valid ? *reinterpret_cast<const uint2*>(xr + c0) : make_uint2(0u, 0u);
+      const uint32_t w2[2] = {raw.x, raw.y};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = bf16_to_f32(static_cast<uint16_t>(e & 1 ? w2[e >> 1] >> 16 : w2[e >> 1] & 0xffffu));
+        dot += (x < 0.0f ? -1.0f : 1.0f) * acc[cb][4 * b + e];
+      }
+    }
+  dot = sum_halves(dot) * scale / static_cast<float>(d);
+  if (!valid) return;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int c0 = cb * 32 + 8 * b + 4 * lh;
+      const uint2 raw = *reinterpret_cast<const uint2*>(xr + c0);
+      const uint32_t w2[2] = {raw.x, raw.y};
+      v4f o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = bf16_to_f32(static_cast<uint16_t>(e & 1 ? w2[e >> 1] >> 16 : w2[e >> 1] & 0xffffu));
+        const float g = scale * acc[cb][4 * b + e];
+        o[e] = (x < 0.0f ? -dot : dot) + (fabsf(x) <= 1.0f ? alpha * g : 0.0f);
+      }
+      *reinterpret_cast<v4f*>(out + c0) = o;
+    }
+}
+
+template <int ROLE, int NCH, int CB, int BIAS>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+attn_bwd_kernel(BwdArgs ba) {
+  __shared__ __attribute__((aligned(16))) BwdTileBuf<ROLE, NCH, CB, BIAS> tb0;
+  __shared__ __attribute__((aligned(16))) BwdTileBuf<ROLE, NCH, CB, BIAS> tb1;
+  __shared__ float red[kThreads / 64];
+  extern __shared__ __attribute__((aligned(16))) float s_table[];
+  const FwdArgs& a = ba.f;
+
+  Ctx<NCH> c;
+  (void)workgroup_setup<NCH, CB, BIAS>(c, a, red, s_table);
+  const int64_t bhN = static_cast<int64_t>(c.bh) * a.N;
+  BwdCtx bc;
+  constexpr int kTBytes = 32 * CB * kBN * 2;
+  const int ntile = a.Npad / kBN;
+  bc.zrs = make_rsrc(reinterpret_cast<const char*>(ba.zt) + static_cast<int64_t>(c.bh) * ntile * kTBytes,
+                     static_cast<uint32_t>(ntile * kTBytes));
+  bc.z2rs = bc.zrs;
+  if (ROLE == kRoleKV)
+    bc.z2rs = make_rsrc(reinterpret_cast<const char*>(ba.zt2) + static_cast<int64_t>(c.bh) * ntile * kTBytes,
+                        static_cast<uint32_t>(ntile * kTBytes));
+  bc.yrs = make_rsrc(ba.ynat + bhN * a.d, static_cast<uint32_t>(a.N * a.d * 2));
+  bc.lrs = make_rsrc(ba.lse + c.tokbase, static_cast<uint32_t>(a.Npad * 4));
+  bc.drs = make_rsrc(ba.delta + c.tokbase, static_cast<uint32_t>(a.Npad * 4));
+
+  // the lane's dP operand: its dO row (kRoleQ) or V row (kRoleKV), 8
+  // channels per 16-channel step
+  const bool valid = c.qi < a.N;
+  const uint16_t* xr = ba.xrow + (bhN + (valid ? c.qi : 0)) * a.d;
+  v8bf xop[2 * CB];
+#pragma unroll
+  for (int t = 0; t < 2 * CB; ++t) {
+    const uint4 raw = valid ? *reinterpret_cast<const uint4*>(xr + 16 * t + 8 * c.lh) : make_uint4(0u, 0u, 0u, 0u);
+    xop[t] = __builtin_bit_cast(v8bf, raw);
+  }
+  float lrow = 0.0f, drow = 0.0f;
+  if (ROLE == kRoleQ) {
+    // delta_i = <dO_i, O_i>: this lane's half of the channels, then both
+    const uint16_t* orw = ba.orow + (bhN + (valid ? c.qi : 0)) * a.d;
+    float part = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2 * CB; ++t) {
+      const uint4 ro = valid ? *reinterpret_cast<const uint4*>(orw + 16 * t + 8 * c.lh) : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 rg = __builtin_bit_cast(uint4, xop[t]);
+      const uint32_t wo[4] = {ro.x, ro.y, ro.z, ro.w}, wg[4] = {rg.x, rg.y, rg.z, rg.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        part += bf16_to_f32(static_cast<uint16_t>(wo[e] & 0xffffu)) * bf16_to_f32(static_cast<uint16_t>(wg[e] & 0xffffu)) +
+                bf16_to_f32(static_cast<uint16_t>(wo[e] >> 16)) * bf16_to_f32(static_cast<uint16_t>(wg[e] >> 16));
+    }
+    drow = sum_halves(part);
+    lrow = ba.lse[c.tokbase + c.qi];
+    if (c.lh == 0) ba.delta[c.tokbase + c.qi] = valid ? drow : 0.0f;
+  }
+
+  BwdAcc<ROLE, CB> acc;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    acc.a1[cb] = v16f{};
+    if (ROLE == kRoleKV) acc.a2[cb] = v16f{};
+  }
+  KeyPos kp;
+  kp.k0 = 0;
+  kp.ky[0] = 0;
+  kp.kx[0] = 0;
+  kp.ky[1] = (BIAS == kBiasRows && a.gw == 32) ? 1 : 0;
+  kp.kx[1] = (BIAS == kBiasRows && a.gw == 32) ? 0 : 32;
+  bwd_copy<ROLE, NCH, CB, BIAS>(c, bc, tb0, 0, kp);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int nkt = (a.N + kBN - 1) / kBN;
+  for (int t = 0; t < nkt; t += 2) {
+    bwd_step<ROLE, NCH, CB, BIAS>(c, bc, tb0, tb1, t, nkt, kp, xop, lrow, drow, acc);
+    if (t + 1 < nkt) bwd_step<ROLE, NCH, CB, BIAS>(c, bc, tb1, tb0, t + 1, nkt, kp, xop, lrow, drow, acc);
+  }
+
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    pin_uniform(acc.a1[cb]);
+    if (ROLE == kRoleKV) pin_uniform(acc.a2[cb]);
+  }
+  // the lane's own row token (q for kRoleQ, k for kRoleKV) for dx~ -> dx
+  const uint16_t* tr = a.q + (bhN + (valid ? c.qi : 0)) * a.d;
+  binarize_back_store<CB>(valid, tr, c.alpha, a.d, c.lh, ba.scale, acc.a1, ba.out1 + (bhN + (valid ? c.qi : 0)) * a.d);
+  if (ROLE == kRoleKV && valid) {
+    float* dvr = ba.out2 + (bhN + c.qi) * a.d;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int c0 = cb * 32 + 8 * b + 4 * c.lh;
+        const v4f o = {acc.a2[cb][4 * b], acc.a2[cb][4 * b + 1], acc.a2[cb][4 * b + 2], acc.a2[cb][4 * b + 3]};
+        *reinterpret_cast<v4f*>(dvr + c0) = o;
+      }
+  }
+}
+
+template <int ROLE, int BIAS>
+static int bwd_static_lds_for(int cb) {
+  constexpr int kRed = kThreads / 64 * 4;
+  switch (cb) {
+    case 1: return 2 * sizeof(BwdTileBuf<ROLE, 1, 1, BIAS>) + kRed;
+    case 2: return 2 * sizeof(BwdTileBuf<ROLE, 1, 2, BIAS>) + kRed;
+    default: return 2 * sizeof(BwdTileBuf<ROLE, 2, 4, BIAS>) + kRed;
+  }
+}
+
+int bwd_static_lds(int role, int dpad, int mode) {
+  const int cb = dpad / 32;
+  if (role == kRoleQ) {
+    switch (mode) {
+      case kBiasNone: return bwd_static_lds_for<kRoleQ, kBiasNone>(cb);
+      case kBiasRows: return bwd_static_lds_for<kRoleQ, kBiasRows>(cb);
+      default: return bwd_static_lds_for<kRoleQ, kBiasTable>(cb);
+    }
+  }
+  switch (mode) {
+    case kBiasNone: return bwd_static_lds_for<kRoleKV, kBiasNone>(cb);
+    case kBiasRows: return bwd_static_lds_for<kRoleKV, kBiasRows>(cb);
+    default: return bwd_static_lds_for<kRoleKV, kBiasTable>(cb);
+  }
+}
+
+template <int ROLE, int NCH, int CB>
+static int launch_bwd_nc(const BwdArgs& a, int mode, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(a.f.nwg), block(kThreads);
+  const int lds = a.f.dyn_lds;
+  switch (mode) {
+    case kBiasNone:
+      hipLaunchKernelGGL((attn_bwd_kernel<ROLE, NCH, CB, kBiasNone>), grid, block, lds, s, a);
+      break;
+    case kBiasRows:
+      hipLaunchKernelGGL((attn_bwd_kernel<ROLE, NCH, CB, kBiasRows>), grid, block, lds, s, a);
+      break;
+    case kBiasTable:
+      hipLaunchKernelGGL((attn_bwd_kernel<ROLE, NCH, CB, kBiasTable>), grid, block, lds, s, a);
+      break;
+    default:
+      return static_cast<int>(hipErrorInvalidValue);
+  }
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_backward(const BwdArgs& a, int role, int mode, void* stream) {
+  const int cb = a.f.dpad / 32;
+  if (role == kRoleQ) {
+    switch (cb) {
+      case 1: return launch_bwd_nc<kRoleQ, 1, 1>(a, mode, stream);
+      case 2: return launch_bwd_nc<kRoleQ, 1, 2>(a, mode, stream);
+      case 4: return launch_bwd_nc<kRoleQ, 2, 4>(a, mode, stream);
+      default: return static_cast<int>(hipErrorInvalidValue);
+    }
+  }
+  switch (cb) {
+    case 1: return launch_bwd_nc<kRoleKV, 1, 1>(a, mode, stream);
+    case 2: return launch_bwd_nc<kRoleKV, 1, 2>(a, mode, stream);
+    case 4: return launch_bwd_nc<kRoleKV, 2, 4>(a, mode, stream);
+    default: return static_cast<int>(hipErrorInvalidValue);
   }
 }
 

@@ -63,6 +63,9 @@ struct KvJob {
   const float* vpart; // [BH][Npad/64][dpad] max |v| of each tile and channel
   float* vscale;      // [BH][dpad] max |v| / 127 (written by tile 0)
   int* vcsum;         // [BH][dpad] sum of the codes over the keys (atomic adds)
+  // backward: the signs of the tile's tokens as +/-1 bf16 in the V^T layout
+  // (nullptr: not written)
+  uint16_t* kst;      // [BH][Npad/64][dpad][64]
   Strides ks, vs;
   int64_t BH;
   int H, N, Npad, d, W, nch, dpad;
@@ -85,6 +88,14 @@ struct BiasJob {
   float* bias4;           // [H][2gh-1+2*kBiasPadRows][4][Lpad]
   float* row_max;         // [H][2gh-1]: max |entry| * log2(e) of each row
   int gh, gw, Lpad;
+  int flip;               // 1: rows of the table flipped in both axes (the
+                          // bias seen with queries and keys exchanged)
+};
+
+// Sets n floats to zero (the accumulators of the backward pass).
+struct FillJob {
+  float* x;
+  int64_t n;
 };
 
 // One launch runs the blocks of every job present (a job with 0 blocks is
@@ -98,6 +109,10 @@ struct PrologueArgs {
   int64_t bias_blocks;
   VstatJob vstat;
   int64_t vstat_blocks;
+  BiasJob bias2;          // a second bias-row job (the flipped rows of the backward)
+  int64_t bias2_blocks;
+  FillJob fill;
+  int64_t fill_blocks;
   int lds;  // dynamic LDS bytes per block
 };
 
@@ -127,6 +142,8 @@ struct FwdArgs {
   const float* vscale;     // 8-bit P.V: [BH][dpad] value scales
   const int* vcsum;        // 8-bit P.V: [BH][dpad] column sums of the codes
   uint16_t* o;             // bf16 output (strides os)
+  float* lse;              // optional [BH][Npad]: mrow + log2(row sum), the
+                           // logits' log2-sum-exp2 (for the backward pass)
   Strides qs, os;
   int B, H, N, Npad, d, W, dpad;
   int gh, gw, Lpad;
@@ -136,6 +153,7 @@ struct FwdArgs {
   int nwg;                 // workgroups
   int xcd_remap;           // 1: spread consecutive heads over the 8 XCDs
   int dyn_lds;             // dynamic LDS bytes per workgroup (table and/or padding)
+  int table_flip;          // kBiasTable: read the table flipped in both axes
   int prio_balance;        // 1: lower the wave priority over the last keys
                            // (every workgroup of the grid is resident at once)
 };
@@ -155,6 +173,29 @@ int fwd_waves_per_simd(int dpad, int d);
 int launch_attention(const FwdArgs& a, int mode, void* stream);
 // The fused kernel of the 8-bit P.V forward (d <= 128; no dense bias).
 int launch_attention_int8(const FwdArgs& a, int mode, void* stream);
+
+// Backward pass (d in {32, 64, 128}; table-row, table or no bias).  One
+// kernel, two roles: kRoleQ (lane = query; dq, delta, table gradient) and
+// kRoleKV (lane = key; dk, dv).  f describes the row side (f.q: the lanes'
+// tokens) and the column side (f.kop, f.alpha_k, f.kmax_blk, the bias) as
+// the forward's arguments do.
+enum BwdRole { kRoleQ = 0, kRoleKV = 1 };
+struct BwdArgs {
+  FwdArgs f;
+  const uint16_t* xrow;    // [BH][N][d] the lanes' dP operand rows: dO (kRoleQ) or V (kRoleKV)
+  const uint16_t* ynat;    // [BH][N][d] natural column tiles: V (kRoleQ) or dO (kRoleKV)
+  const uint16_t* zt;      // [BH][Npad/64][dpad][64]: K signs (kRoleQ) or dO^T (kRoleKV)
+  const uint16_t* zt2;     // [BH][Npad/64][dpad][64]: Q signs (kRoleKV)
+  const uint16_t* orow;    // kRoleQ: [BH][N][d] the forward output, for delta
+  float* lse;              // [BH][Npad] log2-sum-exp2 of the query rows
+  float* delta;            // [BH][Npad] <dO_i, O_i> (written by kRoleQ)
+  float* out1;             // [BH][N][d] float32: dq (kRoleQ) or dk (kRoleKV)
+  float* out2;             // kRoleKV: [BH][N][d] float32 dv
+  float* dtable;           // kRoleQ: [H][2gh-1][2gw-1] float32 accumulated (nullptr: skipped)
+  float scale;             // the softmax scale
+};
+int bwd_static_lds(int role, int dpad, int mode);
+int launch_backward(const BwdArgs& a, int role, int mode, void* stream);
 
 struct DotArgs {
   const uint32_t* qbits;  // [BH][N][W]

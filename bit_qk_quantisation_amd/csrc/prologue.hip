@@ -184,6 +184,29 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
                          static_cast<uint32_t>(op[2]), static_cast<uint32_t>(op[3]));
   }
 
+  if (job.kst) {
+    // the tokens' signs as +/-1 bf16, transposed exactly as V^T below
+    uint16_t* sout = job.kst + blk * static_cast<int64_t>(job.dpad) * kPackTok;
+    for (int g = threadIdx.x; g < job.dpad * 8; g += kThreads) {
+      const int c = g >> 3, q = g & 7;
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t h2[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int key = vt_slot_key(8 * q + 2 * k + e);
+          if (c < d && n0 + key < job.N) {
+            const uint32_t neg = (sb[key * 4 * W + (c >> 3)] >> (c & 7)) & 1u;
+            h2[e] = neg ? 0xBF80u : 0x3F80u;
+          }
+        }
+        w[k] = h2[0] | (h2[1] << 16);
+      }
+      const int pos = q ^ ((c >> 1) & 7);
+      *reinterpret_cast<uint4*>(sout + c * kPackTok + pos * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
   if (job.vq) {
     kv_codes(job, blk, bh, tile, vs, stride, reinterpret_cast<float*>(vs + kPackTok * stride));
     return;
@@ -315,7 +338,8 @@ __device__ void bias_block(const BiasJob& job, int64_t blk) {
   const int64_t h = blk / prow;
   const int dyp = static_cast<int>(blk - h * prow), dy = dyp - kBiasPadRows;
   const bool inside = dy >= 0 && dy < rows;
-  const uint16_t* trow = job.table + (h * rows + (inside ? dy : 0)) * cols;
+  // flipped: T'[dy][x] = T[rows-1-dy][cols-1-x]
+  const uint16_t* trow = job.table + (h * rows + (inside ? (job.flip ? rows - 1 - dy : dy) : 0)) * cols;
   float* out = job.bias4 + (h * prow + dyp) * 4 * static_cast<int64_t>(job.Lpad);
   float m = 0.0f;
   for (int e = threadIdx.x; e < 4 * job.Lpad; e += blockDim.x) {
@@ -326,7 +350,7 @@ __device__ void bias_block(const BiasJob& job, int64_t blk) {
     // inside the rows; that kernel masks padded keys itself, since a padded
     // key seen from a query on grid row >= 1 falls on a real row.
     float val = inside ? 0.0f : -INFINITY;
-    if (inside && u <= cols - 1) val = kLog2e * bf16_to_f32(trow[cols - 1 - u]);
+    if (inside && u <= cols - 1) val = kLog2e * bf16_to_f32(trow[job.flip ? u : cols - 1 - u]);
     out[e] = val;
     if (inside) m = fmaxf(m, fabsf(val));
   }
@@ -361,11 +385,28 @@ __global__ void __launch_bounds__(kThreads) prologue_kernel(PrologueArgs a) {
     return;
   }
   blk -= a.bias_blocks;
-  if (blk < a.vstat_blocks) vstat_block(a.vstat, blk, smem);
+  if (blk < a.vstat_blocks) {
+    vstat_block(a.vstat, blk, smem);
+    return;
+  }
+  blk -= a.vstat_blocks;
+  if (blk < a.bias2_blocks) {
+    bias_block(a.bias2, blk);
+    return;
+  }
+  blk -= a.bias2_blocks;
+  if (blk < a.fill_blocks) {
+    const int64_t i0 = blk * kThreads * 4;
+    for (int e = 0; e < 4; ++e) {
+      const int64_t i = i0 + e * kThreads + threadIdx.x;
+      if (i < a.fill.n) a.fill.x[i] = 0.0f;
+    }
+  }
 }
 
 int launch_prologue(const PrologueArgs& a, void* stream) {
-  const int64_t blocks = a.pack_blocks + a.kv_blocks + a.bias_blocks + a.vstat_blocks;
+  const int64_t blocks =
+      a.pack_blocks + a.kv_blocks + a.bias_blocks + a.vstat_blocks + a.bias2_blocks + a.fill_blocks;
   hipLaunchKernelGGL(prologue_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), a.lds,
                      static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());
