@@ -2,7 +2,7 @@
 """Benchmark of the BinaryAttention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--layout bhnd|bnhd|qkv] [--bias table|dense|dense-batch] [--pv bf16|int8]
+                    [--layout bhnd|bnhd|qkv] [--bias table|dense|dense-batch] [--pv bf16|int8] [--bwd]
 
 One step is one full forward (ba_attention_prepare + ba_attention_fwd_prepared,
 i.e. exactly ba_attention_fwd) over the resident bf16 inputs of the chosen
@@ -26,6 +26,12 @@ kernel is closer to.
 --pv int8 runs the pages' hybrid 8-bit P.V (ba_attention_fwd_int8pv: three
 kernels in one call), so only the whole step is timed; its roofline takes the
 fp4 QK + int8 P.V matrix-core bound.
+
+--bwd times the backward instead (ba_attention_bwd: five kernels in one call,
+the forward recomputed inside), counted as 10*B*H*N^2*d FLOP-eq per step (the
+products S, dP, dV, dQ and dK of a flash-attention backward); its roofline
+takes the fp4 + bf16 matrix-core bound of those products (S on fp4, the
+other four on bf16).
 
 Printed: one JSON line on stdout with the throughput in TFLOP-eq/s
 (4*B*H*N^2*d per step, the FLOPs of dense QK^T and P.V), the fused kernel's
@@ -181,6 +187,7 @@ def main() -> int:
                     help="host time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--layout", choices=("bhnd", "bnhd", "qkv"), default="bhnd",
                     help="memory layout of q, k, v and o (see above)")
+    ap.add_argument("--bwd", action="store_true", help="time the backward pass (see above)")
     ap.add_argument("--pv", choices=("bf16", "int8"), default="bf16",
                     help="P.V precision (see above)")
     ap.add_argument("--bias", choices=("table", "dense", "dense-batch"), default="table",
@@ -249,8 +256,31 @@ def main() -> int:
                 q.data_ptr(), dense.data_ptr(), dsb, dense.stride(1), dense.stride(2), B, H, N, d, scale,
                 out.data_ptr(), wsp, nbytes, sp))
 
-    split = args.layout == "bhnd" and args.pv == "bf16"
-    if args.pv == "int8":
+    split = args.layout == "bhnd" and args.pv == "bf16" and not args.bwd
+    if args.bwd:
+        if args.layout != "bhnd" or dense is not None or args.pv != "bf16":
+            log("--bwd runs with the contiguous layout, the table bias and bf16 P.V only")
+            return 2
+        nbb = lib.ba_workspace_bytes_bwd(B, H, N, d, gh, gw)
+        if nbb == 0:
+            log(f"the backward does not support d = {d}")
+            return 2
+        wsb = torch.empty(nbb + 256, dtype=torch.uint8, device=dev)
+        wspb = (wsb.data_ptr() + 255) // 256 * 256
+        g = torch.Generator().manual_seed(w.seed + 200)
+        dout = torch.randn((B, H, N, d), generator=g).to(torch.bfloat16).to(dev)
+        gq = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+        gk, gv = torch.empty_like(gq), torch.empty_like(gq)
+        gt = None if table is None else torch.empty(table.shape, dtype=torch.float32, device=dev)
+
+        def prepare():  # noqa: F811 -- one call runs the whole backward
+            bq.check(lib, lib.ba_attention_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), tp, gh, gw, B, H, N, d,
+                                               scale, dout.data_ptr(), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(),
+                                               None if gt is None else gt.data_ptr(), wspb, nbb, sp))
+
+        def fused():  # noqa: F811
+            pass
+    elif args.pv == "int8":
         if args.layout != "bhnd" or dense is not None:
             log("--pv int8 runs with the contiguous layout and the table bias only")
             return 2
@@ -323,6 +353,9 @@ def main() -> int:
     if not split:  # the "prologue" interval held the whole step
         fus_ms = pro_ms
     peak = PEAK_MFMA_FP4_INT8 if args.pv == "int8" else PEAK_MFMA_COMPOSITE
+    if args.bwd:
+        # S on the fp4 unit (2 flops per score and channel), dP, dV, dQ, dK on bf16 (8)
+        peak = 10.0 / (2.0 / PEAK_FP4 + 8.0 / PEAK_BF16)
 
     if args.copy_mb:
         src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
@@ -330,7 +363,7 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    flop = w.flop_eq
+    flop = w.flop_eq * (2.5 if args.bwd else 1.0)
     value = flop / (ms_step * 1e-3) / 1e12
     fused_tf = flop / (fus_ms * 1e-3) / 1e12
     npad = (N + 127) // 128 * 128
@@ -341,13 +374,14 @@ def main() -> int:
     hbm_bound = dense is not None and fused_gbs / PEAK_HBM_GBS > fused_tf / peak
 
     baseline = None
-    if args.cpu_seconds > 0 and (dense is not None or args.pv != "bf16"):
-        log("[bench] no CPU baseline with --bias dense or --pv int8")
+    if args.cpu_seconds > 0 and (dense is not None or args.pv != "bf16" or args.bwd):
+        log("[bench] no CPU baseline with --bias dense, --pv int8 or --bwd")
     elif args.cpu_seconds > 0:
         baseline = cpu_baseline(w, inp, out, args.cpu_seconds)
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if not args.bwd else
+                  "binary-QK attention bwd TFLOP-eq/s (10·B·H·N²·d) + % roofline",
         "value": round(value, 2),
         "unit": "TFLOP-eq/s",
         "n_gpus": 1,
@@ -367,6 +401,7 @@ def main() -> int:
         "roofline": {
             "bound": "mfma",
             "kernel": ("attn_fwd_kernel (fused)" if split else
+                       "whole backward (5 kernels, one call; forward recomputed)" if args.bwd else
                        "whole step (3 kernels, one call; fp4 QK + int8 P.V bound)" if args.pv == "int8" else
                        "whole step (prologue + fused, one strided call)"),
             "achieved": round(fused_tf, 1),
@@ -402,7 +437,8 @@ def main() -> int:
         log(f"[bench] {name}: step {ms_step * 1e3:.1f} us (prologue {pro_ms * 1e3:.1f} us, "
             f"fused {fus_ms * 1e3:.1f} us) -> {value:.1f} TFLOP-eq/s")
     else:
-        log(f"[bench] {name} ({args.layout}, pv {args.pv}): step {ms_step * 1e3:.1f} us -> {value:.1f} TFLOP-eq/s")
+        log(f"[bench] {name} ({args.layout}, pv {args.pv}{', backward' if args.bwd else ''}): "
+            f"step {ms_step * 1e3:.1f} us -> {value:.1f} TFLOP-eq/s")
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -11,6 +11,7 @@ If the library is missing the calls raise; there is no CPU fallback.
                                               a [B,N,H,d] tensor transposed)
     attention_fwd_dense_bias(q, k, v, bias) -> O (bf16); bias [1 or B, H, N, N]
     attention_fwd_int8pv(q, k, v, table, gh, gw) -> O (bf16), 8-bit P.V
+    attention_bwd(q, k, v, dO, table, gh, gw) -> (dq, dk, dv, dtable), float32
     qk_int_dot(qbits, kbits, d, route)     -> D (int32)
     workspace_bytes(B, H, N, d, gh, gw)    -> int
 """
@@ -25,7 +26,8 @@ import torch
 from ._lib import (BinAttnError, EXPORTS, ROUTE_MFMA_FP4,  # noqa: F401
                    ROUTE_VALU_POPCOUNT, check, load)
 
-__all__ = ["pack_signs", "attention_fwd", "attention_fwd_dense_bias", "attention_fwd_int8pv", "qk_int_dot", "workspace_bytes",
+__all__ = ["pack_signs", "attention_fwd", "attention_fwd_dense_bias", "attention_fwd_int8pv", "attention_bwd",
+           "qk_int_dot", "workspace_bytes",
            "pack_words", "BinAttnError", "ROUTE_MFMA_FP4", "ROUTE_VALU_POPCOUNT",
            "Workspace"]
 
@@ -225,6 +227,45 @@ def attention_fwd_int8pv(q, k, v, table=None, gh: int = 0, gw: int = 0, scale=No
         int(gh), int(gw), B, H, N, d, float(scale), out.data_ptr(), aligned,
         ws.numel() - (aligned - base), _stream(q.device)))
     return out
+
+
+def attention_bwd(q, k, v, dout, table=None, gh: int = 0, gw: int = 0, scale=None,
+                  workspace: Workspace | None = None):
+    """Gradients of attention_fwd for the output gradient dout: contiguous
+    bf16 q, k, v, dout [B,H,N,d] (+ bf16 table [H, 2gh-1, 2gw-1]) ->
+    float32 dq, dk, dv [B,H,N,d] and dtable [H, 2gh-1, 2gw-1] (None without a
+    table).  The sign function takes the clipped straight-through estimator
+    and alpha = mean |x| its exact derivative."""
+    lib = load()
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _need(t, name, torch.bfloat16, 4)
+    if not (q.shape == k.shape == v.shape == dout.shape):
+        raise ValueError("q, k, v and dout must have the same shape")
+    B, H, N, d = q.shape
+    if table is not None:
+        _need(table, "table", torch.bfloat16, 3)
+        if tuple(table.shape) != (H, 2 * gh - 1, 2 * gw - 1):
+            raise ValueError(f"table must be [H, 2gh-1, 2gw-1] = {(H, 2*gh-1, 2*gw-1)}")
+    else:
+        gh = gw = 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = lib.ba_workspace_bytes_bwd(B, H, N, d, gh, gw)
+    if nbytes == 0:
+        raise BinAttnError(3, f"unsupported problem B={B} H={H} N={N} d={d} grid={gh}x{gw}")
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    dtable = None if table is None else torch.empty(table.shape, dtype=torch.float32, device=q.device)
+    ws = (workspace or _default_ws).get(q.device, nbytes)
+    base = ws.data_ptr()
+    aligned = (base + 255) // 256 * 256
+    check(lib, lib.ba_attention_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), None if table is None else table.data_ptr(),
+        int(gh), int(gw), B, H, N, d, float(scale), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+        dv.data_ptr(), None if dtable is None else dtable.data_ptr(), aligned,
+        ws.numel() - (aligned - base), _stream(q.device)))
+    return dq, dk, dv, dtable
 
 
 def qk_int_dot(qbits, kbits, d: int, route: int = ROUTE_MFMA_FP4):

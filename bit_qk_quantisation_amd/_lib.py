@@ -12,7 +12,7 @@ EXPORTS = (
     "ba_version", "ba_status_string", "ba_last_error", "ba_pack_words",
     "ba_pack_signs", "ba_workspace_bytes", "ba_attention_fwd", "ba_attention_fwd_strided",
     "ba_attention_fwd_dense_bias", "ba_attention_fwd_dense_bias_prepared", "ba_attention_prepare",
-    "ba_workspace_bytes_int8pv", "ba_attention_fwd_int8pv",
+    "ba_workspace_bytes_int8pv", "ba_attention_fwd_int8pv", "ba_workspace_bytes_bwd", "ba_attention_bwd",
     "ba_attention_fwd_prepared", "ba_qk_int_dot",
 )
 
@@ -74,6 +74,11 @@ def load(path=None) -> ctypes.CDLL:
     lib.ba_attention_fwd_int8pv.restype = i32
     lib.ba_attention_fwd_int8pv.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32,
                                             ctypes.c_float, vp, vp, sz, vp]
+    lib.ba_workspace_bytes_bwd.restype = sz
+    lib.ba_workspace_bytes_bwd.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.ba_attention_bwd.restype = i32
+    lib.ba_attention_bwd.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, ctypes.c_float, vp,
+                                     vp, vp, vp, vp, vp, sz, vp]
     lib.ba_attention_prepare.restype = i32
     lib.ba_attention_prepare.argtypes = [vp, vp, vp, i32, i32, i64, i64, i64, i32, vp, sz, vp]
     lib.ba_attention_fwd_prepared.restype = i32

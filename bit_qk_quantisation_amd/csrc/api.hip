@@ -204,6 +204,49 @@ int fused_dynamic_lds(int static_lds, int table_lds, int64_t nwg) {
   return dyn;
 }
 
+// ---- backward -------------------------------------------------------------
+// Workspace of ba_attention_bwd: the forward's sections, then (256-byte
+// aligned, in this order) the K signs transposed, the forward output, the
+// rows' log2-sum-exp2 and delta, the Q operand tiles, Q scales and their
+// tile maxima, dO^T, the Q signs transposed, and the flipped bias rows.
+struct BwdLayout {
+  Layout fwd;
+  int64_t kst, obuf, lse, delta, qop, alpha_q, qmax, dot, qst, bias4f, rowmaxf, total;
+};
+
+BwdLayout bwd_layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int gw) {
+  BwdLayout L{};
+  L.fwd = layout(B, H, N, d, has_bias, gh, gw);
+  const int64_t BH = B * H, Npad = L.fwd.Npad, dpad = L.fwd.dpad, W = L.fwd.W;
+  int64_t off = L.fwd.total;
+  auto take = [&](int64_t bytes) {
+    const int64_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  L.kst = take(BH * Npad * dpad * 2);
+  L.obuf = take(BH * N * d * 2);
+  L.lse = take(BH * Npad * 4);
+  L.delta = take(BH * Npad * 4);
+  L.qop = take(BH * Npad * ((W + 1) / 2) * 32);
+  L.alpha_q = take(BH * Npad * 4);
+  L.qmax = take(BH * (Npad / 64) * 4);
+  L.dot = take(BH * Npad * dpad * 2);
+  L.qst = take(BH * Npad * dpad * 2);
+  const bool rows = L.fwd.mode == ba::kBiasRows;
+  L.bias4f = take(rows ? H * (2 * gh - 1 + 2 * ba::kBiasPadRows) * 4 * L.fwd.Lpad * 4 : 0);
+  L.rowmaxf = take(rows ? H * (2 * gh - 1) * 4 : 0);
+  L.total = off;
+  return L;
+}
+
+ba_status check_bwd_dims(int64_t B, int64_t H, int64_t N, int d) {
+  ba_status st = check_dims(B, H, N, d);
+  if (st != BA_OK) return st;
+  if (d != 32 && d != 64 && d != 128) return fail(BA_ERR_UNSUPPORTED, "the backward supports d in {32, 64, 128} (d = %d)", d);
+  return BA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -551,6 +594,139 @@ ba_status ba_attention_fwd_dense_bias(const void* q, const void* k, const void* 
                                       void* workspace, size_t ws_bytes, void* stream) {
   const DenseBias dense{bias, bias_sb, bias_sh, bias_ld};
   return run_forward(q, k, v, nullptr, 0, 0, B, H, N, d, scale, o, strides, &dense, workspace, ws_bytes, stream);
+}
+
+ba_status ba_attention_bwd(const void* q, const void* k, const void* v, const void* bias, int gh, int gw,
+                           int64_t B, int64_t H, int64_t N, int d, float scale, const void* dout, float* dq,
+                           float* dk, float* dv, float* dtable, void* workspace, size_t ws_bytes, void* stream) {
+  ba_status st = check_bwd_dims(B, H, N, d);
+  if (st != BA_OK) return st;
+  if (!q || !dout || !dq || !dk || !dv) return fail(BA_ERR_NULL, "q, dout, dq, dk and dv must be non-NULL");
+  if (!std::isfinite(scale) || scale < 0.0f) return fail(BA_ERR_SHAPE, "scale must be finite and >= 0");
+  if (!aligned16(q)) return fail(BA_ERR_ALIGN, "q must be 16-byte aligned");
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || (dtable && !aligned16(dtable)))
+    return fail(BA_ERR_ALIGN, "dout, dq, dk, dv and dtable must be 16-byte aligned");
+  const BwdLayout BL = bwd_layout(B, H, N, d, bias != nullptr, gh, gw);
+  if (ws_bytes < static_cast<size_t>(BL.total))
+    return fail(BA_ERR_WORKSPACE, "workspace too small: %zu < %lld bytes", ws_bytes, (long long)BL.total);
+  // the forward's plan validates q, k, v, the bias and the first part of the workspace
+  Plan fp;
+  st = make_plan(q, k, v, true, bias, gh, gw, B, H, N, d, scale, nullptr, false, nullptr, nullptr, workspace,
+                 ws_bytes, &fp);
+  if (st != BA_OK) return st;
+  if (!workspace) return fail(BA_ERR_WORKSPACE, "workspace is NULL");
+  const size_t tb = static_cast<size_t>(B * H * N * d);
+  const void* ins[4] = {q, k, v, dout};
+  const void* outs[3] = {dq, dk, dv};
+  for (const void* o : outs) {
+    for (const void* i : ins)
+      if (overlaps(o, tb * 4, i, tb * 2)) return fail(BA_ERR_SHAPE, "gradients must not overlap the inputs");
+    if (overlaps(o, tb * 4, workspace, BL.total)) return fail(BA_ERR_WORKSPACE, "gradients overlap the workspace");
+  }
+  if (overlaps(dq, tb * 4, dk, tb * 4) || overlaps(dq, tb * 4, dv, tb * 4) || overlaps(dk, tb * 4, dv, tb * 4))
+    return fail(BA_ERR_SHAPE, "dq, dk and dv must not overlap");
+  const int mode = fp.mode;
+  const int64_t tcount = bias ? H * (2 * gh - 1) * (2 * gw - 1) : 0;
+  if (dtable && !bias) return fail(BA_ERR_SHAPE, "dtable needs a bias table");
+  if (dtable && overlaps(dtable, tcount * 4, workspace, BL.total))
+    return fail(BA_ERR_WORKSPACE, "dtable overlaps the workspace");
+  (void)tcount;
+
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  uint16_t* obuf = reinterpret_cast<uint16_t*>(ws + BL.obuf);
+  float* lse = reinterpret_cast<float*>(ws + BL.lse);
+  float* delta = reinterpret_cast<float*>(ws + BL.delta);
+
+  // 1. keys and values (with the K signs transposed), both bias-row orientations
+  ba::PrologueArgs p1 = fp.p;
+  p1.kv.kst = reinterpret_cast<uint16_t*>(ws + BL.kst);
+  if (mode == ba::kBiasRows) {
+    p1.bias2 = p1.bias;
+    p1.bias2.bias4 = reinterpret_cast<float*>(ws + BL.bias4f);
+    p1.bias2.row_max = reinterpret_cast<float*>(ws + BL.rowmaxf);
+    p1.bias2.flip = 1;
+    p1.bias2_blocks = p1.bias_blocks;
+  }
+  // 2. the forward, keeping O and the rows' log2-sum-exp2
+  ba::FwdArgs f = fp.f;
+  f.o = obuf;
+  f.os = contiguous_strides(H, N, d);
+  f.lse = lse;
+  // 3. queries and dO as the keys and values of a second prologue pass
+  ba::PrologueArgs p3{};
+  p3.kv = p1.kv;
+  p3.kv.k = static_cast<const uint16_t*>(q);
+  p3.kv.v = static_cast<const uint16_t*>(dout);
+  p3.kv.kop = reinterpret_cast<uint32_t*>(ws + BL.qop);
+  p3.kv.alpha = reinterpret_cast<float*>(ws + BL.alpha_q);
+  p3.kv.alpha_max = reinterpret_cast<float*>(ws + BL.qmax);
+  p3.kv.vt = reinterpret_cast<uint16_t*>(ws + BL.dot);
+  p3.kv.kst = reinterpret_cast<uint16_t*>(ws + BL.qst);
+  p3.kv.ks = contiguous_strides(H, N, d);
+  p3.kv.vs = contiguous_strides(H, N, d);
+  p3.kv_blocks = p1.kv_blocks;
+  p3.lds = p1.lds;
+  if (dtable) {
+    p3.fill = ba::FillJob{dtable, tcount};
+    p3.fill_blocks = (tcount + ba::kThreads * 4 - 1) / (ba::kThreads * 4);
+  }
+  // 4. query role: dq (and delta, the table gradient)
+  ba::BwdArgs bq{};
+  bq.f = fp.f;
+  bq.xrow = static_cast<const uint16_t*>(dout);
+  bq.ynat = static_cast<const uint16_t*>(v);
+  bq.zt = reinterpret_cast<const uint16_t*>(ws + BL.kst);
+  bq.orow = obuf;
+  bq.lse = lse;
+  bq.delta = delta;
+  bq.out1 = dq;
+  bq.dtable = dtable;
+  bq.scale = scale;
+  // 5. key role: dk, dv; queries and keys exchanged, the bias flipped
+  ba::BwdArgs bk = bq;
+  bk.f.q = static_cast<const uint16_t*>(k);
+  bk.f.kop = reinterpret_cast<const uint32_t*>(ws + BL.qop);
+  bk.f.alpha_k = reinterpret_cast<const float*>(ws + BL.alpha_q);
+  bk.f.kmax_blk = reinterpret_cast<const float*>(ws + BL.qmax);
+  if (mode == ba::kBiasRows) {
+    bk.f.bias4 = reinterpret_cast<const float*>(ws + BL.bias4f);
+    bk.f.bias_row_max = reinterpret_cast<const float*>(ws + BL.rowmaxf);
+  }
+  bk.f.table_flip = 1;
+  bk.xrow = static_cast<const uint16_t*>(v);
+  bk.ynat = static_cast<const uint16_t*>(dout);
+  bk.zt = reinterpret_cast<const uint16_t*>(ws + BL.dot);
+  bk.zt2 = reinterpret_cast<const uint16_t*>(ws + BL.qst);
+  bk.orow = nullptr;
+  bk.out1 = dk;
+  bk.out2 = dv;
+  bk.dtable = nullptr;
+  for (int role = 0; role < 2; ++role) {
+    ba::BwdArgs& b = role == 0 ? bq : bk;
+    const int sl = ba::bwd_static_lds(role, b.f.dpad, mode);
+    // the query role keeps a table-sized gradient accumulator after the table
+    const int tl = ba::fwd_table_lds(b.f, mode) * ((role == 0 && dtable) ? 2 : 1);
+    if (sl + tl > kMaxLds) return fail(BA_ERR_UNSUPPORTED, "the backward's tiles and bias table do not fit in LDS");
+    b.f.dyn_lds = tl;
+    b.f.prio_balance = 0;
+  }
+
+  int err = ba::launch_prologue(p1, stream);
+  if (err == 0) err = ba::launch_attention(f, mode, stream);
+  if (err == 0) err = ba::launch_prologue(p3, stream);
+  if (err == 0) err = ba::launch_backward(bq, ba::kRoleQ, mode, stream);
+  if (err == 0) err = ba::launch_backward(bk, ba::kRoleKV, mode, stream);
+  if (err != 0) return hip_fail(err, "backward launch");
+  return BA_OK;
+}
+
+size_t ba_workspace_bytes_bwd(int64_t B, int64_t H, int64_t N, int d, int gh, int gw) {
+  if (check_dims(B, H, N, d) != BA_OK || (d != 32 && d != 64 && d != 128)) return 0;
+  const bool has_bias = gh > 0 || gw > 0;
+  if (has_bias && (gh < 1 || gw < 1 || static_cast<int64_t>(gh) * gw != N)) return 0;
+  const BwdLayout L = bwd_layout(B, H, N, d, has_bias, gh, gw);
+  if (L.fwd.mode < 0) return 0;
+  return static_cast<size_t>(L.total);
 }
 
 ba_status ba_qk_int_dot(const uint32_t* qbits, const uint32_t* kbits, int64_t B, int64_t H, int64_t N,

@@ -987,6 +987,9 @@ struct BwdTileBuf {
   uint16_t vt[32 * CB * kBN];                    // K signs (kRoleQ) / dO^T (kRoleKV)
   uint16_t vt2[ROLE == kRoleKV ? 32 * CB * kBN : 8];  // Q signs (kRoleKV)
   float win[BiasSizes<BIAS>::kWin];              // bias window (table-row mode)
+  // kRoleQ, table rows: this tile's table-gradient window, win_rows rows of
+  // 2gw-1 entries (row = (yq - yq_lo) + (yk_hi - yk), column = xq - xk + gw - 1)
+  float dwin[ROLE == kRoleQ && BIAS == kBiasRows ? kMaxWindowFloats : 4];
 };
 
 // Buffer resources of the backward's own column copies.
@@ -1043,10 +1046,15 @@ struct BwdAcc {
   v16f a2[ROLE == kRoleKV ? CB : 1];   // dv (kRoleKV)
 };
 
+// The table gradient (kRoleQ, want_dt): every dS_ij is added in LDS at the
+// table entry of its grid offset, with ds_add_f32 (the lanes of one
+// instruction hold consecutive queries, so the addresses are consecutive):
+// in table-row mode into this tile's window tb.dwin, in table mode into a
+// copy of the whole table that follows it in dynamic LDS.
 template <int ROLE, bool MASK, int NCH, int CB, int BIAS>
-__device__ __forceinline__ void bwd_tile(const Ctx<NCH>& c, const BwdTileBuf<ROLE, NCH, CB, BIAS>& tb,
+__device__ __forceinline__ void bwd_tile(const Ctx<NCH>& c, BwdTileBuf<ROLE, NCH, CB, BIAS>& tb,
                                          const KeyPos& kp, const v8bf (&xop)[2 * CB], float lrow, float drow,
-                                         BwdAcc<ROLE, CB>& acc, int nblk) {
+                                         BwdAcc<ROLE, CB>& acc, int nblk, bool want_dt) {
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     if (blk >= nblk) break;  // uniform: the padded block of a ragged table-row tile
@@ -1069,6 +1077,7 @@ __device__ __forceinline__ void bwd_tile(const Ctx<NCH>& c, const BwdTileBuf<ROL
       cdv = lds_load<float>(tb.cd, c.off_akb + blk * 128);
     }
     uint32_t pw[8], ww[8];
+    float dsv[16];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       float p0, p1, d0, d1;
@@ -1085,6 +1094,29 @@ __device__ __forceinline__ void bwd_tile(const Ctx<NCH>& c, const BwdTileBuf<ROL
       }
       ww[r / 2] = pack_bf16x2(d0 * row_bcast(akv, r), d1 * row_bcast(akv, r + 1));
       pw[r / 2] = pack_bf16x2(p0, p1);
+      dsv[r] = d0;
+      dsv[r + 1] = d1;
+    }
+    if (ROLE == kRoleQ && BIAS == kBiasRows && want_dt) {
+      // keys of the block: grid row ky[blk], columns kx[blk] + 8 g + 4 lh + i
+      const FwdArgs& a = *c.a;
+      const int w2 = 2 * a.gw - 1;
+      const int row = (c.yq - c.yq_lo) + (kp.ky[1] - kp.ky[blk]);
+      float* base = tb.dwin + row * w2 + (c.xq - kp.kx[blk] + a.gw - 1) - 4 * c.lh;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) atomicAdd(base - (8 * (r >> 2) + (r & 3)), dsv[r]);
+    }
+    if (ROLE == kRoleQ && BIAS == kBiasTable && want_dt) {
+      const FwdArgs& a = *c.a;
+      float* tacc = c.table + (2 * a.gh - 1) * (2 * a.gw - 1) + c.fidx;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const v4i g = lds_load<v4i>(tb.gk, c.off_gk + (blk * 32 + 8 * b) * 4);
+        atomicAdd(tacc - g.x, dsv[4 * b + 0]);
+        atomicAdd(tacc - g.y, dsv[4 * b + 1]);
+        atomicAdd(tacc - g.z, dsv[4 * b + 2]);
+        atomicAdd(tacc - g.w, dsv[4 * b + 3]);
+      }
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -1108,22 +1140,42 @@ __device__ __forceinline__ void bwd_tile(const Ctx<NCH>& c, const BwdTileBuf<ROL
   }
 }
 
+// Adds a tile's table-gradient window to the global table gradient (one
+// atomic per nonzero entry) and clears it.  kp: that tile's key position.
+template <int NCH>
+__device__ __forceinline__ void flush_dwin(const Ctx<NCH>& c, float* dwin, const KeyPos& kp, float* dtable) {
+  const FwdArgs& a = *c.a;
+  const int w2 = 2 * a.gw - 1, rows = 2 * a.gh - 1;
+  const int dy0 = c.yq_lo - kp.ky[1] + a.gh - 1;  // table row of window row 0
+  for (int e = c.tid; e < a.win_rows * w2; e += kThreads) {
+    const int r = e / w2, col = e - r * w2, dyi = dy0 + r;
+    const float v = dwin[e];
+    if (v != 0.0f && dyi >= 0 && dyi < rows) atomicAdd(dtable + (static_cast<int64_t>(c.head) * rows + dyi) * w2 + col, v);
+    dwin[e] = 0.0f;
+  }
+}
+
 template <int ROLE, int NCH, int CB, int BIAS>
-__device__ __forceinline__ void bwd_step(const Ctx<NCH>& c, const BwdCtx& bc,
-                                         const BwdTileBuf<ROLE, NCH, CB, BIAS>& cur,
+__device__ __forceinline__ void bwd_step(const Ctx<NCH>& c, const BwdCtx& bc, const BwdArgs& ba,
+                                         BwdTileBuf<ROLE, NCH, CB, BIAS>& cur,
                                          BwdTileBuf<ROLE, NCH, CB, BIAS>& nxt, int t, int nkt, KeyPos& kp,
-                                         const v8bf (&xop)[2 * CB], float lrow, float drow, BwdAcc<ROLE, CB>& acc) {
+                                         KeyPos& kprev, const v8bf (&xop)[2 * CB], float lrow, float drow,
+                                         BwdAcc<ROLE, CB>& acc) {
   const FwdArgs& a = *c.a;
   const KeyPos kn = next_keys(kp, a.gw);
   if (t + 1 < nkt) bwd_copy<ROLE, NCH, CB, BIAS>(c, bc, nxt, t + 1, kn);
+  // the previous tile's window sits in nxt (the copies do not touch it)
+  if (ROLE == kRoleQ && BIAS == kBiasRows && ba.dtable && t > 0) flush_dwin(c, nxt.dwin, kprev, ba.dtable);
+  const bool want_dt = ROLE == kRoleQ && ba.dtable != nullptr;
   if (BIAS == kBiasRows)  // as in pass_step
-    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, kp.k0 + 32 < a.N ? 2 : 1);
+    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, kp.k0 + 32 < a.N ? 2 : 1, want_dt);
   else if (kp.k0 + kBN <= a.N)
-    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2);
+    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2, want_dt);
   else
-    bwd_tile<ROLE, true, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2);
+    bwd_tile<ROLE, true, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2, want_dt);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  kprev = kp;
   kp = kn;
 }
 
@@ -1233,13 +1285,31 @@ attn_bwd_kernel(BwdArgs ba) {
   kp.kx[0] = 0;
   kp.ky[1] = (BIAS == kBiasRows && a.gw == 32) ? 1 : 0;
   kp.kx[1] = (BIAS == kBiasRows && a.gw == 32) ? 0 : 32;
+  // table-gradient accumulators start at zero
+  const int tsize = (2 * a.gh - 1) * (2 * a.gw - 1);
+  if (ROLE == kRoleQ && ba.dtable) {
+    if (BIAS == kBiasRows)
+      for (int e = c.tid; e < kMaxWindowFloats; e += kThreads) tb0.dwin[e] = tb1.dwin[e] = 0.0f;
+    if (BIAS == kBiasTable)
+      for (int e = c.tid; e < tsize; e += kThreads) c.table[tsize + e] = 0.0f;
+  }
   bwd_copy<ROLE, NCH, CB, BIAS>(c, bc, tb0, 0, kp);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int nkt = (a.N + kBN - 1) / kBN;
+  KeyPos kprev = kp;
   for (int t = 0; t < nkt; t += 2) {
-    bwd_step<ROLE, NCH, CB, BIAS>(c, bc, tb0, tb1, t, nkt, kp, xop, lrow, drow, acc);
-    if (t + 1 < nkt) bwd_step<ROLE, NCH, CB, BIAS>(c, bc, tb1, tb0, t + 1, nkt, kp, xop, lrow, drow, acc);
+    bwd_step<ROLE, NCH, CB, BIAS>(c, bc, ba, tb0, tb1, t, nkt, kp, kprev, xop, lrow, drow, acc);
+    if (t + 1 < nkt) bwd_step<ROLE, NCH, CB, BIAS>(c, bc, ba, tb1, tb0, t + 1, nkt, kp, kprev, xop, lrow, drow, acc);
+  }
+  if (ROLE == kRoleQ && ba.dtable) {
+    // the last tile's window (rows), or the whole table (table mode)
+    if (BIAS == kBiasRows) flush_dwin(c, (nkt & 1) ? tb0.dwin : tb1.dwin, kprev, ba.dtable);
+    if (BIAS == kBiasTable)
+      for (int e = c.tid; e < tsize; e += kThreads) {
+        const float v = c.table[tsize + e];
+        if (v != 0.0f) atomicAdd(ba.dtable + static_cast<int64_t>(c.head) * tsize + e, v);
+      }
   }
 
 #pragma unroll

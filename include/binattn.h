@@ -252,6 +252,36 @@ ba_status ba_attention_fwd_dense_bias_prepared(const void* q, const void* bias,
                                                const void* workspace, size_t ws_bytes,
                                                void* stream);
 
+/* Workspace bytes of ba_attention_bwd (0 for sizes it rejects; d must be
+ * 32, 64 or 128). */
+size_t ba_workspace_bytes_bwd(int64_t B, int64_t H, int64_t N, int d, int gh, int gw);
+
+/* ba_attention_bwd -- gradients of ba_attention_fwd for an output gradient
+ * dout (the loss L with dL/dO = dout).  The pages train BinaryAttention with
+ * quantization-aware training and self-distillation ("Entrenamiento y
+ * Optimizacion") but give no gradient for sign; here alpha = mean |x| takes
+ * its exact derivative sign(x)/d and sign the clipped straight-through
+ * estimator (derivative 1 where |x| <= 1, else 0):
+ *   dV = P^T dO,  dS = P * (dO V^T - rowsum(dO * O)),
+ *   dq~ = scale dS (alpha_k sign k),  dk~ = scale dS^T (alpha_q sign q),
+ *   dx = sign(x) <sign(x), dx~> / d + alpha_x 1{|x| <= 1} dx~   (x = q, k),
+ *   dtable[h, dy, dx] = sum over b and all (i, j) at that grid offset of dS.
+ *   q, k, v, dout  bf16 [B,H,N,d], contiguous; d in {32, 64, 128}
+ *   bias, gh, gw   as for ba_attention_fwd
+ *   dq, dk, dv     float32 [B,H,N,d] outputs
+ *   dtable         float32 [H, 2gh-1, 2gw-1] output, or NULL (it must be
+ *                  NULL without a bias table)
+ *   workspace      >= ba_workspace_bytes_bwd(B,H,N,d,gh,gw) bytes, 256-byte
+ *                  aligned
+ * The forward is recomputed inside (its O and row log2-sum-exp2 are kept in
+ * the workspace): five kernels are enqueued.  Errors: as ba_attention_fwd;
+ * BA_ERR_UNSUPPORTED for other d. */
+ba_status ba_attention_bwd(const void* q, const void* k, const void* v,
+                           const void* bias, int gh, int gw,
+                           int64_t B, int64_t H, int64_t N, int d, float scale,
+                           const void* dout, float* dq, float* dk, float* dv, float* dtable,
+                           void* workspace, size_t ws_bytes, void* stream);
+
 /* QK integer-dot routes for ba_qk_int_dot. */
 #define BA_ROUTE_MFMA_FP4 0 /* +/-1 in fp4 (e2m1) on the scaled f8f6f4 MFMA;
                                the route the fused kernel uses */

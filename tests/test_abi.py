@@ -298,3 +298,26 @@ def test_int8pv_validation(lib):
     need = lib.ba_workspace_bytes_int8pv(1, 2, 64, 64, 0, 0)
     assert need > lib.ba_workspace_bytes(1, 2, 64, 64, 0, 0) - 2 * 64 * 128 * 2
     assert call(ws_bytes=need - 1) == 5
+
+
+def test_bwd_validation(lib):
+    """ba_attention_bwd checks (nothing is launched)."""
+    assert lib.ba_workspace_bytes_bwd(1, 2, 64, 72, 0, 0) == 0           # d must be 32, 64 or 128
+    need = lib.ba_workspace_bytes_bwd(1, 2, 64, 64, 8, 8)
+    assert need > lib.ba_workspace_bytes(1, 2, 64, 64, 8, 8)
+
+    def call(**kw):
+        a = dict(q=A, k=A + GB, v=A + 2 * GB, bias=None, gh=0, gw=0, B=1, H=2, N=64, d=64, scale=0.125,
+                 do=A + 3 * GB, dq=A + 5 * GB, dk=A + 6 * GB, dv=A + 7 * GB, dt=None, ws=A + 4 * GB, wsb=16)
+        a.update(kw)
+        return lib.ba_attention_bwd(a["q"], a["k"], a["v"], a["bias"], a["gh"], a["gw"], a["B"], a["H"], a["N"],
+                                    a["d"], a["scale"], a["do"], a["dq"], a["dk"], a["dv"], a["dt"], a["ws"],
+                                    a["wsb"], None)
+    assert call(d=72) == 3
+    assert call(do=None) == 1
+    assert call(dq=A + 5 * GB + 4) == 4
+    assert call(scale=float("nan")) == 2
+    assert call() == 5                                                     # workspace too small
+    big = 1 << 40
+    assert call(dt=A + 8 * GB, wsb=big) == 2                               # dtable without a table
+    assert call(dk=A + 5 * GB + 64, wsb=big) == 2                          # dq and dk overlap

@@ -1,0 +1,84 @@
+"""GPU parity of ba_attention_bwd with the oracle's binary_attention_backward.
+
+Bar, per gradient tensor G: max |G_gpu - G_oracle| <= 1e-2 * max |G_oracle|.
+Derivation: the kernels round P, dS * alpha and the value / output rows to
+bf16 (relative 2^-9 each) before the matrix products, accumulate in fp32,
+and rebuild P from the forward's row sums of bf16 P (the forward's own
+normalisation, R3); the +/-1 sign operands and the straight-through
+decision |x| <= 1 are exact (bf16 inputs on both sides).  Each gradient
+entry is a sum of such rounded terms, so its error is a few 2^-9 of the
+sum of the magnitudes of its terms, which on these inputs stays below 0.5 %
+of the largest entry (measured 0.1-0.3 %); the table gradient sums dS over
+many pairs and lands lower (measured < 0.05 %)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_cases import announce, device, np32, to_dev
+
+pytestmark = pytest.mark.gpu
+
+bq = pytest.importorskip("bit_qk_quantisation_amd")
+
+TOL = 1e-2
+
+
+def run_case(B, H, gh, gw, d, seed, bias=True, q_scale=1.0):
+    N = gh * gw
+    inp = workloads.make_inputs(B, H, N, d, seed=seed, grid=(gh, gw) if bias else None, bias=bias,
+                                q_scale=q_scale)
+    rng = np.random.default_rng(seed + 1)
+    do = torch.from_numpy(rng.standard_normal((B, H, N, d)).astype(np.float32)).to(torch.bfloat16)
+    dev = to_dev(inp)
+    got = bq.attention_bwd(dev["q"], dev["k"], dev["v"], do.to(device()), dev["table"], inp["gh"], inp["gw"])
+    torch.cuda.synchronize()
+    ref = oracle.binary_attention_backward(np32(inp["q"]), np32(inp["k"]), np32(inp["v"]), np32(do),
+                                           np32(inp["table"]) if bias else None, inp["gh"], inp["gw"])
+    errs = {}
+    for name, g in zip(("dq", "dk", "dv", "dtable"), got):
+        if g is None:
+            assert ref[name] is None
+            continue
+        gg = g.cpu().numpy().astype(np.float64)
+        assert np.isfinite(gg).all(), name
+        errs[name] = float(np.abs(gg - ref[name]).max() / np.abs(ref[name]).max())
+    print("relative max errors:", errs)
+    for name, e in errs.items():
+        assert e <= TOL, (name, e)
+
+
+@pytest.mark.parametrize("B,H,gh,gw,d", [
+    (1, 1, 8, 8, 64),      # table mode
+    (2, 2, 7, 9, 32),      # table mode, N = 63 (ragged tile)
+    (1, 3, 14, 14, 64),    # the tiny ViT grid
+    (1, 2, 4, 32, 64),     # table rows
+    (2, 1, 3, 32, 32),     # table rows, N = 96: ragged tile, padded block skipped
+    (1, 1, 5, 13, 128),
+    (1, 1, 2, 64, 128),    # table rows, d = 128
+    (2, 2, 16, 64, 64),
+])
+def test_bwd_with_bias(B, H, gh, gw, d):
+    announce("bwd", B, H, gh, gw, d)
+    run_case(B, H, gh, gw, d, seed=6000 + gh * gw + d)
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 1, 64, 64), (2, 1, 100, 32), (1, 2, 130, 128)])
+def test_bwd_no_bias(B, H, N, d):
+    announce("bwd no bias", B, H, N, d)
+    run_case(B, H, 1, N, d, seed=6100 + N + d, bias=False)
+
+
+def test_bwd_large_logits():
+    """Queries scaled up: the forward takes its exact path, whose row maximum
+    enters the saved log2-sum-exp2."""
+    announce("bwd large logits")
+    run_case(1, 2, 4, 32, 64, seed=6201, q_scale=8.0)
+
+
+def test_bwd_full_length_64x64():
+    """N = 4096 on the 64x64 grid (the detection shape's sequence), one head."""
+    announce("bwd 64x64")
+    run_case(1, 1, 64, 64, 64, seed=6301)
