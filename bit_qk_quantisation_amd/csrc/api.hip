@@ -211,8 +211,19 @@ int fused_dynamic_lds(int static_lds, int table_lds, int64_t nwg) {
 // tile maxima, dO^T, the Q signs transposed, and the flipped bias rows.
 struct BwdLayout {
   Layout fwd;
-  int64_t kst, obuf, lse, delta, qop, alpha_q, qmax, dot, qst, bias4f, rowmaxf, total;
+  int64_t kst, obuf, lse, delta, qop, alpha_q, qmax, dot, qst, bias4f, rowmaxf, dtpart, total;
+  int prow;  // rows of one workgroup's share of the table gradient
 };
+
+// Largest number of grid rows, minus one, that a 128-query tile spans.
+int query_span(int64_t N, int gw) {
+  int qspan = 0;
+  for (int64_t q0 = 0; q0 < round_up(N, ba::kNAlign); q0 += ba::kBM) {
+    const int sp = static_cast<int>((q0 + ba::kBM - 1) / gw - q0 / gw);
+    if (sp > qspan) qspan = sp;
+  }
+  return qspan;
+}
 
 BwdLayout bwd_layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int gw) {
   BwdLayout L{};
@@ -236,6 +247,10 @@ BwdLayout bwd_layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int 
   const bool rows = L.fwd.mode == ba::kBiasRows;
   L.bias4f = take(rows ? H * (2 * gh - 1 + 2 * ba::kBiasPadRows) * 4 * L.fwd.Lpad * 4 : 0);
   L.rowmaxf = take(rows ? H * (2 * gh - 1) * 4 : 0);
+  // the shares of the table gradient: table rows yq_lo .. yq_hi + gh - 1 of
+  // each query tile (table-row mode), or the whole table (table mode)
+  L.prow = rows ? gh + query_span(N, gw) : (has_bias ? 2 * gh - 1 : 0);
+  L.dtpart = take(has_bias ? BH * (Npad / ba::kBM) * L.prow * (2 * static_cast<int64_t>(gw) - 1) * 4 : 0);
   L.total = off;
   return L;
 }
@@ -630,7 +645,6 @@ ba_status ba_attention_bwd(const void* q, const void* k, const void* v, const vo
   if (dtable && !bias) return fail(BA_ERR_SHAPE, "dtable needs a bias table");
   if (dtable && overlaps(dtable, tcount * 4, workspace, BL.total))
     return fail(BA_ERR_WORKSPACE, "dtable overlaps the workspace");
-  (void)tcount;
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   uint16_t* obuf = reinterpret_cast<uint16_t*>(ws + BL.obuf);
@@ -666,9 +680,12 @@ ba_status ba_attention_bwd(const void* q, const void* k, const void* v, const vo
   p3.kv.vs = contiguous_strides(H, N, d);
   p3.kv_blocks = p1.kv_blocks;
   p3.lds = p1.lds;
+  // 6. the table gradient: the sum of the query role's per-workgroup shares
+  ba::PrologueArgs p6{};
   if (dtable) {
-    p3.fill = ba::FillJob{dtable, tcount};
-    p3.fill_blocks = (tcount + ba::kThreads * 4 - 1) / (ba::kThreads * 4);
+    p6.dtr = ba::DtReduceJob{reinterpret_cast<const float*>(ws + BL.dtpart), dtable, static_cast<int>(B),
+                             static_cast<int>(H), fp.f.nqt, gh, gw, BL.prow, mode == ba::kBiasRows ? 1 : 0};
+    p6.dtr_blocks = (tcount + ba::kThreads - 1) / ba::kThreads;
   }
   // 4. query role: dq (and delta, the table gradient)
   ba::BwdArgs bq{};
@@ -681,6 +698,8 @@ ba_status ba_attention_bwd(const void* q, const void* k, const void* v, const vo
   bq.delta = delta;
   bq.out1 = dq;
   bq.dtable = dtable;
+  bq.dtpart = reinterpret_cast<float*>(ws + BL.dtpart);
+  bq.prow = BL.prow;
   bq.scale = scale;
   // 5. key role: dk, dv; queries and keys exchanged, the bias flipped
   ba::BwdArgs bk = bq;
@@ -715,6 +734,7 @@ ba_status ba_attention_bwd(const void* q, const void* k, const void* v, const vo
   if (err == 0) err = ba::launch_attention(f, mode, stream);
   if (err == 0) err = ba::launch_prologue(p3, stream);
   if (err == 0) err = ba::launch_backward(bq, ba::kRoleQ, mode, stream);
+  if (err == 0 && dtable) err = ba::launch_prologue(p6, stream);
   if (err == 0) err = ba::launch_backward(bk, ba::kRoleKV, mode, stream);
   if (err != 0) return hip_fail(err, "backward launch");
   return BA_OK;

@@ -1046,15 +1046,69 @@ struct BwdAcc {
   v16f a2[ROLE == kRoleKV ? CB : 1];   // dv (kRoleKV)
 };
 
-// The table gradient (kRoleQ, want_dt): every dS_ij is added in LDS at the
-// table entry of its grid offset, with ds_add_f32 (the lanes of one
-// instruction hold consecutive queries, so the addresses are consecutive):
-// in table-row mode into this tile's window tb.dwin, in table mode into a
-// copy of the whole table that follows it in dynamic LDS.
+// Diagonal sums of one 32x32 block of dS in the MFMA result layout (lane
+// l = 32 lh + li holds query li; register r = 4 g + i holds key
+// j = 8 g + 4 lh + i).  Returns, in lane t, the sum of dS[li][j] over
+// li - j = t - 32 (lane 0, diagonal -32, is always 0).
+//
+// Write li = 16 qh + L (qh: the lane's row of 16 within its half) and
+// j = 16 kh + 8 (g & 1) + 4 lh + i.  Shifting register r left inside the
+// 16-lane rows by s = 8 (g & 1) + i brings the keys of one diagonal into one
+// lane: lane L then holds diagonal 16 (qh - kh) + L - 4 lh, and the values
+// that leave the row (shifted the other way, by 16 - s) diagonal
+// 16 (qh - kh - 1) + L - 4 lh.  So three accumulators a[e], e = kh or kh + 1,
+// each hold diagonal 16 (qh - e) + L - 4 lh in lane L.  The upper half is
+// then moved 4 lanes down (what leaves its rows goes to a[e + 1]; a[2]'s
+// lanes 0..3 there are empty), after which a[e] in rows (lh, qh) belongs to
+// output row qh - e + 2 in both halves, and two lane-half swaps and one row
+// swap put every partial sum in its lane.
+__device__ __forceinline__ float diagonal_sums(const float (&x)[16]) {
+  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f;
+#define BA_DIAG_STEP(R, S, LO, HI)                 \
+  LO += row_shl_c<S>(0.0f, x[R]);                  \
+  HI += row_shr_c<16 - S>(0.0f, x[R]);
+  a0 += x[0];
+  BA_DIAG_STEP(1, 1, a0, a1)
+  BA_DIAG_STEP(2, 2, a0, a1)
+  BA_DIAG_STEP(3, 3, a0, a1)
+  BA_DIAG_STEP(4, 8, a0, a1)
+  BA_DIAG_STEP(5, 9, a0, a1)
+  BA_DIAG_STEP(6, 10, a0, a1)
+  BA_DIAG_STEP(7, 11, a0, a1)
+  a1 += x[8];
+  BA_DIAG_STEP(9, 1, a1, a2)
+  BA_DIAG_STEP(10, 2, a1, a2)
+  BA_DIAG_STEP(11, 3, a1, a2)
+  BA_DIAG_STEP(12, 8, a1, a2)
+  BA_DIAG_STEP(13, 9, a1, a2)
+  BA_DIAG_STEP(14, 10, a1, a2)
+  BA_DIAG_STEP(15, 11, a1, a2)
+#undef BA_DIAG_STEP
+  // upper half (rows 2, 3): 4 lanes down, the overflow into the next e
+  a2 = row_shl_c<4, 0xC>(a2, a2) + row_shr_c<12, 0xC>(0.0f, a1);
+  a1 = row_shl_c<4, 0xC>(a1, a1) + row_shr_c<12, 0xC>(0.0f, a0);
+  a0 = row_shl_c<4, 0xC>(a0, a0);
+  // e = 2 to output rows 0, 1 and e = 0 to rows 2, 3 (sums of both halves)
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a2), __float_as_uint(a0), false, false);
+  const float u = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  // e = 1: rows (qh = 0) to output row 1, (qh = 1) to output row 2
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(a1), __float_as_uint(a1), false, false);
+  const auto r = __builtin_amdgcn_permlane32_swap(q[0], q[1], false, false);
+  return u + rows_only<0x6>(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+// The table gradient (kRoleQ, want_dt).  Table-row mode: a wave's 32 queries
+// and a block's 32 keys each lie in one grid row, so the block adds its 63
+// diagonal sums (diagonal_sums) to consecutive entries of one row of this
+// wave's window; dsk/dbase keep the sums and the window position, and
+// bwd_step adds them once the tile's copies have landed.  Table mode: every
+// dS_ij is added with ds_add_f32 at the entry of its grid offset in a copy of
+// the whole table that follows the table in dynamic LDS.
 template <int ROLE, bool MASK, int NCH, int CB, int BIAS>
 __device__ __forceinline__ void bwd_tile(const Ctx<NCH>& c, BwdTileBuf<ROLE, NCH, CB, BIAS>& tb,
                                          const KeyPos& kp, const v8bf (&xop)[2 * CB], float lrow, float drow,
-                                         BwdAcc<ROLE, CB>& acc, int nblk, bool want_dt) {
+                                         BwdAcc<ROLE, CB>& acc, int nblk, bool want_dt, float (&dsk)[2],
+                                         int (&dbase)[2]) {
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     if (blk >= nblk) break;  // uniform: the padded block of a ragged table-row tile
@@ -1098,13 +1152,11 @@ __device__ __forceinline__ void bwd_tile(const Ctx<NCH>& c, BwdTileBuf<ROLE, NCH
       dsv[r + 1] = d1;
     }
     if (ROLE == kRoleQ && BIAS == kBiasRows && want_dt) {
-      // keys of the block: grid row ky[blk], columns kx[blk] + 8 g + 4 lh + i
+      // window row ky[1] - ky[blk]; diagonal 0 (query column xq - li, key
+      // column kx[blk]) at column xq - li - kx[blk] + gw - 1
       const FwdArgs& a = *c.a;
-      const int w2 = 2 * a.gw - 1;
-      const int row = (c.yq - c.yq_lo) + (kp.ky[1] - kp.ky[blk]);
-      float* base = tb.dwin + row * w2 + (c.xq - kp.kx[blk] + a.gw - 1) - 4 * c.lh;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) atomicAdd(base - (8 * (r >> 2) + (r & 3)), dsv[r]);
+      dbase[blk] = (kp.ky[1] - kp.ky[blk]) * (2 * a.gw - 1) + (c.xq - c.li - kp.kx[blk] + a.gw - 1);
+      dsk[blk] = diagonal_sums(dsv);
     }
     if (ROLE == kRoleQ && BIAS == kBiasTable && want_dt) {
       const FwdArgs& a = *c.a;
@@ -1140,18 +1192,38 @@ __device__ __forceinline__ void bwd_tile(const Ctx<NCH>& c, BwdTileBuf<ROLE, NCH
   }
 }
 
-// Adds a tile's table-gradient window to the global table gradient (one
-// atomic per nonzero entry) and clears it.  kp: that tile's key position.
+// Table-row mode: each wave owns kWaveWindow floats of the tile's window
+// buffer, two rows of 2gw - 1 entries (the rows ky[1] and ky[1] - 1 of the
+// tile's keys, against the wave's one query row).
+constexpr int kWaveWindow = kMaxWindowFloats / 4;
+
+// Adds a tile's four wave windows into this workgroup's share of the table
+// gradient (no other workgroup touches it: plain loads and stores, ordered by
+// the tile barriers) and clears them.  kp: that tile's key position.  Entry
+// (row, col) of the workgroup's window, row = (yq - yq_lo) + (ky[1] - yk),
+// sums row row - (yq - yq_lo) of every wave window that has it; it belongs
+// to share row gh - 1 - ky[1] + row.
 template <int NCH>
-__device__ __forceinline__ void flush_dwin(const Ctx<NCH>& c, float* dwin, const KeyPos& kp, float* dtable) {
+__device__ __forceinline__ void flush_dwin(const Ctx<NCH>& c, float* dwin, const KeyPos& kp, float* share, int prow) {
   const FwdArgs& a = *c.a;
-  const int w2 = 2 * a.gw - 1, rows = 2 * a.gh - 1;
-  const int dy0 = c.yq_lo - kp.ky[1] + a.gh - 1;  // table row of window row 0
+  const int w2 = 2 * a.gw - 1;
+  const int r0 = a.gh - 1 - kp.ky[1];  // share row of window row 0
+  int wrow[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) wrow[w] = (c.q0 + 32 * w) / a.gw - c.yq_lo;
   for (int e = c.tid; e < a.win_rows * w2; e += kThreads) {
-    const int r = e / w2, col = e - r * w2, dyi = dy0 + r;
-    const float v = dwin[e];
-    if (v != 0.0f && dyi >= 0 && dyi < rows) atomicAdd(dtable + (static_cast<int64_t>(c.head) * rows + dyi) * w2 + col, v);
-    dwin[e] = 0.0f;
+    const int rw = e / w2, col = e - rw * w2, r = r0 + rw;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int rr = rw - wrow[w];
+      if (rr == 0 || rr == 1) {
+        float* p = dwin + w * kWaveWindow + rr * w2 + col;
+        v += *p;
+        *p = 0.0f;
+      }
+    }
+    if (v != 0.0f && r >= 0 && r < prow) share[r * w2 + col] += v;
   }
 }
 
@@ -1160,20 +1232,34 @@ __device__ __forceinline__ void bwd_step(const Ctx<NCH>& c, const BwdCtx& bc, co
                                          BwdTileBuf<ROLE, NCH, CB, BIAS>& cur,
                                          BwdTileBuf<ROLE, NCH, CB, BIAS>& nxt, int t, int nkt, KeyPos& kp,
                                          KeyPos& kprev, const v8bf (&xop)[2 * CB], float lrow, float drow,
-                                         BwdAcc<ROLE, CB>& acc) {
+                                         BwdAcc<ROLE, CB>& acc, float* share) {
   const FwdArgs& a = *c.a;
   const KeyPos kn = next_keys(kp, a.gw);
+  // the previous tile's window sits in nxt; it is added to the share before
+  // the next copies into nxt start (no copy is in flight here)
+  if (ROLE == kRoleQ && BIAS == kBiasRows && ba.dtable && t > 0) flush_dwin(c, nxt.dwin, kprev, share, ba.prow);
   if (t + 1 < nkt) bwd_copy<ROLE, NCH, CB, BIAS>(c, bc, nxt, t + 1, kn);
-  // the previous tile's window sits in nxt (the copies do not touch it)
-  if (ROLE == kRoleQ && BIAS == kBiasRows && ba.dtable && t > 0) flush_dwin(c, nxt.dwin, kprev, ba.dtable);
   const bool want_dt = ROLE == kRoleQ && ba.dtable != nullptr;
+  float dsk[2] = {0.0f, 0.0f};
+  int dbase[2] = {0, 0};
+  const int nb = BIAS == kBiasRows ? (kp.k0 + 32 < a.N ? 2 : 1) : 2;
   if (BIAS == kBiasRows)  // as in pass_step
-    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, kp.k0 + 32 < a.N ? 2 : 1, want_dt);
+    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, nb, want_dt, dsk, dbase);
   else if (kp.k0 + kBN <= a.N)
-    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2, want_dt);
+    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2, want_dt, dsk, dbase);
   else
-    bwd_tile<ROLE, true, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2, want_dt);
+    bwd_tile<ROLE, true, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2, want_dt, dsk, dbase);
   __builtin_amdgcn_s_waitcnt(0);
+  if (ROLE == kRoleQ && BIAS == kBiasRows && want_dt && c.lane != 0) {
+    // lane t: diagonal t - 32 (lane 0 holds the empty diagonal -32); the
+    // wave's own window, so plain read-modify-writes in program order
+    float* wwin = cur.dwin + c.wave * kWaveWindow + c.lane - 32;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      if (blk >= nb) break;
+      wwin[dbase[blk]] += dsk[blk];
+    }
+  }
   __syncthreads();
   kprev = kp;
   kp = kn;
@@ -1285,11 +1371,16 @@ attn_bwd_kernel(BwdArgs ba) {
   kp.kx[0] = 0;
   kp.ky[1] = (BIAS == kBiasRows && a.gw == 32) ? 1 : 0;
   kp.kx[1] = (BIAS == kBiasRows && a.gw == 32) ? 0 : 32;
-  // table-gradient accumulators start at zero
+  // table-gradient accumulators start at zero; this workgroup's share of
+  // the table gradient (table rows: cleared here, added to per tile)
   const int tsize = (2 * a.gh - 1) * (2 * a.gw - 1);
+  float* share = nullptr;
   if (ROLE == kRoleQ && ba.dtable) {
-    if (BIAS == kBiasRows)
+    share = ba.dtpart + (static_cast<int64_t>(c.bh) * a.nqt + c.q0 / kBM) * ba.prow * (2 * a.gw - 1);
+    if (BIAS == kBiasRows) {
       for (int e = c.tid; e < kMaxWindowFloats; e += kThreads) tb0.dwin[e] = tb1.dwin[e] = 0.0f;
+      for (int e = c.tid; e < ba.prow * (2 * a.gw - 1); e += kThreads) share[e] = 0.0f;
+    }
     if (BIAS == kBiasTable)
       for (int e = c.tid; e < tsize; e += kThreads) c.table[tsize + e] = 0.0f;
   }
@@ -1299,17 +1390,15 @@ attn_bwd_kernel(BwdArgs ba) {
   const int nkt = (a.N + kBN - 1) / kBN;
   KeyPos kprev = kp;
   for (int t = 0; t < nkt; t += 2) {
-    bwd_step<ROLE, NCH, CB, BIAS>(c, bc, ba, tb0, tb1, t, nkt, kp, kprev, xop, lrow, drow, acc);
-    if (t + 1 < nkt) bwd_step<ROLE, NCH, CB, BIAS>(c, bc, ba, tb1, tb0, t + 1, nkt, kp, kprev, xop, lrow, drow, acc);
+    bwd_step<ROLE, NCH, CB, BIAS>(c, bc, ba, tb0, tb1, t, nkt, kp, kprev, xop, lrow, drow, acc, share);
+    if (t + 1 < nkt)
+      bwd_step<ROLE, NCH, CB, BIAS>(c, bc, ba, tb1, tb0, t + 1, nkt, kp, kprev, xop, lrow, drow, acc, share);
   }
   if (ROLE == kRoleQ && ba.dtable) {
     // the last tile's window (rows), or the whole table (table mode)
-    if (BIAS == kBiasRows) flush_dwin(c, (nkt & 1) ? tb0.dwin : tb1.dwin, kprev, ba.dtable);
+    if (BIAS == kBiasRows) flush_dwin(c, (nkt & 1) ? tb0.dwin : tb1.dwin, kprev, share, ba.prow);
     if (BIAS == kBiasTable)
-      for (int e = c.tid; e < tsize; e += kThreads) {
-        const float v = c.table[tsize + e];
-        if (v != 0.0f) atomicAdd(ba.dtable + static_cast<int64_t>(c.head) * tsize + e, v);
-      }
+      for (int e = c.tid; e < tsize; e += kThreads) share[e] = c.table[tsize + e];
   }
 
 #pragma unroll
@@ -1382,6 +1471,11 @@ static int launch_bwd_nc(const BwdArgs& a, int mode, void* stream) {
 
 int launch_backward(const BwdArgs& a, int role, int mode, void* stream) {
   const int cb = a.f.dpad / 32;
+  // the table gradient's wave windows hold two rows of 2gw - 1 entries
+  // whenever a key tile spans two grid rows (window of two rows or more)
+  if (role == kRoleQ && mode == kBiasRows && a.dtable &&
+      (a.f.win_rows > 1 ? 2 : 1) * (2 * a.f.gw - 1) > kWaveWindow)
+    return static_cast<int>(hipErrorInvalidValue);
   if (role == kRoleQ) {
     switch (cb) {
       case 1: return launch_bwd_nc<kRoleQ, 1, 1>(a, mode, stream);

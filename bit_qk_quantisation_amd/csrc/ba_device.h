@@ -134,6 +134,24 @@ __device__ __forceinline__ float row_bcast(float x, int n) {
   }
 }
 
+// DPP shifts inside each row of 16 lanes, zero where the source lane falls
+// outside the row: row_shl:N gives lane l the value of lane l + N, row_shr:N
+// that of lane l - N.  ROWS selects the rows that take the result; the other
+// rows keep `old`.
+template <int N, int ROWS = 0xF>
+__device__ __forceinline__ float row_shl_c(float old, float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), 0x100 + N, ROWS, 0xF, true));
+}
+template <int N, int ROWS = 0xF>
+__device__ __forceinline__ float row_shr_c(float old, float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), 0x110 + N, ROWS, 0xF, true));
+}
+// x in the rows ROWS selects, 0 in the others.
+template <int ROWS>
+__device__ __forceinline__ float rows_only(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xE4, ROWS, 0xF, true));
+}
+
 // Cross-half reductions for the 32x32 layout: lanes l and l^32 hold the two
 // halves of one query's keys.  v_permlane32_swap of x with itself leaves
 // (lower, lower) in r[0] and (upper, upper) in r[1], so r[0] op r[1] is the

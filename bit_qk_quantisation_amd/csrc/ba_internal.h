@@ -98,6 +98,16 @@ struct FillJob {
   int64_t n;
 };
 
+// Sums the workgroups' shares of the table gradient (see BwdArgs::dtpart):
+// dtable[h][dyi][dx] = sum over b and query tiles qt of
+// share[(b H + h) nqt + qt][dyi - row0(qt)][dx], row0 = (128 qt) / gw in
+// table-row mode, 0 in table mode.  One thread per table entry.
+struct DtReduceJob {
+  const float* part;
+  float* dtable;
+  int B, H, nqt, gh, gw, prow, rows_mode;
+};
+
 // One launch runs the blocks of every job present (a job with 0 blocks is
 // absent): the pack blocks first, then the key/value tiles, then the bias rows.
 struct PrologueArgs {
@@ -113,6 +123,8 @@ struct PrologueArgs {
   int64_t bias2_blocks;
   FillJob fill;
   int64_t fill_blocks;
+  DtReduceJob dtr;
+  int64_t dtr_blocks;
   int lds;  // dynamic LDS bytes per block
 };
 
@@ -191,7 +203,11 @@ struct BwdArgs {
   float* delta;            // [BH][Npad] <dO_i, O_i> (written by kRoleQ)
   float* out1;             // [BH][N][d] float32: dq (kRoleQ) or dk (kRoleKV)
   float* out2;             // kRoleKV: [BH][N][d] float32 dv
-  float* dtable;           // kRoleQ: [H][2gh-1][2gw-1] float32 accumulated (nullptr: skipped)
+  float* dtable;           // kRoleQ: nullptr = no table gradient, else non-null (see dtpart)
+  float* dtpart;           // kRoleQ: each workgroup's share of the table gradient,
+                           // [B*H*nqt][prow][2gw-1]: rows dy from yq_lo - gh + 1
+                           // (table rows) or the whole table (table mode, prow = 2gh-1)
+  int prow;                // rows of one share
   float scale;             // the softmax scale
 };
 int bwd_static_lds(int role, int dpad, int mode);

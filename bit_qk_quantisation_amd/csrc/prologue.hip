@@ -395,6 +395,26 @@ __global__ void __launch_bounds__(kThreads) prologue_kernel(PrologueArgs a) {
     return;
   }
   blk -= a.bias2_blocks;
+  if (blk < a.dtr_blocks) {
+    const DtReduceJob& j = a.dtr;
+    const int w2 = 2 * j.gw - 1, rows = 2 * j.gh - 1;
+    const int64_t e = blk * kThreads + threadIdx.x;
+    if (e < static_cast<int64_t>(j.H) * rows * w2) {
+      const int h = static_cast<int>(e / (rows * w2));
+      const int rem = static_cast<int>(e - static_cast<int64_t>(h) * rows * w2);
+      const int dyi = rem / w2, col = rem - dyi * w2;
+      float acc = 0.0f;
+      for (int b = 0; b < j.B; ++b)
+        for (int qt = 0; qt < j.nqt; ++qt) {
+          const int r = dyi - (j.rows_mode ? (128 * qt) / j.gw : 0);
+          if (r >= 0 && r < j.prow)
+            acc += j.part[((static_cast<int64_t>(b) * j.H + h) * j.nqt + qt) * j.prow * w2 + r * w2 + col];
+        }
+      j.dtable[e] = acc;
+    }
+    return;
+  }
+  blk -= a.dtr_blocks;
   if (blk < a.fill_blocks) {
     const int64_t i0 = blk * kThreads * 4;
     for (int e = 0; e < 4; ++e) {
@@ -405,8 +425,8 @@ __global__ void __launch_bounds__(kThreads) prologue_kernel(PrologueArgs a) {
 }
 
 int launch_prologue(const PrologueArgs& a, void* stream) {
-  const int64_t blocks =
-      a.pack_blocks + a.kv_blocks + a.bias_blocks + a.vstat_blocks + a.bias2_blocks + a.fill_blocks;
+  const int64_t blocks = a.pack_blocks + a.kv_blocks + a.bias_blocks + a.vstat_blocks + a.bias2_blocks +
+                        a.dtr_blocks + a.fill_blocks;
   hipLaunchKernelGGL(prologue_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), a.lds,
                      static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());

@@ -274,7 +274,9 @@ size_t ba_workspace_bytes_bwd(int64_t B, int64_t H, int64_t N, int d, int gh, in
  *   workspace      >= ba_workspace_bytes_bwd(B,H,N,d,gh,gw) bytes, 256-byte
  *                  aligned
  * The forward is recomputed inside (its O and row log2-sum-exp2 are kept in
- * the workspace): five kernels are enqueued.  Errors: as ba_attention_fwd;
+ * the workspace): five kernels are enqueued, six with dtable.  dtable is
+ * reduced from per-workgroup shares in a fixed order (no atomics), so it is
+ * the same from run to run.  Errors: as ba_attention_fwd;
  * BA_ERR_UNSUPPORTED for other d. */
 ba_status ba_attention_bwd(const void* q, const void* k, const void* v,
                            const void* bias, int gh, int gw,
