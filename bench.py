@@ -27,8 +27,8 @@ kernel is closer to.
 kernels in one call), so only the whole step is timed; its roofline takes the
 fp4 QK + int8 P.V matrix-core bound.
 
---bwd times the backward instead (ba_attention_bwd: five kernels in one call,
-the forward recomputed inside), counted as 10*B*H*N^2*d FLOP-eq per step (the
+--bwd times the backward instead (ba_attention_bwd: six kernels in one call
+with the table gradient, the forward recomputed inside), counted as 10*B*H*N^2*d FLOP-eq per step (the
 products S, dP, dV, dQ and dK of a flash-attention backward); its roofline
 takes the fp4 + bf16 matrix-core bound of those products (S on fp4, the
 other four on bf16).
@@ -401,7 +401,7 @@ def main() -> int:
         "roofline": {
             "bound": "mfma",
             "kernel": ("attn_fwd_kernel (fused)" if split else
-                       "whole backward (5 kernels, one call; forward recomputed)" if args.bwd else
+                       "whole backward (6 kernels, one call; forward recomputed)" if args.bwd else
                        "whole step (3 kernels, one call; fp4 QK + int8 P.V bound)" if args.pv == "int8" else
                        "whole step (prologue + fused, one strided call)"),
             "achieved": round(fused_tf, 1),

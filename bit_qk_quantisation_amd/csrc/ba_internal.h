@@ -92,12 +92,6 @@ struct BiasJob {
                           // bias seen with queries and keys exchanged)
 };
 
-// Sets n floats to zero (the accumulators of the backward pass).
-struct FillJob {
-  float* x;
-  int64_t n;
-};
-
 // Sums the workgroups' shares of the table gradient (see BwdArgs::dtpart):
 // dtable[h][dyi][dx] = sum over b and query tiles qt of
 // share[(b H + h) nqt + qt][dyi - row0(qt)][dx], row0 = (128 qt) / gw in
@@ -109,7 +103,8 @@ struct DtReduceJob {
 };
 
 // One launch runs the blocks of every job present (a job with 0 blocks is
-// absent): the pack blocks first, then the key/value tiles, then the bias rows.
+// absent), in this order: pack, key/value tiles, bias rows, value
+// statistics, the second bias rows, the table-gradient reduction.
 struct PrologueArgs {
   PackJob pack;
   int64_t pack_blocks;
@@ -121,8 +116,6 @@ struct PrologueArgs {
   int64_t vstat_blocks;
   BiasJob bias2;          // a second bias-row job (the flipped rows of the backward)
   int64_t bias2_blocks;
-  FillJob fill;
-  int64_t fill_blocks;
   DtReduceJob dtr;
   int64_t dtr_blocks;
   int lds;  // dynamic LDS bytes per block

@@ -412,21 +412,12 @@ __global__ void __launch_bounds__(kThreads) prologue_kernel(PrologueArgs a) {
         }
       j.dtable[e] = acc;
     }
-    return;
-  }
-  blk -= a.dtr_blocks;
-  if (blk < a.fill_blocks) {
-    const int64_t i0 = blk * kThreads * 4;
-    for (int e = 0; e < 4; ++e) {
-      const int64_t i = i0 + e * kThreads + threadIdx.x;
-      if (i < a.fill.n) a.fill.x[i] = 0.0f;
-    }
   }
 }
 
 int launch_prologue(const PrologueArgs& a, void* stream) {
   const int64_t blocks = a.pack_blocks + a.kv_blocks + a.bias_blocks + a.vstat_blocks + a.bias2_blocks +
-                        a.dtr_blocks + a.fill_blocks;
+                        a.dtr_blocks;
   hipLaunchKernelGGL(prologue_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), a.lds,
                      static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());
