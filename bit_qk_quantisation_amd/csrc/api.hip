@@ -74,7 +74,7 @@ int64_t row_pad(int gw) {
 int choose_mode(bool has_bias, int gh, int gw, int64_t N) {
   if (!has_bias) return ba::kBiasNone;
   if (gw % 32 == 0 && window_rows(N, gw) > 0 && window_rows(N, gw) <= ba::kBiasPadRows &&
-      window_rows(N, gw) * 4 * row_pad(gw) <= ba::kMaxWindowFloats)
+      window_rows(N, gw) * 4 * row_pad(gw) <= ba::kMaxWindowFloats && row_pad(gw) <= 64 * ba::kBiasPieces)
     return ba::kBiasRows;
   if (static_cast<int64_t>(2 * gh - 1) * (2 * gw - 1) * 4 <= 48 * 1024) return ba::kBiasTable;
   return -1;
@@ -492,9 +492,10 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   plan->p0 = ba::PrologueArgs{};
   ba::PrologueArgs& pb = int8pv ? plan->p0 : p;
   if (mode == ba::kBiasRows) {
+    const int64_t nrows = H * (2 * gh - 1 + 2 * ba::kBiasPadRows);
     pb.bias = ba::BiasJob{static_cast<const uint16_t*>(bias), const_cast<float*>(f.bias4),
-                          const_cast<float*>(f.bias_row_max), gh, gw, f.Lpad};
-    pb.bias_blocks = H * (2 * gh - 1 + 2 * ba::kBiasPadRows);
+                          const_cast<float*>(f.bias_row_max), gh, gw, f.Lpad, 0, nrows};
+    pb.bias_blocks = (nrows + ba::kBiasRowsPerBlock - 1) / ba::kBiasRowsPerBlock;
   }
   if (int8pv) {
     float* vpart = reinterpret_cast<float*>(ws + L.vpart);

@@ -83,6 +83,12 @@ struct VstatJob {
   int H, N, Npad, d, dpad;
 };
 
+// Rows of the padded bias table one prologue block writes (one wave per
+// row), and the 16-byte pieces per lane that cover a row: Lpad <= 320 floats
+// (row mode has gw <= 128 in practice: 2gw-1+3 rounded to 16 mod 64 is 272).
+constexpr int kBiasRowsPerBlock = 4;
+constexpr int kBiasPieces = 5;
+
 struct BiasJob {
   const uint16_t* table;  // bf16 [H][2gh-1][2gw-1]
   float* bias4;           // [H][2gh-1+2*kBiasPadRows][4][Lpad]
@@ -90,6 +96,7 @@ struct BiasJob {
   int gh, gw, Lpad;
   int flip;               // 1: rows of the table flipped in both axes (the
                           // bias seen with queries and keys exchanged)
+  int64_t nrows;          // H * (2gh-1+2*kBiasPadRows) padded rows
 };
 
 // Sums the workgroups' shares of the table gradient (see BwdArgs::dtpart):

@@ -327,44 +327,54 @@ __device__ void vstat_block(const VstatJob& job, int64_t blk, unsigned char* sme
 }
 
 // ---------------------------------------------------------------- bias ----
-// One block = one row of the padded table: rows kBiasPadRows..kBiasPadRows +
-// 2gh-2 hold the table rows dy = 0..2gh-2; the kBiasPadRows rows on each side
-// are -inf (the fused kernel's windows reach them only for padded tokens).  Each row is 4 shifted copies of Lpad floats:
+// One wave per row of the padded table, four rows per block:
+// rows kBiasPadRows..kBiasPadRows + 2gh-2 hold the table rows dy = 0..2gh-2;
+// the kBiasPadRows rows on each side are -inf (the fused kernel's windows
+// reach them only for padded tokens).  Each row is 4 shifted copies of Lpad
+// floats:
 // R[u] = log2e * T[h, dy, 2gw-2-u] for 0 <= u <= 2gw-2 (else 0), and copy s
 // holds C_s[v] = R[v+s].
 __device__ void bias_block(const BiasJob& job, int64_t blk) {
   const int rows = 2 * job.gh - 1, cols = 2 * job.gw - 1;
   const int prow = rows + 2 * kBiasPadRows;
-  const int64_t h = blk / prow;
-  const int dyp = static_cast<int>(blk - h * prow), dy = dyp - kBiasPadRows;
+  const int lane = threadIdx.x & 63;
+  // one wave per padded row; padded row `row` = h * prow + dyp
+  const int64_t row = blk * kBiasRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= job.nrows) return;  // uniform in the wave; no barrier follows
+  const int64_t h = row / prow;
+  const int dyp = static_cast<int>(row - h * prow), dy = dyp - kBiasPadRows;
   const bool inside = dy >= 0 && dy < rows;
   // flipped: T'[dy][x] = T[rows-1-dy][cols-1-x]
   const uint16_t* trow = job.table + (h * rows + (inside ? (job.flip ? rows - 1 - dy : dy) : 0)) * cols;
-  float* out = job.bias4 + (h * prow + dyp) * 4 * static_cast<int64_t>(job.Lpad);
+  float4* out = reinterpret_cast<float4*>(job.bias4 + row * 4 * static_cast<int64_t>(job.Lpad));
+  // Every table entry of the lane's 16-byte pieces is loaded before any
+  // piece is stored.  Lpad % 4 == 0: the four floats of a piece lie in one
+  // copy s.
+  float val[kBiasPieces][4];
   float m = 0.0f;
-  for (int e = threadIdx.x; e < 4 * job.Lpad; e += blockDim.x) {
-    const int s = e / job.Lpad, v = e - s * job.Lpad;
-    const int u = v + s;
-    // Padding rows are -inf: the only (query, key) pairs that reach them
-    // involve a padded token.  They keep the fused kernel's window reads
-    // inside the rows; that kernel masks padded keys itself, since a padded
-    // key seen from a query on grid row >= 1 falls on a real row.
-    float val = inside ? 0.0f : -INFINITY;
-    if (inside && u <= cols - 1) val = kLog2e * bf16_to_f32(trow[job.flip ? u : cols - 1 - u]);
-    out[e] = val;
-    if (inside) m = fmaxf(m, fabsf(val));
+#pragma unroll
+  for (int i = 0; i < kBiasPieces; ++i) {
+    const int e = 4 * (lane + 64 * i), s = e / job.Lpad, v = e - s * job.Lpad;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int u = v + t + s;
+      // Padding rows are -inf: the only (query, key) pairs that reach them
+      // involve a padded token.  They keep the fused kernel's window reads
+      // inside the rows; that kernel masks padded keys itself, since a
+      // padded key seen from a query on grid row >= 1 falls on a real row.
+      val[i][t] = inside ? 0.0f : -INFINITY;
+      if (inside && e < 4 * job.Lpad && u <= cols - 1)
+        val[i][t] = kLog2e * bf16_to_f32(trow[job.flip ? u : cols - 1 - u]);
+      if (inside) m = fmaxf(m, fabsf(val[i][t]));
+    }
   }
+#pragma unroll
+  for (int i = 0; i < kBiasPieces; ++i)
+    if (lane + 64 * i < job.Lpad) out[lane + 64 * i] = make_float4(val[i][0], val[i][1], val[i][2], val[i][3]);
   // row maximum of |entry| * log2e, for the logit bound
-  __shared__ float wmax[kThreads / 64];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0 && inside) {
-    float r = wmax[0];
-    for (int i = 1; i < static_cast<int>(blockDim.x >> 6); ++i) r = fmaxf(r, wmax[i]);
-    job.row_max[h * rows + dy] = r;
-  }
+  if (lane == 0 && inside) job.row_max[h * rows + dy] = m;
 }
 
 __global__ void __launch_bounds__(kThreads) prologue_kernel(PrologueArgs a) {
