@@ -37,7 +37,9 @@ Printed: one JSON line on stdout with the throughput in TFLOP-eq/s
 (4*B*H*N^2*d per step, the FLOPs of dense QK^T and P.V), the fused kernel's
 roofline position and the CPU oracle's own throughput on a bounded sample of
 the same workload (the oracle runs on the host cores; it is a baseline, not
-the target).  Diagnostics go to stderr.
+the target).  Every mode times its own oracle: the bf16, 8-bit P.V or
+dense-bias forward, or the backward; the sample's parity against the GPU
+result rides along.  Diagnostics go to stderr.
 
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -128,18 +130,23 @@ def algorithmic_bytes(w, npad, dense_bytes=None):
     return prologue, fused
 
 
-def cpu_baseline(w, inp, o_gpu, seconds: float):
+def _host_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads") or 1 for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover - informational only
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w, inp, o_gpu, seconds: float, pv: str = "bf16", dense=None):
     """The float64 oracle on whole (b, h) heads of the same inputs, for about
-    `seconds` of host time; also returns the parity of those rows."""
+    `seconds` of host time; also returns the parity of those rows.  pv="int8"
+    times the 8-bit P.V oracle; `dense` (the GPU's [Bb,H,N,N] bias) the
+    dense-bias oracle, one head's bias copied to the host at a time."""
     import numpy as np
 
     import oracle
     import workloads
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads") or 1 for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover - informational only
-        threads = os.cpu_count() or 1
     q = workloads.as_f32(inp["q"])
     k = workloads.as_f32(inp["k"])
     v = workloads.as_f32(inp["v"])
@@ -152,11 +159,19 @@ def cpu_baseline(w, inp, o_gpu, seconds: float):
     elapsed = 0.0
     for b in range(w.B):
         for h in range(w.H):
+            qs, ks, vs = q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1]
+            if dense is not None:
+                bias = dense[b if dense.shape[0] > 1 else 0, h].float().cpu().numpy()[None, None]
             for r0 in range(0, w.N, rows_per):
                 rows = np.arange(r0, min(w.N, r0 + rows_per))
-                res = oracle.binary_attention_rows(
-                    q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
-                    None if t is None else t[h:h + 1], inp["gh"], inp["gw"], rows=rows)
+                if dense is not None:
+                    res = oracle.binary_attention_dense_bias_rows(qs, ks, vs, bias, rows=rows)
+                elif pv == "int8":
+                    res = oracle.binary_attention_int8_pv_rows(qs, ks, vs, None if t is None else t[h:h + 1],
+                                                               inp["gh"], inp["gw"], rows=rows)
+                else:
+                    res = oracle.binary_attention_rows(qs, ks, vs, None if t is None else t[h:h + 1],
+                                                       inp["gh"], inp["gw"], rows=rows)
                 err = float(np.abs(res["O"][0, 0] - og[b, h, rows]).max()) / vmax
                 worst = max(worst, err)
             heads += 1
@@ -166,14 +181,61 @@ def cpu_baseline(w, inp, o_gpu, seconds: float):
         if elapsed >= seconds:
             break
     flop = 4.0 * heads * w.N * w.N * w.d
+    what = ("binary_attention_dense_bias_rows" if dense is not None else
+            "binary_attention_int8_pv_rows" if pv == "int8" else "binary_attention_rows")
     return {
         "value": flop / elapsed / 1e12,
         "unit": "TFLOP-eq/s",
-        "cores": int(threads),
+        "cores": int(_host_threads()),
         "kind": "oracle",
         "sample": f"{heads} of {w.B * w.H} (b,h) heads, all {w.N} query rows each, "
-                  f"float64 numpy on the host ({elapsed:.1f} s)",
+                  f"float64 numpy on the host, oracle.{what} ({elapsed:.1f} s)",
         "parity_max_err_over_max_v": worst,
+    }
+
+
+def cpu_baseline_bwd(w, inp, dout, grads, seconds: float):
+    """The float64 backward oracle on the whole batch of one head at a time
+    (the table gradient sums over the batch), for about `seconds` of host
+    time, counted as 10 N^2 d FLOP-eq per (b, h).  Parity: per gradient,
+    max |GPU - oracle| over max |oracle| on the heads done."""
+    import numpy as np
+
+    import oracle
+    import workloads
+    q = workloads.as_f32(inp["q"])
+    k = workloads.as_f32(inp["k"])
+    v = workloads.as_f32(inp["v"])
+    t = workloads.as_f32(inp["table"])
+    do = dout.float().cpu().numpy()
+    gq, gk, gv, gt = (None if x is None else x.float().cpu().numpy() for x in grads)
+    worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0, "dtable": 0.0}
+    heads = 0
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    for h in range(w.H):
+        sl = slice(h, h + 1)
+        res = oracle.binary_attention_backward(q[:, sl], k[:, sl], v[:, sl], do[:, sl],
+                                               None if t is None else t[sl], inp["gh"], inp["gw"])
+        for name, got in (("dq", gq[:, sl]), ("dk", gk[:, sl]), ("dv", gv[:, sl]),
+                          ("dtable", None if gt is None else gt[sl])):
+            ref = res[name]
+            if got is None or ref is None:
+                continue
+            worst[name] = max(worst[name], float(np.abs(got - ref).max()) / max(float(np.abs(ref).max()), 1e-300))
+        heads += w.B
+        elapsed = time.perf_counter() - t0
+        if elapsed >= seconds:
+            break
+    flop = 10.0 * heads * w.N * w.N * w.d
+    return {
+        "value": flop / elapsed / 1e12,
+        "unit": "TFLOP-eq/s",
+        "cores": int(_host_threads()),
+        "kind": "oracle",
+        "sample": f"{heads} of {w.B * w.H} (b,h) heads (all {w.B} batch entries of {heads // w.B} heads), "
+                  f"float64 numpy on the host, oracle.binary_attention_backward ({elapsed:.1f} s)",
+        "parity_max_err_over_max_ref": worst,
     }
 
 
@@ -374,10 +436,10 @@ def main() -> int:
     hbm_bound = dense is not None and fused_gbs / PEAK_HBM_GBS > fused_tf / peak
 
     baseline = None
-    if args.cpu_seconds > 0 and (dense is not None or args.pv != "bf16" or args.bwd):
-        log("[bench] no CPU baseline with --bias dense, --pv int8 or --bwd")
+    if args.cpu_seconds > 0 and args.bwd:
+        baseline = cpu_baseline_bwd(w, inp, dout, (gq, gk, gv, gt), args.cpu_seconds)
     elif args.cpu_seconds > 0:
-        baseline = cpu_baseline(w, inp, out, args.cpu_seconds)
+        baseline = cpu_baseline(w, inp, out, args.cpu_seconds, pv=args.pv, dense=dense)
 
     rec = {
         "metric": METRIC if not args.bwd else
