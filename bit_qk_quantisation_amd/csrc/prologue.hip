@@ -116,7 +116,7 @@ __device__ __forceinline__ int vt_slot_key(int slot) {
 
 
 __device__ void kv_codes(const KvJob& job, int64_t blk, int64_t bh, int tile, const uint16_t* vs, int stride,
-                         float* sinv);
+                         float* sinv, float* red);
 
 __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
   const int d = job.d, W = job.W, C = d / 8, stride = d + 8;  // bf16 units
@@ -208,7 +208,7 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
     }
   }
   if (job.vq) {
-    kv_codes(job, blk, bh, tile, vs, stride, reinterpret_cast<float*>(vs + kPackTok * stride));
+    kv_codes(job, blk, bh, tile, vs, stride, reinterpret_cast<float*>(vs + kPackTok * stride), sp);
     return;
   }
 
@@ -247,11 +247,30 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
 // the 16 rows one quarter-wave reads hit 16 different bank groups.  The
 // codes of each channel are summed over the tile's keys into vcsum.
 __device__ void kv_codes(const KvJob& job, int64_t blk, int64_t bh, int tile, const uint16_t* vs, int stride,
-                         float* sinv) {
+                         float* sinv, float* red) {
   const int tiles = job.Npad / kPackTok, n0 = tile * kPackTok;
+  // The head's channel maxima from the tile maxima, with every thread: thread
+  // (r, g) takes the maxima of channels 4g..4g+3 over tiles r, r + R, ...
+  // (16-byte loads, all issued before they are used), then R partial maxima
+  // per channel meet in `red` (the partial-sum scratch, free again here:
+  // R * dpad <= 4 * kThreads floats).
+  const int nc4 = job.dpad / 4, R = kThreads / nc4;
+  const int g = threadIdx.x % nc4, r = threadIdx.x / nc4;
+  __syncthreads();  // the key scales are done with `red`
+  if (r < R) {
+    const float4* vp = reinterpret_cast<const float4*>(job.vpart) + bh * tiles * nc4 + g;
+    float4 m = make_float4(0.0f, 0.0f, 0.0f, 0.0f);  // maxima of |v| are >= 0
+#pragma unroll 4
+    for (int t = r; t < tiles; t += R) {
+      const float4 x = vp[t * nc4];
+      m = make_float4(fmaxf(m.x, x.x), fmaxf(m.y, x.y), fmaxf(m.z, x.z), fmaxf(m.w, x.w));
+    }
+    reinterpret_cast<float4*>(red)[r * nc4 + g] = m;
+  }
+  __syncthreads();
   for (int c = threadIdx.x; c < job.dpad; c += kThreads) {
     float m = 0.0f;
-    for (int t = 0; t < tiles; ++t) m = fmaxf(m, job.vpart[(bh * tiles + t) * job.dpad + c]);
+    for (int i = 0; i < R; ++i) m = fmaxf(m, red[i * job.dpad + c]);
     sinv[c] = m > 0.0f ? __fdiv_rn(127.0f, m) : 0.0f;
     if (tile == 0) job.vscale[bh * job.dpad + c] = __fdiv_rn(m, 127.0f);
   }
