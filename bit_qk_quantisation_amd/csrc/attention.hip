@@ -235,17 +235,24 @@ __device__ __forceinline__ int window_offset(const Ctx<NCH>& c, const KeyPos& kp
   return off;
 }
 
+// What block_logits runs at the start of each group of 4 keys (the
+// pipelined exact path issues a share of the pending block's P.V there).
+struct NoHook {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
 // Logits of one 32-key block in base 2:
 //   D * alpha_k * (alpha_q scale log2e) + log2e b
-template <bool MASK, int NCH, int CB, int BIAS, class TB = TileBuf<NCH, CB, BIAS>>
+template <bool MASK, int NCH, int CB, int BIAS, class TB = TileBuf<NCH, CB, BIAS>, class HOOK = NoHook>
 __device__ __forceinline__ void block_logits(const Ctx<NCH>& c, const TB& tb, const KeyPos& kp,
-                                             int blk, const v16f& s, float (&sc)[16]) {
+                                             int blk, const v16f& s, float (&sc)[16], const HOOK& hook = HOOK{}) {
   const FwdArgs& a = *c.a;
   int woff = 0;
   if (BIAS == kBiasRows) woff = window_offset(c, kp, blk);
   const float akv = lds_load<float>(tb.ak, c.off_akb + blk * 128);
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
+    hook(b);
     const float u0 = s[4 * b] * row_bcast(akv, 4 * b), u1 = s[4 * b + 1] * row_bcast(akv, 4 * b + 1);
     const float u2 = s[4 * b + 2] * row_bcast(akv, 4 * b + 2), u3 = s[4 * b + 3] * row_bcast(akv, 4 * b + 3);
     if (BIAS == kBiasRows) {
@@ -315,41 +322,6 @@ __device__ __forceinline__ void block_rescale(float (&sc)[16], Acc<CB, XONES>& a
   } else {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] -= mrow;
-  }
-}
-
-// One 64-key tile for this wave's 32 queries, one 32-key block at a time:
-// QK, logits, exp2 and bf16 packing, then P.V (and the row sums).
-// FAST: offset-free exp2, no row max.  MASK: keys >= N get probability 0.
-template <bool FAST, bool MASK, int NCH, int CB, bool XONES, int BIAS>
-__device__ __forceinline__ void compute_tile(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& tb, const KeyPos& kp,
-                                             Acc<CB, XONES>& acc, float& mrow, int nblk) {
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    if (blk >= nblk) break;  // uniform: the padded block of a ragged table-row tile
-    v16f s = v16f{};
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch)
-      s = mfma_signs_32x32x64(lds_load<v4i>(tb.k, c.off_k + ch * 2048 + blk * 1024), c.qop[ch], s);
-    float sc[16];
-    block_logits<MASK, NCH, CB, BIAS>(c, tb, kp, blk, s, sc);
-    if (!FAST) block_rescale<BIAS == kBiasDense>(sc, acc, mrow);
-    uint32_t pk[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) pk[j] = pack_bf16x2(fast_exp2(sc[2 * j]), fast_exp2(sc[2 * j + 1]));
-    if (XONES) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc.rs[b & 1] = add_bf16x2(pk[2 * b], add_bf16x2(pk[2 * b + 1], acc.rs[b & 1]));
-    }
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int p = 2 * blk + half;
-      const v4u pw = {pk[4 * half], pk[4 * half + 1], pk[4 * half + 2], pk[4 * half + 3]};
-      const v8bf pop = __builtin_bit_cast(v8bf, pw);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-        acc.o[cb] = mfma_bf16_32x32x16(lds_load<v8bf>(tb.vt, c.off_v[p] + cb * 4096), pop, acc.o[cb]);
-    }
   }
 }
 
@@ -520,13 +492,60 @@ __device__ __forceinline__ void run_fast_pass(const Ctx<NCH>& c, TileBuf<NCH, CB
   if (XONES) acc.rs[0] = sum_halves(acc.rs[0] + acc.rs[1]);
 }
 
-// One key tile: start the copies of tile t+1 into `nxt`, compute tile t from
-// `cur`, expand the next keys into `nxt`, wait, barrier.
-template <bool FAST, int NCH, int CB, bool XONES, int BIAS>
-__device__ __forceinline__ void pass_step(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& cur, TileBuf<NCH, CB, BIAS>& nxt,
-                                          int t, int nkt, KeyPos& kp, Acc<CB, XONES>& acc, float& mrow) {
+// ------------------------------------------------ pipelined exact path ----
+// The online softmax with a running row maximum (exact path), pipelined as
+// the fast path is: the pending block's P.V runs while this block's logits
+// are formed (a share per group of 4 keys), before this block's maximum is
+// known, so a rescale of the accumulators also covers the pending product.
+template <int CB, bool XONES>
+struct PendingHook {
+  const PendingPV<CB>& pp;
+  Acc<CB, XONES>& acc;
+  __device__ __forceinline__ void operator()(int b) const {
+    constexpr int kMf = 2 * CB;
+#pragma unroll
+    for (int i = b * kMf / 4; i < (b + 1) * kMf / 4; ++i) pv_mfma<CB, XONES>(i, pp, acc);
+  }
+};
+
+template <bool MASK, bool HAVE_PENDING, int NCH, int CB, bool XONES, int BIAS>
+__device__ __forceinline__ void exact_block(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& tb, const KeyPos& kp,
+                                            int blk, PendingPV<CB>& pp, Acc<CB, XONES>& acc, float& mrow) {
+  v16f s = v16f{};
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+    s = mfma_signs_32x32x64(lds_load<v4i>(tb.k, c.off_k + ch * 2048 + blk * 1024), c.qop[ch], s);
+  if (HAVE_PENDING) {
+#pragma unroll
+    for (int i = 0; i < 2 * CB; ++i) pv_mfma<CB, XONES>(i, pp, acc);
+  }
+  float sc[16];
+  block_logits<MASK, NCH, CB, BIAS>(c, tb, kp, blk, s, sc);
+  block_rescale<BIAS == kBiasDense>(sc, acc, mrow);
+  uint32_t pk[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pk[j] = pack_bf16x2(fast_exp2(sc[2 * j]), fast_exp2(sc[2 * j + 1]));
+  if (XONES) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc.rs[b & 1] = add_bf16x2(pk[2 * b], add_bf16x2(pk[2 * b + 1], acc.rs[b & 1]));
+  }
+  // this block becomes pending: P and its V^T operands
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pp.pk[j] = pk[j];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      pp.vop[half][cb] = lds_load<v8bf>(tb.vt, c.off_v[2 * blk + half] + cb * 4096);
+}
+
+// One key tile of the exact path: start the copies of tile t+1 into `nxt`,
+// compute tile t from `cur`, wait, barrier.
+template <bool FIRST, int NCH, int CB, bool XONES, int BIAS>
+__device__ __forceinline__ void exact_step(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& cur,
+                                           TileBuf<NCH, CB, BIAS>& nxt, int t, int nkt, KeyPos& kp,
+                                           Acc<CB, XONES>& acc, PendingPV<CB>& pp, float& mrow) {
   const FwdArgs& a = *c.a;
-  tile_priority(a, t, nkt);
   const bool more = t + 1 < nkt;
   const KeyPos kn = next_keys(kp, a.gw);
   if (more) copy_tile_async<NCH, CB, BIAS>(c, nxt, t + 1, kn);
@@ -536,22 +555,27 @@ __device__ __forceinline__ void pass_step(const Ctx<NCH>& c, const TileBuf<NCH, 
   // a query on grid row >= 1, falls on a real table row).  Table rows have
   // N % 32 == 0, so there the ragged tile is a real block and a block of
   // padded keys, which is skipped; the other modes mask key by key.
-  if (BIAS == kBiasRows)
-    compute_tile<FAST, false, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow, kp.k0 + 32 < a.N ? 2 : 1);
-  else if (kp.k0 + kBN <= a.N)
-    compute_tile<FAST, false, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow, 2);
-  else
-    compute_tile<FAST, true, NCH, CB, XONES, BIAS>(c, cur, kp, acc, mrow, 2);
+  if (BIAS == kBiasRows) {
+    exact_block<false, !FIRST, NCH, CB, XONES, BIAS>(c, cur, kp, 0, pp, acc, mrow);
+    if (kp.k0 + 32 < a.N) exact_block<false, true, NCH, CB, XONES, BIAS>(c, cur, kp, 1, pp, acc, mrow);
+  } else if (kp.k0 + kBN <= a.N) {
+    exact_block<false, !FIRST, NCH, CB, XONES, BIAS>(c, cur, kp, 0, pp, acc, mrow);
+    exact_block<false, true, NCH, CB, XONES, BIAS>(c, cur, kp, 1, pp, acc, mrow);
+  } else {
+    exact_block<true, !FIRST, NCH, CB, XONES, BIAS>(c, cur, kp, 0, pp, acc, mrow);
+    exact_block<true, true, NCH, CB, XONES, BIAS>(c, cur, kp, 1, pp, acc, mrow);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   kp = kn;
 }
 
-// One pass over all keys; O^T (and the row sums) accumulate in acc.
-// Returns the row maximum (log2 units) the sums are taken against.
-template <bool FAST, int NCH, int CB, bool XONES, int BIAS>
-__device__ __forceinline__ float run_pass(const Ctx<NCH>& c, TileBuf<NCH, CB, BIAS>& tb0, TileBuf<NCH, CB, BIAS>& tb1,
-                                          Acc<CB, XONES>& acc) {
+// One pass over all keys with the exact softmax; O^T (and the row sums)
+// accumulate in acc.  Returns the row maximum (log2 units) the sums are
+// taken against.
+template <int NCH, int CB, bool XONES, int BIAS>
+__device__ __forceinline__ float run_exact_pass(const Ctx<NCH>& c, TileBuf<NCH, CB, BIAS>& tb0,
+                                                TileBuf<NCH, CB, BIAS>& tb1, Acc<CB, XONES>& acc) {
   const FwdArgs& a = *c.a;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc.o[cb] = v16f{};
@@ -567,10 +591,16 @@ __device__ __forceinline__ float run_pass(const Ctx<NCH>& c, TileBuf<NCH, CB, BI
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int nkt = (a.N + kBN - 1) / kBN;
-  for (int t = 0; t < nkt; t += 2) {
-    pass_step<FAST, NCH, CB, XONES, BIAS>(c, tb0, tb1, t, nkt, kp, acc, mrow);
-    if (t + 1 < nkt) pass_step<FAST, NCH, CB, XONES, BIAS>(c, tb1, tb0, t + 1, nkt, kp, acc, mrow);
+  PendingPV<CB> pp;
+  exact_step<true, NCH, CB, XONES, BIAS>(c, tb0, tb1, 0, nkt, kp, acc, pp, mrow);
+  for (int t = 1; t < nkt; t += 2) {
+    tile_priority(a, t, nkt);
+    exact_step<false, NCH, CB, XONES, BIAS>(c, tb1, tb0, t, nkt, kp, acc, pp, mrow);
+    if (t + 1 < nkt) exact_step<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, t + 1, nkt, kp, acc, pp, mrow);
   }
+  // drain: the last block's P.V
+#pragma unroll
+  for (int i = 0; i < 2 * CB; ++i) pv_mfma<CB, XONES>(i, pp, acc);
   if (XONES) acc.rs[0] = sum_halves(acc.rs[0] + acc.rs[1]);
   return mrow;
 }
@@ -750,12 +780,12 @@ attn_fwd_kernel(FwdArgs a) {
   if constexpr (BIAS == kBiasDense) {
     // no bound on a dense bias short of reading all of it: exact softmax
     (void)M;
-    mrow = run_pass<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
+    mrow = run_exact_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
   } else {
     if (M <= kFastMaxLogit)  // false for NaN as well
       run_fast_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
     else
-      mrow = run_pass<false, NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
+      mrow = run_exact_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
   }
 
   // ---- epilogue: O = O^T / l, bf16, one query per lane --------------------
