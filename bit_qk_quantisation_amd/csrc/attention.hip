@@ -235,24 +235,17 @@ __device__ __forceinline__ int window_offset(const Ctx<NCH>& c, const KeyPos& kp
   return off;
 }
 
-// What block_logits runs at the start of each group of 4 keys (the
-// pipelined exact path issues a share of the pending block's P.V there).
-struct NoHook {
-  __device__ __forceinline__ void operator()(int) const {}
-};
-
 // Logits of one 32-key block in base 2:
 //   D * alpha_k * (alpha_q scale log2e) + log2e b
-template <bool MASK, int NCH, int CB, int BIAS, class TB = TileBuf<NCH, CB, BIAS>, class HOOK = NoHook>
+template <bool MASK, int NCH, int CB, int BIAS, class TB = TileBuf<NCH, CB, BIAS>>
 __device__ __forceinline__ void block_logits(const Ctx<NCH>& c, const TB& tb, const KeyPos& kp,
-                                             int blk, const v16f& s, float (&sc)[16], const HOOK& hook = HOOK{}) {
+                                             int blk, const v16f& s, float (&sc)[16]) {
   const FwdArgs& a = *c.a;
   int woff = 0;
   if (BIAS == kBiasRows) woff = window_offset(c, kp, blk);
   const float akv = lds_load<float>(tb.ak, c.off_akb + blk * 128);
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    hook(b);
     const float u0 = s[4 * b] * row_bcast(akv, 4 * b), u1 = s[4 * b + 1] * row_bcast(akv, 4 * b + 1);
     const float u2 = s[4 * b + 2] * row_bcast(akv, 4 * b + 2), u3 = s[4 * b + 3] * row_bcast(akv, 4 * b + 3);
     if (BIAS == kBiasRows) {
@@ -327,11 +320,13 @@ __device__ __forceinline__ void block_rescale(float (&sc)[16], Acc<CB, XONES>& a
 
 // ------------------------------------------------- pipelined fast path ----
 // P.V of a finished 32-key block waits in registers (bf16 P and its V^T
-// operands) and runs while the next block's logits are formed: each of its
-// 2 CB matrix instructions is followed by a quarter of the next
-// block's vector work, so the matrix cores and the vector ALUs of a SIMD
-// overlap even within one wave, and the V^T operands no longer tie the
-// block to its LDS buffer (the pipeline runs across tile barriers).
+// operands) and is issued right after the next block's QK, so its matrix
+// instructions run while that block's logits are formed: the matrix cores
+// and the vector ALUs of a SIMD overlap even within one wave, and the V^T
+// operands no longer tie the block to its LDS buffer (the pipeline runs
+// across tile barriers).  Issuing them all at once frees their registers
+// before the logits are live; spreading them over the four groups of keys
+// measured no faster.
 template <int CB>
 struct PendingPV {
   uint32_t pk[8];     // bf16 P, 16 keys x 2 steps
@@ -345,8 +340,8 @@ __device__ __forceinline__ void pv_mfma(int i, const PendingPV<CB>& pp, Acc<CB, 
   acc.o[cb] = mfma_bf16_32x32x16(pp.vop[half][cb], __builtin_bit_cast(v8bf, pw), acc.o[cb]);
 }
 
-// Block `blk` of tile `tb`: its QK, then the pending block's P.V interleaved
-// with this block's logits / exp2 / bf16 packing; this block becomes pending.
+// Block `blk` of tile `tb`: its QK, the pending block's P.V, then this
+// block's logits / exp2 / bf16 packing; this block becomes pending.
 template <bool MASK, bool HAVE_PENDING, int NCH, int CB, bool XONES, int BIAS>
 __device__ __forceinline__ void pipelined_block(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& tb, const KeyPos& kp,
                                                 int blk, PendingPV<CB>& pp, Acc<CB, XONES>& acc) {
@@ -356,17 +351,16 @@ __device__ __forceinline__ void pipelined_block(const Ctx<NCH>& c, const TileBuf
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch)
     s = mfma_signs_32x32x64(lds_load<v4i>(tb.k, c.off_k + ch * 2048 + blk * 1024), c.qop[ch], s);
+  if (HAVE_PENDING) {
+#pragma unroll
+    for (int i = 0; i < kMf; ++i) pv_mfma<CB, XONES>(i, pp, acc);
+  }
   int woff = 0;
   if (BIAS == kBiasRows) woff = window_offset(c, kp, blk);
   const float akv = lds_load<float>(tb.ak, c.off_akb + blk * 128);
   uint32_t pk[8];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    if (HAVE_PENDING) {
-      // this group's share of the pending block's matrix instructions
-#pragma unroll
-      for (int i = b * kMf / 4; i < (b + 1) * kMf / 4; ++i) pv_mfma<CB, XONES>(i, pp, acc);
-    }
     float x0 = s[4 * b] * row_bcast(akv, 4 * b), x1 = s[4 * b + 1] * row_bcast(akv, 4 * b + 1);
     float x2 = s[4 * b + 2] * row_bcast(akv, 4 * b + 2), x3 = s[4 * b + 3] * row_bcast(akv, 4 * b + 3);
     if (BIAS == kBiasRows) {
@@ -494,20 +488,9 @@ __device__ __forceinline__ void run_fast_pass(const Ctx<NCH>& c, TileBuf<NCH, CB
 
 // ------------------------------------------------ pipelined exact path ----
 // The online softmax with a running row maximum (exact path), pipelined as
-// the fast path is: the pending block's P.V runs while this block's logits
-// are formed (a share per group of 4 keys), before this block's maximum is
-// known, so a rescale of the accumulators also covers the pending product.
-template <int CB, bool XONES>
-struct PendingHook {
-  const PendingPV<CB>& pp;
-  Acc<CB, XONES>& acc;
-  __device__ __forceinline__ void operator()(int b) const {
-    constexpr int kMf = 2 * CB;
-#pragma unroll
-    for (int i = b * kMf / 4; i < (b + 1) * kMf / 4; ++i) pv_mfma<CB, XONES>(i, pp, acc);
-  }
-};
-
+// the fast path is: the pending block's P.V is issued after this block's QK,
+// before this block's maximum is known, so a rescale of the accumulators
+// also covers the pending product.
 template <bool MASK, bool HAVE_PENDING, int NCH, int CB, bool XONES, int BIAS>
 __device__ __forceinline__ void exact_block(const Ctx<NCH>& c, const TileBuf<NCH, CB, BIAS>& tb, const KeyPos& kp,
                                             int blk, PendingPV<CB>& pp, Acc<CB, XONES>& acc, float& mrow) {
