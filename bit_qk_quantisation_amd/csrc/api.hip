@@ -211,7 +211,7 @@ int fused_dynamic_lds(int static_lds, int table_lds, int64_t nwg) {
 // tile maxima, dO^T, the Q signs transposed, and the flipped bias rows.
 struct BwdLayout {
   Layout fwd;
-  int64_t kst, obuf, lse, delta, qop, alpha_q, qmax, dot, qst, bias4f, rowmaxf, dtpart, total;
+  int64_t kst, obuf, lse, delta, qop, alpha_q, qmax, dot, qst, bias4f, rowmaxf, vmax, dtpart, total;
   int prow;  // rows of one workgroup's share of the table gradient
 };
 
@@ -247,6 +247,9 @@ BwdLayout bwd_layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int 
   const bool rows = L.fwd.mode == ba::kBiasRows;
   L.bias4f = take(rows ? H * (2 * gh - 1 + 2 * ba::kBiasPadRows) * 4 * L.fwd.Lpad * 4 : 0);
   L.rowmaxf = take(rows ? H * (2 * gh - 1) * 4 : 0);
+  // table mode: the largest |v| of each key tile, for the table gradient's
+  // fixed-point scale
+  L.vmax = take(L.fwd.mode == ba::kBiasTable ? BH * (Npad / ba::kPackTok) * 4 : 0);
   // the shares of the table gradient: table rows yq_lo .. yq_hi + gh - 1 of
   // each query tile (table-row mode), or the whole table (table mode)
   L.prow = rows ? gh + query_span(N, gw) : (has_bias ? 2 * gh - 1 : 0);
@@ -483,7 +486,7 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   p = ba::PrologueArgs{};
   p.kv = ba::KvJob{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), const_cast<uint32_t*>(f.kop),
                    const_cast<float*>(f.alpha_k), const_cast<float*>(f.kmax_blk), const_cast<uint16_t*>(f.vt),
-                   nullptr, nullptr, nullptr, nullptr, nullptr,
+                   nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                    vs[1], vs[2], BH, static_cast<int>(H), f.N, f.Npad, d, f.W, (f.W + 1) / 2, f.dpad};
   p.kv_blocks = BH * (L.Npad / ba::kPackTok);
   p.lds = ba::prologue_lds(d, true);
@@ -655,6 +658,8 @@ ba_status ba_attention_bwd(const void* q, const void* k, const void* v, const vo
   // 1. keys and values (with the K signs transposed), both bias-row orientations
   ba::PrologueArgs p1 = fp.p;
   p1.kv.kst = reinterpret_cast<uint16_t*>(ws + BL.kst);
+  float* vmax = (mode == ba::kBiasTable && dtable) ? reinterpret_cast<float*>(ws + BL.vmax) : nullptr;
+  p1.kv.vmax = vmax;
   if (mode == ba::kBiasRows) {
     p1.bias2 = p1.bias;
     p1.bias2.bias4 = reinterpret_cast<float*>(ws + BL.bias4f);
@@ -670,6 +675,7 @@ ba_status ba_attention_bwd(const void* q, const void* k, const void* v, const vo
   // 3. queries and dO as the keys and values of a second prologue pass
   ba::PrologueArgs p3{};
   p3.kv = p1.kv;
+  p3.kv.vmax = nullptr;  // dO's maxima are not needed
   p3.kv.k = static_cast<const uint16_t*>(q);
   p3.kv.v = static_cast<const uint16_t*>(dout);
   p3.kv.kop = reinterpret_cast<uint32_t*>(ws + BL.qop);
@@ -700,6 +706,7 @@ ba_status ba_attention_bwd(const void* q, const void* k, const void* v, const vo
   bq.out1 = dq;
   bq.dtable = dtable;
   bq.dtpart = reinterpret_cast<float*>(ws + BL.dtpart);
+  bq.vmax = vmax;
   bq.prow = BL.prow;
   bq.scale = scale;
   // 5. key role: dk, dv; queries and keys exchanged, the bias flipped

@@ -129,6 +129,18 @@ __device__ __forceinline__ KeyPos next_keys(const KeyPos& p, int gw) {
   return n;
 }
 
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) r += red[w];
+  return r;
+}
+
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
@@ -1008,6 +1020,7 @@ struct BwdTileBuf {
 // Buffer resources of the backward's own column copies.
 struct BwdCtx {
   rsrc_t zrs, z2rs, yrs, lrs, drs;
+  int dtk;  // table mode: the table gradient is summed in LDS as round(dS 2^dtk)
 };
 
 // 16-byte chunk position of chunk `ch` of row `row` in the natural tile
@@ -1115,13 +1128,15 @@ __device__ __forceinline__ float diagonal_sums(const float (&x)[16]) {
 // diagonal sums (diagonal_sums) to consecutive entries of one row of this
 // wave's window; dsk/dbase keep the sums and the window position, and
 // bwd_step adds them once the tile's copies have landed.  Table mode: every
-// dS_ij is added with ds_add_f32 at the entry of its grid offset in a copy of
-// the whole table that follows the table in dynamic LDS.
+// dS_ij is added at the entry of its grid offset in a copy of the whole
+// table that follows the table in dynamic LDS, as the integer round(dS 2^dtk)
+// with an integer LDS add (float LDS adds run several times slower); dtk
+// keeps the workgroup's sums below 2^30 (see attn_bwd_kernel).
 template <int ROLE, bool MASK, int NCH, int CB, int BIAS>
 __device__ __forceinline__ void bwd_tile(const Ctx<NCH>& c, BwdTileBuf<ROLE, NCH, CB, BIAS>& tb,
                                          const KeyPos& kp, const v8bf (&xop)[2 * CB], float lrow, float drow,
                                          BwdAcc<ROLE, CB>& acc, int nblk, bool want_dt, float (&dsk)[2],
-                                         int (&dbase)[2]) {
+                                         int (&dbase)[2], int dtk) {
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     if (blk >= nblk) break;  // uniform: the padded block of a ragged table-row tile
@@ -1173,14 +1188,14 @@ __device__ __forceinline__ void bwd_tile(const Ctx<NCH>& c, BwdTileBuf<ROLE, NCH
     }
     if (ROLE == kRoleQ && BIAS == kBiasTable && want_dt) {
       const FwdArgs& a = *c.a;
-      float* tacc = c.table + (2 * a.gh - 1) * (2 * a.gw - 1) + c.fidx;
+      int* tacc = reinterpret_cast<int*>(c.table + (2 * a.gh - 1) * (2 * a.gw - 1)) + c.fidx;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const v4i g = lds_load<v4i>(tb.gk, c.off_gk + (blk * 32 + 8 * b) * 4);
-        atomicAdd(tacc - g.x, dsv[4 * b + 0]);
-        atomicAdd(tacc - g.y, dsv[4 * b + 1]);
-        atomicAdd(tacc - g.z, dsv[4 * b + 2]);
-        atomicAdd(tacc - g.w, dsv[4 * b + 3]);
+        atomicAdd(tacc - g.x, __float2int_rn(ldexpf(dsv[4 * b + 0], dtk)));
+        atomicAdd(tacc - g.y, __float2int_rn(ldexpf(dsv[4 * b + 1], dtk)));
+        atomicAdd(tacc - g.z, __float2int_rn(ldexpf(dsv[4 * b + 2], dtk)));
+        atomicAdd(tacc - g.w, __float2int_rn(ldexpf(dsv[4 * b + 3], dtk)));
       }
     }
 #pragma unroll
@@ -1257,11 +1272,11 @@ __device__ __forceinline__ void bwd_step(const Ctx<NCH>& c, const BwdCtx& bc, co
   int dbase[2] = {0, 0};
   const int nb = BIAS == kBiasRows ? (kp.k0 + 32 < a.N ? 2 : 1) : 2;
   if (BIAS == kBiasRows)  // as in pass_step
-    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, nb, want_dt, dsk, dbase);
+    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, nb, want_dt, dsk, dbase, bc.dtk);
   else if (kp.k0 + kBN <= a.N)
-    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2, want_dt, dsk, dbase);
+    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2, want_dt, dsk, dbase, bc.dtk);
   else
-    bwd_tile<ROLE, true, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2, want_dt, dsk, dbase);
+    bwd_tile<ROLE, true, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2, want_dt, dsk, dbase, bc.dtk);
   __builtin_amdgcn_s_waitcnt(0);
   if (ROLE == kRoleQ && BIAS == kBiasRows && want_dt && c.lane != 0) {
     // lane t: diagonal t - 32 (lane 0 holds the empty diagonal -32); the
@@ -1397,6 +1412,28 @@ attn_bwd_kernel(BwdArgs ba) {
     if (BIAS == kBiasTable)
       for (int e = c.tid; e < tsize; e += kThreads) c.table[tsize + e] = 0.0f;
   }
+  // Table mode: the scale of the integer sums.  With P <= 1, |dP_ij| and
+  // |delta_i| both at most |dO_i|_1 max|v|, so |dS_ij| <= 2 |dO_i|_1 max|v|,
+  // and a query meets each grid offset at most once: every entry's sum over
+  // this workgroup is below B = 2 max|v| sum_i |dO_i|_1.  2^dtk B < 2^30, so
+  // no sum overflows, and each rounds by at most 64 2^-dtk, below 1e-7 B.
+  bc.dtk = 0;
+  if (ROLE == kRoleQ && BIAS == kBiasTable && ba.dtable) {
+    float l1 = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2 * CB; ++t) {
+      const uint4 rg = __builtin_bit_cast(uint4, xop[t]);
+      const uint32_t wg[4] = {rg.x, rg.y, rg.z, rg.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        l1 += fabsf(bf16_to_f32(static_cast<uint16_t>(wg[e] & 0xffffu))) + fabsf(bf16_to_f32(static_cast<uint16_t>(wg[e] >> 16)));
+    }
+    const float dsum = block_sum(l1, red);  // both halves of every query's row
+    float vm = 0.0f;
+    for (int t = c.tid; t < ntile; t += kThreads) vm = fmaxf(vm, ba.vmax[static_cast<int64_t>(c.bh) * ntile + t]);
+    const float bound = 2.0f * block_max(vm, red) * dsum;
+    if (bound > 0.0f && bound < INFINITY) bc.dtk = 29 - ilogbf(bound);
+  }
   bwd_copy<ROLE, NCH, CB, BIAS>(c, bc, tb0, 0, kp);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -1410,8 +1447,10 @@ attn_bwd_kernel(BwdArgs ba) {
   if (ROLE == kRoleQ && ba.dtable) {
     // the last tile's window (rows), or the whole table (table mode)
     if (BIAS == kBiasRows) flush_dwin(c, (nkt & 1) ? tb0.dwin : tb1.dwin, kprev, share, ba.prow);
-    if (BIAS == kBiasTable)
-      for (int e = c.tid; e < tsize; e += kThreads) share[e] = c.table[tsize + e];
+    if (BIAS == kBiasTable) {
+      const int* tsum = reinterpret_cast<const int*>(c.table + tsize);
+      for (int e = c.tid; e < tsize; e += kThreads) share[e] = ldexpf(static_cast<float>(tsum[e]), -bc.dtk);
+    }
   }
 
 #pragma unroll

@@ -66,6 +66,8 @@ struct KvJob {
   // backward: the signs of the tile's tokens as +/-1 bf16 in the V^T layout
   // (nullptr: not written)
   uint16_t* kst;      // [BH][Npad/64][dpad][64]
+  // backward: the largest |v| of each tile (nullptr: not written)
+  float* vmax;        // [BH][Npad/64]
   Strides ks, vs;
   int64_t BH;
   int H, N, Npad, d, W, nch, dpad;
@@ -204,6 +206,8 @@ struct BwdArgs {
   float* out1;             // [BH][N][d] float32: dq (kRoleQ) or dk (kRoleKV)
   float* out2;             // kRoleKV: [BH][N][d] float32 dv
   float* dtable;           // kRoleQ: nullptr = no table gradient, else non-null (see dtpart)
+  const float* vmax;       // kRoleQ, table mode with dtable: [BH][Npad/64] largest |v|
+                           // of each key tile (the bound of the fixed-point sums)
   float* dtpart;           // kRoleQ: each workgroup's share of the table gradient,
                            // [B*H*nqt][prow][2gw-1]: rows dy from yq_lo - gh + 1
                            // (table rows) or the whole table (table mode, prow = 2gh-1)

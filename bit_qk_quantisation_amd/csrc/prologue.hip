@@ -158,7 +158,28 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
     }
   }
   zero_pad_bytes(sb, C, W);
+  __shared__ float vwave[kThreads / 64];
+  if (job.vmax) {
+    // largest |v| of the tile (chunks past N hold 0)
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxChunks; ++i) {
+      const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        m = fmaxf(m, fmaxf(fabsf(bf16_to_f32(static_cast<uint16_t>(w[e] & 0xffffu))),
+                           fabsf(bf16_to_f32(static_cast<uint16_t>(w[e] >> 16)))));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((threadIdx.x & 63) == 0) vwave[threadIdx.x >> 6] = m;
+  }
   __syncthreads();
+  if (job.vmax && threadIdx.x == 0) {
+    float m = vwave[0];
+    for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, vwave[i]);
+    job.vmax[blk] = m;
+  }
 
   // key scales and the tile's largest one (wave 0 holds all 64 tokens)
   if (threadIdx.x < kPackTok) {

@@ -82,3 +82,32 @@ def test_bwd_full_length_64x64():
     """N = 4096 on the 64x64 grid (the detection shape's sequence), one head."""
     announce("bwd 64x64")
     run_case(1, 1, 64, 64, 64, seed=6301)
+
+
+@pytest.mark.parametrize("gh,gw", [(14, 14), (7, 9)])
+def test_bwd_table_gradient_scales_exactly(gh, gw):
+    """Table mode sums the table gradient as integers round(dS 2^k), with k
+    chosen per workgroup from a bound that is linear in dO.  Every step of
+    the backward is linear in dO, so scaling dO by 2^10 or 2^-10 must scale
+    the table gradient by exactly that power of two (the same integers are
+    summed at a shifted scale), and the result stays within the bar of the
+    oracle at both scales."""
+    announce("bwd table gradient scaling", gh, gw)
+    B, H, d = 2, 2, 64
+    N = gh * gw
+    inp = workloads.make_inputs(B, H, N, d, seed=6300 + N, grid=(gh, gw))
+    rng = np.random.default_rng(6301 + N)
+    do = torch.from_numpy(rng.standard_normal((B, H, N, d)).astype(np.float32)).to(torch.bfloat16)
+    dev = to_dev(inp)
+    tabs = {}
+    for e in (0, 10, -10):
+        dos = (do.float() * 2.0 ** e).to(torch.bfloat16)  # exact: a power of two
+        got = bq.attention_bwd(dev["q"], dev["k"], dev["v"], dos.to(device()), dev["table"], gh, gw)
+        torch.cuda.synchronize()
+        tabs[e] = got[3].cpu().numpy().astype(np.float64)
+        assert np.isfinite(tabs[e]).all()
+    for e in (10, -10):
+        assert np.array_equal(tabs[e], tabs[0] * 2.0 ** e), e
+    ref = oracle.binary_attention_backward(np32(inp["q"]), np32(inp["k"]), np32(inp["v"]), np32(do),
+                                           np32(inp["table"]), gh, gw)["dtable"]
+    assert float(np.abs(tabs[0] - ref).max() / np.abs(ref).max()) <= TOL
