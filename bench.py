@@ -28,7 +28,10 @@ kernels in one call), so only the whole step is timed; its roofline takes the
 fp4 QK + int8 P.V matrix-core bound.
 
 --bwd times the backward instead (ba_attention_bwd: six kernels in one call
-with the table gradient, the forward recomputed inside), counted as 10*B*H*N^2*d FLOP-eq per step (the
+with the table gradient, the forward recomputed inside; with --saved,
+ba_attention_bwd_saved on the O and log-sum-exp of one earlier
+ba_attention_fwd_train call, five kernels, as a training step runs it),
+counted as 10*B*H*N^2*d FLOP-eq per step (the
 products S, dP, dV, dQ and dK of a flash-attention backward); its roofline
 takes the fp4 + bf16 matrix-core bound of those products (S on fp4, the
 other four on bf16).
@@ -250,6 +253,8 @@ def main() -> int:
     ap.add_argument("--layout", choices=("bhnd", "bnhd", "qkv"), default="bhnd",
                     help="memory layout of q, k, v and o (see above)")
     ap.add_argument("--bwd", action="store_true", help="time the backward pass (see above)")
+    ap.add_argument("--saved", action="store_true",
+                    help="with --bwd: the backward on a saved O and log-sum-exp (see above)")
     ap.add_argument("--pv", choices=("bf16", "int8"), default="bf16",
                     help="P.V precision (see above)")
     ap.add_argument("--bias", choices=("table", "dense", "dense-batch"), default="table",
@@ -319,6 +324,9 @@ def main() -> int:
                 out.data_ptr(), wsp, nbytes, sp))
 
     split = args.layout == "bhnd" and args.pv == "bf16" and not args.bwd
+    if args.saved and not args.bwd:
+        log("--saved goes with --bwd")
+        return 2
     if args.bwd:
         if args.layout != "bhnd" or dense is not None or args.pv != "bf16":
             log("--bwd runs with the contiguous layout, the table bias and bf16 P.V only")
@@ -339,6 +347,19 @@ def main() -> int:
             bq.check(lib, lib.ba_attention_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), tp, gh, gw, B, H, N, d,
                                                scale, dout.data_ptr(), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(),
                                                None if gt is None else gt.data_ptr(), wspb, nbb, sp))
+
+        if args.saved:
+            o_sv = torch.empty_like(q)
+            lse_sv = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+            bq.check(lib, lib.ba_attention_fwd_train(q.data_ptr(), k.data_ptr(), v.data_ptr(), tp, gh, gw,
+                                                     B, H, N, d, scale, o_sv.data_ptr(), lse_sv.data_ptr(),
+                                                     wsp, nbytes, sp))
+
+            def prepare():  # noqa: F811 -- the backward on the saved O and log-sum-exp
+                bq.check(lib, lib.ba_attention_bwd_saved(
+                    q.data_ptr(), k.data_ptr(), v.data_ptr(), tp, gh, gw, B, H, N, d, scale, o_sv.data_ptr(),
+                    lse_sv.data_ptr(), dout.data_ptr(), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(),
+                    None if gt is None else gt.data_ptr(), wspb, nbb, sp))
 
         def fused():  # noqa: F811
             pass
@@ -459,10 +480,12 @@ def main() -> int:
                    "pv": ("bf16 MFMA, fp32 accumulate" if args.pv == "bf16" else
                           "u8 coefficients x per-channel s8 values on int8 MFMA, int32 accumulate"),
                    "softmax": "fp32, base 2",
-                   "parallelism": "single GPU", "layout": args.layout, "bias": args.bias},
+                   "parallelism": "single GPU", "layout": args.layout, "bias": args.bias,
+                   **({"backward": "saved O and lse" if args.saved else "forward recomputed"} if args.bwd else {})},
         "roofline": {
             "bound": "mfma",
             "kernel": ("attn_fwd_kernel (fused)" if split else
+                       "whole backward on saved O and lse (5 kernels, one call)" if args.bwd and args.saved else
                        "whole backward (6 kernels, one call; forward recomputed)" if args.bwd else
                        "whole step (3 kernels, one call; fp4 QK + int8 P.V bound)" if args.pv == "int8" else
                        "whole step (prologue + fused, one strided call)"),

@@ -26,7 +26,8 @@ import torch
 from ._lib import (BinAttnError, EXPORTS, ROUTE_MFMA_FP4,  # noqa: F401
                    ROUTE_VALU_POPCOUNT, check, load)
 
-__all__ = ["pack_signs", "attention_fwd", "attention_fwd_dense_bias", "attention_fwd_int8pv", "attention_bwd",
+__all__ = ["pack_signs", "attention_fwd", "attention_fwd_dense_bias", "attention_fwd_int8pv", "attention_fwd_train",
+           "attention_bwd",
            "qk_int_dot", "workspace_bytes",
            "pack_words", "BinAttnError", "ROUTE_MFMA_FP4", "ROUTE_VALU_POPCOUNT",
            "Workspace"]
@@ -229,19 +230,61 @@ def attention_fwd_int8pv(q, k, v, table=None, gh: int = 0, gw: int = 0, scale=No
     return out
 
 
+def attention_fwd_train(q, k, v, table=None, gh: int = 0, gw: int = 0, scale=None,
+                        workspace: Workspace | None = None):
+    """attention_fwd for a training step: contiguous bf16 q, k, v [B,H,N,d]
+    (+ bf16 table) -> (bf16 O [B,H,N,d], float32 lse [B,H,N]) with
+    lse[b,h,i] = ln sum_j exp(S_ij); pass both to attention_bwd."""
+    lib = load()
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, torch.bfloat16, 4)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k and v must have the same shape")
+    B, H, N, d = q.shape
+    if table is not None:
+        _need(table, "table", torch.bfloat16, 3)
+        if tuple(table.shape) != (H, 2 * gh - 1, 2 * gw - 1):
+            raise ValueError(f"table must be [H, 2gh-1, 2gw-1] = {(H, 2*gh-1, 2*gw-1)}")
+    else:
+        gh = gw = 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = lib.ba_workspace_bytes(B, H, N, d, gh, gw)
+    if nbytes == 0:
+        raise BinAttnError(2, f"unsupported problem B={B} H={H} N={N} d={d} grid={gh}x{gw}")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    ws = (workspace or _default_ws).get(q.device, nbytes)
+    base = ws.data_ptr()
+    aligned = (base + 255) // 256 * 256
+    check(lib, lib.ba_attention_fwd_train(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), None if table is None else table.data_ptr(), int(gh), int(gw),
+        B, H, N, d, float(scale), out.data_ptr(), lse.data_ptr(), aligned, ws.numel() - (aligned - base),
+        _stream(q.device)))
+    return out, lse
+
+
 def attention_bwd(q, k, v, dout, table=None, gh: int = 0, gw: int = 0, scale=None,
-                  workspace: Workspace | None = None):
+                  workspace: Workspace | None = None, o=None, lse=None):
     """Gradients of attention_fwd for the output gradient dout: contiguous
     bf16 q, k, v, dout [B,H,N,d] (+ bf16 table [H, 2gh-1, 2gw-1]) ->
     float32 dq, dk, dv [B,H,N,d] and dtable [H, 2gh-1, 2gw-1] (None without a
     table).  The sign function takes the clipped straight-through estimator
-    and alpha = mean |x| its exact derivative."""
+    and alpha = mean |x| its exact derivative.  With o and lse from
+    attention_fwd_train the forward is not recomputed."""
     lib = load()
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _need(t, name, torch.bfloat16, 4)
     if not (q.shape == k.shape == v.shape == dout.shape):
         raise ValueError("q, k, v and dout must have the same shape")
+    if (o is None) != (lse is None):
+        raise ValueError("pass both o and lse, or neither")
     B, H, N, d = q.shape
+    if o is not None:
+        _need(o, "o", torch.bfloat16, 4)
+        _need(lse, "lse", torch.float32, 3)
+        if o.shape != q.shape or tuple(lse.shape) != (B, H, N):
+            raise ValueError("o must be [B,H,N,d] and lse [B,H,N]")
     if table is not None:
         _need(table, "table", torch.bfloat16, 3)
         if tuple(table.shape) != (H, 2 * gh - 1, 2 * gw - 1):
@@ -260,11 +303,19 @@ def attention_bwd(q, k, v, dout, table=None, gh: int = 0, gw: int = 0, scale=Non
     ws = (workspace or _default_ws).get(q.device, nbytes)
     base = ws.data_ptr()
     aligned = (base + 255) // 256 * 256
-    check(lib, lib.ba_attention_bwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), None if table is None else table.data_ptr(),
-        int(gh), int(gw), B, H, N, d, float(scale), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-        dv.data_ptr(), None if dtable is None else dtable.data_ptr(), aligned,
-        ws.numel() - (aligned - base), _stream(q.device)))
+    tp = None if table is None else table.data_ptr()
+    dtp = None if dtable is None else dtable.data_ptr()
+    ws_len = ws.numel() - (aligned - base)
+    if o is None:
+        check(lib, lib.ba_attention_bwd(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), tp, int(gh), int(gw), B, H, N, d, float(scale),
+            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dtp, aligned, ws_len,
+            _stream(q.device)))
+    else:
+        check(lib, lib.ba_attention_bwd_saved(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), tp, int(gh), int(gw), B, H, N, d, float(scale),
+            o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dtp,
+            aligned, ws_len, _stream(q.device)))
     return dq, dk, dv, dtable
 
 

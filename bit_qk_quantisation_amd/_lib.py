@@ -13,7 +13,7 @@ EXPORTS = (
     "ba_pack_signs", "ba_workspace_bytes", "ba_attention_fwd", "ba_attention_fwd_strided",
     "ba_attention_fwd_dense_bias", "ba_attention_fwd_dense_bias_prepared", "ba_attention_prepare",
     "ba_workspace_bytes_int8pv", "ba_attention_fwd_int8pv", "ba_workspace_bytes_bwd", "ba_attention_bwd",
-    "ba_attention_fwd_prepared", "ba_qk_int_dot",
+    "ba_attention_fwd_prepared", "ba_qk_int_dot", "ba_attention_fwd_train", "ba_attention_bwd_saved",
 )
 
 STATUS = {0: "BA_OK", 1: "BA_ERR_NULL", 2: "BA_ERR_SHAPE", 3: "BA_ERR_UNSUPPORTED",
@@ -79,6 +79,12 @@ def load(path=None) -> ctypes.CDLL:
     lib.ba_attention_bwd.restype = i32
     lib.ba_attention_bwd.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, ctypes.c_float, vp,
                                      vp, vp, vp, vp, vp, sz, vp]
+    lib.ba_attention_fwd_train.restype = i32
+    lib.ba_attention_fwd_train.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, ctypes.c_float,
+                                           vp, vp, vp, sz, vp]
+    lib.ba_attention_bwd_saved.restype = i32
+    lib.ba_attention_bwd_saved.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, ctypes.c_float,
+                                           vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ba_attention_prepare.restype = i32
     lib.ba_attention_prepare.argtypes = [vp, vp, vp, i32, i32, i64, i64, i64, i32, vp, sz, vp]
     lib.ba_attention_fwd_prepared.restype = i32

@@ -521,11 +521,21 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
 
 ba_status run_forward(const void* q, const void* k, const void* v, const void* bias, int gh, int gw, int64_t B,
                       int64_t H, int64_t N, int d, float scale, void* o, const int64_t* strides,
-                      const DenseBias* dense, void* workspace, size_t ws_bytes, void* stream) {
+                      const DenseBias* dense, void* workspace, size_t ws_bytes, void* stream,
+                      float* lse_out = nullptr) {
   Plan plan;
   ba_status st = make_plan(q, k, v, true, bias, gh, gw, B, H, N, d, scale, o, true, strides, dense, workspace,
                            ws_bytes, &plan);
   if (st != BA_OK) return st;
+  if (lse_out) {
+    const size_t lb = static_cast<size_t>(B * H * N) * 4, tb = static_cast<size_t>(B * H * N * d) * 2;
+    if ((reinterpret_cast<uintptr_t>(lse_out) & 3u) != 0) return fail(BA_ERR_ALIGN, "lse must be 4-byte aligned");
+    const void* others[4] = {q, k, v, o};
+    for (const void* x : others)
+      if (overlaps(lse_out, lb, x, tb)) return fail(BA_ERR_SHAPE, "lse must not overlap q, k, v or o");
+    if (overlaps(lse_out, lb, workspace, ws_bytes)) return fail(BA_ERR_WORKSPACE, "lse overlaps the workspace");
+    plan.f.lse_out = lse_out;
+  }
   int err = ba::launch_prologue(plan.p, stream);
   if (err != 0) return hip_fail(err, "prologue launch");
   err = ba::launch_attention(plan.f, plan.mode, stream);
@@ -597,6 +607,15 @@ ba_status ba_attention_fwd(const void* q, const void* k, const void* v,
   return run_forward(q, k, v, bias, gh, gw, B, H, N, d, scale, o, nullptr, nullptr, workspace, ws_bytes, stream);
 }
 
+ba_status ba_attention_fwd_train(const void* q, const void* k, const void* v,
+                                 const void* bias, int gh, int gw,
+                                 int64_t B, int64_t H, int64_t N, int d, float scale,
+                                 void* o, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  if (!lse) return fail(BA_ERR_NULL, "lse must be non-NULL");
+  return run_forward(q, k, v, bias, gh, gw, B, H, N, d, scale, o, nullptr, nullptr, workspace, ws_bytes, stream,
+                     lse);
+}
+
 ba_status ba_attention_fwd_strided(const void* q, const void* k, const void* v,
                                    const void* bias, int gh, int gw,
                                    int64_t B, int64_t H, int64_t N, int d, float scale,
@@ -615,9 +634,16 @@ ba_status ba_attention_fwd_dense_bias(const void* q, const void* k, const void* 
   return run_forward(q, k, v, nullptr, 0, 0, B, H, N, d, scale, o, strides, &dense, workspace, ws_bytes, stream);
 }
 
-ba_status ba_attention_bwd(const void* q, const void* k, const void* v, const void* bias, int gh, int gw,
-                           int64_t B, int64_t H, int64_t N, int d, float scale, const void* dout, float* dq,
-                           float* dk, float* dv, float* dtable, void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward, with the forward recomputed (o_saved == nullptr) or with the
+// caller's O and log-sum-exp from ba_attention_fwd_train.
+ba_status run_backward(const void* q, const void* k, const void* v, const void* bias, int gh, int gw, int64_t B,
+                       int64_t H, int64_t N, int d, float scale, const void* o_saved, const float* lse_saved,
+                       const void* dout, float* dq, float* dk, float* dv, float* dtable, void* workspace,
+                       size_t ws_bytes, void* stream) {
   ba_status st = check_bwd_dims(B, H, N, d);
   if (st != BA_OK) return st;
   if (!q || !dout || !dq || !dk || !dv) return fail(BA_ERR_NULL, "q, dout, dq, dk and dv must be non-NULL");
@@ -649,6 +675,20 @@ ba_status ba_attention_bwd(const void* q, const void* k, const void* v, const vo
   if (dtable && !bias) return fail(BA_ERR_SHAPE, "dtable needs a bias table");
   if (dtable && overlaps(dtable, tcount * 4, workspace, BL.total))
     return fail(BA_ERR_WORKSPACE, "dtable overlaps the workspace");
+  const bool saved = o_saved != nullptr;
+  if (saved) {
+    if (!lse_saved) return fail(BA_ERR_NULL, "lse must be non-NULL");
+    if (!aligned16(o_saved)) return fail(BA_ERR_ALIGN, "o must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(lse_saved) & 3u) != 0) return fail(BA_ERR_ALIGN, "lse must be 4-byte aligned");
+    const size_t lb = static_cast<size_t>(B * H * N) * 4;
+    for (const void* g : outs)
+      if (overlaps(g, tb * 4, o_saved, tb * 2) || overlaps(g, tb * 4, lse_saved, lb))
+        return fail(BA_ERR_SHAPE, "gradients must not overlap o or lse");
+    if (dtable && (overlaps(dtable, tcount * 4, o_saved, tb * 2) || overlaps(dtable, tcount * 4, lse_saved, lb)))
+      return fail(BA_ERR_SHAPE, "dtable must not overlap o or lse");
+    if (overlaps(o_saved, tb * 2, workspace, BL.total) || overlaps(lse_saved, lb, workspace, BL.total))
+      return fail(BA_ERR_WORKSPACE, "o and lse must not overlap the workspace");
+  }
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   uint16_t* obuf = reinterpret_cast<uint16_t*>(ws + BL.obuf);
@@ -687,6 +727,11 @@ ba_status ba_attention_bwd(const void* q, const void* k, const void* v, const vo
   p3.kv.vs = contiguous_strides(H, N, d);
   p3.kv_blocks = p1.kv_blocks;
   p3.lds = p1.lds;
+  if (saved) {
+    // the caller's log-sum-exp, in the rows' log2 units and padded layout
+    p3.lsej = ba::LseJob{lse_saved, lse, B * H, static_cast<int>(N), static_cast<int>(BL.fwd.Npad)};
+    p3.lse_blocks = (B * H * BL.fwd.Npad + ba::kThreads - 1) / ba::kThreads;
+  }
   // 6. the table gradient: the sum of the query role's per-workgroup shares
   ba::PrologueArgs p6{};
   if (dtable) {
@@ -700,7 +745,7 @@ ba_status ba_attention_bwd(const void* q, const void* k, const void* v, const vo
   bq.xrow = static_cast<const uint16_t*>(dout);
   bq.ynat = static_cast<const uint16_t*>(v);
   bq.zt = reinterpret_cast<const uint16_t*>(ws + BL.kst);
-  bq.orow = obuf;
+  bq.orow = saved ? static_cast<const uint16_t*>(o_saved) : obuf;
   bq.lse = lse;
   bq.delta = delta;
   bq.out1 = dq;
@@ -739,13 +784,33 @@ ba_status ba_attention_bwd(const void* q, const void* k, const void* v, const vo
   }
 
   int err = ba::launch_prologue(p1, stream);
-  if (err == 0) err = ba::launch_attention(f, mode, stream);
+  if (err == 0 && !saved) err = ba::launch_attention(f, mode, stream);
   if (err == 0) err = ba::launch_prologue(p3, stream);
   if (err == 0) err = ba::launch_backward(bq, ba::kRoleQ, mode, stream);
   if (err == 0 && dtable) err = ba::launch_prologue(p6, stream);
   if (err == 0) err = ba::launch_backward(bk, ba::kRoleKV, mode, stream);
   if (err != 0) return hip_fail(err, "backward launch");
   return BA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ba_status ba_attention_bwd(const void* q, const void* k, const void* v, const void* bias, int gh, int gw,
+                           int64_t B, int64_t H, int64_t N, int d, float scale, const void* dout, float* dq,
+                           float* dk, float* dv, float* dtable, void* workspace, size_t ws_bytes, void* stream) {
+  return run_backward(q, k, v, bias, gh, gw, B, H, N, d, scale, nullptr, nullptr, dout, dq, dk, dv, dtable,
+                      workspace, ws_bytes, stream);
+}
+
+ba_status ba_attention_bwd_saved(const void* q, const void* k, const void* v, const void* bias, int gh, int gw,
+                                 int64_t B, int64_t H, int64_t N, int d, float scale, const void* o,
+                                 const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                                 float* dtable, void* workspace, size_t ws_bytes, void* stream) {
+  if (!o || !lse) return fail(BA_ERR_NULL, "o and lse must be non-NULL");
+  return run_backward(q, k, v, bias, gh, gw, B, H, N, d, scale, o, lse, dout, dq, dk, dv, dtable, workspace,
+                      ws_bytes, stream);
 }
 
 size_t ba_workspace_bytes_bwd(int64_t B, int64_t H, int64_t N, int d, int gh, int gw) {

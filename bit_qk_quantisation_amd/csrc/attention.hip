@@ -799,6 +799,8 @@ attn_fwd_kernel(FwdArgs a) {
   // log2 of the softmax denominator, kept for the backward pass (0 for the
   // padding rows, which the backward reads as masked columns)
   if (a.lse && c.lh == 0) a.lse[c.tokbase + c.qi] = c.qi < a.N ? mrow + log2f(lsum) : 0.0f;
+  if (a.lse_out && c.lh == 0 && c.qi < a.N)
+    a.lse_out[static_cast<int64_t>(c.bh) * a.N + c.qi] = (mrow + log2f(lsum)) * kLn2;
   if (c.qi < a.N) {
     uint16_t* orow = a.o + token_offset(a.os, c.bh / a.H, c.head, c.qi);
 #pragma unroll

@@ -101,6 +101,15 @@ struct BiasJob {
   int64_t nrows;          // H * (2gh-1+2*kBiasPadRows) padded rows
 };
 
+// Converts a caller's log-sum-exp ([BH][N], natural log) into the backward's
+// row log2-sum-exp2 ([BH][Npad], 0 past N).  One thread per output entry.
+struct LseJob {
+  const float* in;
+  float* out;
+  int64_t BH;
+  int N, Npad;
+};
+
 // Sums the workgroups' shares of the table gradient (see BwdArgs::dtpart):
 // dtable[h][dyi][dx] = sum over b and query tiles qt of
 // share[(b H + h) nqt + qt][dyi - row0(qt)][dx], row0 = (128 qt) / gw in
@@ -113,7 +122,8 @@ struct DtReduceJob {
 
 // One launch runs the blocks of every job present (a job with 0 blocks is
 // absent), in this order: pack, key/value tiles, bias rows, value
-// statistics, the second bias rows, the table-gradient reduction.
+// statistics, the second bias rows, the table-gradient reduction, the
+// log-sum-exp conversion.
 struct PrologueArgs {
   PackJob pack;
   int64_t pack_blocks;
@@ -127,6 +137,8 @@ struct PrologueArgs {
   int64_t bias2_blocks;
   DtReduceJob dtr;
   int64_t dtr_blocks;
+  LseJob lsej;
+  int64_t lse_blocks;
   int lds;  // dynamic LDS bytes per block
 };
 
@@ -158,6 +170,8 @@ struct FwdArgs {
   uint16_t* o;             // bf16 output (strides os)
   float* lse;              // optional [BH][Npad]: mrow + log2(row sum), the
                            // logits' log2-sum-exp2 (for the backward pass)
+  float* lse_out;          // optional [B*H][N]: the same in natural-log units,
+                           // ln sum_j exp(S_ij) (the caller's copy)
   Strides qs, os;
   int B, H, N, Npad, d, W, dpad;
   int gh, gw, Lpad;

@@ -462,12 +462,23 @@ __global__ void __launch_bounds__(kThreads) prologue_kernel(PrologueArgs a) {
         }
       j.dtable[e] = acc;
     }
+    return;
+  }
+  blk -= a.dtr_blocks;
+  if (blk < a.lse_blocks) {
+    const LseJob& j = a.lsej;
+    const int64_t e = blk * kThreads + threadIdx.x;
+    if (e < j.BH * j.Npad) {
+      const int64_t bh = e / j.Npad;
+      const int i = static_cast<int>(e - bh * j.Npad);
+      j.out[e] = i < j.N ? j.in[bh * j.N + i] * kLog2e : 0.0f;
+    }
   }
 }
 
 int launch_prologue(const PrologueArgs& a, void* stream) {
   const int64_t blocks = a.pack_blocks + a.kv_blocks + a.bias_blocks + a.vstat_blocks + a.bias2_blocks +
-                        a.dtr_blocks;
+                        a.dtr_blocks + a.lse_blocks;
   hipLaunchKernelGGL(prologue_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), a.lds,
                      static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());

@@ -284,6 +284,36 @@ ba_status ba_attention_bwd(const void* q, const void* k, const void* v,
                            const void* dout, float* dq, float* dk, float* dv, float* dtable,
                            void* workspace, size_t ws_bytes, void* stream);
 
+/* ba_attention_fwd_train -- ba_attention_fwd that also writes each query
+ * row's log-sum-exp, the quantity a training step keeps for the backward:
+ *   lse  float32 [B,H,N] output, lse[b,h,i] = ln sum_j exp(S_ij), S as in
+ *        ba_attention_fwd (natural-log units; the kernel forms it as
+ *        (m_i + log2 l_i) ln 2 from its base-2 row maximum and the row sum of
+ *        the bf16 P it multiplies V with, so it carries that P's rounding,
+ *        about 2^-9 of l_i)
+ * o is bit for bit the output of ba_attention_fwd on the same arguments.
+ * lse must be 4-byte aligned and must not overlap q, k, v, o or the
+ * workspace.  Other arguments and errors as ba_attention_fwd. */
+ba_status ba_attention_fwd_train(const void* q, const void* k, const void* v,
+                                 const void* bias, int gh, int gw,
+                                 int64_t B, int64_t H, int64_t N, int d, float scale,
+                                 void* o, float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/* ba_attention_bwd_saved -- ba_attention_bwd without the recomputed forward:
+ * o (bf16 [B,H,N,d], contiguous, 16-byte aligned) and lse (float32 [B,H,N],
+ * 4-byte aligned) are the outputs of ba_attention_fwd_train on the same q,
+ * k, v, bias and scale.  Four kernels are enqueued (five with dtable); the
+ * gradients equal ba_attention_bwd's up to the rounding of lse's change of
+ * units.  o and lse must not overlap the gradients or the workspace.  Other
+ * arguments, the workspace (ba_workspace_bytes_bwd) and errors as
+ * ba_attention_bwd. */
+ba_status ba_attention_bwd_saved(const void* q, const void* k, const void* v,
+                                 const void* bias, int gh, int gw,
+                                 int64_t B, int64_t H, int64_t N, int d, float scale,
+                                 const void* o, const float* lse,
+                                 const void* dout, float* dq, float* dk, float* dv, float* dtable,
+                                 void* workspace, size_t ws_bytes, void* stream);
+
 /* QK integer-dot routes for ba_qk_int_dot. */
 #define BA_ROUTE_MFMA_FP4 0 /* +/-1 in fp4 (e2m1) on the scaled f8f6f4 MFMA;
                                the route the fused kernel uses */

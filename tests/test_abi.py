@@ -321,3 +321,37 @@ def test_bwd_validation(lib):
     big = 1 << 40
     assert call(dt=A + 8 * GB, wsb=big) == 2                               # dtable without a table
     assert call(dk=A + 5 * GB + 64, wsb=big) == 2                          # dq and dk overlap
+
+
+def test_fwd_train_validation(lib):
+    """ba_attention_fwd_train checks lse after the forward's own checks
+    (nothing is launched: every case below fails)."""
+    def call(**kw):
+        a = dict(q=A, k=A + GB, v=A + 2 * GB, o=A + 3 * GB, lse=A + 5 * GB, ws=A + 4 * GB, wsb=1 << 40)
+        a.update(kw)
+        return lib.ba_attention_fwd_train(a["q"], a["k"], a["v"], None, 0, 0, 1, 2, 64, 64, 0.125, a["o"],
+                                          a["lse"], a["ws"], a["wsb"], None)
+    assert call(lse=None) == 1
+    assert call(lse=A + 5 * GB + 2) == 4                                    # not 4-byte aligned
+    assert call(lse=A + GB + 64) == 2                                       # inside k
+    assert call(lse=A + 4 * GB + 256) == 5                                  # inside the workspace
+    assert call(wsb=16) == 5                                                # the forward's own check
+
+
+def test_bwd_saved_validation(lib):
+    """ba_attention_bwd_saved checks o and lse (nothing is launched)."""
+    def call(**kw):
+        a = dict(q=A, k=A + GB, v=A + 2 * GB, o=A + 9 * GB, lse=A + 10 * GB, do=A + 3 * GB, dq=A + 5 * GB,
+                 dk=A + 6 * GB, dv=A + 7 * GB, ws=A + 4 * GB, wsb=1 << 40)
+        a.update(kw)
+        return lib.ba_attention_bwd_saved(a["q"], a["k"], a["v"], None, 0, 0, 1, 2, 64, 64, 0.125, a["o"],
+                                          a["lse"], a["do"], a["dq"], a["dk"], a["dv"], None, a["ws"], a["wsb"],
+                                          None)
+    assert call(o=None) == 1
+    assert call(lse=None) == 1
+    assert call(o=A + 9 * GB + 8) == 4                                      # o not 16-byte aligned
+    assert call(lse=A + 10 * GB + 2) == 4                                   # lse not 4-byte aligned
+    assert call(o=A + 5 * GB) == 2                                          # o overlaps dq
+    assert call(lse=A + 6 * GB + 4) == 2                                    # lse overlaps dk
+    assert call(lse=A + 4 * GB + 256) == 5                                  # lse inside the workspace
+    assert call(wsb=16) == 5

@@ -111,3 +111,60 @@ def test_bwd_table_gradient_scales_exactly(gh, gw):
     ref = oracle.binary_attention_backward(np32(inp["q"]), np32(inp["k"]), np32(inp["v"]), np32(do),
                                            np32(inp["table"]), gh, gw)["dtable"]
     assert float(np.abs(tabs[0] - ref).max() / np.abs(ref).max()) <= TOL
+
+
+TRAIN_CASES = [
+    # B, H, gh, gw, d, bias, q_scale
+    (2, 2, 8, 8, 64, True, 1.0),      # table mode
+    (1, 2, 4, 32, 64, True, 1.0),     # table rows
+    (1, 2, 4, 32, 64, True, 8.0),     # table rows, exact path (large logits)
+    (2, 1, 1, 100, 32, False, 1.0),   # no bias, ragged tile
+]
+
+
+@pytest.mark.parametrize("B,H,gh,gw,d,bias,q_scale", TRAIN_CASES)
+def test_fwd_train_and_saved_bwd(B, H, gh, gw, d, bias, q_scale):
+    """attention_fwd_train gives attention_fwd's O bit for bit and each row's
+    ln sum_j exp(S_ij); attention_bwd with that O and lse gives the
+    gradients of the recomputing backward.
+
+    lse bar: the kernel forms the row sum l from the bf16 P it multiplies V
+    with (relative rounding at most 2^-9 per term, so at most 2^-9 for the
+    sum), and m + log2 l in fp32, so |lse - lse_oracle| <= 2^-9 + a few ulps:
+    4e-3 here.  The two backwards differ only by lse's change of units
+    (natural log and back, two fp32 roundings), which can flip a bf16 rounding
+    of P or dS now and then: 1e-3 of each gradient's largest entry."""
+    announce("fwd train / saved bwd", B, H, gh, gw, d, bias, q_scale)
+    N = gh * gw
+    inp = workloads.make_inputs(B, H, N, d, seed=6400 + N + d, grid=(gh, gw) if bias else None, bias=bias,
+                                q_scale=q_scale)
+    dev = to_dev(inp)
+    tg, tgh, tgw = (dev["table"], inp["gh"], inp["gw"]) if bias else (None, 0, 0)
+    o_ref = bq.attention_fwd(dev["q"], dev["k"], dev["v"], tg, tgh, tgw)
+    o, lse = bq.attention_fwd_train(dev["q"], dev["k"], dev["v"], tg, tgh, tgw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    ref = oracle.binary_attention_rows(np32(inp["q"]), np32(inp["k"]), np32(inp["v"]),
+                                       np32(inp["table"]) if bias else None, inp["gh"], inp["gw"], keep=True)
+    s = ref["S"]
+    smax = s.max(axis=-1, keepdims=True)
+    lse_ref = (smax + np.log(np.exp(s - smax).sum(axis=-1, keepdims=True)))[..., 0]
+    err = float(np.abs(lse.cpu().numpy().astype(np.float64) - lse_ref).max())
+    print("lse max abs error", err)
+    assert err <= 4e-3
+
+    rng = np.random.default_rng(6401 + N)
+    do = torch.from_numpy(rng.standard_normal((B, H, N, d)).astype(np.float32)).to(torch.bfloat16).to(device())
+    g_re = bq.attention_bwd(dev["q"], dev["k"], dev["v"], do, tg, tgh, tgw)
+    g_sv = bq.attention_bwd(dev["q"], dev["k"], dev["v"], do, tg, tgh, tgw, o=o, lse=lse)
+    torch.cuda.synchronize()
+    gref = oracle.binary_attention_backward(np32(inp["q"]), np32(inp["k"]), np32(inp["v"]), np32(do.cpu()),
+                                            np32(inp["table"]) if bias else None, inp["gh"], inp["gw"])
+    for name, a, b in zip(("dq", "dk", "dv", "dtable"), g_re, g_sv):
+        if a is None:
+            assert b is None
+            continue
+        a64, b64 = a.cpu().numpy().astype(np.float64), b.cpu().numpy().astype(np.float64)
+        scale = np.abs(a64).max()
+        assert float(np.abs(a64 - b64).max()) <= 1e-3 * scale, name
+        assert float(np.abs(b64 - gref[name]).max() / np.abs(gref[name]).max()) <= TOL, name
