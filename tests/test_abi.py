@@ -355,3 +355,15 @@ def test_bwd_saved_validation(lib):
     assert call(lse=A + 6 * GB + 4) == 2                                    # lse overlaps dk
     assert call(lse=A + 4 * GB + 256) == 5                                  # lse inside the workspace
     assert call(wsb=16) == 5
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus above 1 exits with a message, before
+    it touches a GPU."""
+    import subprocess
+    import sys
+    root = pathlib.Path(__file__).resolve().parents[1]
+    r = subprocess.run([sys.executable, str(root / "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       cwd=root, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
