@@ -323,7 +323,12 @@ def main() -> int:
                 q.data_ptr(), dense.data_ptr(), dsb, dense.stride(1), dense.stride(2), B, H, N, d, scale,
                 out.data_ptr(), wsp, nbytes, sp))
 
-    split = args.layout == "bhnd" and args.pv == "bf16" and not args.bwd
+    # Short sequences (N <= 256, d in {32, 64}, a table that is not read in
+    # rows, or none) run as one launch that packs K and V in LDS: there is no
+    # prologue to time apart, so the step is the whole ba_attention_fwd call.
+    one_launch = (args.layout == "bhnd" and args.pv == "bf16" and not args.bwd and dense is None
+                  and N <= 256 and d in (32, 64) and (table is None or gw % 32 != 0))
+    split = args.layout == "bhnd" and args.pv == "bf16" and not args.bwd and not one_launch
     if args.saved and not args.bwd:
         log("--saved goes with --bwd")
         return 2
@@ -374,6 +379,13 @@ def main() -> int:
         def prepare():  # noqa: F811 -- one call runs all three kernels
             bq.check(lib, lib.ba_attention_fwd_int8pv(q.data_ptr(), k.data_ptr(), v.data_ptr(), tp, gh, gw,
                                                       B, H, N, d, scale, out.data_ptr(), wsp8, nb8, sp))
+
+        def fused():  # noqa: F811
+            pass
+    elif one_launch:
+        def prepare():  # noqa: F811 -- the whole forward, one kernel
+            bq.check(lib, lib.ba_attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), tp, gh, gw, B, H, N, d,
+                                               scale, out.data_ptr(), wsp, nbytes, sp))
 
         def fused():  # noqa: F811
             pass
@@ -488,6 +500,7 @@ def main() -> int:
                        "whole backward on saved O and lse (5 kernels, one call)" if args.bwd and args.saved else
                        "whole backward (6 kernels, one call; forward recomputed)" if args.bwd else
                        "whole step (3 kernels, one call; fp4 QK + int8 P.V bound)" if args.pv == "int8" else
+                       "attn_fwd_small_kernel (the whole step: one launch, K and V packed in LDS)" if one_launch else
                        "whole step (prologue + fused, one strided call)"),
             "achieved": round(fused_tf, 1),
             "peak": round(peak, 1),

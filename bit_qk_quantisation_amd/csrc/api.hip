@@ -455,6 +455,10 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   f.o = static_cast<uint16_t*>(o);
   f.qs = vs[0];
   f.os = vs[3];
+  f.k = static_cast<const uint16_t*>(k);
+  f.v = static_cast<const uint16_t*>(v);
+  f.ks = vs[1];
+  f.vs = vs[2];
   f.B = static_cast<int>(B);
   f.H = static_cast<int>(H);
   f.N = static_cast<int>(N);
@@ -535,6 +539,17 @@ ba_status run_forward(const void* q, const void* k, const void* v, const void* b
       if (overlaps(lse_out, lb, x, tb)) return fail(BA_ERR_SHAPE, "lse must not overlap q, k, v or o");
     if (overlaps(lse_out, lb, workspace, ws_bytes)) return fail(BA_ERR_WORKSPACE, "lse overlaps the workspace");
     plan.f.lse_out = lse_out;
+  }
+  if (!dense && ba::small_supported(N, d, plan.mode)) {
+    // short sequences: one launch, the keys and values packed in LDS
+    ba::FwdArgs f = plan.f;
+    const int sl = ba::small_static_lds(f.dpad / 32, plan.mode);
+    f.dyn_lds = fused_dynamic_lds(sl, ba::fwd_table_lds(f, plan.mode), f.nwg);
+    if (sl + f.dyn_lds <= kMaxLds) {
+      const int err = ba::launch_attention_small(f, plan.mode, stream);
+      if (err != 0) return hip_fail(err, "attention launch");
+      return BA_OK;
+    }
   }
   int err = ba::launch_prologue(plan.p, stream);
   if (err != 0) return hip_fail(err, "prologue launch");

@@ -604,8 +604,11 @@ __device__ __forceinline__ float run_exact_pass(const Ctx<NCH>& c, TileBuf<NCH, 
 // query tile, this lane's packed query, the per-lane LDS offsets, the
 // buffer resources of the tile copies, the bias table in LDS (table mode).
 // Returns the logit bound M (log2 units) of the workgroup.
-template <int NCH, int CB, int BIAS>
-__device__ __forceinline__ float workgroup_setup(Ctx<NCH>& c, const FwdArgs& a, float* red, float* s_table) {
+// SMALL: the one-launch kernel for short sequences, whose key scales are in
+// LDS already; kmax_small is their maximum over the head.
+template <int NCH, int CB, int BIAS, bool SMALL = false>
+__device__ __forceinline__ float workgroup_setup(Ctx<NCH>& c, const FwdArgs& a, float* red, float* s_table,
+                                                 float kmax_small = 0.0f) {
   c.a = &a;
   c.table = s_table;
   c.tid = threadIdx.x;
@@ -731,7 +734,10 @@ __device__ __forceinline__ float workgroup_setup(Ctx<NCH>& c, const FwdArgs& a, 
   // ---- logit bound M (log2 units) ------------------------------------------
   const int nblk = a.Npad / 64;
   float km = 0.0f, bm = 0.0f;
-  for (int e = c.tid; e < nblk; e += kThreads) km = fmaxf(km, a.kmax_blk[static_cast<int64_t>(c.bh) * nblk + e]);
+  if (SMALL)
+    km = kmax_small;
+  else
+    for (int e = c.tid; e < nblk; e += kThreads) km = fmaxf(km, a.kmax_blk[static_cast<int64_t>(c.bh) * nblk + e]);
   if (BIAS == kBiasRows) {
     const int rows = 2 * a.gh - 1;
     for (int e = c.tid; e < rows; e += kThreads) bm = fmaxf(bm, a.bias_row_max[c.head * rows + e]);
@@ -753,37 +759,9 @@ __device__ __forceinline__ float workgroup_setup(Ctx<NCH>& c, const FwdArgs& a, 
   return a.qscale * qm * km * static_cast<float>(a.d) + bm;
 }
 
-// Waves per SIMD the register budget is sized for (accumulator blocks).
-template <int NB>
-struct Occupancy {
-  static constexpr int kWaves = fwd_waves_for_blocks(NB);
-};
-
-template <int NCH, int CB, bool XONES, int BIAS>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<CB + XONES>::kWaves)))
-attn_fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb0;
-  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb1;
-  __shared__ float red[kThreads / 64];
-  extern __shared__ __attribute__((aligned(16))) float s_table[];
-
-  Ctx<NCH> c;
-  const float M = workgroup_setup<NCH, CB, BIAS>(c, a, red, s_table);
-
-  Acc<CB, XONES> acc;
-  float mrow = 0.0f;  // the offset the row sums are taken against (log2 units)
-  if constexpr (BIAS == kBiasDense) {
-    // no bound on a dense bias short of reading all of it: exact softmax
-    (void)M;
-    mrow = run_exact_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
-  } else {
-    if (M <= kFastMaxLogit)  // false for NaN as well
-      run_fast_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
-    else
-      mrow = run_exact_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
-  }
-
-  // ---- epilogue: O = O^T / l, bf16, one query per lane --------------------
+// O = O^T / l, bf16, one query per lane; the rows' log-sum-exp when asked.
+template <int NCH, int CB, bool XONES>
+__device__ __forceinline__ void fwd_epilogue(const Ctx<NCH>& c, const FwdArgs& a, Acc<CB, XONES>& acc, float mrow) {
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) pin_uniform(acc.o[cb]);
   float lsum;
@@ -816,6 +794,206 @@ attn_fwd_kernel(FwdArgs a) {
         }
       }
   }
+}
+
+// Waves per SIMD the register budget is sized for (accumulator blocks).
+template <int NB>
+struct Occupancy {
+  static constexpr int kWaves = fwd_waves_for_blocks(NB);
+};
+
+template <int NCH, int CB, bool XONES, int BIAS>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<CB + XONES>::kWaves)))
+attn_fwd_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb0;
+  __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb1;
+  __shared__ float red[kThreads / 64];
+  extern __shared__ __attribute__((aligned(16))) float s_table[];
+
+  Ctx<NCH> c;
+  const float M = workgroup_setup<NCH, CB, BIAS>(c, a, red, s_table);
+
+  Acc<CB, XONES> acc;
+  float mrow = 0.0f;  // the offset the row sums are taken against (log2 units)
+  if constexpr (BIAS == kBiasDense) {
+    // no bound on a dense bias short of reading all of it: exact softmax
+    (void)M;
+    mrow = run_exact_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
+  } else {
+    if (M <= kFastMaxLogit)  // false for NaN as well
+      run_fast_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
+    else
+      mrow = run_exact_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
+  }
+
+  fwd_epilogue<NCH, CB, XONES>(c, a, acc, mrow);
+}
+
+// -------------------------------------------------- one launch, short N ---
+// For N <= kSmallKeys and d in {32, 64} (table or no bias) a workgroup packs
+// all keys and values of its head straight into LDS, in exactly the tile
+// layouts the prologue writes and the copies bring (so the result is bit for
+// bit the two-launch path's), and runs the key loop without copies: one
+// launch instead of two and no round trip of the key operands and V^T
+// through HBM.  Each head's K and V are read by its ceil(N / 128)
+// workgroups.
+constexpr int kSmallTiles = 4;
+constexpr int kSmallKeys = kSmallTiles * kBN;
+
+// P.V slot of key r (0..15) of a 16-key group in the V^T tile: the inverse of
+// the prologue's slot order (slots 8h..8h+3 = keys 4h..4h+3, slots
+// 8h+4..8h+7 = keys 8+4h..8+4h+3).
+__device__ __forceinline__ int vt_key_slot(int key) {
+  const int r = key & 15;
+  return (key & ~15) + 8 * ((r >> 2) & 1) + (r & 3) + 4 * (r >> 3);
+}
+
+template <int CB, int BIAS>
+__device__ __forceinline__ float pack_head(const FwdArgs& a, int bh, TileBuf<1, CB, BIAS>* tiles, float* red) {
+  const int64_t b = bh / a.H, h = bh - b * a.H;
+  const int nkt = (a.N + kBN - 1) / kBN;
+  const int W = a.d / 32;
+  float km = 0.0f;
+  // keys: one task per (key, 32-channel word); the word's fp4 operand dwords
+  // and its sum of |k| (chunk by chunk, in the prologue's order), the two
+  // words of a key in lanes e and e ^ 1
+  for (int e = threadIdx.x; e < nkt * kBN * 2; e += kThreads) {
+    const int key = e >> 1, half = e & 1;
+    uint32_t w = 0;
+    float part = 0.0f;
+    if (key < a.N && half < W) {
+      const uint16_t* row = a.k + token_offset(a.ks, b, h, key) + 32 * half;
+      float p[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) w |= chunk_signs(*reinterpret_cast<const uint4*>(row + 8 * kk), p[kk]) << (8 * kk);
+      part = (p[0] + p[1]) + (p[2] + p[3]);
+    }
+    TileBuf<1, CB, BIAS>& tb = tiles[key >> 6];
+    tb.k[(key & 63) * 2 + half] = expand_signs_fp4(w, fp4_magnitude(word_valid(a.d, half)));
+    const float other = __shfl_xor(part, 1, 64);
+    if (half == 0) {
+      const float alpha = key < a.N ? (part + other) / static_cast<float>(a.d) : 0.0f;
+      tb.ak[key & 63] = alpha;
+      km = fmaxf(km, alpha);
+      if (BIAS == kBiasTable) {
+        const int j = key < a.N ? key : a.N - 1;
+        const int yj = j / a.gw;
+        tb.gk[key & 63] = yj * (2 * a.gw - 1) + (j - yj * a.gw);
+      }
+    }
+  }
+  // values: one task per (key, 8-channel chunk), written into V^T at the
+  // key's slot, chunk q at position q ^ ((c >> 1) & 7) of row c; padded keys
+  // get zeros
+  const int C = a.d / 8;
+  for (int e = threadIdx.x; e < nkt * kBN * C; e += kThreads) {
+    const int key = e / C, ch = e - key * C;
+    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+    if (key < a.N) raw = *reinterpret_cast<const uint4*>(a.v + token_offset(a.vs, b, h, key) + 8 * ch);
+    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint16_t* vt = tiles[key >> 6].vt;
+    const int slot = vt_key_slot(key & 63);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int cc = 8 * ch + i;
+      const uint16_t x = static_cast<uint16_t>((wv[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+      vt[cc * kBN + ((((slot >> 3) ^ ((cc >> 1) & 7))) << 3) + (slot & 7)] = x;
+    }
+  }
+  return block_max(km, red);  // its barriers also publish the tiles
+}
+
+// One tile of the short-N loop (no copies, no barrier).
+template <bool FIRST, bool FAST, int CB, int BIAS>
+__device__ __forceinline__ void small_tile(const Ctx<1>& c, const TileBuf<1, CB, BIAS>& tb, int t,
+                                           Acc<CB, true>& acc, PendingPV<CB>& pp, float& mrow) {
+  const FwdArgs& a = *c.a;
+  KeyPos kp;
+  kp.k0 = t * kBN;
+  kp.ky[0] = kp.ky[1] = kp.kx[0] = 0;
+  kp.kx[1] = 32;
+  if (kp.k0 + kBN <= a.N) {
+    if (FAST) {
+      pipelined_block<false, !FIRST, 1, CB, true, BIAS>(c, tb, kp, 0, pp, acc);
+      pipelined_block<false, true, 1, CB, true, BIAS>(c, tb, kp, 1, pp, acc);
+    } else {
+      exact_block<false, !FIRST, 1, CB, true, BIAS>(c, tb, kp, 0, pp, acc, mrow);
+      exact_block<false, true, 1, CB, true, BIAS>(c, tb, kp, 1, pp, acc, mrow);
+    }
+  } else {
+    if (FAST) {
+      pipelined_block<true, !FIRST, 1, CB, true, BIAS>(c, tb, kp, 0, pp, acc);
+      pipelined_block<true, true, 1, CB, true, BIAS>(c, tb, kp, 1, pp, acc);
+    } else {
+      exact_block<true, !FIRST, 1, CB, true, BIAS>(c, tb, kp, 0, pp, acc, mrow);
+      exact_block<true, true, 1, CB, true, BIAS>(c, tb, kp, 1, pp, acc, mrow);
+    }
+  }
+}
+
+template <bool FAST, int CB, int BIAS>
+__device__ __forceinline__ float small_pass(const Ctx<1>& c, const TileBuf<1, CB, BIAS>* tiles, Acc<CB, true>& acc) {
+  const FwdArgs& a = *c.a;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) acc.o[cb] = v16f{};
+  acc.rs[0] = acc.rs[1] = 0.0f;
+  float mrow = FAST ? 0.0f : -INFINITY;
+  const int nkt = (a.N + kBN - 1) / kBN;
+  PendingPV<CB> pp;
+  small_tile<true, FAST, CB, BIAS>(c, tiles[0], 0, acc, pp, mrow);
+  for (int t = 1; t < nkt; ++t) small_tile<false, FAST, CB, BIAS>(c, tiles[t], t, acc, pp, mrow);
+#pragma unroll
+  for (int i = 0; i < 2 * CB; ++i) pv_mfma<CB, true>(i, pp, acc);
+  acc.rs[0] = sum_halves(acc.rs[0] + acc.rs[1]);
+  return mrow;
+}
+
+template <int CB, int BIAS>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<CB + 1>::kWaves)))
+attn_fwd_small_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) TileBuf<1, CB, BIAS> tiles[kSmallTiles];
+  __shared__ float red[kThreads / 64];
+  extern __shared__ __attribute__((aligned(16))) float s_table[];
+  int wg = blockIdx.x;
+  if (a.xcd_remap) {
+    const int per = a.nwg >> 3;
+    wg = (wg & 7) * per + (wg >> 3);
+  }
+  const float kmax = pack_head<CB, BIAS>(a, wg / a.nqt, tiles, red);
+  Ctx<1> c;
+  const float M = workgroup_setup<1, CB, BIAS, true>(c, a, red, s_table, kmax);
+  Acc<CB, true> acc;
+  float mrow = 0.0f;
+  if (M <= kFastMaxLogit)
+    small_pass<true, CB, BIAS>(c, tiles, acc);
+  else
+    mrow = small_pass<false, CB, BIAS>(c, tiles, acc);
+  fwd_epilogue<1, CB, true>(c, a, acc, mrow);
+}
+
+int small_static_lds(int cb, int mode) {
+  if (mode == kBiasTable)
+    return cb == 1 ? static_cast<int>(sizeof(TileBuf<1, 1, kBiasTable>)) * kSmallTiles + 16
+                   : static_cast<int>(sizeof(TileBuf<1, 2, kBiasTable>)) * kSmallTiles + 16;
+  return cb == 1 ? static_cast<int>(sizeof(TileBuf<1, 1, kBiasNone>)) * kSmallTiles + 16
+                 : static_cast<int>(sizeof(TileBuf<1, 2, kBiasNone>)) * kSmallTiles + 16;
+}
+
+bool small_supported(int64_t N, int d, int mode) {
+  return N <= kSmallKeys && (d == 32 || d == 64) && (mode == kBiasNone || mode == kBiasTable);
+}
+
+int launch_attention_small(const FwdArgs& a, int mode, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(a.nwg), block(kThreads);
+  const int lds = a.dyn_lds;
+  const int cb = a.dpad / 32;
+  if (cb == 1 && mode == kBiasTable) hipLaunchKernelGGL((attn_fwd_small_kernel<1, kBiasTable>), grid, block, lds, s, a);
+  else if (cb == 1 && mode == kBiasNone) hipLaunchKernelGGL((attn_fwd_small_kernel<1, kBiasNone>), grid, block, lds, s, a);
+  else if (cb == 2 && mode == kBiasTable) hipLaunchKernelGGL((attn_fwd_small_kernel<2, kBiasTable>), grid, block, lds, s, a);
+  else if (cb == 2 && mode == kBiasNone) hipLaunchKernelGGL((attn_fwd_small_kernel<2, kBiasNone>), grid, block, lds, s, a);
+  else return static_cast<int>(hipErrorInvalidValue);
+  return static_cast<int>(hipGetLastError());
 }
 
 // ------------------------------------------------------ 8-bit P.V path ---

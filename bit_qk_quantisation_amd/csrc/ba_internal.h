@@ -181,6 +181,10 @@ struct FwdArgs {
   int nwg;                 // workgroups
   int xcd_remap;           // 1: spread consecutive heads over the 8 XCDs
   int dyn_lds;             // dynamic LDS bytes per workgroup (table and/or padding)
+  // the one-launch short-N kernel reads K and V itself (strides ks, vs)
+  const uint16_t* k;
+  const uint16_t* v;
+  Strides ks, vs;
   int table_flip;          // kBiasTable: read the table flipped in both axes
   int prio_balance;        // 1: lower the wave priority over the last keys
                            // (every workgroup of the grid is resident at once)
@@ -199,6 +203,11 @@ int fwd_waves_per_simd(int dpad, int d);
 
 // Launch the fused kernel (template selected from d and the bias mode).
 int launch_attention(const FwdArgs& a, int mode, void* stream);
+// The one-launch kernel for short sequences (no prologue): N <= 256,
+// d in {32, 64}, table or no bias; reads a.k, a.v.
+bool small_supported(int64_t N, int d, int mode);
+int small_static_lds(int cb, int mode);
+int launch_attention_small(const FwdArgs& a, int mode, void* stream);
 // The fused kernel of the 8-bit P.V forward (d <= 128; no dense bias).
 int launch_attention_int8(const FwdArgs& a, int mode, void* stream);
 
