@@ -840,12 +840,12 @@ attn_fwd_kernel(FwdArgs a) {
 constexpr int kSmallTiles = 4;
 constexpr int kSmallKeys = kSmallTiles * kBN;
 
-// P.V slot of key r (0..15) of a 16-key group in the V^T tile: the inverse of
-// the prologue's slot order (slots 8h..8h+3 = keys 4h..4h+3, slots
-// 8h+4..8h+7 = keys 8+4h..8+4h+3).
-__device__ __forceinline__ int vt_key_slot(int key) {
-  const int r = key & 15;
-  return (key & ~15) + 8 * ((r >> 2) & 1) + (r & 3) + 4 * (r >> 3);
+// Key (within its 64-key tile) that P.V slot `slot` of the V^T tile holds:
+// slots 8h..8h+3 of a 16-slot group hold keys 4h..4h+3, slots 8h+4..8h+7
+// keys 8+4h..8+4h+3 (the order in which a lane holds its keys after QK).
+__device__ __forceinline__ int vt_slot_key_fwd(int slot) {
+  const int g = slot >> 4, s16 = slot & 15, hh = s16 >> 3, s = s16 & 7;
+  return g * 16 + (s < 4 ? 4 * hh + s : 8 + 4 * hh + (s - 4));
 }
 
 template <int CB, int BIAS>
@@ -882,22 +882,33 @@ __device__ __forceinline__ float pack_head(const FwdArgs& a, int bh, TileBuf<1, 
       }
     }
   }
-  // values: one task per (key, 8-channel chunk), written into V^T at the
-  // key's slot, chunk q at position q ^ ((c >> 1) & 7) of row c; padded keys
-  // get zeros
+  // values: one task per (tile, 8-slot chunk q, 8-channel group g): the 8
+  // keys of slots 8q..8q+7 are loaded, transposed in registers, and leave as
+  // the 16-byte chunks q of rows 8g..8g+7 of V^T, chunk q of row c at
+  // position q ^ ((c >> 1) & 7); padded keys give zeros
   const int C = a.d / 8;
-  for (int e = threadIdx.x; e < nkt * kBN * C; e += kThreads) {
-    const int key = e / C, ch = e - key * C;
-    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-    if (key < a.N) raw = *reinterpret_cast<const uint4*>(a.v + token_offset(a.vs, b, h, key) + 8 * ch);
-    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
-    uint16_t* vt = tiles[key >> 6].vt;
-    const int slot = vt_key_slot(key & 63);
+  for (int e = threadIdx.x; e < nkt * 8 * C; e += kThreads) {
+    const int t = e / (8 * C), r = e - t * 8 * C, q = r / C, g = r - q * C;
+    uint4 x[8];
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      const int key = t * kBN + vt_slot_key_fwd(8 * q + sl);
+      x[sl] = key < a.N ? *reinterpret_cast<const uint4*>(a.v + token_offset(a.vs, b, h, key) + 8 * g)
+                        : make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint16_t* vt = tiles[t].vt;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int cc = 8 * ch + i;
-      const uint16_t x = static_cast<uint16_t>((wv[i >> 1] >> (16 * (i & 1))) & 0xffffu);
-      vt[cc * kBN + ((((slot >> 3) ^ ((cc >> 1) & 7))) << 3) + (slot & 7)] = x;
+      const int cc = 8 * g + i;
+      // halfword i of each key's chunk; dword m = slots 2m, 2m + 1
+      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t w[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t lo = (&x[2 * m].x)[i >> 1], hi = (&x[2 * m + 1].x)[i >> 1];
+        w[m] = __builtin_amdgcn_perm(hi, lo, sel);
+      }
+      *reinterpret_cast<uint4*>(vt + cc * kBN + ((q ^ ((cc >> 1) & 7)) << 3)) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
   return block_max(km, red);  // its barriers also publish the tiles
