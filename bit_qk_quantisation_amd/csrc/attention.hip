@@ -129,6 +129,31 @@ __device__ __forceinline__ KeyPos next_keys(const KeyPos& p, int gw) {
   return n;
 }
 
+// Floats of the workgroup reductions' LDS scratch (three per wave).
+constexpr int kRedFloats = 3 * kThreads / 64;
+
+// The workgroup maxima of three values with one pair of barriers.
+__device__ __forceinline__ v3f block_max3(float x, float y, float z, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    x = fmaxf(x, __shfl_xor(x, off, 64));
+    y = fmaxf(y, __shfl_xor(y, off, 64));
+    z = fmaxf(z, __shfl_xor(z, off, 64));
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    red[3 * (threadIdx.x >> 6)] = x;
+    red[3 * (threadIdx.x >> 6) + 1] = y;
+    red[3 * (threadIdx.x >> 6) + 2] = z;
+  }
+  __syncthreads();
+  v3f r = {red[0], red[1], red[2]};
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w)
+    r = v3f{fmaxf(r[0], red[3 * w]), fmaxf(r[1], red[3 * w + 1]), fmaxf(r[2], red[3 * w + 2])};
+  return r;
+}
+
 __device__ __forceinline__ float block_sum(float v, float* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -745,6 +770,7 @@ __device__ __forceinline__ float workgroup_setup(Ctx<NCH>& c, const FwdArgs& a, 
     // the whole table goes to LDS once, as float32 * log2e
     const int n = (2 * a.gh - 1) * (2 * a.gw - 1);
     const uint16_t* t = a.table + static_cast<int64_t>(c.head) * n;
+#pragma unroll 4
     for (int e = c.tid; e < n; e += kThreads) {
       const float v = kLog2e * bf16_to_f32(t[a.table_flip ? n - 1 - e : e]);  // flip: both axes
       c.table[e] = v;
@@ -753,10 +779,8 @@ __device__ __forceinline__ float workgroup_setup(Ctx<NCH>& c, const FwdArgs& a, 
     const int yc = c.yq < a.gh ? c.yq : a.gh - 1;
     c.fidx = (yc + a.gh - 1) * (2 * a.gw - 1) + c.xq + a.gw - 1;
   }
-  km = block_max(km, red);
-  bm = block_max(bm, red);
-  const float qm = block_max(alpha_q, red);
-  return a.qscale * qm * km * static_cast<float>(a.d) + bm;
+  const v3f mx = block_max3(km, bm, alpha_q, red);
+  return a.qscale * mx[2] * mx[0] * static_cast<float>(a.d) + mx[1];
 }
 
 // O = O^T / l, bf16, one query per lane; the rows' log-sum-exp when asked.
@@ -807,7 +831,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(O
 attn_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb0;
   __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb1;
-  __shared__ float red[kThreads / 64];
+  __shared__ float red[kRedFloats];
   extern __shared__ __attribute__((aligned(16))) float s_table[];
 
   Ctx<NCH> c;
@@ -963,7 +987,7 @@ template <int CB, int BIAS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<CB + 1>::kWaves)))
 attn_fwd_small_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) TileBuf<1, CB, BIAS> tiles[kSmallTiles];
-  __shared__ float red[kThreads / 64];
+  __shared__ float red[kRedFloats];
   extern __shared__ __attribute__((aligned(16))) float s_table[];
   int wg = blockIdx.x;
   if (a.xcd_remap) {
@@ -984,10 +1008,10 @@ attn_fwd_small_kernel(FwdArgs a) {
 
 int small_static_lds(int cb, int mode) {
   if (mode == kBiasTable)
-    return cb == 1 ? static_cast<int>(sizeof(TileBuf<1, 1, kBiasTable>)) * kSmallTiles + 16
-                   : static_cast<int>(sizeof(TileBuf<1, 2, kBiasTable>)) * kSmallTiles + 16;
-  return cb == 1 ? static_cast<int>(sizeof(TileBuf<1, 1, kBiasNone>)) * kSmallTiles + 16
-                 : static_cast<int>(sizeof(TileBuf<1, 2, kBiasNone>)) * kSmallTiles + 16;
+    return cb == 1 ? static_cast<int>(sizeof(TileBuf<1, 1, kBiasTable>)) * kSmallTiles + kRedFloats * 4
+                   : static_cast<int>(sizeof(TileBuf<1, 2, kBiasTable>)) * kSmallTiles + kRedFloats * 4;
+  return cb == 1 ? static_cast<int>(sizeof(TileBuf<1, 1, kBiasNone>)) * kSmallTiles + kRedFloats * 4
+                 : static_cast<int>(sizeof(TileBuf<1, 2, kBiasNone>)) * kSmallTiles + kRedFloats * 4;
 }
 
 bool small_supported(int64_t N, int d, int mode) {
@@ -1118,7 +1142,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(O
 attn_fwd_int8_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb0;
   __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb1;
-  __shared__ float red[kThreads / 64];
+  __shared__ float red[kRedFloats];
   extern __shared__ __attribute__((aligned(16))) float s_table[];
 
   Ctx<NCH> c;
@@ -1528,7 +1552,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 attn_bwd_kernel(BwdArgs ba) {
   __shared__ __attribute__((aligned(16))) BwdTileBuf<ROLE, NCH, CB, BIAS> tb0;
   __shared__ __attribute__((aligned(16))) BwdTileBuf<ROLE, NCH, CB, BIAS> tb1;
-  __shared__ float red[kThreads / 64];
+  __shared__ float red[kRedFloats];
   extern __shared__ __attribute__((aligned(16))) float s_table[];
   const FwdArgs& a = ba.f;
 
@@ -1667,7 +1691,7 @@ attn_bwd_kernel(BwdArgs ba) {
 
 template <int ROLE, int BIAS>
 static int bwd_static_lds_for(int cb) {
-  constexpr int kRed = kThreads / 64 * 4;
+  constexpr int kRed = kRedFloats * 4;
   switch (cb) {
     case 1: return 2 * sizeof(BwdTileBuf<ROLE, 1, 1, BIAS>) + kRed;
     case 2: return 2 * sizeof(BwdTileBuf<ROLE, 1, 2, BIAS>) + kRed;
@@ -1742,7 +1766,7 @@ int fwd_table_lds(const FwdArgs& a, int mode) {
 
 template <int BIAS>
 static int static_lds_for(int cb) {
-  constexpr int kRed = kThreads / 64 * 4;
+  constexpr int kRed = kRedFloats * 4;
   switch (cb) {
     case 1: return 2 * sizeof(TileBuf<1, 1, BIAS>) + kRed;
     case 2: return 2 * sizeof(TileBuf<1, 2, BIAS>) + kRed;
