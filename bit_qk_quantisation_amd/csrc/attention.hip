@@ -1287,6 +1287,47 @@ struct BwdAcc {
   v16f a2[ROLE == kRoleKV ? CB : 1];   // dv (kRoleKV)
 };
 
+// The last products of a finished block wait in registers (its bf16 dS * scale
+// and P, and their operand tiles) and are issued after the next block's QK,
+// so they run while that block's vector work goes on, as in the forward's
+// pipeline: dq~ += (alpha dS) sign K (kRoleQ); dv += P^T dO and
+// dk~ += (alpha dS^T) sign Q (kRoleKV).
+template <int ROLE, int CB>
+struct BwdPending {
+  uint32_t ww[8];                                  // bf16 dS * the other side's scale
+  uint32_t pw[ROLE == kRoleKV ? 8 : 1];            // bf16 P (kRoleKV)
+  v8bf vop[2][CB];                                 // K signs (kRoleQ) / dO^T (kRoleKV)
+  v8bf vop2[ROLE == kRoleKV ? 2 : 1][ROLE == kRoleKV ? CB : 1];  // Q signs (kRoleKV)
+};
+
+// Where the held operands fit the register budget: table rows, and the
+// query role at d <= 64.  Elsewhere each block issues its products at its
+// end (holding them spilled registers to scratch).
+template <int ROLE, int NCH, int BIAS>
+constexpr bool bwd_pipelined() { return BIAS == kBiasRows || (ROLE == kRoleQ && NCH == 1); }
+
+template <int ROLE, int CB>
+__device__ __forceinline__ void bwd_pending_mfma(const BwdPending<ROLE, CB>& pd, BwdAcc<ROLE, CB>& acc) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const v4u wv = {pd.ww[4 * half], pd.ww[4 * half + 1], pd.ww[4 * half + 2], pd.ww[4 * half + 3]};
+    const v8bf wop = __builtin_bit_cast(v8bf, wv);
+    if (ROLE == kRoleQ) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) acc.a1[cb] = mfma_bf16_32x32x16(pd.vop[half][cb], wop, acc.a1[cb]);
+    } else {
+      const v4u pv = {pd.pw[4 * half], pd.pw[4 * half + 1], pd.pw[4 * half + 2], pd.pw[4 * half + 3]};
+      const v8bf pop = __builtin_bit_cast(v8bf, pv);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        acc.a2[cb] = mfma_bf16_32x32x16(pd.vop[half][cb], pop, acc.a2[cb]);
+        acc.a1[cb] = mfma_bf16_32x32x16(pd.vop2[ROLE == kRoleKV ? half : 0][ROLE == kRoleKV ? cb : 0], wop,
+                                        acc.a1[cb]);
+      }
+    }
+  }
+}
+
 // Diagonal sums of one 32x32 block of dS in the MFMA result layout (lane
 // l = 32 lh + li holds query li; register r = 4 g + i holds key
 // j = 8 g + 4 lh + i).  Returns, in lane t, the sum of dS[li][j] over
@@ -1351,7 +1392,7 @@ template <int ROLE, bool MASK, int NCH, int CB, int BIAS>
 __device__ __forceinline__ void bwd_tile(const Ctx<NCH>& c, BwdTileBuf<ROLE, NCH, CB, BIAS>& tb,
                                          const KeyPos& kp, const v8bf (&xop)[2 * CB], float lrow, float drow,
                                          BwdAcc<ROLE, CB>& acc, int nblk, bool want_dt, float (&dsk)[2],
-                                         int (&dbase)[2], int dtk) {
+                                         int (&dbase)[2], int dtk, BwdPending<ROLE, CB>& pd, bool& pending) {
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     if (blk >= nblk) break;  // uniform: the padded block of a ragged table-row tile
@@ -1359,6 +1400,7 @@ __device__ __forceinline__ void bwd_tile(const Ctx<NCH>& c, BwdTileBuf<ROLE, NCH
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch)
       s = mfma_signs_32x32x64(lds_load<v4i>(tb.k, c.off_k + ch * 2048 + blk * 1024), c.qop[ch], s);
+    if (pending) bwd_pending_mfma<ROLE, CB>(pd, acc);  // uniform: false for the first block only
     float sc[16];
     block_logits<MASK, NCH, CB, BIAS>(c, tb, kp, blk, s, sc);
     // dP: rows = the block's columns, one row token per lane
@@ -1415,23 +1457,24 @@ __device__ __forceinline__ void bwd_tile(const Ctx<NCH>& c, BwdTileBuf<ROLE, NCH
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
+      // this block becomes pending: its operand tiles leave LDS now, so the
+      // pipeline runs across tile barriers
       const int pidx = 2 * blk + half;
-      const v4u wv = {ww[4 * half], ww[4 * half + 1], ww[4 * half + 2], ww[4 * half + 3]};
-      const v8bf wop = __builtin_bit_cast(v8bf, wv);
-      if (ROLE == kRoleQ) {
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          acc.a1[cb] = mfma_bf16_32x32x16(lds_load<v8bf>(tb.vt, c.off_v[pidx] + cb * 4096), wop, acc.a1[cb]);
-      } else {
-        const v4u pv = {pw[4 * half], pw[4 * half + 1], pw[4 * half + 2], pw[4 * half + 3]};
-        const v8bf pop = __builtin_bit_cast(v8bf, pv);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          acc.a2[cb] = mfma_bf16_32x32x16(lds_load<v8bf>(tb.vt, c.off_v[pidx] + cb * 4096), pop, acc.a2[cb]);
-          acc.a1[cb] = mfma_bf16_32x32x16(lds_load<v8bf>(tb.vt2, c.off_v[pidx] + cb * 4096), wop, acc.a1[cb]);
-        }
+      for (int cb = 0; cb < CB; ++cb) {
+        pd.vop[half][cb] = lds_load<v8bf>(tb.vt, c.off_v[pidx] + cb * 4096);
+        if (ROLE == kRoleKV)
+          pd.vop2[ROLE == kRoleKV ? half : 0][ROLE == kRoleKV ? cb : 0] =
+              lds_load<v8bf>(tb.vt2, c.off_v[pidx] + cb * 4096);
       }
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pd.ww[j] = ww[j];
+      if (ROLE == kRoleKV) pd.pw[ROLE == kRoleKV ? j : 0] = pw[j];
+    }
+    if (!bwd_pipelined<ROLE, NCH, BIAS>()) bwd_pending_mfma<ROLE, CB>(pd, acc);
+    pending = bwd_pipelined<ROLE, NCH, BIAS>();
   }
 }
 
@@ -1475,7 +1518,8 @@ __device__ __forceinline__ void bwd_step(const Ctx<NCH>& c, const BwdCtx& bc, co
                                          BwdTileBuf<ROLE, NCH, CB, BIAS>& cur,
                                          BwdTileBuf<ROLE, NCH, CB, BIAS>& nxt, int t, int nkt, KeyPos& kp,
                                          KeyPos& kprev, const v8bf (&xop)[2 * CB], float lrow, float drow,
-                                         BwdAcc<ROLE, CB>& acc, float* share) {
+                                         BwdAcc<ROLE, CB>& acc, float* share, BwdPending<ROLE, CB>& pd,
+                                         bool& pending) {
   const FwdArgs& a = *c.a;
   const KeyPos kn = next_keys(kp, a.gw);
   // the previous tile's window sits in nxt; it is added to the share before
@@ -1487,11 +1531,11 @@ __device__ __forceinline__ void bwd_step(const Ctx<NCH>& c, const BwdCtx& bc, co
   int dbase[2] = {0, 0};
   const int nb = BIAS == kBiasRows ? (kp.k0 + 32 < a.N ? 2 : 1) : 2;
   if (BIAS == kBiasRows)  // as in pass_step
-    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, nb, want_dt, dsk, dbase, bc.dtk);
+    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, nb, want_dt, dsk, dbase, bc.dtk, pd, pending);
   else if (kp.k0 + kBN <= a.N)
-    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2, want_dt, dsk, dbase, bc.dtk);
+    bwd_tile<ROLE, false, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2, want_dt, dsk, dbase, bc.dtk, pd, pending);
   else
-    bwd_tile<ROLE, true, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2, want_dt, dsk, dbase, bc.dtk);
+    bwd_tile<ROLE, true, NCH, CB, BIAS>(c, cur, kp, xop, lrow, drow, acc, 2, want_dt, dsk, dbase, bc.dtk, pd, pending);
   __builtin_amdgcn_s_waitcnt(0);
   if (ROLE == kRoleQ && BIAS == kBiasRows && want_dt && c.lane != 0) {
     // lane t: diagonal t - 32 (lane 0 holds the empty diagonal -32); the
@@ -1654,11 +1698,15 @@ attn_bwd_kernel(BwdArgs ba) {
   __syncthreads();
   const int nkt = (a.N + kBN - 1) / kBN;
   KeyPos kprev = kp;
+  BwdPending<ROLE, CB> pd;
+  bool pending = false;
   for (int t = 0; t < nkt; t += 2) {
-    bwd_step<ROLE, NCH, CB, BIAS>(c, bc, ba, tb0, tb1, t, nkt, kp, kprev, xop, lrow, drow, acc, share);
+    bwd_step<ROLE, NCH, CB, BIAS>(c, bc, ba, tb0, tb1, t, nkt, kp, kprev, xop, lrow, drow, acc, share, pd, pending);
     if (t + 1 < nkt)
-      bwd_step<ROLE, NCH, CB, BIAS>(c, bc, ba, tb1, tb0, t + 1, nkt, kp, kprev, xop, lrow, drow, acc, share);
+      bwd_step<ROLE, NCH, CB, BIAS>(c, bc, ba, tb1, tb0, t + 1, nkt, kp, kprev, xop, lrow, drow, acc, share, pd,
+                                    pending);
   }
+  if (pending) bwd_pending_mfma<ROLE, CB>(pd, acc);  // the last block's products
   if (ROLE == kRoleQ && ba.dtable) {
     // the last tile's window (rows), or the whole table (table mode)
     if (BIAS == kBiasRows) flush_dwin(c, (nkt & 1) ? tb0.dwin : tb1.dwin, kprev, share, ba.prow);
