@@ -752,7 +752,7 @@ ba_status run_backward(const void* q, const void* k, const void* v, const void* 
   if (dtable) {
     p6.dtr = ba::DtReduceJob{reinterpret_cast<const float*>(ws + BL.dtpart), dtable, static_cast<int>(B),
                              static_cast<int>(H), fp.f.nqt, gh, gw, BL.prow, mode == ba::kBiasRows ? 1 : 0};
-    p6.dtr_blocks = (tcount + ba::kThreads - 1) / ba::kThreads;
+    p6.dtr_blocks = (tcount + ba::kDtEntries - 1) / ba::kDtEntries;
   }
   // 4. query role: dq (and delta, the table gradient)
   ba::BwdArgs bq{};

@@ -113,7 +113,10 @@ struct LseJob {
 // Sums the workgroups' shares of the table gradient (see BwdArgs::dtpart):
 // dtable[h][dyi][dx] = sum over b and query tiles qt of
 // share[(b H + h) nqt + qt][dyi - row0(qt)][dx], row0 = (128 qt) / gw in
-// table-row mode, 0 in table mode.  One thread per table entry.
+// table-row mode, 0 in table mode.  kDtEntries entries per block, kDtGroups
+// threads per entry.
+constexpr int kDtEntries = 32;
+constexpr int kDtGroups = kThreads / kDtEntries;
 struct DtReduceJob {
   const float* part;
   float* dtable;

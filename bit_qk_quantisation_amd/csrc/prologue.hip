@@ -446,21 +446,57 @@ __global__ void __launch_bounds__(kThreads) prologue_kernel(PrologueArgs a) {
   }
   blk -= a.bias2_blocks;
   if (blk < a.dtr_blocks) {
+    // 32 table entries per block, each summed by 8 threads over consecutive
+    // runs of its B * nqt shares (i = b nqt + qt); the 8 partial sums meet in
+    // LDS and are added in a fixed order, so the result is the same on every
+    // run.
     const DtReduceJob& j = a.dtr;
     const int w2 = 2 * j.gw - 1, rows = 2 * j.gh - 1;
-    const int64_t e = blk * kThreads + threadIdx.x;
-    if (e < static_cast<int64_t>(j.H) * rows * w2) {
+    const int64_t total = static_cast<int64_t>(j.H) * rows * w2;
+    const int64_t e = blk * kDtEntries + (threadIdx.x % kDtEntries);
+    const int grp = threadIdx.x / kDtEntries;
+    const int n = j.B * j.nqt, per = (n + kDtGroups - 1) / kDtGroups;
+    float acc = 0.0f;
+    if (e < total) {
       const int h = static_cast<int>(e / (rows * w2));
       const int rem = static_cast<int>(e - static_cast<int64_t>(h) * rows * w2);
       const int dyi = rem / w2, col = rem - dyi * w2;
-      float acc = 0.0f;
-      for (int b = 0; b < j.B; ++b)
-        for (int qt = 0; qt < j.nqt; ++qt) {
-          const int r = dyi - (j.rows_mode ? (128 * qt) / j.gw : 0);
-          if (r >= 0 && r < j.prow)
-            acc += j.part[((static_cast<int64_t>(b) * j.H + h) * j.nqt + qt) * j.prow * w2 + r * w2 + col];
+      // the query tile's first table row by a multiplication when gw
+      // divides 128
+      const int step = (j.rows_mode && 128 % j.gw == 0) ? 128 / j.gw : -1;
+      const int i0 = grp * per, i1 = (i0 + per < n) ? i0 + per : n;
+      int b = i0 / j.nqt, qt = i0 - b * j.nqt;
+      // eight loads in flight at a time: a share that does not cover the
+      // entry (or lies past the run) reads the first element instead and
+      // adds zero
+      for (int i = i0; i < i1; i += 8) {
+        float v[8];
+        bool use[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int row0 = !j.rows_mode ? 0 : (step > 0 ? qt * step : (128 * qt) / j.gw);
+          const int r = dyi - row0;
+          use[u] = i + u < i1 && r >= 0 && r < j.prow;
+          const int64_t off =
+              ((static_cast<int64_t>(b) * j.H + h) * j.nqt + qt) * j.prow * w2 + r * w2 + col;
+          v[u] = j.part[use[u] ? off : 0];
+          if (++qt == j.nqt) {
+            qt = 0;
+            ++b;
+          }
         }
-      j.dtable[e] = acc;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (use[u]) acc += v[u];
+      }
+    }
+    __shared__ float dpart[kDtGroups][kDtEntries];
+    dpart[grp][threadIdx.x % kDtEntries] = acc;
+    __syncthreads();
+    if (grp == 0 && e < total) {
+      float sum = dpart[0][threadIdx.x];
+      for (int g = 1; g < kDtGroups; ++g) sum += dpart[g][threadIdx.x];
+      j.dtable[e] = sum;
     }
     return;
   }
