@@ -784,8 +784,18 @@ __device__ __forceinline__ float workgroup_setup(Ctx<NCH>& c, const FwdArgs& a, 
 }
 
 // O = O^T / l, bf16, one query per lane; the rows' log-sum-exp when asked.
+// Without `stage` each lane stores its 4-channel pieces straight to HBM
+// (8 bytes in each of 32 rows per instruction).  With `stage` (every wave of
+// the workgroup calls it, at the end of its key loop) the wave's 32 rows go
+// through LDS first: waves 0, 1 use stage0, waves 2, 3 stage1, 32 * d bf16
+// each, rows of d / 8 16-byte chunks, chunk j of row r at position
+// j ^ (r & 7) when d % 64 == 0 (conflict-free 8-byte writes and 16-byte
+// reads).  The rows then leave as
+// whole 16-byte chunks, 8 rows per instruction, in nontemporal stores that
+// stream out while other workgroups still run.
 template <int NCH, int CB, bool XONES>
-__device__ __forceinline__ void fwd_epilogue(const Ctx<NCH>& c, const FwdArgs& a, Acc<CB, XONES>& acc, float mrow) {
+__device__ __forceinline__ void fwd_epilogue(const Ctx<NCH>& c, const FwdArgs& a, Acc<CB, XONES>& acc, float mrow,
+                                             unsigned char* stage0 = nullptr, unsigned char* stage1 = nullptr) {
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) pin_uniform(acc.o[cb]);
   float lsum;
@@ -803,20 +813,51 @@ __device__ __forceinline__ void fwd_epilogue(const Ctx<NCH>& c, const FwdArgs& a
   if (a.lse && c.lh == 0) a.lse[c.tokbase + c.qi] = c.qi < a.N ? mrow + log2f(lsum) : 0.0f;
   if (a.lse_out && c.lh == 0 && c.qi < a.N)
     a.lse_out[static_cast<int64_t>(c.bh) * a.N + c.qi] = (mrow + log2f(lsum)) * kLn2;
-  if (c.qi < a.N) {
-    uint16_t* orow = a.o + token_offset(a.os, c.bh / a.H, c.head, c.qi);
+  if (stage0 == nullptr) {
+    if (c.qi < a.N) {
+      uint16_t* orow = a.o + token_offset(a.os, c.bh / a.H, c.head, c.qi);
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int c0 = cb * 32 + 8 * b + 4 * c.lh;
-        if (c0 < a.d) {
-          uint2 w;
-          w.x = pack_bf16x2(acc.o[cb][4 * b + 0] * inv, acc.o[cb][4 * b + 1] * inv);
-          w.y = pack_bf16x2(acc.o[cb][4 * b + 2] * inv, acc.o[cb][4 * b + 3] * inv);
-          *reinterpret_cast<uint2*>(orow + c0) = w;
+        for (int b = 0; b < 4; ++b) {
+          const int c0 = cb * 32 + 8 * b + 4 * c.lh;
+          if (c0 < a.d) {
+            uint2 w;
+            w.x = pack_bf16x2(acc.o[cb][4 * b + 0] * inv, acc.o[cb][4 * b + 1] * inv);
+            w.y = pack_bf16x2(acc.o[cb][4 * b + 2] * inv, acc.o[cb][4 * b + 3] * inv);
+            *reinterpret_cast<uint2*>(orow + c0) = w;
+          }
         }
+    }
+    return;
+  }
+  // lane and wave recomputed here rather than kept live through the key loop
+  const int lane = static_cast<int>(threadIdx.x & 63), li = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int C = a.d >> 3, sw = (C & 7) == 0 ? 7 : 0;
+  unsigned char* ws = (wave < 2 ? stage0 : stage1) + (wave & 1) * 64 * a.d;
+  __syncthreads();  // every wave is past its last read of the tile buffers
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int c0 = cb * 32 + 8 * b + 4 * (lane >> 5);
+      if (c0 < a.d) {
+        v2u w;
+        w[0] = pack_bf16x2(acc.o[cb][4 * b + 0] * inv, acc.o[cb][4 * b + 1] * inv);
+        w[1] = pack_bf16x2(acc.o[cb][4 * b + 2] * inv, acc.o[cb][4 * b + 3] * inv);
+        *reinterpret_cast<v2u*>(ws + (li * C + ((c0 >> 3) ^ (li & sw))) * 16 + (c0 & 4) * 2) = w;
       }
+    }
+  __syncthreads();
+  const int r0 = c.q0 + wave * 32;
+  const int64_t bidx = c.bh / a.H;
+  for (int e = lane; e < 32 * C; e += 64) {
+    const int r = e / C, j = e - r * C;
+    if (r0 + r < a.N) {
+      const v4u x = lds_load<v4u>(ws, (r * C + (j ^ (r & sw))) * 16);
+      __builtin_nontemporal_store(x, reinterpret_cast<v4u*>(a.o + token_offset(a.os, bidx, c.head, r0 + r) + 8 * j));
+    }
   }
 }
 
@@ -850,7 +891,16 @@ attn_fwd_kernel(FwdArgs a) {
       mrow = run_exact_pass<NCH, CB, XONES, BIAS>(c, tb0, tb1, acc);
   }
 
-  fwd_epilogue<NCH, CB, XONES>(c, a, acc, mrow);
+  if constexpr (BIAS == kBiasDense || (CB != 1 && CB != 2 && CB != 4)) {
+    // direct stores: staging costs these variants registers (spills) inside
+    // the key loop
+    fwd_epilogue<NCH, CB, XONES>(c, a, acc, mrow);
+  } else {
+    // waves 0, 1 stage their rows in tb0's V^T tile, waves 2, 3 in tb1's
+    static_assert(sizeof(tb0.vt) >= 2 * 32 * (32 * CB) * 2, "two waves' output rows fit one V^T tile");
+    fwd_epilogue<NCH, CB, XONES>(c, a, acc, mrow, reinterpret_cast<unsigned char*>(tb0.vt),
+                                 reinterpret_cast<unsigned char*>(tb1.vt));
+  }
 }
 
 // -------------------------------------------------- one launch, short N ---

@@ -42,6 +42,7 @@ def run(inp):
     (1, 1, 3, 32, 72),     # d = 72 (bits padded to 96), N = 96: ragged tile
     (1, 2, 6, 32, 96),
     (1, 1, 5, 64, 128),    # N = 320
+    (1, 2, 9, 32, 32),     # d = 32, N = 288: two launches, output rows staged in LDS
     (1, 1, 2, 96, 40),     # gw = 96, d = 40
     (1, 1, 3, 32, 200),
     (1, 1, 2, 64, 256),

@@ -46,6 +46,7 @@ SHAPES = [
     (1, 2, 4, 32, 64),     # row mode, N = 128
     (2, 2, 3, 32, 72),     # d = 72 padded to 96, N = 96 (ragged tile)
     (1, 2, 5, 13, 128),    # N = 65
+    (1, 2, 9, 32, 64),     # N = 288: two launches, staged rows into strided o
 ]
 
 
