@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <utility>
 #include <cmath>
 #include <cstdarg>
@@ -184,6 +185,45 @@ int device_cus() {
     cache[dev].store(n, std::memory_order_relaxed);
   }
   return n;
+}
+
+// A second stream per device, on which the backward's key role runs beside
+// the query role, with the events that fork it from the caller's stream and
+// join it back.  Default priority, created on
+// the device's first backward call and kept until the process ends.  The
+// mutex spans fork to join, so calls from several host threads cannot mix
+// their event records.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+// The side stream for work on `stream`, or nullptr when `stream` is not on
+// the current device or creating the stream or its events failed (the caller
+// then stays on one stream).  Call with g_side_mu held.
+SideStream* side_stream_for(void* stream) {
+  int dev = 0;
+  hipDevice_t sdev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess || sdev != dev) return nullptr;
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    hipStream_t s = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+      if (f) (void)hipEventDestroy(f);
+      (void)hipStreamDestroy(s);
+      return nullptr;
+    }
+    ss.s = s;
+    ss.fork = f;
+    ss.join = j;
+  }
+  return &ss;
 }
 
 // Dynamic LDS of the fused kernel: the bias table (table mode), raised when
@@ -690,6 +730,14 @@ ba_status run_backward(const void* q, const void* k, const void* v, const void* 
   if (dtable && !bias) return fail(BA_ERR_SHAPE, "dtable needs a bias table");
   if (dtable && overlaps(dtable, tcount * 4, workspace, BL.total))
     return fail(BA_ERR_WORKSPACE, "dtable overlaps the workspace");
+  if (dtable) {
+    // (dtable is written while the key role writes dk and dv)
+    for (const void* o : outs)
+      if (overlaps(dtable, tcount * 4, o, tb * 4)) return fail(BA_ERR_SHAPE, "dtable must not overlap dq, dk or dv");
+    for (const void* i : ins)
+      if (overlaps(dtable, tcount * 4, i, tb * 2)) return fail(BA_ERR_SHAPE, "dtable must not overlap the inputs");
+    if (overlaps(dtable, tcount * 4, bias, tcount * 2)) return fail(BA_ERR_SHAPE, "dtable must not overlap the table");
+  }
   const bool saved = o_saved != nullptr;
   if (saved) {
     if (!lse_saved) return fail(BA_ERR_NULL, "lse must be non-NULL");
@@ -727,7 +775,7 @@ ba_status run_backward(const void* q, const void* k, const void* v, const void* 
   f.o = obuf;
   f.os = contiguous_strides(H, N, d);
   f.lse = lse;
-  // 3. queries and dO as the keys and values of a second prologue pass
+  // 3. queries and dO as the keys and values of a second prologue pass, and delta
   ba::PrologueArgs p3{};
   p3.kv = p1.kv;
   p3.kv.vmax = nullptr;  // dO's maxima are not needed
@@ -747,6 +795,10 @@ ba_status run_backward(const void* q, const void* k, const void* v, const void* 
     p3.lsej = ba::LseJob{lse_saved, lse, B * H, static_cast<int>(N), static_cast<int>(BL.fwd.Npad)};
     p3.lse_blocks = (B * H * BL.fwd.Npad + ba::kThreads - 1) / ba::kThreads;
   }
+  // delta_i = <dO_i, O_i> for both roles, two threads per row
+  p3.delta = ba::DeltaJob{saved ? static_cast<const uint16_t*>(o_saved) : obuf, static_cast<const uint16_t*>(dout),
+                          delta, B * H, static_cast<int>(N), static_cast<int>(BL.fwd.Npad), d};
+  p3.delta_blocks = (2 * B * H * BL.fwd.Npad + ba::kThreads - 1) / ba::kThreads;
   // 6. the table gradient: the sum of the query role's per-workgroup shares
   ba::PrologueArgs p6{};
   if (dtable) {
@@ -754,13 +806,12 @@ ba_status run_backward(const void* q, const void* k, const void* v, const void* 
                              static_cast<int>(H), fp.f.nqt, gh, gw, BL.prow, mode == ba::kBiasRows ? 1 : 0};
     p6.dtr_blocks = (tcount + ba::kDtEntries - 1) / ba::kDtEntries;
   }
-  // 4. query role: dq (and delta, the table gradient)
+  // 4. query role: dq (and the table gradient's shares)
   ba::BwdArgs bq{};
   bq.f = fp.f;
   bq.xrow = static_cast<const uint16_t*>(dout);
   bq.ynat = static_cast<const uint16_t*>(v);
   bq.zt = reinterpret_cast<const uint16_t*>(ws + BL.kst);
-  bq.orow = saved ? static_cast<const uint16_t*>(o_saved) : obuf;
   bq.lse = lse;
   bq.delta = delta;
   bq.out1 = dq;
@@ -784,7 +835,6 @@ ba_status run_backward(const void* q, const void* k, const void* v, const void* 
   bk.ynat = static_cast<const uint16_t*>(dout);
   bk.zt = reinterpret_cast<const uint16_t*>(ws + BL.dot);
   bk.zt2 = reinterpret_cast<const uint16_t*>(ws + BL.qst);
-  bk.orow = nullptr;
   bk.out1 = dk;
   bk.out2 = dv;
   bk.dtable = nullptr;
@@ -801,9 +851,35 @@ ba_status run_backward(const void* q, const void* k, const void* v, const void* 
   int err = ba::launch_prologue(p1, stream);
   if (err == 0 && !saved) err = ba::launch_attention(f, mode, stream);
   if (err == 0) err = ba::launch_prologue(p3, stream);
+  if (err != 0) return hip_fail(err, "backward launch");
+  // After the second prologue the two roles depend on nothing of each other
+  // (they share inputs only; dtable is checked apart from dk and dv): with
+  // the table gradient and N >= 1024 the key role runs on the side stream
+  // beside the query role and the table-gradient reduction.  The query role
+  // then carries the extra table-gradient work, and each role alone fits two
+  // workgroups per CU, leaving its grid's last wave on part of the CUs, which
+  // the other role's workgroups fill (detection shape with the table rows:
+  // 651 -> 611 us).  Without the table gradient it gains nothing, and on
+  // short sequences the fork and join cost more than they save (ViT-Base
+  // 14x14: 141 -> 152 us).
+  std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
+  SideStream* ss = nullptr;
+  if (dtable && N >= 1024) {
+    lock.lock();
+    ss = side_stream_for(stream);
+  }
+  hipStream_t main_s = static_cast<hipStream_t>(stream);
+  if (ss) {
+    err = static_cast<int>(hipEventRecord(ss->fork, main_s));
+    if (err == 0) err = static_cast<int>(hipStreamWaitEvent(ss->s, ss->fork, 0));
+  }
+  if (err == 0) err = ba::launch_backward(bk, ba::kRoleKV, mode, ss ? static_cast<void*>(ss->s) : stream);
   if (err == 0) err = ba::launch_backward(bq, ba::kRoleQ, mode, stream);
   if (err == 0 && dtable) err = ba::launch_prologue(p6, stream);
-  if (err == 0) err = ba::launch_backward(bk, ba::kRoleKV, mode, stream);
+  if (err == 0 && ss) {
+    err = static_cast<int>(hipEventRecord(ss->join, ss->s));
+    if (err == 0) err = static_cast<int>(hipStreamWaitEvent(main_s, ss->join, 0));
+  }
   if (err != 0) return hip_fail(err, "backward launch");
   return BA_OK;
 }

@@ -1678,22 +1678,10 @@ attn_bwd_kernel(BwdArgs ba) {
   }
   float lrow = 0.0f, drow = 0.0f;
   if (ROLE == kRoleQ) {
-    // delta_i = <dO_i, O_i>: this lane's half of the channels, then both
-    const uint16_t* orw = ba.orow + (bhN + (valid ? c.qi : 0)) * a.d;
-    float part = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 2 * CB; ++t) {
-      const uint4 ro = valid ? *reinterpret_cast<const uint4*>(orw + 16 * t + 8 * c.lh) : make_uint4(0u, 0u, 0u, 0u);
-      const uint4 rg = __builtin_bit_cast(uint4, xop[t]);
-      const uint32_t wo[4] = {ro.x, ro.y, ro.z, ro.w}, wg[4] = {rg.x, rg.y, rg.z, rg.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        part += bf16_to_f32(static_cast<uint16_t>(wo[e] & 0xffffu)) * bf16_to_f32(static_cast<uint16_t>(wg[e] & 0xffffu)) +
-                bf16_to_f32(static_cast<uint16_t>(wo[e] >> 16)) * bf16_to_f32(static_cast<uint16_t>(wg[e] >> 16));
-    }
-    drow = sum_halves(part);
+    // the row's log2-sum-exp2 and delta_i = <dO_i, O_i> (0 past N), both
+    // written before this launch
     lrow = ba.lse[c.tokbase + c.qi];
-    if (c.lh == 0) ba.delta[c.tokbase + c.qi] = valid ? drow : 0.0f;
+    drow = ba.delta[c.tokbase + c.qi];
   }
 
   BwdAcc<ROLE, CB> acc;

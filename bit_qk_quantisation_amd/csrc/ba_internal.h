@@ -110,6 +110,18 @@ struct LseJob {
   int N, Npad;
 };
 
+// The backward's delta_i = <dO_i, O_i> ([BH][Npad], 0 past N), from the
+// contiguous [BH][N][d] dO and O, d % 16 == 0.  Two threads per row, each
+// summing the products over its half of the channels (the 8-channel pieces
+// 16 t + 8 half, in order of t), then the two halves added.
+struct DeltaJob {
+  const uint16_t* o;
+  const uint16_t* dout;
+  float* delta;
+  int64_t BH;
+  int N, Npad, d;
+};
+
 // Sums the workgroups' shares of the table gradient (see BwdArgs::dtpart):
 // dtable[h][dyi][dx] = sum over b and query tiles qt of
 // share[(b H + h) nqt + qt][dyi - row0(qt)][dx], row0 = (128 qt) / gw in
@@ -142,6 +154,8 @@ struct PrologueArgs {
   int64_t dtr_blocks;
   LseJob lsej;
   int64_t lse_blocks;
+  DeltaJob delta;
+  int64_t delta_blocks;
   int lds;  // dynamic LDS bytes per block
 };
 
@@ -226,9 +240,8 @@ struct BwdArgs {
   const uint16_t* ynat;    // [BH][N][d] natural column tiles: V (kRoleQ) or dO (kRoleKV)
   const uint16_t* zt;      // [BH][Npad/64][dpad][64]: K signs (kRoleQ) or dO^T (kRoleKV)
   const uint16_t* zt2;     // [BH][Npad/64][dpad][64]: Q signs (kRoleKV)
-  const uint16_t* orow;    // kRoleQ: [BH][N][d] the forward output, for delta
   float* lse;              // [BH][Npad] log2-sum-exp2 of the query rows
-  float* delta;            // [BH][Npad] <dO_i, O_i> (written by kRoleQ)
+  float* delta;            // [BH][Npad] <dO_i, O_i> (a prologue job, DeltaJob)
   float* out1;             // [BH][N][d] float32: dq (kRoleQ) or dk (kRoleKV)
   float* out2;             // kRoleKV: [BH][N][d] float32 dv
   float* dtable;           // kRoleQ: nullptr = no table gradient, else non-null (see dtpart)

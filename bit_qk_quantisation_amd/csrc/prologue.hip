@@ -520,12 +520,41 @@ __global__ void __launch_bounds__(kThreads) prologue_kernel(PrologueArgs a) {
       const int i = static_cast<int>(e - bh * j.Npad);
       j.out[e] = i < j.N ? j.in[bh * j.N + i] * kLog2e : 0.0f;
     }
+    return;
+  }
+  blk -= a.lse_blocks;
+  if (blk < a.delta_blocks) {
+    // thread pair (2r, 2r + 1): row r of the launch, channel halves 0 and 1;
+    // every lane reaches the exchange (rows past BH * Npad contribute 0)
+    const DeltaJob& j = a.delta;
+    const int64_t e = blk * kThreads + threadIdx.x, row = e >> 1;
+    const int half = static_cast<int>(e & 1);
+    const bool inrow = row < j.BH * j.Npad;
+    const int64_t bh = inrow ? row / j.Npad : 0;
+    const int i = inrow ? static_cast<int>(row - bh * j.Npad) : 0;
+    const bool valid = inrow && i < j.N;
+    float part = 0.0f;
+    if (valid) {
+      const uint16_t* orow = j.o + (bh * j.N + i) * j.d;
+      const uint16_t* grow = j.dout + (bh * j.N + i) * j.d;
+      for (int t = 0; t < j.d / 16; ++t) {
+        const uint4 ro = *reinterpret_cast<const uint4*>(orow + 16 * t + 8 * half);
+        const uint4 rg = *reinterpret_cast<const uint4*>(grow + 16 * t + 8 * half);
+        const uint32_t wo[4] = {ro.x, ro.y, ro.z, ro.w}, wg[4] = {rg.x, rg.y, rg.z, rg.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          part += bf16_to_f32(static_cast<uint16_t>(wo[k] & 0xffffu)) * bf16_to_f32(static_cast<uint16_t>(wg[k] & 0xffffu)) +
+                  bf16_to_f32(static_cast<uint16_t>(wo[k] >> 16)) * bf16_to_f32(static_cast<uint16_t>(wg[k] >> 16));
+      }
+    }
+    const float sum = part + __shfl_xor(part, 1, 64);
+    if (inrow && half == 0) j.delta[row] = valid ? sum : 0.0f;
   }
 }
 
 int launch_prologue(const PrologueArgs& a, void* stream) {
   const int64_t blocks = a.pack_blocks + a.kv_blocks + a.bias_blocks + a.vstat_blocks + a.bias2_blocks +
-                        a.dtr_blocks + a.lse_blocks;
+                        a.dtr_blocks + a.lse_blocks + a.delta_blocks;
   hipLaunchKernelGGL(prologue_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), a.lds,
                      static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());

@@ -321,6 +321,10 @@ def test_bwd_validation(lib):
     big = 1 << 40
     assert call(dt=A + 8 * GB, wsb=big) == 2                               # dtable without a table
     assert call(dk=A + 5 * GB + 64, wsb=big) == 2                          # dq and dk overlap
+    tab = dict(bias=A + 9 * GB, gh=8, gw=8, wsb=big)
+    assert call(dt=A + 6 * GB + 64, **tab) == 2                            # dtable inside dk
+    assert call(dt=A + GB + 64, **tab) == 2                                # dtable inside k
+    assert call(dt=A + 9 * GB + 16, **tab) == 2                            # dtable overlaps the table
 
 
 def test_fwd_train_validation(lib):
