@@ -274,10 +274,17 @@ size_t ba_workspace_bytes_bwd(int64_t B, int64_t H, int64_t N, int d, int gh, in
  *   workspace      >= ba_workspace_bytes_bwd(B,H,N,d,gh,gw) bytes, 256-byte
  *                  aligned
  * The forward is recomputed inside (its O and row log2-sum-exp2 are kept in
- * the workspace): five kernels are enqueued, six with dtable.  dtable is
+ * the workspace): five kernels are enqueued, six with dtable.  With dtable
+ * and N >= 1024 the key-role kernel (dk, dv) goes to a second stream that
+ * the library owns on the current device (default priority, created on the
+ * first such call): an event recorded on `stream` after the second prologue
+ * forks it, and `stream` waits for an event recorded after it, so all of the
+ * call's work still comes before later work on `stream`.  `stream` must then
+ * be on the current device, else everything stays on `stream`.  dtable is
  * reduced from per-workgroup shares in a fixed order (no atomics), so it is
  * the same from run to run.  Errors: as ba_attention_fwd;
- * BA_ERR_UNSUPPORTED for other d. */
+ * BA_ERR_UNSUPPORTED for other d; BA_ERR_SHAPE if dtable overlaps dq, dk, dv,
+ * the inputs or the table. */
 ba_status ba_attention_bwd(const void* q, const void* k, const void* v,
                            const void* bias, int gh, int gw,
                            int64_t B, int64_t H, int64_t N, int d, float scale,
