@@ -248,8 +248,8 @@ __device__ __forceinline__ void copy_tile_async(const Ctx<NCH>& c, TB& tb, int t
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int m = c.wave + 4 * j;
-      dma16(c.drs, ddst + m * 1024, c.dvoff + static_cast<uint32_t>(m * 8) * c.dld2 + static_cast<uint32_t>(kp.k0 * 2),
-            0u);
+      dma16_nt(c.drs, ddst + m * 1024, c.dvoff + static_cast<uint32_t>(m * 8) * c.dld2 + static_cast<uint32_t>(kp.k0 * 2),
+               0u);
     }
   }
   if (BIAS == kBiasTable && c.tid < kBN) {

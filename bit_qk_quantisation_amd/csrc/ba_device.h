@@ -208,6 +208,14 @@ __device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t voff, uint32
                                            voff, soff, 0, 0);
 }
 
+// As dma16, for data read once (a dense bias tile): the load is marked
+// nontemporal, so it streams through L2 without displacing the key and value
+// tiles that the other query tiles of the head read again.
+__device__ __forceinline__ void dma16_nt(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds), 16,
+                                           voff, soff, 0, 2);
+}
+
 // 4 bytes per lane into LDS: lane l writes lds[4 l, 4 l + 4).
 __device__ __forceinline__ void dma4(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds), 4,
