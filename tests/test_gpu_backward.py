@@ -119,6 +119,7 @@ TRAIN_CASES = [
     (1, 2, 4, 32, 64, True, 1.0),     # table rows
     (1, 2, 4, 32, 64, True, 8.0),     # table rows, exact path (large logits)
     (2, 1, 1, 100, 32, False, 1.0),   # no bias, ragged tile
+    (1, 2, 16, 64, 64, True, 1.0),    # table rows, N = 1024: the key role on the side stream
 ]
 
 
