@@ -1053,7 +1053,9 @@ attn_fwd_small_kernel(FwdArgs a) {
     small_pass<true, CB, BIAS>(c, tiles, acc);
   else
     mrow = small_pass<false, CB, BIAS>(c, tiles, acc);
-  fwd_epilogue<1, CB, true>(c, a, acc, mrow);
+  // the output rows leave through LDS (tiles 0 and 1's V^T, free by then)
+  fwd_epilogue<1, CB, true>(c, a, acc, mrow, reinterpret_cast<unsigned char*>(tiles[0].vt),
+                            reinterpret_cast<unsigned char*>(tiles[1].vt));
 }
 
 int small_static_lds(int cb, int mode) {
