@@ -783,6 +783,25 @@ __device__ __forceinline__ float workgroup_setup(Ctx<NCH>& c, const FwdArgs& a, 
   return a.qscale * mx[2] * mx[0] * static_cast<float>(a.d) + mx[1];
 }
 
+// A wave's 32 bf16 output rows staged in LDS (see fwd_epilogue): rows of
+// C = d / 8 16-byte chunks, chunk j of row r at position j ^ (r & sw).
+// out_stage_put stores channels c0..c0+3 of row li; out_stage_flush writes
+// rows r0 .. r0+31 below N as whole chunks, nontemporal.
+__device__ __forceinline__ void out_stage_put(unsigned char* ws, int li, int C, int sw, int c0, v2u w) {
+  *reinterpret_cast<v2u*>(ws + (li * C + ((c0 >> 3) ^ (li & sw))) * 16 + (c0 & 4) * 2) = w;
+}
+
+__device__ __forceinline__ void out_stage_flush(const FwdArgs& a, const unsigned char* ws, int C, int sw, int lane,
+                                                int64_t bidx, int head, int r0) {
+  for (int e = lane; e < 32 * C; e += 64) {
+    const int r = e / C, j = e - r * C;
+    if (r0 + r < a.N) {
+      const v4u x = lds_load<v4u>(ws, (r * C + (j ^ (r & sw))) * 16);
+      __builtin_nontemporal_store(x, reinterpret_cast<v4u*>(a.o + token_offset(a.os, bidx, head, r0 + r) + 8 * j));
+    }
+  }
+}
+
 // O = O^T / l, bf16, one query per lane; the rows' log-sum-exp when asked.
 // Without `stage` each lane stores its 4-channel pieces straight to HBM
 // (8 bytes in each of 32 rows per instruction).  With `stage` (every wave of
@@ -846,19 +865,11 @@ __device__ __forceinline__ void fwd_epilogue(const Ctx<NCH>& c, const FwdArgs& a
         v2u w;
         w[0] = pack_bf16x2(acc.o[cb][4 * b + 0] * inv, acc.o[cb][4 * b + 1] * inv);
         w[1] = pack_bf16x2(acc.o[cb][4 * b + 2] * inv, acc.o[cb][4 * b + 3] * inv);
-        *reinterpret_cast<v2u*>(ws + (li * C + ((c0 >> 3) ^ (li & sw))) * 16 + (c0 & 4) * 2) = w;
+        out_stage_put(ws, li, C, sw, c0, w);
       }
     }
   __syncthreads();
-  const int r0 = c.q0 + wave * 32;
-  const int64_t bidx = c.bh / a.H;
-  for (int e = lane; e < 32 * C; e += 64) {
-    const int r = e / C, j = e - r * C;
-    if (r0 + r < a.N) {
-      const v4u x = lds_load<v4u>(ws, (r * C + (j ^ (r & sw))) * 16);
-      __builtin_nontemporal_store(x, reinterpret_cast<v4u*>(a.o + token_offset(a.os, bidx, c.head, r0 + r) + 8 * j));
-    }
-  }
+  out_stage_flush(a, ws, C, sw, lane, c.bh / a.H, c.head, c.q0 + wave * 32);
 }
 
 // Waves per SIMD the register budget is sized for (accumulator blocks).
@@ -1225,26 +1236,43 @@ attn_fwd_int8_kernel(FwdArgs a) {
   for (int cb = 0; cb < CB; ++cb) pin_uniform_i(acc.o[cb]);
   const auto pr = __builtin_amdgcn_permlane32_swap(rsum, rsum, false, false);
   const float inv = 1.0f / static_cast<float>(pr[0] + pr[1]);
-  if (c.qi < a.N) {
+  const float* vsc = a.vscale + static_cast<int64_t>(c.bh) * a.dpad;
+  const int* vcs = a.vcsum + static_cast<int64_t>(c.bh) * a.dpad;
+  // channels c0..c0+3 of the lane's row, packed to bf16
+  auto out4 = [&](int cb, int b, int c0) {
+    const v4f sv = *reinterpret_cast<const v4f*>(vsc + c0);
+    const v4i cs = *reinterpret_cast<const v4i*>(vcs + c0);
+    float o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = static_cast<float>(acc.o[cb][4 * b + i] + 128 * cs[i]) * sv[i] * inv;
+    return v2u{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+  };
+  if constexpr (CB == 1 || CB == 2 || CB == 4) {
+    // the rows leave through LDS as in fwd_epilogue: waves 0, 1 in tb0's
+    // V^T tile, waves 2, 3 in tb1's (rows past N are formed but not written)
+    static_assert(sizeof(tb0.vt) >= 2 * 32 * (32 * CB) * 2, "two waves' output rows fit one V^T tile");
+    const int lane = static_cast<int>(threadIdx.x & 63), li = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int C = a.d >> 3, sw = (C & 7) == 0 ? 7 : 0;
+    unsigned char* ws = reinterpret_cast<unsigned char*>(wave < 2 ? tb0.vt : tb1.vt) + (wave & 1) * 64 * a.d;
+    __syncthreads();  // every wave is past its last read of the tile buffers
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int c0 = cb * 32 + 8 * b + 4 * (lane >> 5);
+        if (c0 < a.d) out_stage_put(ws, li, C, sw, c0, out4(cb, b, c0));
+      }
+    __syncthreads();
+    out_stage_flush(a, ws, C, sw, lane, c.bh / a.H, c.head, c.q0 + wave * 32);
+  } else if (c.qi < a.N) {
     uint16_t* orow = a.o + token_offset(a.os, c.bh / a.H, c.head, c.qi);
-    const float* vsc = a.vscale + static_cast<int64_t>(c.bh) * a.dpad;
-    const int* vcs = a.vcsum + static_cast<int64_t>(c.bh) * a.dpad;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int c0 = cb * 32 + 8 * b + 4 * c.lh;
-        if (c0 < a.d) {
-          const v4f sv = *reinterpret_cast<const v4f*>(vsc + c0);
-          const v4i cs = *reinterpret_cast<const v4i*>(vcs + c0);
-          float o[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = static_cast<float>(acc.o[cb][4 * b + i] + 128 * cs[i]) * sv[i] * inv;
-          uint2 w;
-          w.x = pack_bf16x2(o[0], o[1]);
-          w.y = pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<uint2*>(orow + c0) = w;
-        }
+        if (c0 < a.d) *reinterpret_cast<v2u*>(orow + c0) = out4(cb, b, c0);
       }
   }
 }
