@@ -92,16 +92,22 @@ def pack_signs(x: torch.Tensor):
 
 
 class Workspace:
-    """A reusable device workspace, grown on demand (one per device)."""
+    """A reusable device workspace, grown on demand: one buffer per (device,
+    stream).  Calls on one stream run in order, so they may share a buffer;
+    calls on two streams get two buffers and cannot race on it.  A buffer is
+    allocated while its stream is current, so when a larger one replaces it,
+    torch's allocator hands the old memory out again only in that stream's
+    order, after the kernels that used it."""
 
     def __init__(self):
         self._buf = {}
 
-    def get(self, device: torch.device, nbytes: int) -> torch.Tensor:
-        buf = self._buf.get(device)
+    def get(self, device: torch.device, nbytes: int, stream=None) -> torch.Tensor:
+        key = (str(device), stream)
+        buf = self._buf.get(key)
         if buf is None or buf.numel() < nbytes:
             buf = torch.empty(max(nbytes, 256) + 256, dtype=torch.uint8, device=device)
-            self._buf[device] = buf
+            self._buf[key] = buf
         return buf
 
 
@@ -136,7 +142,7 @@ def attention_fwd(q, k, v, table=None, gh: int = 0, gw: int = 0, scale=None,
     nbytes = lib.ba_workspace_bytes(B, H, N, d, gh, gw)
     if nbytes == 0:
         raise BinAttnError(2, f"unsupported problem B={B} H={H} N={N} d={d} grid={gh}x{gw}")
-    ws = (workspace or _default_ws).get(q.device, nbytes)
+    ws = (workspace or _default_ws).get(q.device, nbytes, _stream(q.device))
     base = ws.data_ptr()
     aligned = (base + 255) // 256 * 256
     tp = None if table is None else table.data_ptr()
@@ -182,7 +188,7 @@ def attention_fwd_dense_bias(q, k, v, bias, scale=None, out=None,
     nbytes = lib.ba_workspace_bytes(B, H, N, d, 0, 0)
     if nbytes == 0:
         raise BinAttnError(2, f"unsupported problem B={B} H={H} N={N} d={d}")
-    ws = (workspace or _default_ws).get(q.device, nbytes)
+    ws = (workspace or _default_ws).get(q.device, nbytes, _stream(q.device))
     base = ws.data_ptr()
     aligned = (base + 255) // 256 * 256
     views = (q, k, v, out)
@@ -220,7 +226,7 @@ def attention_fwd_int8pv(q, k, v, table=None, gh: int = 0, gw: int = 0, scale=No
     nbytes = lib.ba_workspace_bytes_int8pv(B, H, N, d, gh, gw)
     if nbytes == 0:
         raise BinAttnError(3, f"unsupported problem B={B} H={H} N={N} d={d} grid={gh}x{gw}")
-    ws = (workspace or _default_ws).get(q.device, nbytes)
+    ws = (workspace or _default_ws).get(q.device, nbytes, _stream(q.device))
     base = ws.data_ptr()
     aligned = (base + 255) // 256 * 256
     check(lib, lib.ba_attention_fwd_int8pv(
@@ -254,7 +260,7 @@ def attention_fwd_train(q, k, v, table=None, gh: int = 0, gw: int = 0, scale=Non
         raise BinAttnError(2, f"unsupported problem B={B} H={H} N={N} d={d} grid={gh}x{gw}")
     out = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    ws = (workspace or _default_ws).get(q.device, nbytes)
+    ws = (workspace or _default_ws).get(q.device, nbytes, _stream(q.device))
     base = ws.data_ptr()
     aligned = (base + 255) // 256 * 256
     check(lib, lib.ba_attention_fwd_train(
@@ -300,7 +306,7 @@ def attention_bwd(q, k, v, dout, table=None, gh: int = 0, gw: int = 0, scale=Non
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)
     dtable = None if table is None else torch.empty(table.shape, dtype=torch.float32, device=q.device)
-    ws = (workspace or _default_ws).get(q.device, nbytes)
+    ws = (workspace or _default_ws).get(q.device, nbytes, _stream(q.device))
     base = ws.data_ptr()
     aligned = (base + 255) // 256 * 256
     tp = None if table is None else table.data_ptr()

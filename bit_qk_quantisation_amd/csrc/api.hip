@@ -467,6 +467,8 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
     return fail(BA_ERR_WORKSPACE, "workspace must not overlap q or o");
   if (kv && (overlaps(workspace, L.total, k, kb) || overlaps(workspace, L.total, v, vb)))
     return fail(BA_ERR_WORKSPACE, "workspace must not overlap k or v");
+  if (bias && overlaps(workspace, L.total, bias, static_cast<size_t>(H * (2 * gh - 1) * (2 * gw - 1)) * 2))
+    return fail(BA_ERR_WORKSPACE, "workspace must not overlap the bias table");
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   const int64_t BH = B * H;
@@ -718,6 +720,12 @@ ba_status run_backward(const void* q, const void* k, const void* v, const void* 
   const size_t tb = static_cast<size_t>(B * H * N * d);
   const void* ins[4] = {q, k, v, dout};
   const void* outs[3] = {dq, dk, dv};
+  // the backward writes all of its workspace, also the part past the forward's
+  for (const void* i : ins)
+    if (overlaps(i, tb * 2, workspace, BL.total))
+      return fail(BA_ERR_WORKSPACE, "q, k, v and dout must not overlap the workspace");
+  if (bias && overlaps(bias, static_cast<size_t>(H * (2 * gh - 1) * (2 * gw - 1)) * 2, workspace, BL.total))
+    return fail(BA_ERR_WORKSPACE, "the bias table must not overlap the workspace");
   for (const void* o : outs) {
     for (const void* i : ins)
       if (overlaps(o, tb * 4, i, tb * 2)) return fail(BA_ERR_SHAPE, "gradients must not overlap the inputs");
@@ -872,13 +880,20 @@ ba_status run_backward(const void* q, const void* k, const void* v, const void* 
   if (ss) {
     err = static_cast<int>(hipEventRecord(ss->fork, main_s));
     if (err == 0) err = static_cast<int>(hipStreamWaitEvent(ss->s, ss->fork, 0));
+    if (err != 0) return hip_fail(err, "backward fork");  // nothing is queued on the side stream yet
   }
   if (err == 0) err = ba::launch_backward(bk, ba::kRoleKV, mode, ss ? static_cast<void*>(ss->s) : stream);
   if (err == 0) err = ba::launch_backward(bq, ba::kRoleQ, mode, stream);
   if (err == 0 && dtable) err = ba::launch_prologue(p6, stream);
-  if (err == 0 && ss) {
-    err = static_cast<int>(hipEventRecord(ss->join, ss->s));
-    if (err == 0) err = static_cast<int>(hipStreamWaitEvent(main_s, ss->join, 0));
+  if (ss) {
+    // Once forked, the caller's stream always waits for the side stream,
+    // also when a launch above failed: the key role may be running on the
+    // caller's buffers and the workspace.  If the join itself cannot be
+    // queued, the host waits for the side stream instead.
+    int jerr = static_cast<int>(hipEventRecord(ss->join, ss->s));
+    if (jerr == 0) jerr = static_cast<int>(hipStreamWaitEvent(main_s, ss->join, 0));
+    if (jerr != 0) (void)hipStreamSynchronize(ss->s);
+    if (err == 0) err = jerr;
   }
   if (err != 0) return hip_fail(err, "backward launch");
   return BA_OK;

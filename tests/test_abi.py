@@ -143,6 +143,7 @@ def test_fwd_workspace(lib):
     need = lib.ba_workspace_bytes(1, 2, 64, 64, 0, 0)
     assert fwd(lib, ws_bytes=need - 1) == 5
     assert b"too small" in lib.ba_last_error()
+    assert fwd(lib, bias=A + 4 * GB + 256, gh=8, gw=8) == 5       # the table inside the workspace
 
 
 def test_pack_validation(lib):
@@ -325,6 +326,15 @@ def test_bwd_validation(lib):
     assert call(dt=A + 6 * GB + 64, **tab) == 2                            # dtable inside dk
     assert call(dt=A + GB + 64, **tab) == 2                                # dtable inside k
     assert call(dt=A + 9 * GB + 16, **tab) == 2                            # dtable overlaps the table
+    # inputs inside the workspace, also in its part past the forward's sections
+    fwd = lib.ba_workspace_bytes(1, 2, 64, 64, 0, 0)
+    full = lib.ba_workspace_bytes_bwd(1, 2, 64, 64, 0, 0)
+    assert full > fwd + 4096
+    assert call(q=A + 4 * GB + 256, wsb=big) == 5
+    assert call(do=A + 4 * GB + fwd + 256, wsb=big) == 5
+    assert call(k=A + 4 * GB + full - 4096, wsb=big) == 5
+    assert call(v=A + 4 * GB - 4096, wsb=big) == 5                        # v's rows run into it
+    assert call(bias=A + 4 * GB + full - 512, gh=8, gw=8, wsb=big) == 5    # the table inside it
 
 
 def test_fwd_train_validation(lib):
@@ -371,3 +381,19 @@ def test_bench_refuses_several_gpus():
                        cwd=root, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_default_workspace_per_stream():
+    """The binding's workspace cache gives each (device, stream) its own
+    buffer, so calls on two streams cannot race on one, and grows a buffer
+    in place of the old one only for its own stream."""
+    import torch
+    from bit_qk_quantisation_amd import Workspace
+    ws = Workspace()
+    cpu = torch.device("cpu")
+    a = ws.get(cpu, 1000, stream=111)
+    b = ws.get(cpu, 1000, stream=222)
+    assert a.data_ptr() != b.data_ptr()
+    assert ws.get(cpu, 900, stream=111).data_ptr() == a.data_ptr()
+    c = ws.get(cpu, 5000, stream=111)
+    assert c.numel() >= 5000 and ws.get(cpu, 1000, stream=222).data_ptr() == b.data_ptr()

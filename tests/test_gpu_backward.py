@@ -26,10 +26,10 @@ bq = pytest.importorskip("bit_qk_quantisation_amd")
 TOL = 1e-2
 
 
-def run_case(B, H, gh, gw, d, seed, bias=True, q_scale=1.0):
+def run_case(B, H, gh, gw, d, seed, bias=True, q_scale=1.0, table_sigma=0.02, discriminate=False):
     N = gh * gw
     inp = workloads.make_inputs(B, H, N, d, seed=seed, grid=(gh, gw) if bias else None, bias=bias,
-                                q_scale=q_scale)
+                                q_scale=q_scale, table_sigma=table_sigma)
     rng = np.random.default_rng(seed + 1)
     do = torch.from_numpy(rng.standard_normal((B, H, N, d)).astype(np.float32)).to(torch.bfloat16)
     dev = to_dev(inp)
@@ -37,6 +37,16 @@ def run_case(B, H, gh, gw, d, seed, bias=True, q_scale=1.0):
     torch.cuda.synchronize()
     ref = oracle.binary_attention_backward(np32(inp["q"]), np32(inp["k"]), np32(inp["v"]), np32(do),
                                            np32(inp["table"]) if bias else None, inp["gh"], inp["gw"])
+    if discriminate:
+        # the same gradients with the bias dropped or mirrored miss the bar
+        # by five times or more in dq, dk and dv
+        t = np32(inp["table"])
+        for name, tm in (("dropped", None), ("negated", -t), ("dx mirrored", t[:, :, ::-1].copy())):
+            alt = oracle.binary_attention_backward(np32(inp["q"]), np32(inp["k"]), np32(inp["v"]), np32(do),
+                                                   tm, inp["gh"], inp["gw"])
+            for g in ("dq", "dk", "dv"):
+                sep = float(np.abs(alt[g] - ref[g]).max() / np.abs(ref[g]).max())
+                assert sep > 5 * TOL, (name, g, sep)
     errs = {}
     for name, g in zip(("dq", "dk", "dv", "dtable"), got):
         if g is None:
@@ -69,6 +79,18 @@ def test_bwd_with_bias(B, H, gh, gw, d):
 def test_bwd_no_bias(B, H, N, d):
     announce("bwd no bias", B, H, N, d)
     run_case(B, H, 1, N, d, seed=6100 + N + d, bias=False)
+
+
+@pytest.mark.parametrize("B,H,gh,gw,d", [
+    (1, 2, 14, 14, 64),    # table in LDS
+    (1, 2, 4, 32, 64),     # table rows
+    (1, 1, 2, 64, 128),    # table rows, d = 128
+])
+def test_bwd_wide_table(B, H, gh, gw, d):
+    """A sigma-2 table: the bias shapes P, so the gradients see how it is
+    read (shown on the host with the bias dropped, negated and mirrored)."""
+    announce("bwd wide table", B, H, gh, gw, d)
+    run_case(B, H, gh, gw, d, seed=6300 + gh * gw + d, table_sigma=2.0, discriminate=True)
 
 
 def test_bwd_large_logits():

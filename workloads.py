@@ -79,12 +79,15 @@ def _to_bf16(a: np.ndarray) -> torch.Tensor:
 
 def make_inputs(B: int, H: int, N: int, d: int, seed: int, *,
                 grid=None, outlier_frac: float = 0.0, bias: bool = True,
-                q_scale: float = 1.0, k_scale: float = 1.0) -> dict:
+                q_scale: float = 1.0, k_scale: float = 1.0,
+                table_sigma: float = 0.02) -> dict:
     """Draw one seeded case.  Returns CPU bf16 tensors q, k, v [B,H,N,d] and
     table [H, 2gh-1, 2gw-1] (or None), plus gh, gw.
 
     grid=(gh, gw) with gh*gw == N is required when bias is True.
-    q_scale/k_scale multiply Q/K before rounding (large-logit cases).
+    q_scale/k_scale multiply Q/K before rounding (large-logit cases);
+    table_sigma is the table's standard deviation (0.02 for the workloads;
+    tests that must see the bias use 1 or 2).
     """
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, H, N, d), dtype=np.float32)
@@ -95,8 +98,8 @@ def make_inputs(B: int, H: int, N: int, d: int, seed: int, *,
     if bias:
         if gh * gw != N:
             raise ValueError("bias needs grid=(gh, gw) with gh*gw == N")
-        table = 0.02 * rng.standard_normal((H, 2 * gh - 1, 2 * gw - 1),
-                                           dtype=np.float32)
+        table = np.float32(table_sigma) * rng.standard_normal(
+            (H, 2 * gh - 1, 2 * gw - 1), dtype=np.float32)
     perm = rng.permutation(d)
     n_out = int(round(outlier_frac * d))
     if n_out:
@@ -113,9 +116,9 @@ def make_inputs(B: int, H: int, N: int, d: int, seed: int, *,
     }
 
 
-def workload_inputs(w: Workload) -> dict:
+def workload_inputs(w: Workload, **kw) -> dict:
     return make_inputs(w.B, w.H, w.N, w.d, w.seed, grid=(w.gh, w.gw),
-                       outlier_frac=w.outlier_frac)
+                       outlier_frac=w.outlier_frac, **kw)
 
 
 def make_dense_bias(Bb: int, H: int, N: int, seed: int, sigma: float = 0.02,
