@@ -4,13 +4,16 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--layout bhnd|bnhd|qkv] [--bias table|dense|dense-batch] [--pv bf16|int8] [--bwd]
 
-One step is one full forward (ba_attention_prepare + ba_attention_fwd_prepared,
-i.e. exactly ba_attention_fwd) over the resident bf16 inputs of the chosen
-workload (default: the 64x64-grid detection backbone, B=2 H=12 N=4096 d=64).
-W untimed steps run first, then exactly K steps are timed between two
-device synchronisations.  HIP events on the launch stream also bracket each
-kernel, which gives the average duration of the fused kernel and of the
-prologue.
+One step is one full forward, one ba_attention_fwd call, over the resident
+bf16 inputs of the chosen workload (default: the 64x64-grid detection
+backbone, B=2 H=12 N=4096 d=64).  W untimed steps run first, then exactly K
+steps are timed between two device synchronisations.  A second pass of K
+steps brackets each call with HIP events on the launch stream, followed by
+the fused kernel alone (ba_attention_fwd_prepared on a workspace that
+ba_attention_prepare filled once, outside both passes): that gives the fused
+kernel's average duration, and the rest of the call is the prologue.  Shapes
+the pipelined kernel does not take run ba_attention_prepare +
+ba_attention_fwd_prepared per step (exactly what ba_attention_fwd runs).
 
 --layout bnhd stores q, k, v and o as [B,N,H,d]; --layout qkv takes q, k and
 v as the slices of one [B,N,3,H,d] tensor and writes a [B,N,H,d] o.  Both go
@@ -79,7 +82,7 @@ PEAK_MFMA_INT8_BF16 = 4.0 / (2.0 / PEAK_INT8 + 2.0 / PEAK_BF16)
 PEAK_MFMA_FP4_INT8 = 4.0 / (2.0 / PEAK_FP4 + 2.0 / PEAK_INT8)
 
 PROFILES = ROOT / "profiles"
-FUSED_SOURCES = ("bit_qk_quantisation_amd/csrc/attention.hip",
+FUSED_SOURCES = ("bit_qk_quantisation_amd/csrc/flash.hip",
                  "bit_qk_quantisation_amd/csrc/ba_device.h",
                  "bit_qk_quantisation_amd/csrc/ba_internal.h")
 
@@ -107,11 +110,39 @@ def measured_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+def _lpad(gw):
+    lpad = (2 * gw - 1 + 3 + 3) // 4 * 4
+    while lpad % 64 != 16:
+        lpad += 4
+    return lpad
+
+
+def _window_rows(N, gw):
+    qspan = max(((q0 + 127) // gw - q0 // gw) for q0 in range(0, (N + 127) // 128 * 128, 128))
+    kspan = max(((k0 + 63) // gw - k0 // gw) for k0 in range(0, N, 64))
+    return qspan + kspan + 1
+
+
+def pipelined(w, table=True):
+    """Whether ba_attention_fwd runs the pipelined kernel (natural V, no V^T
+    from the prologue) on this workload: d in {32, 64, 128}, and table rows
+    whose per-tile window fits its buffers or no bias; shorter sequences with
+    a table or no bias (N <= 256, d in {32, 64}) take the one-launch kernel."""
+    rows = table and w.gw % 32 == 0
+    if w.d not in (32, 64, 128) or (table and not rows):
+        return False
+    if w.N <= 256 and w.d in (32, 64) and not rows:
+        return False
+    return not rows or _window_rows(w.N, w.gw) * 4 * _lpad(w.gw) <= (1664 if w.d <= 64 else 1152)
+
+
 def algorithmic_bytes(w, npad, dense_bytes=None):
-    """Compulsory HBM bytes of the two kernels of one step: the prologue reads
-    K and V and writes the fp4 key operands, the key scales (and their maxima
-    per 64 tokens), V^T and the bias rows; the fused kernel reads Q and all of
-    those and writes O."""
+    """Compulsory HBM bytes of the two kernels of one step.  Pipelined
+    kernel: the prologue reads K and writes the fp4 key operands and the key
+    scales (and their maxima per 64 tokens), plus the bias rows from the
+    table; the fused kernel reads Q, those, V and the bias rows and writes O.
+    Otherwise the prologue also reads V and writes V^T, which the fused kernel
+    reads instead of V."""
     W = (w.d + 31) // 32
     nch = (W + 1) // 2
     dpad = 32 * W
@@ -121,13 +152,14 @@ def algorithmic_bytes(w, npad, dense_bytes=None):
     vt = bh * dpad * npad * 2
     rows = 0
     if w.gw % 32 == 0:
-        lpad = (2 * w.gw - 1 + 3 + 3) // 4 * 4
-        while lpad % 64 != 16:
-            lpad += 4
-        rows = w.H * (2 * w.gh - 1 + 16) * 4 * lpad * 4
+        rows = w.H * (2 * w.gh - 1 + 16) * 4 * _lpad(w.gw) * 4
     table = w.H * (2 * w.gh - 1) * (2 * w.gw - 1) * 2
     if dense_bytes is not None:  # no table: the fused kernel reads the dense bias once
         return 2 * tok * w.d * 2 + keys + vt, tok * w.d * 2 + keys + vt + dense_bytes + tok * w.d * 2
+    if pipelined(w):
+        prologue = tok * w.d * 2 + keys + ((table + rows) if rows else 0)
+        fused = tok * w.d * 2 + keys + tok * w.d * 2 + (rows if rows else table) + tok * w.d * 2
+        return prologue, fused
     prologue = 2 * tok * w.d * 2 + keys + vt + ((table + rows) if rows else 0)
     fused = tok * w.d * 2 + keys + vt + (rows if rows else table) + tok * w.d * 2
     return prologue, fused
@@ -412,9 +444,26 @@ def main() -> int:
         def fused():  # noqa: F811
             pass
 
-    for _ in range(args.warmup):
+    if split and dense is None and pipelined(w, table is not None):
+        # The step is one ba_attention_fwd call (its prologue packs K only;
+        # the pipelined kernel reads V in place).  The fused kernel alone is
+        # timed as ba_attention_fwd_prepared on a workspace prepared once
+        # outside the timed loops: the same kernel on the same shapes, with V
+        # from the workspace's contiguous copy.
         prepare()
-        fused()
+
+        def step():
+            bq.check(lib, lib.ba_attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), tp, gh, gw, B, H, N, d,
+                                               scale, out.data_ptr(), wsp, nbytes, sp))
+        whole_call = True
+    else:
+        def step():
+            prepare()
+            fused()
+        whole_call = False
+
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -425,8 +474,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t_start.record(stream)
     for _ in range(K):
-        prepare()
-        fused()
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -438,13 +486,18 @@ def main() -> int:
     torch.cuda.synchronize()
     for i in range(K):
         ev[i][0].record(stream)
-        prepare()
+        if whole_call:
+            step()
+        else:
+            prepare()
         ev[i][1].record(stream)
         fused()
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     pro_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
     fus_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    if whole_call:  # the first interval held a whole forward: its prologue is the rest
+        pro_ms = max(pro_ms - fus_ms, 0.0)
     if not split:  # the "prologue" interval held the whole step
         fus_ms = pro_ms
     peak = PEAK_MFMA_FP4_INT8 if args.pv == "int8" else PEAK_MFMA_COMPOSITE
@@ -496,7 +549,8 @@ def main() -> int:
                    **({"backward": "saved O and lse" if args.saved else "forward recomputed"} if args.bwd else {})},
         "roofline": {
             "bound": "mfma",
-            "kernel": ("attn_fwd_kernel (fused)" if split else
+            "kernel": ("flash_fwd_kernel (fused, pipelined)" if whole_call else
+                       "attn_fwd_kernel (fused)" if split else
                        "whole backward on saved O and lse (5 kernels, one call)" if args.bwd and args.saved else
                        "whole backward (6 kernels, one call; forward recomputed)" if args.bwd else
                        "whole step (3 kernels, one call; fp4 QK + int8 P.V bound)" if args.pv == "int8" else

@@ -2,8 +2,9 @@
 
     python -m bit_qk_quantisation_amd.build
 
-hipcc compiles every csrc/*.hip file into one shared library next to this
-file.  Packed fp32 VALU forms are disabled for all device code.
+hipcc compiles every csrc/*.hip file (in parallel, one object each) and
+links them into one shared library next to this file.  Packed fp32 VALU
+forms are disabled for all device code.
 """
 
 from __future__ import annotations
@@ -33,16 +34,12 @@ def sources():
     return sorted(str(p) for p in CSRC.glob("*.hip"))
 
 
-def build(verbose: bool = False, extra=()) -> pathlib.Path:
-    """Compile every kernel and the host layer into LIB; returns its path."""
-    tmp = LIB.with_name(LIB.name + f".tmp{os.getpid()}")
-    cmd = [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wno-unused-command-line-argument",
-        f"-I{INCLUDE}", f"-I{CSRC}",
-        *extra, *sources(), "-o", str(tmp),
-    ]
+OBJ = PKG / "_build"
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wno-unused-command-line-argument"]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,6 +49,30 @@ def build(verbose: bool = False, extra=()) -> pathlib.Path:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False, extra=()) -> pathlib.Path:
+    """Compile every kernel and the host layer into LIB; returns its path.
+    Each source compiles to its own object, in parallel (no device code
+    crosses files), and one link makes the library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    OBJ.mkdir(exist_ok=True)
+    tag = os.getpid()
+    jobs = []
+    for src in sources():
+        obj = OBJ / (pathlib.Path(src).stem + f".{tag}.o")
+        jobs.append((obj, [hipcc(), f"--offload-arch={ARCH}", *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *extra,
+                           "-c", src, "-o", str(obj)]))
+    workers = max(1, min(len(jobs), os.cpu_count() or 1))
+    with ThreadPoolExecutor(workers) as ex:
+        for f in [ex.submit(_run, cmd, verbose) for _, cmd in jobs]:
+            f.result()
+    tmp = LIB.with_name(LIB.name + f".tmp{tag}")
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *[str(o) for o, _ in jobs], "-o", str(tmp)],
+         verbose)
+    for o, _ in jobs:
+        o.unlink()
     os.replace(tmp, LIB)
     return LIB
 

@@ -84,13 +84,29 @@ int choose_mode(bool has_bias, int gh, int gw, int64_t N) {
 // Byte offsets of the workspace sections of ba_attention_fwd.
 struct Layout {
   int64_t Npad, W, dpad, Lpad;
-  int64_t kop, alpha_k, kmax, vt, vq, vpart, vscale, vcsum, bias4, rowmax, total;
+  int64_t kop, alpha_k, kmax, vt, vq, vpart, vscale, vcsum, bias4, rowmax, vnat, total;
   int mode;
+  bool flash_prepared;  // the prepared forward runs the pipelined kernel on vnat
+  bool no_vt;           // compact layout without V^T: only the pipelined kernel can run on it
 };
+
+// Whether the prepared forward (ba_attention_prepare + _fwd_prepared) runs
+// the pipelined kernel: the kernel takes the shape, and the whole forward
+// would not take the one-launch kernel (the pair then equals
+// ba_attention_fwd bit for bit in every case).
+bool prepared_flash(int64_t N, int d, int mode, int gw) {
+  if (ba::small_supported(N, d, mode)) return false;
+  const int win = mode == ba::kBiasRows ? window_rows(N, gw) : 0;
+  return ba::flash_supported(d, mode, win, mode == ba::kBiasRows ? static_cast<int>(row_pad(gw)) : 0);
+}
 
 // int8pv: the 8-bit P.V forward, whose values are int8 code tiles with
 // per-channel scales instead of the bf16 V^T copy.
-Layout layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int gw, bool int8pv = false) {
+// compact: the layout of ba_attention_fwd_static, which holds only what the
+// whole forward reads: no V^T when the pipelined kernel runs (it reads V in
+// place) and no natural copy of V (only the prepared forward uses one).
+Layout layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int gw, bool int8pv = false,
+              bool compact = false) {
   Layout L{};
   L.Npad = round_up(N, ba::kNAlign);
   L.W = (d + 31) / 32;
@@ -107,7 +123,11 @@ Layout layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int
   L.kop = take(BH * L.Npad * ((L.W + 1) / 2) * 32);  // fp4 key operands: 32 B per 64 channels
   L.alpha_k = take(BH * L.Npad * 4);
   L.kmax = take(BH * (L.Npad / 64) * 4);
-  L.vt = take(int8pv ? 0 : BH * L.dpad * L.Npad * 2);
+  const bool rows0 = L.mode == ba::kBiasRows;
+  const bool whole_flash = compact && !int8pv && L.mode >= 0 &&
+                           ba::flash_supported(d, L.mode, rows0 ? window_rows(N, gw) : 0, static_cast<int>(L.Lpad));
+  L.no_vt = whole_flash;
+  L.vt = take((int8pv || whole_flash) ? 0 : BH * L.dpad * L.Npad * 2);
   L.vq = take(int8pv ? BH * L.dpad * L.Npad : 0);
   L.vpart = take(int8pv ? BH * (L.Npad / ba::kPackTok) * L.dpad * 4 : 0);
   L.vscale = take(int8pv ? BH * L.dpad * 4 : 0);
@@ -115,6 +135,9 @@ Layout layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int
   const bool rows = L.mode == ba::kBiasRows;
   L.bias4 = take(rows ? H * (2 * gh - 1 + 2 * ba::kBiasPadRows) * 4 * L.Lpad * 4 : 0);
   L.rowmax = take(rows ? H * (2 * gh - 1) * 4 : 0);
+  // the values' natural rows, for the prepared forward's pipelined kernel
+  L.flash_prepared = !int8pv && !compact && L.mode >= 0 && prepared_flash(N, d, L.mode, gw);
+  L.vnat = take(L.flash_prepared ? BH * L.Npad * d * 2 : 0);
   L.total = off;
   return L;
 }
@@ -381,6 +404,7 @@ struct Plan {
   ba::PrologueArgs p;
   int mode;
   bool int8pv;
+  bool flash;  // the pipelined kernel (natural V, no V^T in the prologue)
 };
 
 // Validates a forward request.  `kv` selects the checks of k and v (the
@@ -392,7 +416,7 @@ struct Plan {
 ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const void* bias, int gh, int gw,
                     int64_t B, int64_t H, int64_t N, int d, float scale, void* o, bool qo,
                     const int64_t* strides, const DenseBias* dense, void* workspace, size_t ws_bytes,
-                    Plan* plan, bool int8pv = false) {
+                    Plan* plan, bool int8pv = false, bool allow_flash = true, bool compact = false) {
   if (kv && (!k || !v)) return fail(BA_ERR_NULL, "k and v must be non-NULL");
   if (qo && (!q || !o)) return fail(BA_ERR_NULL, "q and o must be non-NULL");
   ba_status st = check_dims(B, H, N, d);
@@ -457,7 +481,7 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
     return fail(BA_ERR_UNSUPPORTED,
                 "bias grid %dx%d: the table rows do not fit the tile window and the table exceeds 48 KiB",
                 gh, gw);
-  const Layout L = layout(B, H, N, d, bias != nullptr, dense ? 0 : gh, dense ? 0 : gw, int8pv);
+  const Layout L = layout(B, H, N, d, bias != nullptr, dense ? 0 : gh, dense ? 0 : gw, int8pv, compact);
   if (!workspace) return fail(BA_ERR_WORKSPACE, "workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(BA_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -512,27 +536,59 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   f.gw = gw;
   f.Lpad = static_cast<int>(L.Lpad);
   f.win_rows = (mode == ba::kBiasRows) ? window_rows(N, gw) : 0;
+  f.gw32_magic = 0;  // gw == 32: the block index is the grid row
+  if (mode == ba::kBiasRows && gw > 32) {
+    const uint64_t g32 = static_cast<uint64_t>(gw / 32);
+    f.gw32_magic = static_cast<uint32_t>(((uint64_t{1} << 32) + g32 - 1) / g32);
+  }
   f.qscale = dense ? scale : scale * ba::kLog2e;  // dense logits stay in natural units
   f.nqt = static_cast<int>(L.Npad / ba::kBM);
   const int64_t nwg = BH * f.nqt;
   if (nwg > 0x7fffffff) return fail(BA_ERR_SHAPE, "too many workgroups");
   f.nwg = static_cast<int>(nwg);
   f.xcd_remap = (f.nwg % 8 == 0) ? 1 : 0;
-  const int static_lds = ba::fwd_static_lds(f.dpad, mode), table_lds = ba::fwd_table_lds(f, mode);
+  // The pipelined kernel reads V in its natural layout: from the caller's v
+  // in a whole forward, from the workspace copy ba_attention_prepare writes
+  // for the prepared forward.  Its copies address one head's value rows with
+  // 32-bit byte offsets.
+  // ba_attention_prepare (kv, not qo) writes V^T (for the dense-bias
+  // prepared forward and the other kernels) and, when the prepared forward
+  // takes the pipelined kernel, the natural copy as well.
+  const bool whole = kv && qo, prepared = qo && !kv, preparing = kv && !qo;
+  bool flash = allow_flash && !dense && !int8pv && !preparing &&
+               (prepared ? L.flash_prepared : ba::flash_supported(d, mode, f.win_rows, f.Lpad));
+  if (flash && whole && (static_cast<int64_t>(L.Npad) * vs[2].sn + d) * 2 >= (int64_t{1} << 31)) flash = false;
+  if (L.no_vt && !flash)
+    return fail(BA_ERR_UNSUPPORTED, "the value rows span 2 GiB or more: this entry point cannot run the problem");
+  uint16_t* vnat = reinterpret_cast<uint16_t*>(ws + L.vnat);
+  if (flash) {
+    if (whole) {
+      f.v = static_cast<const uint16_t*>(v);
+      f.vs = vs[2];
+    } else {
+      f.v = vnat;
+      f.vs = ba::Strides{H * L.Npad * d, L.Npad * d, d};
+    }
+  }
+  const int static_lds = flash ? ba::flash_static_lds(d, mode) : ba::fwd_static_lds(f.dpad, mode);
+  const int table_lds = flash ? 0 : ba::fwd_table_lds(f, mode);
   if (static_lds + table_lds > kMaxLds) return fail(BA_ERR_UNSUPPORTED, "bias window does not fit in LDS");
   f.dyn_lds = fused_dynamic_lds(static_lds, table_lds, nwg);
   {
     const int cus = device_cus();
     const int per_wg = static_cast<int>(round_up(static_lds + f.dyn_lds, kLdsGranule));
-    const int resident = std::min(ba::fwd_waves_per_simd(f.dpad, d), kMaxLds / per_wg);
+    const int waves = flash ? ba::flash_waves_per_simd(d) : ba::fwd_waves_per_simd(f.dpad, d);
+    const int resident = std::min(waves, kMaxLds / per_wg);
     f.prio_balance = (cus > 0 && nwg <= static_cast<int64_t>(cus) * resident) ? 1 : 0;
   }
 
   ba::PrologueArgs& p = plan->p;
   p = ba::PrologueArgs{};
   p.kv = ba::KvJob{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), const_cast<uint32_t*>(f.kop),
-                   const_cast<float*>(f.alpha_k), const_cast<float*>(f.kmax_blk), const_cast<uint16_t*>(f.vt),
+                   const_cast<float*>(f.alpha_k), const_cast<float*>(f.kmax_blk),
+                   flash ? nullptr : const_cast<uint16_t*>(f.vt),
                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                   (preparing && L.flash_prepared) ? vnat : nullptr,
                    vs[1], vs[2], BH, static_cast<int>(H), f.N, f.Npad, d, f.W, (f.W + 1) / 2, f.dpad};
   p.kv_blocks = BH * (L.Npad / ba::kPackTok);
   p.lds = ba::prologue_lds(d, true);
@@ -562,16 +618,17 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   if (pblocks > 0x7fffffff) return fail(BA_ERR_SHAPE, "problem too large");
   plan->mode = mode;
   plan->int8pv = int8pv;
+  plan->flash = flash;
   return BA_OK;
 }
 
 ba_status run_forward(const void* q, const void* k, const void* v, const void* bias, int gh, int gw, int64_t B,
                       int64_t H, int64_t N, int d, float scale, void* o, const int64_t* strides,
                       const DenseBias* dense, void* workspace, size_t ws_bytes, void* stream,
-                      float* lse_out = nullptr) {
+                      float* lse_out = nullptr, bool compact = false) {
   Plan plan;
   ba_status st = make_plan(q, k, v, true, bias, gh, gw, B, H, N, d, scale, o, true, strides, dense, workspace,
-                           ws_bytes, &plan);
+                           ws_bytes, &plan, false, true, compact);
   if (st != BA_OK) return st;
   if (lse_out) {
     const size_t lb = static_cast<size_t>(B * H * N) * 4, tb = static_cast<size_t>(B * H * N * d) * 2;
@@ -595,7 +652,7 @@ ba_status run_forward(const void* q, const void* k, const void* v, const void* b
   }
   int err = ba::launch_prologue(plan.p, stream);
   if (err != 0) return hip_fail(err, "prologue launch");
-  err = ba::launch_attention(plan.f, plan.mode, stream);
+  err = plan.flash ? ba::launch_flash(plan.f, plan.mode, stream) : ba::launch_attention(plan.f, plan.mode, stream);
   if (err != 0) return hip_fail(err, "attention launch");
   return BA_OK;
 }
@@ -622,7 +679,7 @@ ba_status ba_attention_fwd_prepared(const void* q, const void* bias, int gh, int
   ba_status st = make_plan(q, nullptr, nullptr, false, bias, gh, gw, B, H, N, d, scale, o, true, nullptr, nullptr,
                            const_cast<void*>(workspace), ws_bytes, &plan);
   if (st != BA_OK) return st;
-  const int err = ba::launch_attention(plan.f, plan.mode, stream);
+  const int err = plan.flash ? ba::launch_flash(plan.f, plan.mode, stream) : ba::launch_attention(plan.f, plan.mode, stream);
   if (err != 0) return hip_fail(err, "attention launch");
   return BA_OK;
 }
@@ -714,7 +771,7 @@ ba_status run_backward(const void* q, const void* k, const void* v, const void* 
   // the forward's plan validates q, k, v, the bias and the first part of the workspace
   Plan fp;
   st = make_plan(q, k, v, true, bias, gh, gw, B, H, N, d, scale, nullptr, false, nullptr, nullptr, workspace,
-                 ws_bytes, &fp);
+                 ws_bytes, &fp, false, false);
   if (st != BA_OK) return st;
   if (!workspace) return fail(BA_ERR_WORKSPACE, "workspace is NULL");
   const size_t tb = static_cast<size_t>(B * H * N * d);

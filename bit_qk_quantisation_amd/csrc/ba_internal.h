@@ -68,6 +68,10 @@ struct KvJob {
   uint16_t* kst;      // [BH][Npad/64][dpad][64]
   // backward: the largest |v| of each tile (nullptr: not written)
   float* vmax;        // [BH][Npad/64]
+  // the values' rows as they are, contiguous [BH][Npad][d], zero past N
+  // (nullptr: not written); with vt, vq, vmax and vnat all nullptr the
+  // values are not read at all
+  uint16_t* vnat;
   Strides ks, vs;
   int64_t BH;
   int H, N, Npad, d, W, nch, dpad;
@@ -205,6 +209,9 @@ struct FwdArgs {
   int table_flip;          // kBiasTable: read the table flipped in both axes
   int prio_balance;        // 1: lower the wave priority over the last keys
                            // (every workgroup of the grid is resident at once)
+  uint32_t gw32_magic;     // table rows: ceil(2^32 / (gw / 32)), so that key
+                           // block b starts on grid row umulhi(b, magic);
+                           // 0 when gw == 32 (the row is b)
 };
 
 // LDS bytes of the fused kernel: the bias table (table mode, dynamic) and
@@ -227,6 +234,14 @@ int small_static_lds(int cb, int mode);
 int launch_attention_small(const FwdArgs& a, int mode, void* stream);
 // The fused kernel of the 8-bit P.V forward (d <= 128; no dense bias).
 int launch_attention_int8(const FwdArgs& a, int mode, void* stream);
+// The pipelined fused kernel (flash.hip): d in {32, 64, 128}, table rows or
+// no bias; reads V in its natural layout from a.v (strides a.vs), so the
+// prologue writes no V^T for it.  win_rows * 4 * Lpad floats of bias window
+// per key tile must fit its buffers.
+bool flash_supported(int d, int mode, int win_rows, int Lpad);
+int flash_static_lds(int d, int mode);
+int flash_waves_per_simd(int d);
+int launch_flash(const FwdArgs& a, int mode, void* stream);
 
 // Backward pass (d in {32, 64, 128}; table-row, table or no bias).  One
 // kernel, two roles: kRoleQ (lane = query; dq, delta, table gradient) and

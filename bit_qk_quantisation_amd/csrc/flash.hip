@@ -1,0 +1,671 @@
+// Fused BinaryAttention forward for gfx950, pipelined across key blocks.
+//
+// Per (b, h) and query i it computes O_i = sum_j softmax_j(S_ij) V_j with
+//   S_ij = scale * alpha_q,i * alpha_k,j * <sign q_i, sign k_j> + bias(h, i, j)
+// (the scaled 1-bit similarity and the learnable bias of the BinaryAttention
+// summaries: es page, section 2, "Representaciones Binarias Escaladas" and
+// "Mejora mediante Sesgo"; ko page, section 2 (b)), tiled as FlashAttention2
+// is (es page, section 2, "Implementacion en Hardware").
+//
+// Where the time goes on CDNA4.  A 32 x 32 block of scores costs a wave one
+// fp4 MFMA for QK, 2d/16 bf16 MFMAs for P.V, and per lane 16 scores of vector
+// work: a multiply by alpha_k, an FMA with alpha_q and the bias, an exp2 and
+// half a bf16 pack.  The vector ALU is the scarcer unit (4 cycles per wave64
+// instruction, 8 for the exp2), so the kernel is built to keep it issuing:
+//   * the QK product of the NEXT block is issued before this block's vector
+//     work, so no wave waits on a matrix result (the S accumulator is double
+//     buffered in registers);
+//   * the P.V of the previous block (P and its V operands held in registers)
+//     is issued at the start of the block and runs beside the vector work;
+//   * the row sums l_i = sum_j P_ij come out of the matrix cores: one
+//     v_mfma_f32_16x16x32_bf16 per 16 keys whose A operand is 1 where the
+//     lane's B columns belong to the output row's query and 0 elsewhere, so
+//     the product adds up exactly the bf16 P that multiplies V (no v_dot2,
+//     which does not overlap with matrix instructions);
+//   * V is read in its natural [key][channel] layout: the tile copies bring
+//     contiguous key rows into LDS, and the transposing LDS read
+//     (ds_read_b64_tr_b16) hands each lane 4 keys of one channel, which is
+//     the A-operand layout of the P.V product; no transposed copy of V is
+//     written anywhere.
+//
+// Workgroup: 4 waves x 32 queries = 128 queries of one (b, h).  Key tiles of
+// 64 (two blocks of 32) go through three LDS buffers: tile t+2 is copied
+// while tile t is computed and the QK of tile t+1's first block is issued;
+// one barrier per tile, between its two blocks.
+//
+// Softmax in base 2 with log2(e) folded into the scales.  Every logit of the
+// workgroup obeys |s| <= M = scale log2e max alpha_q max alpha_k d +
+// log2e max|b|; when M <= 32 the softmax is taken with no offset (it does not
+// depend on one), otherwise a running row maximum is kept and the
+// accumulators are rescaled when it grows by more than 8.
+#include "ba_internal.h"
+
+namespace ba {
+
+namespace {
+
+constexpr float kFlashFastMax = 32.0f;
+
+template <int D>
+struct FDims {
+  static_assert(D == 32 || D == 64 || D == 128, "the pipelined kernel takes d in {32, 64, 128}");
+  static constexpr int NCH = (D + 63) / 64;      // 64-channel fp4 QK chunks
+  static constexpr int CB = D / 32;               // 32-channel output blocks
+  static constexpr int ROW = 2 * D;               // bytes of one key's values
+  static constexpr int VBYTES = 64 * ROW;         // V of one key tile
+  static constexpr int VPIECES = VBYTES / 1024;   // 1 KiB copy pieces
+  static constexpr int RPP = 1024 / ROW;          // key rows per piece
+  static constexpr int CPR = ROW / 16;            // 16-byte chunks per row
+  static constexpr int KBYTES = NCH * 2048;       // fp4 key operands of one tile
+  // floats of the table-row bias window of one tile (the host checks that
+  // the grid's window fits)
+  static constexpr int WIN = D <= 64 ? 1664 : 1152;
+  static constexpr int WAVES = D <= 64 ? 3 : 2;   // waves per SIMD the registers allow
+};
+
+// Position of 16-byte chunk j of key row r of a V tile: j ^ vswz(r).  The
+// transposing reads of one instruction cover 8 rows and 32 channels; with
+// this swizzle those 512 bytes fall on every LDS bank exactly twice.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D == 32 ? 0 : (D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3));
+}
+
+template <int D, int BIAS>
+struct FBuf {
+  v4i k[FDims<D>::NCH * 128];                  // fp4 key operands [chunk][key][half]
+  float ak[64];                                // key scales
+  v4u v[FDims<D>::VBYTES / 16];                // V rows, chunks swizzled
+  float win[BIAS == kBiasRows ? FDims<D>::WIN : 4];  // table-row bias window
+};
+
+template <int D>
+struct FAcc {
+  v16f o[FDims<D>::CB];  // O^T: lane = query, register = channel
+  v4f l;                 // row sums (all four registers hold l of the lane's query)
+};
+
+// P.V of one finished block, waiting in registers for the next block.
+template <int D>
+struct FPend {
+  uint32_t pk[8];                   // bf16 P: 16 keys x 2 steps of 16
+  v8bf vop[2][FDims<D>::CB];        // V^T operands of the two steps
+};
+
+template <int D>
+struct FCtx {
+  const FwdArgs* a;
+  int lane, wave, li, lh;
+  int bh, head, q0, qi;
+  float aq;                    // alpha_q * scale * log2e
+  v4i qop[FDims<D>::NCH];      // the lane's query operand (fp4 +/-1)
+  v8bf ones;                   // A operand of the row-sum product
+  int off_k, off_akb, off_win; // LDS byte offsets inside a buffer
+  int off_v[FDims<D>::CB];     // byte offset of the lane's transposing reads
+  int yq_lo;
+  rsrc_t krs, ars, vrs, brs;   // sources of the tile copies
+  uint32_t voff;               // the lane's byte offset inside a V copy piece
+  uint32_t vsn;                // bytes from one key's values to the next
+  int win_bytes;
+};
+
+// Grid position of the keys of a tile (table rows: gw % 32 == 0, so a
+// 32-key block never straddles a grid row).  Key block bi starts at row
+// bi / (gw / 32), column 32 (bi % (gw / 32)); the division is a
+// multiplication by the host's ceil(2^32 / (gw / 32)), or none when
+// gw == 32 (magic 0).
+struct FPos {
+  int k0;
+  int ky[2], kx[2];  // grid row and column of the first key of each block
+};
+
+template <int BIAS>
+__device__ __forceinline__ FPos flash_pos(const FwdArgs& a, int t) {
+  FPos p;
+  p.k0 = t * kBN;
+  p.ky[0] = p.ky[1] = p.kx[0] = p.kx[1] = 0;
+  if (BIAS == kBiasRows) {
+    const uint32_t g32 = static_cast<uint32_t>(a.gw) >> 5;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const uint32_t bi = static_cast<uint32_t>(2 * t + blk);
+      const uint32_t y = a.gw32_magic != 0 ? __umulhi(bi, a.gw32_magic) : bi;
+      p.ky[blk] = static_cast<int>(y);
+      p.kx[blk] = static_cast<int>(32 * (bi - y * g32));
+    }
+  }
+  return p;
+}
+
+template <typename T>
+__device__ __forceinline__ T flds(const void* base, int byte_off) {
+  return *reinterpret_cast<const T*>(__builtin_assume_aligned(static_cast<const char*>(base) + byte_off, 8));
+}
+
+// 4 keys of one channel from the natural V tile (see FCtx::off_v).
+__device__ __forceinline__ v2u tr_read(const void* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(const_cast<void*>(p)));
+  return __builtin_bit_cast(v2u, r);
+}
+
+__device__ __forceinline__ v3f fmax3_block(float x, float y, float z, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    x = fmaxf(x, __shfl_xor(x, off, 64));
+    y = fmaxf(y, __shfl_xor(y, off, 64));
+    z = fmaxf(z, __shfl_xor(z, off, 64));
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    red[3 * (threadIdx.x >> 6)] = x;
+    red[3 * (threadIdx.x >> 6) + 1] = y;
+    red[3 * (threadIdx.x >> 6) + 2] = z;
+  }
+  __syncthreads();
+  v3f r = {red[0], red[1], red[2]};
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w)
+    r = v3f{fmaxf(r[0], red[3 * w]), fmaxf(r[1], red[3 * w + 1]), fmaxf(r[2], red[3 * w + 2])};
+  return r;
+}
+
+// ------------------------------------------------------------------ setup --
+// The workgroup's (b, h) and query tile, the lane's packed query, LDS
+// offsets, copy sources and the logit bound M (log2 units).
+template <int D, int BIAS>
+__device__ __forceinline__ float flash_setup(FCtx<D>& c, const FwdArgs& a, float* red) {
+  using F = FDims<D>;
+  c.a = &a;
+  const int tid = threadIdx.x;
+  c.lane = tid & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  c.li = c.lane & 31;
+  c.lh = c.lane >> 5;
+  int wg = blockIdx.x;
+  if (a.xcd_remap) {
+    // consecutive query tiles of a head on one XCD (its K/V stay in that L2)
+    const int per = a.nwg >> 3;
+    wg = (wg & 7) * per + (wg >> 3);
+  }
+  c.bh = wg / a.nqt;
+  const int qt = wg - c.bh * a.nqt;
+  c.head = c.bh % a.H;
+  const int b = c.bh / a.H;
+  c.q0 = qt * kBM;
+  c.qi = c.q0 + c.wave * 32 + c.li;
+
+  // The lane's query: lane (li, lh) forms sign words 2 ch + lh of query qi
+  // and the sum of |q| over them; the partner lane l ^ 32 holds the other
+  // words, so the two partial sums give alpha_q = mean |q|.  Queries past N
+  // are zero (scale 0).
+  float qpart = 0.0f;
+  {
+    const uint16_t* qrow = a.q + token_offset(a.qs, b, c.head, c.qi < a.N ? c.qi : 0);
+#pragma unroll
+    for (int ch = 0; ch < F::NCH; ++ch) {
+      const int word = 2 * ch + c.lh;
+      uint32_t w = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c0 = 32 * word + 8 * k;
+        if (c.qi < a.N && c0 < D) {
+          float part;
+          w |= chunk_signs(*reinterpret_cast<const uint4*>(qrow + c0), part) << (8 * k);
+          qpart += part;
+        }
+      }
+      c.qop[ch] = expand_signs_fp4(w, fp4_magnitude(word_valid(D, word)));
+    }
+  }
+  const float alpha_q = sum_halves(qpart) / static_cast<float>(D);
+  c.aq = alpha_q * a.qscale;
+
+  // Row-sum operand: lane l supplies A row l % 16 for k-slots 8 (l / 16) ..;
+  // those slots hold P of query 16 ((l / 16) % 2) + column, so a 1 where
+  // (l / 16) % 2 == ((l % 16) / 4) % 2 makes output row r sum the P of query
+  // 16 ((r / 4) % 2) + column: every output register of lane l is l of its
+  // query l % 32.
+  {
+    const bool one = ((c.lane >> 4) & 1) == (((c.lane & 15) >> 2) & 1);
+    const __bf16 x = one ? (__bf16)1.0f : (__bf16)0.0f;
+    c.ones = v8bf{x, x, x, x, x, x, x, x};
+  }
+
+  c.off_k = (c.li * 2 + c.lh) * 16;
+  // the key scale register r of a 16-lane row needs sits in lane 16 row + r
+  c.off_akb = 4 * (8 * ((c.lane & 15) >> 2) + 4 * c.lh + (c.lane & 3));
+  {
+    // Transposing reads: in each group of 16 lanes, lane 4k + m supplies the
+    // address of 4 channels of key row 4 lh + k, and lane i then receives
+    // channel i of the group's 16 of those 4 rows.  Lane l (query column,
+    // A row = channel 16 ((l/16) % 2) + i) thus gets keys 4 lh .. 4 lh + 3
+    // of its channel: the slots 0..3 of its half of the 16-key step.
+    const int g = c.lane >> 4, j = c.lane & 15, kk = j >> 2, m = j & 3;
+    const int row = 4 * c.lh + kk;
+#pragma unroll
+    for (int cb = 0; cb < F::CB; ++cb) {
+      const int ch0 = 32 * cb + 16 * (g & 1) + 4 * m;
+      c.off_v[cb] = row * F::ROW + (((ch0 >> 3) ^ vswz<D>(row)) << 4) + ((ch0 >> 2) & 1) * 8;
+    }
+  }
+  c.off_win = 0;
+  c.yq_lo = 0;
+  if (BIAS == kBiasRows) {
+    // bias(i, j) = R[dy][gw-1-xi+xj], read from copy s = (gw-1-xi) & 3 at an
+    // aligned float offset, in window row (yq - yq_lo) + (yk_hi - yk)
+    const int yq = c.qi / a.gw, xq = c.qi - yq * a.gw;
+    c.yq_lo = c.q0 / a.gw;
+    const int bsel = (a.gw - 1 - xq) & 3;
+    c.off_win = (((yq - c.yq_lo) * 4 + bsel) * a.Lpad + (a.gw - 1 - xq + 4 * c.lh - bsel)) * 4;
+  }
+
+  // copy sources: every range lies inside the section it names
+  c.krs = make_rsrc(reinterpret_cast<const char*>(a.kop) + static_cast<int64_t>(c.bh) * (a.Npad / kBN) * F::KBYTES,
+                    static_cast<uint32_t>((a.Npad / kBN) * F::KBYTES));
+  c.ars = make_rsrc(a.alpha_k + static_cast<int64_t>(c.bh) * a.Npad, static_cast<uint32_t>(a.Npad * 4));
+  // V rows of this head; keys past N read as 0 (the range ends at key N-1)
+  c.vsn = static_cast<uint32_t>(a.vs.sn * 2);
+  c.vrs = make_rsrc(a.v + token_offset(a.vs, b, c.head, 0),
+                    static_cast<uint32_t>((static_cast<int64_t>(a.N - 1) * a.vs.sn + D) * 2));
+  {
+    const int r = c.lane / F::CPR, pos = c.lane % F::CPR;
+    c.voff = static_cast<uint32_t>(r) * c.vsn + static_cast<uint32_t>((pos ^ vswz<D>(r)) << 4);
+  }
+  c.brs = c.ars;
+  c.win_bytes = 0;
+  if (BIAS == kBiasRows) {
+    const int rows_p = 2 * a.gh - 1 + 2 * kBiasPadRows;
+    c.brs = make_rsrc(a.bias4 + static_cast<int64_t>(c.head) * rows_p * 4 * a.Lpad,
+                      static_cast<uint32_t>(rows_p * 16 * a.Lpad));
+    c.win_bytes = a.win_rows * 16 * a.Lpad;
+  }
+
+  // logit bound
+  const int nblk = a.Npad / 64;
+  float km = 0.0f, bm = 0.0f;
+  for (int e = tid; e < nblk; e += kThreads) km = fmaxf(km, a.kmax_blk[static_cast<int64_t>(c.bh) * nblk + e]);
+  if (BIAS == kBiasRows) {
+    const int rows = 2 * a.gh - 1;
+    for (int e = tid; e < rows; e += kThreads) bm = fmaxf(bm, a.bias_row_max[c.head * rows + e]);
+  }
+  const v3f mx = fmax3_block(km, bm, alpha_q, red);
+  return a.qscale * mx[2] * mx[0] * static_cast<float>(D) + mx[1];
+}
+
+// ---------------------------------------------------------------- copies --
+// Starts the copies of key tile t (first key kp.k0) into `tb`; lane l of a
+// wave fills bytes [16 l, 16 l + 16) of a 1 KiB piece (4 bytes of the key
+// scales).
+template <int D, int BIAS>
+__device__ __forceinline__ void flash_copy(const FCtx<D>& c, FBuf<D, BIAS>& tb, int t) {
+  using F = FDims<D>;
+  const FwdArgs& a = *c.a;
+  const FPos kp = flash_pos<BIAS>(a, __builtin_amdgcn_readfirstlane(t));
+  char* kdst = reinterpret_cast<char*>(&tb.k[0]);
+#pragma unroll
+  for (int j = 0; j < (2 * F::NCH + 3) / 4; ++j)
+    if (c.wave + 4 * j < 2 * F::NCH)
+      dma16(c.krs, kdst + (c.wave + 4 * j) * 1024, static_cast<uint32_t>(c.lane * 16),
+            __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kp.k0 / kBN * F::KBYTES + (c.wave + 4 * j) * 1024)));
+  char* vdst = reinterpret_cast<char*>(&tb.v[0]);
+#pragma unroll
+  for (int j = 0; j < (F::VPIECES + 3) / 4; ++j) {
+    const int p = c.wave + 4 * j;
+    if (p < F::VPIECES)
+      dma16(c.vrs, vdst + p * 1024, c.voff,
+            __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kp.k0 + p * F::RPP) * c.vsn));
+  }
+  if (c.wave == 0)
+    dma4(c.ars, &tb.ak[0], static_cast<uint32_t>(c.lane * 4),
+         __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kp.k0 * 4)));
+  if (BIAS == kBiasRows) {
+    // window rows start at dy = yq_lo - yk_hi; yk_hi is the row of block 1
+    const int dy0 = c.yq_lo - kp.ky[1] + a.gh - 1 + kBiasPadRows;
+    const uint32_t bs = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(dy0 * 16 * a.Lpad));
+    const uint32_t loff = static_cast<uint32_t>(c.wave * 1024 + c.lane * 16);
+    char* bdst = reinterpret_cast<char*>(&tb.win[0]);
+#pragma unroll
+    for (int j = 0; j < (F::WIN * 4 + 4095) / 4096; ++j)
+      if (static_cast<int>(loff) + 4096 * j < c.win_bytes)
+        dma16(c.brs, bdst + (c.wave + 4 * j) * 1024, loff + 4096 * j, bs);
+  }
+}
+
+// --------------------------------------------------------------- compute --
+template <int D, int BIAS>
+__device__ __forceinline__ v16f flash_qk(const FCtx<D>& c, const FBuf<D, BIAS>& tb, int blk) {
+  v16f s = v16f{};
+#pragma unroll
+  for (int ch = 0; ch < FDims<D>::NCH; ++ch)
+    s = mfma_signs_32x32x64(flds<v4i>(tb.k, c.off_k + ch * 2048 + blk * 1024), c.qop[ch], s);
+  return s;
+}
+
+template <int D>
+__device__ __forceinline__ void flash_pv(const FCtx<D>& c, const FPend<D>& pp, FAcc<D>& acc) {
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const v4u pw = {pp.pk[4 * st], pp.pk[4 * st + 1], pp.pk[4 * st + 2], pp.pk[4 * st + 3]};
+    const v8bf p = __builtin_bit_cast(v8bf, pw);
+#pragma unroll
+    for (int cb = 0; cb < FDims<D>::CB; ++cb) acc.o[cb] = mfma_bf16_32x32x16(pp.vop[st][cb], p, acc.o[cb]);
+    acc.l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.ones, p, acc.l, 0, 0, 0);
+  }
+}
+
+// V^T operands of block `blk` of the tile: per 16-key step, per 32-channel
+// block, two transposing reads (slots 0..3 and 4..7 of the lane's half).
+template <int D, int BIAS>
+__device__ __forceinline__ void flash_vops(const FCtx<D>& c, const FBuf<D, BIAS>& tb, int blk, FPend<D>& pp) {
+  using F = FDims<D>;
+  const char* vb = reinterpret_cast<const char*>(&tb.v[0]);
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int cb = 0; cb < F::CB; ++cb) {
+      const int base = c.off_v[cb] + (32 * blk + 16 * st) * F::ROW;
+      const v2u lo = tr_read(vb + base);
+      const v2u hi = tr_read(vb + base + 8 * F::ROW);
+      pp.vop[st][cb] = __builtin_bit_cast(v8bf, v4u{lo[0], lo[1], hi[0], hi[1]});
+    }
+}
+
+template <int D>
+__device__ __forceinline__ int flash_win_off(const FCtx<D>& c, const FPos& kp, int blk) {
+  const int u = __builtin_amdgcn_readfirstlane((kp.ky[1] - kp.ky[blk]) * 16 * c.a->Lpad + kp.kx[blk] * 4);
+  int off = c.off_win + u;
+  asm("" : "+v"(off));
+  return off;
+}
+
+// u[r] = s[r] * alpha_k of the key accumulator register r holds, taken by
+// DPP row broadcast from lane 16 row + r (one v_mul_f32_dpp per score).  The
+// compiler splits a share of these into a broadcast move and a multiply,
+// which costs a vector instruction per score, so they are written out.  The
+// s_nop covers a vector write of akv right before the first broadcast read.
+__device__ __forceinline__ void scale_by_keys(const v16f& s, float akv, float (&u)[16]) {
+  const float s0 = s[0], s1 = s[1], s2 = s[2], s3 = s[3], s4 = s[4], s5 = s[5], s6 = s[6], s7 = s[7];
+  const float s8 = s[8], s9 = s[9], s10 = s[10], s11 = s[11], s12 = s[12], s13 = s[13], s14 = s[14], s15 = s[15];
+  asm("s_nop 1\n\t"
+      "v_mul_f32_dpp %0, %32, %16 row_newbcast:0 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %1, %32, %17 row_newbcast:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %2, %32, %18 row_newbcast:2 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %3, %32, %19 row_newbcast:3 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %4, %32, %20 row_newbcast:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %5, %32, %21 row_newbcast:5 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %6, %32, %22 row_newbcast:6 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %7, %32, %23 row_newbcast:7 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %8, %32, %24 row_newbcast:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %9, %32, %25 row_newbcast:9 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %10, %32, %26 row_newbcast:10 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %11, %32, %27 row_newbcast:11 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %12, %32, %28 row_newbcast:12 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %13, %32, %29 row_newbcast:13 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %14, %32, %30 row_newbcast:14 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %15, %32, %31 row_newbcast:15 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "=&v"(u[0]), "=&v"(u[1]), "=&v"(u[2]), "=&v"(u[3]), "=&v"(u[4]), "=&v"(u[5]), "=&v"(u[6]),
+        "=&v"(u[7]), "=&v"(u[8]), "=&v"(u[9]), "=&v"(u[10]), "=&v"(u[11]), "=&v"(u[12]), "=&v"(u[13]),
+        "=&v"(u[14]), "=&v"(u[15])
+      : "v"(s0), "v"(s1), "v"(s2), "v"(s3), "v"(s4), "v"(s5), "v"(s6), "v"(s7), "v"(s8), "v"(s9), "v"(s10),
+        "v"(s11), "v"(s12), "v"(s13), "v"(s14), "v"(s15), "v"(akv));
+}
+
+
+// Logits of block `blk` (base 2), then P = exp2(s - offset) as bf16 pairs.
+// EXACT: the running row maximum (mrow) is the offset, with the lazy
+// rescale of the accumulators; otherwise the offset is 0.  mask: keys past
+// N get probability 0 (the ragged last tile; never with table rows).
+template <int D, int BIAS, bool EXACT>
+__device__ __forceinline__ void flash_probs(const FCtx<D>& c, const FBuf<D, BIAS>& tb, const FPos& kp, int blk,
+                                            const v16f& s, bool mask, uint32_t (&pk)[8], FAcc<D>& acc,
+                                            float& mrow) {
+  const FwdArgs& a = *c.a;
+  int woff = 0;
+  if (BIAS == kBiasRows) woff = flash_win_off(c, kp, blk);
+  const float akv = flds<float>(tb.ak, c.off_akb + blk * 128);
+  float x[16], u[16];
+  scale_by_keys(s, akv, u);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const float u0 = u[4 * b], u1 = u[4 * b + 1], u2 = u[4 * b + 2], u3 = u[4 * b + 3];
+    if (BIAS == kBiasRows) {
+      const v4f bias = flds<v4f>(tb.win, woff + 32 * b);
+      x[4 * b + 0] = fmaf(u0, c.aq, bias.x);
+      x[4 * b + 1] = fmaf(u1, c.aq, bias.y);
+      x[4 * b + 2] = fmaf(u2, c.aq, bias.z);
+      x[4 * b + 3] = fmaf(u3, c.aq, bias.w);
+    } else {
+      x[4 * b + 0] = u0 * c.aq;
+      x[4 * b + 1] = u1 * c.aq;
+      x[4 * b + 2] = u2 * c.aq;
+      x[4 * b + 3] = u3 * c.aq;
+    }
+  }
+  if (BIAS != kBiasRows && mask) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kp.k0 + blk * 32 + 8 * (r >> 2) + 4 * c.lh + (r & 3);
+      if (key >= a.N) x[r] = -INFINITY;
+    }
+  }
+  if (EXACT) {
+    float mt = x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
+    mt = max_halves(mt);
+    const float mnew = fmaxf(mrow, mt);
+    if (__any(mnew > mrow + 8.0f)) {
+      const float f = fast_exp2(mrow - mnew);
+#pragma unroll
+      for (int cb = 0; cb < FDims<D>::CB; ++cb) acc.o[cb] *= f;
+      acc.l *= f;
+      mrow = mnew;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] -= mrow;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pk[j] = pack_bf16x2(fast_exp2(x[2 * j]), fast_exp2(x[2 * j + 1]));
+}
+
+// Wave priority over the last three eighths of the keys (see the host's
+// prio_balance): equal-priority waves issue oldest first, so without this the
+// first workgroup of a CU finishes long before the last one.
+__device__ __forceinline__ void flash_priority(const FwdArgs& a, int t, int nkt) {
+  if (!a.prio_balance) return;
+  const int e = (8 * t) / nkt;
+  if (e <= 4)
+    __builtin_amdgcn_s_setprio(3);
+  else if (e == 5)
+    __builtin_amdgcn_s_setprio(2);
+  else if (e == 6)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
+// Keeps `pk` computed here: without it the compiler sinks the vector work
+// of a block towards the product that uses it, past the barrier, and splits
+// the key-scale broadcasts from the multiplies they should fold into.
+__device__ __forceinline__ void flash_pin(uint32_t (&pk)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(pk[j]));
+}
+
+// One key tile: block 0, the barrier, the copies of tile t+2, block 1.
+// s0 holds the QK of this tile's block 0 on entry; block 1's goes to s1
+// while block 0 is worked on, and the next tile's block 0 back into s0.
+template <int D, int BIAS, bool EXACT>
+__device__ __forceinline__ void flash_tile(const FCtx<D>& c, const FBuf<D, BIAS>& cur, const FBuf<D, BIAS>& nxt,
+                                           FBuf<D, BIAS>& far, int t, int nkt, v16f& s0, v16f& s1,
+                                           FPend<D>& pp, FAcc<D>& acc, float& mrow) {
+  const FwdArgs& a = *c.a;
+  const FPos kp = flash_pos<BIAS>(a, t);
+  const int k0 = kp.k0;
+  const bool has1 = k0 + 32 < a.N;
+  // block 0
+  if (has1) s1 = flash_qk(c, cur, 1);
+  flash_pv(c, pp, acc);
+  flash_probs<D, BIAS, EXACT>(c, cur, kp, 0, s0, k0 + 32 > a.N, pp.pk, acc, mrow);
+  flash_pin(pp.pk);
+  flash_vops(c, cur, 0, pp);
+  // tile t+1 is in `nxt` once every wave's copies have landed; every wave is
+  // done with tile t-1, whose buffer `far` takes tile t+2
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (t + 2 < nkt) flash_copy(c, far, t + 2);
+  flash_priority(a, t, nkt);
+  if (has1) {
+    if (t + 1 < nkt) s0 = flash_qk(c, nxt, 0);
+    flash_pv(c, pp, acc);
+    flash_probs<D, BIAS, EXACT>(c, cur, kp, 1, s1, k0 + 64 > a.N, pp.pk, acc, mrow);
+    flash_pin(pp.pk);
+    flash_vops(c, cur, 1, pp);
+  }
+}
+
+// All keys; returns the offset the sums are taken against (log2 units).
+template <int D, int BIAS, bool EXACT>
+__device__ __forceinline__ float flash_pass(const FCtx<D>& c, FBuf<D, BIAS>& b0, FBuf<D, BIAS>& b1,
+                                            FBuf<D, BIAS>& b2, FAcc<D>& acc) {
+  const FwdArgs& a = *c.a;
+#pragma unroll
+  for (int cb = 0; cb < FDims<D>::CB; ++cb) acc.o[cb] = v16f{};
+  acc.l = v4f{};
+  float mrow = EXACT ? -INFINITY : 0.0f;
+  const int nkt = (a.N + kBN - 1) / kBN;
+  flash_copy(c, b0, 0);
+  if (nkt > 1) flash_copy(c, b1, 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  v16f s0 = flash_qk(c, b0, 0), s1 = v16f{};
+  // nothing is pending before the first block: P = 0
+  FPend<D> pp;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pp.pk[j] = 0u;
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int cb = 0; cb < FDims<D>::CB; ++cb) pp.vop[st][cb] = v8bf{};
+  for (int t = 0; t < nkt; t += 3) {
+    flash_tile<D, BIAS, EXACT>(c, b0, b1, b2, t, nkt, s0, s1, pp, acc, mrow);
+    if (t + 1 >= nkt) break;
+    flash_tile<D, BIAS, EXACT>(c, b1, b2, b0, t + 1, nkt, s0, s1, pp, acc, mrow);
+    if (t + 2 >= nkt) break;
+    flash_tile<D, BIAS, EXACT>(c, b2, b0, b1, t + 2, nkt, s0, s1, pp, acc, mrow);
+  }
+  flash_pv(c, pp, acc);
+  return mrow;
+}
+
+// O = O^T / l in bf16; each wave stages its 32 rows in LDS (the V regions of
+// two buffers, free after the key loop) and writes whole rows with
+// nontemporal 16-byte stores.
+template <int D>
+__device__ __forceinline__ void flash_epilogue(const FCtx<D>& c, const FwdArgs& a, FAcc<D>& acc, float mrow,
+                                               unsigned char* stage0, unsigned char* stage1) {
+#pragma unroll
+  for (int cb = 0; cb < FDims<D>::CB; ++cb) pin_uniform(acc.o[cb]);
+  float l = acc.l[0];
+  {
+    float e = l;
+    asm volatile("" : "+v"(e));
+    l = e;
+  }
+  const float inv = 1.0f / l;
+  if (a.lse_out && c.lh == 0 && c.qi < a.N)
+    a.lse_out[static_cast<int64_t>(c.bh) * a.N + c.qi] = (mrow + log2f(l)) * kLn2;
+  constexpr int C = D / 8;
+  constexpr int sw = (C & 7) == 0 ? 7 : 0;
+  unsigned char* ws = (c.wave < 2 ? stage0 : stage1) + (c.wave & 1) * 64 * D;
+  __syncthreads();  // every wave is past its last read of the tile buffers
+#pragma unroll
+  for (int cb = 0; cb < FDims<D>::CB; ++cb)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int c0 = cb * 32 + 8 * b + 4 * c.lh;
+      v2u w;
+      w[0] = pack_bf16x2(acc.o[cb][4 * b + 0] * inv, acc.o[cb][4 * b + 1] * inv);
+      w[1] = pack_bf16x2(acc.o[cb][4 * b + 2] * inv, acc.o[cb][4 * b + 3] * inv);
+      *reinterpret_cast<v2u*>(ws + (c.li * C + ((c0 >> 3) ^ (c.li & sw))) * 16 + (c0 & 4) * 2) = w;
+    }
+  __syncthreads();
+  const int r0 = c.q0 + c.wave * 32;
+  const int64_t b = c.bh / a.H;
+  for (int e = c.lane; e < 32 * C; e += 64) {
+    const int r = e / C, j = e - r * C;
+    if (r0 + r < a.N) {
+      const v4u x = flds<v4u>(ws, (r * C + (j ^ (r & sw))) * 16);
+      __builtin_nontemporal_store(x, reinterpret_cast<v4u*>(a.o + token_offset(a.os, b, c.head, r0 + r) + 8 * j));
+    }
+  }
+}
+
+template <int D, int BIAS>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FDims<D>::WAVES)))
+flash_fwd_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) FBuf<D, BIAS> b0;
+  __shared__ __attribute__((aligned(16))) FBuf<D, BIAS> b1;
+  __shared__ __attribute__((aligned(16))) FBuf<D, BIAS> b2;
+  __shared__ float red[3 * kThreads / 64];
+  FCtx<D> c;
+  const float M = flash_setup<D, BIAS>(c, a, red);
+  FAcc<D> acc;
+  float mrow;
+  if (M <= kFlashFastMax)  // false for NaN as well
+    mrow = flash_pass<D, BIAS, false>(c, b0, b1, b2, acc);
+  else
+    mrow = flash_pass<D, BIAS, true>(c, b0, b1, b2, acc);
+  flash_epilogue<D>(c, a, acc, mrow, reinterpret_cast<unsigned char*>(&b0.v[0]),
+                    reinterpret_cast<unsigned char*>(&b1.v[0]));
+}
+
+template <int D, int BIAS>
+int flash_lds() {
+  return static_cast<int>(3 * sizeof(FBuf<D, BIAS>) + 3 * kThreads / 64 * 4);
+}
+
+template <int D>
+int launch_flash_d(const FwdArgs& a, int mode, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(a.nwg), block(kThreads);
+  if (mode == kBiasRows)
+    hipLaunchKernelGGL((flash_fwd_kernel<D, kBiasRows>), grid, block, a.dyn_lds, s, a);
+  else
+    hipLaunchKernelGGL((flash_fwd_kernel<D, kBiasNone>), grid, block, a.dyn_lds, s, a);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace
+
+bool flash_supported(int d, int mode, int win_rows, int Lpad) {
+  if (d != 32 && d != 64 && d != 128) return false;
+  if (mode == kBiasNone) return true;
+  if (mode != kBiasRows) return false;
+  const int win = win_rows * 4 * Lpad;
+  return win <= (d <= 64 ? FDims<64>::WIN : FDims<128>::WIN);
+}
+
+int flash_static_lds(int d, int mode) {
+  const bool rows = mode == kBiasRows;
+  switch (d) {
+    case 32: return rows ? flash_lds<32, kBiasRows>() : flash_lds<32, kBiasNone>();
+    case 64: return rows ? flash_lds<64, kBiasRows>() : flash_lds<64, kBiasNone>();
+    default: return rows ? flash_lds<128, kBiasRows>() : flash_lds<128, kBiasNone>();
+  }
+}
+
+int flash_waves_per_simd(int d) { return d <= 64 ? FDims<64>::WAVES : FDims<128>::WAVES; }
+
+int launch_flash(const FwdArgs& a, int mode, void* stream) {
+  switch (a.d) {
+    case 32: return launch_flash_d<32>(a, mode, stream);
+    case 64: return launch_flash_d<64>(a, mode, stream);
+    case 128: return launch_flash_d<128>(a, mode, stream);
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
+}
+
+}  // namespace ba

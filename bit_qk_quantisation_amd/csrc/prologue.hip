@@ -144,6 +144,8 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
   const int64_t b = bh / job.H, h = bh - b * job.H;
   const uint16_t* kbase = job.k + token_offset(job.ks, b, h, n0);
   const uint16_t* vbase = job.v + token_offset(job.vs, b, h, n0);
+  // the values are read only for an output that needs them
+  const bool want_v = job.vt || job.vq || job.vmax || job.vnat;
   uint4 kr[kMaxChunks], vr[kMaxChunks];
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
@@ -152,7 +154,7 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
     if (g < total) {
       const int tok = g / C, ch = g - tok * C;
       kr[i] = *reinterpret_cast<const uint4*>(kbase + tok * job.ks.sn + ch * 8);
-      vr[i] = *reinterpret_cast<const uint4*>(vbase + tok * job.vs.sn + ch * 8);
+      if (want_v) vr[i] = *reinterpret_cast<const uint4*>(vbase + tok * job.vs.sn + ch * 8);
     }
   }
 #pragma unroll
@@ -163,7 +165,9 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
       float part;
       store_sign_bytes(sb, tok, ch, W, chunk_signs(kr[i], part));
       sp[tok * 33 + ch] = part;
-      *reinterpret_cast<uint4*>(vs + tok * stride + ch * 8) = vr[i];
+      if (job.vt || job.vq) *reinterpret_cast<uint4*>(vs + tok * stride + ch * 8) = vr[i];
+      if (job.vnat)
+        stream_out(job.vnat + (bh * job.Npad + n0 + tok) * d + ch * 8, v4u{vr[i].x, vr[i].y, vr[i].z, vr[i].w});
     }
   }
   zero_pad_bytes(sb, C, W);
@@ -241,6 +245,7 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
     kv_codes(job, blk, bh, tile, vs, stride, reinterpret_cast<float*>(vs + kPackTok * stride), sp);
     return;
   }
+  if (!job.vt) return;
 
   // V^T
   uint16_t* out = job.vt + blk * static_cast<int64_t>(job.dpad) * kPackTok;

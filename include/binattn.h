@@ -19,8 +19,10 @@
  *   [H, 2*gh-1, 2*gw-1].  Packed sign words are uint32 [B, H, N, W] with
  *   W = ceil(d/32).  Scales are float32 [B, H, N].
  * - All pointers are device pointers (hipMalloc'ed or equivalent) aligned to
- *   16 bytes.  The caller owns every buffer.  The library never allocates,
- *   frees or synchronises.
+ *   16 bytes.  The caller owns every buffer.  The library allocates no device
+ *   memory, frees nothing and does not synchronise, with one stated
+ *   exception: ba_attention_bwd creates one side stream and two events per
+ *   device on its first call there (see that entry).
  * - stream is a hipStream_t passed as void*; NULL means the default stream.
  *   All work is enqueued on it, and the call returns before it completes.
  *   Buffers must stay valid until the stream has passed the work.
@@ -91,11 +93,13 @@ ba_status ba_pack_signs(const void* x, int64_t B, int64_t H, int64_t N, int d,
 
 /* Workspace bytes that ba_attention_fwd needs for this problem: the K signs
  * as fp4 +/-1 matrix operands (32 bytes per token and 64 channels), the K
- * scales and their maximum per 64 tokens, a key-major V^T copy (per head, N
- * padded to a multiple of 128) and, for a bias grid with gw % 32 == 0, the
- * table rows in float32.  The queries are packed inside the fused kernel.
- * Pass gh = gw = 0 for a call without bias table.  Returns 0 for sizes the
- * library rejects (including gh*gw != N when a grid is given). */
+ * scales and their maximum per 64 tokens, a key-major V^T section (per
+ * head, N padded to a multiple of 128), for a bias grid with gw % 32 == 0 the
+ * table rows in float32, and, where the prepared forward runs the pipelined
+ * kernel (see ba_attention_fwd), a copy of V in its own layout [B,H,Npad,d].
+ * The queries are packed inside the fused kernel.  Pass gh = gw = 0 for a
+ * call without bias table.  Returns 0 for sizes the library rejects
+ * (including gh*gw != N when a grid is given). */
 size_t ba_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int gh, int gw);
 
 /* ba_attention_fwd -- BinaryAttention forward.
@@ -118,8 +122,12 @@ size_t ba_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int gh, int gw
  *              bytes (gh = gw = 0 there when bias is NULL),
  *              256-byte aligned.  Its contents on entry do not matter, and it
  *              must not be shared by calls that may overlap on the GPU.
- * Two kernels are enqueued: the sign/scale pack of K with the V^T copy,
- * then the fused attention kernel (which packs Q).
+ * Two kernels are enqueued: the sign/scale pack of K (with the bias rows),
+ * then the fused attention kernel, which packs Q.  For d in {32, 64, 128}
+ * with the table rows (gw % 32 == 0, window small enough) or no bias, the
+ * fused kernel is the pipelined one, which reads V where it lies; otherwise
+ * the prologue also writes V^T into the workspace for it.  For N <= 256,
+ * d in {32, 64} and no table rows, one kernel does everything.
  * Errors: BA_ERR_NULL, BA_ERR_SHAPE, BA_ERR_UNSUPPORTED, BA_ERR_ALIGN,
  *         BA_ERR_WORKSPACE, BA_ERR_HIP. */
 ba_status ba_attention_fwd(const void* q, const void* k, const void* v,
@@ -211,12 +219,14 @@ ba_status ba_attention_fwd_int8pv(const void* q, const void* k, const void* v,
                                   void* stream);
 
 /* The two halves of ba_attention_fwd, for callers that time or schedule the
- * two kernels separately.
+ * two kernels separately, or serve several queries from one K and V.
  *
  * ba_attention_prepare -- enqueues the prologue kernel: the signs and scales
- * of K ("Representaciones Binarias Escaladas"), the key-major V^T copy and,
- * for gw % 32 == 0, the float32 bias rows, all written into `workspace`.
- * Same arguments and errors as ba_attention_fwd, without q, scale and o.
+ * of K ("Representaciones Binarias Escaladas"), the key-major V^T copy, a
+ * copy of V in its own layout where the prepared forward runs the pipelined
+ * kernel, and, for gw % 32 == 0, the float32 bias rows, all written into
+ * `workspace`.  Same arguments and errors as ba_attention_fwd, without q,
+ * scale and o.
  *
  * ba_attention_fwd_prepared -- enqueues only the fused kernel, which packs
  * the queries itself and reads a workspace that ba_attention_prepare filled
@@ -224,8 +234,10 @@ ba_status ba_attention_fwd_int8pv(const void* q, const void* k, const void* v,
  * prepare first).  The bias table is read again here when gw % 32 != 0.
  * Same arguments and errors as ba_attention_fwd, without k and v.
  *
- * ba_attention_fwd(...) is ba_attention_prepare(...) followed by
- * ba_attention_fwd_prepared(...) on the same stream. */
+ * The pair gives ba_attention_fwd's O bit for bit (for contiguous inputs:
+ * the kernels and their arithmetic are the same; where ba_attention_fwd
+ * runs one kernel for short sequences, the pair runs the two-kernel path
+ * with the same arithmetic). */
 ba_status ba_attention_prepare(const void* k, const void* v,
                                const void* bias, int gh, int gw,
                                int64_t B, int64_t H, int64_t N, int d,

@@ -70,13 +70,36 @@ def expected_workspace(B, H, N, d, gh=0, gw=0, int8pv=False):
         secs += [B * H * dpad * npad, B * H * (npad // 64) * dpad * 4, B * H * dpad * 4, B * H * dpad * 4]
     else:
         secs.append(B * H * dpad * npad * 2)
-    if gh and gw % 32 == 0:
+    rows = bool(gh) and gw % 32 == 0
+    lpad = 0
+    if rows:
         lpad = _round(2 * gw - 1 + 3, 4)
         while lpad % 64 != 16:
             lpad += 4
         secs.append(H * (2 * gh - 1 + 16) * 4 * lpad * 4)
         secs.append(H * (2 * gh - 1) * 4)
+    if not int8pv and _prepared_pipelined(N, d, gh, gw, rows, lpad):
+        # the values' natural rows, for the prepared forward's pipelined kernel
+        secs.append(B * H * npad * d * 2)
     return sum(_round(s, 256) for s in secs)
+
+
+def _window_rows(N, gw):
+    qspan = max(((q0 + 127) // gw - q0 // gw) for q0 in range(0, _round(N, 128), 128))
+    kspan = max(((k0 + 63) // gw - k0 // gw) for k0 in range(0, N, 64))
+    return qspan + kspan + 1
+
+
+def _prepared_pipelined(N, d, gh, gw, rows, lpad):
+    """The prepared forward runs the pipelined kernel (and the workspace holds
+    a natural copy of V) for d in {32, 64, 128} with table rows whose window
+    fits its buffers, or without a bias, unless the whole forward would run
+    as one launch (N <= 256, d in {32, 64}, no table rows)."""
+    if d not in (32, 64, 128) or (gh and not rows):
+        return False
+    if N <= 256 and d in (32, 64) and not rows:
+        return False
+    return not rows or _window_rows(N, gw) * 4 * lpad <= (1664 if d <= 64 else 1152)
 
 
 @pytest.mark.parametrize("shape", [(1, 3, 196, 64, 14, 14), (32, 12, 196, 64, 14, 14),
@@ -397,3 +420,4 @@ def test_default_workspace_per_stream():
     assert ws.get(cpu, 900, stream=111).data_ptr() == a.data_ptr()
     c = ws.get(cpu, 5000, stream=111)
     assert c.numel() >= 5000 and ws.get(cpu, 1000, stream=222).data_ptr() == b.data_ptr()
+
