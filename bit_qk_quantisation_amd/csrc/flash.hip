@@ -334,43 +334,11 @@ __device__ __forceinline__ void flash_copy(const FCtx<D>& c, FBuf<D, BIAS>& tb, 
 }
 
 // --------------------------------------------------------------- compute --
-template <int D, int BIAS>
-__device__ __forceinline__ v16f flash_qk(const FCtx<D>& c, const FBuf<D, BIAS>& tb, int blk) {
-  v16f s = v16f{};
-#pragma unroll
-  for (int ch = 0; ch < FDims<D>::NCH; ++ch)
-    s = mfma_signs_32x32x64(flds<v4i>(tb.k, c.off_k + ch * 2048 + blk * 1024), c.qop[ch], s);
-  return s;
-}
-
-template <int D>
-__device__ __forceinline__ void flash_pv(const FCtx<D>& c, const FPend<D>& pp, FAcc<D>& acc) {
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const v4u pw = {pp.pk[4 * st], pp.pk[4 * st + 1], pp.pk[4 * st + 2], pp.pk[4 * st + 3]};
-    const v8bf p = __builtin_bit_cast(v8bf, pw);
-#pragma unroll
-    for (int cb = 0; cb < FDims<D>::CB; ++cb) acc.o[cb] = mfma_bf16_32x32x16(pp.vop[st][cb], p, acc.o[cb]);
-    acc.l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.ones, p, acc.l, 0, 0, 0);
-  }
-}
-
-// V^T operands of block `blk` of the tile: per 16-key step, per 32-channel
-// block, two transposing reads (slots 0..3 and 4..7 of the lane's half).
-template <int D, int BIAS>
-__device__ __forceinline__ void flash_vops(const FCtx<D>& c, const FBuf<D, BIAS>& tb, int blk, FPend<D>& pp) {
-  using F = FDims<D>;
-  const char* vb = reinterpret_cast<const char*>(&tb.v[0]);
-#pragma unroll
-  for (int st = 0; st < 2; ++st)
-#pragma unroll
-    for (int cb = 0; cb < F::CB; ++cb) {
-      const int base = c.off_v[cb] + (32 * blk + 16 * st) * F::ROW;
-      const v2u lo = tr_read(vb + base);
-      const v2u hi = tr_read(vb + base + 8 * F::ROW);
-      pp.vop[st][cb] = __builtin_bit_cast(v8bf, v4u{lo[0], lo[1], hi[0], hi[1]});
-    }
-}
+// What the vector work of a block reads from LDS, fetched one block ahead.
+struct FIn {
+  float akv;     // the key scale this lane hands to its row's broadcasts
+  v4f bias[4];   // table rows: the lane's 16 bias values (0 without a table)
+};
 
 template <int D>
 __device__ __forceinline__ int flash_win_off(const FCtx<D>& c, const FPos& kp, int blk) {
@@ -380,94 +348,222 @@ __device__ __forceinline__ int flash_win_off(const FCtx<D>& c, const FPos& kp, i
   return off;
 }
 
-// u[r] = s[r] * alpha_k of the key accumulator register r holds, taken by
-// DPP row broadcast from lane 16 row + r (one v_mul_f32_dpp per score).  The
-// compiler splits a share of these into a broadcast move and a multiply,
-// which costs a vector instruction per score, so they are written out.  The
-// s_nop covers a vector write of akv right before the first broadcast read.
-__device__ __forceinline__ void scale_by_keys(const v16f& s, float akv, float (&u)[16]) {
-  const float s0 = s[0], s1 = s[1], s2 = s[2], s3 = s[3], s4 = s[4], s5 = s[5], s6 = s[6], s7 = s[7];
-  const float s8 = s[8], s9 = s[9], s10 = s[10], s11 = s[11], s12 = s[12], s13 = s[13], s14 = s[14], s15 = s[15];
-  asm("s_nop 1\n\t"
-      "v_mul_f32_dpp %0, %32, %16 row_newbcast:0 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %1, %32, %17 row_newbcast:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %2, %32, %18 row_newbcast:2 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %3, %32, %19 row_newbcast:3 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %4, %32, %20 row_newbcast:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %5, %32, %21 row_newbcast:5 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %6, %32, %22 row_newbcast:6 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %7, %32, %23 row_newbcast:7 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %8, %32, %24 row_newbcast:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %9, %32, %25 row_newbcast:9 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %10, %32, %26 row_newbcast:10 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %11, %32, %27 row_newbcast:11 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %12, %32, %28 row_newbcast:12 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %13, %32, %29 row_newbcast:13 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %14, %32, %30 row_newbcast:14 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %15, %32, %31 row_newbcast:15 row_mask:0xf bank_mask:0xf bound_ctrl:1"
-      : "=&v"(u[0]), "=&v"(u[1]), "=&v"(u[2]), "=&v"(u[3]), "=&v"(u[4]), "=&v"(u[5]), "=&v"(u[6]),
-        "=&v"(u[7]), "=&v"(u[8]), "=&v"(u[9]), "=&v"(u[10]), "=&v"(u[11]), "=&v"(u[12]), "=&v"(u[13]),
-        "=&v"(u[14]), "=&v"(u[15])
-      : "v"(s0), "v"(s1), "v"(s2), "v"(s3), "v"(s4), "v"(s5), "v"(s6), "v"(s7), "v"(s8), "v"(s9), "v"(s10),
-        "v"(s11), "v"(s12), "v"(s13), "v"(s14), "v"(s15), "v"(akv));
+template <int D, int BIAS>
+__device__ __forceinline__ void flash_fetch(const FCtx<D>& c, const FBuf<D, BIAS>& tb, const FPos& kp, int blk,
+                                            FIn& in) {
+  in.akv = flds<float>(tb.ak, c.off_akb + blk * 128);
+  if (BIAS == kBiasRows) {
+    const int woff = flash_win_off(c, kp, blk);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) in.bias[b] = flds<v4f>(tb.win, woff + 32 * b);
+  } else {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) in.bias[b] = v4f{};
+  }
 }
 
+// fp4 key operands of block `blk`, one per 64-channel chunk.
+template <int D, int BIAS>
+__device__ __forceinline__ void flash_kops(const FCtx<D>& c, const FBuf<D, BIAS>& tb, int blk,
+                                           v4i (&kop)[FDims<D>::NCH]) {
+#pragma unroll
+  for (int ch = 0; ch < FDims<D>::NCH; ++ch) kop[ch] = flds<v4i>(tb.k, c.off_k + ch * 2048 + blk * 1024);
+}
 
-// Logits of block `blk` (base 2), then P = exp2(s - offset) as bf16 pairs.
-// EXACT: the running row maximum (mrow) is the offset, with the lazy
-// rescale of the accumulators; otherwise the offset is 0.  mask: keys past
-// N get probability 0 (the ragged last tile; never with table rows).
-template <int D, int BIAS, bool EXACT>
-__device__ __forceinline__ void flash_probs(const FCtx<D>& c, const FBuf<D, BIAS>& tb, const FPos& kp, int blk,
-                                            const v16f& s, bool mask, uint32_t (&pk)[8], FAcc<D>& acc,
-                                            float& mrow) {
+// V^T operands of 16-key step `st` of block `blk` of the tile: per 32-channel
+// block, two transposing reads (slots 0..3 and 4..7 of the lane's half).
+template <int D, int BIAS>
+__device__ __forceinline__ void flash_vops(const FCtx<D>& c, const FBuf<D, BIAS>& tb, int blk, int st,
+                                           FPend<D>& pp) {
+  using F = FDims<D>;
+  const char* vb = reinterpret_cast<const char*>(&tb.v[0]);
+#pragma unroll
+  for (int cb = 0; cb < F::CB; ++cb) {
+    const int base = c.off_v[cb] + (32 * blk + 16 * st) * F::ROW;
+    const v2u lo = tr_read(vb + base);
+    const v2u hi = tr_read(vb + base + 8 * F::ROW);
+    pp.vop[st][cb] = __builtin_bit_cast(v8bf, v4u{lo[0], lo[1], hi[0], hi[1]});
+  }
+}
+
+// Holds the next block's QK result where it is issued.  The DPP multiplies
+// that first read it are inline assembly, which the compiler neither delays
+// after a matrix instruction nor keeps the product away from: the product
+// could otherwise sink to just before them, inside the wait states a matrix
+// result needs before a vector read.  The barrier keeps every instruction
+// after this point after the product.
+__device__ __forceinline__ void flash_qk_anchor(v16f& sn) {
+  asm volatile("" : "+v"(sn));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// u[e] = s[4 b + e] * alpha_k of the key that accumulator register 4 b + e
+// holds, taken by DPP row broadcast from lane 16 row + 4 b + e: one
+// v_mul_f32_dpp per score.  (Left to itself the compiler splits a share of
+// these into a broadcast move and a multiply.)  The s_nop covers a vector
+// write of akv right before the broadcast reads it.
+#define FLASH_DPP4(R0, R1, R2, R3)                                                               \
+  asm("s_nop 1\n\t"                                                                              \
+      "v_mul_f32_dpp %0, %8, %4 row_newbcast:" #R0 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+      "v_mul_f32_dpp %1, %8, %5 row_newbcast:" #R1 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+      "v_mul_f32_dpp %2, %8, %6 row_newbcast:" #R2 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+      "v_mul_f32_dpp %3, %8, %7 row_newbcast:" #R3 " row_mask:0xf bank_mask:0xf bound_ctrl:1"     \
+      : "=&v"(u[0]), "=&v"(u[1]), "=&v"(u[2]), "=&v"(u[3])                                         \
+      : "v"(s0), "v"(s1), "v"(s2), "v"(s3), "v"(akv))
+
+template <int B>
+__device__ __forceinline__ void scale4(const v16f& s, float akv, float (&u)[4]) {
+  const float s0 = s[4 * B], s1 = s[4 * B + 1], s2 = s[4 * B + 2], s3 = s[4 * B + 3];
+  if (B == 0) FLASH_DPP4(0, 1, 2, 3);
+  if (B == 1) FLASH_DPP4(4, 5, 6, 7);
+  if (B == 2) FLASH_DPP4(8, 9, 10, 11);
+  if (B == 3) FLASH_DPP4(12, 13, 14, 15);
+}
+#undef FLASH_DPP4
+
+// The matrix instructions of a block, in issue order: the pending block's
+// first 16-key step (CB P.V products, then its row-sum product), the QK
+// chunks of the next block, the pending block's second step.
+template <int D>
+struct FOrder {
+  static constexpr int CB = FDims<D>::CB, NCH = FDims<D>::NCH;
+  static constexpr int NM = 2 * (CB + 1) + NCH;  // instructions per block
+  static constexpr int QK0 = CB + 1;              // first QK chunk
+  static constexpr int QKL = CB + NCH;            // last QK chunk
+  static constexpr int LASTV0 = CB - 1;           // last product reading step 0's V^T
+  static constexpr int LASTV1 = 2 * CB + NCH;     // last product reading step 1's V^T
+};
+
+template <int D>
+__device__ __forceinline__ void flash_pv(int st, int i, const FCtx<D>& c, const FPend<D>& old, FAcc<D>& acc) {
+  const v4u pw = {old.pk[4 * st], old.pk[4 * st + 1], old.pk[4 * st + 2], old.pk[4 * st + 3]};
+  const v8bf p = __builtin_bit_cast(v8bf, pw);
+  if (i < FDims<D>::CB)
+    acc.o[i] = mfma_bf16_32x32x16(old.vop[st][i], p, acc.o[i]);
+  else
+    acc.l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.ones, p, acc.l, 0, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void flash_mfma(int m, const FCtx<D>& c, const FPend<D>& old, const v4i (&kop)[FDims<D>::NCH],
+                                           v16f& sn, FAcc<D>& acc) {
+  using O = FOrder<D>;
+  if (m < O::QK0) {
+    flash_pv<D>(0, m, c, old, acc);
+  } else if (m <= O::QKL) {
+    const int ch = m - O::QK0;
+    sn = mfma_signs_32x32x64(kop[ch], c.qop[ch], sn);
+    if (m == O::QKL) flash_qk_anchor(sn);
+  } else {
+    flash_pv<D>(1, m - O::QKL - 1, c, old, acc);
+  }
+}
+
+// One block, offset-free softmax.  The pending block's matrix work and the
+// next block's QK are spread over four chunks of vector work (4 scores
+// each), so that no wave issues its matrix instructions back to back and the
+// vector ALU keeps issuing beside them; scheduling barriers hold that order.
+// The QK lands in the third chunk at the latest, so at least two chunks of
+// vector work (28 instructions, more than the 19 wait states a matrix result
+// needs) separate it from its first reader in the next block.  Writes P of
+// this block into nw.pk and its V^T operands into nw.vop, each step's once
+// the pending block's products have consumed the same registers' old values.
+template <int D, int BIAS>
+__device__ __forceinline__ void flash_block_fast(const FCtx<D>& c, const FBuf<D, BIAS>& tb, int blk, const v16f& s,
+                                                 const FIn& in, const v4i (&kop)[FDims<D>::NCH], v16f& sn,
+                                                 const FPend<D>& old, FPend<D>& nw, FAcc<D>& acc, int key0,
+                                                 bool mask) {
+  using O = FOrder<D>;
+  constexpr int NM = O::NM;
+  static_assert(O::QKL < 3 * NM / 4, "the QK must issue before the last chunk");
   const FwdArgs& a = *c.a;
-  int woff = 0;
-  if (BIAS == kBiasRows) woff = flash_win_off(c, kp, blk);
-  const float akv = flds<float>(tb.ak, c.off_akb + blk * 128);
-  float x[16], u[16];
-  scale_by_keys(s, akv, u);
+  sn = v16f{};
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const float u0 = u[4 * b], u1 = u[4 * b + 1], u2 = u[4 * b + 2], u3 = u[4 * b + 3];
-    if (BIAS == kBiasRows) {
-      const v4f bias = flds<v4f>(tb.win, woff + 32 * b);
-      x[4 * b + 0] = fmaf(u0, c.aq, bias.x);
-      x[4 * b + 1] = fmaf(u1, c.aq, bias.y);
-      x[4 * b + 2] = fmaf(u2, c.aq, bias.z);
-      x[4 * b + 3] = fmaf(u3, c.aq, bias.w);
-    } else {
-      x[4 * b + 0] = u0 * c.aq;
-      x[4 * b + 1] = u1 * c.aq;
-      x[4 * b + 2] = u2 * c.aq;
-      x[4 * b + 3] = u3 * c.aq;
+#pragma unroll
+    for (int m = b * NM / 4; m < (b + 1) * NM / 4; ++m) flash_mfma<D>(m, c, old, kop, sn, acc);
+    if (b * NM / 4 <= O::LASTV0 && O::LASTV0 < (b + 1) * NM / 4) flash_vops(c, tb, blk, 0, nw);
+    if (b * NM / 4 <= O::LASTV1 && O::LASTV1 < (b + 1) * NM / 4) flash_vops(c, tb, blk, 1, nw);
+    float u[4];
+    if (b == 0) scale4<0>(s, in.akv, u);
+    if (b == 1) scale4<1>(s, in.akv, u);
+    if (b == 2) scale4<2>(s, in.akv, u);
+    if (b == 3) scale4<3>(s, in.akv, u);
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = BIAS == kBiasRows ? fmaf(u[e], c.aq, in.bias[b][e]) : u[e] * c.aq;
+    if (BIAS != kBiasRows && mask) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (key0 + 8 * b + 4 * c.lh + e >= a.N) x[e] = -INFINITY;
     }
+    nw.pk[2 * b] = pack_bf16x2(fast_exp2(x[0]), fast_exp2(x[1]));
+    nw.pk[2 * b + 1] = pack_bf16x2(fast_exp2(x[2]), fast_exp2(x[3]));
+    // keep this chunk's vector work here: left alone, the compiler sinks it
+    // to the product that uses it, past the barrier and into the next block
+    asm volatile("" : "+v"(nw.pk[2 * b]), "+v"(nw.pk[2 * b + 1]));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One block with the online softmax: the pending block's products and the
+// next block's QK go first (a rescale of the accumulators must cover the
+// products; the QK is then a whole block of vector work ahead of its
+// reader), then the logits, the row maximum (log2 units, mrow) with the lazy
+// rescale and P = exp2(s - mrow).
+template <int D, int BIAS>
+__device__ __forceinline__ void flash_block_exact(const FCtx<D>& c, const FBuf<D, BIAS>& tb, int blk,
+                                                  const v16f& s, const FIn& in,
+                                                  const v4i (&kop)[FDims<D>::NCH], v16f& sn,
+                                                  const FPend<D>& old, FPend<D>& nw, FAcc<D>& acc, int key0,
+                                                  bool mask, float& mrow) {
+  const FwdArgs& a = *c.a;
+  sn = v16f{};
+#pragma unroll
+  for (int m = 0; m < FOrder<D>::NM; ++m) flash_mfma<D>(m, c, old, kop, sn, acc);
+  flash_vops(c, tb, blk, 0, nw);
+  flash_vops(c, tb, blk, 1, nw);
+  float x[16];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    float u[4];
+    if (b == 0) scale4<0>(s, in.akv, u);
+    if (b == 1) scale4<1>(s, in.akv, u);
+    if (b == 2) scale4<2>(s, in.akv, u);
+    if (b == 3) scale4<3>(s, in.akv, u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * b + e] = BIAS == kBiasRows ? fmaf(u[e], c.aq, in.bias[b][e]) : u[e] * c.aq;
   }
   if (BIAS != kBiasRows && mask) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kp.k0 + blk * 32 + 8 * (r >> 2) + 4 * c.lh + (r & 3);
-      if (key >= a.N) x[r] = -INFINITY;
-    }
+    for (int r = 0; r < 16; ++r)
+      if (key0 + 8 * (r >> 2) + 4 * c.lh + (r & 3) >= a.N) x[r] = -INFINITY;
   }
-  if (EXACT) {
-    float mt = x[0];
+  float mt = x[0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
-    mt = max_halves(mt);
-    const float mnew = fmaxf(mrow, mt);
-    if (__any(mnew > mrow + 8.0f)) {
-      const float f = fast_exp2(mrow - mnew);
+  for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
+  mt = max_halves(mt);
+  const float mnew = fmaxf(mrow, mt);
+  if (__any(mnew > mrow + 8.0f)) {
+    const float f = fast_exp2(mrow - mnew);
 #pragma unroll
-      for (int cb = 0; cb < FDims<D>::CB; ++cb) acc.o[cb] *= f;
-      acc.l *= f;
-      mrow = mnew;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] -= mrow;
+    for (int cb = 0; cb < FDims<D>::CB; ++cb) acc.o[cb] *= f;
+    acc.l *= f;
+    mrow = mnew;
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) pk[j] = pack_bf16x2(fast_exp2(x[2 * j]), fast_exp2(x[2 * j + 1]));
+  for (int j = 0; j < 8; ++j) nw.pk[j] = pack_bf16x2(fast_exp2(x[2 * j] - mrow), fast_exp2(x[2 * j + 1] - mrow));
+}
+
+template <int D, int BIAS, bool EXACT>
+__device__ __forceinline__ void flash_block(const FCtx<D>& c, const FBuf<D, BIAS>& tb, int blk, const v16f& s,
+                                            const FIn& in, const v4i (&kop)[FDims<D>::NCH], v16f& sn,
+                                            const FPend<D>& old, FPend<D>& nw, FAcc<D>& acc, int key0, bool mask,
+                                            float& mrow) {
+  if (EXACT)
+    flash_block_exact<D, BIAS>(c, tb, blk, s, in, kop, sn, old, nw, acc, key0, mask, mrow);
+  else
+    flash_block_fast<D, BIAS>(c, tb, blk, s, in, kop, sn, old, nw, acc, key0, mask);
 }
 
 // Wave priority over the last three eighths of the keys (see the host's
@@ -486,31 +582,23 @@ __device__ __forceinline__ void flash_priority(const FwdArgs& a, int t, int nkt)
     __builtin_amdgcn_s_setprio(0);
 }
 
-// Keeps `pk` computed here: without it the compiler sinks the vector work
-// of a block towards the product that uses it, past the barrier, and splits
-// the key-scale broadcasts from the multiplies they should fold into.
-__device__ __forceinline__ void flash_pin(uint32_t (&pk)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(pk[j]));
-}
-
 // One key tile: block 0, the barrier, the copies of tile t+2, block 1.
-// s0 holds the QK of this tile's block 0 on entry; block 1's goes to s1
-// while block 0 is worked on, and the next tile's block 0 back into s0.
+// On entry s0 / in0 hold the QK and the LDS inputs of this tile's block 0
+// and ppa the pending block; on exit the same for the next tile.  Block 1's
+// QK and inputs go through s1 / in1, its pending block through ppb.
 template <int D, int BIAS, bool EXACT>
 __device__ __forceinline__ void flash_tile(const FCtx<D>& c, const FBuf<D, BIAS>& cur, const FBuf<D, BIAS>& nxt,
-                                           FBuf<D, BIAS>& far, int t, int nkt, v16f& s0, v16f& s1,
-                                           FPend<D>& pp, FAcc<D>& acc, float& mrow) {
+                                           FBuf<D, BIAS>& far, int t, int nkt, v16f& s0, v16f& s1, FIn& in0,
+                                           FIn& in1, FPend<D>& ppa, FPend<D>& ppb, FAcc<D>& acc, float& mrow) {
   const FwdArgs& a = *c.a;
   const FPos kp = flash_pos<BIAS>(a, t);
   const int k0 = kp.k0;
   const bool has1 = k0 + 32 < a.N;
-  // block 0
-  if (has1) s1 = flash_qk(c, cur, 1);
-  flash_pv(c, pp, acc);
-  flash_probs<D, BIAS, EXACT>(c, cur, kp, 0, s0, k0 + 32 > a.N, pp.pk, acc, mrow);
-  flash_pin(pp.pk);
-  flash_vops(c, cur, 0, pp);
+  v4i kop[FDims<D>::NCH];
+  // block 0: the next block is this tile's block 1
+  flash_kops(c, cur, 1, kop);
+  flash_fetch(c, cur, kp, 1, in1);
+  flash_block<D, BIAS, EXACT>(c, cur, 0, s0, in0, kop, s1, ppa, ppb, acc, k0, k0 + 32 > a.N, mrow);
   // tile t+1 is in `nxt` once every wave's copies have landed; every wave is
   // done with tile t-1, whose buffer `far` takes tile t+2
   __builtin_amdgcn_s_waitcnt(0);
@@ -518,11 +606,13 @@ __device__ __forceinline__ void flash_tile(const FCtx<D>& c, const FBuf<D, BIAS>
   if (t + 2 < nkt) flash_copy(c, far, t + 2);
   flash_priority(a, t, nkt);
   if (has1) {
-    if (t + 1 < nkt) s0 = flash_qk(c, nxt, 0);
-    flash_pv(c, pp, acc);
-    flash_probs<D, BIAS, EXACT>(c, cur, kp, 1, s1, k0 + 64 > a.N, pp.pk, acc, mrow);
-    flash_pin(pp.pk);
-    flash_vops(c, cur, 1, pp);
+    // block 1: the next block is tile t+1's block 0
+    const FPos kn = flash_pos<BIAS>(a, t + 1);
+    flash_kops(c, nxt, 0, kop);
+    flash_fetch(c, nxt, kn, 0, in0);
+    flash_block<D, BIAS, EXACT>(c, cur, 1, s1, in1, kop, s0, ppb, ppa, acc, k0 + 32, k0 + 64 > a.N, mrow);
+  } else {
+    ppa = ppb;  // the last tile ends after block 0
   }
 }
 
@@ -540,23 +630,40 @@ __device__ __forceinline__ float flash_pass(const FCtx<D>& c, FBuf<D, BIAS>& b0,
   if (nkt > 1) flash_copy(c, b1, 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  v16f s0 = flash_qk(c, b0, 0), s1 = v16f{};
-  // nothing is pending before the first block: P = 0
-  FPend<D> pp;
+  v16f s0, s1 = v16f{};
+  {
+    v4i kop[FDims<D>::NCH];
+    flash_kops(c, b0, 0, kop);
+    s0 = v16f{};
 #pragma unroll
-  for (int j = 0; j < 8; ++j) pp.pk[j] = 0u;
+    for (int ch = 0; ch < FDims<D>::NCH; ++ch) s0 = mfma_signs_32x32x64(kop[ch], c.qop[ch], s0);
+    // the first block reads s0 in inline assembly: wait out the matrix
+    // result's 19 wait states here, once
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  FIn in0, in1;
+  flash_fetch(c, b0, flash_pos<BIAS>(a, 0), 0, in0);
+  // nothing is pending before the first block: P = 0
+  FPend<D> ppa, ppb;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ppa.pk[j] = 0u;
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
-    for (int cb = 0; cb < FDims<D>::CB; ++cb) pp.vop[st][cb] = v8bf{};
+    for (int cb = 0; cb < FDims<D>::CB; ++cb) ppa.vop[st][cb] = v8bf{};
   for (int t = 0; t < nkt; t += 3) {
-    flash_tile<D, BIAS, EXACT>(c, b0, b1, b2, t, nkt, s0, s1, pp, acc, mrow);
+    flash_tile<D, BIAS, EXACT>(c, b0, b1, b2, t, nkt, s0, s1, in0, in1, ppa, ppb, acc, mrow);
     if (t + 1 >= nkt) break;
-    flash_tile<D, BIAS, EXACT>(c, b1, b2, b0, t + 1, nkt, s0, s1, pp, acc, mrow);
+    flash_tile<D, BIAS, EXACT>(c, b1, b2, b0, t + 1, nkt, s0, s1, in0, in1, ppa, ppb, acc, mrow);
     if (t + 2 >= nkt) break;
-    flash_tile<D, BIAS, EXACT>(c, b2, b0, b1, t + 2, nkt, s0, s1, pp, acc, mrow);
+    flash_tile<D, BIAS, EXACT>(c, b2, b0, b1, t + 2, nkt, s0, s1, in0, in1, ppa, ppb, acc, mrow);
   }
-  flash_pv(c, pp, acc);
+  // drain: the last block's P.V and row sums
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int i = 0; i <= FDims<D>::CB; ++i) flash_pv<D>(st, i, c, ppa, acc);
   return mrow;
 }
 
