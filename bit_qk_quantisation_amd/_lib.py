@@ -14,6 +14,7 @@ EXPORTS = (
     "ba_attention_fwd_dense_bias", "ba_attention_fwd_dense_bias_prepared", "ba_attention_prepare",
     "ba_workspace_bytes_int8pv", "ba_attention_fwd_int8pv", "ba_workspace_bytes_bwd", "ba_attention_bwd",
     "ba_attention_fwd_prepared", "ba_qk_int_dot", "ba_attention_fwd_train", "ba_attention_bwd_saved",
+    "ba_attention_fwd_static",
 )
 
 STATUS = {0: "BA_OK", 1: "BA_ERR_NULL", 2: "BA_ERR_SHAPE", 3: "BA_ERR_UNSUPPORTED",
@@ -90,6 +91,8 @@ def load(path=None) -> ctypes.CDLL:
     lib.ba_attention_fwd_prepared.restype = i32
     lib.ba_attention_fwd_prepared.argtypes = [vp, vp, i32, i32, i64, i64, i64, i32, ctypes.c_float,
                                               vp, vp, sz, vp]
+    lib.ba_attention_fwd_static.restype = i32
+    lib.ba_attention_fwd_static.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, ctypes.c_float, vp, vp]
     lib.ba_qk_int_dot.restype = i32
     lib.ba_qk_int_dot.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp, vp]
     if path is None:

@@ -739,6 +739,9 @@ ba_status ba_attention_fwd_strided(const void* q, const void* k, const void* v,
   return run_forward(q, k, v, bias, gh, gw, B, H, N, d, scale, o, strides, nullptr, workspace, ws_bytes, stream);
 }
 
+ba_status ba_attention_fwd_static(const void* q, const void* k, const void* v, const void* bias, int gh, int gw,
+                                  int64_t B, int64_t H, int64_t N, int d, float scale, void* o, void* stream);
+
 ba_status ba_attention_fwd_dense_bias(const void* q, const void* k, const void* v,
                                       const void* bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_ld,
                                       int64_t B, int64_t H, int64_t N, int d, float scale,
@@ -1000,6 +1003,70 @@ ba_status ba_qk_int_dot(const uint32_t* qbits, const uint32_t* kbits, int64_t B,
   const int err = ba::launch_qk_dot(a, route, stream);
   if (err != 0) return hip_fail(err, "qk_int_dot launch");
   return BA_OK;
+}
+
+}  // extern "C"
+
+// ---- the forward that allocates nothing ------------------------------------
+// ba_attention_fwd_static runs ba_attention_fwd on a workspace the library
+// keeps in device memory of its own: this array, one copy per device, which
+// the runtime places when it loads the library's code on that device and
+// keeps until the process ends.  Host code never passes the array's name to
+// a kernel (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, looked up once per device on the
+// first call there.
+
+namespace {
+constexpr size_t kStaticScratchBytes = size_t{BA_STATIC_SCRATCH_MIB} << 20;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+// The device address of `scratch` on the current device.
+ba_status static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(BA_ERR_HIP, "no current HIP device (or more than 64 devices)");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(static_cast<int>(e), "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(BA_ERR_HIP, "hipGetSymbolAddress(scratch) gave no address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ba_status ba_attention_fwd_static(const void* q, const void* k, const void* v, const void* bias, int gh, int gw,
+                                  int64_t B, int64_t H, int64_t N, int d, float scale, void* o, void* stream) {
+  ba_status st = check_dims(B, H, N, d);
+  if (st != BA_OK) return st;
+  const bool has_bias = bias != nullptr;
+  if (has_bias && (gh < 1 || gw < 1 || static_cast<int64_t>(gh) * gw != N))
+    return fail(BA_ERR_SHAPE, "with a bias table gh*gw must equal N (gh=%d gw=%d N=%lld)", gh, gw, (long long)N);
+  const Layout L = layout(B, H, N, d, has_bias, has_bias ? gh : 0, has_bias ? gw : 0, false, true);
+  if (L.mode < 0)
+    return fail(BA_ERR_UNSUPPORTED, "bias grid %dx%d: the table rows do not fit the tile window and the table "
+                "exceeds 48 KiB", gh, gw);
+  if (static_cast<size_t>(L.total) > kStaticScratchBytes)
+    return fail(BA_ERR_WORKSPACE, "the problem needs %lld bytes of scratch; ba_attention_fwd_static keeps %zu "
+                "(use ba_attention_fwd with a workspace)", (long long)L.total, kStaticScratchBytes);
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != BA_OK) return st;
+  return run_forward(q, k, v, bias, has_bias ? gh : 0, has_bias ? gw : 0, B, H, N, d, scale, o, nullptr, nullptr,
+                     ws, kStaticScratchBytes, stream, nullptr, true);
 }
 
 }  // extern "C"

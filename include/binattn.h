@@ -20,9 +20,11 @@
  *   W = ceil(d/32).  Scales are float32 [B, H, N].
  * - All pointers are device pointers (hipMalloc'ed or equivalent) aligned to
  *   16 bytes.  The caller owns every buffer.  The library allocates no device
- *   memory, frees nothing and does not synchronise, with one stated
- *   exception: ba_attention_bwd creates one side stream and two events per
- *   device on its first call there (see that entry).
+ *   memory at run time, frees nothing and does not synchronise, with two
+ *   stated exceptions: ba_attention_bwd creates one side stream and two
+ *   events per device on its first call there (see that entry), and
+ *   ba_attention_fwd_static uses a fixed scratch array the library's code
+ *   object carries (see that entry).
  * - stream is a hipStream_t passed as void*; NULL means the default stream.
  *   All work is enqueued on it, and the call returns before it completes.
  *   Buffers must stay valid until the stream has passed the work.
@@ -52,6 +54,9 @@ extern "C" {
 #endif
 
 #define BA_VERSION 1
+
+/* Size of the per-device scratch of ba_attention_fwd_static, in MiB. */
+#define BA_STATIC_SCRATCH_MIB 64
 
 typedef enum ba_status {
   BA_OK = 0,
@@ -263,6 +268,30 @@ ba_status ba_attention_fwd_dense_bias_prepared(const void* q, const void* bias,
                                                float scale, void* o,
                                                const void* workspace, size_t ws_bytes,
                                                void* stream);
+
+/* ba_attention_fwd_static -- ba_attention_fwd for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid device allocation.  It takes no workspace: the library keeps
+ * one scratch array of BA_STATIC_SCRATCH_MIB MiB in device memory of each
+ * GPU it runs on (placed when the library's code is loaded there, held
+ * until the process ends) and runs ba_attention_fwd on it.  Nothing is
+ * allocated or freed by the call; its device address is looked up once per
+ * device, on the first call there, with the device current.
+ *   q, k, v, bias, gh, gw, B, H, N, d, scale, o, stream: as ba_attention_fwd
+ *   (contiguous [B,H,N,d] tensors).
+ * The scratch holds the K signs and scales and the bias rows (no V^T where
+ * the pipelined kernel runs), at most BA_STATIC_SCRATCH_MIB MiB: larger
+ * problems get BA_ERR_WORKSPACE before anything is enqueued.  Every call on
+ * one GPU shares that GPU's scratch, so calls that may overlap on one GPU
+ * (two streams, two host threads) race on it; calls in one stream do not.
+ * Nothing in the scratch needs to start at zero.  O is bit for bit
+ * ba_attention_fwd's.  Errors: as ba_attention_fwd, with BA_ERR_WORKSPACE
+ * for problems beyond the scratch and BA_ERR_HIP if the address lookup
+ * fails. */
+ba_status ba_attention_fwd_static(const void* q, const void* k, const void* v,
+                                  const void* bias, int gh, int gw,
+                                  int64_t B, int64_t H, int64_t N, int d, float scale,
+                                  void* o, void* stream);
 
 /* Workspace bytes of ba_attention_bwd (0 for sizes it rejects; d must be
  * 32, 64 or 128). */

@@ -421,3 +421,19 @@ def test_default_workspace_per_stream():
     c = ws.get(cpu, 5000, stream=111)
     assert c.numel() >= 5000 and ws.get(cpu, 1000, stream=222).data_ptr() == b.data_ptr()
 
+
+def test_static_forward_validation(lib):
+    """ba_attention_fwd_static refuses, before any HIP call, what
+    ba_attention_fwd refuses, and problems beyond its scratch array."""
+    def call(**kw):
+        a = dict(q=A, k=A + GB, v=A + 2 * GB, bias=None, gh=0, gw=0, B=1, H=2, N=64, d=64, scale=0.125,
+                 o=A + 3 * GB)
+        a.update(kw)
+        return lib.ba_attention_fwd_static(a["q"], a["k"], a["v"], a["bias"], a["gh"], a["gw"], a["B"], a["H"],
+                                           a["N"], a["d"], a["scale"], a["o"], None)
+    assert call(d=72 + 4) == 3
+    assert call(N=0) == 2
+    assert call(bias=A + 5 * GB, gh=4, gw=15) == 2
+    assert call(B=64, H=16, N=16384, d=128) == 5          # needs more than BA_STATIC_SCRATCH_MIB
+    assert b"scratch" in lib.ba_last_error()
+    assert call(bias=A + 5 * GB, gh=100, gw=70, N=7000) == 3
