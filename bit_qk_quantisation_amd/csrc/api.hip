@@ -536,11 +536,6 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   f.gw = gw;
   f.Lpad = static_cast<int>(L.Lpad);
   f.win_rows = (mode == ba::kBiasRows) ? window_rows(N, gw) : 0;
-  f.gw32_magic = 0;  // gw == 32: the block index is the grid row
-  if (mode == ba::kBiasRows && gw > 32) {
-    const uint64_t g32 = static_cast<uint64_t>(gw / 32);
-    f.gw32_magic = static_cast<uint32_t>(((uint64_t{1} << 32) + g32 - 1) / g32);
-  }
   f.qscale = dense ? scale : scale * ba::kLog2e;  // dense logits stay in natural units
   f.nqt = static_cast<int>(L.Npad / ba::kBM);
   const int64_t nwg = BH * f.nqt;

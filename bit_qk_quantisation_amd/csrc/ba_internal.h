@@ -209,9 +209,6 @@ struct FwdArgs {
   int table_flip;          // kBiasTable: read the table flipped in both axes
   int prio_balance;        // 1: lower the wave priority over the last keys
                            // (every workgroup of the grid is resident at once)
-  uint32_t gw32_magic;     // table rows: ceil(2^32 / (gw / 32)), so that key
-                           // block b starts on grid row umulhi(b, magic);
-                           // 0 when gw == 32 (the row is b)
 };
 
 // LDS bytes of the fused kernel: the bias table (table mode, dynamic) and

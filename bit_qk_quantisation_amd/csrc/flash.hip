@@ -109,33 +109,19 @@ struct FCtx {
   int win_bytes;
 };
 
-// Grid position of the keys of a tile (table rows: gw % 32 == 0, so a
-// 32-key block never straddles a grid row).  Key block bi starts at row
-// bi / (gw / 32), column 32 (bi % (gw / 32)); the division is a
-// multiplication by the host's ceil(2^32 / (gw / 32)), or none when
-// gw == 32 (magic 0).
-struct FPos {
-  int k0;
-  int ky[2], kx[2];  // grid row and column of the first key of each block
+// The tile the copies fetch next: its first key and (table rows) the grid
+// row and column of its first 32-key block.  gw % 32 == 0, so a block never
+// straddles a grid row and the next block starts 32 columns on, or at
+// column 0 of the next row.  Every field is wave-uniform.
+struct FRun {
+  int k0, by, bx;
 };
 
-template <int BIAS>
-__device__ __forceinline__ FPos flash_pos(const FwdArgs& a, int t) {
-  FPos p;
-  p.k0 = t * kBN;
-  p.ky[0] = p.ky[1] = p.kx[0] = p.kx[1] = 0;
-  if (BIAS == kBiasRows) {
-    const uint32_t g32 = static_cast<uint32_t>(a.gw) >> 5;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const uint32_t bi = static_cast<uint32_t>(2 * t + blk);
-      const uint32_t y = a.gw32_magic != 0 ? __umulhi(bi, a.gw32_magic) : bi;
-      p.ky[blk] = static_cast<int>(y);
-      p.kx[blk] = static_cast<int>(32 * (bi - y * g32));
-    }
-  }
-  return p;
-}
+// Left by the copy of a tile for the reads from its buffer: the uniform part
+// of the bias-window offset of each of its two blocks.
+struct FWin {
+  int u[2];
+};
 
 template <typename T>
 __device__ __forceinline__ T flds(const void* base, int byte_off) {
@@ -295,41 +281,55 @@ __device__ __forceinline__ float flash_setup(FCtx<D>& c, const FwdArgs& a, float
 }
 
 // ---------------------------------------------------------------- copies --
-// Starts the copies of key tile t (first key kp.k0) into `tb`; lane l of a
-// wave fills bytes [16 l, 16 l + 16) of a 1 KiB piece (4 bytes of the key
-// scales).
+// Starts the copies of the tile `run` names into `tb`, records its window
+// offsets in `w` and advances `run` to the next tile.  Lane l of a wave
+// fills bytes [16 l, 16 l + 16) of a 1 KiB piece (4 bytes of the key
+// scales).  Every source offset is uniform; the per-wave piece choices are
+// uniform branches.
 template <int D, int BIAS>
-__device__ __forceinline__ void flash_copy(const FCtx<D>& c, FBuf<D, BIAS>& tb, int t) {
+__device__ __forceinline__ void flash_copy(const FCtx<D>& c, FBuf<D, BIAS>& tb, FRun& run, FWin& w) {
   using F = FDims<D>;
   const FwdArgs& a = *c.a;
-  const FPos kp = flash_pos<BIAS>(a, __builtin_amdgcn_readfirstlane(t));
+  const uint32_t k0 = static_cast<uint32_t>(run.k0);
   char* kdst = reinterpret_cast<char*>(&tb.k[0]);
 #pragma unroll
   for (int j = 0; j < (2 * F::NCH + 3) / 4; ++j)
     if (c.wave + 4 * j < 2 * F::NCH)
       dma16(c.krs, kdst + (c.wave + 4 * j) * 1024, static_cast<uint32_t>(c.lane * 16),
-            __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kp.k0 / kBN * F::KBYTES + (c.wave + 4 * j) * 1024)));
+            k0 / kBN * F::KBYTES + static_cast<uint32_t>((c.wave + 4 * j) * 1024));
   char* vdst = reinterpret_cast<char*>(&tb.v[0]);
 #pragma unroll
   for (int j = 0; j < (F::VPIECES + 3) / 4; ++j) {
     const int p = c.wave + 4 * j;
-    if (p < F::VPIECES)
-      dma16(c.vrs, vdst + p * 1024, c.voff,
-            __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kp.k0 + p * F::RPP) * c.vsn));
+    if (p < F::VPIECES) dma16(c.vrs, vdst + p * 1024, c.voff, (k0 + static_cast<uint32_t>(p * F::RPP)) * c.vsn);
   }
-  if (c.wave == 0)
-    dma4(c.ars, &tb.ak[0], static_cast<uint32_t>(c.lane * 4),
-         __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kp.k0 * 4)));
+  if (c.wave == 3) dma4(c.ars, &tb.ak[0], static_cast<uint32_t>(c.lane * 4), k0 * 4);
+  run.k0 += kBN;
   if (BIAS == kBiasRows) {
+    int ky[2], kx[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      ky[blk] = run.by;
+      kx[blk] = run.bx;
+      run.bx += 32;
+      if (run.bx == a.gw) {
+        run.bx = 0;
+        run.by += 1;
+      }
+    }
     // window rows start at dy = yq_lo - yk_hi; yk_hi is the row of block 1
-    const int dy0 = c.yq_lo - kp.ky[1] + a.gh - 1 + kBiasPadRows;
-    const uint32_t bs = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(dy0 * 16 * a.Lpad));
+    const int dy0 = c.yq_lo - ky[1] + a.gh - 1 + kBiasPadRows;
+    const uint32_t bs = static_cast<uint32_t>(dy0 * 16 * a.Lpad);
     const uint32_t loff = static_cast<uint32_t>(c.wave * 1024 + c.lane * 16);
     char* bdst = reinterpret_cast<char*>(&tb.win[0]);
 #pragma unroll
     for (int j = 0; j < (F::WIN * 4 + 4095) / 4096; ++j)
       if (static_cast<int>(loff) + 4096 * j < c.win_bytes)
         dma16(c.brs, bdst + (c.wave + 4 * j) * 1024, loff + 4096 * j, bs);
+    w.u[0] = (ky[1] - ky[0]) * 16 * a.Lpad + kx[0] * 4;
+    w.u[1] = kx[1] * 4;
+  } else {
+    w.u[0] = w.u[1] = 0;
   }
 }
 
@@ -340,20 +340,13 @@ struct FIn {
   v4f bias[4];   // table rows: the lane's 16 bias values (0 without a table)
 };
 
-template <int D>
-__device__ __forceinline__ int flash_win_off(const FCtx<D>& c, const FPos& kp, int blk) {
-  const int u = __builtin_amdgcn_readfirstlane((kp.ky[1] - kp.ky[blk]) * 16 * c.a->Lpad + kp.kx[blk] * 4);
-  int off = c.off_win + u;
-  asm("" : "+v"(off));
-  return off;
-}
-
 template <int D, int BIAS>
-__device__ __forceinline__ void flash_fetch(const FCtx<D>& c, const FBuf<D, BIAS>& tb, const FPos& kp, int blk,
+__device__ __forceinline__ void flash_fetch(const FCtx<D>& c, const FBuf<D, BIAS>& tb, const FWin& w, int blk,
                                             FIn& in) {
   in.akv = flds<float>(tb.ak, c.off_akb + blk * 128);
   if (BIAS == kBiasRows) {
-    const int woff = flash_win_off(c, kp, blk);
+    int woff = c.off_win + w.u[blk];
+    asm("" : "+v"(woff));  // one vector add here, the window reads take immediate offsets
 #pragma unroll
     for (int b = 0; b < 4; ++b) in.bias[b] = flds<v4f>(tb.win, woff + 32 * b);
   } else {
@@ -566,50 +559,60 @@ __device__ __forceinline__ void flash_block(const FCtx<D>& c, const FBuf<D, BIAS
     flash_block_fast<D, BIAS>(c, tb, blk, s, in, kop, sn, old, nw, acc, key0, mask);
 }
 
-// Wave priority over the last three eighths of the keys (see the host's
-// prio_balance): equal-priority waves issue oldest first, so without this the
-// first workgroup of a CU finishes long before the last one.
-__device__ __forceinline__ void flash_priority(const FwdArgs& a, int t, int nkt) {
-  if (!a.prio_balance) return;
-  const int e = (8 * t) / nkt;
-  if (e <= 4)
-    __builtin_amdgcn_s_setprio(3);
-  else if (e == 5)
-    __builtin_amdgcn_s_setprio(2);
-  else if (e == 6)
-    __builtin_amdgcn_s_setprio(1);
-  else
-    __builtin_amdgcn_s_setprio(0);
+// Wave priority (when the host sets prio_balance: every workgroup of the
+// grid is resident at once).  Equal-priority waves issue oldest first, so
+// left alone the first workgroup of a CU finishes long before the last one;
+// instead the priority steps down from 3 to 0 at 5/8, 6/8 and 7/8 of the key
+// tiles, so that waves that get there first yield to the others.  The
+// thresholds th[] are tile indices; the step is taken on the tile that
+// reaches one.
+struct FPrio {
+  int th[3];  // first tile of priority 2, 1, 0 (past the last tile: never)
+  int level;
+};
+
+__device__ __forceinline__ void flash_priority(FPrio& p, int t) {
+  const int want = t >= p.th[2] ? 0 : (t >= p.th[1] ? 1 : (t >= p.th[0] ? 2 : 3));
+  if (__builtin_expect(want != p.level, 0)) {
+    p.level = want;
+    if (want == 2)
+      __builtin_amdgcn_s_setprio(2);
+    else if (want == 1)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
+  }
 }
 
-// One key tile: block 0, the barrier, the copies of tile t+2, block 1.
-// On entry s0 / in0 hold the QK and the LDS inputs of this tile's block 0
-// and ppa the pending block; on exit the same for the next tile.  Block 1's
-// QK and inputs go through s1 / in1, its pending block through ppb.
+// One key tile: block 0, the barrier, the copies of the tile `run` names
+// (t+2), block 1.  On entry s0 / in0 hold the QK and the LDS inputs of this
+// tile's block 0 and ppa the pending block; on exit the same for the next
+// tile.  Block 1's QK and inputs go through s1 / in1, its pending block
+// through ppb.  wc, wn, wf: the window offsets of the tiles in cur, nxt and
+// far.
 template <int D, int BIAS, bool EXACT>
 __device__ __forceinline__ void flash_tile(const FCtx<D>& c, const FBuf<D, BIAS>& cur, const FBuf<D, BIAS>& nxt,
-                                           FBuf<D, BIAS>& far, int t, int nkt, v16f& s0, v16f& s1, FIn& in0,
-                                           FIn& in1, FPend<D>& ppa, FPend<D>& ppb, FAcc<D>& acc, float& mrow) {
+                                           FBuf<D, BIAS>& far, const FWin& wc, const FWin& wn, FWin& wf, FRun& run,
+                                           FPrio& prio, int t, int nkt, v16f& s0, v16f& s1, FIn& in0, FIn& in1,
+                                           FPend<D>& ppa, FPend<D>& ppb, FAcc<D>& acc, float& mrow) {
   const FwdArgs& a = *c.a;
-  const FPos kp = flash_pos<BIAS>(a, t);
-  const int k0 = kp.k0;
+  const int k0 = t * kBN;
   const bool has1 = k0 + 32 < a.N;
   v4i kop[FDims<D>::NCH];
   // block 0: the next block is this tile's block 1
   flash_kops(c, cur, 1, kop);
-  flash_fetch(c, cur, kp, 1, in1);
+  flash_fetch(c, cur, wc, 1, in1);
   flash_block<D, BIAS, EXACT>(c, cur, 0, s0, in0, kop, s1, ppa, ppb, acc, k0, k0 + 32 > a.N, mrow);
   // tile t+1 is in `nxt` once every wave's copies have landed; every wave is
   // done with tile t-1, whose buffer `far` takes tile t+2
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (t + 2 < nkt) flash_copy(c, far, t + 2);
-  flash_priority(a, t, nkt);
-  if (has1) {
+  if (t + 2 < nkt) flash_copy(c, far, run, wf);
+  flash_priority(prio, t);
+  if (__builtin_expect(has1, 1)) {
     // block 1: the next block is tile t+1's block 0
-    const FPos kn = flash_pos<BIAS>(a, t + 1);
     flash_kops(c, nxt, 0, kop);
-    flash_fetch(c, nxt, kn, 0, in0);
+    flash_fetch(c, nxt, wn, 0, in0);
     flash_block<D, BIAS, EXACT>(c, cur, 1, s1, in1, kop, s0, ppb, ppa, acc, k0 + 32, k0 + 64 > a.N, mrow);
   } else {
     ppa = ppb;  // the last tile ends after block 0
@@ -626,8 +629,21 @@ __device__ __forceinline__ float flash_pass(const FCtx<D>& c, FBuf<D, BIAS>& b0,
   acc.l = v4f{};
   float mrow = EXACT ? -INFINITY : 0.0f;
   const int nkt = (a.N + kBN - 1) / kBN;
-  flash_copy(c, b0, 0);
-  if (nkt > 1) flash_copy(c, b1, 1);
+  FPrio prio;
+  prio.level = 3;
+  for (int i = 0; i < 3; ++i) prio.th[i] = a.prio_balance ? ((5 + i) * nkt + 7) / 8 : nkt;
+  if (a.prio_balance) __builtin_amdgcn_s_setprio(3);
+  FRun run;
+  run.k0 = 0;
+  run.by = 0;
+  run.bx = 0;
+  FWin w0, w1, w2;
+  w2.u[0] = w2.u[1] = 0;
+  flash_copy(c, b0, run, w0);
+  if (nkt > 1)
+    flash_copy(c, b1, run, w1);
+  else
+    w1 = w2;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   v16f s0, s1 = v16f{};
@@ -643,7 +659,7 @@ __device__ __forceinline__ float flash_pass(const FCtx<D>& c, FBuf<D, BIAS>& b0,
     __builtin_amdgcn_sched_barrier(0);
   }
   FIn in0, in1;
-  flash_fetch(c, b0, flash_pos<BIAS>(a, 0), 0, in0);
+  flash_fetch(c, b0, w0, 0, in0);
   // nothing is pending before the first block: P = 0
   FPend<D> ppa, ppb;
 #pragma unroll
@@ -653,11 +669,13 @@ __device__ __forceinline__ float flash_pass(const FCtx<D>& c, FBuf<D, BIAS>& b0,
 #pragma unroll
     for (int cb = 0; cb < FDims<D>::CB; ++cb) ppa.vop[st][cb] = v8bf{};
   for (int t = 0; t < nkt; t += 3) {
-    flash_tile<D, BIAS, EXACT>(c, b0, b1, b2, t, nkt, s0, s1, in0, in1, ppa, ppb, acc, mrow);
+    flash_tile<D, BIAS, EXACT>(c, b0, b1, b2, w0, w1, w2, run, prio, t, nkt, s0, s1, in0, in1, ppa, ppb, acc, mrow);
     if (t + 1 >= nkt) break;
-    flash_tile<D, BIAS, EXACT>(c, b1, b2, b0, t + 1, nkt, s0, s1, in0, in1, ppa, ppb, acc, mrow);
+    flash_tile<D, BIAS, EXACT>(c, b1, b2, b0, w1, w2, w0, run, prio, t + 1, nkt, s0, s1, in0, in1, ppa, ppb, acc,
+                               mrow);
     if (t + 2 >= nkt) break;
-    flash_tile<D, BIAS, EXACT>(c, b2, b0, b1, t + 2, nkt, s0, s1, in0, in1, ppa, ppb, acc, mrow);
+    flash_tile<D, BIAS, EXACT>(c, b2, b0, b1, w2, w0, w1, run, prio, t + 2, nkt, s0, s1, in0, in1, ppa, ppb, acc,
+                               mrow);
   }
   // drain: the last block's P.V and row sums
 #pragma unroll
