@@ -84,7 +84,7 @@ int choose_mode(bool has_bias, int gh, int gw, int64_t N) {
 // Byte offsets of the workspace sections of ba_attention_fwd.
 struct Layout {
   int64_t Npad, W, dpad, Lpad;
-  int64_t kop, alpha_k, kmax, vt, vq, vpart, vscale, vcsum, bias4, rowmax, vnat, total;
+  int64_t kop, alpha_k, kmax, vt, vq, vpart, vscale, vcsum, bias4, rowmax, vnat, aks, total;
   int mode;
   bool flash_prepared;  // the prepared forward runs the pipelined kernel on vnat
   bool no_vt;           // compact layout without V^T: only the pipelined kernel can run on it
@@ -138,6 +138,10 @@ Layout layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int
   // the values' natural rows, for the prepared forward's pipelined kernel
   L.flash_prepared = !int8pv && !compact && L.mode >= 0 && prepared_flash(N, d, L.mode, gw);
   L.vnat = take(L.flash_prepared ? BH * L.Npad * d * 2 : 0);
+  // the pipelined kernel's key-scale operands (12 bytes per key)
+  const bool flash_shape = !int8pv && L.mode >= 0 &&
+                           ba::flash_supported(d, L.mode, rows0 ? window_rows(N, gw) : 0, static_cast<int>(L.Lpad));
+  L.aks = take(flash_shape ? BH * L.Npad * 12 : 0);
   L.total = off;
   return L;
 }
@@ -556,6 +560,8 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
   if (L.no_vt && !flash)
     return fail(BA_ERR_UNSUPPORTED, "the value rows span 2 GiB or more: this entry point cannot run the problem");
   uint16_t* vnat = reinterpret_cast<uint16_t*>(ws + L.vnat);
+  uint32_t* aks = reinterpret_cast<uint32_t*>(ws + L.aks);
+  f.aks = aks;
   if (flash) {
     if (whole) {
       f.v = static_cast<const uint16_t*>(v);
@@ -584,7 +590,8 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
                    flash ? nullptr : const_cast<uint16_t*>(f.vt),
                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                    (preparing && L.flash_prepared) ? vnat : nullptr,
-                   vs[1], vs[2], BH, static_cast<int>(H), f.N, f.Npad, d, f.W, (f.W + 1) / 2, f.dpad};
+                   vs[1], vs[2], BH, static_cast<int>(H), f.N, f.Npad, d, f.W, (f.W + 1) / 2, f.dpad,
+                   (flash || (preparing && L.flash_prepared)) ? aks : nullptr};
   p.kv_blocks = BH * (L.Npad / ba::kPackTok);
   p.lds = ba::prologue_lds(d, true);
   // the 8-bit forward builds the bias rows in its first launch, beside the

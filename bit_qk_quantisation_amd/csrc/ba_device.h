@@ -108,6 +108,50 @@ __device__ __forceinline__ v16f mfma_bf16_32x32x16(v8bf a, v8bf b, v16f acc) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
 }
 
+// ---- scale products on the matrix cores ------------------------------------
+// The logit of query i and key j multiplies the integer dot by
+// w_ij = (alpha_q,i * scale * log2e) * alpha_k,j, an outer product.  A bf16
+// 32x32x16 product computes a 32 x 32 block of it at fp32 precision when
+// each factor enters as three bf16 terms x = x0 + x1 + x2 (each the
+// round-to-nearest-even bf16 of what the earlier ones leave; every remainder
+// is exact in fp32, so the terms carry x to within 2^-24 of itself): k-slots
+// 0..5 hold the six products a_i b_j with i + j <= 2, which are exact, and
+// the terms left out (i + j >= 3) add up to about 2^-25 a b.  So w is the
+// product to within a few fp32 roundings.  Keys supply the A operand (row =
+// key), queries the B operand (column = query); slots 6..15 hold zeros.
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ void split3_bf16(float x, uint32_t (&t)[3]) {
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    t[i] = bf16_rne_bits(x);
+    x -= __uint_as_float(t[i] << 16);
+  }
+}
+
+// The three A operand words of one key: slots 0..5 = b0 b1 b2 b0 b1 b0 (the
+// fourth word, slots 6 and 7, is zero).
+__device__ __forceinline__ void scale_split_a(float alpha_k, uint32_t (&w)[3]) {
+  uint32_t b[3];
+  split3_bf16(alpha_k, b);
+  w[0] = b[0] | (b[1] << 16);
+  w[1] = b[2] | (b[0] << 16);
+  w[2] = b[1] | (b[0] << 16);
+}
+
+// B operand words of one query (slots 0..5 = a0 a0 a0 a1 a1 a2) for a lane
+// of the low half; zeros for the high half (slots 8..15).
+__device__ __forceinline__ v4u scale_split_b(float aq, bool low_half) {
+  uint32_t a[3];
+  split3_bf16(aq, a);
+  if (!low_half) return v4u{0u, 0u, 0u, 0u};
+  return v4u{a[0] | (a[0] << 16), a[0] | (a[1] << 16), a[1] | (a[2] << 16), 0u};
+}
+
 // Value of x in lane n of this lane's row of 16 lanes (DPP row_newbcast:n).
 // n must be a constant once loops are unrolled; the broadcast then folds
 // into the instruction that uses it as a DPP source operand.

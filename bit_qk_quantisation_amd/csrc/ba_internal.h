@@ -75,6 +75,10 @@ struct KvJob {
   Strides ks, vs;
   int64_t BH;
   int H, N, Npad, d, W, nch, dpad;
+  // the pipelined kernel's key-scale operands, per 64-token tile the words
+  // w0 w1 of scale_split_a of each token (8 bytes each), then its w2 (nullptr:
+  // not written)
+  uint32_t* aks;      // [BH][Npad/64][192]
 };
 
 // Per-tile channel maxima of |V| for the 8-bit value codes, one 64-token
@@ -181,6 +185,7 @@ struct FwdArgs {
   const float* bias4;      // kBiasRows: [H][2gh-1+2*kBiasPadRows][4][Lpad]
   const float* bias_row_max;  // kBiasRows: [H][2gh-1], max |b| log2e per row
   const float* kmax_blk;   // [BH][Npad/64] max alpha_k per 64-token block
+  const uint32_t* aks;     // pipelined kernel: [BH][Npad/64][192] scale_split_a(alpha_k), see KvJob
   const uint16_t* table;   // kBiasTable: bf16 [H][2gh-1][2gw-1]
   const uint16_t* dense;   // kBiasDense: bias(b, h, i, j) at b*dsb + h*dsh + i*dld + j
   int64_t dsb, dsh, dld;

@@ -8,10 +8,12 @@
 // is (es page, section 2, "Implementacion en Hardware").
 //
 // Where the time goes on CDNA4.  A 32 x 32 block of scores costs a wave one
-// fp4 MFMA for QK, 2d/16 bf16 MFMAs for P.V, and per lane 16 scores of vector
-// work: a multiply by alpha_k, an FMA with alpha_q and the bias, an exp2 and
-// half a bf16 pack.  The vector ALU is the scarcer unit (4 cycles per wave64
-// instruction, 8 for the exp2), so the kernel is built to keep it issuing:
+// fp4 MFMA for QK, 2d/16 bf16 MFMAs for P.V, one bf16 MFMA for the scale
+// products w_ij = alpha_q,i alpha_k,j (scale log2e folded in; both factors
+// enter as three bf16 terms, so w is exact to fp32 rounding), and per lane
+// 16 scores of vector work: an FMA s w + bias, an exp2 and half a bf16 pack.
+// The vector ALU is the scarcer unit (4 cycles per wave64 instruction, 8 for
+// the exp2), so the kernel is built to keep it issuing:
 //   * the QK product of the NEXT block is issued before this block's vector
 //     work, so no wave waits on a matrix result (the S accumulator is double
 //     buffered in registers);
@@ -74,7 +76,7 @@ __device__ __forceinline__ int vswz(int r) {
 template <int D, int BIAS>
 struct FBuf {
   v4i k[FDims<D>::NCH * 128];                  // fp4 key operands [chunk][key][half]
-  float ak[64];                                // key scales
+  uint32_t aks[192];                           // key scales as matrix operands: w0 w1 [64], w2 [64]
   v4u v[FDims<D>::VBYTES / 16];                // V rows, chunks swizzled
   float win[BIAS == kBiasRows ? FDims<D>::WIN : 4];  // table-row bias window
 };
@@ -100,7 +102,8 @@ struct FCtx {
   float aq;                    // alpha_q * scale * log2e
   v4i qop[FDims<D>::NCH];      // the lane's query operand (fp4 +/-1)
   v8bf ones;                   // A operand of the row-sum product
-  int off_k, off_akb, off_win; // LDS byte offsets inside a buffer
+  v8bf bq;                     // B operand of the scale product (the lane's aq split)
+  int off_k, off_aks, off_win; // LDS byte offsets inside a buffer
   int off_v[FDims<D>::CB];     // byte offset of the lane's transposing reads
   int yq_lo;
   rsrc_t krs, ars, vrs, brs;   // sources of the tile copies
@@ -218,10 +221,10 @@ __device__ __forceinline__ float flash_setup(FCtx<D>& c, const FwdArgs& a, float
     const __bf16 x = one ? (__bf16)1.0f : (__bf16)0.0f;
     c.ones = v8bf{x, x, x, x, x, x, x, x};
   }
+  c.bq = __builtin_bit_cast(v8bf, scale_split_b(c.aq, c.lh == 0));
 
   c.off_k = (c.li * 2 + c.lh) * 16;
-  // the key scale register r of a 16-lane row needs sits in lane 16 row + r
-  c.off_akb = 4 * (8 * ((c.lane & 15) >> 2) + 4 * c.lh + (c.lane & 3));
+  c.off_aks = c.li * 8;   // A row li of the scale product: key li of the block
   {
     // Transposing reads: in each group of 16 lanes, lane 4k + m supplies the
     // address of 4 channels of key row 4 lh + k, and lane i then receives
@@ -250,7 +253,7 @@ __device__ __forceinline__ float flash_setup(FCtx<D>& c, const FwdArgs& a, float
   // copy sources: every range lies inside the section it names
   c.krs = make_rsrc(reinterpret_cast<const char*>(a.kop) + static_cast<int64_t>(c.bh) * (a.Npad / kBN) * F::KBYTES,
                     static_cast<uint32_t>((a.Npad / kBN) * F::KBYTES));
-  c.ars = make_rsrc(a.alpha_k + static_cast<int64_t>(c.bh) * a.Npad, static_cast<uint32_t>(a.Npad * 4));
+  c.ars = make_rsrc(a.aks + static_cast<int64_t>(c.bh) * (a.Npad / 64) * 192, static_cast<uint32_t>(a.Npad * 12));
   // V rows of this head; keys past N read as 0 (the range ends at key N-1)
   c.vsn = static_cast<uint32_t>(a.vs.sn * 2);
   c.vrs = make_rsrc(a.v + token_offset(a.vs, b, c.head, 0),
@@ -303,7 +306,7 @@ __device__ __forceinline__ void flash_copy(const FCtx<D>& c, FBuf<D, BIAS>& tb, 
     const int p = c.wave + 4 * j;
     if (p < F::VPIECES) dma16(c.vrs, vdst + p * 1024, c.voff, (k0 + static_cast<uint32_t>(p * F::RPP)) * c.vsn);
   }
-  if (c.wave == 3) dma4(c.ars, &tb.ak[0], static_cast<uint32_t>(c.lane * 4), k0 * 4);
+  if (c.wave == 3 && c.lane < 48) dma16(c.ars, &tb.aks[0], static_cast<uint32_t>(c.lane * 16), k0 * 12);
   run.k0 += kBN;
   if (BIAS == kBiasRows) {
     int ky[2], kx[2];
@@ -334,24 +337,28 @@ __device__ __forceinline__ void flash_copy(const FCtx<D>& c, FBuf<D, BIAS>& tb, 
 }
 
 // --------------------------------------------------------------- compute --
-// What the vector work of a block reads from LDS, fetched one block ahead.
+// What a block reads from LDS before its first scores, fetched one block
+// ahead: the A operand of its scale product and its first 4 bias values (the
+// other 12 are read inside the block, a chunk or two ahead of their use).
 struct FIn {
-  float akv;     // the key scale this lane hands to its row's broadcasts
-  v4f bias[4];   // table rows: the lane's 16 bias values (0 without a table)
+  v4u aop;       // scale_split_a of key li of the block (fourth word 0)
+  v4f bias0;     // table rows: bias of the lane's scores 0..3 (0 without a table)
+  int woff;      // table rows: the lane's window offset for the block
 };
 
 template <int D, int BIAS>
 __device__ __forceinline__ void flash_fetch(const FCtx<D>& c, const FBuf<D, BIAS>& tb, const FWin& w, int blk,
                                             FIn& in) {
-  in.akv = flds<float>(tb.ak, c.off_akb + blk * 128);
+  const v2u w01 = flds<v2u>(tb.aks, c.off_aks + blk * 256);
+  in.aop = v4u{w01[0], w01[1], flds<uint32_t>(tb.aks, 512 + c.off_aks / 2 + blk * 128), 0u};
   if (BIAS == kBiasRows) {
     int woff = c.off_win + w.u[blk];
     asm("" : "+v"(woff));  // one vector add here, the window reads take immediate offsets
-#pragma unroll
-    for (int b = 0; b < 4; ++b) in.bias[b] = flds<v4f>(tb.win, woff + 32 * b);
+    in.woff = woff;
+    in.bias0 = flds<v4f>(tb.win, woff);
   } else {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) in.bias[b] = v4f{};
+    in.woff = 0;
+    in.bias0 = v4f{};
   }
 }
 
@@ -379,40 +386,22 @@ __device__ __forceinline__ void flash_vops(const FCtx<D>& c, const FBuf<D, BIAS>
   }
 }
 
-// Holds the next block's QK result where it is issued.  The DPP multiplies
-// that first read it are inline assembly, which the compiler neither delays
-// after a matrix instruction nor keeps the product away from: the product
-// could otherwise sink to just before them, inside the wait states a matrix
-// result needs before a vector read.  The barrier keeps every instruction
-// after this point after the product.
+// Holds the next block's QK product where it is issued: left alone the
+// compiler sinks it into the branch that runs the next block, right before
+// the vector work that reads it, where the wave then waits for it.  The
+// barrier keeps every instruction after this point after the product.
 __device__ __forceinline__ void flash_qk_anchor(v16f& sn) {
   asm volatile("" : "+v"(sn));
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// u[e] = s[4 b + e] * alpha_k of the key that accumulator register 4 b + e
-// holds, taken by DPP row broadcast from lane 16 row + 4 b + e: one
-// v_mul_f32_dpp per score.  (Left to itself the compiler splits a share of
-// these into a broadcast move and a multiply.)  The s_nop covers a vector
-// write of akv right before the broadcast reads it.
-#define FLASH_DPP4(R0, R1, R2, R3)                                                               \
-  asm("s_nop 1\n\t"                                                                              \
-      "v_mul_f32_dpp %0, %8, %4 row_newbcast:" #R0 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
-      "v_mul_f32_dpp %1, %8, %5 row_newbcast:" #R1 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
-      "v_mul_f32_dpp %2, %8, %6 row_newbcast:" #R2 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
-      "v_mul_f32_dpp %3, %8, %7 row_newbcast:" #R3 " row_mask:0xf bank_mask:0xf bound_ctrl:1"     \
-      : "=&v"(u[0]), "=&v"(u[1]), "=&v"(u[2]), "=&v"(u[3])                                         \
-      : "v"(s0), "v"(s1), "v"(s2), "v"(s3), "v"(akv))
-
-template <int B>
-__device__ __forceinline__ void scale4(const v16f& s, float akv, float (&u)[4]) {
-  const float s0 = s[4 * B], s1 = s[4 * B + 1], s2 = s[4 * B + 2], s3 = s[4 * B + 3];
-  if (B == 0) FLASH_DPP4(0, 1, 2, 3);
-  if (B == 1) FLASH_DPP4(4, 5, 6, 7);
-  if (B == 2) FLASH_DPP4(8, 9, 10, 11);
-  if (B == 3) FLASH_DPP4(12, 13, 14, 15);
+// The scale products of the block whose A operand is `aop`: w[r] = aq of
+// the lane's query times alpha_k of the key in accumulator register r (the
+// QK layout), exact to fp32 rounding (see scale_split_a).
+template <int D>
+__device__ __forceinline__ v16f flash_scales(const FCtx<D>& c, const v4u& aop) {
+  return mfma_bf16_32x32x16(__builtin_bit_cast(v8bf, aop), c.bq, v16f{});
 }
-#undef FLASH_DPP4
 
 // The matrix instructions of a block, in issue order: the pending block's
 // first 16-key step (CB P.V products, then its row-sum product), the QK
@@ -456,20 +445,26 @@ __device__ __forceinline__ void flash_mfma(int m, const FCtx<D>& c, const FPend<
 // next block's QK are spread over four chunks of vector work (4 scores
 // each), so that no wave issues its matrix instructions back to back and the
 // vector ALU keeps issuing beside them; scheduling barriers hold that order.
-// The QK lands in the third chunk at the latest, so at least two chunks of
-// vector work (28 instructions, more than the 19 wait states a matrix result
-// needs) separate it from its first reader in the next block.  Writes P of
-// this block into nw.pk and its V^T operands into nw.vop, each step's once
-// the pending block's products have consumed the same registers' old values.
+// The scores are s w + bias with the block's scale products w; after the
+// last chunk w takes the next block's (its A operand in innext).  Writes P
+// of this block into nw.pk and its V^T operands into nw.vop, each step's
+// once the pending block's products have consumed the same registers' old
+// values.
 template <int D, int BIAS>
 __device__ __forceinline__ void flash_block_fast(const FCtx<D>& c, const FBuf<D, BIAS>& tb, int blk, const v16f& s,
                                                  const FIn& in, const v4i (&kop)[FDims<D>::NCH], v16f& sn,
                                                  const FPend<D>& old, FPend<D>& nw, FAcc<D>& acc, int key0,
-                                                 bool mask) {
+                                                 bool mask, v16f& w, const FIn& innext) {
   using O = FOrder<D>;
   constexpr int NM = O::NM;
-  static_assert(O::QKL < 3 * NM / 4, "the QK must issue before the last chunk");
   const FwdArgs& a = *c.a;
+  v4f bias[4];
+  bias[0] = in.bias0;
+  bias[1] = bias[2] = bias[3] = v4f{};
+  if (BIAS == kBiasRows) {
+    bias[1] = flds<v4f>(tb.win, in.woff + 32);
+    bias[2] = flds<v4f>(tb.win, in.woff + 64);
+  }
   sn = v16f{};
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -477,14 +472,11 @@ __device__ __forceinline__ void flash_block_fast(const FCtx<D>& c, const FBuf<D,
     for (int m = b * NM / 4; m < (b + 1) * NM / 4; ++m) flash_mfma<D>(m, c, old, kop, sn, acc);
     if (b * NM / 4 <= O::LASTV0 && O::LASTV0 < (b + 1) * NM / 4) flash_vops(c, tb, blk, 0, nw);
     if (b * NM / 4 <= O::LASTV1 && O::LASTV1 < (b + 1) * NM / 4) flash_vops(c, tb, blk, 1, nw);
-    float u[4];
-    if (b == 0) scale4<0>(s, in.akv, u);
-    if (b == 1) scale4<1>(s, in.akv, u);
-    if (b == 2) scale4<2>(s, in.akv, u);
-    if (b == 3) scale4<3>(s, in.akv, u);
+    if (b == 0 && BIAS == kBiasRows) bias[3] = flds<v4f>(tb.win, in.woff + 96);
     float x[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = BIAS == kBiasRows ? fmaf(u[e], c.aq, in.bias[b][e]) : u[e] * c.aq;
+    for (int e = 0; e < 4; ++e)
+      x[e] = BIAS == kBiasRows ? fmaf(s[4 * b + e], w[4 * b + e], bias[b][e]) : s[4 * b + e] * w[4 * b + e];
     if (BIAS != kBiasRows && mask) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -497,20 +489,25 @@ __device__ __forceinline__ void flash_block_fast(const FCtx<D>& c, const FBuf<D,
     asm volatile("" : "+v"(nw.pk[2 * b]), "+v"(nw.pk[2 * b + 1]));
     __builtin_amdgcn_sched_barrier(0);
   }
+  w = flash_scales(c, innext.aop);
 }
 
 // One block with the online softmax: the pending block's products and the
 // next block's QK go first (a rescale of the accumulators must cover the
-// products; the QK is then a whole block of vector work ahead of its
-// reader), then the logits, the row maximum (log2 units, mrow) with the lazy
-// rescale and P = exp2(s - mrow).
+// products), then the logits s w + bias, the row maximum (log2 units, mrow)
+// with the lazy rescale, P = exp2(s - mrow), and the next block's scale
+// products.
 template <int D, int BIAS>
 __device__ __forceinline__ void flash_block_exact(const FCtx<D>& c, const FBuf<D, BIAS>& tb, int blk,
                                                   const v16f& s, const FIn& in,
                                                   const v4i (&kop)[FDims<D>::NCH], v16f& sn,
                                                   const FPend<D>& old, FPend<D>& nw, FAcc<D>& acc, int key0,
-                                                  bool mask, float& mrow) {
+                                                  bool mask, float& mrow, v16f& w, const FIn& innext) {
   const FwdArgs& a = *c.a;
+  v4f bias[4];
+  bias[0] = in.bias0;
+#pragma unroll
+  for (int b = 1; b < 4; ++b) bias[b] = BIAS == kBiasRows ? flds<v4f>(tb.win, in.woff + 32 * b) : v4f{};
   sn = v16f{};
 #pragma unroll
   for (int m = 0; m < FOrder<D>::NM; ++m) flash_mfma<D>(m, c, old, kop, sn, acc);
@@ -518,15 +515,8 @@ __device__ __forceinline__ void flash_block_exact(const FCtx<D>& c, const FBuf<D
   flash_vops(c, tb, blk, 1, nw);
   float x[16];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    float u[4];
-    if (b == 0) scale4<0>(s, in.akv, u);
-    if (b == 1) scale4<1>(s, in.akv, u);
-    if (b == 2) scale4<2>(s, in.akv, u);
-    if (b == 3) scale4<3>(s, in.akv, u);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[4 * b + e] = BIAS == kBiasRows ? fmaf(u[e], c.aq, in.bias[b][e]) : u[e] * c.aq;
-  }
+  for (int r = 0; r < 16; ++r)
+    x[r] = BIAS == kBiasRows ? fmaf(s[r], w[r], bias[r >> 2][r & 3]) : s[r] * w[r];
   if (BIAS != kBiasRows && mask) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
@@ -546,17 +536,18 @@ __device__ __forceinline__ void flash_block_exact(const FCtx<D>& c, const FBuf<D
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) nw.pk[j] = pack_bf16x2(fast_exp2(x[2 * j] - mrow), fast_exp2(x[2 * j + 1] - mrow));
+  w = flash_scales(c, innext.aop);
 }
 
 template <int D, int BIAS, bool EXACT>
 __device__ __forceinline__ void flash_block(const FCtx<D>& c, const FBuf<D, BIAS>& tb, int blk, const v16f& s,
                                             const FIn& in, const v4i (&kop)[FDims<D>::NCH], v16f& sn,
                                             const FPend<D>& old, FPend<D>& nw, FAcc<D>& acc, int key0, bool mask,
-                                            float& mrow) {
+                                            float& mrow, v16f& w, const FIn& innext) {
   if (EXACT)
-    flash_block_exact<D, BIAS>(c, tb, blk, s, in, kop, sn, old, nw, acc, key0, mask, mrow);
+    flash_block_exact<D, BIAS>(c, tb, blk, s, in, kop, sn, old, nw, acc, key0, mask, mrow, w, innext);
   else
-    flash_block_fast<D, BIAS>(c, tb, blk, s, in, kop, sn, old, nw, acc, key0, mask);
+    flash_block_fast<D, BIAS>(c, tb, blk, s, in, kop, sn, old, nw, acc, key0, mask, w, innext);
 }
 
 // Wave priority (when the host sets prio_balance: every workgroup of the
@@ -594,7 +585,7 @@ template <int D, int BIAS, bool EXACT>
 __device__ __forceinline__ void flash_tile(const FCtx<D>& c, const FBuf<D, BIAS>& cur, const FBuf<D, BIAS>& nxt,
                                            FBuf<D, BIAS>& far, const FWin& wc, const FWin& wn, FWin& wf, FRun& run,
                                            FPrio& prio, int t, int nkt, v16f& s0, v16f& s1, FIn& in0, FIn& in1,
-                                           FPend<D>& ppa, FPend<D>& ppb, FAcc<D>& acc, float& mrow) {
+                                           FPend<D>& ppa, FPend<D>& ppb, FAcc<D>& acc, float& mrow, v16f& w) {
   const FwdArgs& a = *c.a;
   const int k0 = t * kBN;
   const bool has1 = k0 + 32 < a.N;
@@ -602,7 +593,7 @@ __device__ __forceinline__ void flash_tile(const FCtx<D>& c, const FBuf<D, BIAS>
   // block 0: the next block is this tile's block 1
   flash_kops(c, cur, 1, kop);
   flash_fetch(c, cur, wc, 1, in1);
-  flash_block<D, BIAS, EXACT>(c, cur, 0, s0, in0, kop, s1, ppa, ppb, acc, k0, k0 + 32 > a.N, mrow);
+  flash_block<D, BIAS, EXACT>(c, cur, 0, s0, in0, kop, s1, ppa, ppb, acc, k0, k0 + 32 > a.N, mrow, w, in1);
   // tile t+1 is in `nxt` once every wave's copies have landed; every wave is
   // done with tile t-1, whose buffer `far` takes tile t+2
   __builtin_amdgcn_s_waitcnt(0);
@@ -613,7 +604,7 @@ __device__ __forceinline__ void flash_tile(const FCtx<D>& c, const FBuf<D, BIAS>
     // block 1: the next block is tile t+1's block 0
     flash_kops(c, nxt, 0, kop);
     flash_fetch(c, nxt, wn, 0, in0);
-    flash_block<D, BIAS, EXACT>(c, cur, 1, s1, in1, kop, s0, ppb, ppa, acc, k0 + 32, k0 + 64 > a.N, mrow);
+    flash_block<D, BIAS, EXACT>(c, cur, 1, s1, in1, kop, s0, ppb, ppa, acc, k0 + 32, k0 + 64 > a.N, mrow, w, in0);
   } else {
     ppa = ppb;  // the last tile ends after block 0
   }
@@ -653,13 +644,10 @@ __device__ __forceinline__ float flash_pass(const FCtx<D>& c, FBuf<D, BIAS>& b0,
     s0 = v16f{};
 #pragma unroll
     for (int ch = 0; ch < FDims<D>::NCH; ++ch) s0 = mfma_signs_32x32x64(kop[ch], c.qop[ch], s0);
-    // the first block reads s0 in inline assembly: wait out the matrix
-    // result's 19 wait states here, once
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0));
-    __builtin_amdgcn_sched_barrier(0);
   }
   FIn in0, in1;
   flash_fetch(c, b0, w0, 0, in0);
+  v16f wk = flash_scales(c, in0.aop);  // the scale products of block 0
   // nothing is pending before the first block: P = 0
   FPend<D> ppa, ppb;
 #pragma unroll
@@ -669,13 +657,13 @@ __device__ __forceinline__ float flash_pass(const FCtx<D>& c, FBuf<D, BIAS>& b0,
 #pragma unroll
     for (int cb = 0; cb < FDims<D>::CB; ++cb) ppa.vop[st][cb] = v8bf{};
   for (int t = 0; t < nkt; t += 3) {
-    flash_tile<D, BIAS, EXACT>(c, b0, b1, b2, w0, w1, w2, run, prio, t, nkt, s0, s1, in0, in1, ppa, ppb, acc, mrow);
+    flash_tile<D, BIAS, EXACT>(c, b0, b1, b2, w0, w1, w2, run, prio, t, nkt, s0, s1, in0, in1, ppa, ppb, acc, mrow, wk);
     if (t + 1 >= nkt) break;
     flash_tile<D, BIAS, EXACT>(c, b1, b2, b0, w1, w2, w0, run, prio, t + 1, nkt, s0, s1, in0, in1, ppa, ppb, acc,
-                               mrow);
+                               mrow, wk);
     if (t + 2 >= nkt) break;
     flash_tile<D, BIAS, EXACT>(c, b2, b0, b1, w2, w0, w1, run, prio, t + 2, nkt, s0, s1, in0, in1, ppa, ppb, acc,
-                               mrow);
+                               mrow, wk);
   }
   // drain: the last block's P.V and row sums
 #pragma unroll
@@ -734,9 +722,10 @@ flash_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) FBuf<D, BIAS> b0;
   __shared__ __attribute__((aligned(16))) FBuf<D, BIAS> b1;
   __shared__ __attribute__((aligned(16))) FBuf<D, BIAS> b2;
-  __shared__ float red[3 * kThreads / 64];
   FCtx<D> c;
-  const float M = flash_setup<D, BIAS>(c, a, red);
+  // the setup's reduction borrows b2, which the first copies leave alone
+  // (it takes tile 2, after several barriers)
+  const float M = flash_setup<D, BIAS>(c, a, reinterpret_cast<float*>(&b2.v[0]));
   FAcc<D> acc;
   float mrow;
   if (M <= kFlashFastMax)  // false for NaN as well
@@ -749,7 +738,7 @@ flash_fwd_kernel(FwdArgs a) {
 
 template <int D, int BIAS>
 int flash_lds() {
-  return static_cast<int>(3 * sizeof(FBuf<D, BIAS>) + 3 * kThreads / 64 * 4);
+  return static_cast<int>(3 * sizeof(FBuf<D, BIAS>));
 }
 
 template <int D>

@@ -199,6 +199,13 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
     const int tok = threadIdx.x;
     const float a = tok < rows ? token_sum(sp + tok * 33, C) / static_cast<float>(d) : 0.0f;
     job.alpha[bh * job.Npad + n0 + tok] = a;
+    if (job.aks) {
+      uint32_t w[3];
+      scale_split_a(a, w);
+      uint32_t* t = job.aks + blk * 192;
+      *reinterpret_cast<v2u*>(t + 2 * tok) = v2u{w[0], w[1]};
+      t[128 + tok] = w[2];
+    }
     float m = a;  // scales are >= 0
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));

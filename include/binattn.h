@@ -100,9 +100,11 @@ ba_status ba_pack_signs(const void* x, int64_t B, int64_t H, int64_t N, int d,
  * as fp4 +/-1 matrix operands (32 bytes per token and 64 channels), the K
  * scales and their maximum per 64 tokens, a key-major V^T section (per
  * head, N padded to a multiple of 128), for a bias grid with gw % 32 == 0 the
- * table rows in float32, and, where the prepared forward runs the pipelined
- * kernel (see ba_attention_fwd), a copy of V in its own layout [B,H,Npad,d].
- * The queries are packed inside the fused kernel.  Pass gh = gw = 0 for a
+ * table rows in float32, where the prepared forward runs the pipelined
+ * kernel (see ba_attention_fwd) a copy of V in its own layout [B,H,Npad,d],
+ * and, for shapes the pipelined kernel takes, each K scale as three bf16
+ * terms laid out as a matrix operand (12 bytes per token).  The queries are
+ * packed inside the fused kernel.  Pass gh = gw = 0 for a
  * call without bias table.  Returns 0 for sizes the library rejects
  * (including gh*gw != N when a grid is given). */
 size_t ba_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int gh, int gw);
@@ -229,7 +231,8 @@ ba_status ba_attention_fwd_int8pv(const void* q, const void* k, const void* v,
  * ba_attention_prepare -- enqueues the prologue kernel: the signs and scales
  * of K ("Representaciones Binarias Escaladas"), the key-major V^T copy, a
  * copy of V in its own layout where the prepared forward runs the pipelined
- * kernel, and, for gw % 32 == 0, the float32 bias rows, all written into
+ * kernel together with the K scales as its matrix operands, and, for
+ * gw % 32 == 0, the float32 bias rows, all written into
  * `workspace`.  Same arguments and errors as ba_attention_fwd, without q,
  * scale and o.
  *

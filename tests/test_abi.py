@@ -81,6 +81,9 @@ def expected_workspace(B, H, N, d, gh=0, gw=0, int8pv=False):
     if not int8pv and _prepared_pipelined(N, d, gh, gw, rows, lpad):
         # the values' natural rows, for the prepared forward's pipelined kernel
         secs.append(B * H * npad * d * 2)
+    if not int8pv and _pipelined_shape(N, d, gh, gw, rows, lpad):
+        # the key scales as the pipelined kernel's matrix operands
+        secs.append(B * H * npad * 12)
     return sum(_round(s, 256) for s in secs)
 
 
@@ -88,6 +91,14 @@ def _window_rows(N, gw):
     qspan = max(((q0 + 127) // gw - q0 // gw) for q0 in range(0, _round(N, 128), 128))
     kspan = max(((k0 + 63) // gw - k0 // gw) for k0 in range(0, N, 64))
     return qspan + kspan + 1
+
+
+def _pipelined_shape(N, d, gh, gw, rows, lpad):
+    """The pipelined kernel takes d in {32, 64, 128} with table rows whose
+    window fits its buffers, or without a bias."""
+    if d not in (32, 64, 128) or (gh and not rows):
+        return False
+    return not rows or _window_rows(N, gw) * 4 * lpad <= (1664 if d <= 64 else 1152)
 
 
 def _prepared_pipelined(N, d, gh, gw, rows, lpad):
@@ -357,7 +368,8 @@ def test_bwd_validation(lib):
     assert call(do=A + 4 * GB + fwd + 256, wsb=big) == 5
     assert call(k=A + 4 * GB + full - 4096, wsb=big) == 5
     assert call(v=A + 4 * GB - 4096, wsb=big) == 5                        # v's rows run into it
-    assert call(bias=A + 4 * GB + full - 512, gh=8, gw=8, wsb=big) == 5    # the table inside it
+    full_t = lib.ba_workspace_bytes_bwd(1, 2, 64, 64, 8, 8)
+    assert call(bias=A + 4 * GB + full_t - 512, gh=8, gw=8, wsb=big) == 5  # the table inside it
 
 
 def test_fwd_train_validation(lib):
