@@ -139,8 +139,9 @@ def pipelined(w, table=True):
 def algorithmic_bytes(w, npad, dense_bytes=None):
     """Compulsory HBM bytes of the two kernels of one step.  Pipelined
     kernel: the prologue reads K and writes the fp4 key operands and the key
-    scales (and their maxima per 64 tokens), plus the bias rows from the
-    table; the fused kernel reads Q, those, V and the bias rows and writes O.
+    scales as matrix operands (and the scales' maxima per 64 tokens), plus the
+    bias rows from the table; the fused kernel reads Q, those, V and the bias
+    rows and writes O.
     Otherwise the prologue also reads V and writes V^T, which the fused kernel
     reads instead of V."""
     W = (w.d + 31) // 32
@@ -149,6 +150,9 @@ def algorithmic_bytes(w, npad, dense_bytes=None):
     bh = w.B * w.H
     tok = bh * w.N
     keys = bh * npad * (32 * nch + 4) + bh * (npad // 64) * 4
+    # the pipelined kernel takes the key scales as matrix operands (12 bytes
+    # per key) instead of floats
+    keys_p = bh * npad * (32 * nch + 12) + bh * (npad // 64) * 4
     vt = bh * dpad * npad * 2
     rows = 0
     if w.gw % 32 == 0:
@@ -157,8 +161,8 @@ def algorithmic_bytes(w, npad, dense_bytes=None):
     if dense_bytes is not None:  # no table: the fused kernel reads the dense bias once
         return 2 * tok * w.d * 2 + keys + vt, tok * w.d * 2 + keys + vt + dense_bytes + tok * w.d * 2
     if pipelined(w):
-        prologue = tok * w.d * 2 + keys + ((table + rows) if rows else 0)
-        fused = tok * w.d * 2 + keys + tok * w.d * 2 + (rows if rows else table) + tok * w.d * 2
+        prologue = tok * w.d * 2 + keys_p + ((table + rows) if rows else 0)
+        fused = tok * w.d * 2 + keys_p + tok * w.d * 2 + (rows if rows else table) + tok * w.d * 2
         return prologue, fused
     prologue = 2 * tok * w.d * 2 + keys + vt + ((table + rows) if rows else 0)
     fused = tok * w.d * 2 + keys + vt + (rows if rows else table) + tok * w.d * 2

@@ -585,8 +585,10 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
 
   ba::PrologueArgs& p = plan->p;
   p = ba::PrologueArgs{};
+  // the pipelined kernel takes the key scales only as matrix operands (aks)
+  const bool scales_as_floats = !(flash && whole);
   p.kv = ba::KvJob{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), const_cast<uint32_t*>(f.kop),
-                   const_cast<float*>(f.alpha_k), const_cast<float*>(f.kmax_blk),
+                   scales_as_floats ? const_cast<float*>(f.alpha_k) : nullptr, const_cast<float*>(f.kmax_blk),
                    flash ? nullptr : const_cast<uint16_t*>(f.vt),
                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                    (preparing && L.flash_prepared) ? vnat : nullptr,

@@ -53,7 +53,7 @@ struct KvJob {
   const uint16_t* k;  // bf16, strides ks
   const uint16_t* v;  // bf16, strides vs
   uint32_t* kop;      // fp4 key operands [BH][Npad/64][NCH][64][2][4]
-  float* alpha;       // key scales [BH][Npad]
+  float* alpha;       // key scales [BH][Npad] (nullptr: not written)
   float* alpha_max;   // largest key scale of each tile [BH][Npad/64]
   uint16_t* vt;       // bf16 [BH][Npad/64][dpad][64], see the prologue
   // 8-bit P.V (vq != nullptr, then vt is unused): value codes, written as

@@ -198,7 +198,7 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
   if (threadIdx.x < kPackTok) {
     const int tok = threadIdx.x;
     const float a = tok < rows ? token_sum(sp + tok * 33, C) / static_cast<float>(d) : 0.0f;
-    job.alpha[bh * job.Npad + n0 + tok] = a;
+    if (job.alpha) job.alpha[bh * job.Npad + n0 + tok] = a;
     if (job.aks) {
       uint32_t w[3];
       scale_split_a(a, w);
