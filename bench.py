@@ -73,6 +73,13 @@ PEAK_FP4 = 10100.0
 PEAK_BF16 = 2500.0
 PEAK_INT8 = 5000.0
 PEAK_HBM_GBS = 8000.0
+# Vector ALU: 256 CUs x 4 SIMDs x 16 lanes issue 16 lane-operations per SIMD
+# per cycle at 2.4 GHz (a wave64 FMA takes 4 cycles), 39.3 T lane-cycles/s.
+# The pipelined kernel's vector work per score is one exp2 (a transcendental,
+# which takes a SIMD twice as long as an FMA: 8 cycles per wave64
+# instruction, measured), one FMA and half a bf16 pack: 3.5 lane-cycles.
+PEAK_VALU_TLC = 256 * 4 * 16 * 2.4e9 / 1e12
+VALU_LC_PER_SCORE = 3.5
 # The fused kernel runs QK (2d flops-eq per score) on the fp4 unit and P.V
 # (2d flops per score) on the bf16 unit; with both at their peaks, one after
 # the other, the matrix-core bound of 4d flops-eq per score is:
@@ -524,6 +531,12 @@ def main() -> int:
     traffic = measured_traffic(name) if split and dense is None else None
     fused_gbs = fus_bytes / (fus_ms * 1e-3) / 1e9
     hbm_bound = dense is not None and fused_gbs / PEAK_HBM_GBS > fused_tf / peak
+    # the pipelined kernel's vector work against its matrix work: the bound
+    # whose minimum time is longer is the one reported
+    scores = w.B * w.H * w.N * w.N
+    alu_tlc = scores * VALU_LC_PER_SCORE / (fus_ms * 1e-3) / 1e12
+    alu_bound = (whole_call and not hbm_bound and
+                 scores * VALU_LC_PER_SCORE / PEAK_VALU_TLC > flop / peak)
 
     baseline = None
     if args.cpu_seconds > 0 and args.bwd:
@@ -565,7 +578,15 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(fused_tf / peak, 4),
             "traffic": traffic,
-        } if not hbm_bound else {
+        } if not hbm_bound and not alu_bound else {
+            "bound": "alu",
+            "kernel": "flash_fwd_kernel (fused, pipelined): exp2 + FMA + half a bf16 pack per score",
+            "achieved": round(alu_tlc, 2),
+            "peak": round(PEAK_VALU_TLC, 2),
+            "unit": "T lane-cycles/s",
+            "frac": round(alu_tlc / PEAK_VALU_TLC, 4),
+            "traffic": traffic,
+        } if alu_bound else {
             "bound": "hbm",
             "kernel": "attn_fwd_kernel (fused, dense bias)",
             "achieved": round(fused_gbs, 1),
@@ -580,6 +601,7 @@ def main() -> int:
             "prologue_us": round(pro_ms * 1e3, 2) if split else None,
             "step_us": round(ms_step * 1e3, 2),
             "frac_of_int8_bf16_mfma_roofline": round(fused_tf / PEAK_MFMA_INT8_BF16, 4),
+            "fused_frac_of_valu_roofline": round(alu_tlc / PEAK_VALU_TLC, 4) if whole_call else None,
             "step_frac_of_composite_mfma_roofline": round(value / PEAK_MFMA_COMPOSITE, 4),
             "prologue_algorithmic_GBps": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1) if split else None,
             "prologue_frac_of_hbm": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if split else None,
