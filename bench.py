@@ -26,6 +26,11 @@ the step is then ba_attention_prepare + ba_attention_fwd_dense_bias_prepared,
 and the roofline object names whichever bound (matrix cores or HBM) the fused
 kernel is closer to.
 
+--qk-routes times ba_qk_int_dot's row-sum form for the three ways of taking
+the integer dots (fp4 MFMA, the fused kernel's route; int8 MFMA; VALU
+xor/popcount) on the workload's packed Q and K, and prints their times
+instead of the forward's line.
+
 --pv int8 runs the pages' hybrid 8-bit P.V (ba_attention_fwd_int8pv: three
 kernels in one call), so only the whole step is timed; its roofline takes the
 fp4 QK + int8 P.V matrix-core bound.
@@ -285,6 +290,47 @@ def cpu_baseline_bwd(w, inp, dout, grads, seconds: float):
     }
 
 
+def qk_routes(args, w, inp, lib, dev) -> int:
+    """Times ba_qk_int_dot in its row-sum form for the fp4-MFMA, int8-MFMA
+    and VALU xor/popcount routes on the workload's packed Q and K (the three
+    ways of taking the integer dots); prints one JSON line."""
+    import torch
+
+    import bit_qk_quantisation_amd as bq
+    B, H, N, d = w.B, w.H, w.N, w.d
+    qb, _ = bq.pack_signs(inp["q"].to(dev))
+    kb, _ = bq.pack_signs(inp["k"].to(dev))
+    sums = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    res, ref = {}, None
+    for name, route in (("mfma_fp4", bq.ROUTE_MFMA_FP4), ("mfma_int8", bq.ROUTE_MFMA_INT8),
+                        ("valu_popcount", bq.ROUTE_VALU_POPCOUNT)):
+        def run():
+            bq.check(lib, lib.ba_qk_int_dot(qb.data_ptr(), kb.data_ptr(), B, H, N, d, route | bq.QK_ROWSUM,
+                                            sums.data_ptr(), sp))
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        got = sums.clone()
+        if ref is None:
+            ref = got
+        res[name] = {"us_per_launch": round(us, 2),
+                     "tops_eq": round(2.0 * B * H * N * N * d / (us * 1e-6) / 1e12, 1),
+                     "same_sums_as_fp4": bool(torch.equal(got, ref))}
+        log(f"[qk-routes] {w.name} {name}: {us:.2f} us")
+    print(json.dumps({"metric": "QK integer dots, row-sum form: time per launch by route",
+                      "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d},
+                      "routes": res}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +348,8 @@ def main() -> int:
                     help="P.V precision (see above)")
     ap.add_argument("--bias", choices=("table", "dense", "dense-batch"), default="table",
                     help="bias form (see above)")
+    ap.add_argument("--qk-routes", action="store_true",
+                    help="time the three QK routes against each other instead (see above)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB "
                          "(reference kernel for HBM counter calibration)")
@@ -328,6 +376,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
 
     inp = workloads.workload_inputs(w)
+    if args.qk_routes:
+        return qk_routes(args, w, inp, lib, dev)
     q = inp["q"].to(dev)
     k = inp["k"].to(dev)
     v = inp["v"].to(dev)

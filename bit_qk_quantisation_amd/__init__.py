@@ -23,13 +23,14 @@ import math
 
 import torch
 
-from ._lib import (BinAttnError, EXPORTS, ROUTE_MFMA_FP4,  # noqa: F401
-                   ROUTE_VALU_POPCOUNT, check, load)
+from ._lib import (BinAttnError, EXPORTS, QK_ROWSUM, ROUTE_MFMA_FP4,  # noqa: F401
+                   ROUTE_MFMA_INT8, ROUTE_VALU_POPCOUNT, check, load)
 
 __all__ = ["pack_signs", "attention_fwd", "attention_fwd_dense_bias", "attention_fwd_int8pv", "attention_fwd_train",
            "attention_bwd",
            "qk_int_dot", "workspace_bytes",
-           "pack_words", "BinAttnError", "ROUTE_MFMA_FP4", "ROUTE_VALU_POPCOUNT",
+           "pack_words", "BinAttnError", "ROUTE_MFMA_FP4", "ROUTE_VALU_POPCOUNT", "ROUTE_MFMA_INT8",
+           "QK_ROWSUM",
            "Workspace"]
 
 
@@ -325,8 +326,9 @@ def attention_bwd(q, k, v, dout, table=None, gh: int = 0, gw: int = 0, scale=Non
     return dq, dk, dv, dtable
 
 
-def qk_int_dot(qbits, kbits, d: int, route: int = ROUTE_MFMA_FP4):
-    """All-pairs integer dots <sign q_i, sign k_j> from packed bits."""
+def qk_int_dot(qbits, kbits, d: int, route: int = ROUTE_MFMA_FP4, rowsum: bool = False):
+    """All-pairs integer dots <sign q_i, sign k_j> from packed bits, or
+    with rowsum=True their sums over the keys, int32 [B,H,N]."""
     lib = load()
     _need(qbits, "qbits", torch.int32, 4)
     _need(kbits, "kbits", torch.int32, 4)
@@ -335,7 +337,9 @@ def qk_int_dot(qbits, kbits, d: int, route: int = ROUTE_MFMA_FP4):
     B, H, N, W = qbits.shape
     if W != lib.ba_pack_words(d):
         raise ValueError("word count does not match d")
-    dots = torch.empty((B, H, N, N), dtype=torch.int32, device=qbits.device)
+    shape = (B, H, N) if rowsum else (B, H, N, N)
+    dots = torch.empty(shape, dtype=torch.int32, device=qbits.device)
+    route = int(route) | (QK_ROWSUM if rowsum else 0)
     check(lib, lib.ba_qk_int_dot(qbits.data_ptr(), kbits.data_ptr(), B, H, N, int(d),
                                  int(route), dots.data_ptr(), _stream(qbits.device)))
     return dots

@@ -22,6 +22,8 @@ STATUS = {0: "BA_OK", 1: "BA_ERR_NULL", 2: "BA_ERR_SHAPE", 3: "BA_ERR_UNSUPPORTE
 
 ROUTE_MFMA_FP4 = 0
 ROUTE_VALU_POPCOUNT = 1
+ROUTE_MFMA_INT8 = 2
+QK_ROWSUM = 0x100
 
 _lib = None
 

@@ -997,14 +997,16 @@ ba_status ba_qk_int_dot(const uint32_t* qbits, const uint32_t* kbits, int64_t B,
   if (!qbits || !kbits || !dots) return fail(BA_ERR_NULL, "qbits, kbits and dots must be non-NULL");
   ba_status st = check_dims(B, H, N, d);
   if (st != BA_OK) return st;
-  if (route != BA_ROUTE_MFMA_FP4 && route != BA_ROUTE_VALU_POPCOUNT)
+  const bool rowsum = (route & BA_QK_ROWSUM) != 0;
+  const int r = route & ~BA_QK_ROWSUM;
+  if (r != BA_ROUTE_MFMA_FP4 && r != BA_ROUTE_VALU_POPCOUNT && r != BA_ROUTE_MFMA_INT8)
     return fail(BA_ERR_UNSUPPORTED, "unknown route %d", route);
   if (N > 65535 || B * H > 65535) return fail(BA_ERR_SHAPE, "qk_int_dot needs N <= 65535 and B*H <= 65535");
-  if (B * H * N > (int64_t{1} << 40) / N) return fail(BA_ERR_SHAPE, "B*H*N*N exceeds 2^40");
+  if (!rowsum && B * H * N > (int64_t{1} << 40) / N) return fail(BA_ERR_SHAPE, "B*H*N*N exceeds 2^40");
   if (!aligned16(qbits) || !aligned16(kbits) || !aligned16(dots))
     return fail(BA_ERR_ALIGN, "qbits, kbits and dots must be 16-byte aligned");
-  ba::DotArgs a{qbits, kbits, dots, B * H, static_cast<int>(N), d, (d + 31) / 32};
-  const int err = ba::launch_qk_dot(a, route, stream);
+  ba::DotArgs a{qbits, kbits, dots, B * H, static_cast<int>(N), d, (d + 31) / 32, rowsum ? 1 : 0};
+  const int err = ba::launch_qk_dot(a, r, stream);
   if (err != 0) return hip_fail(err, "qk_int_dot launch");
   return BA_OK;
 }

@@ -276,9 +276,10 @@ int launch_backward(const BwdArgs& a, int role, int mode, void* stream);
 struct DotArgs {
   const uint32_t* qbits;  // [BH][N][W]
   const uint32_t* kbits;  // [BH][N][W]
-  int32_t* dots;          // [BH][N][N]
+  int32_t* dots;          // [BH][N][N], or [BH][N] row sums
   int64_t BH;
   int N, d, W;
+  int rowsum;             // 1: dots[bh][i] = sum_j D_ij
 };
 
 int launch_qk_dot(const DotArgs& a, int route, void* stream);

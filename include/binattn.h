@@ -369,17 +369,24 @@ ba_status ba_attention_bwd_saved(const void* q, const void* k, const void* v,
 #define BA_ROUTE_MFMA_FP4 0 /* +/-1 in fp4 (e2m1) on the scaled f8f6f4 MFMA;
                                the route the fused kernel uses */
 #define BA_ROUTE_VALU_POPCOUNT 1 /* v_xor + v_bcnt on the packed words */
+#define BA_ROUTE_MFMA_INT8 2 /* +/-1 in int8 on v_mfma_i32_32x32x32_i8 */
+/* OR'ed into the route: row sums instead of the N x N matrix (see below). */
+#define BA_QK_ROWSUM 0x100
 
 /* ba_qk_int_dot -- the integer similarities D_ij = <sign q_i, sign k_j> for
  * all pairs, from packed signs ("XNOR y popcount", "Representaciones
  * Binarias Escaladas").  It exists to check the fused kernel's QK step bit
- * for bit: route BA_ROUTE_MFMA_FP4 runs the same device code the fused kernel
- * uses.
+ * for bit (route BA_ROUTE_MFMA_FP4 runs the same device code the fused kernel
+ * uses) and to time the three ways of taking these dots against each other.
  *   qbits, kbits  uint32 [B,H,N,W] in the packed layout
- *   dots          int32 [B,H,N,N] output, dots[b,h,i,j] = D_ij
+ *   route         BA_ROUTE_*, optionally | BA_QK_ROWSUM
+ *   dots          int32 [B,H,N,N] output, dots[b,h,i,j] = D_ij; with
+ *                 BA_QK_ROWSUM int32 [B,H,N], dots[b,h,i] = sum_j D_ij (each
+ *                 workgroup shares 64-key tiles in LDS across 128 queries, as
+ *                 the fused kernel does, so the time is the route's arithmetic)
  * Errors: BA_ERR_NULL, BA_ERR_SHAPE (also if B*H*N*N overflows int64 or
- *         exceeds 2^40 elements), BA_ERR_UNSUPPORTED (unknown route or d),
- *         BA_ERR_ALIGN, BA_ERR_HIP. */
+ *         exceeds 2^40 elements without BA_QK_ROWSUM), BA_ERR_UNSUPPORTED
+ *         (unknown route or d), BA_ERR_ALIGN, BA_ERR_HIP. */
 ba_status ba_qk_int_dot(const uint32_t* qbits, const uint32_t* kbits,
                         int64_t B, int64_t H, int64_t N, int d, int route,
                         int32_t* dots, void* stream);

@@ -192,6 +192,11 @@ def test_qk_dot_validation(lib):
     assert lib.ba_qk_int_dot(A, A + GB, 1, 1, 8, 64, 7, A + 2 * GB, None) == 3
     assert lib.ba_qk_int_dot(A, A + GB, 1, 1, 70000, 64, 0, A + 2 * GB, None) == 2
     assert lib.ba_qk_int_dot(A, A + GB, 1, 1, 8, 64, 0, A + 2 * GB + 4, None) == 4
+    assert lib.ba_qk_int_dot(A, A + GB, 1, 1, 8, 64, 3 | 0x100, A + 2 * GB, None) == 3   # unknown route
+    assert lib.ba_qk_int_dot(A, A + GB, 1, 1, 8, 72, 0x200, A + 2 * GB, None) == 3       # unknown flag
+    # the row sums write B*H*N values, so the 2^40 bound on N*N does not apply
+    assert lib.ba_qk_int_dot(A, A + GB, 65535, 1, 65535, 64, 0, A + 2 * GB, None) == 2
+    assert lib.ba_qk_int_dot(A, A + GB, 1, 1, 65535, 64, 0x100 | 2, A + 2 * GB + 4, None) == 4
 
 
 def test_last_error_is_thread_local(lib):

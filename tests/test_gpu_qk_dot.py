@@ -1,6 +1,7 @@
 """GPU integer dots D_ij = <sign q_i, sign k_j> (ba_qk_int_dot) against the
-oracle, bit-exact, for both routes.  The fp4-MFMA route runs the device
-code of the fused kernel's QK step."""
+oracle, bit-exact, for the three routes (fp4 MFMA, int8 MFMA, VALU
+xor/popcount), as all pairs and as row sums.  The fp4-MFMA route runs the
+device code of the fused kernel's QK step."""
 
 import numpy as np
 import pytest
@@ -14,10 +15,13 @@ pytestmark = pytest.mark.gpu
 bq = pytest.importorskip("bit_qk_quantisation_amd")
 
 
-@pytest.mark.parametrize("route", [bq.ROUTE_MFMA_FP4, bq.ROUTE_VALU_POPCOUNT])
-@pytest.mark.parametrize("B,H,N,d", [(1, 1, 1, 8), (1, 2, 33, 32), (2, 1, 65, 64),
-                                     (1, 2, 196, 64), (1, 1, 100, 72), (1, 1, 64, 96),
-                                     (1, 2, 97, 128), (1, 1, 40, 200), (1, 1, 70, 256)])
+ROUTES = [bq.ROUTE_MFMA_FP4, bq.ROUTE_VALU_POPCOUNT, bq.ROUTE_MFMA_INT8]
+SHAPES = [(1, 1, 1, 8), (1, 2, 33, 32), (2, 1, 65, 64), (1, 2, 196, 64), (1, 1, 100, 72), (1, 1, 64, 96),
+          (1, 2, 97, 128), (1, 1, 40, 200), (1, 1, 70, 256)]
+
+
+@pytest.mark.parametrize("route", ROUTES)
+@pytest.mark.parametrize("B,H,N,d", SHAPES)
 def test_qk_dot_bit_exact(route, B, H, N, d):
     announce("qk_dot", route, B, H, N, d)
     inp = workloads.make_inputs(B, H, N, d, seed=200 + N + d, bias=False)
@@ -28,6 +32,20 @@ def test_qk_dot_bit_exact(route, B, H, N, d):
     want = oracle.sign_dots(qf, kf)
     assert np.array_equal(dots, want)
     assert np.array_equal(dots, oracle.sign_dots_from_bits(bits_u32(qb), bits_u32(kb), d))
+
+
+@pytest.mark.parametrize("route", ROUTES)
+@pytest.mark.parametrize("B,H,N,d", SHAPES + [(1, 1, 300, 64), (1, 1, 129, 128)])
+def test_qk_rowsum_bit_exact(route, B, H, N, d):
+    """Row sums sum_j D_ij, including ragged key tiles (keys past N must add
+    nothing) and query tiles."""
+    announce("qk_rowsum", route, B, H, N, d)
+    inp = workloads.make_inputs(B, H, N, d, seed=400 + N + d, bias=False)
+    qb, _ = bq.pack_signs(inp["q"].cuda())
+    kb, _ = bq.pack_signs(inp["k"].cuda())
+    sums = bq.qk_int_dot(qb, kb, d, route, rowsum=True).cpu().numpy().astype(np.int64)
+    want = oracle.sign_dots(np32(inp["q"]), np32(inp["k"])).sum(axis=-1)
+    assert np.array_equal(sums, want)
 
 
 def test_qk_dot_extremes():
