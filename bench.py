@@ -137,15 +137,15 @@ def _window_rows(N, gw):
 
 def pipelined(w, table=True):
     """Whether ba_attention_fwd runs the pipelined kernel (natural V, no V^T
-    from the prologue) on this workload: d in {32, 64, 128}, and table rows
+    from the prologue) on this workload: d in {32, 64, 72, 128}, and table rows
     whose per-tile window fits its buffers or no bias; shorter sequences with
     a table or no bias (N <= 256, d in {32, 64}) take the one-launch kernel."""
     rows = table and w.gw % 32 == 0
-    if w.d not in (32, 64, 128) or (table and not rows):
+    if w.d not in (32, 64, 72, 128) or (table and not rows):
         return False
     if w.N <= 256 and w.d in (32, 64) and not rows:
         return False
-    return not rows or _window_rows(w.N, w.gw) * 4 * _lpad(w.gw) <= (1664 if w.d <= 64 else 1152)
+    return not rows or _window_rows(w.N, w.gw) * 4 * _lpad(w.gw) <= (1664 if w.d <= 72 else 1152)
 
 
 def algorithmic_bytes(w, npad, dense_bytes=None):

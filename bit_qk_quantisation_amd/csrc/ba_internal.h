@@ -236,7 +236,7 @@ int small_static_lds(int cb, int mode);
 int launch_attention_small(const FwdArgs& a, int mode, void* stream);
 // The fused kernel of the 8-bit P.V forward (d <= 128; no dense bias).
 int launch_attention_int8(const FwdArgs& a, int mode, void* stream);
-// The pipelined fused kernel (flash.hip): d in {32, 64, 128}, table rows or
+// The pipelined fused kernel (flash.hip): d in {32, 64, 72, 128}, table rows or
 // no bias; reads V in its natural layout from a.v (strides a.vs), so the
 // prologue writes no V^T for it.  win_rows * 4 * Lpad floats of bias window
 // per key tile must fit its buffers.

@@ -50,27 +50,33 @@ constexpr float kFlashFastMax = 32.0f;
 
 template <int D>
 struct FDims {
-  static_assert(D == 32 || D == 64 || D == 128, "the pipelined kernel takes d in {32, 64, 128}");
+  static_assert(D == 32 || D == 64 || D == 72 || D == 128, "the pipelined kernel takes d in {32, 64, 72, 128}");
   static constexpr int NCH = (D + 63) / 64;      // 64-channel fp4 QK chunks
-  static constexpr int CB = D / 32;               // 32-channel output blocks
+  static constexpr int CB = (D + 31) / 32;        // 32-channel output blocks
+  // d % 32 != 0: the V^T operand's channel d is 1 for every key, so output
+  // channel d of P.V is the row sum and no row-sum product is needed
+  static constexpr bool XONES = D % 32 != 0;
+  static constexpr int PVS = CB + (XONES ? 0 : 1); // products per 16-key step
   static constexpr int ROW = 2 * D;               // bytes of one key's values
   static constexpr int VBYTES = 64 * ROW;         // V of one key tile
-  static constexpr int VPIECES = VBYTES / 1024;   // 1 KiB copy pieces
-  static constexpr int RPP = 1024 / ROW;          // key rows per piece
+  static constexpr int VPIECES = (VBYTES + 1023) / 1024;  // 1 KiB copy pieces
   static constexpr int CPR = ROW / 16;            // 16-byte chunks per row
+  static constexpr bool SWZ = (D & (D - 1)) == 0; // rows of a power-of-two size are swizzled
   static constexpr int KBYTES = NCH * 2048;       // fp4 key operands of one tile
   // floats of the table-row bias window of one tile (the host checks that
   // the grid's window fits)
-  static constexpr int WIN = D <= 64 ? 1664 : 1152;
+  static constexpr int WIN = D <= 72 ? 1664 : 1152;
   static constexpr int WAVES = D <= 64 ? 3 : 2;   // waves per SIMD the registers allow
 };
 
 // Position of 16-byte chunk j of key row r of a V tile: j ^ vswz(r).  The
 // transposing reads of one instruction cover 8 rows and 32 channels; with
-// this swizzle those 512 bytes fall on every LDS bank exactly twice.
+// this swizzle those 512 bytes fall on every LDS bank exactly twice.  Rows
+// of 144 bytes (d = 72) are not swizzled: 8 of them start 36 banks apart,
+// which spreads them already.
 template <int D>
 __device__ __forceinline__ int vswz(int r) {
-  return D == 32 ? 0 : (D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3));
+  return (D == 32 || !FDims<D>::SWZ) ? 0 : (D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3));
 }
 
 template <int D, int BIAS>
@@ -78,13 +84,16 @@ struct FBuf {
   v4i k[FDims<D>::NCH * 128];                  // fp4 key operands [chunk][key][half]
   uint32_t aks[192];                           // key scales as matrix operands: w0 w1 [64], w2 [64]
   v4u v[FDims<D>::VBYTES / 16];                // V rows, chunks swizzled
+  // ones channel: channels d .. d+3 of every key = 1 0 0 0, then 4 zeros
+  v4u vpad[FDims<D>::XONES ? 1 : 0];
   float win[BIAS == kBiasRows ? FDims<D>::WIN : 4];  // table-row bias window
 };
 
 template <int D>
 struct FAcc {
   v16f o[FDims<D>::CB];  // O^T: lane = query, register = channel
-  v4f l;                 // row sums (all four registers hold l of the lane's query)
+  v4f l;                 // row sums (all four registers hold l of the lane's query;
+                         // unused when the ones channel of O^T carries them)
 };
 
 // P.V of one finished block, waiting in registers for the next block.
@@ -105,9 +114,13 @@ struct FCtx {
   v8bf bq;                     // B operand of the scale product (the lane's aq split)
   int off_k, off_aks, off_win; // LDS byte offsets inside a buffer
   int off_v[FDims<D>::CB];     // byte offset of the lane's transposing reads
+  // ones channel: full addresses of the last block's reads (read k of a
+  // block takes rows 8 k .. 8 k + 7), pointing at the constant piece for
+  // channels past d
+  int off_vx[FDims<D>::XONES ? 8 : 1];
   int yq_lo;
   rsrc_t krs, ars, vrs, brs;   // sources of the tile copies
-  uint32_t voff;               // the lane's byte offset inside a V copy piece
+  uint32_t voff[FDims<D>::SWZ ? 1 : (FDims<D>::VPIECES + 3) / 4];  // the lane's byte offsets in its V pieces
   uint32_t vsn;                // bytes from one key's values to the next
   int win_bytes;
 };
@@ -161,15 +174,13 @@ __device__ __forceinline__ v3f fmax3_block(float x, float y, float z, float* red
 }
 
 // ------------------------------------------------------------------ setup --
-// The workgroup's (b, h) and query tile, the lane's packed query, LDS
-// offsets, copy sources and the logit bound M (log2 units).
+// The workgroup's (b, h) and query tile, LDS offsets and copy sources.
 template <int D, int BIAS>
-__device__ __forceinline__ float flash_setup(FCtx<D>& c, const FwdArgs& a, float* red) {
+__device__ __forceinline__ void flash_index(FCtx<D>& c, const FwdArgs& a) {
   using F = FDims<D>;
   c.a = &a;
-  const int tid = threadIdx.x;
-  c.lane = tid & 63;
-  c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  c.lane = threadIdx.x & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   c.li = c.lane & 31;
   c.lh = c.lane >> 5;
   int wg = blockIdx.x;
@@ -181,48 +192,10 @@ __device__ __forceinline__ float flash_setup(FCtx<D>& c, const FwdArgs& a, float
   c.bh = wg / a.nqt;
   const int qt = wg - c.bh * a.nqt;
   c.head = c.bh % a.H;
-  const int b = c.bh / a.H;
   c.q0 = qt * kBM;
   c.qi = c.q0 + c.wave * 32 + c.li;
 
-  // The lane's query: lane (li, lh) forms sign words 2 ch + lh of query qi
-  // and the sum of |q| over them; the partner lane l ^ 32 holds the other
-  // words, so the two partial sums give alpha_q = mean |q|.  Queries past N
-  // are zero (scale 0).
-  float qpart = 0.0f;
-  {
-    const uint16_t* qrow = a.q + token_offset(a.qs, b, c.head, c.qi < a.N ? c.qi : 0);
-#pragma unroll
-    for (int ch = 0; ch < F::NCH; ++ch) {
-      const int word = 2 * ch + c.lh;
-      uint32_t w = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int c0 = 32 * word + 8 * k;
-        if (c.qi < a.N && c0 < D) {
-          float part;
-          w |= chunk_signs(*reinterpret_cast<const uint4*>(qrow + c0), part) << (8 * k);
-          qpart += part;
-        }
-      }
-      c.qop[ch] = expand_signs_fp4(w, fp4_magnitude(word_valid(D, word)));
-    }
-  }
-  const float alpha_q = sum_halves(qpart) / static_cast<float>(D);
-  c.aq = alpha_q * a.qscale;
-
-  // Row-sum operand: lane l supplies A row l % 16 for k-slots 8 (l / 16) ..;
-  // those slots hold P of query 16 ((l / 16) % 2) + column, so a 1 where
-  // (l / 16) % 2 == ((l % 16) / 4) % 2 makes output row r sum the P of query
-  // 16 ((r / 4) % 2) + column: every output register of lane l is l of its
-  // query l % 32.
-  {
-    const bool one = ((c.lane >> 4) & 1) == (((c.lane & 15) >> 2) & 1);
-    const __bf16 x = one ? (__bf16)1.0f : (__bf16)0.0f;
-    c.ones = v8bf{x, x, x, x, x, x, x, x};
-  }
-  c.bq = __builtin_bit_cast(v8bf, scale_split_b(c.aq, c.lh == 0));
-
+  const int b = c.bh / a.H;
   c.off_k = (c.li * 2 + c.lh) * 16;
   c.off_aks = c.li * 8;   // A row li of the scale product: key li of the block
   {
@@ -237,6 +210,16 @@ __device__ __forceinline__ float flash_setup(FCtx<D>& c, const FwdArgs& a, float
     for (int cb = 0; cb < F::CB; ++cb) {
       const int ch0 = 32 * cb + 16 * (g & 1) + 4 * m;
       c.off_v[cb] = row * F::ROW + (((ch0 >> 3) ^ vswz<D>(row)) << 4) + ((ch0 >> 2) & 1) * 8;
+    }
+    if (F::XONES) {
+      // the last block's channels past d come from the constant piece after
+      // the tile (1 for channel d, 0 beyond), whatever the key row
+      const int ch0 = 32 * (F::CB - 1) + 16 * (g & 1) + 4 * m;
+      const int pad = F::VBYTES + (ch0 == D ? 0 : 8);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) c.off_vx[k] = ch0 < D ? c.off_v[F::CB - 1] + 8 * k * F::ROW : pad;
+    } else {
+      c.off_vx[0] = 0;
     }
   }
   c.off_win = 0;
@@ -258,9 +241,15 @@ __device__ __forceinline__ float flash_setup(FCtx<D>& c, const FwdArgs& a, float
   c.vsn = static_cast<uint32_t>(a.vs.sn * 2);
   c.vrs = make_rsrc(a.v + token_offset(a.vs, b, c.head, 0),
                     static_cast<uint32_t>((static_cast<int64_t>(a.N - 1) * a.vs.sn + D) * 2));
-  {
-    const int r = c.lane / F::CPR, pos = c.lane % F::CPR;
-    c.voff = static_cast<uint32_t>(r) * c.vsn + static_cast<uint32_t>((pos ^ vswz<D>(r)) << 4);
+  // lane l of piece p copies 16-byte chunk e = 64 p + l of the tile: row
+  // e / CPR, chunk e % CPR (read from the swizzled position, so that the
+  // LDS copy, written in chunk order, holds each row swizzled).  Power-of-
+  // two rows: the piece's first row goes in the scalar offset and voff[0]
+  // serves every piece.
+#pragma unroll
+  for (int j = 0; j < (F::SWZ ? 1 : (F::VPIECES + 3) / 4); ++j) {
+    const int e = F::SWZ ? c.lane : 64 * (c.wave + 4 * j) + c.lane, r = e / F::CPR, pos = e % F::CPR;
+    c.voff[j] = static_cast<uint32_t>(r) * c.vsn + static_cast<uint32_t>((pos ^ vswz<D>(r)) << 4);
   }
   c.brs = c.ars;
   c.win_bytes = 0;
@@ -271,13 +260,89 @@ __device__ __forceinline__ float flash_setup(FCtx<D>& c, const FwdArgs& a, float
     c.win_bytes = a.win_rows * 16 * a.Lpad;
   }
 
-  // logit bound
-  const int nblk = a.Npad / 64;
-  float km = 0.0f, bm = 0.0f;
-  for (int e = tid; e < nblk; e += kThreads) km = fmaxf(km, a.kmax_blk[static_cast<int64_t>(c.bh) * nblk + e]);
+}
+
+// What the query side needs from global memory, loaded before the first
+// tile copies are issued so that those stay in flight while it is used:
+// the lane's 8-channel chunks of its query and the inputs of the logit bound.
+template <int D>
+struct FQin {
+  uint4 q[FDims<D>::NCH][4];
+  float km, bm;
+};
+
+template <int D, int BIAS>
+__device__ __forceinline__ void flash_query_loads(const FCtx<D>& c, const FwdArgs& a, FQin<D>& in) {
+  using F = FDims<D>;
+  const int b = c.bh / a.H;
+  const uint16_t* qrow = a.q + token_offset(a.qs, b, c.head, c.qi < a.N ? c.qi : 0);
+#pragma unroll
+  for (int ch = 0; ch < F::NCH; ++ch)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c0 = 32 * (2 * ch + c.lh) + 8 * k;
+      in.q[ch][k] = make_uint4(0u, 0u, 0u, 0u);
+      if (c.qi < a.N && c0 < D) in.q[ch][k] = *reinterpret_cast<const uint4*>(qrow + c0);
+    }
+  // one load per thread here, with no wait on it; the rest, for sequences
+  // past 16384 keys or grids past 128 rows, in flash_queries
+  const int tid = threadIdx.x, nblk = a.Npad / 64;
+  in.km = tid < nblk ? a.kmax_blk[static_cast<int64_t>(c.bh) * nblk + tid] : 0.0f;
+  in.bm = 0.0f;
   if (BIAS == kBiasRows) {
     const int rows = 2 * a.gh - 1;
-    for (int e = tid; e < rows; e += kThreads) bm = fmaxf(bm, a.bias_row_max[c.head * rows + e]);
+    in.bm = tid < rows ? a.bias_row_max[c.head * rows + tid] : 0.0f;
+  }
+}
+
+// The lane's packed query, its scale and operands, and the logit bound M
+// (log2 units).
+template <int D, int BIAS>
+__device__ __forceinline__ float flash_queries(FCtx<D>& c, const FwdArgs& a, const FQin<D>& in, float* red) {
+  using F = FDims<D>;
+  // The lane's query: lane (li, lh) forms sign words 2 ch + lh of query qi
+  // and the sum of |q| over them; the partner lane l ^ 32 holds the other
+  // words, so the two partial sums give alpha_q = mean |q|.  Queries past N
+  // are zero (scale 0).
+  float qpart = 0.0f;
+#pragma unroll
+  for (int ch = 0; ch < F::NCH; ++ch) {
+    const int word = 2 * ch + c.lh;
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (c.qi < a.N && 32 * word + 8 * k < D) {
+        float part;
+        w |= chunk_signs(in.q[ch][k], part) << (8 * k);
+        qpart += part;
+      }
+    }
+    c.qop[ch] = expand_signs_fp4(w, fp4_magnitude(word_valid(D, word)));
+  }
+  const float alpha_q = sum_halves(qpart) / static_cast<float>(D);
+  c.aq = alpha_q * a.qscale;
+
+  // Row-sum operand: lane l supplies A row l % 16 for k-slots 8 (l / 16) ..;
+  // those slots hold P of query 16 ((l / 16) % 2) + column, so a 1 where
+  // (l / 16) % 2 == ((l % 16) / 4) % 2 makes output row r sum the P of query
+  // 16 ((r / 4) % 2) + column: every output register of lane l is l of its
+  // query l % 32.
+  {
+    const bool one = ((c.lane >> 4) & 1) == (((c.lane & 15) >> 2) & 1);
+    const __bf16 x = one ? (__bf16)1.0f : (__bf16)0.0f;
+    c.ones = v8bf{x, x, x, x, x, x, x, x};
+  }
+  c.bq = __builtin_bit_cast(v8bf, scale_split_b(c.aq, c.lh == 0));
+
+  float km = in.km, bm = in.bm;
+  {
+    const int tid = threadIdx.x, nblk = a.Npad / 64;
+    for (int e = tid + kThreads; e < nblk; e += kThreads)
+      km = fmaxf(km, a.kmax_blk[static_cast<int64_t>(c.bh) * nblk + e]);
+    if (BIAS == kBiasRows) {
+      const int rows = 2 * a.gh - 1;
+      for (int e = tid + kThreads; e < rows; e += kThreads) bm = fmaxf(bm, a.bias_row_max[c.head * rows + e]);
+    }
   }
   const v3f mx = fmax3_block(km, bm, alpha_q, red);
   return a.qscale * mx[2] * mx[0] * static_cast<float>(D) + mx[1];
@@ -293,20 +358,27 @@ template <int D, int BIAS>
 __device__ __forceinline__ void flash_copy(const FCtx<D>& c, FBuf<D, BIAS>& tb, FRun& run, FWin& w) {
   using F = FDims<D>;
   const FwdArgs& a = *c.a;
-  const uint32_t k0 = static_cast<uint32_t>(run.k0);
+  // (the scalar offsets go through readfirstlane: the compiler cannot tell
+  // that they are uniform and would otherwise loop over their lane values)
+  const uint32_t k0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(run.k0));
   char* kdst = reinterpret_cast<char*>(&tb.k[0]);
 #pragma unroll
   for (int j = 0; j < (2 * F::NCH + 3) / 4; ++j)
     if (c.wave + 4 * j < 2 * F::NCH)
       dma16(c.krs, kdst + (c.wave + 4 * j) * 1024, static_cast<uint32_t>(c.lane * 16),
-            k0 / kBN * F::KBYTES + static_cast<uint32_t>((c.wave + 4 * j) * 1024));
+            __builtin_amdgcn_readfirstlane(k0 / kBN * F::KBYTES + static_cast<uint32_t>((c.wave + 4 * j) * 1024)));
   char* vdst = reinterpret_cast<char*>(&tb.v[0]);
 #pragma unroll
   for (int j = 0; j < (F::VPIECES + 3) / 4; ++j) {
     const int p = c.wave + 4 * j;
-    if (p < F::VPIECES) dma16(c.vrs, vdst + p * 1024, c.voff, (k0 + static_cast<uint32_t>(p * F::RPP)) * c.vsn);
+    // power-of-two rows: whole rows per piece, one lane offset for every
+    // piece and the piece's first row in the scalar offset
+    if (p < F::VPIECES)
+      dma16(c.vrs, vdst + p * 1024, F::SWZ ? c.voff[0] : c.voff[j],
+            __builtin_amdgcn_readfirstlane((k0 + static_cast<uint32_t>(F::SWZ ? p * (1024 / F::ROW) : 0)) * c.vsn));
   }
-  if (c.wave == 3 && c.lane < 48) dma16(c.ars, &tb.aks[0], static_cast<uint32_t>(c.lane * 16), k0 * 12);
+  if (c.wave == 3 && c.lane < 48)
+    dma16(c.ars, &tb.aks[0], static_cast<uint32_t>(c.lane * 16), __builtin_amdgcn_readfirstlane(k0 * 12));
   run.k0 += kBN;
   if (BIAS == kBiasRows) {
     int ky[2], kx[2];
@@ -322,8 +394,13 @@ __device__ __forceinline__ void flash_copy(const FCtx<D>& c, FBuf<D, BIAS>& tb, 
     }
     // window rows start at dy = yq_lo - yk_hi; yk_hi is the row of block 1
     const int dy0 = c.yq_lo - ky[1] + a.gh - 1 + kBiasPadRows;
-    const uint32_t bs = static_cast<uint32_t>(dy0 * 16 * a.Lpad);
-    const uint32_t loff = static_cast<uint32_t>(c.wave * 1024 + c.lane * 16);
+    const uint32_t bs = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(dy0 * 16 * a.Lpad));
+    // the lane's offset, formed here from the thread index: held across the
+    // loop it would be one more register, which the allocator spills (and a
+    // reload from scratch waits for every copy in flight)
+    uint32_t tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const uint32_t loff = tid * 16;
     char* bdst = reinterpret_cast<char*>(&tb.win[0]);
 #pragma unroll
     for (int j = 0; j < (F::WIN * 4 + 4095) / 4096; ++j)
@@ -379,9 +456,13 @@ __device__ __forceinline__ void flash_vops(const FCtx<D>& c, const FBuf<D, BIAS>
   const char* vb = reinterpret_cast<const char*>(&tb.v[0]);
 #pragma unroll
   for (int cb = 0; cb < F::CB; ++cb) {
-    const int base = c.off_v[cb] + (32 * blk + 16 * st) * F::ROW;
-    const v2u lo = tr_read(vb + base);
-    const v2u hi = tr_read(vb + base + 8 * F::ROW);
+    int a_lo = c.off_v[cb] + (32 * blk + 16 * st) * F::ROW, a_hi = a_lo + 8 * F::ROW;
+    if (F::XONES && cb == F::CB - 1) {
+      a_lo = c.off_vx[4 * blk + 2 * st];
+      a_hi = c.off_vx[4 * blk + 2 * st + 1];
+    }
+    const v2u lo = tr_read(vb + a_lo);
+    const v2u hi = tr_read(vb + a_hi);
     pp.vop[st][cb] = __builtin_bit_cast(v8bf, v4u{lo[0], lo[1], hi[0], hi[1]});
   }
 }
@@ -408,12 +489,12 @@ __device__ __forceinline__ v16f flash_scales(const FCtx<D>& c, const v4u& aop) {
 // chunks of the next block, the pending block's second step.
 template <int D>
 struct FOrder {
-  static constexpr int CB = FDims<D>::CB, NCH = FDims<D>::NCH;
-  static constexpr int NM = 2 * (CB + 1) + NCH;  // instructions per block
-  static constexpr int QK0 = CB + 1;              // first QK chunk
-  static constexpr int QKL = CB + NCH;            // last QK chunk
+  static constexpr int CB = FDims<D>::CB, NCH = FDims<D>::NCH, PVS = FDims<D>::PVS;
+  static constexpr int NM = 2 * PVS + NCH;        // instructions per block
+  static constexpr int QK0 = PVS;                 // first QK chunk
+  static constexpr int QKL = PVS + NCH - 1;       // last QK chunk
   static constexpr int LASTV0 = CB - 1;           // last product reading step 0's V^T
-  static constexpr int LASTV1 = 2 * CB + NCH;     // last product reading step 1's V^T
+  static constexpr int LASTV1 = PVS + NCH + CB - 1;  // last product reading step 1's V^T
 };
 
 template <int D>
@@ -437,7 +518,7 @@ __device__ __forceinline__ void flash_mfma(int m, const FCtx<D>& c, const FPend<
     sn = mfma_signs_32x32x64(kop[ch], c.qop[ch], sn);
     if (m == O::QKL) flash_qk_anchor(sn);
   } else {
-    flash_pv<D>(1, m - O::QKL - 1, c, old, acc);
+    flash_pv<D>(1, m - O::QKL - 1, c, old, acc);  // m - QKL - 1 < PVS
   }
 }
 
@@ -610,10 +691,12 @@ __device__ __forceinline__ void flash_tile(const FCtx<D>& c, const FBuf<D, BIAS>
   }
 }
 
-// All keys; returns the offset the sums are taken against (log2 units).
+// All keys, after the copies of tiles 0 and 1 into b0 and b1 (run names
+// tile 2; w0, w1 hold the window offsets of tiles 0 and 1); returns the
+// offset the sums are taken against (log2 units).
 template <int D, int BIAS, bool EXACT>
 __device__ __forceinline__ float flash_pass(const FCtx<D>& c, FBuf<D, BIAS>& b0, FBuf<D, BIAS>& b1,
-                                            FBuf<D, BIAS>& b2, FAcc<D>& acc) {
+                                            FBuf<D, BIAS>& b2, FAcc<D>& acc, FRun run, FWin w0, FWin w1) {
   const FwdArgs& a = *c.a;
 #pragma unroll
   for (int cb = 0; cb < FDims<D>::CB; ++cb) acc.o[cb] = v16f{};
@@ -624,17 +707,8 @@ __device__ __forceinline__ float flash_pass(const FCtx<D>& c, FBuf<D, BIAS>& b0,
   prio.level = 3;
   for (int i = 0; i < 3; ++i) prio.th[i] = a.prio_balance ? ((5 + i) * nkt + 7) / 8 : nkt;
   if (a.prio_balance) __builtin_amdgcn_s_setprio(3);
-  FRun run;
-  run.k0 = 0;
-  run.by = 0;
-  run.bx = 0;
-  FWin w0, w1, w2;
+  FWin w2;
   w2.u[0] = w2.u[1] = 0;
-  flash_copy(c, b0, run, w0);
-  if (nkt > 1)
-    flash_copy(c, b1, run, w1);
-  else
-    w1 = w2;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   v16f s0, s1 = v16f{};
@@ -669,7 +743,7 @@ __device__ __forceinline__ float flash_pass(const FCtx<D>& c, FBuf<D, BIAS>& b0,
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
-    for (int i = 0; i <= FDims<D>::CB; ++i) flash_pv<D>(st, i, c, ppa, acc);
+    for (int i = 0; i < FDims<D>::PVS; ++i) flash_pv<D>(st, i, c, ppa, acc);
   return mrow;
 }
 
@@ -679,9 +753,16 @@ __device__ __forceinline__ float flash_pass(const FCtx<D>& c, FBuf<D, BIAS>& b0,
 template <int D>
 __device__ __forceinline__ void flash_epilogue(const FCtx<D>& c, const FwdArgs& a, FAcc<D>& acc, float mrow,
                                                unsigned char* stage0, unsigned char* stage1) {
+  using F = FDims<D>;
 #pragma unroll
-  for (int cb = 0; cb < FDims<D>::CB; ++cb) pin_uniform(acc.o[cb]);
+  for (int cb = 0; cb < F::CB; ++cb) pin_uniform(acc.o[cb]);
   float l = acc.l[0];
+  if (F::XONES) {
+    // output channel d: block CB-1, register 4 (ch / 8) + ch % 4 of the lanes
+    // of half (ch / 4) % 2, ch = d - 32 (CB-1)
+    constexpr int ch = D - 32 * (F::CB - 1), r = 4 * (ch / 8) + ch % 4, half = (ch / 4) % 2;
+    l = __shfl(acc.o[F::CB - 1][r], c.li + 32 * half, 64);
+  }
   {
     float e = l;
     asm volatile("" : "+v"(e));
@@ -699,6 +780,7 @@ __device__ __forceinline__ void flash_epilogue(const FCtx<D>& c, const FwdArgs& 
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int c0 = cb * 32 + 8 * b + 4 * c.lh;
+      if (c0 >= D) continue;  // padded channels (the ones channel among them)
       v2u w;
       w[0] = pack_bf16x2(acc.o[cb][4 * b + 0] * inv, acc.o[cb][4 * b + 1] * inv);
       w[1] = pack_bf16x2(acc.o[cb][4 * b + 2] * inv, acc.o[cb][4 * b + 3] * inv);
@@ -723,15 +805,35 @@ flash_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) FBuf<D, BIAS> b1;
   __shared__ __attribute__((aligned(16))) FBuf<D, BIAS> b2;
   FCtx<D> c;
-  // the setup's reduction borrows b2, which the first copies leave alone
+  flash_index<D, BIAS>(c, a);
+  // The query side's global loads go out first and the copies of tiles 0
+  // and 1 after them, so that the copies are still in flight while the
+  // queries are packed and the logit bound is reduced.
+  FQin<D> qin;
+  flash_query_loads<D, BIAS>(c, a, qin);
+  FRun run;
+  run.k0 = 0;
+  run.by = 0;
+  run.bx = 0;
+  FWin w0, w1;
+  flash_copy(c, b0, run, w0);
+  w1.u[0] = w1.u[1] = 0;
+  if (a.N > kBN) flash_copy(c, b1, run, w1);
+  if (FDims<D>::XONES && threadIdx.x < 3) {
+    // the constant piece of each buffer (the first barrier of the key loop
+    // orders these writes before every read)
+    FBuf<D, BIAS>& pb = threadIdx.x == 0 ? b0 : (threadIdx.x == 1 ? b1 : b2);
+    pb.vpad[0] = v4u{0x3f80u, 0u, 0u, 0u};
+  }
+  // the bound's reduction borrows b2, which the first copies leave alone
   // (it takes tile 2, after several barriers)
-  const float M = flash_setup<D, BIAS>(c, a, reinterpret_cast<float*>(&b2.v[0]));
+  const float M = flash_queries<D, BIAS>(c, a, qin, reinterpret_cast<float*>(&b2.v[0]));
   FAcc<D> acc;
   float mrow;
   if (M <= kFlashFastMax)  // false for NaN as well
-    mrow = flash_pass<D, BIAS, false>(c, b0, b1, b2, acc);
+    mrow = flash_pass<D, BIAS, false>(c, b0, b1, b2, acc, run, w0, w1);
   else
-    mrow = flash_pass<D, BIAS, true>(c, b0, b1, b2, acc);
+    mrow = flash_pass<D, BIAS, true>(c, b0, b1, b2, acc, run, w0, w1);
   flash_epilogue<D>(c, a, acc, mrow, reinterpret_cast<unsigned char*>(&b0.v[0]),
                     reinterpret_cast<unsigned char*>(&b1.v[0]));
 }
@@ -755,11 +857,11 @@ int launch_flash_d(const FwdArgs& a, int mode, void* stream) {
 }  // namespace
 
 bool flash_supported(int d, int mode, int win_rows, int Lpad) {
-  if (d != 32 && d != 64 && d != 128) return false;
+  if (d != 32 && d != 64 && d != 72 && d != 128) return false;
   if (mode == kBiasNone) return true;
   if (mode != kBiasRows) return false;
   const int win = win_rows * 4 * Lpad;
-  return win <= (d <= 64 ? FDims<64>::WIN : FDims<128>::WIN);
+  return win <= (d <= 72 ? FDims<64>::WIN : FDims<128>::WIN);
 }
 
 int flash_static_lds(int d, int mode) {
@@ -767,16 +869,19 @@ int flash_static_lds(int d, int mode) {
   switch (d) {
     case 32: return rows ? flash_lds<32, kBiasRows>() : flash_lds<32, kBiasNone>();
     case 64: return rows ? flash_lds<64, kBiasRows>() : flash_lds<64, kBiasNone>();
+    case 72: return rows ? flash_lds<72, kBiasRows>() : flash_lds<72, kBiasNone>();
     default: return rows ? flash_lds<128, kBiasRows>() : flash_lds<128, kBiasNone>();
   }
 }
 
 int flash_waves_per_simd(int d) { return d <= 64 ? FDims<64>::WAVES : FDims<128>::WAVES; }
+static_assert(FDims<72>::WAVES == FDims<128>::WAVES, "d = 72 takes the d = 128 budget");
 
 int launch_flash(const FwdArgs& a, int mode, void* stream) {
   switch (a.d) {
     case 32: return launch_flash_d<32>(a, mode, stream);
     case 64: return launch_flash_d<64>(a, mode, stream);
+    case 72: return launch_flash_d<72>(a, mode, stream);
     case 128: return launch_flash_d<128>(a, mode, stream);
     default: return static_cast<int>(hipErrorInvalidValue);
   }

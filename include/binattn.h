@@ -130,7 +130,7 @@ size_t ba_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int gh, int gw
  *              256-byte aligned.  Its contents on entry do not matter, and it
  *              must not be shared by calls that may overlap on the GPU.
  * Two kernels are enqueued: the sign/scale pack of K (with the bias rows),
- * then the fused attention kernel, which packs Q.  For d in {32, 64, 128}
+ * then the fused attention kernel, which packs Q.  For d in {32, 64, 72, 128}
  * with the table rows (gw % 32 == 0, window small enough) or no bias, the
  * fused kernel is the pipelined one, which reads V where it lies; otherwise
  * the prologue also writes V^T into the workspace for it.  For N <= 256,

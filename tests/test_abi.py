@@ -94,23 +94,23 @@ def _window_rows(N, gw):
 
 
 def _pipelined_shape(N, d, gh, gw, rows, lpad):
-    """The pipelined kernel takes d in {32, 64, 128} with table rows whose
+    """The pipelined kernel takes d in {32, 64, 72, 128} with table rows whose
     window fits its buffers, or without a bias."""
-    if d not in (32, 64, 128) or (gh and not rows):
+    if d not in (32, 64, 72, 128) or (gh and not rows):
         return False
-    return not rows or _window_rows(N, gw) * 4 * lpad <= (1664 if d <= 64 else 1152)
+    return not rows or _window_rows(N, gw) * 4 * lpad <= (1664 if d <= 72 else 1152)
 
 
 def _prepared_pipelined(N, d, gh, gw, rows, lpad):
     """The prepared forward runs the pipelined kernel (and the workspace holds
-    a natural copy of V) for d in {32, 64, 128} with table rows whose window
+    a natural copy of V) for d in {32, 64, 72, 128} with table rows whose window
     fits its buffers, or without a bias, unless the whole forward would run
     as one launch (N <= 256, d in {32, 64}, no table rows)."""
-    if d not in (32, 64, 128) or (gh and not rows):
+    if d not in (32, 64, 72, 128) or (gh and not rows):
         return False
     if N <= 256 and d in (32, 64) and not rows:
         return False
-    return not rows or _window_rows(N, gw) * 4 * lpad <= (1664 if d <= 64 else 1152)
+    return not rows or _window_rows(N, gw) * 4 * lpad <= (1664 if d <= 72 else 1152)
 
 
 @pytest.mark.parametrize("shape", [(1, 3, 196, 64, 14, 14), (32, 12, 196, 64, 14, 14),
