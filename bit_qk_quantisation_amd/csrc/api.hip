@@ -69,22 +69,31 @@ int64_t row_pad(int gw) {
   return l;
 }
 
+// Any other grid: the prologue writes the table out as a dense bias
+// [H][Npad][Npad] in the workspace, which the dense-bias kernel reads.  Not a
+// kernel mode: the plan turns it into kBiasDense.
+constexpr int kModeExpand = 4;
+
 // How the fused kernel reads the bias: table rows staged per key tile (grid
 // width a multiple of 32, window small enough for the tile prefetch), the
-// whole table in LDS (small tables), or no bias.  -1: unsupported.
+// whole table in LDS (small tables), the table expanded into a dense bias
+// (every other grid, up to 46336 tokens: the dense kernel addresses one
+// head's bias with 32-bit offsets), or no bias.  -1: unsupported.
 int choose_mode(bool has_bias, int gh, int gw, int64_t N) {
   if (!has_bias) return ba::kBiasNone;
   if (gw % 32 == 0 && window_rows(N, gw) > 0 && window_rows(N, gw) <= ba::kBiasPadRows &&
       window_rows(N, gw) * 4 * row_pad(gw) <= ba::kMaxWindowFloats && row_pad(gw) <= 64 * ba::kBiasPieces)
     return ba::kBiasRows;
   if (static_cast<int64_t>(2 * gh - 1) * (2 * gw - 1) * 4 <= 48 * 1024) return ba::kBiasTable;
+  const int64_t npad = round_up(N, ba::kNAlign);
+  if ((npad * npad + npad) * 2 < (int64_t{1} << 32)) return kModeExpand;
   return -1;
 }
 
 // Byte offsets of the workspace sections of ba_attention_fwd.
 struct Layout {
   int64_t Npad, W, dpad, Lpad;
-  int64_t kop, alpha_k, kmax, vt, vq, vpart, vscale, vcsum, bias4, rowmax, vnat, aks, total;
+  int64_t kop, alpha_k, kmax, vt, vq, vpart, vscale, vcsum, bias4, rowmax, vnat, aks, expand, total;
   int mode;
   bool flash_prepared;  // the prepared forward runs the pipelined kernel on vnat
   bool no_vt;           // compact layout without V^T: only the pipelined kernel can run on it
@@ -142,6 +151,8 @@ Layout layout(int64_t B, int64_t H, int64_t N, int d, bool has_bias, int gh, int
   const bool flash_shape = !int8pv && L.mode >= 0 &&
                            ba::flash_supported(d, L.mode, rows0 ? window_rows(N, gw) : 0, static_cast<int>(L.Lpad));
   L.aks = take(flash_shape ? BH * L.Npad * 12 : 0);
+  // the table written out as a dense bias, shared by the batch
+  L.expand = take(L.mode == kModeExpand ? H * L.Npad * L.Npad * 2 : 0);
   L.total = off;
   return L;
 }
@@ -377,7 +388,7 @@ size_t ba_workspace_bytes_int8pv(int64_t B, int64_t H, int64_t N, int d, int gh,
   const bool has_bias = gh > 0 || gw > 0;
   if (has_bias && (gh < 1 || gw < 1 || static_cast<int64_t>(gh) * gw != N)) return 0;
   const Layout L = layout(B, H, N, d, has_bias, gh, gw, true);
-  if (L.mode < 0) return 0;
+  if (L.mode < 0 || L.mode == kModeExpand) return 0;
   return static_cast<size_t>(L.total);
 }
 
@@ -480,11 +491,15 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
       return fail(BA_ERR_UNSUPPORTED, "the 8-bit P.V forward supports N <= 65536 (exact int32 sums), N = %lld",
                   (long long)N);
   }
-  const int mode = dense ? static_cast<int>(ba::kBiasDense) : choose_mode(bias != nullptr, gh, gw, N);
+  int mode = dense ? static_cast<int>(ba::kBiasDense) : choose_mode(bias != nullptr, gh, gw, N);
   if (mode < 0)
     return fail(BA_ERR_UNSUPPORTED,
-                "bias grid %dx%d: the table rows do not fit the tile window and the table exceeds 48 KiB",
-                gh, gw);
+                "bias grid %dx%d: the table rows do not fit the tile window, the table exceeds 48 KiB and its "
+                "dense form would span 4 GiB or more per head", gh, gw);
+  const bool expand = mode == kModeExpand;
+  if (expand && int8pv)
+    return fail(BA_ERR_UNSUPPORTED, "bias grid %dx%d: the 8-bit P.V forward takes table rows (gw %% 32 == 0) or "
+                "tables of at most 48 KiB", gh, gw);
   const Layout L = layout(B, H, N, d, bias != nullptr, dense ? 0 : gh, dense ? 0 : gw, int8pv, compact);
   if (!workspace) return fail(BA_ERR_WORKSPACE, "workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -500,6 +515,12 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   const int64_t BH = B * H;
+  DenseBias expanded{};
+  if (expand) {  // the fused kernel reads the prologue's dense form of the table
+    expanded = DenseBias{ws + L.expand, 0, L.Npad * L.Npad, L.Npad};
+    dense = &expanded;
+    mode = ba::kBiasDense;
+  }
   ba::FwdArgs& f = plan->f;
   f = ba::FwdArgs{};
   f.q = static_cast<const uint16_t*>(q);
@@ -618,7 +639,12 @@ ba_status make_plan(const void* q, const void* k, const void* v, bool kv, const 
     p.kv.vscale = reinterpret_cast<float*>(ws + L.vscale);
     p.kv.vcsum = vcsum;
   }
-  const int64_t pblocks = p.kv_blocks + pb.bias_blocks + pb.vstat_blocks;
+  if (expand) {
+    p.expand = ba::ExpandJob{static_cast<const uint16_t*>(bias), reinterpret_cast<uint16_t*>(ws + L.expand), gh, gw,
+                             f.N, f.Npad};
+    p.expand_blocks = kv ? H * L.Npad : 0;
+  }
+  const int64_t pblocks = p.kv_blocks + pb.bias_blocks + pb.vstat_blocks + p.expand_blocks;
   if (pblocks > 0x7fffffff) return fail(BA_ERR_SHAPE, "problem too large");
   plan->mode = mode;
   plan->int8pv = int8pv;
@@ -773,6 +799,9 @@ ba_status run_backward(const void* q, const void* k, const void* v, const void* 
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || (dtable && !aligned16(dtable)))
     return fail(BA_ERR_ALIGN, "dout, dq, dk, dv and dtable must be 16-byte aligned");
   const BwdLayout BL = bwd_layout(B, H, N, d, bias != nullptr, gh, gw);
+  if (BL.fwd.mode == kModeExpand)
+    return fail(BA_ERR_UNSUPPORTED, "bias grid %dx%d: the backward takes table rows (gw %% 32 == 0) or tables of at "
+                "most 48 KiB", gh, gw);
   if (ws_bytes < static_cast<size_t>(BL.total))
     return fail(BA_ERR_WORKSPACE, "workspace too small: %zu < %lld bytes", ws_bytes, (long long)BL.total);
   // the forward's plan validates q, k, v, the bias and the first part of the workspace
@@ -988,7 +1017,7 @@ size_t ba_workspace_bytes_bwd(int64_t B, int64_t H, int64_t N, int d, int gh, in
   const bool has_bias = gh > 0 || gw > 0;
   if (has_bias && (gh < 1 || gw < 1 || static_cast<int64_t>(gh) * gw != N)) return 0;
   const BwdLayout L = bwd_layout(B, H, N, d, has_bias, gh, gw);
-  if (L.fwd.mode < 0) return 0;
+  if (L.fwd.mode < 0 || L.fwd.mode == kModeExpand) return 0;
   return static_cast<size_t>(L.total);
 }
 

@@ -143,10 +143,21 @@ struct DtReduceJob {
   int B, H, nqt, gh, gw, prow, rows_mode;
 };
 
+// The relative-position table written out as a dense bias, for grids whose
+// table rows fit neither the pipelined kernel's window nor LDS whole:
+// out[h][i][j] = table[h][yi - yj + gh - 1][xi - xj + gw - 1] for i, j < N
+// (token t at (t / gw, t % gw)), 0 for i or j in [N, Npad).  One block per
+// (h, i) row.
+struct ExpandJob {
+  const uint16_t* table;  // bf16 [H][2gh-1][2gw-1]
+  uint16_t* out;          // bf16 [H][Npad][Npad]
+  int gh, gw, N, Npad;
+};
+
 // One launch runs the blocks of every job present (a job with 0 blocks is
 // absent), in this order: pack, key/value tiles, bias rows, value
 // statistics, the second bias rows, the table-gradient reduction, the
-// log-sum-exp conversion.
+// log-sum-exp conversion, the dense expansion of a table.
 struct PrologueArgs {
   PackJob pack;
   int64_t pack_blocks;
@@ -164,6 +175,8 @@ struct PrologueArgs {
   int64_t lse_blocks;
   DeltaJob delta;
   int64_t delta_blocks;
+  ExpandJob expand;
+  int64_t expand_blocks;
   int lds;  // dynamic LDS bytes per block
 };
 

@@ -440,6 +440,35 @@ __device__ void bias_block(const BiasJob& job, int64_t blk) {
   if (lane == 0 && inside) job.row_max[h * rows + dy] = m;
 }
 
+// ------------------------------------------------------------- expansion --
+// Row (h, i) of the dense bias (see ExpandJob): 8 consecutive keys per
+// thread and 16-byte stores.  Keys on one grid row read consecutive table
+// columns in reverse order (xi - xj falls as xj rises).
+__device__ void expand_row(const ExpandJob& j, int64_t blk) {
+  const int h = static_cast<int>(blk / j.Npad), i = static_cast<int>(blk - static_cast<int64_t>(h) * j.Npad);
+  const int rows = 2 * j.gh - 1, cols = 2 * j.gw - 1;
+  const uint16_t* tab = j.table + static_cast<int64_t>(h) * rows * cols;
+  uint16_t* out = j.out + (static_cast<int64_t>(h) * j.Npad + i) * j.Npad;
+  const int yi = i / j.gw, xi = i - yi * j.gw;
+  for (int j0 = 8 * threadIdx.x; j0 < j.Npad; j0 += 8 * kThreads) {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (i < j.N) {
+      int yj = j0 / j.gw, xj = j0 - yj * j.gw;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t val = 0u;
+        if (j0 + e < j.N) val = tab[(yi - yj + j.gh - 1) * cols + (xi - xj + j.gw - 1)];
+        w[e >> 1] |= val << (16 * (e & 1));
+        if (++xj == j.gw) {
+          xj = 0;
+          ++yj;
+        }
+      }
+    }
+    stream_out(out + j0, v4u{w[0], w[1], w[2], w[3]});
+  }
+}
+
 __global__ void __launch_bounds__(kThreads) prologue_kernel(PrologueArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int64_t blk = blockIdx.x;
@@ -561,12 +590,15 @@ __global__ void __launch_bounds__(kThreads) prologue_kernel(PrologueArgs a) {
     }
     const float sum = part + __shfl_xor(part, 1, 64);
     if (inrow && half == 0) j.delta[row] = valid ? sum : 0.0f;
+    return;
   }
+  blk -= a.delta_blocks;
+  if (blk < a.expand_blocks) expand_row(a.expand, blk);
 }
 
 int launch_prologue(const PrologueArgs& a, void* stream) {
   const int64_t blocks = a.pack_blocks + a.kv_blocks + a.bias_blocks + a.vstat_blocks + a.bias2_blocks +
-                        a.dtr_blocks + a.lse_blocks + a.delta_blocks;
+                        a.dtr_blocks + a.lse_blocks + a.delta_blocks + a.expand_blocks;
   hipLaunchKernelGGL(prologue_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), a.lds,
                      static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());

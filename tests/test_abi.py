@@ -58,9 +58,11 @@ def expected_workspace(B, H, N, d, gh=0, gw=0, int8pv=False):
     MFMA operands (32 bytes per 64 channels), the K scales, their maxima per
     64 tokens and V^T, per head
     padded to a multiple of 128 tokens, each section 256-byte aligned; plus,
-    for a grid width that is a multiple of 32, the float32 bias rows (4
-    shifted copies per row, each padded to 16 mod 64 floats, 8 padding rows
-    on each side) and their maxima."""
+    for a grid width that is a multiple of 32 and a key tile's window of at
+    most 8 rows and 2048 floats, the float32 bias rows (4 shifted copies per
+    row, each padded to 16 mod 64 floats, 8 padding rows on each side) and
+    their maxima; for other grids whose table exceeds 48 KiB of float32, the
+    table written out as a dense bias."""
     npad = _round(N, 128)
     W = (d + 31) // 32
     dpad = 32 * W
@@ -70,12 +72,15 @@ def expected_workspace(B, H, N, d, gh=0, gw=0, int8pv=False):
         secs += [B * H * dpad * npad, B * H * (npad // 64) * dpad * 4, B * H * dpad * 4, B * H * dpad * 4]
     else:
         secs.append(B * H * dpad * npad * 2)
-    rows = bool(gh) and gw % 32 == 0
     lpad = 0
-    if rows:
+    if gh and gw % 32 == 0:
         lpad = _round(2 * gw - 1 + 3, 4)
         while lpad % 64 != 16:
             lpad += 4
+    # table rows: a window of at most 8 rows and 2048 floats per key tile
+    rows = bool(gh) and gw % 32 == 0 and _window_rows(N, gw) <= 8 and _window_rows(N, gw) * 4 * lpad <= 2048 \
+        and lpad <= 64 * 5
+    if rows:
         secs.append(H * (2 * gh - 1 + 16) * 4 * lpad * 4)
         secs.append(H * (2 * gh - 1) * 4)
     if not int8pv and _prepared_pipelined(N, d, gh, gw, rows, lpad):
@@ -84,6 +89,9 @@ def expected_workspace(B, H, N, d, gh=0, gw=0, int8pv=False):
     if not int8pv and _pipelined_shape(N, d, gh, gw, rows, lpad):
         # the key scales as the pipelined kernel's matrix operands
         secs.append(B * H * npad * 12)
+    if gh and not rows and (2 * gh - 1) * (2 * gw - 1) * 4 > 48 * 1024:
+        # any other grid: the table written out as a dense bf16 bias per head
+        secs.append(H * npad * npad * 2)
     return sum(_round(s, 256) for s in secs)
 
 
@@ -115,7 +123,8 @@ def _prepared_pipelined(N, d, gh, gw, rows, lpad):
 
 @pytest.mark.parametrize("shape", [(1, 3, 196, 64, 14, 14), (32, 12, 196, 64, 14, 14),
                                    (8, 16, 1024, 72, 32, 32), (2, 12, 4096, 64, 64, 64),
-                                   (1, 16, 16384, 128, 128, 128), (2, 2, 100, 40, 0, 0)])
+                                   (1, 16, 16384, 128, 128, 128), (2, 2, 100, 40, 0, 0),
+                                   (1, 2, 10000, 64, 100, 100), (1, 1, 32768, 64, 128, 256)])
 def test_workspace_bytes(lib, shape):
     B, H, N, d, gh, gw = shape
     assert lib.ba_workspace_bytes(B, H, N, d, gh, gw) == expected_workspace(*shape)
@@ -162,8 +171,25 @@ def test_fwd_unsupported_d(lib, d):
 
 
 def test_fwd_unsupported_bias_table(lib):
-    # gw not a multiple of 32 and a table bigger than 48 KiB of float32
-    assert fwd(lib, bias=A + 5 * GB, gh=100, gw=70, N=7000) == 3
+    # gw not a multiple of 32, a table bigger than 48 KiB of float32, and a
+    # dense form of 4 GiB or more per head (N = 50000)
+    assert fwd(lib, bias=A + 5 * GB, gh=200, gw=250, N=50000) == 3
+    assert lib.ba_workspace_bytes(1, 2, 50000, 64, 200, 250) == 0
+
+
+def test_expanded_table_limits(lib):
+    """Grids that only the dense expansion takes: the forward accepts them
+    (it gets as far as the launch here, without a GPU), the 8-bit P.V forward
+    and the backward refuse them."""
+    tab = dict(bias=A + 5 * GB, gh=100, gw=70, N=7000)
+    assert fwd(lib, **tab) == 6
+    assert lib.ba_workspace_bytes_int8pv(1, 2, 7000, 64, 100, 70) == 0
+    assert lib.ba_workspace_bytes_bwd(1, 2, 7000, 64, 100, 70) == 0
+    assert lib.ba_attention_fwd_int8pv(A, A + GB, A + 2 * GB, A + 5 * GB, 100, 70, 1, 2, 7000, 64, 0.125,
+                                       A + 3 * GB, A + 4 * GB, 1 << 40, None) == 3
+    big = 1 << 40
+    assert lib.ba_attention_bwd(A, A + GB, A + 2 * GB, A + 5 * GB, 100, 70, 1, 2, 7000, 64, 0.125, A + 6 * GB,
+                                A + 7 * GB, A + 8 * GB, A + 9 * GB, None, A + 4 * GB, big, None) == 3
 
 
 def test_fwd_alignment(lib):
@@ -453,4 +479,4 @@ def test_static_forward_validation(lib):
     assert call(bias=A + 5 * GB, gh=4, gw=15) == 2
     assert call(B=64, H=16, N=16384, d=128) == 5          # needs more than BA_STATIC_SCRATCH_MIB
     assert b"scratch" in lib.ba_last_error()
-    assert call(bias=A + 5 * GB, gh=100, gw=70, N=7000) == 3
+    assert call(bias=A + 5 * GB, gh=100, gw=70, N=7000) == 5             # its dense bias exceeds the scratch
