@@ -361,6 +361,7 @@ __device__ __forceinline__ void flash_copy(const FCtx<D>& c, FBuf<D, BIAS>& tb, 
   // (the scalar offsets go through readfirstlane: the compiler cannot tell
   // that they are uniform and would otherwise loop over their lane values)
   const uint32_t k0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(run.k0));
+  __builtin_assume(static_cast<unsigned>(c.wave) < 4u);  // kThreads = 256
   char* kdst = reinterpret_cast<char*>(&tb.k[0]);
 #pragma unroll
   for (int j = 0; j < (2 * F::NCH + 3) / 4; ++j)
@@ -402,10 +403,20 @@ __device__ __forceinline__ void flash_copy(const FCtx<D>& c, FBuf<D, BIAS>& tb, 
     asm volatile("" : "+v"(tid));
     const uint32_t loff = tid * 16;
     char* bdst = reinterpret_cast<char*>(&tb.win[0]);
+    // 1 KiB pieces, every lane copying 16 bytes; when the window is not a
+    // whole number of pieces its last piece ends at the window's end and
+    // overlaps the one before it (both write the same bytes there), so no
+    // copy depends on a lane condition.  Windows are at least 1280 bytes.
+    const int full = c.win_bytes >> 10, pieces = (c.win_bytes + 1023) >> 10;
+    const int back = c.win_bytes - 1024 * pieces;  // -(1024 - rest) or 0
 #pragma unroll
-    for (int j = 0; j < (F::WIN * 4 + 4095) / 4096; ++j)
-      if (static_cast<int>(loff) + 4096 * j < c.win_bytes)
-        dma16(c.brs, bdst + (c.wave + 4 * j) * 1024, loff + 4096 * j, bs);
+    for (int j = 0; j < (F::WIN * 4 + 4095) / 4096; ++j) {
+      const int p = c.wave + 4 * j;
+      if (p < pieces) {
+        const int sh = p == full ? back : 0;
+        dma16(c.brs, bdst + p * 1024 + sh, loff + 4096 * j, bs + static_cast<uint32_t>(sh));
+      }
+    }
     w.u[0] = (ky[1] - ky[0]) * 16 * a.Lpad + kx[0] * 4;
     w.u[1] = kx[1] * 4;
   } else {
@@ -662,30 +673,32 @@ __device__ __forceinline__ void flash_priority(FPrio& p, int t) {
 // tile.  Block 1's QK and inputs go through s1 / in1, its pending block
 // through ppb.  wc, wn, wf: the window offsets of the tiles in cur, nxt and
 // far.
-template <int D, int BIAS, bool EXACT>
+template <int D, int BIAS, bool EXACT, bool INNER>
 __device__ __forceinline__ void flash_tile(const FCtx<D>& c, const FBuf<D, BIAS>& cur, const FBuf<D, BIAS>& nxt,
                                            FBuf<D, BIAS>& far, const FWin& wc, const FWin& wn, FWin& wf, FRun& run,
                                            FPrio& prio, int t, int nkt, v16f& s0, v16f& s1, FIn& in0, FIn& in1,
                                            FPend<D>& ppa, FPend<D>& ppb, FAcc<D>& acc, float& mrow, v16f& w) {
   const FwdArgs& a = *c.a;
   const int k0 = t * kBN;
-  const bool has1 = k0 + 32 < a.N;
+  const bool has1 = INNER || k0 + 32 < a.N;
   v4i kop[FDims<D>::NCH];
   // block 0: the next block is this tile's block 1
   flash_kops(c, cur, 1, kop);
   flash_fetch(c, cur, wc, 1, in1);
-  flash_block<D, BIAS, EXACT>(c, cur, 0, s0, in0, kop, s1, ppa, ppb, acc, k0, k0 + 32 > a.N, mrow, w, in1);
+  flash_block<D, BIAS, EXACT>(c, cur, 0, s0, in0, kop, s1, ppa, ppb, acc, k0, !INNER && k0 + 32 > a.N, mrow, w,
+                              in1);
   // tile t+1 is in `nxt` once every wave's copies have landed; every wave is
   // done with tile t-1, whose buffer `far` takes tile t+2
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (t + 2 < nkt) flash_copy(c, far, run, wf);
+  if (INNER || t + 2 < nkt) flash_copy(c, far, run, wf);
   flash_priority(prio, t);
   if (__builtin_expect(has1, 1)) {
     // block 1: the next block is tile t+1's block 0
     flash_kops(c, nxt, 0, kop);
     flash_fetch(c, nxt, wn, 0, in0);
-    flash_block<D, BIAS, EXACT>(c, cur, 1, s1, in1, kop, s0, ppb, ppa, acc, k0 + 32, k0 + 64 > a.N, mrow, w, in0);
+    flash_block<D, BIAS, EXACT>(c, cur, 1, s1, in1, kop, s0, ppb, ppa, acc, k0 + 32, !INNER && k0 + 64 > a.N, mrow,
+                                w, in0);
   } else {
     ppa = ppb;  // the last tile ends after block 0
   }
@@ -730,14 +743,26 @@ __device__ __forceinline__ float flash_pass(const FCtx<D>& c, FBuf<D, BIAS>& b0,
   for (int st = 0; st < 2; ++st)
 #pragma unroll
     for (int cb = 0; cb < FDims<D>::CB; ++cb) ppa.vop[st][cb] = v8bf{};
-  for (int t = 0; t < nkt; t += 3) {
-    flash_tile<D, BIAS, EXACT>(c, b0, b1, b2, w0, w1, w2, run, prio, t, nkt, s0, s1, in0, in1, ppa, ppb, acc, mrow, wk);
+  // Inner tiles (a copy to issue and two full blocks; every tile but the
+  // last four) in groups of three with no per-tile tests, then the rest.
+  int t = 0;
+  for (; t + 5 <= nkt; t += 3) {
+    flash_tile<D, BIAS, EXACT, true>(c, b0, b1, b2, w0, w1, w2, run, prio, t, nkt, s0, s1, in0, in1, ppa, ppb, acc,
+                                     mrow, wk);
+    flash_tile<D, BIAS, EXACT, true>(c, b1, b2, b0, w1, w2, w0, run, prio, t + 1, nkt, s0, s1, in0, in1, ppa, ppb, acc,
+                                     mrow, wk);
+    flash_tile<D, BIAS, EXACT, true>(c, b2, b0, b1, w2, w0, w1, run, prio, t + 2, nkt, s0, s1, in0, in1, ppa, ppb, acc,
+                                     mrow, wk);
+  }
+  for (; t < nkt; t += 3) {
+    flash_tile<D, BIAS, EXACT, false>(c, b0, b1, b2, w0, w1, w2, run, prio, t, nkt, s0, s1, in0, in1, ppa, ppb, acc,
+                                      mrow, wk);
     if (t + 1 >= nkt) break;
-    flash_tile<D, BIAS, EXACT>(c, b1, b2, b0, w1, w2, w0, run, prio, t + 1, nkt, s0, s1, in0, in1, ppa, ppb, acc,
-                               mrow, wk);
+    flash_tile<D, BIAS, EXACT, false>(c, b1, b2, b0, w1, w2, w0, run, prio, t + 1, nkt, s0, s1, in0, in1, ppa, ppb,
+                                      acc, mrow, wk);
     if (t + 2 >= nkt) break;
-    flash_tile<D, BIAS, EXACT>(c, b2, b0, b1, w2, w0, w1, run, prio, t + 2, nkt, s0, s1, in0, in1, ppa, ppb, acc,
-                               mrow, wk);
+    flash_tile<D, BIAS, EXACT, false>(c, b2, b0, b1, w2, w0, w1, run, prio, t + 2, nkt, s0, s1, in0, in1, ppa, ppb,
+                                      acc, mrow, wk);
   }
   // drain: the last block's P.V and row sums
 #pragma unroll
@@ -861,7 +886,9 @@ bool flash_supported(int d, int mode, int win_rows, int Lpad) {
   if (mode == kBiasNone) return true;
   if (mode != kBiasRows) return false;
   const int win = win_rows * 4 * Lpad;
-  return win <= (d <= 72 ? FDims<64>::WIN : FDims<128>::WIN);
+  // the copies take the window in 1 KiB pieces, the last one ending at the
+  // window's end
+  return win >= 256 && win <= (d <= 72 ? FDims<64>::WIN : FDims<128>::WIN);
 }
 
 int flash_static_lds(int d, int mode) {

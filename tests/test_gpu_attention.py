@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import workloads
-from gpu_cases import announce, o_error, oracle_rows, sample_rows, to_dev
+from gpu_cases import announce, device, o_error, oracle_rows, sample_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -94,6 +94,28 @@ def test_fwd_large_logits_ragged_rows():
     announce("fwd large logits ragged rows")
     inp = workloads.make_inputs(1, 2, 96, 64, seed=19, grid=(3, 32), q_scale=8.0, k_scale=8.0)
     o = run(inp)
+    err = o_error(o, oracle_rows(inp), inp["v"])
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("N,d,grid", [(100, 64, None), (65, 72, None), (160, 128, None), (96, 64, (3, 32)),
+                                      (96, 72, (3, 32)), (480, 32, (5, 96))])
+def test_fwd_keys_past_n_never_read(N, d, grid):
+    """Keys past N of the last head: V ends where the allocation's NaN-filled
+    tail starts, so a tile copy that read rows past N would put NaN into O
+    (a masked key has P = 0, and 0 * NaN is NaN)."""
+    announce("fwd V at the end of a NaN tail", N, d, grid)
+    B, H = 1, 2
+    inp = workloads.make_inputs(B, H, N, d, seed=700 + N + d, grid=grid, bias=grid is not None)
+    dev = to_dev(inp)
+    n = B * H * N * d
+    store = torch.full((n + 64 * 1024,), float("nan"), dtype=torch.bfloat16, device=device())
+    store[:n] = dev["v"].reshape(-1)
+    v = store[:n].view(B, H, N, d)
+    gh, gw = grid if grid is not None else (0, 0)
+    o = bq.attention_fwd(dev["q"], dev["k"], v, dev["table"], gh, gw)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
     err = o_error(o, oracle_rows(inp), inp["v"])
     assert err <= TOL, err
 
