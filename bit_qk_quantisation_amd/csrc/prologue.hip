@@ -127,6 +127,9 @@ __device__ __forceinline__ int vt_slot_key(int slot) {
 __device__ void kv_codes(const KvJob& job, int64_t blk, int64_t bh, int tile, const uint16_t* vs, int stride,
                          float* sinv, float* red);
 
+// KONLY: the keys alone (no value tile, codes, maxima or sign tiles), the
+// variant the forward launches when its fused kernel reads V in place.
+template <bool KONLY>
 __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
   const int d = job.d, W = job.W, C = d / 8, stride = d + 8;  // bf16 units
   const int tiles = job.Npad / kPackTok;
@@ -145,7 +148,7 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
   const uint16_t* kbase = job.k + token_offset(job.ks, b, h, n0);
   const uint16_t* vbase = job.v + token_offset(job.vs, b, h, n0);
   // the values are read only for an output that needs them
-  const bool want_v = job.vt || job.vq || job.vmax || job.vnat;
+  const bool want_v = !KONLY && (job.vt || job.vq || job.vmax || job.vnat);
   uint4 kr[kMaxChunks], vr[kMaxChunks];
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
@@ -165,14 +168,14 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
       float part;
       store_sign_bytes(sb, tok, ch, W, chunk_signs(kr[i], part));
       sp[tok * 33 + ch] = part;
-      if (job.vt || job.vq) *reinterpret_cast<uint4*>(vs + tok * stride + ch * 8) = vr[i];
-      if (job.vnat)
+      if (!KONLY && (job.vt || job.vq)) *reinterpret_cast<uint4*>(vs + tok * stride + ch * 8) = vr[i];
+      if (!KONLY && job.vnat)
         stream_out(job.vnat + (bh * job.Npad + n0 + tok) * d + ch * 8, v4u{vr[i].x, vr[i].y, vr[i].z, vr[i].w});
     }
   }
   zero_pad_bytes(sb, C, W);
   __shared__ float vwave[kThreads / 64];
-  if (job.vmax) {
+  if (!KONLY && job.vmax) {
     // largest |v| of the tile (chunks past N hold 0)
     float m = 0.0f;
 #pragma unroll
@@ -188,7 +191,7 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
     if ((threadIdx.x & 63) == 0) vwave[threadIdx.x >> 6] = m;
   }
   __syncthreads();
-  if (job.vmax && threadIdx.x == 0) {
+  if (!KONLY && job.vmax && threadIdx.x == 0) {
     float m = vwave[0];
     for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, vwave[i]);
     job.vmax[blk] = m;
@@ -225,6 +228,7 @@ __device__ void kv_block(const KvJob& job, int64_t blk, unsigned char* smem) {
                              static_cast<uint32_t>(op[2]), static_cast<uint32_t>(op[3])});
   }
 
+  if (KONLY) return;
   if (job.kst) {
     // the tokens' signs as +/-1 bf16, transposed exactly as V^T below
     uint16_t* sout = job.kst + blk * static_cast<int64_t>(job.dpad) * kPackTok;
@@ -469,16 +473,23 @@ __device__ void expand_row(const ExpandJob& j, int64_t blk) {
   }
 }
 
+// FWD: the forward's jobs alone (keys without values, bias rows, the
+// expanded bias), compiled without the others so that the kernel needs
+// fewer registers (63 instead of 95 VGPRs, no scratch) and more of its
+// blocks are resident at once.
+template <bool FWD>
 __global__ void __launch_bounds__(kThreads) prologue_kernel(PrologueArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int64_t blk = blockIdx.x;
-  if (blk < a.pack_blocks) {
-    pack_block(a.pack, blk, smem);
-    return;
+  if (!FWD) {
+    if (blk < a.pack_blocks) {
+      pack_block(a.pack, blk, smem);
+      return;
+    }
+    blk -= a.pack_blocks;
   }
-  blk -= a.pack_blocks;
   if (blk < a.kv_blocks) {
-    kv_block(a.kv, blk, smem);
+    kv_block<FWD>(a.kv, blk, smem);
     return;
   }
   blk -= a.kv_blocks;
@@ -487,6 +498,10 @@ __global__ void __launch_bounds__(kThreads) prologue_kernel(PrologueArgs a) {
     return;
   }
   blk -= a.bias_blocks;
+  if (FWD) {
+    if (blk < a.expand_blocks) expand_row(a.expand, blk);
+    return;
+  }
   if (blk < a.vstat_blocks) {
     vstat_block(a.vstat, blk, smem);
     return;
@@ -599,8 +614,19 @@ __global__ void __launch_bounds__(kThreads) prologue_kernel(PrologueArgs a) {
 int launch_prologue(const PrologueArgs& a, void* stream) {
   const int64_t blocks = a.pack_blocks + a.kv_blocks + a.bias_blocks + a.vstat_blocks + a.bias2_blocks +
                         a.dtr_blocks + a.lse_blocks + a.delta_blocks + a.expand_blocks;
-  hipLaunchKernelGGL(prologue_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), a.lds,
-                     static_cast<hipStream_t>(stream), a);
+  const KvJob& kv = a.kv;
+  const bool keys_only = a.kv_blocks == 0 || (!kv.vt && !kv.vq && !kv.vmax && !kv.vnat && !kv.kst);
+  const bool fwd = keys_only && a.pack_blocks == 0 && a.vstat_blocks == 0 && a.bias2_blocks == 0 &&
+                   a.dtr_blocks == 0 && a.lse_blocks == 0 && a.delta_blocks == 0;
+  if (fwd) {
+    // the keys-only tile needs the partial sums and sign words alone
+    const int lds = a.kv_blocks > 0 ? prologue_lds(kv.d, false) : 0;
+    hipLaunchKernelGGL(prologue_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), lds,
+                       static_cast<hipStream_t>(stream), a);
+  } else {
+    hipLaunchKernelGGL(prologue_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), a.lds,
+                       static_cast<hipStream_t>(stream), a);
+  }
   return static_cast<int>(hipGetLastError());
 }
 
