@@ -14,7 +14,8 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * - Tensors are dense, row-major, with no strides:
+ * - Tensors are dense and row-major (ba_attention_fwd_strided and the
+ *   dense-bias entries also take strided views, as they state):
  *   Q, K, V and O are bf16 [B, H, N, d].  The bias table is bf16
  *   [H, 2*gh-1, 2*gw-1].  Packed sign words are uint32 [B, H, N, W] with
  *   W = ceil(d/32).  Scales are float32 [B, H, N].
@@ -38,7 +39,7 @@
  *   BA_ERR_UNSUPPORTED.  N >= 1, B >= 1, H >= 1, and B*H*N must stay below
  *   2^31 tokens.
  *
- * Packed-sign layout (fixed; ba_pack_signs writes it and the fused kernel
+ * Packed-sign layout (fixed; ba_pack_signs writes it and ba_qk_int_dot
  * reads it): channel c goes to word c/32, bit c%32, least significant bit
  * first.  A bit is 1 iff the channel value compares < 0, so +0.0 and -0.0
  * both give 0 (sign +1).  Bits for channels >= d are 0.
@@ -103,7 +104,9 @@ ba_status ba_pack_signs(const void* x, int64_t B, int64_t H, int64_t N, int d,
  * table rows in float32, where the prepared forward runs the pipelined
  * kernel (see ba_attention_fwd) a copy of V in its own layout [B,H,Npad,d],
  * and, for shapes the pipelined kernel takes, each K scale as three bf16
- * terms laid out as a matrix operand (12 bytes per token).  The queries are
+ * terms laid out as a matrix operand (12 bytes per token), and for a grid
+ * whose table is written out as a dense bias (see ba_attention_fwd) that
+ * bias, bf16 [H, Npad, Npad].  The queries are
  * packed inside the fused kernel.  Pass gh = gw = 0 for a
  * call without bias table.  Returns 0 for sizes the library rejects
  * (including gh*gw != N when a grid is given). */
@@ -134,7 +137,11 @@ size_t ba_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int gh, int gw
  * with the table rows (gw % 32 == 0, window small enough) or no bias, the
  * fused kernel is the pipelined one, which reads V where it lies; otherwise
  * the prologue also writes V^T into the workspace for it.  For N <= 256,
- * d in {32, 64} and no table rows, one kernel does everything.
+ * d in {32, 64} and no table rows, one kernel does everything.  A table on
+ * a grid that neither the table-row reads (gw % 32 == 0) nor the whole-table
+ * reads (table <= 48 KB) take is written out by the prologue as a dense bias
+ * bf16 [H, Npad, Npad] in the workspace, which the dense-bias kernel reads
+ * (N up to 46336; beyond that such a table gives BA_ERR_UNSUPPORTED).
  * Errors: BA_ERR_NULL, BA_ERR_SHAPE, BA_ERR_UNSUPPORTED, BA_ERR_ALIGN,
  *         BA_ERR_WORKSPACE, BA_ERR_HIP. */
 ba_status ba_attention_fwd(const void* q, const void* k, const void* v,
