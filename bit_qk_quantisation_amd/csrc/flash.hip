@@ -351,9 +351,9 @@ __device__ __forceinline__ float flash_queries(FCtx<D>& c, const FwdArgs& a, con
 // ---------------------------------------------------------------- copies --
 // Starts the copies of the tile `run` names into `tb`, records its window
 // offsets in `w` and advances `run` to the next tile.  Lane l of a wave
-// fills bytes [16 l, 16 l + 16) of a 1 KiB piece (4 bytes of the key
-// scales).  Every source offset is uniform; the per-wave piece choices are
-// uniform branches.
+// fills bytes [16 l, 16 l + 16) of a 1 KiB piece (the 768 bytes of key-scale
+// operands take 48 lanes of one wave).  Every source offset is uniform; the
+// per-wave piece choices are uniform branches.
 template <int D, int BIAS>
 __device__ __forceinline__ void flash_copy(const FCtx<D>& c, FBuf<D, BIAS>& tb, FRun& run, FWin& w) {
   using F = FDims<D>;
@@ -672,7 +672,8 @@ __device__ __forceinline__ void flash_priority(FPrio& p, int t) {
 // tile's block 0 and ppa the pending block; on exit the same for the next
 // tile.  Block 1's QK and inputs go through s1 / in1, its pending block
 // through ppb.  wc, wn, wf: the window offsets of the tiles in cur, nxt and
-// far.
+// far.  INNER: a tile with a copy to issue and two full blocks (every tile
+// but the last four), so none of the per-tile tests run.
 template <int D, int BIAS, bool EXACT, bool INNER>
 __device__ __forceinline__ void flash_tile(const FCtx<D>& c, const FBuf<D, BIAS>& cur, const FBuf<D, BIAS>& nxt,
                                            FBuf<D, BIAS>& far, const FWin& wc, const FWin& wn, FWin& wf, FRun& run,
