@@ -54,6 +54,9 @@ SMALL = [
     (1, 1, 32, 32, 72, 2.0, 1.0),   # table rows, d = 72
     (1, 2, 32, 32, 64, 1.0, 8.0),   # table rows, online softmax
     (1, 1, 4, 128, 64, 2.0, 1.0),   # table rows, width 128
+    (1, 2, 9, 32, 32, 2.0, 1.0),    # table rows, d = 32 (N = 288: inner tile group, then the last tiles)
+    (1, 1, 6, 64, 32, 1.0, 8.0),    # table rows, d = 32, online softmax
+    (1, 1, 4, 128, 128, 2.0, 1.0),  # table rows, width 128, d = 128 (one window row per tile)
 ]
 
 
