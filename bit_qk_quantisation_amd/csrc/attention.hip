@@ -325,8 +325,9 @@ __device__ __forceinline__ void block_logits(const Ctx<NCH>& c, const TB& tb, co
 // rescales the accumulators when it grows by more than 8, and shifts the
 // logits by it.  NATURAL: the logits come in natural-log units and are
 // turned into log2 units by the shift itself (one FMA per logit).  A row
-// whose keys so far all have logit -inf (a dense bias may mask keys) keeps
-// mrow = -inf and is shifted by 0, so its probabilities stay 0, not NaN.
+// whose keys so far all have logit -inf (a dense bias or a table may mask
+// keys) keeps mrow = -inf, its (zero) sums unscaled, and is shifted by 0, so
+// its probabilities stay 0, not NaN.
 template <bool NATURAL, int CB, bool XONES>
 __device__ __forceinline__ void block_rescale(float (&sc)[16], Acc<CB, XONES>& acc, float& mrow) {
   float mt = sc[0];
@@ -336,7 +337,7 @@ __device__ __forceinline__ void block_rescale(float (&sc)[16], Acc<CB, XONES>& a
   if (NATURAL) mt *= kLog2e;
   const float mnew = fmaxf(mrow, mt);
   if (__any(mnew > mrow + 8.0f)) {
-    const float f = fast_exp2(mrow - mnew);
+    const float f = mnew > -INFINITY ? fast_exp2(mrow - mnew) : 1.0f;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc.o[cb] *= f;
     if (XONES) {
@@ -350,8 +351,9 @@ __device__ __forceinline__ void block_rescale(float (&sc)[16], Acc<CB, XONES>& a
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = fmaf(sc[r], kLog2e, -shift);
   } else {
+    const float shift = mrow == -INFINITY ? 0.0f : mrow;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sc[r] -= mrow;
+    for (int r = 0; r < 16; ++r) sc[r] -= shift;
   }
 }
 

@@ -620,14 +620,17 @@ __device__ __forceinline__ void flash_block_exact(const FCtx<D>& c, const FBuf<D
   mt = max_halves(mt);
   const float mnew = fmaxf(mrow, mt);
   if (__any(mnew > mrow + 8.0f)) {
-    const float f = fast_exp2(mrow - mnew);
+    // a row that has seen only -inf logits keeps its (zero) sums
+    const float f = mnew > -INFINITY ? fast_exp2(mrow - mnew) : 1.0f;
 #pragma unroll
     for (int cb = 0; cb < FDims<D>::CB; ++cb) acc.o[cb] *= f;
     acc.l *= f;
     mrow = mnew;
   }
+  // such a row takes its P against 0: exp2(-inf) = 0, not exp2(-inf + inf)
+  const float off = mrow > -INFINITY ? mrow : 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) nw.pk[j] = pack_bf16x2(fast_exp2(x[2 * j] - mrow), fast_exp2(x[2 * j + 1] - mrow));
+  for (int j = 0; j < 8; ++j) nw.pk[j] = pack_bf16x2(fast_exp2(x[2 * j] - off), fast_exp2(x[2 * j + 1] - off));
   w = flash_scales(c, innext.aop);
 }
 

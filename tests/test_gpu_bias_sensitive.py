@@ -183,3 +183,38 @@ def test_fwd_rescale_late_in_the_keys(gh, gw):
     err = o_error(o, ref, inp["v"], rows)
     print("max err / max|V| =", err)
     assert err <= TOL, err
+
+
+LOCAL = [
+    # B, H, gh, gw, d: table rows (pipelined kernel), the whole table in LDS
+    # (one-launch and general kernels), d = 72 and d = 128
+    (1, 2, 8, 64, 64),
+    (1, 1, 4, 32, 72),
+    (1, 1, 4, 128, 128),
+    (1, 2, 14, 14, 64),
+    (1, 2, 20, 20, 64),
+]
+
+
+@pytest.mark.parametrize("B,H,gh,gw,d", LOCAL)
+def test_fwd_local_window_table(B, H, gh, gw, d):
+    """A table that masks every key more than 1 grid row or 3 columns away
+    with -inf (windowed attention through the bias).  The logit bound is
+    infinite, so the online softmax runs, and most queries meet whole key
+    blocks of -inf logits before their first finite one: those blocks must
+    contribute 0, not NaN."""
+    announce("fwd local-window table", B, H, gh, gw, d)
+    inp = workloads.make_inputs(B, H, gh * gw, d, seed=7100 + gh * gw + d, grid=(gh, gw), table_sigma=1.0)
+    t = inp["table"].clone()
+    dy = torch.arange(-(gh - 1), gh).abs().view(1, -1, 1)
+    dx = torch.arange(-(gw - 1), gw).abs().view(1, 1, -1)
+    far = ((dy > 1) | (dx > 3)).expand_as(t)
+    t[far] = float("-inf")
+    inp["table"] = t
+    ref = bc.oracle_o(inp)
+    assert np.isfinite(ref).all()
+    o = run(inp)
+    assert torch.isfinite(o.float()).all()
+    err = o_error(o, ref, inp["v"])
+    print("max err / max|V| =", err)
+    assert err <= TOL, err
