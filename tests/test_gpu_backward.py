@@ -26,10 +26,12 @@ bq = pytest.importorskip("bit_qk_quantisation_amd")
 TOL = 1e-2
 
 
-def run_case(B, H, gh, gw, d, seed, bias=True, q_scale=1.0, table_sigma=0.02, discriminate=False):
+def run_case(B, H, gh, gw, d, seed, bias=True, q_scale=1.0, table_sigma=0.02, discriminate=False, table_fn=None):
     N = gh * gw
     inp = workloads.make_inputs(B, H, N, d, seed=seed, grid=(gh, gw) if bias else None, bias=bias,
                                 q_scale=q_scale, table_sigma=table_sigma)
+    if table_fn is not None:
+        inp["table"] = table_fn(inp["table"])
     rng = np.random.default_rng(seed + 1)
     do = torch.from_numpy(rng.standard_normal((B, H, N, d)).astype(np.float32)).to(torch.bfloat16)
     dev = to_dev(inp)
@@ -191,3 +193,23 @@ def test_fwd_train_and_saved_bwd(B, H, gh, gw, d, bias, q_scale):
         scale = np.abs(a64).max()
         assert float(np.abs(a64 - b64).max()) <= 1e-3 * scale, name
         assert float(np.abs(b64 - gref[name]).max() / np.abs(gref[name]).max()) <= TOL, name
+
+
+def local_window(table):
+    """-inf for every offset more than one grid row or three columns away."""
+    H, r, c = table.shape
+    gh, gw = (r + 1) // 2, (c + 1) // 2
+    dy = torch.arange(-(gh - 1), gh).abs().view(1, -1, 1)
+    dx = torch.arange(-(gw - 1), gw).abs().view(1, 1, -1)
+    t = table.clone()
+    t[((dy > 1) | (dx > 3)).expand_as(t)] = float("-inf")
+    return t
+
+
+@pytest.mark.parametrize("B,H,gh,gw,d", [(1, 2, 8, 8, 64), (1, 1, 8, 64, 64), (1, 1, 4, 32, 128)])
+def test_bwd_local_window_table(B, H, gh, gw, d):
+    """Gradients through a table that masks far keys with -inf: the masked
+    pairs contribute nothing to dq, dk, dv, and their table entries get a
+    zero gradient (table mode, table rows, d = 128)."""
+    announce("bwd local-window table", B, H, gh, gw, d)
+    run_case(B, H, gh, gw, d, seed=7300 + gh * gw + d, table_sigma=1.0, table_fn=local_window)
