@@ -874,14 +874,15 @@ __device__ __forceinline__ void fwd_epilogue(const Ctx<NCH>& c, const FwdArgs& a
   out_stage_flush(a, ws, C, sw, lane, c.bh / a.H, c.head, c.q0 + wave * 32);
 }
 
-// Waves per SIMD the register budget is sized for (accumulator blocks).
-template <int NB>
+// Waves per SIMD the register budget is sized for (accumulator blocks, QK
+// chunks).
+template <int NB, int NCH = 1>
 struct Occupancy {
-  static constexpr int kWaves = fwd_waves_for_blocks(NB);
+  static constexpr int kWaves = fwd_waves_for_blocks(NB, NCH);
 };
 
 template <int NCH, int CB, bool XONES, int BIAS>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<CB + XONES>::kWaves)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<CB + XONES, NCH>::kWaves)))
 attn_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb0;
   __shared__ __attribute__((aligned(16))) TileBuf<NCH, CB, BIAS> tb1;
@@ -1897,7 +1898,7 @@ static int static_lds_for(int cb) {
   }
 }
 
-int fwd_waves_per_simd(int dpad, int d) { return fwd_waves_for_blocks(dpad / 32 + (d % 32 == 0 ? 1 : 0)); }
+int fwd_waves_per_simd(int dpad, int d) { return fwd_waves_for_blocks(dpad / 32 + (d % 32 == 0 ? 1 : 0), (d + 63) / 64); }
 
 int fwd_static_lds(int dpad, int mode) {
   const int cb = dpad / 32;

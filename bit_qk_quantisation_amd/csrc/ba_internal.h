@@ -237,7 +237,13 @@ int fwd_static_lds(int dpad, int mode);
 // Waves per SIMD the fused kernel's register budget allows: 3 for up to 3
 // accumulator blocks (32 output channels each, plus one when d % 32 == 0),
 // 2 for up to 5, else 1.
-constexpr int fwd_waves_for_blocks(int nb) { return nb <= 3 ? 3 : (nb <= 5 ? 2 : 1); }
+// Waves per SIMD the general kernel's register budget is sized for, from
+// its accumulator blocks nb and its 64-channel QK chunks nch: three blocks
+// fit 168 registers with one chunk and not with two (d in (64, 96)), five
+// fit 256 with two chunks and not with three (d in (128, 160)).
+constexpr int fwd_waves_for_blocks(int nb, int nch = 1) {
+  return (nb <= 3 && nch == 1) ? 3 : ((nb <= 5 && nch <= 2) ? 2 : 1);
+}
 int fwd_waves_per_simd(int dpad, int d);
 
 // Launch the fused kernel (template selected from d and the bias mode).

@@ -45,6 +45,9 @@ def run(inp):
     (1, 2, 9, 32, 32),     # d = 32, N = 288: two launches, output rows staged in LDS
     (1, 1, 2, 96, 40),     # gw = 96, d = 40
     (1, 1, 3, 32, 200),
+    (1, 1, 7, 9, 80),      # table mode, d = 80: two QK chunks, three output blocks
+    (1, 1, 7, 9, 144),     # table mode, d = 144: three QK chunks, five output blocks
+    (1, 1, 3, 32, 144),    # table rows, d = 144
     (1, 1, 2, 64, 256),
     (1, 1, 2, 128, 8),
     # table rows with a ragged last tile (N % 64 == 32) and d % 32 == 0, where
@@ -62,7 +65,8 @@ def test_fwd_small_with_bias(B, H, gh, gw, d):
 
 
 @pytest.mark.parametrize("B,H,N,d", [(1, 1, 1, 64), (1, 2, 2, 64), (2, 1, 63, 32), (1, 1, 64, 64),
-                                     (1, 2, 65, 72), (1, 1, 129, 128), (1, 1, 300, 16)])
+                                     (1, 2, 65, 72), (1, 1, 129, 128), (1, 1, 300, 16),
+                                     (1, 1, 100, 144)])
 def test_fwd_small_no_bias(B, H, N, d):
     announce("fwd nobias", B, H, N, d)
     inp = workloads.make_inputs(B, H, N, d, seed=400 + N + d, bias=False)
