@@ -1674,8 +1674,18 @@ __device__ __forceinline__ void binarize_back_store(bool valid, const uint16_t* 
     }
 }
 
+// Waves per SIMD the backward's register budget is sized for.  At d = 128
+// (two QK chunks) the tiles take 75-125 KB of LDS, one or two workgroups per
+// CU; held to 256 registers the query-role variants spilled 55 and 71 of
+// them, and at one wave they run 19-22 % faster.  The d <= 64 variants keep
+// two waves (their few spills cost less than half the occupancy).
+template <int NCH>
+struct BwdOcc {
+  static constexpr int kWaves = NCH == 2 ? 1 : 2;
+};
+
 template <int ROLE, int NCH, int CB, int BIAS>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BwdOcc<NCH>::kWaves)))
 attn_bwd_kernel(BwdArgs ba) {
   __shared__ __attribute__((aligned(16))) BwdTileBuf<ROLE, NCH, CB, BIAS> tb0;
   __shared__ __attribute__((aligned(16))) BwdTileBuf<ROLE, NCH, CB, BIAS> tb1;
