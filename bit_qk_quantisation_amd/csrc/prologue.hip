@@ -413,26 +413,36 @@ __device__ void bias_block(const BiasJob& job, int64_t blk) {
   const uint16_t* trow = job.table + (h * rows + (inside ? (job.flip ? rows - 1 - dy : dy) : 0)) * cols;
   float4* out = reinterpret_cast<float4*>(job.bias4 + row * 4 * static_cast<int64_t>(job.Lpad));
   // Every table entry of the lane's 16-byte pieces is loaded before any
-  // piece is stored.  Lpad % 4 == 0: the four floats of a piece lie in one
-  // copy s.
-  float val[kBiasPieces][4];
-  float m = 0.0f;
+  // piece is stored, and every load is issued unconditionally (an entry the
+  // piece does not take reads column 0 and is discarded): loads under a
+  // condition would each wait for the one before.  Lpad % 4 == 0: the four
+  // floats of a piece lie in one copy s.
+  uint16_t raw[kBiasPieces][4];
+  bool take[kBiasPieces][4];
 #pragma unroll
   for (int i = 0; i < kBiasPieces; ++i) {
     const int e = 4 * (lane + 64 * i), s = e / job.Lpad, v = e - s * job.Lpad;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int u = v + t + s;
+      take[i][t] = inside && e < 4 * job.Lpad && u <= cols - 1;
+      const int uc = take[i][t] ? u : 0;
+      raw[i][t] = trow[job.flip ? uc : cols - 1 - uc];
+    }
+  }
+  float val[kBiasPieces][4];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kBiasPieces; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
       // Padding rows are -inf: the only (query, key) pairs that reach them
       // involve a padded token.  They keep the fused kernel's window reads
       // inside the rows; that kernel masks padded keys itself, since a
       // padded key seen from a query on grid row >= 1 falls on a real row.
-      val[i][t] = inside ? 0.0f : -INFINITY;
-      if (inside && e < 4 * job.Lpad && u <= cols - 1)
-        val[i][t] = kLog2e * bf16_to_f32(trow[job.flip ? u : cols - 1 - u]);
+      val[i][t] = take[i][t] ? kLog2e * bf16_to_f32(raw[i][t]) : (inside ? 0.0f : -INFINITY);
       if (inside) m = fmaxf(m, fabsf(val[i][t]));
     }
-  }
 #pragma unroll
   for (int i = 0; i < kBiasPieces; ++i)
     if (lane + 64 * i < job.Lpad)
@@ -458,16 +468,21 @@ __device__ void expand_row(const ExpandJob& j, int64_t blk) {
     uint32_t w[4] = {0u, 0u, 0u, 0u};
     if (i < j.N) {
       int yj = j0 / j.gw, xj = j0 - yj * j.gw;
+      // the eight loads go out unconditionally (a key past N reads the
+      // table's centre entry and is dropped), so that none waits for another
+      uint32_t val[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        uint32_t val = 0u;
-        if (j0 + e < j.N) val = tab[(yi - yj + j.gh - 1) * cols + (xi - xj + j.gw - 1)];
-        w[e >> 1] |= val << (16 * (e & 1));
+        const bool real = j0 + e < j.N;
+        val[e] = tab[real ? (yi - yj + j.gh - 1) * cols + (xi - xj + j.gw - 1) : (j.gh - 1) * cols + j.gw - 1];
+        val[e] = real ? val[e] : 0u;
         if (++xj == j.gw) {
           xj = 0;
           ++yj;
         }
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e >> 1] |= val[e] << (16 * (e & 1));
     }
     stream_out(out + j0, v4u{w[0], w[1], w[2], w[3]});
   }
