@@ -676,6 +676,17 @@ __device__ __forceinline__ float workgroup_setup(Ctx<NCH>& c, const FwdArgs& a, 
   float qpart = 0.0f;
   {
     const uint16_t* qrow = a.q + token_offset(a.qs, c.bh / a.H, c.head, c.qi < a.N ? c.qi : 0);
+    // every piece is loaded before any is used: a load consumed at once
+    // waits for the one before it, one memory round trip per piece
+    uint4 qv[NCH][4];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c0 = 32 * (2 * ch + c.lh) + 8 * k;
+        qv[ch][k] = make_uint4(0u, 0u, 0u, 0u);
+        if (c.qi < a.N && c0 < a.d) qv[ch][k] = *reinterpret_cast<const uint4*>(qrow + c0);
+      }
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       const int word = 2 * ch + c.lh;
@@ -685,7 +696,7 @@ __device__ __forceinline__ float workgroup_setup(Ctx<NCH>& c, const FwdArgs& a, 
         const int c0 = 32 * word + 8 * k;
         if (c.qi < a.N && c0 < a.d) {
           float part;
-          w |= chunk_signs(*reinterpret_cast<const uint4*>(qrow + c0), part) << (8 * k);
+          w |= chunk_signs(qv[ch][k], part) << (8 * k);
           qpart += part;
         }
       }
